@@ -1,0 +1,520 @@
+/*
+ * tt_oracle.c -- plain, slow CPU oracle for the TT-EmbeddingBag hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no code, header
+ * or table with the GPU library and must never be used by it.
+ *
+ * Everything is computed in fp64 from fp32 inputs widened exactly; the build
+ * uses -ffp-contract=off so every multiply and add rounds on its own.
+ *
+ * What is computed (sources are the pages this project follows):
+ *  - "FlowTT: Exploiting Computation Flow Reuse in Irregular Tensor-Train
+ *    Embedding" (paperlayer summary), sections 2.4 and 3.3: a row index is a
+ *    mixed-radix number whose early (high-order) digits select the leading TT
+ *    cores; rows that share those digits share the prefix intermediate.
+ *  - same page, section 3.2: the forward contracts C = A.B (first two cores),
+ *    then E = C.D (third core), then pools; the backward reverses it.
+ *  - same page, section 4 (latency breakdown): grouping is index sorting,
+ *    unique extraction, mixed-radix conversion, prefix extraction and
+ *    run-length encoding, in that order.
+ *  - "TT-Rec: Tensor Train Compression for Deep Learning Recommendation
+ *    Models" (abstract): the operator is an EmbeddingBag over rows rebuilt
+ *    from TT cores.
+ *
+ * Readings where the pages are silent (kept identical in the GPU library's
+ * documentation):
+ *  - digits are big-endian: i = (i1*n2 + i2)*n3 + i3, prefix = (i1, i2);
+ *  - core k is stored row-major as [n_k][R_{k-1}][d_k][R_k], R_0 = R_3 = 1;
+ *  - output column j = (j1*d2 + j2)*d3 + j3;
+ *  - pooling is a sum; an empty bag pools to 0;
+ *  - offsets are table-major CSR with T*B+1 entries; bag (t,b) is
+ *    indices[offsets[t*B+b] .. offsets[t*B+b+1]);
+ *  - the output is [B][sum_t D_t], tables concatenated in order;
+ *  - grouping sorts lookups by (table, row, position) -- a stable sort by row
+ *    within each table.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_ERR_ARG (-1)
+#define ORC_ERR_INDEX (-2)
+#define ORC_ERR_NOMEM (-6)
+
+/* ---------------------------------------------------------------- decode */
+
+/* Mixed-radix split of a row index into its three TT-core digits
+ * (FlowTT summary, sections 2.4 and 3.3: shared high-order digits). */
+static void decode3(int64_t i, const int32_t *n, int64_t *i1, int64_t *i2, int64_t *i3)
+{
+    *i3 = i % n[2];
+    int64_t q = i / n[2];
+    *i2 = q % n[1];
+    *i1 = q / n[1];
+}
+
+int orc_decode(int64_t i, const int32_t *n, int64_t *out3)
+{
+    if (i < 0 || n[0] <= 0 || n[1] <= 0 || n[2] <= 0) return ORC_ERR_ARG;
+    decode3(i, n, &out3[0], &out3[1], &out3[2]);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------ contraction */
+
+/* Prefix intermediate C = A.B of FlowTT section 3.2:
+ *   C[j1][j2][r2] = sum_{r1} G1[i1][0][j1][r1] * G2[i2][r1][j2][r2],
+ * r1 ascending.  C is stored [d1*d2][R2]. */
+static void prefix_c(const float *G1, const float *G2, const int32_t *d, const int32_t *R,
+                     int64_t i1, int64_t i2, double *C)
+{
+    const int d1 = d[0], d2 = d[1], R1 = R[1], R2 = R[2];
+    const float *g1 = G1 + i1 * (int64_t)d1 * R1;
+    const float *g2 = G2 + i2 * (int64_t)R1 * d2 * R2;
+    for (int j1 = 0; j1 < d1; ++j1)
+        for (int j2 = 0; j2 < d2; ++j2)
+            for (int r2 = 0; r2 < R2; ++r2) {
+                double acc = 0.0;
+                for (int r1 = 0; r1 < R1; ++r1)
+                    acc += (double)g1[j1 * R1 + r1] * (double)g2[((int64_t)r1 * d2 + j2) * R2 + r2];
+                C[(j1 * d2 + j2) * R2 + r2] = acc;
+            }
+}
+
+/* Row E = C.D of FlowTT section 3.2:
+ *   E[(j1*d2+j2)*d3 + j3] = sum_{r2} C[j1 j2][r2] * G3[i3][r2][j3][0],
+ * r2 ascending. */
+static void suffix_e(const double *C, const float *G3, const int32_t *d, const int32_t *R,
+                     int64_t i3, double *E)
+{
+    const int d12 = d[0] * d[1], d3 = d[2], R2 = R[2];
+    const float *g3 = G3 + i3 * (int64_t)R2 * d3;
+    for (int m = 0; m < d12; ++m)
+        for (int j3 = 0; j3 < d3; ++j3) {
+            double acc = 0.0;
+            for (int r2 = 0; r2 < R2; ++r2)
+                acc += C[m * R2 + r2] * (double)g3[r2 * d3 + j3];
+            E[m * d3 + j3] = acc;
+        }
+}
+
+/* One embedding row rebuilt from the cores, with no reuse (TT-Rec abstract:
+ * rows are reconstructed from TT cores; FlowTT 3.2 gives the order). */
+int orc_row(const float *G1, const float *G2, const float *G3, const int32_t *n,
+            const int32_t *d, const int32_t *R, int64_t i, double *E)
+{
+    int64_t i1, i2, i3;
+    if (i < 0) return ORC_ERR_INDEX;
+    decode3(i, n, &i1, &i2, &i3);
+    if (i1 >= n[0]) return ORC_ERR_INDEX;
+    double *C = (double *)malloc(sizeof(double) * (size_t)d[0] * d[1] * R[2]);
+    if (!C) return ORC_ERR_NOMEM;
+    prefix_c(G1, G2, d, R, i1, i2, C);
+    suffix_e(C, G3, d, R, i3, E);
+    free(C);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------- checking */
+
+static int check_tables(int32_t T, const int64_t *N, const int32_t *n, const int32_t *d,
+                        const int32_t *R)
+{
+    if (T <= 0) return ORC_ERR_ARG;
+    for (int t = 0; t < T; ++t) {
+        const int32_t *nt = n + 3 * t, *dt = d + 3 * t, *Rt = R + 4 * t;
+        if (N[t] <= 0) return ORC_ERR_ARG;
+        for (int k = 0; k < 3; ++k)
+            if (nt[k] <= 0 || dt[k] <= 0) return ORC_ERR_ARG;
+        if (Rt[0] != 1 || Rt[3] != 1 || Rt[1] <= 0 || Rt[2] <= 0) return ORC_ERR_ARG;
+        if ((int64_t)nt[0] * nt[1] * nt[2] < N[t]) return ORC_ERR_ARG;
+    }
+    return ORC_OK;
+}
+
+static int check_csr(int32_t T, const int64_t *N, const int64_t *indices, const int64_t *offsets,
+                     int64_t B, int64_t nnz)
+{
+    if (B < 0 || nnz < 0) return ORC_ERR_ARG;
+    if (offsets[0] != 0 || offsets[(int64_t)T * B] != nnz) return ORC_ERR_ARG;
+    for (int64_t k = 0; k < (int64_t)T * B; ++k)
+        if (offsets[k + 1] < offsets[k]) return ORC_ERR_ARG;
+    for (int t = 0; t < T; ++t)
+        for (int64_t l = offsets[(int64_t)t * B]; l < offsets[(int64_t)(t + 1) * B]; ++l)
+            if (indices[l] < 0 || indices[l] >= N[t]) return ORC_ERR_INDEX;
+    return ORC_OK;
+}
+
+static int64_t sum_dims(int32_t T, const int32_t *d, int64_t *col_off)
+{
+    int64_t s = 0;
+    for (int t = 0; t < T; ++t) {
+        col_off[t] = s;
+        s += (int64_t)d[3 * t] * d[3 * t + 1] * d[3 * t + 2];
+    }
+    return s;
+}
+
+static int max_work(int32_t T, const int32_t *d, const int32_t *R, int64_t *maxC, int64_t *maxD)
+{
+    *maxC = 1;
+    *maxD = 1;
+    for (int t = 0; t < T; ++t) {
+        int64_t c = (int64_t)d[3 * t] * d[3 * t + 1] * R[4 * t + 2];
+        int64_t e = (int64_t)d[3 * t] * d[3 * t + 1] * d[3 * t + 2];
+        if (c > *maxC) *maxC = c;
+        if (e > *maxD) *maxD = e;
+    }
+    return ORC_OK;
+}
+
+/* --------------------------------------------------------------- forward */
+
+/* Pooled forward with NO reuse: every index recomputes its row, rows are
+ * summed over the bag in CSR order (FlowTT 3.2: contraction, then pooling;
+ * TT-Rec abstract: EmbeddingBag).  out is fp64 [nsel][sum D]; bag_sel lists
+ * the bag ids b (0..B-1) to evaluate, or is NULL for all B bags. */
+int orc_forward(int32_t T, const int64_t *N, const int32_t *n, const int32_t *d, const int32_t *R,
+                const float *const *cores, const int64_t *indices, const int64_t *offsets,
+                int64_t B, int64_t nnz, const int64_t *bag_sel, int64_t nsel, double *out,
+                int32_t nthreads)
+{
+    int rc = check_tables(T, N, n, d, R);
+    if (rc) return rc;
+    rc = check_csr(T, N, indices, offsets, B, nnz);
+    if (rc) return rc;
+    int64_t *col_off = (int64_t *)malloc(sizeof(int64_t) * T);
+    if (!col_off) return ORC_ERR_NOMEM;
+    const int64_t SD = sum_dims(T, d, col_off);
+    int64_t maxC, maxD;
+    max_work(T, d, R, &maxC, &maxD);
+    const int64_t nb = bag_sel ? nsel : B;
+    for (int64_t s = 0; s < nb; ++s)
+        if (bag_sel && (bag_sel[s] < 0 || bag_sel[s] >= B)) {
+            free(col_off);
+            return ORC_ERR_ARG;
+        }
+    memset(out, 0, sizeof(double) * (size_t)(nb * SD));
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel reduction(| : failed)
+#endif
+    {
+        double *C = (double *)malloc(sizeof(double) * (size_t)maxC);
+        double *E = (double *)malloc(sizeof(double) * (size_t)maxD);
+        if (!C || !E) failed = 1;
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 16)
+#endif
+        for (int64_t s = 0; s < nb; ++s) {
+            if (!C || !E) continue;
+            const int64_t b = bag_sel ? bag_sel[s] : s;
+            for (int t = 0; t < T; ++t) {
+                const int32_t *nt = n + 3 * t, *dt = d + 3 * t, *Rt = R + 4 * t;
+                const int64_t Dt = (int64_t)dt[0] * dt[1] * dt[2];
+                double *acc = out + s * SD + col_off[t];
+                for (int64_t l = offsets[(int64_t)t * B + b]; l < offsets[(int64_t)t * B + b + 1]; ++l) {
+                    int64_t i1, i2, i3;
+                    decode3(indices[l], nt, &i1, &i2, &i3);
+                    prefix_c(cores[3 * t], cores[3 * t + 1], dt, Rt, i1, i2, C);
+                    suffix_e(C, cores[3 * t + 2], dt, Rt, i3, E);
+                    for (int64_t j = 0; j < Dt; ++j) acc[j] += E[j];
+                }
+            }
+        }
+        free(C);
+        free(E);
+    }
+    free(col_off);
+    return failed ? ORC_ERR_NOMEM : ORC_OK;
+}
+
+/* -------------------------------------------------------------- grouping */
+
+typedef struct {
+    int64_t row;
+    int64_t pos;
+} entry_t;
+
+static int cmp_entry(const void *a, const void *b)
+{
+    const entry_t *x = (const entry_t *)a, *y = (const entry_t *)b;
+    if (x->row != y->row) return x->row < y->row ? -1 : 1;
+    if (x->pos != y->pos) return x->pos < y->pos ? -1 : 1;
+    return 0;
+}
+
+/* Index grouping in the stage order of FlowTT section 4 (breakdown):
+ *  1. sort lookups by row within each table, ties by position (stable);
+ *  2. unique extraction: runs of equal row -> uniq_row, uniq_start, inv;
+ *  3. mixed-radix conversion of each unique row, prefix q = row div n3
+ *     (= i1*n2 + i2, the shared high-order digits of section 3.3);
+ *  4. run-length encoding of equal prefixes -> grp_prefix, grp_start.
+ * Arrays are concatenated over tables in table order; ids are global.
+ * Capacities: perm/inv nnz; uniq_row, grp_prefix nnz; uniq_start, grp_start
+ * nnz+1; tab_* T+1.  counts[0] = U (unique rows), counts[1] = G (groups). */
+int orc_grouping(int32_t T, const int64_t *N, const int32_t *n, const int64_t *indices,
+                 const int64_t *offsets, int64_t B, int64_t nnz, int32_t *perm,
+                 int32_t *uniq_row, int32_t *uniq_start, int32_t *inv, int32_t *grp_prefix,
+                 int32_t *grp_start, int32_t *tab_uniq_start, int32_t *tab_grp_start,
+                 int64_t *counts)
+{
+    if (T <= 0 || B < 0 || nnz < 0 || nnz > 0x7fffffffLL) return ORC_ERR_ARG;
+    for (int t = 0; t < T; ++t)
+        if (N[t] <= 0 || n[3 * t + 2] <= 0 || n[3 * t + 1] <= 0) return ORC_ERR_ARG;
+    int rc = check_csr(T, N, indices, offsets, B, nnz);
+    if (rc) return rc;
+    entry_t *e = (entry_t *)malloc(sizeof(entry_t) * (size_t)(nnz > 0 ? nnz : 1));
+    if (!e) return ORC_ERR_NOMEM;
+    for (int64_t l = 0; l < nnz; ++l) {
+        e[l].row = indices[l];
+        e[l].pos = l;
+    }
+    /* Step 1: per table segment (positions of table t are contiguous). */
+    for (int t = 0; t < T; ++t) {
+        int64_t lo = offsets[(int64_t)t * B], hi = offsets[(int64_t)(t + 1) * B];
+        if (hi > lo) qsort(e + lo, (size_t)(hi - lo), sizeof(entry_t), cmp_entry);
+    }
+    for (int64_t k = 0; k < nnz; ++k) perm[k] = (int32_t)e[k].pos;
+    /* Step 2: unique rows. */
+    int64_t U = 0;
+    for (int t = 0; t < T; ++t) {
+        int64_t lo = offsets[(int64_t)t * B], hi = offsets[(int64_t)(t + 1) * B];
+        tab_uniq_start[t] = (int32_t)U;
+        for (int64_t k = lo; k < hi; ++k) {
+            if (k == lo || e[k].row != e[k - 1].row) {
+                uniq_row[U] = (int32_t)e[k].row;
+                uniq_start[U] = (int32_t)k;
+                ++U;
+            }
+            inv[e[k].pos] = (int32_t)(U - 1);
+        }
+    }
+    tab_uniq_start[T] = (int32_t)U;
+    uniq_start[U] = (int32_t)nnz;
+    /* Steps 3-4: prefix of each unique row and run-length encoding. */
+    int64_t G = 0;
+    for (int t = 0; t < T; ++t) {
+        const int64_t n3 = n[3 * t + 2];
+        tab_grp_start[t] = (int32_t)G;
+        int64_t prev = -1;
+        for (int64_t u = tab_uniq_start[t]; u < tab_uniq_start[t + 1]; ++u) {
+            int64_t q = (int64_t)uniq_row[u] / n3;
+            if (u == tab_uniq_start[t] || q != prev) {
+                grp_prefix[G] = (int32_t)q;
+                grp_start[G] = (int32_t)u;
+                ++G;
+            }
+            prev = q;
+        }
+    }
+    tab_grp_start[T] = (int32_t)G;
+    grp_start[G] = (int32_t)U;
+    counts[0] = U;
+    counts[1] = G;
+    free(e);
+    return ORC_OK;
+}
+
+/* Grouped forward: the prefix intermediate C is computed once per group,
+ * each unique row once from its group's C, and bags are pooled in CSR order
+ * through inv (FlowTT 3.2/3.3: prefix-shared reuse).  Uses the same loops as
+ * the per-index path, so in exact arithmetic and in this fp64 build the two
+ * results are identical; reuse changes cost, not value (FlowTT section 4,
+ * prefix-reuse ablation).  out is fp64 [B][sum D]. */
+int orc_forward_grouped(int32_t T, const int64_t *N, const int32_t *n, const int32_t *d,
+                        const int32_t *R, const float *const *cores, const int64_t *indices,
+                        const int64_t *offsets, int64_t B, int64_t nnz, double *out)
+{
+    int rc = check_tables(T, N, n, d, R);
+    if (rc) return rc;
+    const int64_t cap = nnz > 0 ? nnz : 1;
+    int32_t *perm = (int32_t *)malloc(sizeof(int32_t) * cap);
+    int32_t *urow = (int32_t *)malloc(sizeof(int32_t) * cap);
+    int32_t *ustart = (int32_t *)malloc(sizeof(int32_t) * (cap + 1));
+    int32_t *inv = (int32_t *)malloc(sizeof(int32_t) * cap);
+    int32_t *gpre = (int32_t *)malloc(sizeof(int32_t) * cap);
+    int32_t *gstart = (int32_t *)malloc(sizeof(int32_t) * (cap + 1));
+    int32_t *tu = (int32_t *)malloc(sizeof(int32_t) * (T + 1));
+    int32_t *tg = (int32_t *)malloc(sizeof(int32_t) * (T + 1));
+    int64_t *col_off = (int64_t *)malloc(sizeof(int64_t) * T);
+    int64_t counts[2];
+    double *C = NULL, *Erows = NULL;
+    rc = ORC_ERR_NOMEM;
+    if (!perm || !urow || !ustart || !inv || !gpre || !gstart || !tu || !tg || !col_off) goto done;
+    rc = orc_grouping(T, N, n, indices, offsets, B, nnz, perm, urow, ustart, inv, gpre, gstart,
+                      tu, tg, counts);
+    if (rc) goto done;
+    {
+        int64_t maxC, maxD;
+        max_work(T, d, R, &maxC, &maxD);
+        const int64_t SD = sum_dims(T, d, col_off);
+        const int64_t U = counts[0];
+        rc = ORC_ERR_NOMEM;
+        C = (double *)malloc(sizeof(double) * (size_t)maxC);
+        Erows = (double *)malloc(sizeof(double) * (size_t)((U > 0 ? U : 1) * maxD));
+        if (!C || !Erows) goto done;
+        for (int t = 0; t < T; ++t) {
+            const int32_t *nt = n + 3 * t, *dt = d + 3 * t, *Rt = R + 4 * t;
+            for (int64_t g = tg[t]; g < tg[t + 1]; ++g) {
+                const int64_t q = gpre[g];
+                prefix_c(cores[3 * t], cores[3 * t + 1], dt, Rt, q / nt[1], q % nt[1], C);
+                for (int64_t u = gstart[g]; u < gstart[g + 1]; ++u)
+                    suffix_e(C, cores[3 * t + 2], dt, Rt, (int64_t)urow[u] % nt[2],
+                             Erows + u * maxD);
+            }
+        }
+        memset(out, 0, sizeof(double) * (size_t)(B * SD));
+        for (int t = 0; t < T; ++t) {
+            const int64_t Dt = (int64_t)d[3 * t] * d[3 * t + 1] * d[3 * t + 2];
+            for (int64_t b = 0; b < B; ++b) {
+                double *acc = out + b * SD + col_off[t];
+                for (int64_t l = offsets[(int64_t)t * B + b]; l < offsets[(int64_t)t * B + b + 1]; ++l) {
+                    const double *E = Erows + (int64_t)inv[l] * maxD;
+                    for (int64_t j = 0; j < Dt; ++j) acc[j] += E[j];
+                }
+            }
+        }
+        rc = ORC_OK;
+    }
+done:
+    free(perm); free(urow); free(ustart); free(inv); free(gpre); free(gstart);
+    free(tu); free(tg); free(col_off); free(C); free(Erows);
+    return rc;
+}
+
+/* -------------------------------------------------------------- backward */
+
+/* Gradients of L = sum(grad_out * out) with respect to every core (FlowTT
+ * 3.2: the backward reverses C = A.B, E = C.D, pooling).  Per index, with
+ * g = grad_out[b][table block] viewed as [d1*d2][d3] and C recomputed:
+ *   dG3[i3][r2][j3]    += sum_{m} C[m][r2] g[m][j3]
+ *   dC[m][r2]           = sum_{j3} g[m][j3] G3[i3][r2][j3]
+ *   dG1[i1][0][j1][r1] += sum_{j2,r2} dC[j1 j2][r2] G2[i2][r1][j2][r2]
+ *   dG2[i2][r1][j2][r2]+= sum_{j1} G1[i1][0][j1][r1] dC[j1 j2][r2]
+ * dG are fp64 arrays shaped like the cores, overwritten (untouched slices 0).
+ * sel (optional, [T*3]) restricts the work to one slice per (table, core):
+ * sel[3t+k] = slice index to compute, -1 = all slices, -2 = none; lookups
+ * touching no selected slice are skipped.  Tables run in parallel; each
+ * table's sums are sequential in CSR order. */
+int orc_backward(int32_t T, const int64_t *N, const int32_t *n, const int32_t *d, const int32_t *R,
+                 const float *const *cores, const int64_t *indices, const int64_t *offsets,
+                 int64_t B, int64_t nnz, const float *grad_out, const int64_t *sel,
+                 double *const *dG, int32_t nthreads)
+{
+    int rc = check_tables(T, N, n, d, R);
+    if (rc) return rc;
+    rc = check_csr(T, N, indices, offsets, B, nnz);
+    if (rc) return rc;
+    int64_t *col_off = (int64_t *)malloc(sizeof(int64_t) * T);
+    if (!col_off) return ORC_ERR_NOMEM;
+    const int64_t SD = sum_dims(T, d, col_off);
+    for (int t = 0; t < T; ++t)
+        for (int k = 0; k < 3; ++k) {
+            const int32_t *nt = n + 3 * t, *dt = d + 3 * t, *Rt = R + 4 * t;
+            size_t sz = (size_t)nt[k] * Rt[k] * dt[k] * Rt[k + 1];
+            memset(dG[3 * t + k], 0, sizeof(double) * sz);
+        }
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+#endif
+    for (int t = 0; t < T; ++t) {
+        const int32_t *nt = n + 3 * t, *dt = d + 3 * t, *Rt = R + 4 * t;
+        const int d1 = dt[0], d2 = dt[1], d3 = dt[2], R1 = Rt[1], R2 = Rt[2];
+        const int d12 = d1 * d2;
+        const float *G1 = cores[3 * t], *G2 = cores[3 * t + 1], *G3 = cores[3 * t + 2];
+        double *dG1 = dG[3 * t], *dG2 = dG[3 * t + 1], *dG3 = dG[3 * t + 2];
+        const int64_t s1 = sel ? sel[3 * t] : -1, s2 = sel ? sel[3 * t + 1] : -1,
+                      s3 = sel ? sel[3 * t + 2] : -1;
+        double *C = (double *)malloc(sizeof(double) * (size_t)d12 * R2);
+        double *dC = (double *)malloc(sizeof(double) * (size_t)d12 * R2);
+        if (!C || !dC) {
+            failed = 1;
+            free(C);
+            free(dC);
+            continue;
+        }
+        for (int64_t b = 0; b < B; ++b) {
+            const float *g = grad_out + b * SD + col_off[t];
+            for (int64_t l = offsets[(int64_t)t * B + b]; l < offsets[(int64_t)t * B + b + 1]; ++l) {
+                int64_t i1, i2, i3;
+                decode3(indices[l], nt, &i1, &i2, &i3);
+                const int w1 = (s1 == -1 || s1 == i1), w2 = (s2 == -1 || s2 == i2),
+                          w3 = (s3 == -1 || s3 == i3);
+                if (!w1 && !w2 && !w3) continue;
+                prefix_c(G1, G2, dt, Rt, i1, i2, C);
+                const float *g3 = G3 + i3 * (int64_t)R2 * d3;
+                if (w3) {
+                    double *o = dG3 + i3 * (int64_t)R2 * d3;
+                    for (int r2 = 0; r2 < R2; ++r2)
+                        for (int j3 = 0; j3 < d3; ++j3) {
+                            double acc = 0.0;
+                            for (int m = 0; m < d12; ++m)
+                                acc += C[m * R2 + r2] * (double)g[m * d3 + j3];
+                            o[r2 * d3 + j3] += acc;
+                        }
+                }
+                if (!w1 && !w2) continue;
+                for (int m = 0; m < d12; ++m)
+                    for (int r2 = 0; r2 < R2; ++r2) {
+                        double acc = 0.0;
+                        for (int j3 = 0; j3 < d3; ++j3)
+                            acc += (double)g[m * d3 + j3] * (double)g3[r2 * d3 + j3];
+                        dC[m * R2 + r2] = acc;
+                    }
+                const float *g1 = G1 + i1 * (int64_t)d1 * R1;
+                const float *g2 = G2 + i2 * (int64_t)R1 * d2 * R2;
+                if (w1) {
+                    double *o = dG1 + i1 * (int64_t)d1 * R1;
+                    for (int j1 = 0; j1 < d1; ++j1)
+                        for (int r1 = 0; r1 < R1; ++r1) {
+                            double acc = 0.0;
+                            for (int j2 = 0; j2 < d2; ++j2)
+                                for (int r2 = 0; r2 < R2; ++r2)
+                                    acc += dC[(j1 * d2 + j2) * R2 + r2] *
+                                           (double)g2[((int64_t)r1 * d2 + j2) * R2 + r2];
+                            o[j1 * R1 + r1] += acc;
+                        }
+                }
+                if (w2) {
+                    double *o = dG2 + i2 * (int64_t)R1 * d2 * R2;
+                    for (int r1 = 0; r1 < R1; ++r1)
+                        for (int j2 = 0; j2 < d2; ++j2)
+                            for (int r2 = 0; r2 < R2; ++r2) {
+                                double acc = 0.0;
+                                for (int j1 = 0; j1 < d1; ++j1)
+                                    acc += (double)g1[j1 * R1 + r1] * dC[(j1 * d2 + j2) * R2 + r2];
+                                o[((int64_t)r1 * d2 + j2) * R2 + r2] += acc;
+                            }
+                }
+            }
+        }
+        free(C);
+        free(dC);
+    }
+    free(col_off);
+    return failed ? ORC_ERR_NOMEM : ORC_OK;
+}
+
+/* Plain SGD step of the training configuration: delta = -lr * dG. */
+void orc_sgd_delta(const double *dG, int64_t count, double lr, double *delta)
+{
+    for (int64_t k = 0; k < count; ++k) delta[k] = -lr * dG[k];
+}
+
+int orc_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
