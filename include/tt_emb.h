@@ -1,0 +1,179 @@
+/*
+ * tt_emb.h -- C ABI of the MI355X (gfx950) TT-EmbeddingBag library, libtt_emb.so.
+ *
+ * The operator is an EmbeddingBag with sum pooling whose rows are rebuilt from
+ * tensor-train cores ("TT-Rec: Tensor Train Compression for Deep Learning
+ * Recommendation Models", abstract: TT-EmbeddingBag), evaluated the way the
+ * FlowTT page ("FlowTT: Exploiting Computation Flow Reuse in Irregular
+ * Tensor-Train Embedding") describes: lookups are grouped by the shared
+ * high-order mixed-radix digits of their row (section 3.3), each group's prefix
+ * intermediate C = G1[i1].G2[i2] is computed once and kept on chip, every row
+ * of the group is E = C.G3[i3], rows are pooled per bag (section 3.2), and the
+ * work runs on persistent blocks with chunk stealing and L2 checkpoints of
+ * prefix intermediates (section 3.4).  The backward reverses the contraction
+ * (section 3.2).
+ *
+ * Conventions (the pages leave these open; the choices are the plainest ones):
+ *  - table t has N_t rows factored as n = (n1, n2, n3), n1*n2*n3 >= N_t, and
+ *    D_t = d1*d2*d3 columns; TT ranks R = (1, R1, R2, 1);
+ *  - row index digits are big-endian: i = (i1*n2 + i2)*n3 + i3; the prefix of
+ *    a row is (i1, i2), i.e. q = i div n3;
+ *  - core k of table t is fp32, row-major [n_k][R_{k-1}][d_k][R_k];
+ *  - output column j = (j1*d2 + j2)*d3 + j3;
+ *  - indices and offsets are int64; offsets are table-major CSR with T*B+1
+ *    entries (offsets[0] = 0, non-decreasing, offsets[T*B] = nnz); bag (t, b)
+ *    is indices[offsets[t*B+b] .. offsets[t*B+b+1]); an empty bag pools to 0;
+ *  - out is fp32 [B][sum_t D_t], bag-major, tables concatenated in order;
+ *  - valid rows are 0 <= i < N_t; anything else is an index error.
+ *
+ * Ownership and ordering: the caller owns every device buffer (cores, indices,
+ * offsets, out, gradients, workspace).  The handle owns host metadata and a
+ * small device copy of the table descriptors made at create time.  Forward,
+ * backward and the update never allocate memory and never synchronise the
+ * host: all work is enqueued on the given stream (a hipStream_t passed as
+ * void*, NULL = the default stream).  Concurrent calls on one handle need
+ * distinct workspaces.
+ *
+ * Errors: argument errors the host can see are returned synchronously and
+ * nothing is enqueued.  Errors only the device can see (an index out of range,
+ * malformed offsets) set a flag in the workspace; tt_emb_poll_error reports
+ * it.  After such an error the outputs are unspecified but every kernel stays
+ * in bounds.  No C++ exception crosses this interface.
+ */
+#ifndef TT_EMB_H
+#define TT_EMB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tt_emb *tt_emb_t;
+
+enum {
+    TT_EMB_OK = 0,
+    TT_EMB_ERR_ARG = -1,         /* bad argument (null pointer, bad size or shape) */
+    TT_EMB_ERR_INDEX = -2,       /* an index outside [0, N_t) (device-detected) */
+    TT_EMB_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+    TT_EMB_ERR_UNSUPPORTED = -4, /* shape outside what this build supports */
+    TT_EMB_ERR_HIP = -5,         /* a HIP runtime call failed */
+    TT_EMB_ERR_NOMEM = -6,       /* host or create-time device allocation failed */
+    TT_EMB_ERR_OFFSETS = -7      /* malformed offsets (device-detected) */
+};
+
+/* Scheduling of the persistent contraction kernel (FlowTT section 3.4 and the
+ * scheduling ablation of section 4). */
+enum {
+    TT_EMB_SCHED_DEFAULT = 0,  /* = STEAL_L2 */
+    TT_EMB_SCHED_STATIC = 1,   /* each block runs only its static range of chunks */
+    TT_EMB_SCHED_STEAL = 2,    /* static range first, then steal chunks; no checkpoints */
+    TT_EMB_SCHED_STEAL_L2 = 3  /* stealing plus L2 checkpoints of split prefix tiles */
+};
+
+/* Reuse granularity (FlowTT section 4, prefix reuse vs. exact deduplication). */
+enum {
+    TT_EMB_GROUP_DEFAULT = 0,    /* = PREFIX */
+    TT_EMB_GROUP_PREFIX = 1,     /* one prefix intermediate per (table, i1, i2) */
+    TT_EMB_GROUP_UNIQUE_ONLY = 2 /* one prefix intermediate per unique row */
+};
+
+/* Options; a zeroed struct (or NULL) selects the defaults. */
+typedef struct {
+    int32_t sched_mode;    /* TT_EMB_SCHED_* */
+    int32_t group_mode;    /* TT_EMB_GROUP_* */
+    int32_t chunk_rows;    /* max rows per forward work chunk, 1..4096 (0 = 32) */
+    int32_t num_blocks;    /* persistent grid size (0 = 2 per compute unit) */
+    int32_t check_indices; /* 0 = on (default), 1 = on, -1 = off (caller guarantees) */
+    int32_t force_generic; /* 1 = use the plain (non-MFMA) contraction kernels (testing) */
+    int32_t reserved[2];
+} tt_emb_options;
+
+/* tt_emb_forward / tt_emb_backward flags. */
+#define TT_EMB_REUSE_GROUPING 1u /* ws already holds the grouping of these exact
+                                    (indices, offsets, B, nnz); skip rebuilding it */
+
+/* Device pointers to the grouping arrays held in a workspace (for tests and
+ * tools), all int32, ids global over tables in table order:
+ *  perm[nnz]          lookup positions sorted by (table, row, position);
+ *  uniq_row[U]        row of each unique (table, row);
+ *  uniq_start[U+1]    start of each unique row's run in perm;
+ *  inv[nnz]           position -> unique id;
+ *  grp_prefix[G]      prefix q = row div n3 of each group;
+ *  grp_start[G+1]     first unique id of each group;
+ *  tab_uniq_start[T+1], tab_grp_start[T+1]  per-table starts. */
+typedef struct {
+    int64_t nnz, num_unique, num_groups;
+    const int32_t *perm, *uniq_row, *uniq_start, *inv, *grp_prefix, *grp_start;
+    const int32_t *tab_uniq_start, *tab_grp_start;
+    int64_t num_units, num_tiles, num_chunks, num_split_tiles;
+    /* scheduling statistics of the last forward contraction */
+    int64_t num_steals, num_ckpt_hits, num_ckpt_misses;
+} tt_emb_grouping;
+
+/* Create a handle for T tables (FlowTT section 2.4 problem statement: a TT
+ * gather over sequential core contractions).  num_rows[T] = N_t; n[3T], d[3T]
+ * = row and column factors; R[4T] = ranks with R0 = R3 = 1.  All are host
+ * arrays, copied.  Returns TT_EMB_ERR_ARG for inconsistent shapes and
+ * TT_EMB_ERR_UNSUPPORTED beyond this build's limits (T <= 64, sum N_t < 2^31,
+ * ranks <= 256, D_t <= 1024).  *out receives the handle. */
+int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const int32_t *d,
+                  const int32_t *R, const tt_emb_options *opt, tt_emb_t *out);
+
+/* Release a handle (NULL is accepted). */
+int tt_emb_destroy(tt_emb_t h);
+
+/* Bytes of device workspace that forward + backward need for B bags per table
+ * and nnz lookups (an upper bound that does not depend on the index values). */
+int tt_emb_workspace_size(tt_emb_t h, int64_t B, int64_t nnz, size_t *bytes);
+
+/* Build the grouping of (indices, offsets) into ws: validation and key build,
+ * stable radix sort by (table, row), unique extraction, prefix run-length
+ * encoding and the work list (FlowTT section 4, grouping breakdown). */
+int tt_emb_group(tt_emb_t h, const int64_t *indices, const int64_t *offsets, int64_t B,
+                 int64_t nnz, void *ws, size_t ws_bytes, void *stream);
+
+/* Pooled forward (FlowTT section 3.2: C = A.B, E = C.D, then pooling).
+ * cores: HOST array of 3T device pointers (G1_0, G2_0, G3_0, G1_1, ...);
+ * indices [nnz], offsets [T*B+1] int64 device; out fp32 [B][sum D] device,
+ * fully overwritten.  Builds the grouping first unless
+ * flags & TT_EMB_REUSE_GROUPING. */
+int tt_emb_forward(tt_emb_t h, const float *const *cores, const int64_t *indices,
+                   const int64_t *offsets, int64_t B, int64_t nnz, float *out, void *ws,
+                   size_t ws_bytes, uint32_t flags, void *stream);
+
+/* Backward of out = forward(cores) for the loss sum(grad_out * out) (FlowTT
+ * section 3.2: the backward reverses the forward).  grad_out fp32 [B][sum D]
+ * device; core_grads: HOST array of 3T device pointers, each shaped like its
+ * core and fully OVERWRITTEN (slices no lookup touches become 0).  The core
+ * gradients are reduced in a fixed order with no floating-point atomics, so
+ * results are bit-reproducible run to run. */
+int tt_emb_backward(tt_emb_t h, const float *grad_out, const float *const *cores,
+                    const int64_t *indices, const int64_t *offsets, int64_t B, int64_t nnz,
+                    float *const *core_grads, void *ws, size_t ws_bytes, uint32_t flags,
+                    void *stream);
+
+/* In-place SGD step G_k <- G_k - lr * dG_k on every core (the training step
+ * of the benchmark workloads).  Both arrays are HOST arrays of 3T device
+ * pointers. */
+int tt_emb_sgd_update(tt_emb_t h, float *const *cores, const float *const *core_grads,
+                      float lr, void *stream);
+
+/* Synchronise the stream, then fill *view with device pointers into ws and
+ * the counts it holds (tests and tools only). */
+int tt_emb_grouping_view(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B, int64_t nnz,
+                         void *stream, tt_emb_grouping *view);
+
+/* Synchronise the stream and report a device-detected error recorded in ws
+ * since the last grouping (TT_EMB_OK, TT_EMB_ERR_INDEX or TT_EMB_ERR_OFFSETS). */
+int tt_emb_poll_error(tt_emb_t h, const void *ws, void *stream);
+
+/* Static text for a status code. */
+const char *tt_emb_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TT_EMB_H */

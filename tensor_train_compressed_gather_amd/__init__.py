@@ -1,0 +1,271 @@
+"""MI355X (gfx950) TT-EmbeddingBag with prefix-shared reuse.
+
+Python binding of ``libtt_emb.so`` (C ABI in ``include/tt_emb.h``).  This
+module only marshals arguments: torch supplies device memory and the current
+HIP stream; every step of the path runs in the library's HIP kernels.  There
+is no CPU fallback -- if the library is missing, loading it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtt_emb.so")
+
+TT_EMB_OK = 0
+TT_EMB_ERR_ARG = -1
+TT_EMB_ERR_INDEX = -2
+TT_EMB_ERR_WORKSPACE = -3
+TT_EMB_ERR_UNSUPPORTED = -4
+TT_EMB_ERR_HIP = -5
+TT_EMB_ERR_NOMEM = -6
+TT_EMB_ERR_OFFSETS = -7
+
+TT_EMB_SCHED_DEFAULT, TT_EMB_SCHED_STATIC, TT_EMB_SCHED_STEAL, TT_EMB_SCHED_STEAL_L2 = 0, 1, 2, 3
+TT_EMB_GROUP_DEFAULT, TT_EMB_GROUP_PREFIX, TT_EMB_GROUP_UNIQUE_ONLY = 0, 1, 2
+TT_EMB_REUSE_GROUPING = 1
+
+EXPORTED = (
+    "tt_emb_create", "tt_emb_destroy", "tt_emb_workspace_size", "tt_emb_group", "tt_emb_forward",
+    "tt_emb_backward", "tt_emb_sgd_update", "tt_emb_grouping_view", "tt_emb_poll_error",
+    "tt_emb_status_string",
+)
+
+
+class tt_emb_options(C.Structure):
+    _fields_ = [("sched_mode", C.c_int32), ("group_mode", C.c_int32), ("chunk_rows", C.c_int32),
+                ("num_blocks", C.c_int32), ("check_indices", C.c_int32), ("force_generic", C.c_int32),
+                ("reserved", C.c_int32 * 2)]
+
+
+class tt_emb_grouping(C.Structure):
+    _fields_ = [("nnz", C.c_int64), ("num_unique", C.c_int64), ("num_groups", C.c_int64),
+                ("perm", C.c_void_p), ("uniq_row", C.c_void_p), ("uniq_start", C.c_void_p),
+                ("inv", C.c_void_p), ("grp_prefix", C.c_void_p), ("grp_start", C.c_void_p),
+                ("tab_uniq_start", C.c_void_p), ("tab_grp_start", C.c_void_p),
+                ("num_units", C.c_int64), ("num_tiles", C.c_int64), ("num_chunks", C.c_int64),
+                ("num_split_tiles", C.c_int64), ("num_steals", C.c_int64),
+                ("num_ckpt_hits", C.c_int64), ("num_ckpt_misses", C.c_int64)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load libtt_emb.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                                  "or python -m tensor_train_compressed_gather_amd.build")
+            L = C.CDLL(LIB_PATH)
+            p, i32, i64, u32 = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32
+            L.tt_emb_create.argtypes = [i32, p, p, p, p, C.POINTER(tt_emb_options), C.POINTER(p)]
+            L.tt_emb_destroy.argtypes = [p]
+            L.tt_emb_workspace_size.argtypes = [p, i64, i64, C.POINTER(C.c_size_t)]
+            L.tt_emb_group.argtypes = [p, p, p, i64, i64, p, C.c_size_t, p]
+            L.tt_emb_forward.argtypes = [p, p, p, p, i64, i64, p, p, C.c_size_t, u32, p]
+            L.tt_emb_backward.argtypes = [p, p, p, p, p, i64, i64, p, p, C.c_size_t, u32, p]
+            L.tt_emb_sgd_update.argtypes = [p, p, p, C.c_float, p]
+            L.tt_emb_grouping_view.argtypes = [p, p, C.c_size_t, i64, i64, p, C.POINTER(tt_emb_grouping)]
+            L.tt_emb_poll_error.argtypes = [p, p, p]
+            L.tt_emb_status_string.argtypes = [C.c_int]
+            L.tt_emb_status_string.restype = C.c_char_p
+            for name in EXPORTED:
+                if name != "tt_emb_status_string":
+                    getattr(L, name).restype = C.c_int
+            _lib = L
+    return _lib
+
+
+class TTEmbError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {tt_emb_status_string(status)} ({status})")
+
+
+def _check(rc: int, where: str):
+    if rc != TT_EMB_OK:
+        raise TTEmbError(rc, where)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _ptr_array(tensors):
+    arr = (C.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    return arr
+
+
+def tt_emb_status_string(status: int) -> str:
+    return lib().tt_emb_status_string(int(status)).decode()
+
+
+def tt_emb_create(num_rows, n, d, R, options: tt_emb_options | None = None):
+    """num_rows [T], n [T][3], d [T][3], R [T][4] (host sequences) -> handle."""
+    import numpy as np
+
+    N = np.ascontiguousarray(np.asarray(num_rows, dtype=np.int64).reshape(-1))
+    nn = np.ascontiguousarray(np.asarray(n, dtype=np.int32).reshape(-1))
+    dd = np.ascontiguousarray(np.asarray(d, dtype=np.int32).reshape(-1))
+    RR = np.ascontiguousarray(np.asarray(R, dtype=np.int32).reshape(-1))
+    T = N.shape[0]
+    if nn.shape[0] != 3 * T or dd.shape[0] != 3 * T or RR.shape[0] != 4 * T:
+        raise ValueError("shape arrays must have 3T, 3T and 4T entries")
+    h = C.c_void_p()
+    rc = lib().tt_emb_create(T, N.ctypes.data, nn.ctypes.data, dd.ctypes.data, RR.ctypes.data,
+                             C.byref(options) if options is not None else None, C.byref(h))
+    _check(rc, "tt_emb_create")
+    return h
+
+
+def tt_emb_destroy(h):
+    _check(lib().tt_emb_destroy(h), "tt_emb_destroy")
+
+
+def tt_emb_workspace_size(h, B: int, nnz: int) -> int:
+    out = C.c_size_t()
+    _check(lib().tt_emb_workspace_size(h, int(B), int(nnz), C.byref(out)), "tt_emb_workspace_size")
+    return int(out.value)
+
+
+def tt_emb_group(h, indices, offsets, B: int, ws, stream=None):
+    rc = lib().tt_emb_group(h, _ptr(indices), _ptr(offsets), int(B), int(indices.numel()), _ptr(ws),
+                            ws.numel(), _stream(stream))
+    _check(rc, "tt_emb_group")
+
+
+def tt_emb_forward(h, cores, indices, offsets, B: int, out, ws, flags: int = 0, stream=None):
+    rc = lib().tt_emb_forward(h, _ptr_array(cores), _ptr(indices), _ptr(offsets), int(B),
+                              int(indices.numel()), _ptr(out), _ptr(ws), ws.numel(), int(flags),
+                              _stream(stream))
+    _check(rc, "tt_emb_forward")
+
+
+def tt_emb_backward(h, grad_out, cores, indices, offsets, B: int, core_grads, ws, flags: int = 0,
+                    stream=None):
+    rc = lib().tt_emb_backward(h, _ptr(grad_out), _ptr_array(cores), _ptr(indices), _ptr(offsets),
+                               int(B), int(indices.numel()), _ptr_array(core_grads), _ptr(ws),
+                               ws.numel(), int(flags), _stream(stream))
+    _check(rc, "tt_emb_backward")
+
+
+def tt_emb_sgd_update(h, cores, core_grads, lr: float, stream=None):
+    rc = lib().tt_emb_sgd_update(h, _ptr_array(cores), _ptr_array(core_grads), float(lr), _stream(stream))
+    _check(rc, "tt_emb_sgd_update")
+
+
+def tt_emb_poll_error(h, ws, stream=None) -> int:
+    """Synchronises the stream; returns the device-side status (0 = ok)."""
+    return int(lib().tt_emb_poll_error(h, _ptr(ws), _stream(stream)))
+
+
+def tt_emb_grouping_view(h, ws, B: int, nnz: int, T: int, stream=None) -> dict:
+    """Grouping arrays held in ws, as int32 torch views into ws, plus counts."""
+    import torch
+
+    v = tt_emb_grouping()
+    rc = lib().tt_emb_grouping_view(h, _ptr(ws), ws.numel(), int(B), int(nnz), _stream(stream), C.byref(v))
+    _check(rc, "tt_emb_grouping_view")
+    base = ws.data_ptr()
+    i32 = ws.view(torch.int32) if ws.numel() % 4 == 0 else None
+
+    def arr(ptr, count):
+        off = (ptr - base)
+        assert off % 4 == 0
+        return i32[off // 4: off // 4 + int(count)]
+
+    U, G = v.num_unique, v.num_groups
+    return {
+        "perm": arr(v.perm, nnz), "uniq_row": arr(v.uniq_row, U), "uniq_start": arr(v.uniq_start, U + 1),
+        "inv": arr(v.inv, nnz), "grp_prefix": arr(v.grp_prefix, G), "grp_start": arr(v.grp_start, G + 1),
+        "tab_uniq_start": arr(v.tab_uniq_start, T + 1), "tab_grp_start": arr(v.tab_grp_start, T + 1),
+        "counts": {k: int(getattr(v, k)) for k in ("num_unique", "num_groups", "num_units", "num_tiles",
+                                                    "num_chunks", "num_split_tiles", "num_steals",
+                                                    "num_ckpt_hits", "num_ckpt_misses")},
+    }
+
+
+class TTEmbeddingBag:
+    """Owns a handle and a workspace for one table set (marshalling only).
+
+    ``cores`` is the list of 3T fp32 device tensors shaped
+    [n_k][R_{k-1}][d_k][R_k]; indices/offsets are int64 device tensors in
+    table-major CSR (T*B+1 offsets)."""
+
+    def __init__(self, tables, device="cuda", options: tt_emb_options | None = None):
+        self.tables = list(tables)
+        self.T = len(self.tables)
+        self.handle = tt_emb_create([t.N for t in self.tables], [t.n for t in self.tables],
+                                    [t.d for t in self.tables], [t.R for t in self.tables], options)
+        self.device = device
+        self.sum_D = sum(int(t.d[0] * t.d[1] * t.d[2]) for t in self.tables)
+        self._ws = None
+        self._ws_key = None
+
+    def workspace(self, B: int, nnz: int):
+        import torch
+
+        key = (int(B), int(nnz))
+        if self._ws_key != key:
+            need = tt_emb_workspace_size(self.handle, B, nnz)
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = None
+                self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            self._ws_key = key
+        return self._ws
+
+    def forward(self, cores, indices, offsets, B: int, out=None, flags: int = 0, stream=None):
+        import torch
+
+        if out is None:
+            out = torch.empty((B, self.sum_D), dtype=torch.float32, device=self.device)
+        ws = self.workspace(B, indices.numel())
+        tt_emb_forward(self.handle, cores, indices, offsets, B, out, ws, flags, stream)
+        return out
+
+    def backward(self, grad_out, cores, indices, offsets, B: int, core_grads=None, flags: int = 0,
+                 stream=None):
+        import torch
+
+        if core_grads is None:
+            core_grads = [torch.empty_like(c) for c in cores]
+        ws = self.workspace(B, indices.numel())
+        tt_emb_backward(self.handle, grad_out, cores, indices, offsets, B, core_grads, ws, flags, stream)
+        return core_grads
+
+    def sgd_update(self, cores, core_grads, lr: float, stream=None):
+        tt_emb_sgd_update(self.handle, cores, core_grads, lr, stream)
+
+    def poll_error(self, stream=None) -> int:
+        return tt_emb_poll_error(self.handle, self._ws, stream)
+
+    def grouping(self, B: int, nnz: int, stream=None) -> dict:
+        return tt_emb_grouping_view(self.handle, self._ws, B, nnz, self.T, stream)
+
+    def close(self):
+        if self.handle is not None:
+            tt_emb_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,478 @@
+// api.hip -- host side of the C ABI declared in include/tt_emb.h: argument
+// checks, the workspace plan, and stream-ordered launch sequencing.
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "../../include/tt_emb.h"
+#include "internal.h"
+
+using namespace ttemb;
+
+struct tt_emb {
+    int32_t T;
+    std::vector<TableDesc> tabs;
+    TableDesc *dtab = nullptr;
+    int device = 0;
+    int sched_mode, group_mode, chunk_rows, num_blocks, check_indices, force_generic;
+    bool any_generic;
+    int key_bits, key2_bits, key3_bits;
+    int Dmax, Dpmax, R2max, sumD;
+    int sum_n[3];
+    int64_t max_d1R1, max_R2d3, max_Dp;
+};
+
+namespace {
+
+int bits_for(uint64_t max_value)
+{
+    int b = 0;
+    while (b < 63 && (max_value >> b) != 0) ++b;
+    return b;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+int sort_passes(int64_t n, int bits) { return (n <= 0 || bits <= 0) ? 0 : (bits + 7) / 8; }
+
+// Carve the workspace.  With base == nullptr only the size is computed.
+size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan *p)
+{
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char * {
+        char *r = base ? base + off : nullptr;
+        off += align_up(bytes > 0 ? bytes : 1);
+        return r;
+    };
+    const int64_t n = nnz > 0 ? nnz : 1;
+    const int T = h->T;
+    Ws w{};
+    w.ctrl = (int32_t *)take(sizeof(int32_t) * CTRL_N);
+    w.keys0 = (uint32_t *)take(4 * n);
+    w.keys1 = (uint32_t *)take(4 * n);
+    w.vals0 = (int32_t *)take(4 * n);
+    w.vals1 = (int32_t *)take(4 * n);
+    w.uvals0 = (int32_t *)take(4 * n);
+    w.uvals1 = (int32_t *)take(4 * n);
+    const int64_t nblk = (n + kSortTile - 1) / kSortTile;
+    w.hist = (uint32_t *)take(4 * 256 * nblk);
+    w.part = (uint64_t *)take(8 * (kScanBlocks + 1));
+    w.tstart = (int32_t *)take(4 * (T + 1));
+    w.inv = (int32_t *)take(4 * n);
+    w.ukey = (uint32_t *)take(4 * n);
+    w.uniq_row = (int32_t *)take(4 * n);
+    w.uniq_start = (int32_t *)take(4 * (n + 1));
+    w.grp_prefix = (int32_t *)take(4 * n);
+    w.grp_start = (int32_t *)take(4 * (n + 1));
+    w.tab_uniq_start = (int32_t *)take(4 * (T + 1));
+    w.tab_grp_start = (int32_t *)take(4 * (T + 1));
+    w.ebase = (int64_t *)take(8 * T);
+    w.p3base = (int64_t *)take(8 * T);
+    w.g1base = (int64_t *)take(8 * T);
+    if (h->group_mode == TT_EMB_GROUP_UNIQUE_ONLY) {
+        w.unit_prefix = (int32_t *)take(4 * n);
+        w.unit_start = (int32_t *)take(4 * (n + 1));
+        w.tab_unit_start = (int32_t *)take(4 * (T + 1));
+    } else {
+        w.unit_prefix = w.grp_prefix;
+        w.unit_start = w.grp_start;
+        w.tab_unit_start = w.tab_grp_start;
+    }
+    w.run_start = (int32_t *)take(4 * (n + 1));
+    w.run_tile_start = (int32_t *)take(4 * (n + 1));
+    w.tile_ubeg = (int32_t *)take(4 * n);
+    w.tile_nu = (int32_t *)take(4 * n);
+    w.tile_rows = (int32_t *)take(4 * n);
+    w.tile_slot = (int32_t *)take(4 * n);
+    w.chunk_tile = (int32_t *)take(4 * (2 * n + 1));
+    w.chunk_rbeg = (int32_t *)take(4 * (2 * n + 1));
+    w.chunk_rend = (int32_t *)take(4 * (2 * n + 1));
+    w.heads = (int32_t *)take(4 * (size_t)h->num_blocks);
+    w.flags = (int32_t *)take(4 * (size_t)kMaxCkptSlots);
+    w.ckpt = (float *)take(4 * (size_t)kMaxCkptSlots * (4 * (16 * 68 + 16)));
+    // bounds on unique rows / units per table that do not depend on values
+    int64_t e_elems = 0, p3_elems = 0, g1_elems = 0;
+    for (int t = 0; t < T; ++t) {
+        const TableDesc &d = h->tabs[t];
+        const int64_t urows = d.N < n ? d.N : n;
+        const int64_t pre = (int64_t)d.n1 * d.n2;
+        const int64_t units = h->group_mode == TT_EMB_GROUP_UNIQUE_ONLY ? urows : (pre < n ? pre : n);
+        e_elems += urows * d.Dp;
+        p3_elems += urows * (int64_t)d.R2 * d.d3;
+        g1_elems += units * (int64_t)d.d1 * d.R1;
+    }
+    if (e_elems > n * h->max_Dp) e_elems = n * h->max_Dp;
+    if (p3_elems > n * h->max_R2d3) p3_elems = n * h->max_R2d3;
+    if (g1_elems > n * h->max_d1R1) g1_elems = n * h->max_d1R1;
+    const int64_t pieces = n + n / kGuPiece + 1;
+    const int64_t piece_elems = pieces * h->Dmax;
+    w.E = (float *)take(4 * e_elems);
+    w.bag_of = (int32_t *)take(4 * n);
+    w.piece_u = (int32_t *)take(4 * pieces);
+    w.piece_k = (int32_t *)take(4 * pieces);
+    w.u_piece_start = (int32_t *)take(4 * (n + 1));
+    w.P3 = (float *)take(4 * (p3_elems > piece_elems ? p3_elems : piece_elems));
+    w.piece_sum = w.P3;
+    w.G1P = (float *)take(4 * g1_elems);
+    // buffers where the sorts end
+    const int fm = sort_passes(nnz, h->key_bits) & 1;
+    const int fu = sort_passes(nnz, h->key2_bits) & 1;
+    w.skeys = fm ? w.keys1 : w.keys0;
+    w.perm = fm ? w.vals1 : w.vals0;
+    w.ukey2 = fu ? w.keys1 : w.keys0;
+    w.uorder = fu ? w.uvals1 : w.uvals0;
+    w.u3order = fm ? w.vals0 : w.vals1;
+    w.uvals_free = fu ? w.uvals0 : w.uvals1;
+    w.key3 = nullptr;
+    if (p) {
+        p->T = T;
+        p->B = B;
+        p->nnz = nnz;
+        p->num_blocks = h->num_blocks;
+        p->sched_mode = h->sched_mode;
+        p->group_mode = h->group_mode;
+        p->chunk_rows = h->chunk_rows;
+        p->check_indices = h->check_indices;
+        p->force_generic = h->force_generic;
+        p->any_generic = h->any_generic;
+        p->key_bits = h->key_bits;
+        p->key2_bits = h->key2_bits;
+        p->key3_bits = h->key3_bits;
+        p->Dmax = h->Dmax;
+        p->R2max = h->R2max;
+        p->sumD = h->sumD;
+        for (int k = 0; k < 3; ++k) p->sum_n[k] = h->sum_n[k];
+        p->dtab = h->dtab;
+        p->ws = w;
+    }
+    return off;
+}
+
+bool bad_ptr(const void *ptr) { return ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
+
+int check_call(const tt_emb *h, int64_t B, int64_t nnz, const int64_t *indices, const int64_t *offsets,
+               void *ws, size_t ws_bytes, Plan *p)
+{
+    if (!h || B < 0 || nnz < 0 || nnz >= (int64_t)0x7fffffff) return TT_EMB_ERR_ARG;
+    if ((int64_t)h->T * B >= (int64_t)0x7fffffff) return TT_EMB_ERR_ARG;
+    if (!offsets) return TT_EMB_ERR_ARG;
+    if (nnz > 0 && !indices) return TT_EMB_ERR_ARG;
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return TT_EMB_ERR_WORKSPACE;
+    const size_t need = plan_workspace(h, B, nnz, nullptr, nullptr);
+    if (ws_bytes < need) return TT_EMB_ERR_WORKSPACE;
+    plan_workspace(h, B, nnz, static_cast<char *>(ws), p);
+    return TT_EMB_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TT_EMB_OK : TT_EMB_ERR_HIP; }
+
+int set_device(const tt_emb *h)
+{
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return TT_EMB_ERR_HIP;
+    if (cur != h->device && hipSetDevice(h->device) != hipSuccess) return TT_EMB_ERR_HIP;
+    return TT_EMB_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const int32_t *d, const int32_t *R,
+                  const tt_emb_options *opt, tt_emb_t *out)
+{
+    try {
+        if (!out) return TT_EMB_ERR_ARG;
+        *out = nullptr;
+        if (T <= 0 || !num_rows || !n || !d || !R) return TT_EMB_ERR_ARG;
+        if (T > kMaxTables) return TT_EMB_ERR_UNSUPPORTED;
+        tt_emb_options o{};
+        if (opt) o = *opt;
+        if (o.sched_mode < 0 || o.sched_mode > 3 || o.group_mode < 0 || o.group_mode > 2) return TT_EMB_ERR_ARG;
+        if (o.chunk_rows < 0 || o.chunk_rows > 4096 || o.num_blocks < 0) return TT_EMB_ERR_ARG;
+        tt_emb *h = new (std::nothrow) tt_emb();
+        if (!h) return TT_EMB_ERR_NOMEM;
+        h->T = T;
+        h->sched_mode = o.sched_mode == 0 ? TT_EMB_SCHED_STEAL_L2 : o.sched_mode;
+        h->group_mode = o.group_mode == 0 ? TT_EMB_GROUP_PREFIX : o.group_mode;
+        h->chunk_rows = o.chunk_rows == 0 ? 32 : o.chunk_rows;
+        h->check_indices = o.check_indices >= 0 ? 1 : 0;
+        h->force_generic = o.force_generic ? 1 : 0;
+        uint64_t key = 0, b1 = 0, b2 = 0, b3 = 0;
+        int col = 0;
+        h->any_generic = false;
+        h->Dmax = h->Dpmax = h->R2max = 0;
+        h->max_d1R1 = h->max_R2d3 = h->max_Dp = 1;
+        int rc = TT_EMB_OK;
+        for (int t = 0; t < T && rc == TT_EMB_OK; ++t) {
+            const int32_t *nt = n + 3 * t, *dt = d + 3 * t, *Rt = R + 4 * t;
+            TableDesc td{};
+            td.N = num_rows[t];
+            td.n1 = nt[0];
+            td.n2 = nt[1];
+            td.n3 = nt[2];
+            td.d1 = dt[0];
+            td.d2 = dt[1];
+            td.d3 = dt[2];
+            td.R1 = Rt[1];
+            td.R2 = Rt[2];
+            if (td.N <= 0 || td.n1 <= 0 || td.n2 <= 0 || td.n3 <= 0 || td.d1 <= 0 || td.d2 <= 0 || td.d3 <= 0 ||
+                Rt[0] != 1 || Rt[3] != 1 || td.R1 <= 0 || td.R2 <= 0) {
+                rc = TT_EMB_ERR_ARG;
+                break;
+            }
+            if ((int64_t)td.n1 * td.n2 * td.n3 < td.N) {
+                rc = TT_EMB_ERR_ARG;
+                break;
+            }
+            const int64_t D = (int64_t)td.d1 * td.d2 * td.d3;
+            if (D > 1024 || td.R1 > 256 || td.R2 > 256 || (int64_t)td.d1 * td.d2 * td.R2 > 4096 ||
+                (int64_t)td.R1 * td.d2 * td.R2 > 16384 || (int64_t)td.n1 * td.n2 >= (int64_t)0x7fffffff) {
+                rc = TT_EMB_ERR_UNSUPPORTED;
+                break;
+            }
+            td.D = (int32_t)D;
+            td.Dp = (int32_t)((D + 3) & ~int64_t(3));
+            td.col_off = col;
+            col += td.D;
+            td.key_base = (uint32_t)key;
+            key += (uint64_t)td.N;
+            td.i1_base = (uint32_t)b1;
+            b1 += (uint64_t)td.n1;
+            td.i2_base = (uint32_t)b2;
+            b2 += (uint64_t)td.n2;
+            td.i3_base = (uint32_t)b3;
+            b3 += (uint64_t)td.n3;
+            int cls = -1;
+            if (td.R1 == td.R2 && td.d1 <= 4 && td.d2 <= 4 && td.d3 <= 16) {
+                if (td.R1 == 8) cls = 0;
+                else if (td.R1 == 16) cls = 1;
+                else if (td.R1 == 32) cls = 2;
+                else if (td.R1 == 64) cls = 3;
+            }
+            td.cls = cls;
+            if (cls < 0) h->any_generic = true;
+            if (td.D > h->Dmax) h->Dmax = td.D;
+            if (td.Dp > h->Dpmax) h->Dpmax = td.Dp;
+            if (td.R2 > h->R2max) h->R2max = td.R2;
+            h->max_d1R1 = std::max<int64_t>(h->max_d1R1, (int64_t)td.d1 * td.R1);
+            h->max_R2d3 = std::max<int64_t>(h->max_R2d3, (int64_t)td.R2 * td.d3);
+            h->max_Dp = std::max<int64_t>(h->max_Dp, td.Dp);
+            h->tabs.push_back(td);
+        }
+        if (rc == TT_EMB_OK && (key >= 0x7fffffffull || b2 >= 0x7fffffffull || b3 >= 0x7fffffffull || b1 >= 0x7fffffffull))
+            rc = TT_EMB_ERR_UNSUPPORTED;
+        if (rc != TT_EMB_OK) {
+            delete h;
+            return rc;
+        }
+        h->sumD = col;
+        h->sum_n[0] = (int)b1;
+        h->sum_n[1] = (int)b2;
+        h->sum_n[2] = (int)b3;
+        h->key_bits = bits_for(key - 1);
+        h->key2_bits = bits_for(b2 - 1);
+        h->key3_bits = bits_for(b3 - 1);
+        if (hipGetDevice(&h->device) != hipSuccess) {
+            delete h;
+            return TT_EMB_ERR_HIP;
+        }
+        if (o.num_blocks > 0) {
+            h->num_blocks = (o.num_blocks + 7) / 8 * 8;
+        } else {
+            int cus = 0;
+            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess || cus <= 0)
+                cus = 256;
+            h->num_blocks = (2 * cus + 7) / 8 * 8;
+        }
+        if (hipMalloc((void **)&h->dtab, sizeof(TableDesc) * T) != hipSuccess) {
+            delete h;
+            return TT_EMB_ERR_NOMEM;
+        }
+        if (hipMemcpy(h->dtab, h->tabs.data(), sizeof(TableDesc) * T, hipMemcpyHostToDevice) != hipSuccess) {
+            (void)hipFree(h->dtab);
+            delete h;
+            return TT_EMB_ERR_HIP;
+        }
+        *out = h;
+        return TT_EMB_OK;
+    } catch (...) {
+        return TT_EMB_ERR_NOMEM;
+    }
+}
+
+int tt_emb_destroy(tt_emb_t h)
+{
+    if (!h) return TT_EMB_OK;
+    int rc = TT_EMB_OK;
+    if (h->dtab && hipFree(h->dtab) != hipSuccess) rc = TT_EMB_ERR_HIP;
+    delete h;
+    return rc;
+}
+
+int tt_emb_workspace_size(tt_emb_t h, int64_t B, int64_t nnz, size_t *bytes)
+{
+    if (!h || !bytes || B < 0 || nnz < 0 || nnz >= (int64_t)0x7fffffff) return TT_EMB_ERR_ARG;
+    *bytes = plan_workspace(h, B, nnz, nullptr, nullptr);
+    return TT_EMB_OK;
+}
+
+int tt_emb_group(tt_emb_t h, const int64_t *indices, const int64_t *offsets, int64_t B, int64_t nnz, void *ws,
+                 size_t ws_bytes, void *stream)
+{
+    try {
+        Plan p;
+        int rc = check_call(h, B, nnz, indices, offsets, ws, ws_bytes, &p);
+        if (rc) return rc;
+        if ((rc = set_device(h))) return rc;
+        return hip_status(launch_grouping(p, indices, offsets, (hipStream_t)stream));
+    } catch (...) {
+        return TT_EMB_ERR_NOMEM;
+    }
+}
+
+static int core_ptrs(const tt_emb *h, const float *const *cores, CorePtrs *cp)
+{
+    if (!cores) return TT_EMB_ERR_ARG;
+    for (int t = 0; t < h->T; ++t)
+        for (int k = 0; k < 3; ++k) {
+            const float *c = cores[3 * t + k];
+            if (bad_ptr(c)) return TT_EMB_ERR_ARG;
+            cp->g[t][k] = c;
+        }
+    return TT_EMB_OK;
+}
+
+int tt_emb_forward(tt_emb_t h, const float *const *cores, const int64_t *indices, const int64_t *offsets,
+                   int64_t B, int64_t nnz, float *out, void *ws, size_t ws_bytes, uint32_t flags, void *stream)
+{
+    try {
+        Plan p;
+        int rc = check_call(h, B, nnz, indices, offsets, ws, ws_bytes, &p);
+        if (rc) return rc;
+        if (B > 0 && !out) return TT_EMB_ERR_ARG;
+        CorePtrs cp{};
+        if ((rc = core_ptrs(h, cores, &cp))) return rc;
+        if ((rc = set_device(h))) return rc;
+        hipStream_t s = (hipStream_t)stream;
+        if (!(flags & TT_EMB_REUSE_GROUPING)) {
+            if ((rc = hip_status(launch_grouping(p, indices, offsets, s)))) return rc;
+        }
+        return hip_status(launch_forward(p, cp, offsets, out, s));
+    } catch (...) {
+        return TT_EMB_ERR_NOMEM;
+    }
+}
+
+int tt_emb_backward(tt_emb_t h, const float *grad_out, const float *const *cores, const int64_t *indices,
+                    const int64_t *offsets, int64_t B, int64_t nnz, float *const *core_grads, void *ws,
+                    size_t ws_bytes, uint32_t flags, void *stream)
+{
+    try {
+        Plan p;
+        int rc = check_call(h, B, nnz, indices, offsets, ws, ws_bytes, &p);
+        if (rc) return rc;
+        if (B > 0 && !grad_out) return TT_EMB_ERR_ARG;
+        CorePtrs cp{};
+        if ((rc = core_ptrs(h, cores, &cp))) return rc;
+        if (!core_grads) return TT_EMB_ERR_ARG;
+        GradPtrs gp{};
+        for (int t = 0; t < h->T; ++t)
+            for (int k = 0; k < 3; ++k) {
+                float *g = core_grads[3 * t + k];
+                if (bad_ptr(g)) return TT_EMB_ERR_ARG;
+                gp.g[t][k] = g;
+            }
+        if ((rc = set_device(h))) return rc;
+        hipStream_t s = (hipStream_t)stream;
+        if (!(flags & TT_EMB_REUSE_GROUPING)) {
+            if ((rc = hip_status(launch_grouping(p, indices, offsets, s)))) return rc;
+        }
+        return hip_status(launch_backward(p, grad_out, cp, offsets, gp, s));
+    } catch (...) {
+        return TT_EMB_ERR_NOMEM;
+    }
+}
+
+int tt_emb_sgd_update(tt_emb_t h, float *const *cores, const float *const *core_grads, float lr, void *stream)
+{
+    if (!h || !cores || !core_grads) return TT_EMB_ERR_ARG;
+    for (int i = 0; i < 3 * h->T; ++i)
+        if (bad_ptr(cores[i]) || bad_ptr(core_grads[i])) return TT_EMB_ERR_ARG;
+    int rc = set_device(h);
+    if (rc) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    for (int t = 0; t < h->T; ++t) {
+        const TableDesc &d = h->tabs[t];
+        const int64_t cnt[3] = {(int64_t)d.n1 * d.d1 * d.R1, (int64_t)d.n2 * d.R1 * d.d2 * d.R2,
+                                (int64_t)d.n3 * d.R2 * d.d3};
+        for (int k = 0; k < 3; ++k) {
+            hipError_t e = launch_sgd(cores[3 * t + k], core_grads[3 * t + k], cnt[k], lr, s);
+            if (e != hipSuccess) return TT_EMB_ERR_HIP;
+        }
+    }
+    return TT_EMB_OK;
+}
+
+int tt_emb_grouping_view(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B, int64_t nnz, void *stream,
+                         tt_emb_grouping *view)
+{
+    if (!view) return TT_EMB_ERR_ARG;
+    Plan p;
+    int64_t dummy_off[1] = {0};
+    int rc = check_call(h, B, nnz, nnz > 0 ? dummy_off : nullptr, dummy_off, const_cast<void *>(ws), ws_bytes, &p);
+    if (rc) return rc;
+    if ((rc = set_device(h))) return rc;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TT_EMB_ERR_HIP;
+    int32_t ctrl[CTRL_N];
+    if (hipMemcpy(ctrl, p.ws.ctrl, sizeof(ctrl), hipMemcpyDeviceToHost) != hipSuccess) return TT_EMB_ERR_HIP;
+    view->nnz = nnz;
+    view->num_unique = ctrl[CTRL_U];
+    view->num_groups = ctrl[CTRL_G];
+    view->perm = p.ws.perm;
+    view->uniq_row = p.ws.uniq_row;
+    view->uniq_start = p.ws.uniq_start;
+    view->inv = p.ws.inv;
+    view->grp_prefix = p.ws.grp_prefix;
+    view->grp_start = p.ws.grp_start;
+    view->tab_uniq_start = p.ws.tab_uniq_start;
+    view->tab_grp_start = p.ws.tab_grp_start;
+    view->num_units = ctrl[CTRL_UNITS];
+    view->num_tiles = ctrl[CTRL_TILES];
+    view->num_chunks = ctrl[CTRL_CHUNKS];
+    view->num_split_tiles = ctrl[CTRL_SPLIT];
+    view->num_steals = ctrl[CTRL_STEALS];
+    view->num_ckpt_hits = ctrl[CTRL_CKPT_HIT];
+    view->num_ckpt_misses = ctrl[CTRL_CKPT_MISS];
+    return TT_EMB_OK;
+}
+
+int tt_emb_poll_error(tt_emb_t h, const void *ws, void *stream)
+{
+    if (!h || !ws) return TT_EMB_ERR_ARG;
+    int rc = set_device(h);
+    if (rc) return rc;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TT_EMB_ERR_HIP;
+    int32_t err = 0;
+    if (hipMemcpy(&err, ws, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return TT_EMB_ERR_HIP;
+    if (err & ERRB_OFFSETS) return TT_EMB_ERR_OFFSETS;
+    if (err & ERRB_INDEX) return TT_EMB_ERR_INDEX;
+    return TT_EMB_OK;
+}
+
+const char *tt_emb_status_string(int status)
+{
+    switch (status) {
+    case TT_EMB_OK: return "ok";
+    case TT_EMB_ERR_ARG: return "invalid argument";
+    case TT_EMB_ERR_INDEX: return "index out of range";
+    case TT_EMB_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case TT_EMB_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case TT_EMB_ERR_HIP: return "HIP runtime error";
+    case TT_EMB_ERR_NOMEM: return "out of memory";
+    case TT_EMB_ERR_OFFSETS: return "malformed offsets";
+    default: return "unknown status";
+    }
+}
+
+} // extern "C"

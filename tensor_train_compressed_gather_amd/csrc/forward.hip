@@ -1,0 +1,455 @@
+// forward.hip -- fused prefix-shared TT contraction and bag pooling on gfx950.
+//
+// Follows the FlowTT page ("FlowTT: Exploiting Computation Flow Reuse in
+// Irregular Tensor-Train Embedding"): section 3.2 (compute C = A.B once per
+// prefix group, keep it on chip, reuse it for every E = C.D, then pool),
+// section 3.3 (prefix groups are the execution units) and section 3.4
+// (persistent blocks run their assigned range first, then steal chunks; a
+// prefix tile split over chunks is checkpointed through L2 so other blocks can
+// reuse it).
+//
+// gfx950 mapping (one 256-thread block = 4 waves):
+//  * a tile holds up to four prefix units that share (table, i2).  Their four
+//    G1[i1] slices are stacked into the 16 rows of a v_mfma_f32_16x16x4_f32 A
+//    operand (row = 4*unit + j1), so the skinny d1 x R1 by R1 x d2R2 products
+//    run on the matrix cores at full width.  The G2[i2] slice is the B operand
+//    and stays in VGPRs while consecutive tiles share i2 ("B-stationary").
+//  * the 4 x 16 x R2 prefix tile is written to LDS; each row group of up to
+//    16/d3 unique rows of a unit is one 16x16 output tile of E = C.G3[i3],
+//    A read from LDS, B from the G3 slices of those rows.
+//  * pooling is a separate bag-major pass over the unique-row buffer: one wave
+//    per bag, a fixed summation order and no atomics, so the output is
+//    bit-reproducible.
+#include "primitives.h"
+
+namespace ttemb {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCStride = 68;                   // LDS row stride of a prefix tile (R2 <= 64)
+constexpr int kCUnit = 16 * kCStride + 16;     // floats per unit (extra 16 rotates banks)
+constexpr int kCTile = kUnitsPerTile * kCUnit; // floats per prefix tile
+constexpr int kSchedStatic = 1, kSchedSteal = 2, kSchedStealL2 = 3;
+
+struct FwdArgs {
+    const TableDesc *tab;
+    int T;
+    Ws ws;
+    CorePtrs cores;
+    int sched;
+};
+
+struct ChunkCtx {
+    int tile, t, nu, rbeg, rend, slot, i2, cls;
+    int i1[4], ustart[4], cfirst[4], ccnt[4];
+    int pstart[5];
+};
+
+// Victim order for stealing: own range, then blocks on the same XCD (blocks
+// are dispatched round-robin over the 8 XCDs), then the other XCDs.
+__device__ __forceinline__ int victim_of(int me, int vi, int nb)
+{
+    const int per = nb >> 3;
+    const int xo = vi / per, k = vi - xo * per;
+    return ((me & 7) + xo) % 8 + 8 * (((me >> 3) + k) % per);
+}
+
+__device__ __forceinline__ int range_begin(int v, int64_t C, int nb) { return (int)((int64_t)v * C / nb); }
+
+__global__ __launch_bounds__(kThreads) void k_queue_init(Ws ws, int nb)
+{
+    const int64_t C = ws.ctrl[CTRL_CHUNKS];
+    int split = ws.ctrl[CTRL_SPLIT];
+    if (split > kMaxCkptSlots) split = kMaxCkptSlots;
+    for (int b = threadIdx.x; b < nb; b += blockDim.x) ws.heads[b] = range_begin(b, C, nb);
+    for (int i = threadIdx.x; i < split; i += blockDim.x) ws.flags[i] = 0;
+    if (threadIdx.x == 0) {
+        ws.ctrl[CTRL_STEALS] = 0;
+        ws.ctrl[CTRL_CKPT_HIT] = 0;
+        ws.ctrl[CTRL_CKPT_MISS] = 0;
+    }
+}
+
+// One chunk of a tile on the matrix cores, R1 = R2 = R.
+template <int R>
+__device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkCtx &cx, float *Cs,
+                                           float (&breg)[64], int &bkey, int &lds_tile, int *s_flag)
+{
+    constexpr int KQ = R / 4;           // K values each lane feeds per output tile
+    constexpr int NT = R / 4;           // 16-column tiles of the padded d2*R2 (d2 <= 4)
+    constexpr int NTW = (NT + 3) / 4;   // per wave
+    const TableDesc &tb = a.tab[cx.t];
+    const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, n3 = tb.n3, D12 = d1 * d2;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, kq = lane >> 4;
+    const float *G1 = a.cores.g[cx.t][0];
+    const float *G2 = a.cores.g[cx.t][1];
+    const float *G3 = a.cores.g[cx.t][2];
+
+    // -------- prefix tile C_u = G1[i1_u] . G2[i2] for the (<= 4) units
+    if (lds_tile != cx.tile) {
+        bool have = false;
+        const bool split = cx.slot >= 0 && a.sched == kSchedStealL2;
+        if (split && cx.rbeg > 0) {
+            if (threadIdx.x == 0)
+                *s_flag = __hip_atomic_load(&a.ws.flags[cx.slot], __ATOMIC_ACQUIRE,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (*s_flag) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                const float4 *src = reinterpret_cast<const float4 *>(a.ws.ckpt + (size_t)cx.slot * kCTile);
+                float4 *dst = reinterpret_cast<float4 *>(Cs);
+                for (int i = threadIdx.x; i < kCTile / 4; i += kThreads) dst[i] = src[i];
+                have = true;
+            }
+            if (threadIdx.x == 0) atomicAdd(&a.ws.ctrl[have ? CTRL_CKPT_HIT : CTRL_CKPT_MISS], 1);
+        }
+        if (!have) {
+            const int key = (int)(tb.i2_base + (uint32_t)cx.i2);
+            if (bkey != key) {
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    const int ntg = w + 4 * j;
+                    const int col = ntg * 16 + li;
+                    const int j2 = col / R, r2 = col % R;
+                    const bool ok = ntg < NT && j2 < d2;
+                    const float *src = G2 + ((int64_t)cx.i2 * R * d2 + (ok ? j2 : 0)) * R + r2;
+#pragma unroll
+                    for (int s = 0; s < KQ; ++s) {
+                        const int k = kq * KQ + s;
+                        breg[j * KQ + s] = ok ? src[(int64_t)k * d2 * R] : 0.f;
+                    }
+                }
+                bkey = key;
+            }
+            const int g = li >> 2, j1 = li & 3;
+            const bool oka = g < cx.nu && j1 < d1;
+            const float *srcA = G1 + ((int64_t)(oka ? cx.i1[g] : 0) * d1 + (oka ? j1 : 0)) * R + kq * KQ;
+            float areg[KQ];
+            if constexpr (KQ % 4 == 0) {
+#pragma unroll
+                for (int s = 0; s < KQ; s += 4) {
+                    float4 v = oka ? *reinterpret_cast<const float4 *>(srcA + s) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    areg[s] = v.x;
+                    areg[s + 1] = v.y;
+                    areg[s + 2] = v.z;
+                    areg[s + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < KQ; ++s) areg[s] = oka ? srcA[s] : 0.f;
+            }
+            floatx4 acc[NTW];
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KQ; ++s) {
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+                    if (w + 4 * j < NT)
+                        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(areg[s], breg[j * KQ + s], acc[j], 0, 0, 0);
+            }
+            // lane (kq, li) holds rows 4*kq + v = (unit kq, j1 = v), column ntg*16 + li
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int ntg = w + 4 * j;
+                if (ntg < NT) {
+                    const int col = ntg * 16 + li;
+                    const int j2 = col / R, r2 = col % R;
+                    if (j2 < d2 && kq < cx.nu) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (v < d1) Cs[kq * kCUnit + (v * d2 + j2) * kCStride + r2] = acc[j][v];
+                    }
+                }
+            }
+            __syncthreads();
+            if (split && cx.rbeg == 0) {
+                float4 *dst = reinterpret_cast<float4 *>(a.ws.ckpt + (size_t)cx.slot * kCTile);
+                const float4 *src = reinterpret_cast<const float4 *>(Cs);
+                for (int i = threadIdx.x; i < kCTile / 4; i += kThreads) dst[i] = src[i];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __syncthreads();
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(&a.ws.flags[cx.slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        lds_tile = cx.tile;
+        __syncthreads();
+    }
+
+    // -------- unique rows E_u = C_unit . G3[i3_u], 16/d3 rows per output tile
+    const int P = 16 / d3;
+    const int np = cx.pstart[cx.nu];
+    float *Et = a.ws.E + a.ws.ebase[cx.t];
+    for (int e = w; e < np; e += 4) {
+        int j = 0;
+        while (j < 3 && e >= cx.pstart[j + 1]) ++j;
+        const int rfirst = cx.cfirst[j] + (e - cx.pstart[j]) * P;
+        int cnt = cx.cfirst[j] + cx.ccnt[j] - rfirst;
+        cnt = cnt < P ? cnt : P;
+        const int ufirst = cx.ustart[j] + rfirst;
+        const bool okm = li < D12;
+        const float *ca = Cs + j * kCUnit + (okm ? li : 0) * kCStride + kq * KQ;
+        float a2[KQ];
+        if constexpr (KQ % 4 == 0) {
+#pragma unroll
+            for (int s = 0; s < KQ; s += 4) {
+                float4 v = *reinterpret_cast<const float4 *>(ca + s);
+                a2[s] = okm ? v.x : 0.f;
+                a2[s + 1] = okm ? v.y : 0.f;
+                a2[s + 2] = okm ? v.z : 0.f;
+                a2[s + 3] = okm ? v.w : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < KQ; ++s) a2[s] = okm ? ca[s] : 0.f;
+        }
+        const int slot = li / d3, j3 = li - slot * d3;
+        const bool okb = slot < cnt;
+        const int u = ufirst + (okb ? slot : 0);
+        const int i3 = okb ? a.ws.uniq_row[u] % n3 : 0;
+        const float *gb = G3 + ((int64_t)i3 * R + kq * KQ) * d3 + (okb ? j3 : 0);
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KQ; ++s) {
+            const float b = okb ? gb[s * d3] : 0.f;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[s], b, acc, 0, 0, 0);
+        }
+        if (okb) {
+            float *Erow = Et + (int64_t)u * tb.Dp;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m2 = kq * 4 + v;
+                if (m2 < D12) Erow[m2 * d3 + j3] = acc[v];
+            }
+        }
+    }
+}
+
+// Persistent contraction kernel for every table of an MFMA rank class.
+__global__ __launch_bounds__(kThreads, 2) void k_contract(FwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float Cs[kCTile];
+    __shared__ ChunkCtx cx;
+    __shared__ int s_c, s_flag;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int nb = gridDim.x, me = blockIdx.x;
+    const int64_t C = a.ws.ctrl[CTRL_CHUNKS];
+    const int nvict = a.sched == kSchedStatic ? 1 : nb;
+    float breg[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) breg[i] = 0.f;
+    int bkey = -1, lds_tile = -1, vi = 0;
+    for (;;) {
+        // ---- claim the next chunk: own range first, then steal
+        if (w == 0) {
+            int c = -1;
+            while (vi < nvict) {
+                int got = -1;
+                if (lane == 0) {
+                    const int v = victim_of(me, vi, nb);
+                    const int idx = atomicAdd(&a.ws.heads[v], 1);
+                    if (idx < range_begin(v + 1, C, nb)) got = idx;
+                }
+                got = __shfl(got, 0, 64);
+                if (got >= 0) {
+                    c = got;
+                    if (vi != 0 && lane == 0) atomicAdd(&a.ws.ctrl[CTRL_STEALS], 1);
+                    break;
+                }
+                // the current victim is drained: probe the next 64 in parallel
+                const int cand = vi + 1 + lane;
+                bool avail = false;
+                if (cand < nvict) {
+                    const int v = victim_of(me, cand, nb);
+                    avail = __hip_atomic_load(&a.ws.heads[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                            range_begin(v + 1, C, nb);
+                }
+                const uint64_t m = __ballot(avail);
+                vi = m ? vi + 1 + (__ffsll((unsigned long long)m) - 1) : vi + 65;
+            }
+            if (lane == 0) s_c = c;
+        }
+        __syncthreads();
+        const int c = s_c;
+        if (c < 0) break;
+        // ---- chunk context
+        if (threadIdx.x == 0) {
+            const Ws &ws = a.ws;
+            const int tile = ws.chunk_tile[c];
+            const int rbeg = ws.chunk_rbeg[c], rend = ws.chunk_rend[c];
+            const int ubeg = ws.tile_ubeg[tile], nu = ws.tile_nu[tile];
+            const int u0 = ws.uorder[ubeg];
+            const int t = segment_of(ws.tab_unit_start, a.T, u0);
+            const TableDesc &tb = a.tab[t];
+            cx.tile = tile;
+            cx.t = t;
+            cx.nu = nu;
+            cx.rbeg = rbeg;
+            cx.rend = rend;
+            cx.slot = ws.tile_slot[tile];
+            cx.cls = tb.cls;
+            cx.i2 = ws.unit_prefix[u0] % tb.n2;
+            const int P = 16 / (tb.d3 > 0 && tb.d3 <= 16 ? tb.d3 : 16);
+            int off = 0;
+            cx.pstart[0] = 0;
+            for (int j = 0; j < 4; ++j) {
+                int cf = 0, cc = 0, us = 0, i1 = 0;
+                if (j < nu) {
+                    const int u = ws.uorder[ubeg + j];
+                    us = ws.unit_start[u];
+                    const int cnt = ws.unit_start[u + 1] - us;
+                    i1 = ws.unit_prefix[u] / tb.n2;
+                    const int lo = rbeg > off ? rbeg : off;
+                    const int hi = rend < off + cnt ? rend : off + cnt;
+                    cf = lo - off;
+                    cc = hi > lo ? hi - lo : 0;
+                    off += cnt;
+                }
+                cx.i1[j] = i1;
+                cx.ustart[j] = us;
+                cx.cfirst[j] = cf;
+                cx.ccnt[j] = cc;
+                cx.pstart[j + 1] = cx.pstart[j] + (cc + P - 1) / P;
+            }
+        }
+        __syncthreads();
+        switch (cx.cls) {
+        case 0: chunk_mfma<8>(a, cx, Cs, breg, bkey, lds_tile, &s_flag); break;
+        case 1: chunk_mfma<16>(a, cx, Cs, breg, bkey, lds_tile, &s_flag); break;
+        case 2: chunk_mfma<32>(a, cx, Cs, breg, bkey, lds_tile, &s_flag); break;
+        case 3: chunk_mfma<64>(a, cx, Cs, breg, bkey, lds_tile, &s_flag); break;
+        default: break; // tables outside the rank classes run in k_contract_generic
+        }
+        __syncthreads();
+    }
+}
+
+// Plain fp32 contraction for any shape within the create-time limits: one
+// block per unit, the prefix intermediate in LDS, then every unique row.
+__global__ __launch_bounds__(kThreads) void k_contract_generic(FwdArgs a, int force)
+{
+    __shared__ float Cg[4096];
+    const Ws &ws = a.ws;
+    const int64_t Un = ws.ctrl[CTRL_UNITS];
+    for (int64_t unit = blockIdx.x; unit < Un; unit += gridDim.x) {
+        const int t = segment_of(ws.tab_unit_start, a.T, unit);
+        const TableDesc &tb = a.tab[t];
+        if (!force && tb.cls >= 0) continue;
+        const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, R1 = tb.R1, R2 = tb.R2, D = tb.D;
+        const int q = ws.unit_prefix[unit];
+        const int i1 = q / tb.n2, i2 = q % tb.n2;
+        const float *G1 = a.cores.g[t][0] + (int64_t)i1 * d1 * R1;
+        const float *G2 = a.cores.g[t][1] + (int64_t)i2 * R1 * d2 * R2;
+        const float *G3 = a.cores.g[t][2];
+        for (int e = threadIdx.x; e < d1 * d2 * R2; e += kThreads) {
+            const int m2 = e / R2, r2 = e - m2 * R2, j1 = m2 / d2, j2 = m2 - j1 * d2;
+            float acc = 0.f;
+            for (int r1 = 0; r1 < R1; ++r1) acc = fmaf(G1[j1 * R1 + r1], G2[((int64_t)r1 * d2 + j2) * R2 + r2], acc);
+            Cg[e] = acc;
+        }
+        __syncthreads();
+        const int us = ws.unit_start[unit], ue = ws.unit_start[unit + 1];
+        float *Et = ws.E + ws.ebase[t];
+        for (int64_t e = threadIdx.x; e < (int64_t)(ue - us) * D; e += kThreads) {
+            const int r = (int)(e / D), col = (int)(e - (int64_t)r * D);
+            const int u = us + r;
+            const int i3 = ws.uniq_row[u] % tb.n3;
+            const int m2 = col / d3, j3 = col - m2 * d3;
+            const float *g3 = G3 + (int64_t)i3 * R2 * d3 + j3;
+            float acc = 0.f;
+            for (int r2 = 0; r2 < R2; ++r2) acc = fmaf(Cg[m2 * R2 + r2], g3[r2 * d3], acc);
+            Et[(int64_t)u * tb.Dp + col] = acc;
+        }
+        __syncthreads();
+    }
+}
+
+// Bag-major sum pooling: one wave per bag; lanes split the columns in float4
+// and the lookups in 64/lanes-per-row interleaved streams, combined in a fixed
+// xor-tree order.  Empty bags write zeros.
+__global__ __launch_bounds__(kThreads) void k_pool(const TableDesc *tab, int T, int64_t B,
+                                                   const int64_t *offsets, int64_t nnz, Ws ws,
+                                                   float *out, int SD)
+{
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t bag = (int64_t)blockIdx.x * (kThreads / 64) + w;
+    if (bag >= (int64_t)T * B) return;
+    const int t = (int)(bag / B);
+    const int64_t b = bag - (int64_t)t * B;
+    const TableDesc &tb = tab[t];
+    int64_t lo = offsets[bag], hi = offsets[bag + 1];
+    lo = lo < 0 ? 0 : (lo > nnz ? nnz : lo);
+    hi = hi < lo ? lo : (hi > nnz ? nnz : hi);
+    const int u0 = ws.tab_uniq_start[t], u1 = ws.tab_uniq_start[t + 1];
+    if (u1 <= u0) hi = lo;
+    const float *Et = ws.E + ws.ebase[t];
+    float *o = out + b * SD + tb.col_off;
+    const int D = tb.D;
+    if (D <= 256) {
+        // lanes per row: smallest power of two >= D/4 (float4 columns)
+        const int c4n = (D + 3) >> 2;
+        int lpr = 1;
+        while (lpr < c4n) lpr <<= 1;
+        const int rf = 64 / lpr;
+        const int c4 = lane & (lpr - 1), r = lane / lpr;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c4 < c4n) {
+            for (int64_t l = lo + r; l < hi; l += rf) {
+                int u = ws.inv[l];
+                u = u < u0 ? u0 : (u >= u1 ? u1 - 1 : u);
+                const float4 v = *reinterpret_cast<const float4 *>(Et + (int64_t)u * tb.Dp + 4 * c4);
+                acc.x += v.x;
+                acc.y += v.y;
+                acc.z += v.z;
+                acc.w += v.w;
+            }
+        }
+        for (int m = lpr; m < 64; m <<= 1) {
+            acc.x += __shfl_xor(acc.x, m, 64);
+            acc.y += __shfl_xor(acc.y, m, 64);
+            acc.z += __shfl_xor(acc.z, m, 64);
+            acc.w += __shfl_xor(acc.w, m, 64);
+        }
+        if (r == 0 && c4 < c4n) {
+            const int j = 4 * c4;
+            if (j + 0 < D) o[j + 0] = acc.x;
+            if (j + 1 < D) o[j + 1] = acc.y;
+            if (j + 2 < D) o[j + 2] = acc.z;
+            if (j + 3 < D) o[j + 3] = acc.w;
+        }
+    } else {
+        for (int j = lane; j < D; j += 64) {
+            float acc = 0.f;
+            for (int64_t l = lo; l < hi; ++l) {
+                int u = ws.inv[l];
+                u = u < u0 ? u0 : (u >= u1 ? u1 - 1 : u);
+                acc += Et[(int64_t)u * tb.Dp + j];
+            }
+            o[j] = acc;
+        }
+    }
+}
+
+hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *offsets, float *out,
+                          hipStream_t s)
+{
+    FwdArgs a{p.dtab, p.T, p.ws, cores, p.sched_mode};
+    if (p.nnz > 0) {
+        hipLaunchKernelGGL(k_queue_init, dim3(1), dim3(kThreads), 0, s, p.ws, p.num_blocks);
+        if (!p.force_generic)
+            hipLaunchKernelGGL(k_contract, dim3(p.num_blocks), dim3(kThreads), 0, s, a);
+        if (p.force_generic || p.any_generic)
+            hipLaunchKernelGGL(k_contract_generic, dim3(p.num_blocks * 4), dim3(kThreads), 0, s, a,
+                               p.force_generic ? 1 : 0);
+    }
+    const int64_t nbags = (int64_t)p.T * p.B;
+    if (nbags > 0) {
+        const int64_t g = (nbags + 3) / 4;
+        hipLaunchKernelGGL(k_pool, dim3((unsigned)g), dim3(kThreads), 0, s, p.dtab, p.T, p.B, offsets,
+                           p.nnz, p.ws, out, p.sumD);
+    }
+    return hipGetLastError();
+}
+
+} // namespace ttemb

@@ -1,0 +1,537 @@
+// group.hip -- index grouping on gfx950.
+//
+// Stage order follows the grouping breakdown of the FlowTT page ("FlowTT:
+// Exploiting Computation Flow Reuse in Irregular Tensor-Train Embedding",
+// section 4): index sorting, unique extraction, mixed-radix conversion,
+// prefix extraction and run-length encoding; prefixes are the shared
+// high-order row digits (section 3.3).  Everything is deterministic: a stable
+// LSD radix sort and scans with a fixed block decomposition, so every output
+// array is bit-exact against a plain stable sort.
+//
+// After the canonical arrays, the same pass builds the work list of the
+// contraction: units (groups, or unique rows in the unique-only ablation)
+// re-sorted stably by (table, i2) so that units sharing the second core slice
+// are adjacent (the slice stays resident in registers), cut into tiles of at
+// most four units and then into chunks of at most chunk_rows rows.
+#include "primitives.h"
+
+namespace ttemb {
+
+// ------------------------------------------------------------- set-up
+
+__global__ __launch_bounds__(kThreads) void k_init_ctrl(Ws ws, int T)
+{
+    for (int i = threadIdx.x; i < CTRL_N; i += blockDim.x) ws.ctrl[i] = 0;
+    for (int i = threadIdx.x; i <= T; i += blockDim.x) {
+        ws.tab_uniq_start[i] = 0;
+        ws.tab_grp_start[i] = 0;
+    }
+    if (threadIdx.x == 0) {
+        ws.uniq_start[0] = 0;
+        ws.grp_start[0] = 0;
+    }
+}
+
+// Offsets must start at 0, never decrease and end at nnz.  Malformed offsets
+// set ERRB_OFFSETS; every later kernel clamps ranges so it stays in bounds.
+__global__ __launch_bounds__(kThreads) void k_check_offsets(const int64_t *offsets, int64_t nbags,
+                                                            int64_t nnz, int64_t B, int T, Ws ws)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int bad = 0;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nbags; b += stride) {
+        int64_t o0 = offsets[b], o1 = offsets[b + 1];
+        if (o1 < o0 || o0 < 0 || o1 > nnz) bad = 1;
+        if (b == 0 && o0 != 0) bad = 1;
+        if (b == nbags - 1 && o1 != nnz) bad = 1;
+    }
+    if (__any(bad) && lane_id() == 0) atomicOr(&ws.ctrl[CTRL_ERR], (int)ERRB_OFFSETS);
+    if (blockIdx.x == 0) {
+        for (int t = threadIdx.x; t <= T; t += blockDim.x) {
+            int64_t o = nbags > 0 ? offsets[(int64_t)t * B] : 0;
+            if (t == T) o = nnz;
+            o = o < 0 ? 0 : (o > nnz ? nnz : o);
+            ws.tstart[t] = (int32_t)o;
+        }
+    }
+}
+
+// Range check and sort key (table base + row) of every lookup.
+__global__ __launch_bounds__(kThreads) void k_decode(const int64_t *indices, int64_t nnz,
+                                                     const TableDesc *tab, int T, int check, Ws ws)
+{
+    __shared__ int32_t st[kMaxTables + 1];
+    __shared__ uint32_t kb[kMaxTables];
+    __shared__ int64_t nrows[kMaxTables];
+    for (int t = threadIdx.x; t <= T; t += blockDim.x) {
+        st[t] = ws.tstart[t];
+        if (t < T) {
+            kb[t] = tab[t].key_base;
+            nrows[t] = tab[t].N;
+        }
+    }
+    __syncthreads();
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int bad = 0;
+    for (int64_t l = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; l < nnz; l += stride) {
+        int t = segment_of(st, T, l);
+        int64_t i = indices[l];
+        if (i < 0 || i >= nrows[t]) {
+            bad |= check;
+            i = i < 0 ? 0 : nrows[t] - 1;
+        }
+        ws.keys0[l] = kb[t] + (uint32_t)i;
+        ws.vals0[l] = (int32_t)l;
+    }
+    if (__any(bad) && lane_id() == 0) atomicOr(&ws.ctrl[CTRL_ERR], (int)ERRB_INDEX);
+}
+
+// -------------------------------------------------------- radix sort
+//
+// Stable LSD radix sort of (u32 key, i32 value), 8-bit digits.  Per pass:
+// per-block digit counts (upsweep), one exclusive scan of the digit-major
+// count matrix, then a downsweep that ranks keys inside the block without
+// breaking ties (each wave owns a contiguous quarter of the tile and keeps
+// running per-digit counts) and writes runs of equal digits contiguously.
+
+constexpr int kRadixBits = 8;
+constexpr int kRadix = 1 << kRadixBits;
+
+__global__ __launch_bounds__(kThreads) void k_sort_upsweep(const uint32_t *keys, int64_t n_max,
+                                                           const int32_t *n_dev, int shift,
+                                                           uint32_t *hist, int nblk)
+{
+    __shared__ uint32_t cnt[kRadix];
+    for (int i = threadIdx.x; i < kRadix; i += kThreads) cnt[i] = 0;
+    __syncthreads();
+    const int64_t n = n_dev ? (int64_t)*n_dev : n_max;
+    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+#pragma unroll 4
+    for (int j = 0; j < kSortItems; ++j) {
+        int64_t i = base + j * kThreads + threadIdx.x;
+        if (i < n) atomicAdd(&cnt[(keys[i] >> shift) & (kRadix - 1)], 1u);
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < kRadix; d += kThreads) hist[(int64_t)d * nblk + blockIdx.x] = cnt[d];
+}
+
+struct HistScanOp {
+    uint32_t *hist;
+    int64_t n;
+    __device__ int64_t count() const { return n; }
+    __device__ uint64_t value(int64_t i) const { return hist[i]; }
+    __device__ void emit(int64_t i, uint64_t excl, uint64_t) const { hist[i] = (uint32_t)excl; }
+    __device__ void total(uint64_t, int64_t) const {}
+};
+
+__global__ __launch_bounds__(kThreads) void k_sort_downsweep(const uint32_t *kin, const int32_t *vin,
+                                                             uint32_t *kout, int32_t *vout,
+                                                             int64_t n_max, const int32_t *n_dev,
+                                                             int shift, const uint32_t *hist,
+                                                             int nblk)
+{
+    constexpr int W = kThreads / 64;
+    constexpr int SUB = kSortTile / W;    // keys per wave
+    constexpr int ROUNDS = SUB / 64;
+    __shared__ uint32_t wcnt[W][kRadix];
+    __shared__ uint32_t dstart[kRadix];
+    __shared__ uint32_t gbase[kRadix];
+    __shared__ uint32_t skey[kSortTile];
+    __shared__ int32_t sval[kSortTile];
+    __shared__ uint32_t ssum[W];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t n = n_dev ? (int64_t)*n_dev : n_max;
+    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    if (base >= n) return;
+    for (int i = tid; i < W * kRadix; i += kThreads) (&wcnt[0][0])[i] = 0;
+    for (int d = tid; d < kRadix; d += kThreads) gbase[d] = hist[(int64_t)d * nblk + blockIdx.x];
+    __syncthreads();
+
+    uint32_t key[ROUNDS];
+    int32_t val[ROUNDS];
+    uint32_t rank[ROUNDS];
+    const uint64_t lt = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+        const int64_t i = base + w * SUB + r * 64 + lane;
+        const bool valid = i < n;
+        const uint32_t k = valid ? kin[i] : 0xffffffffu;
+        const uint32_t d = (k >> shift) & (kRadix - 1);
+        uint64_t m = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < kRadixBits; ++b) {
+            const bool bit = (d >> b) & 1u;
+            const uint64_t bb = __ballot(bit);
+            m &= bit ? bb : ~bb;
+        }
+        const uint32_t below = (uint32_t)__popcll(m & lt);
+        const uint32_t prior = wcnt[w][d];
+        __builtin_amdgcn_wave_barrier();
+        if (valid && below == 0) wcnt[w][d] = prior + (uint32_t)__popcll(m);
+        __builtin_amdgcn_wave_barrier();
+        key[r] = k;
+        val[r] = valid ? vin[i] : -1;
+        rank[r] = valid ? prior + below : 0xffffffffu;
+    }
+    __syncthreads();
+    // wave prefixes per digit and the tile total of each digit
+    uint32_t tot_d = 0;
+    const int d0 = tid; // kRadix == kThreads
+    {
+        uint32_t s = 0;
+#pragma unroll
+        for (int ww = 0; ww < W; ++ww) {
+            uint32_t c = wcnt[ww][d0];
+            wcnt[ww][d0] = s;
+            s += c;
+        }
+        tot_d = s;
+    }
+    // exclusive scan of the digit totals -> tile-local digit starts
+    {
+        uint32_t x = wave_inclusive_scan(tot_d);
+        if (lane == 63) ssum[w] = x;
+        __syncthreads();
+        uint32_t pre = 0;
+        for (int ww = 0; ww < w; ++ww) pre += ssum[ww];
+        dstart[d0] = pre + x - tot_d;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+        if (rank[r] != 0xffffffffu) {
+            const uint32_t d = (key[r] >> shift) & (kRadix - 1);
+            const uint32_t pos = dstart[d] + wcnt[w][d] + rank[r];
+            skey[pos] = key[r];
+            sval[pos] = val[r];
+        }
+    }
+    __syncthreads();
+    const int cnt = (int)((n - base) < kSortTile ? (n - base) : kSortTile);
+    for (int j = tid; j < cnt; j += kThreads) {
+        const uint32_t k = skey[j];
+        const uint32_t d = (k >> shift) & (kRadix - 1);
+        const uint32_t o = gbase[d] + (uint32_t)j - dstart[d];
+        kout[o] = k;
+        vout[o] = sval[j];
+    }
+}
+
+hipError_t radix_sort_pairs(const Plan &p, uint32_t *k0, int32_t *v0, uint32_t *k1, int32_t *v1,
+                            int64_t n_max, const int32_t *n_dev, int bits, bool *result_in_1,
+                            hipStream_t s)
+{
+    static_assert(kRadix == kThreads, "downsweep assumes one digit per thread");
+    *result_in_1 = false;
+    if (n_max <= 0 || bits <= 0) return hipSuccess;
+    const int nblk = ceil_div(n_max, kSortTile);
+    const int passes = (bits + kRadixBits - 1) / kRadixBits;
+    uint32_t *kin = k0, *kout = k1;
+    int32_t *vin = v0, *vout = v1;
+    for (int pass = 0; pass < passes; ++pass) {
+        const int shift = pass * kRadixBits;
+        hipLaunchKernelGGL(k_sort_upsweep, dim3(nblk), dim3(kThreads), 0, s, kin, n_max, n_dev,
+                           shift, p.ws.hist, nblk);
+        HistScanOp op{p.ws.hist, (int64_t)kRadix * nblk};
+        hipError_t e = run_scan(op, p.ws.part, scan_blocks(op.n), s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_sort_downsweep, dim3(nblk), dim3(kThreads), 0, s, kin, vin, kout, vout,
+                           n_max, n_dev, shift, p.ws.hist, nblk);
+        uint32_t *tk = kin;
+        kin = kout;
+        kout = tk;
+        int32_t *tv = vin;
+        vin = vout;
+        vout = tv;
+    }
+    *result_in_1 = (passes & 1) != 0;
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------ unique rows
+
+struct UniqueOp {
+    const uint32_t *sk;
+    const int32_t *perm;
+    Ws ws;
+    int64_t n;
+    __device__ int64_t count() const { return n; }
+    __device__ uint64_t value(int64_t k) const { return (k == 0 || sk[k] != sk[k - 1]) ? 1 : 0; }
+    __device__ void emit(int64_t k, uint64_t excl, uint64_t v) const
+    {
+        const int32_t uid = (int32_t)(excl + v) - 1;
+        if (v) {
+            ws.ukey[uid] = sk[k];
+            ws.uniq_start[uid] = (int32_t)k;
+        }
+        ws.inv[perm[k]] = uid;
+    }
+    __device__ void total(uint64_t tot, int64_t nn) const
+    {
+        ws.ctrl[CTRL_U] = (int32_t)tot;
+        ws.uniq_start[tot] = (int32_t)nn;
+    }
+};
+
+// ------------------------------------------ mixed radix + prefix RLE
+
+struct GroupOp {
+    const TableDesc *tab;
+    int T;
+    Ws ws;
+    __device__ int64_t count() const { return ws.ctrl[CTRL_U]; }
+    __device__ void info(int64_t u, int *t, int32_t *row, int32_t *q) const
+    {
+        const uint32_t key = ws.ukey[u];
+        *t = table_of_key(tab, T, key);
+        *row = (int32_t)(key - tab[*t].key_base);
+        *q = *row / tab[*t].n3;
+    }
+    __device__ uint64_t value(int64_t u) const
+    {
+        if (u == 0) return 1;
+        int t0, t1;
+        int32_t r0, r1, q0, q1;
+        info(u - 1, &t0, &r0, &q0);
+        info(u, &t1, &r1, &q1);
+        return (t0 != t1 || q0 != q1) ? 1 : 0;
+    }
+    __device__ void emit(int64_t u, uint64_t excl, uint64_t v) const
+    {
+        int t;
+        int32_t row, q;
+        info(u, &t, &row, &q);
+        const int32_t gid = (int32_t)(excl + v) - 1;
+        ws.uniq_row[u] = row;
+        if (v) {
+            ws.grp_prefix[gid] = q;
+            ws.grp_start[gid] = (int32_t)u;
+        }
+        int tprev = -1;
+        if (u > 0) {
+            int32_t r0, q0;
+            info(u - 1, &tprev, &r0, &q0);
+        }
+        for (int tt = tprev + 1; tt <= t; ++tt) {
+            ws.tab_uniq_start[tt] = (int32_t)u;
+            ws.tab_grp_start[tt] = gid;
+        }
+    }
+    __device__ void total(uint64_t tot, int64_t U) const
+    {
+        ws.ctrl[CTRL_G] = (int32_t)tot;
+        ws.grp_start[tot] = (int32_t)U;
+        int tl = -1;
+        if (U > 0) tl = table_of_key(tab, T, ws.ukey[U - 1]);
+        for (int tt = tl + 1; tt <= T; ++tt) {
+            ws.tab_uniq_start[tt] = (int32_t)U;
+            ws.tab_grp_start[tt] = (int32_t)tot;
+        }
+    }
+};
+
+// Work units in the unique-only ablation: every unique row is its own unit.
+__global__ __launch_bounds__(kThreads) void k_units_unique(const TableDesc *tab, int T, Ws ws)
+{
+    const int64_t U = ws.ctrl[CTRL_U];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < U; u += stride) {
+        const int t = segment_of(ws.tab_uniq_start, T, u);
+        ws.unit_prefix[u] = ws.uniq_row[u] / tab[t].n3;
+        ws.unit_start[u] = (int32_t)u;
+    }
+    if (blockIdx.x == 0) {
+        for (int t = threadIdx.x; t <= T; t += blockDim.x) ws.tab_unit_start[t] = ws.tab_uniq_start[t];
+        if (threadIdx.x == 0) {
+            ws.unit_start[U] = (int32_t)U;
+            ws.ctrl[CTRL_UNITS] = (int32_t)U;
+        }
+    }
+}
+
+// Per-table bases of the E rows and of the backward partial buffers.
+__global__ void k_finalize_bases(const TableDesc *tab, int T, int unique_only, Ws ws)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    if (!unique_only) ws.ctrl[CTRL_UNITS] = ws.ctrl[CTRL_G];
+    int64_t e = 0, p3 = 0, g1 = 0;
+    for (int t = 0; t < T; ++t) {
+        const TableDesc &d = tab[t];
+        const int64_t u0 = ws.tab_uniq_start[t], u1 = ws.tab_uniq_start[t + 1];
+        const int64_t n0 = ws.tab_unit_start[t], n1 = ws.tab_unit_start[t + 1];
+        ws.ebase[t] = e - u0 * d.Dp;
+        e += (u1 - u0) * d.Dp;
+        ws.p3base[t] = p3 - u0 * (int64_t)d.R2 * d.d3;
+        p3 += (u1 - u0) * (int64_t)d.R2 * d.d3;
+        ws.g1base[t] = g1 - n0 * (int64_t)d.d1 * d.R1;
+        g1 += (n1 - n0) * (int64_t)d.d1 * d.R1;
+    }
+}
+
+// ------------------------------------------------ B-stationary work list
+
+__global__ __launch_bounds__(kThreads) void k_unit_keys(const TableDesc *tab, int T, Ws ws)
+{
+    const int64_t Un = ws.ctrl[CTRL_UNITS];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < Un; k += stride) {
+        const int t = segment_of(ws.tab_unit_start, T, k);
+        ws.keys0[k] = tab[t].i2_base + (uint32_t)(ws.unit_prefix[k] % tab[t].n2);
+        ws.uvals0[k] = (int32_t)k;
+    }
+}
+
+struct RunOp {
+    const uint32_t *k2;
+    Ws ws;
+    __device__ int64_t count() const { return ws.ctrl[CTRL_UNITS]; }
+    __device__ uint64_t value(int64_t k) const { return (k == 0 || k2[k] != k2[k - 1]) ? 1 : 0; }
+    __device__ void emit(int64_t k, uint64_t excl, uint64_t v) const
+    {
+        if (v) ws.run_start[excl] = (int32_t)k;
+    }
+    __device__ void total(uint64_t tot, int64_t n) const
+    {
+        ws.ctrl[CTRL_RUNS] = (int32_t)tot;
+        ws.run_start[tot] = (int32_t)n;
+    }
+};
+
+struct TileOp {
+    Ws ws;
+    __device__ int64_t count() const { return ws.ctrl[CTRL_RUNS]; }
+    __device__ uint64_t value(int64_t r) const
+    {
+        const int64_t len = ws.run_start[r + 1] - ws.run_start[r];
+        return (uint64_t)((len + kUnitsPerTile - 1) / kUnitsPerTile);
+    }
+    __device__ void emit(int64_t r, uint64_t excl, uint64_t v) const
+    {
+        const int32_t b = ws.run_start[r], len = ws.run_start[r + 1] - b;
+        ws.run_tile_start[r] = (int32_t)excl;
+        for (uint64_t j = 0; j < v; ++j) {
+            ws.tile_ubeg[excl + j] = b + (int32_t)j * kUnitsPerTile;
+            const int32_t rem = len - (int32_t)j * kUnitsPerTile;
+            ws.tile_nu[excl + j] = rem < kUnitsPerTile ? rem : kUnitsPerTile;
+        }
+    }
+    __device__ void total(uint64_t tot, int64_t nruns) const
+    {
+        ws.ctrl[CTRL_TILES] = (int32_t)tot;
+        ws.run_tile_start[nruns] = (int32_t)tot;
+    }
+};
+
+struct ChunkOp {
+    Ws ws;
+    int S;
+    __device__ int64_t count() const { return ws.ctrl[CTRL_TILES]; }
+    __device__ int32_t rows(int64_t tile) const
+    {
+        const int32_t b = ws.tile_ubeg[tile], nu = ws.tile_nu[tile];
+        int32_t r = 0;
+        for (int j = 0; j < nu; ++j) {
+            const int32_t u = ws.uorder[b + j];
+            r += ws.unit_start[u + 1] - ws.unit_start[u];
+        }
+        return r;
+    }
+    __device__ uint64_t value(int64_t tile) const
+    {
+        const int32_t r = rows(tile);
+        const uint64_t nch = r <= S ? 1 : (uint64_t)((r + S - 1) / S);
+        return nch | (nch > 1 ? (1ull << 32) : 0ull);
+    }
+    __device__ void emit(int64_t tile, uint64_t excl, uint64_t v) const
+    {
+        const int32_t r = rows(tile);
+        const uint32_t nch = (uint32_t)(v & 0xffffffffu);
+        const uint32_t lo = (uint32_t)(excl & 0xffffffffu), hi = (uint32_t)(excl >> 32);
+        ws.tile_rows[tile] = r;
+        ws.tile_slot[tile] = (nch > 1 && hi < (uint32_t)kMaxCkptSlots) ? (int32_t)hi : -1;
+        for (uint32_t c = 0; c < nch; ++c) {
+            ws.chunk_tile[lo + c] = (int32_t)tile;
+            ws.chunk_rbeg[lo + c] = (int32_t)(c * S);
+            const int32_t e = (int32_t)((c + 1) * S);
+            ws.chunk_rend[lo + c] = e < r ? e : r;
+        }
+    }
+    __device__ void total(uint64_t tot, int64_t) const
+    {
+        ws.ctrl[CTRL_CHUNKS] = (int32_t)(tot & 0xffffffffu);
+        ws.ctrl[CTRL_SPLIT] = (int32_t)(tot >> 32);
+    }
+};
+
+hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t *offsets,
+                           hipStream_t s)
+{
+    Ws ws = p.ws;
+    const int T = p.T;
+    const int64_t nnz = p.nnz, nbags = (int64_t)T * p.B;
+    hipLaunchKernelGGL(k_init_ctrl, dim3(1), dim3(kThreads), 0, s, ws, T);
+    {
+        int g = ceil_div(nbags > 0 ? nbags : 1, kThreads);
+        if (g > 4096) g = 4096;
+        hipLaunchKernelGGL(k_check_offsets, dim3(g), dim3(kThreads), 0, s, offsets, nbags, nnz, p.B, T, ws);
+    }
+    if (nnz > 0) {
+        int g = ceil_div(nnz, kThreads * 4);
+        if (g > 8192) g = 8192;
+        hipLaunchKernelGGL(k_decode, dim3(g), dim3(kThreads), 0, s, indices, nnz, p.dtab, T,
+                           p.check_indices ? 1 : 0, ws);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // 1. index sorting by (table, row), stable
+    bool in1 = false;
+    e = radix_sort_pairs(p, ws.keys0, ws.vals0, ws.keys1, ws.vals1, nnz, nullptr, p.key_bits, &in1, s);
+    if (e != hipSuccess) return e;
+    const uint32_t *sk = in1 ? ws.keys1 : ws.keys0;
+    const int32_t *sv = in1 ? ws.vals1 : ws.vals0;
+    // the plan points skeys/perm at the buffers the sort ends in
+    if (sk != ws.skeys || sv != ws.perm) return hipErrorInvalidValue;
+    // 2. unique extraction
+    if (nnz > 0) {
+        UniqueOp uop{sk, sv, ws, nnz};
+        e = run_scan(uop, ws.part, scan_blocks(nnz), s);
+        if (e != hipSuccess) return e;
+        // 3.-4. mixed-radix conversion, prefix extraction, run-length encoding
+        GroupOp gop{p.dtab, T, ws};
+        e = run_scan(gop, ws.part, scan_blocks(nnz), s);
+        if (e != hipSuccess) return e;
+    }
+    const bool unique_only = p.group_mode == 2;
+    if (unique_only) {
+        int g = ceil_div(nnz > 0 ? nnz : 1, kThreads * 4);
+        if (g > 8192) g = 8192;
+        hipLaunchKernelGGL(k_units_unique, dim3(g), dim3(kThreads), 0, s, p.dtab, T, ws);
+    }
+    hipLaunchKernelGGL(k_finalize_bases, dim3(1), dim3(64), 0, s, p.dtab, T, unique_only ? 1 : 0, ws);
+    if (nnz > 0) {
+        // B-stationary order of units: stable sort by (table, i2)
+        int g = ceil_div(nnz, kThreads * 4);
+        if (g > 8192) g = 8192;
+        hipLaunchKernelGGL(k_unit_keys, dim3(g), dim3(kThreads), 0, s, p.dtab, T, ws);
+        bool u1 = false;
+        e = radix_sort_pairs(p, ws.keys0, ws.uvals0, ws.keys1, ws.uvals1, nnz, &ws.ctrl[CTRL_UNITS],
+                             p.key2_bits, &u1, s);
+        if (e != hipSuccess) return e;
+        const uint32_t *k2 = u1 ? ws.keys1 : ws.keys0;
+        const int32_t *uo = u1 ? ws.uvals1 : ws.uvals0;
+        if (k2 != ws.ukey2 || uo != ws.uorder) return hipErrorInvalidValue;
+        RunOp rop{k2, ws};
+        e = run_scan(rop, ws.part, scan_blocks(nnz), s);
+        if (e != hipSuccess) return e;
+        TileOp top{ws};
+        e = run_scan(top, ws.part, scan_blocks(nnz), s);
+        if (e != hipSuccess) return e;
+        ChunkOp cop{ws, p.chunk_rows};
+        e = run_scan(cop, ws.part, scan_blocks(nnz), s);
+        if (e != hipSuccess) return e;
+    }
+    return hipGetLastError();
+}
+
+} // namespace ttemb

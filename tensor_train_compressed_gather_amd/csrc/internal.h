@@ -1,0 +1,160 @@
+// internal.h -- shared definitions of the gfx950 TT-EmbeddingBag library.
+//
+// Data layout in device memory (all caller-owned except the table
+// descriptors):
+//   cores     fp32 [n_k][R_{k-1}][d_k][R_k] per table and core
+//   indices   int64 [nnz], offsets int64 [T*B+1] (table-major CSR)
+//   out       fp32 [B][sum_t D_t]
+//   workspace one caller buffer carved into the regions of WsLayout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace ttemb {
+
+constexpr int kMaxTables = 64;
+constexpr int kThreads = 256;       // threads per block for every kernel
+constexpr int kScanBlocks = 1024;   // blocks of the 3-phase scans
+constexpr int kSortTile = 4096;     // keys per radix-sort block (256 threads x 16)
+constexpr int kSortItems = kSortTile / kThreads;
+constexpr int kMaxCkptSlots = 4096; // L2 checkpoint slots for split prefix tiles
+constexpr int kUnitsPerTile = 4;    // prefix units sharing (table, i2) per tile
+constexpr int kGuPiece = 256;       // lookups per piece of a gradient gather run
+
+// Control words at the head of the workspace.
+enum CtrlSlot {
+    CTRL_ERR = 0,     // error bits (ERRB_*)
+    CTRL_U = 1,       // unique rows
+    CTRL_G = 2,       // prefix groups
+    CTRL_UNITS = 3,   // work units (groups, or unique rows in UNIQUE_ONLY mode)
+    CTRL_RUNS = 4,    // runs of units sharing (table, i2)
+    CTRL_TILES = 5,   // tiles of <= 4 units
+    CTRL_CHUNKS = 6,  // forward work chunks
+    CTRL_SPLIT = 7,   // tiles split over several chunks
+    CTRL_PIECES = 8,  // pieces of the backward gradient gather
+    CTRL_STEALS = 9,  // chunks taken from another block's range (statistics)
+    CTRL_CKPT_HIT = 10,  // split-tile chunks that found a published checkpoint
+    CTRL_CKPT_MISS = 11, // split-tile chunks that recomputed the prefix tile
+    CTRL_N = 64
+};
+enum ErrBits { ERRB_INDEX = 1, ERRB_OFFSETS = 2 };
+
+// Per-table descriptor, copied to the device at create time.
+struct TableDesc {
+    int64_t N;
+    int32_t n1, n2, n3;
+    int32_t d1, d2, d3;
+    int32_t R1, R2;
+    int32_t D;
+    int32_t col_off;   // first column of this table in out
+    uint32_t key_base; // sum of N over earlier tables (sort key = key_base + row)
+    uint32_t i1_base;  // sum of n1 over earlier tables
+    uint32_t i2_base;  // sum of n2 over earlier tables
+    uint32_t i3_base;  // sum of n3 over earlier tables
+    int32_t cls;       // MFMA rank class (0: R=8, 1: 16, 2: 32, 3: 64) or -1
+    int32_t Dp;        // row stride of the unique-row buffer E (D rounded up to 4)
+};
+
+struct CorePtrs {
+    const float *g[kMaxTables][3];
+};
+struct GradPtrs {
+    float *g[kMaxTables][3];
+};
+
+// Device views of the workspace regions (filled by the host plan).
+struct Ws {
+    int32_t *ctrl;
+    uint32_t *keys0, *keys1;
+    int32_t *vals0, *vals1;
+    uint32_t *hist;     // radix histograms [radix][blocks]
+    uint64_t *part;     // scan partials [kScanBlocks + 1]
+    int32_t *tstart;    // [T+1] first lookup of each table (clamped offsets[t*B])
+    // canonical grouping
+    uint32_t *skeys;    // sorted keys [nnz]
+    int32_t *perm;      // sorted positions [nnz]
+    int32_t *inv;       // [nnz]
+    uint32_t *ukey;     // key of each unique row [nnz]
+    int32_t *uniq_row;  // [nnz]
+    int32_t *uniq_start;// [nnz+1]
+    int32_t *grp_prefix;// [nnz]
+    int32_t *grp_start; // [nnz+1]
+    int32_t *tab_uniq_start; // [T+1]
+    int32_t *tab_grp_start;  // [T+1]
+    int64_t *ebase;     // [T] element offset of table t's unique rows in E, minus tab_uniq_start*D
+    int64_t *p3base;    // [T] same for the backward G3 partials
+    int64_t *g1base;    // [T] same for the backward G1 partials (per unit)
+    // work units and the B-stationary work list
+    int32_t *unit_prefix;    // [nnz]   (aliases grp_prefix in PREFIX mode)
+    int32_t *unit_start;     // [nnz+1] (aliases grp_start in PREFIX mode)
+    int32_t *tab_unit_start; // [T+1]
+    uint32_t *ukey2;         // sorted (i2_base + i2) of units [nnz]
+    int32_t *uorder;         // units in (table, i2, i1) order [nnz]
+    int32_t *run_start;      // [nnz+1] into uorder
+    int32_t *run_tile_start; // [nnz+1]
+    int32_t *tile_ubeg;      // [nnz] into uorder
+    int32_t *tile_nu;        // [nnz]
+    int32_t *tile_rows;      // [nnz]
+    int32_t *tile_slot;      // [nnz] checkpoint slot or -1
+    int32_t *chunk_tile;     // [2*nnz]
+    int32_t *chunk_rbeg;     // [2*nnz]
+    int32_t *chunk_rend;     // [2*nnz]
+    int32_t *heads;          // [num_blocks] queue heads
+    int32_t *flags;          // [kMaxCkptSlots] checkpoint ready flags
+    float *ckpt;             // [kMaxCkptSlots][4][16][max R2 + 4]
+    float *E;                // unique rows, per-table segments
+    // backward
+    int32_t *bag_of;         // [nnz]
+    int32_t *piece_u;        // [nnz] unique row of each gather piece
+    int32_t *piece_k;        // [nnz] first sorted position of each piece
+    int32_t *u_piece_start;  // [nnz+1] first piece of each unique row
+    float *piece_sum;        // [nnz/kGuPiece + U][Dmax] partial sums of split runs
+    float *P3;               // per-unique-row G3 partials
+    float *G1P;              // per-unit G1 partials
+    uint32_t *key3;          // sorted (i3_base + i3) of unique rows
+    int32_t *u3order;        // unique rows in (table, i3, unique id) order
+    // sort buffers of the unit order (kept apart from the canonical perm)
+    int32_t *uvals0, *uvals1;
+    int32_t *uvals_free; // the unit-sort value buffer that does not hold uorder
+};
+
+struct Plan {
+    int32_t T;
+    int64_t B, nnz;
+    int num_blocks;
+    int sched_mode, group_mode, chunk_rows, check_indices, force_generic;
+    bool any_generic;
+    int key_bits, key2_bits, key3_bits;
+    int Dmax, R2max, sumD;
+    int sum_n[3]; // sum over tables of n1, n2, n3
+    const TableDesc *dtab; // device copy
+    Ws ws;
+};
+
+// ----------------------------------------------------------------- kernels
+// Grouping (group.hip)
+hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t *offsets,
+                           hipStream_t s);
+// Forward contraction and pooling (forward.hip)
+hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *offsets, float *out,
+                          hipStream_t s);
+// Backward (backward.hip)
+hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs &cores,
+                           const int64_t *offsets, const GradPtrs &grads, hipStream_t s);
+// SGD and fills (misc.hip)
+hipError_t launch_sgd(float *g, const float *dg, int64_t count, float lr, hipStream_t s);
+hipError_t launch_fill_i32(int32_t *p, int32_t v, int64_t count, hipStream_t s);
+hipError_t launch_fill_f32(float *p, float v, int64_t count, hipStream_t s);
+
+// Shared radix sort of (u32 key, i32 value) pairs; n is an upper bound known on
+// the host, n_dev (optional) the actual count on the device.
+hipError_t radix_sort_pairs(const Plan &p, uint32_t *k0, int32_t *v0, uint32_t *k1, int32_t *v1,
+                            int64_t n_max, const int32_t *n_dev, int bits, bool *result_in_1,
+                            hipStream_t s);
+
+inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+} // namespace ttemb

@@ -1,0 +1,180 @@
+// primitives.h -- wave/block scans and a 3-phase device-wide scan (gfx950, wave64).
+#pragma once
+
+#include "internal.h"
+
+namespace ttemb {
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Inclusive scan inside one 64-lane wave.
+template <class T>
+__device__ __forceinline__ T wave_inclusive_scan(T x)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        T y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+template <class T>
+__device__ __forceinline__ T wave_sum(T x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// Exclusive scan over a 256-thread block; smem holds 4 entries.
+template <class T>
+__device__ __forceinline__ T block_exclusive_scan(T v, T *total, T *smem)
+{
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    T x = wave_inclusive_scan(v);
+    if (lane == 63) smem[w] = x;
+    __syncthreads();
+    T wpre = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) {
+        T s = smem[i];
+        if (i < w) wpre += s;
+        tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return wpre + x - v;
+}
+
+// 3-phase exclusive scan.  Op provides
+//   int64_t count() const;                       number of elements (may read device memory)
+//   uint64_t value(int64_t i) const;             element i (called twice: phases 1 and 3)
+//   void emit(int64_t i, uint64_t excl, uint64_t v) const;   phase 3 output
+//   void total(uint64_t tot, int64_t n) const;   called once with the grand total
+// Every block owns one contiguous range, so emit() sees elements in order per block.
+constexpr int kScanItems = 4;
+
+__device__ __forceinline__ void scan_range(int64_t n, int64_t *lo, int64_t *hi)
+{
+    const int64_t tile = (int64_t)kThreads * kScanItems;
+    int64_t per = (n + gridDim.x - 1) / gridDim.x;
+    per = (per + tile - 1) / tile * tile;
+    *lo = (int64_t)blockIdx.x * per;
+    *hi = *lo + per < n ? *lo + per : n;
+}
+
+template <class Op>
+__global__ __launch_bounds__(kThreads) void scan_phase1(Op op, uint64_t *part)
+{
+    __shared__ uint64_t sm[kThreads / 64];
+    const int64_t n = op.count();
+    int64_t lo, hi;
+    scan_range(n, &lo, &hi);
+    uint64_t s = 0;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) s += op.value(i);
+    s = wave_sum(s);
+    if (lane_id() == 0) sm[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t t = 0;
+        for (int i = 0; i < kThreads / 64; ++i) t += sm[i];
+        part[blockIdx.x] = t;
+    }
+}
+
+// One block of 1024 threads scans the nparts (<= 1024) partials.
+template <class Op>
+__global__ __launch_bounds__(1024) void scan_phase2(Op op, uint64_t *part, int nparts)
+{
+    __shared__ uint64_t sm[16];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    uint64_t v = tid < nparts ? part[tid] : 0;
+    uint64_t x = wave_inclusive_scan(v);
+    if (lane == 63) sm[w] = x;
+    __syncthreads();
+    uint64_t wpre = 0, tot = 0;
+    for (int i = 0; i < 16; ++i) {
+        if (i < w) wpre += sm[i];
+        tot += sm[i];
+    }
+    if (tid < nparts) part[tid] = wpre + x - v;
+    if (tid == 0) op.total(tot, op.count());
+}
+
+template <class Op>
+__global__ __launch_bounds__(kThreads) void scan_phase3(Op op, const uint64_t *part)
+{
+    __shared__ uint64_t sm[kThreads / 64];
+    const int64_t n = op.count();
+    int64_t lo, hi;
+    scan_range(n, &lo, &hi);
+    uint64_t carry = part[blockIdx.x];
+    for (int64_t base = lo; base < hi; base += (int64_t)kThreads * kScanItems) {
+        uint64_t v[kScanItems];
+        uint64_t ts = 0;
+#pragma unroll
+        for (int j = 0; j < kScanItems; ++j) {
+            int64_t i = base + (int64_t)threadIdx.x * kScanItems + j;
+            v[j] = i < hi ? op.value(i) : 0;
+            ts += v[j];
+        }
+        uint64_t tot;
+        uint64_t ex = block_exclusive_scan(ts, &tot, sm) + carry;
+#pragma unroll
+        for (int j = 0; j < kScanItems; ++j) {
+            int64_t i = base + (int64_t)threadIdx.x * kScanItems + j;
+            if (i < hi) op.emit(i, ex, v[j]);
+            ex += v[j];
+        }
+        carry += tot;
+    }
+}
+
+template <class Op>
+hipError_t run_scan(const Op &op, uint64_t *part, int blocks, hipStream_t s)
+{
+    if (blocks < 1) blocks = 1;
+    if (blocks > kScanBlocks) blocks = kScanBlocks;
+    hipLaunchKernelGGL(scan_phase1<Op>, dim3(blocks), dim3(kThreads), 0, s, op, part);
+    hipLaunchKernelGGL(scan_phase2<Op>, dim3(1), dim3(1024), 0, s, op, part, blocks);
+    hipLaunchKernelGGL(scan_phase3<Op>, dim3(blocks), dim3(kThreads), 0, s, op, part);
+    return hipGetLastError();
+}
+
+// Blocks for a scan over at most n elements.
+inline int scan_blocks(int64_t n)
+{
+    int64_t b = (n + 16 * kThreads - 1) / (16 * kThreads);
+    if (b < 1) b = 1;
+    if (b > kScanBlocks) b = kScanBlocks;
+    return (int)b;
+}
+
+// Table of a sort key: largest t with key_base[t] <= key.
+__device__ __forceinline__ int table_of_key(const TableDesc *tab, int T, uint32_t key)
+{
+    int lo = 0, hi = T - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (tab[mid].key_base <= key) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Segment of position k in a start array st[0..T] (st non-decreasing): the
+// largest t < T with st[t] <= k.
+__device__ __forceinline__ int segment_of(const int32_t *st, int T, int64_t k)
+{
+    int lo = 0, hi = T - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (st[mid] <= k) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+} // namespace ttemb

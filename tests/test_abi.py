@@ -1,0 +1,97 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point the header declares, and rejects bad shapes before touching
+the device."""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import tensor_train_compressed_gather_amd as tt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "tt_emb.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tt_emb_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = _header_functions()
+    assert "tt_emb_forward" in names and "tt_emb_backward" in names
+    L = tt.lib()
+    for name in names:
+        assert hasattr(L, name), name
+    assert sorted(names) == sorted(tt.EXPORTED)
+
+
+def test_status_strings():
+    for code in range(-7, 1):
+        s = tt.tt_emb_status_string(code)
+        assert s and s != "unknown status"
+    assert tt.tt_emb_status_string(-99) == "unknown status"
+
+
+def _create(N, n, d, R, opt=None):
+    h = C.c_void_p()
+    NN = np.asarray(N, np.int64)
+    nn = np.asarray(n, np.int32).reshape(-1)
+    dd = np.asarray(d, np.int32).reshape(-1)
+    RR = np.asarray(R, np.int32).reshape(-1)
+    rc = tt.lib().tt_emb_create(len(NN), NN.ctypes.data, nn.ctypes.data, dd.ctypes.data, RR.ctypes.data,
+                                C.byref(opt) if opt is not None else None, C.byref(h))
+    return rc, h
+
+
+@pytest.mark.parametrize("N,n,d,R,code", [
+    ([1000], [10, 10, 10], [2, 2, 4], [2, 8, 8, 1], tt.TT_EMB_ERR_ARG),      # R0 != 1
+    ([1000], [10, 10, 10], [2, 2, 4], [1, 8, 8, 2], tt.TT_EMB_ERR_ARG),      # R3 != 1
+    ([1001], [10, 10, 10], [2, 2, 4], [1, 8, 8, 1], tt.TT_EMB_ERR_ARG),      # n1 n2 n3 < N
+    ([0], [10, 10, 10], [2, 2, 4], [1, 8, 8, 1], tt.TT_EMB_ERR_ARG),         # empty table
+    ([1000], [10, 10, 10], [0, 2, 4], [1, 8, 8, 1], tt.TT_EMB_ERR_ARG),      # zero dim
+    ([1000], [10, 10, 10], [16, 16, 8], [1, 8, 8, 1], tt.TT_EMB_ERR_UNSUPPORTED),  # D > 1024
+    ([1000], [10, 10, 10], [2, 2, 4], [1, 512, 8, 1], tt.TT_EMB_ERR_UNSUPPORTED),  # rank > 256
+    ([2 ** 31], [2 ** 11, 2 ** 10, 2 ** 10], [2, 2, 4], [1, 8, 8, 1], tt.TT_EMB_ERR_UNSUPPORTED),
+])
+def test_create_rejects_bad_shapes_before_touching_the_device(N, n, d, R, code):
+    rc, h = _create(N, n, d, R)
+    assert rc == code
+    assert not h.value
+
+
+def test_create_rejects_bad_options():
+    opt = tt.tt_emb_options()
+    opt.sched_mode = 7
+    rc, _ = _create([1000], [10, 10, 10], [2, 2, 4], [1, 8, 8, 1], opt)
+    assert rc == tt.TT_EMB_ERR_ARG
+    opt = tt.tt_emb_options()
+    opt.chunk_rows = 5000
+    rc, _ = _create([1000], [10, 10, 10], [2, 2, 4], [1, 8, 8, 1], opt)
+    assert rc == tt.TT_EMB_ERR_ARG
+    rc = tt.lib().tt_emb_create(65, None, None, None, None, None, C.byref(C.c_void_p()))
+    assert rc == tt.TT_EMB_ERR_ARG
+
+
+def test_null_handles_are_rejected():
+    L = tt.lib()
+    out = C.c_size_t()
+    assert L.tt_emb_workspace_size(None, 1, 1, C.byref(out)) == tt.TT_EMB_ERR_ARG
+    assert L.tt_emb_forward(None, None, None, None, 1, 1, None, None, 0, 0, None) == tt.TT_EMB_ERR_ARG
+    assert L.tt_emb_backward(None, None, None, None, None, 1, 1, None, None, 0, 0, None) == tt.TT_EMB_ERR_ARG
+    assert L.tt_emb_sgd_update(None, None, None, C.c_float(0.1), None) == tt.TT_EMB_ERR_ARG
+    assert L.tt_emb_poll_error(None, None, None) == tt.TT_EMB_ERR_ARG
+    assert L.tt_emb_destroy(None) == tt.TT_EMB_OK
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "tensor_train_compressed_gather_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "tt_oracle" not in text and "liboracle" not in text, f
