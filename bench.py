@@ -1,0 +1,271 @@
+#!/usr/bin/env python
+"""Throughput of the TT-EmbeddingBag hot path on one MI355X.
+
+One step = the whole hot path on one batch: index grouping (validation, sort,
+unique extraction, prefix run-length encoding, work list), the fused
+prefix-shared forward contraction, bag pooling, the backward to every TT core
+and the in-place SGD update (lr 0.01), on the 26-table workload at batch
+32,768 (rows log-uniform in [1e3, 4e7], D = 64, ranks in {16, 32, 64},
+Poisson(20)+1 bag lengths, per-table Zipf skew).  Inputs are seeded and
+synthetic and resident in HBM before the timed region.
+
+Prints one JSON line.  Forward-only throughput of the same 26-table workload
+and of the 10^7-row D = 128 workload are reported alongside, with the phase
+breakdown measured by the library's HIP-event timers on the launch stream.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "pooled TT-embedding lookups/sec at batch 32768 (fwd, fwd+bwd); % of roofline"
+PEAK_FP32_TFLOPS = 157.3   # MI355X dense FP32 (matrix cores; also the vector figure)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def phase_flops(tabs, U_r, U_p, nnz_t):
+    """Algorithmic flops of the contraction phases (prefix reuse counted once)."""
+    fwd = bwd = pool = 0.0
+    for tb, ur, up, nz in zip(tabs, U_r, U_p, nnz_t):
+        d1, d2, d3 = tb.d
+        R1, R2 = tb.R[1], tb.R[2]
+        D = d1 * d2 * d3
+        step1 = 2.0 * d1 * R1 * d2 * R2
+        step2 = 2.0 * D * R2
+        fwd += up * step1 + ur * step2
+        # recompute C, dG1 and dG2 per unit; dC and the dG3 term per unique row
+        bwd += up * 3 * step1 + ur * 2 * step2
+        pool += nz * D
+    return fwd, bwd, pool
+
+
+def phase_bytes(w, U_r):
+    """Compulsory HBM bytes of pooling: read each unique row once, the inverse
+    map and offsets, write the pooled output."""
+    e = sum(ur * tb.D * 4 for tb, ur in zip(w.tables, U_r))
+    return e + 4 * w.nnz + 8 * (w.T * w.B + 1) + 4 * w.B * w.sum_D
+
+
+def kernel_sources_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "tensor_train_compressed_gather_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload, sha):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get(kernel, {})
+    if r.get("workload") != workload or r.get("src_sha") != sha:
+        return None
+    return r.get("bytes_per_launch")
+
+
+class Bench:
+    def __init__(self, w, torch, tt, options=None):
+        self.w, self.torch, self.tt = w, torch, tt
+        dev = "cuda"
+        self.emb = tt.TTEmbeddingBag(w.tables, dev, options)
+        self.cores = [torch.from_numpy(c).to(dev) for c in w.cores]
+        self.idx = torch.from_numpy(w.indices).to(dev)
+        self.off = torch.from_numpy(w.offsets).to(dev)
+        self.out = torch.empty((w.B, w.sum_D), dtype=torch.float32, device=dev)
+        self.grads = [torch.empty_like(c) for c in self.cores]
+        self.gout = torch.from_numpy(w.grad_out).to(dev) if w.grad_out is not None else None
+        self.emb.workspace(w.B, w.nnz)
+
+    def fwd(self):
+        self.emb.forward(self.cores, self.idx, self.off, self.w.B, out=self.out)
+
+    def train_step(self):
+        self.emb.forward(self.cores, self.idx, self.off, self.w.B, out=self.out)
+        self.emb.backward(self.gout, self.cores, self.idx, self.off, self.w.B, core_grads=self.grads,
+                          flags=self.tt.TT_EMB_REUSE_GROUPING)
+        self.emb.sgd_update(self.cores, self.grads, self.w.lr)
+
+    def timed(self, fn, steps, warmup):
+        torch, tt = self.torch, self.tt
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        tt.tt_emb_timing_read(self.emb.handle)          # clear
+        tt.tt_emb_timing_enable(self.emb.handle, True)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        tt.tt_emb_timing_enable(self.emb.handle, False)
+        phases = tt.tt_emb_timing_read(self.emb.handle)
+        assert self.emb.poll_error() == 0
+        return ev0.elapsed_time(ev1) / steps, wall, phases
+
+    def counts(self):
+        g = self.emb.grouping(self.w.B, self.w.nnz)
+        tu = g["tab_uniq_start"].cpu().numpy()
+        tg = g["tab_grp_start"].cpu().numpy()
+        offs = self.w.offsets[:: self.w.B]
+        return [int(x) for x in tu[1:] - tu[:-1]], [int(x) for x in tg[1:] - tg[:-1]], \
+            [int(x) for x in offs[1:] - offs[:-1]], g["counts"]
+
+
+def cpu_baseline(w, target_s=12.0):
+    """The oracle (per-index fp64 contraction, no reuse) on the host cores, on
+    the first S bags of every table, forward + backward when the workload has
+    output gradients."""
+    import numpy as np
+
+    import oracle
+    from tensor_train_compressed_gather_amd import workloads as W
+
+    def sub(S):
+        lens, idx = [], []
+        for t in range(w.T):
+            lo, hi = w.offsets[t * w.B], w.offsets[t * w.B + S]
+            lens.append(np.diff(w.offsets[t * w.B: t * w.B + S + 1]))
+            idx.append(w.indices[lo:hi])
+        s = W.make_custom(w.tables, lens, idx, cores=w.cores)
+        if w.grad_out is not None:
+            s.grad_out = np.ascontiguousarray(w.grad_out[:S])
+        return s
+
+    def run(s):
+        t0 = time.perf_counter()
+        oracle.forward(s)
+        if s.grad_out is not None:
+            oracle.backward(s)
+        return time.perf_counter() - t0
+
+    S = 4
+    s = sub(S)
+    t = run(s)
+    for _ in range(3):  # grow the sample until it takes about target_s
+        if t >= 0.5 * target_s or S >= w.B:
+            break
+        S = int(min(w.B, max(2 * S, S * target_s / max(t, 1e-3))))
+        s = sub(S)
+        t = run(s)
+    kind = "fwd+bwd" if s.grad_out is not None else "fwd"
+    return {"value": s.nnz / t, "unit": "lookups/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"first {S} of {w.B} bags of each of the {w.T} tables ({s.nnz} lookups), "
+                      f"{kind}, per-index fp64, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
+    ap.add_argument("--sched", type=int, default=0, help="0 default, 1 static, 2 steal, 3 steal+L2")
+    ap.add_argument("--group", type=int, default=0, help="0 default, 1 prefix, 2 unique-only")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tensor_train_compressed_gather_amd as tt
+    from tensor_train_compressed_gather_amd import workloads as W
+
+    opts = None
+    if args.sched or args.group:
+        opts = tt.tt_emb_options()
+        opts.sched_mode = args.sched
+        opts.group_mode = args.group
+
+    w = W.make_workload(5)
+    b = Bench(w, torch, tt, opts)
+    ms, wall, ph = b.timed(b.train_step, args.steps, args.warmup)
+    U_r, U_p, nnz_t, cnt = b.counts()
+    F_fwd, F_bwd, F_pool = phase_flops(w.tables, U_r, U_p, nnz_t)
+    value = w.nnz / (ms * 1e-3)
+    phases = {k: round(v[0] / max(v[1], 1), 4) for k, v in ph.items() if v[1]}
+    # dominant kernel of the step and its roofline
+    dom = max(phases, key=phases.get)
+    wl = W.CONFIG_NAMES[5]
+    if dom in ("contract", "bwd_contract"):
+        flops = F_fwd if dom == "contract" else F_bwd
+        src = "forward.hip" if dom == "contract" else "backward.hip"
+        achieved = flops / (phases[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma" if dom == "contract" else "alu", "achieved": achieved,
+                "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
+                "algorithmic": flops,
+                "traffic": load_traffic(dom, wl, kernel_sources_sha([src]))}
+    else:
+        byts = phase_bytes(w, U_r)
+        achieved = byts / (phases[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "algorithmic": byts, "traffic": None}
+    res = {
+        "metric": METRIC, "value": value, "unit": "lookups/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl, "step": "group+fwd+bwd+sgd", "tables": w.T, "batch": w.B, "nnz": w.nnz,
+                   "unique_rows": sum(U_r), "prefix_groups": sum(U_p), "sched": args.sched,
+                   "group": args.group, "wall_s": wall},
+        "phases_ms": phases,
+        "flops": {"fwd_contract": F_fwd, "bwd_contract": F_bwd, "pool_adds": F_pool},
+        "sched_stats": cnt,
+        "roofline": roof,
+    }
+    del b
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        fwd = {}
+        for cfg in (4, 3):
+            wf = W.make_workload(cfg)
+            bf = Bench(wf, torch, tt, opts)
+            fms, _, fph = bf.timed(bf.fwd, args.steps, args.warmup)
+            ur, up, nz, fc = bf.counts()
+            ff, _, _ = phase_flops(wf.tables, ur, up, nz)
+            fphase = {k: round(v[0] / max(v[1], 1), 4) for k, v in fph.items() if v[1]}
+            post = fphase.get("contract", 0) + fphase.get("pool", 0)
+            cms = fphase.get("contract", 0)
+            fwd[W.CONFIG_NAMES[cfg]] = {
+                "lookups_per_s": wf.nnz / (fms * 1e-3), "ms": fms,
+                "post_grouping_ms": post, "post_grouping_lookups_per_s": wf.nnz / (post * 1e-3) if post else None,
+                "phases_ms": fphase, "nnz": wf.nnz, "unique_rows": sum(ur), "prefix_groups": sum(up),
+                "contract_tflops": ff / (cms * 1e-3) / 1e12 if cms else None,
+                "contract_frac_fp32_peak": ff / (cms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS if cms else None,
+                "roofline_ms_fp32": ff / (PEAK_FP32_TFLOPS * 1e12) * 1e3,
+                "post_grouping_frac_of_roofline": (ff / (PEAK_FP32_TFLOPS * 1e12) * 1e3) / post if post else None,
+                "sched_stats": fc,
+            }
+            del bf
+            torch.cuda.empty_cache()
+        res["fwd"] = fwd
+
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -172,6 +172,33 @@ int tt_emb_poll_error(tt_emb_t h, const void *ws, void *stream);
 /* Static text for a status code. */
 const char *tt_emb_status_string(int status);
 
+/* Phase timers (tracing of the grouping / contraction / pooling / backward
+ * breakdown the FlowTT page reports in section 4).  When enabled, every call
+ * records a pair of hipEvents around each phase on the caller's stream. */
+enum {
+    TT_EMB_TIMER_GROUP_SORT = 0, /* validation, key build and radix sort */
+    TT_EMB_TIMER_GROUP_RLE,      /* unique extraction, prefix RLE, work list */
+    TT_EMB_TIMER_CONTRACT,       /* fused prefix-shared contraction (E rows) */
+    TT_EMB_TIMER_POOL,           /* bag pooling */
+    TT_EMB_TIMER_BWD_GATHER,     /* per-row output-gradient gather */
+    TT_EMB_TIMER_BWD_CONTRACT,   /* reverse contraction per (table, i2) run */
+    TT_EMB_TIMER_BWD_REDUCE,     /* fixed-order dG1 / dG3 reductions */
+    TT_EMB_TIMER_SGD,            /* in-place SGD update */
+    TT_EMB_NUM_TIMERS
+};
+
+/* enable != 0 creates the events (up to 1024 calls are kept per timer);
+ * enable == 0 stops recording.  Host-side only; allocates events. */
+int tt_emb_timing_enable(tt_emb_t h, int32_t enable);
+
+/* Synchronise the device, then add up the recorded intervals:
+ * ms[TT_EMB_NUM_TIMERS] total milliseconds, count[TT_EMB_NUM_TIMERS] recorded
+ * intervals per timer (either pointer may be NULL); clears the records. */
+int tt_emb_timing_read(tt_emb_t h, double *ms, int32_t *count);
+
+/* Static name of a timer id (NULL if out of range). */
+const char *tt_emb_timer_name(int32_t id);
+
 #ifdef __cplusplus
 }
 #endif

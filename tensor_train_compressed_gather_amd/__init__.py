@@ -31,8 +31,10 @@ TT_EMB_REUSE_GROUPING = 1
 EXPORTED = (
     "tt_emb_create", "tt_emb_destroy", "tt_emb_workspace_size", "tt_emb_group", "tt_emb_forward",
     "tt_emb_backward", "tt_emb_sgd_update", "tt_emb_grouping_view", "tt_emb_poll_error",
-    "tt_emb_status_string",
+    "tt_emb_status_string", "tt_emb_timing_enable", "tt_emb_timing_read", "tt_emb_timer_name",
 )
+TIMER_NAMES = ("group_sort", "group_rle", "contract", "pool", "bwd_gather", "bwd_contract",
+               "bwd_reduce", "sgd")
 
 
 class tt_emb_options(C.Structure):
@@ -76,8 +78,12 @@ def lib():
             L.tt_emb_poll_error.argtypes = [p, p, p]
             L.tt_emb_status_string.argtypes = [C.c_int]
             L.tt_emb_status_string.restype = C.c_char_p
+            L.tt_emb_timing_enable.argtypes = [p, i32]
+            L.tt_emb_timing_read.argtypes = [p, p, p]
+            L.tt_emb_timer_name.argtypes = [i32]
+            L.tt_emb_timer_name.restype = C.c_char_p
             for name in EXPORTED:
-                if name != "tt_emb_status_string":
+                if name not in ("tt_emb_status_string", "tt_emb_timer_name"):
                     getattr(L, name).restype = C.c_int
             _lib = L
     return _lib
@@ -200,6 +206,24 @@ def tt_emb_grouping_view(h, ws, B: int, nnz: int, T: int, stream=None) -> dict:
                                                     "num_chunks", "num_split_tiles", "num_steals",
                                                     "num_ckpt_hits", "num_ckpt_misses")},
     }
+
+
+def tt_emb_timing_enable(h, enable: bool = True):
+    _check(lib().tt_emb_timing_enable(h, 1 if enable else 0), "tt_emb_timing_enable")
+
+
+def tt_emb_timing_read(h) -> dict:
+    """Synchronises; returns {timer name: (total ms, intervals)} and clears."""
+    n = len(TIMER_NAMES)
+    ms = (C.c_double * n)()
+    cnt = (C.c_int32 * n)()
+    _check(lib().tt_emb_timing_read(h, ms, cnt), "tt_emb_timing_read")
+    return {TIMER_NAMES[i]: (float(ms[i]), int(cnt[i])) for i in range(n)}
+
+
+def tt_emb_timer_name(i: int):
+    r = lib().tt_emb_timer_name(int(i))
+    return None if r is None else r.decode()
 
 
 class TTEmbeddingBag:

@@ -9,7 +9,31 @@
 
 using namespace ttemb;
 
+namespace ttemb {
+// Rings of (start, stop) event pairs, one ring per phase timer.
+struct Timing {
+    static constexpr int kRing = 1024;
+    std::vector<hipEvent_t> ev[TM_COUNT][2];
+    int used[TM_COUNT] = {};
+    bool on = false;
+};
+
+void timer_begin(Timing *tm, int id, hipStream_t s)
+{
+    if (!tm || !tm->on || tm->used[id] >= Timing::kRing) return;
+    (void)hipEventRecord(tm->ev[id][0][tm->used[id]], s);
+}
+
+void timer_end(Timing *tm, int id, hipStream_t s)
+{
+    if (!tm || !tm->on || tm->used[id] >= Timing::kRing) return;
+    (void)hipEventRecord(tm->ev[id][1][tm->used[id]], s);
+    ++tm->used[id];
+}
+} // namespace ttemb
+
 struct tt_emb {
+    Timing *timing = nullptr;
     int32_t T;
     std::vector<TableDesc> tabs;
     TableDesc *dtab = nullptr;
@@ -125,6 +149,7 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.uvals_free = fu ? w.uvals0 : w.uvals1;
     w.key3 = nullptr;
     if (p) {
+        p->timing = (h->timing && h->timing->on) ? h->timing : nullptr;
         p->T = T;
         p->B = B;
         p->nnz = nnz;
@@ -301,10 +326,21 @@ int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const in
     }
 }
 
+static void free_timing(tt_emb *h)
+{
+    if (!h->timing) return;
+    for (int id = 0; id < TM_COUNT; ++id)
+        for (int k = 0; k < 2; ++k)
+            for (hipEvent_t e : h->timing->ev[id][k]) (void)hipEventDestroy(e);
+    delete h->timing;
+    h->timing = nullptr;
+}
+
 int tt_emb_destroy(tt_emb_t h)
 {
     if (!h) return TT_EMB_OK;
     int rc = TT_EMB_OK;
+    free_timing(h);
     if (h->dtab && hipFree(h->dtab) != hipSuccess) rc = TT_EMB_ERR_HIP;
     delete h;
     return rc;
@@ -402,6 +438,8 @@ int tt_emb_sgd_update(tt_emb_t h, float *const *cores, const float *const *core_
     int rc = set_device(h);
     if (rc) return rc;
     hipStream_t s = (hipStream_t)stream;
+    Timing *tm = (h->timing && h->timing->on) ? h->timing : nullptr;
+    timer_begin(tm, TM_SGD, s);
     for (int t = 0; t < h->T; ++t) {
         const TableDesc &d = h->tabs[t];
         const int64_t cnt[3] = {(int64_t)d.n1 * d.d1 * d.R1, (int64_t)d.n2 * d.R1 * d.d2 * d.R2,
@@ -411,7 +449,66 @@ int tt_emb_sgd_update(tt_emb_t h, float *const *cores, const float *const *core_
             if (e != hipSuccess) return TT_EMB_ERR_HIP;
         }
     }
+    timer_end(tm, TM_SGD, s);
     return TT_EMB_OK;
+}
+
+int tt_emb_timing_enable(tt_emb_t h, int32_t enable)
+{
+    if (!h) return TT_EMB_ERR_ARG;
+    try {
+        if (!enable) {
+            if (h->timing) h->timing->on = false;
+            return TT_EMB_OK;
+        }
+        int rc = set_device(h);
+        if (rc) return rc;
+        if (!h->timing) {
+            h->timing = new Timing();
+            for (int id = 0; id < TM_COUNT; ++id)
+                for (int k = 0; k < 2; ++k) {
+                    h->timing->ev[id][k].resize(Timing::kRing);
+                    for (auto &e : h->timing->ev[id][k])
+                        if (hipEventCreate(&e) != hipSuccess) {
+                            free_timing(h);
+                            return TT_EMB_ERR_HIP;
+                        }
+                }
+        }
+        h->timing->on = true;
+        return TT_EMB_OK;
+    } catch (...) {
+        return TT_EMB_ERR_NOMEM;
+    }
+}
+
+int tt_emb_timing_read(tt_emb_t h, double *ms, int32_t *count)
+{
+    if (!h) return TT_EMB_ERR_ARG;
+    int rc = set_device(h);
+    if (rc) return rc;
+    if (hipDeviceSynchronize() != hipSuccess) return TT_EMB_ERR_HIP;
+    for (int id = 0; id < TM_COUNT; ++id) {
+        double tot = 0.0;
+        int n = h->timing ? h->timing->used[id] : 0;
+        for (int k = 0; k < n; ++k) {
+            float x = 0.f;
+            if (hipEventElapsedTime(&x, h->timing->ev[id][0][k], h->timing->ev[id][1][k]) != hipSuccess)
+                return TT_EMB_ERR_HIP;
+            tot += x;
+        }
+        if (ms) ms[id] = tot;
+        if (count) count[id] = n;
+        if (h->timing) h->timing->used[id] = 0;
+    }
+    return TT_EMB_OK;
+}
+
+const char *tt_emb_timer_name(int32_t id)
+{
+    static const char *names[TM_COUNT] = {"group_sort", "group_rle", "contract", "pool",
+                                          "bwd_gather", "bwd_contract", "bwd_reduce", "sgd"};
+    return (id >= 0 && id < TM_COUNT) ? names[id] : nullptr;
 }
 
 int tt_emb_grouping_view(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B, int64_t nnz, void *stream,

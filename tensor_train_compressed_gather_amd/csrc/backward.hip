@@ -324,6 +324,7 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
     BwdArgs a{p.dtab, p.T, p.B, p.ws, cores, grads, grad_out, offsets, p.nnz, p.sumD, p.Dmax};
     const int T = p.T;
     const int sum_n1 = p.sum_n[0], sum_n3 = p.sum_n[2];
+    timer_begin(p.timing, TM_BWD_GATHER, s);
     hipLaunchKernelGGL(k_zero_g2, dim3(256, T), dim3(kThreads), 0, s, a);
     if (p.nnz > 0) {
         const int64_t nbags = (int64_t)T * p.B;
@@ -335,8 +336,12 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k_gu_pieces, dim3(4096), dim3(kThreads), 0, s, a);
         hipLaunchKernelGGL(k_gu_combine, dim3(2048), dim3(kThreads), 0, s, a);
-        hipLaunchKernelGGL(k_bwd_runs, dim3(p.num_blocks * 2), dim3(kThreads), 0, s, a);
     }
+    timer_end(p.timing, TM_BWD_GATHER, s);
+    timer_begin(p.timing, TM_BWD_CONTRACT, s);
+    if (p.nnz > 0) hipLaunchKernelGGL(k_bwd_runs, dim3(p.num_blocks * 2), dim3(kThreads), 0, s, a);
+    timer_end(p.timing, TM_BWD_CONTRACT, s);
+    timer_begin(p.timing, TM_BWD_REDUCE, s);
     hipLaunchKernelGGL(k_reduce_g1, dim3(sum_n1 > 0 ? (sum_n1 < 65535 ? sum_n1 : 65535) : 1), dim3(kThreads), 0,
                        s, a, sum_n1);
     // dG3: sort unique rows by (table, i3) into buffers the forward no longer needs
@@ -358,6 +363,7 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
     }
     hipLaunchKernelGGL(k_reduce_g3, dim3(sum_n3 > 0 ? (sum_n3 < 65535 ? sum_n3 : 65535) : 1), dim3(kThreads), 0,
                        s, a, k3, o3, sum_n3);
+    timer_end(p.timing, TM_BWD_REDUCE, s);
     return hipGetLastError();
 }
 

@@ -435,6 +435,7 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
                           hipStream_t s)
 {
     FwdArgs a{p.dtab, p.T, p.ws, cores, p.sched_mode};
+    timer_begin(p.timing, TM_CONTRACT, s);
     if (p.nnz > 0) {
         hipLaunchKernelGGL(k_queue_init, dim3(1), dim3(kThreads), 0, s, p.ws, p.num_blocks);
         if (!p.force_generic)
@@ -443,12 +444,15 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
             hipLaunchKernelGGL(k_contract_generic, dim3(p.num_blocks * 4), dim3(kThreads), 0, s, a,
                                p.force_generic ? 1 : 0);
     }
+    timer_end(p.timing, TM_CONTRACT, s);
+    timer_begin(p.timing, TM_POOL, s);
     const int64_t nbags = (int64_t)p.T * p.B;
     if (nbags > 0) {
         const int64_t g = (nbags + 3) / 4;
         hipLaunchKernelGGL(k_pool, dim3((unsigned)g), dim3(kThreads), 0, s, p.dtab, p.T, p.B, offsets,
                            p.nnz, p.ws, out, p.sumD);
     }
+    timer_end(p.timing, TM_POOL, s);
     return hipGetLastError();
 }
 

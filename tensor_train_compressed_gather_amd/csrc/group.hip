@@ -470,6 +470,7 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
     Ws ws = p.ws;
     const int T = p.T;
     const int64_t nnz = p.nnz, nbags = (int64_t)T * p.B;
+    timer_begin(p.timing, TM_GROUP_SORT, s);
     hipLaunchKernelGGL(k_init_ctrl, dim3(1), dim3(kThreads), 0, s, ws, T);
     {
         int g = ceil_div(nbags > 0 ? nbags : 1, kThreads);
@@ -492,6 +493,8 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
     const int32_t *sv = in1 ? ws.vals1 : ws.vals0;
     // the plan points skeys/perm at the buffers the sort ends in
     if (sk != ws.skeys || sv != ws.perm) return hipErrorInvalidValue;
+    timer_end(p.timing, TM_GROUP_SORT, s);
+    timer_begin(p.timing, TM_GROUP_RLE, s);
     // 2. unique extraction
     if (nnz > 0) {
         UniqueOp uop{sk, sv, ws, nnz};
@@ -531,6 +534,7 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
         e = run_scan(cop, ws.part, scan_blocks(nnz), s);
         if (e != hipSuccess) return e;
     }
+    timer_end(p.timing, TM_GROUP_RLE, s);
     return hipGetLastError();
 }
 

@@ -121,7 +121,16 @@ struct Ws {
     int32_t *uvals_free; // the unit-sort value buffer that does not hold uorder
 };
 
+enum TimerId {
+    TM_GROUP_SORT = 0, TM_GROUP_RLE, TM_CONTRACT, TM_POOL, TM_BWD_GATHER, TM_BWD_CONTRACT,
+    TM_BWD_REDUCE, TM_SGD, TM_COUNT
+};
+struct Timing; // host-side event rings (api.hip)
+void timer_begin(Timing *tm, int id, hipStream_t s);
+void timer_end(Timing *tm, int id, hipStream_t s);
+
 struct Plan {
+    Timing *timing; // nullptr unless phase timing is enabled
     int32_t T;
     int64_t B, nnz;
     int num_blocks;
