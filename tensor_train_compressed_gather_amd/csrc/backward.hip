@@ -35,6 +35,7 @@ struct BwdArgs {
     int64_t nnz;
     int SD;
     int Dmax; // row stride of the gather partials
+    int force_generic;
 };
 
 // bag_of[l] for every lookup (clamped ranges; used only through clamps).
@@ -142,6 +143,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_runs(BwdArgs a)
         const int k0 = ws.run_start[run], k1 = ws.run_start[run + 1];
         const int t = segment_of(ws.tab_unit_start, a.T, ws.uorder[k0]);
         const TableDesc &tb = a.tab[t];
+        if (!a.force_generic && tb.cls >= 0) continue; // matrix-core kernel owns this run
         const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, R1 = tb.R1, R2 = tb.R2, D = tb.D;
         const int D12 = d1 * d2, CN = D12 * R2, G2N = R1 * d2 * R2;
         const int i2 = ws.unit_prefix[ws.uorder[k0]] % tb.n2;
@@ -307,9 +309,332 @@ __global__ __launch_bounds__(kThreads) void k_reduce_g3(BwdArgs a, const uint32_
     }
 }
 
-// Zero every dG2 core (runs overwrite the slices they own).
+// ------------------------------------------------ matrix-core reverse contraction
+//
+// One block per (table, i2) run of a rank class R (R1 = R2 = R, d1, d2 <= 4,
+// d3 <= 16), runs taken from a shared counter.  The G2[i2] slice is staged in
+// LDS once per run with an XOR swizzle (column ^ (row & 31)), so it can be read
+// both along columns (recomputing C and accumulating dG2) and along rows
+// (forming the dG1 partials) without bank conflicts.  Per tile of <= 4 units:
+//   (1) C[(g,j1)][col]  = sum_r1 G1[i1_g][j1][r1] G2[r1][col]          -> LDS
+//   (2) per row u:  dC_g += g_u . G3[i3_u]^T ;  P3_u = C_g^T . g_u     (g_u staged in LDS)
+//   (3) G1P_g[j1][r1]   = sum_col dC[(g,j1)][col] G2[r1][col]           -> partial buffer
+//   (4) dG2[r1][col]   += sum_(g,j1) G1[i1_g][j1][r1] dC[(g,j1)][col]  (registers)
+// where col = j2*R + r2.  All products are v_mfma_f32_16x16x4_f32 tiles.
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBCStride = 68;                   // LDS row stride of C / dC tiles
+constexpr int kBCUnit = 16 * kBCStride + 16;    // floats per unit
+constexpr int kBGs = 8192;                      // floats of staged output-gradient rows
+
+struct BTileCtx {
+    int nu;
+    int unit[4], i1[4], ustart[4], rowoff[5];
+};
+
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int R>
+__device__ __forceinline__ void bwd_run_mfma(const BwdArgs &a, int t, int i2, int k0, int k1, float *G2s,
+                                             float *Cs, float *dCs, float *Gs, BTileCtx *cx)
+{
+    constexpr int NCOL = 4 * R;          // columns (j2, r2) with d2 padded to 4
+    constexpr int NT = NCOL / 16;        // 16-column blocks
+    constexpr int NTW = (NT + 3) / 4;    // blocks per wave
+    constexpr int MT = (R + 15) / 16;    // 16-row blocks of r1 or r2
+    constexpr int KQ = R / 4;            // K values per lane for K = R
+    constexpr int KS = 4 / MT;           // K split of the dG1 partial over waves
+    constexpr int SPL = R / KS;
+    const TableDesc &tb = a.tab[t];
+    const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, n2 = tb.n2, n3 = tb.n3, D12 = d1 * d2, Dp = tb.Dp;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, kq = lane >> 4;
+    const float *G1 = a.cores.g[t][0];
+    const float *G3 = a.cores.g[t][2];
+    const Ws &ws = a.ws;
+
+    {   // stage G2[i2] as G2s[r][col ^ (r & 31)], zero-padded to NCOL columns
+        const float *src = a.cores.g[t][1] + (int64_t)i2 * R * d2 * R;
+        for (int e = tid; e < R * NCOL; e += kThreads) {
+            const int r = e / NCOL, c = e - r * NCOL;
+            G2s[r * NCOL + (c ^ (r & 31))] = c < d2 * R ? src[r * d2 * R + c] : 0.f;
+        }
+    }
+    floatx4 g2acc[MT][NTW];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) g2acc[mt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    for (int k = k0; k < k1; k += 4) {
+        if (tid == 0) {
+            const int nu = k1 - k < 4 ? k1 - k : 4;
+            int off = 0;
+            for (int j = 0; j < 4; ++j) {
+                int unit = 0, i1 = 0, us = 0, cnt = 0;
+                if (j < nu) {
+                    unit = ws.uorder[k + j];
+                    i1 = ws.unit_prefix[unit] / n2;
+                    us = ws.unit_start[unit];
+                    cnt = ws.unit_start[unit + 1] - us;
+                }
+                cx->unit[j] = unit;
+                cx->i1[j] = i1;
+                cx->ustart[j] = us;
+                cx->rowoff[j] = off;
+                off += cnt;
+            }
+            cx->rowoff[4] = off;
+            cx->nu = nu;
+        }
+        __syncthreads();
+        const int nu = cx->nu;
+
+        // ---- (1) prefix tile C of the <= 4 units
+        {
+            const int g = li >> 2, j1 = li & 3;
+            const bool oka = g < nu && j1 < d1;
+            const float *srcA = G1 + ((int64_t)(oka ? cx->i1[g] : 0) * d1 + (oka ? j1 : 0)) * R + kq * KQ;
+            float areg[KQ];
+#pragma unroll
+            for (int s = 0; s < KQ; ++s) areg[s] = oka ? srcA[s] : 0.f;
+            floatx4 acc[NTW];
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KQ; ++s) {
+                const int r = kq * KQ + s;
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    const int ntg = w + 4 * j;
+                    if (ntg < NT) {
+                        const int col = ntg * 16 + li;
+                        acc[j] = mfma4(areg[s], G2s[r * NCOL + (col ^ (r & 31))], acc[j]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int ntg = w + 4 * j;
+                if (ntg < NT) {
+                    const int col = ntg * 16 + li, j2 = col / R, r2 = col % R;
+                    if (j2 < d2) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (v < d1) Cs[kq * kBCUnit + (v * d2 + j2) * kBCStride + r2] = acc[j][v];
+                    }
+                }
+            }
+        }
+
+        // ---- (2) rows: dC accumulation and G3 partials, items (unit g, r2 block mb)
+        floatx4 dacc[MT];
+#pragma unroll
+        for (int ii = 0; ii < MT; ++ii) dacc[ii] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const int nrows = cx->rowoff[4];
+        const int rch = kBGs / Dp;
+        const int P = 16 / d3;
+        for (int q0 = 0; q0 < nrows; q0 += rch) {
+            const int qn = nrows - q0 < rch ? nrows - q0 : rch;
+            __syncthreads(); // C tile complete; previous staged rows consumed
+            {
+                const int c4n = Dp >> 2;
+                for (int e = tid; e < qn * c4n; e += kThreads) {
+                    const int qq = e / c4n, c4 = e - qq * c4n, q = q0 + qq;
+                    int g = 0;
+                    while (g < 3 && q >= cx->rowoff[g + 1]) ++g;
+                    const int u = cx->ustart[g] + (q - cx->rowoff[g]);
+                    reinterpret_cast<float4 *>(Gs)[qq * c4n + c4] =
+                        reinterpret_cast<const float4 *>(ws.E + ws.ebase[t] + (int64_t)u * Dp)[c4];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ii = 0; ii < MT; ++ii) {
+                const int item = w + 4 * ii, g = item / MT, mb = item % MT;
+                if (g >= nu) continue;
+                const int r2 = mb * 16 + li;
+                const bool okr = r2 < R;
+                const int qa = q0 > cx->rowoff[g] ? q0 : cx->rowoff[g];
+                const int qb = q0 + qn < cx->rowoff[g + 1] ? q0 + qn : cx->rowoff[g + 1];
+                // (2a) dC_g[m2][r2] += sum_j3 g_u[m2][j3] G3[i3_u][r2][j3]
+                for (int q = qa; q < qb; ++q) {
+                    const int u = cx->ustart[g] + (q - cx->rowoff[g]);
+                    const int i3 = ws.uniq_row[u] % n3;
+                    const float *g3 = G3 + ((int64_t)i3 * R + (okr ? r2 : 0)) * d3;
+                    const float *gq = Gs + (q - q0) * Dp;
+                    for (int j0 = 0; j0 < d3; j0 += 4) {
+                        const int j3 = j0 + kq;
+                        const float av = (li < D12 && j3 < d3) ? gq[li * d3 + j3] : 0.f;
+                        const float bv = (okr && j3 < d3) ? g3[j3] : 0.f;
+                        dacc[ii] = mfma4(av, bv, dacc[ii]);
+                    }
+                }
+                // (2b) P3_u[r2][j3] = sum_m2 C_g[m2][r2] g_u[m2][j3], P rows per output tile
+                float ca[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int m2 = kq * 4 + s;
+                    ca[s] = (m2 < D12 && okr) ? Cs[g * kBCUnit + m2 * kBCStride + r2] : 0.f;
+                }
+                const int slot = li / d3, j3 = li - slot * d3;
+                for (int qs = qa; qs < qb; qs += P) {
+                    const int cnt = qb - qs < P ? qb - qs : P;
+                    const bool okb = slot < cnt;
+                    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int m2 = kq * 4 + s;
+                        const float bv = (okb && m2 < D12) ? Gs[(qs + slot - q0) * Dp + m2 * d3 + j3] : 0.f;
+                        acc = mfma4(ca[s], bv, acc);
+                    }
+                    if (okb) {
+                        const int u = cx->ustart[g] + (qs + slot - cx->rowoff[g]);
+                        float *dst = ws.P3 + ws.p3base[t] + (int64_t)u * R * d3 + j3;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int rr = mb * 16 + 4 * kq + v;
+                            if (rr < R) dst[rr * d3] = acc[v];
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads(); // staged rows and C consumed
+#pragma unroll
+        for (int ii = 0; ii < MT; ++ii) {
+            const int item = w + 4 * ii, g = item / MT, mb = item % MT;
+            const int r2 = mb * 16 + li;
+            if (r2 < R) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dCs[g * kBCUnit + (4 * kq + v) * kBCStride + r2] = dacc[ii][v];
+            }
+        }
+        __syncthreads();
+
+        // ---- (3) G1 partial of each unit: sum_col dC[(g,j1)][col] G2[r1][col]
+        {
+            const int mb = w % MT, ks = w / MT;
+            const int g = li >> 2, j1 = li & 3;
+            const bool oka = kq < d2 && j1 < d1;
+            const float *arow = dCs + g * kBCUnit + (oka ? j1 * d2 + kq : 0) * kBCStride;
+            const int r1 = mb * 16 + li;
+            const bool okr = r1 < R;
+            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = ks * SPL; s < (ks + 1) * SPL; ++s) {
+                const int col = kq * R + s;
+                const float av = oka ? arow[s] : 0.f;
+                const float bv = okr ? G2s[r1 * NCOL + (col ^ (r1 & 31))] : 0.f;
+                acc = mfma4(av, bv, acc);
+            }
+            if constexpr (KS > 1) {
+                float *red = Gs; // staged rows are no longer needed
+#pragma unroll
+                for (int v = 0; v < 4; ++v) red[(w * 64 + lane) * 4 + v] = acc[v];
+                __syncthreads();
+                if (ks == 0) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float sum = 0.f;
+#pragma unroll
+                        for (int kk = 0; kk < KS; ++kk) sum += red[((mb + kk * MT) * 64 + lane) * 4 + v];
+                        acc[v] = sum;
+                    }
+                }
+            }
+            if (ks == 0 && okr && kq < nu) {
+                float *dst = ws.G1P + ws.g1base[t] + (int64_t)cx->unit[kq] * d1 * R + r1;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (v < d1) dst[v * R] = acc[v];
+            }
+        }
+
+        // ---- (4) dG2 += G1^T dC over (g, j1)
+        {
+            float ga[MT][4];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int r1 = mt * 16 + li;
+                    const bool ok = kq < nu && s < d1 && r1 < R;
+                    ga[mt][s] = ok ? G1[((int64_t)cx->i1[kq] * d1 + s) * R + r1] : 0.f;
+                }
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int ntg = w + 4 * j;
+                if (ntg < NT) {
+                    const int col = ntg * 16 + li, j2 = col / R, r2 = col % R;
+                    float bv[4];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        bv[s] = (j2 < d2 && s < d1) ? dCs[kq * kBCUnit + (s * d2 + j2) * kBCStride + r2] : 0.f;
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) g2acc[mt][j] = mfma4(ga[mt][s], bv[s], g2acc[mt][j]);
+                }
+            }
+        }
+        __syncthreads(); // before the next tile reuses the LDS buffers
+    }
+    float *dst = a.grads.g[t][1] + (int64_t)i2 * R * d2 * R;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+        const int ntg = w + 4 * j;
+        if (ntg >= NT) continue;
+        const int col = ntg * 16 + li;
+        if (col >= d2 * R) continue;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r1 = mt * 16 + 4 * kq + v;
+                if (r1 < R) dst[(int64_t)r1 * d2 * R + col] = g2acc[mt][j][v];
+            }
+    }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_bwd_mfma(BwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float G2s[64 * 256];
+    __shared__ __attribute__((aligned(16))) float Cs[4 * kBCUnit];
+    __shared__ __attribute__((aligned(16))) float dCs[4 * kBCUnit];
+    __shared__ __attribute__((aligned(16))) float Gs[kBGs];
+    __shared__ BTileCtx cx;
+    __shared__ int s_run;
+    const Ws &ws = a.ws;
+    const int nruns = ws.ctrl[CTRL_RUNS];
+    for (;;) {
+        if (threadIdx.x == 0) s_run = atomicAdd(&ws.ctrl[CTRL_BWD_NEXT], 1);
+        __syncthreads();
+        const int run = s_run;
+        if (run >= nruns) break;
+        const int k0 = ws.run_start[run], k1 = ws.run_start[run + 1];
+        const int u0 = ws.uorder[k0];
+        const int t = segment_of(ws.tab_unit_start, a.T, u0);
+        const TableDesc &tb = a.tab[t];
+        const int i2 = ws.unit_prefix[u0] % tb.n2;
+        switch (a.force_generic ? -1 : tb.cls) {
+        case 0: bwd_run_mfma<8>(a, t, i2, k0, k1, G2s, Cs, dCs, Gs, &cx); break;
+        case 1: bwd_run_mfma<16>(a, t, i2, k0, k1, G2s, Cs, dCs, Gs, &cx); break;
+        case 2: bwd_run_mfma<32>(a, t, i2, k0, k1, G2s, Cs, dCs, Gs, &cx); break;
+        case 3: bwd_run_mfma<64>(a, t, i2, k0, k1, G2s, Cs, dCs, Gs, &cx); break;
+        default: break; // handled by k_bwd_runs
+        }
+        __syncthreads();
+    }
+}
+
+// Zero every dG2 core (runs overwrite the slices they own) and the run counter.
 __global__ __launch_bounds__(kThreads) void k_zero_g2(BwdArgs a)
 {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.ws.ctrl[CTRL_BWD_NEXT] = 0;
     const int t = blockIdx.y;
     const TableDesc &tb = a.tab[t];
     const int64_t n = (int64_t)tb.n2 * tb.R1 * tb.d2 * tb.R2;
@@ -321,7 +646,7 @@ __global__ __launch_bounds__(kThreads) void k_zero_g2(BwdArgs a)
 hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs &cores,
                            const int64_t *offsets, const GradPtrs &grads, hipStream_t s)
 {
-    BwdArgs a{p.dtab, p.T, p.B, p.ws, cores, grads, grad_out, offsets, p.nnz, p.sumD, p.Dmax};
+    BwdArgs a{p.dtab, p.T, p.B, p.ws, cores, grads, grad_out, offsets, p.nnz, p.sumD, p.Dmax, p.force_generic};
     const int T = p.T;
     const int sum_n1 = p.sum_n[0], sum_n3 = p.sum_n[2];
     timer_begin(p.timing, TM_BWD_GATHER, s);
@@ -339,7 +664,14 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
     }
     timer_end(p.timing, TM_BWD_GATHER, s);
     timer_begin(p.timing, TM_BWD_CONTRACT, s);
-    if (p.nnz > 0) hipLaunchKernelGGL(k_bwd_runs, dim3(p.num_blocks * 2), dim3(kThreads), 0, s, a);
+    if (p.nnz > 0) {
+        if (!p.force_generic) {
+            int cus = p.num_blocks / 2;
+            hipLaunchKernelGGL(k_bwd_mfma, dim3(cus > 0 ? cus : 1), dim3(kThreads), 0, s, a);
+        }
+        if (p.force_generic || p.any_generic)
+            hipLaunchKernelGGL(k_bwd_runs, dim3(p.num_blocks * 2), dim3(kThreads), 0, s, a);
+    }
     timer_end(p.timing, TM_BWD_CONTRACT, s);
     timer_begin(p.timing, TM_BWD_REDUCE, s);
     hipLaunchKernelGGL(k_reduce_g1, dim3(sum_n1 > 0 ? (sum_n1 < 65535 ? sum_n1 : 65535) : 1), dim3(kThreads), 0,

@@ -38,6 +38,7 @@ enum CtrlSlot {
     CTRL_STEALS = 9,  // chunks taken from another block's range (statistics)
     CTRL_CKPT_HIT = 10,  // split-tile chunks that found a published checkpoint
     CTRL_CKPT_MISS = 11, // split-tile chunks that recomputed the prefix tile
+    CTRL_BWD_NEXT = 12,  // next run of the backward contraction (work counter)
     CTRL_N = 64
 };
 enum ErrBits { ERRB_INDEX = 1, ERRB_OFFSETS = 2 };
