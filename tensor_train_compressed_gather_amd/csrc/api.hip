@@ -44,6 +44,7 @@ struct tt_emb {
     int Dmax, Dpmax, R2max, sumD;
     int sum_n[3];
     int64_t max_d1R1, max_R2d3, max_Dp;
+    int64_t g3t_elems;
 };
 
 namespace {
@@ -108,9 +109,23 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.tile_nu = (int32_t *)take(4 * n);
     w.tile_rows = (int32_t *)take(4 * n);
     w.tile_slot = (int32_t *)take(4 * n);
-    w.chunk_tile = (int32_t *)take(4 * (2 * n + 1));
-    w.chunk_rbeg = (int32_t *)take(4 * (2 * n + 1));
-    w.chunk_rend = (int32_t *)take(4 * (2 * n + 1));
+    // chunks <= rows/S + tiles, tiles <= units/4 + runs, runs <= sum n2
+    int64_t units_bound = 0;
+    for (int t = 0; t < T; ++t) {
+        const TableDesc &d = h->tabs[t];
+        const int64_t pre = (int64_t)d.n1 * d.n2;
+        int64_t ub = h->group_mode == TT_EMB_GROUP_UNIQUE_ONLY ? d.N : (pre < d.N ? pre : d.N);
+        units_bound += ub < n ? ub : n;
+    }
+    if (units_bound > n) units_bound = n;
+    int64_t chunks = n / h->chunk_rows + 1 + units_bound / 4 + 1 + h->sum_n[1] + 1;
+    if (chunks > 2 * n + 1) chunks = 2 * n + 1;
+    w.chunk_tile = (int32_t *)take(4 * chunks);
+    w.chunk_rbeg = (int32_t *)take(4 * chunks);
+    w.chunk_rend = (int32_t *)take(4 * chunks);
+    w.crec = (ChunkRec *)take(sizeof(ChunkRec) * chunks);
+    w.chunk_cap = chunks;
+    w.g3t = (float *)take(4 * (size_t)h->g3t_elems);
     w.heads = (int32_t *)take(4 * (size_t)h->num_blocks);
     w.flags = (int32_t *)take(4 * (size_t)kMaxCkptSlots);
     w.ckpt = (float *)take(4 * (size_t)kMaxCkptSlots * (4 * (16 * 68 + 16)));
@@ -214,13 +229,14 @@ int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const in
         tt_emb_options o{};
         if (opt) o = *opt;
         if (o.sched_mode < 0 || o.sched_mode > 3 || o.group_mode < 0 || o.group_mode > 2) return TT_EMB_ERR_ARG;
-        if (o.chunk_rows < 0 || o.chunk_rows > 4096 || o.num_blocks < 0) return TT_EMB_ERR_ARG;
+        if (o.chunk_rows < 0 || o.chunk_rows > kMaxChunkRows || o.num_blocks < 0) return TT_EMB_ERR_ARG;
         tt_emb *h = new (std::nothrow) tt_emb();
         if (!h) return TT_EMB_ERR_NOMEM;
         h->T = T;
         h->sched_mode = o.sched_mode == 0 ? TT_EMB_SCHED_STEAL_L2 : o.sched_mode;
         h->group_mode = o.group_mode == 0 ? TT_EMB_GROUP_PREFIX : o.group_mode;
-        h->chunk_rows = o.chunk_rows == 0 ? 32 : o.chunk_rows;
+        h->chunk_rows = o.chunk_rows == 0 ? kMaxChunkRows : o.chunk_rows;
+        h->g3t_elems = 0;
         h->check_indices = o.check_indices >= 0 ? 1 : 0;
         h->force_generic = o.force_generic ? 1 : 0;
         uint64_t key = 0, b1 = 0, b2 = 0, b3 = 0;
@@ -276,6 +292,8 @@ int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const in
                 else if (td.R1 == 64) cls = 3;
             }
             td.cls = cls;
+            td.g3t_off = h->g3t_elems;
+            if (cls >= 0) h->g3t_elems += (int64_t)td.n3 * td.R2 * td.d3;
             if (cls < 0) h->any_generic = true;
             if (td.D > h->Dmax) h->Dmax = td.D;
             if (td.Dp > h->Dpmax) h->Dpmax = td.Dp;
@@ -552,6 +570,7 @@ int tt_emb_poll_error(tt_emb_t h, const void *ws, void *stream)
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TT_EMB_ERR_HIP;
     int32_t err = 0;
     if (hipMemcpy(&err, ws, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return TT_EMB_ERR_HIP;
+    if (err & ERRB_CAPACITY) return TT_EMB_ERR_WORKSPACE;
     if (err & ERRB_OFFSETS) return TT_EMB_ERR_OFFSETS;
     if (err & ERRB_INDEX) return TT_EMB_ERR_INDEX;
     return TT_EMB_OK;

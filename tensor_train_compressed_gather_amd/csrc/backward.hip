@@ -94,17 +94,63 @@ __global__ __launch_bounds__(kThreads) void k_gu_pieces(BwdArgs a)
         const int D = tb.D;
         const bool single = (ws.u_piece_start[u + 1] - ws.u_piece_start[u]) == 1;
         float *dst = single ? ws.E + ws.ebase[t] + (int64_t)u * tb.Dp : ws.P3 + p * (int64_t)a.Dmax;
-        for (int j0 = 0; j0 < D; j0 += 64) {
-            const int j = j0 + lane;
-            float acc = 0.f;
-            for (int k = k0; k < k1; ++k) {
-                int64_t bag = ws.bag_of[ws.perm[k]];
-                bag = bag < 0 ? 0 : (bag >= nbags ? nbags - 1 : bag);
-                const int64_t b = bag - (int64_t)t * a.B;
-                const int64_t bb = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
-                if (j < D) acc += a.grad_out[bb * a.SD + tb.col_off + j];
+        const float *go = a.grad_out + tb.col_off;
+        // lanes per row: float4 columns rounded up to a power of two; rows in flight
+        const int c4n = (D + 3) >> 2;
+        int lpr = 1;
+        while (lpr < c4n) lpr <<= 1;
+        const bool vec = lpr <= 64 && ((a.SD | tb.col_off) & 3) == 0;
+        if (vec) {
+            const int rf = 64 / lpr, c4 = lane & (lpr - 1), r = lane / lpr;
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int kb = k0; kb < k1; kb += 64) {
+                const int nk = k1 - kb < 64 ? k1 - kb : 64;
+                // the bag (row of grad_out) of lookups kb .. kb+63, one per lane
+                int64_t bb = 0;
+                if (lane < nk) {
+                    int64_t bag = ws.bag_of[ws.perm[kb + lane]];
+                    bag = bag < 0 ? 0 : (bag >= nbags ? nbags - 1 : bag);
+                    const int64_t b = bag - (int64_t)t * a.B;
+                    bb = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
+                }
+#pragma unroll 4
+                for (int i = 0; i < nk; i += rf) {
+                    const int64_t row = __shfl(bb, i + r < 64 ? i + r : 0, 64);
+                    if (i + r < nk && c4 < c4n) {
+                        const float4 v = reinterpret_cast<const float4 *>(go + row * a.SD)[c4];
+                        acc.x += v.x;
+                        acc.y += v.y;
+                        acc.z += v.z;
+                        acc.w += v.w;
+                    }
+                }
             }
-            if (j < D) dst[j] = acc;
+            for (int m = lpr; m < 64; m <<= 1) {
+                acc.x += __shfl_xor(acc.x, m, 64);
+                acc.y += __shfl_xor(acc.y, m, 64);
+                acc.z += __shfl_xor(acc.z, m, 64);
+                acc.w += __shfl_xor(acc.w, m, 64);
+            }
+            if (r == 0 && c4 < c4n) {
+                const int j = 4 * c4;
+                if (j + 0 < D) dst[j + 0] = acc.x;
+                if (j + 1 < D) dst[j + 1] = acc.y;
+                if (j + 2 < D) dst[j + 2] = acc.z;
+                if (j + 3 < D) dst[j + 3] = acc.w;
+            }
+        } else {
+            for (int j0 = 0; j0 < D; j0 += 64) {
+                const int j = j0 + lane;
+                float acc = 0.f;
+                for (int k = k0; k < k1; ++k) {
+                    int64_t bag = ws.bag_of[ws.perm[k]];
+                    bag = bag < 0 ? 0 : (bag >= nbags ? nbags - 1 : bag);
+                    const int64_t b = bag - (int64_t)t * a.B;
+                    const int64_t bb = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
+                    if (j < D) acc += go[bb * a.SD + j];
+                }
+                if (j < D) dst[j] = acc;
+            }
         }
     }
 }
@@ -301,10 +347,31 @@ __global__ __launch_bounds__(kThreads) void k_reduce_g3(BwdArgs a, const uint32_
         const int64_t last = lo;
         const int per = tb.R2 * tb.d3;
         float *dst = a.grads.g[t][2] + (int64_t)i3 * per;
-        for (int e = threadIdx.x; e < per; e += kThreads) {
+        const float *src = ws.P3 + ws.p3base[t];
+        // rp row phases of per-element threads; phase ph sums rows first+ph,
+        // first+ph+rp, ... in order, then the phases are added in order.
+        const int rp = per >= kThreads ? 1 : kThreads / per;
+        const int ph = threadIdx.x / per < rp ? threadIdx.x / per : rp; // rp = idle
+        __shared__ float part[kThreads];
+        for (int e0 = 0; e0 < per; e0 += kThreads) {
+            const int e = e0 + (rp == 1 ? threadIdx.x : threadIdx.x - ph * per);
             float c = 0.f;
-            for (int64_t q = first; q < last; ++q) c += ws.P3[ws.p3base[t] + (int64_t)order[q] * per + e];
-            dst[e] = c;
+            if (ph < rp && e < per) {
+#pragma unroll 8
+                for (int64_t q = first + ph; q < last; q += rp) c += src[(int64_t)order[q] * per + e];
+            }
+            if (rp == 1) {
+                if (e < per) dst[e] = c;
+            } else {
+                part[threadIdx.x] = c;
+                __syncthreads();
+                if (threadIdx.x < per) {
+                    float s = 0.f;
+                    for (int k = 0; k < rp; ++k) s += part[k * per + threadIdx.x];
+                    dst[threadIdx.x] = s;
+                }
+                __syncthreads();
+            }
         }
     }
 }

@@ -39,12 +39,6 @@ struct FwdArgs {
     int sched;
 };
 
-struct ChunkCtx {
-    int tile, t, nu, rbeg, rend, slot, i2, cls;
-    int i1[4], ustart[4], cfirst[4], ccnt[4];
-    int pstart[5];
-};
-
 // Victim order for stealing: own range, then blocks on the same XCD (blocks
 // are dispatched round-robin over the 8 XCDs), then the other XCDs.
 __device__ __forceinline__ int victim_of(int me, int vi, int nb)
@@ -70,33 +64,123 @@ __global__ __launch_bounds__(kThreads) void k_queue_init(Ws ws, int nb)
     }
 }
 
+// Transposed copy G3t[i3][j3][r2] = G3[i3][r2][j3] of every MFMA-class table,
+// so a lane's run of r2 values is contiguous (float4 loads).
+__global__ __launch_bounds__(kThreads) void k_g3t(FwdArgs a)
+{
+    const int t = blockIdx.y;
+    const TableDesc &tb = a.tab[t];
+    if (tb.cls < 0) return;
+    const int R2 = tb.R2, d3 = tb.d3, per = R2 * d3;
+    const int64_t n = (int64_t)tb.n3 * per;
+    const float *src = a.cores.g[t][2];
+    float *dst = a.ws.g3t + tb.g3t_off;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i3 = i / per;
+        const int rem = (int)(i - i3 * per), j3 = rem / R2, r2 = rem - j3 * R2;
+        dst[i] = src[(i3 * R2 + r2) * d3 + j3];
+    }
+}
+
+// Claiming work (wave 0 of a block).  claim_start() issues the atomic on the
+// current victim's head; claim_finish() checks it and, when that victim is
+// drained, probes the next 64 victims in parallel and retries.  Every chunk is
+// handed out exactly once (heads only grow) and the loop ends once every
+// victim has been seen drained.
+__device__ __forceinline__ int claim_start(const Ws &ws, int me, int vi, int nb, int nvict)
+{
+    int raw = 0x7fffffff;
+    if (vi < nvict && (threadIdx.x & 63) == 0) raw = atomicAdd(&ws.heads[victim_of(me, vi, nb)], 1);
+    return raw;
+}
+
+__device__ int claim_finish(const Ws &ws, int me, int &vi, int nb, int nvict, int64_t C, int raw)
+{
+    const int lane = threadIdx.x & 63;
+    for (;;) {
+        if (vi >= nvict) return -1;
+        const int v = victim_of(me, vi, nb);
+        int got = -1;
+        if (lane == 0 && raw < range_begin(v + 1, C, nb)) got = raw;
+        got = __shfl(got, 0, 64);
+        if (got >= 0) {
+            if (vi != 0 && lane == 0) atomicAdd(&ws.ctrl[CTRL_STEALS], 1);
+            return got;
+        }
+        const int cand = vi + 1 + lane;
+        bool avail = false;
+        if (cand < nvict) {
+            const int vv = victim_of(me, cand, nb);
+            avail = __hip_atomic_load(&ws.heads[vv], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                    range_begin(vv + 1, C, nb);
+        }
+        const uint64_t m = __ballot(avail);
+        vi = m ? vi + 1 + (__ffsll((unsigned long long)m) - 1) : vi + 65;
+        raw = claim_start(ws, me, vi, nb, nvict);
+    }
+}
+
 // One chunk of a tile on the matrix cores, R1 = R2 = R.
 template <int R>
-__device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkCtx &cx, float *Cs,
+__device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec, float *Cs,
                                            float (&breg)[64], int &bkey, int &lds_tile, int *s_flag)
 {
     constexpr int KQ = R / 4;           // K values each lane feeds per output tile
     constexpr int NT = R / 4;           // 16-column tiles of the padded d2*R2 (d2 <= 4)
     constexpr int NTW = (NT + 3) / 4;   // per wave
-    const TableDesc &tb = a.tab[cx.t];
-    const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, n3 = tb.n3, D12 = d1 * d2;
+    const int t = rec.t;
+    const TableDesc &tb = a.tab[t];
+    const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, D12 = d1 * d2, Dp = tb.Dp;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, kq = lane >> 4;
-    const float *G1 = a.cores.g[cx.t][0];
-    const float *G2 = a.cores.g[cx.t][1];
-    const float *G3 = a.cores.g[cx.t][2];
+    const float *G1 = a.cores.g[t][0];
+    const float *G2 = a.cores.g[t][1];
+    const float *G3t = a.ws.g3t + tb.g3t_off;
+    const int P = 16 / d3;
+    const int np = rec.pstart[rec.nu];
+    const int slot = li / d3, j3 = li - slot * d3;
+
+    // output tile e -> unit j, first row (chunk numbering) and row count
+    auto piece = [&](int e, int &j, int &rb, int &cnt) {
+        j = 0;
+        while (j < 3 && e >= rec.pstart[j + 1]) ++j;
+        rb = rec.rowoff[j] + (e - rec.pstart[j]) * P;
+        const int rem = rec.rowoff[j] + rec.ccnt[j] - rb;
+        cnt = rem < P ? rem : P;
+    };
+    // B operand of an output tile: G3t[i3][j3][kq*KQ .. kq*KQ+KQ-1] of the lane's row
+    auto load_b = [&](int e, float (&b)[KQ]) {
+        int j, rb, cnt;
+        piece(e, j, rb, cnt);
+        const bool ok = slot < cnt;
+        const float *src = G3t + ((int64_t)(ok ? rec.i3[rb + slot] : 0) * d3 + (ok ? j3 : 0)) * R + kq * KQ;
+        if constexpr (KQ % 4 == 0) {
+#pragma unroll
+            for (int s = 0; s < KQ; s += 4) {
+                const float4 v = ok ? *reinterpret_cast<const float4 *>(src + s) : make_float4(0.f, 0.f, 0.f, 0.f);
+                b[s] = v.x;
+                b[s + 1] = v.y;
+                b[s + 2] = v.z;
+                b[s + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < KQ; ++s) b[s] = ok ? src[s] : 0.f;
+        }
+    };
+    float bnext[KQ];
+    if (w < np) load_b(w, bnext); // in flight while the prefix tile is computed
 
     // -------- prefix tile C_u = G1[i1_u] . G2[i2] for the (<= 4) units
-    if (lds_tile != cx.tile) {
+    if (lds_tile != rec.tile) {
         bool have = false;
-        const bool split = cx.slot >= 0 && a.sched == kSchedStealL2;
-        if (split && cx.rbeg > 0) {
+        const bool split = rec.slot >= 0 && a.sched == kSchedStealL2;
+        if (split && rec.rbeg > 0) {
             if (threadIdx.x == 0)
-                *s_flag = __hip_atomic_load(&a.ws.flags[cx.slot], __ATOMIC_ACQUIRE,
-                                            __HIP_MEMORY_SCOPE_AGENT);
+                *s_flag = __hip_atomic_load(&a.ws.flags[rec.slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
             if (*s_flag) {
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                const float4 *src = reinterpret_cast<const float4 *>(a.ws.ckpt + (size_t)cx.slot * kCTile);
+                const float4 *src = reinterpret_cast<const float4 *>(a.ws.ckpt + (size_t)rec.slot * kCTile);
                 float4 *dst = reinterpret_cast<float4 *>(Cs);
                 for (int i = threadIdx.x; i < kCTile / 4; i += kThreads) dst[i] = src[i];
                 have = true;
@@ -104,31 +188,14 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkCtx &cx,
             if (threadIdx.x == 0) atomicAdd(&a.ws.ctrl[have ? CTRL_CKPT_HIT : CTRL_CKPT_MISS], 1);
         }
         if (!have) {
-            const int key = (int)(tb.i2_base + (uint32_t)cx.i2);
-            if (bkey != key) {
-#pragma unroll
-                for (int j = 0; j < NTW; ++j) {
-                    const int ntg = w + 4 * j;
-                    const int col = ntg * 16 + li;
-                    const int j2 = col / R, r2 = col % R;
-                    const bool ok = ntg < NT && j2 < d2;
-                    const float *src = G2 + ((int64_t)cx.i2 * R * d2 + (ok ? j2 : 0)) * R + r2;
-#pragma unroll
-                    for (int s = 0; s < KQ; ++s) {
-                        const int k = kq * KQ + s;
-                        breg[j * KQ + s] = ok ? src[(int64_t)k * d2 * R] : 0.f;
-                    }
-                }
-                bkey = key;
-            }
             const int g = li >> 2, j1 = li & 3;
-            const bool oka = g < cx.nu && j1 < d1;
-            const float *srcA = G1 + ((int64_t)(oka ? cx.i1[g] : 0) * d1 + (oka ? j1 : 0)) * R + kq * KQ;
+            const bool oka = g < rec.nu && j1 < d1;
+            const float *srcA = G1 + ((int64_t)(oka ? rec.i1[g] : 0) * d1 + (oka ? j1 : 0)) * R + kq * KQ;
             float areg[KQ];
             if constexpr (KQ % 4 == 0) {
 #pragma unroll
                 for (int s = 0; s < KQ; s += 4) {
-                    float4 v = oka ? *reinterpret_cast<const float4 *>(srcA + s) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    const float4 v = oka ? *reinterpret_cast<const float4 *>(srcA + s) : make_float4(0.f, 0.f, 0.f, 0.f);
                     areg[s] = v.x;
                     areg[s + 1] = v.y;
                     areg[s + 2] = v.z;
@@ -137,6 +204,23 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkCtx &cx,
             } else {
 #pragma unroll
                 for (int s = 0; s < KQ; ++s) areg[s] = oka ? srcA[s] : 0.f;
+            }
+            const int key = (int)(tb.i2_base + (uint32_t)rec.i2);
+            if (bkey != key) {
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    const int ntg = w + 4 * j;
+                    const int col = ntg * 16 + li;
+                    const int j2 = col / R, r2 = col % R;
+                    const bool ok = ntg < NT && j2 < d2;
+                    const float *src = G2 + ((int64_t)rec.i2 * R * d2 + (ok ? j2 : 0)) * R + r2;
+#pragma unroll
+                    for (int s = 0; s < KQ; ++s) {
+                        const int k = kq * KQ + s;
+                        breg[j * KQ + s] = ok ? src[(int64_t)k * d2 * R] : 0.f;
+                    }
+                }
+                bkey = key;
             }
             floatx4 acc[NTW];
 #pragma unroll
@@ -155,7 +239,7 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkCtx &cx,
                 if (ntg < NT) {
                     const int col = ntg * 16 + li;
                     const int j2 = col / R, r2 = col % R;
-                    if (j2 < d2 && kq < cx.nu) {
+                    if (j2 < d2 && kq < rec.nu) {
 #pragma unroll
                         for (int v = 0; v < 4; ++v)
                             if (v < d1) Cs[kq * kCUnit + (v * d2 + j2) * kCStride + r2] = acc[j][v];
@@ -163,60 +247,49 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkCtx &cx,
                 }
             }
             __syncthreads();
-            if (split && cx.rbeg == 0) {
-                float4 *dst = reinterpret_cast<float4 *>(a.ws.ckpt + (size_t)cx.slot * kCTile);
+            if (split && rec.rbeg == 0) {
+                float4 *dst = reinterpret_cast<float4 *>(a.ws.ckpt + (size_t)rec.slot * kCTile);
                 const float4 *src = reinterpret_cast<const float4 *>(Cs);
                 for (int i = threadIdx.x; i < kCTile / 4; i += kThreads) dst[i] = src[i];
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
                 __syncthreads();
                 if (threadIdx.x == 0)
-                    __hip_atomic_store(&a.ws.flags[cx.slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&a.ws.flags[rec.slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        lds_tile = cx.tile;
-        __syncthreads();
+        lds_tile = rec.tile;
     }
+    __syncthreads();
 
     // -------- unique rows E_u = C_unit . G3[i3_u], 16/d3 rows per output tile
-    const int P = 16 / d3;
-    const int np = cx.pstart[cx.nu];
-    float *Et = a.ws.E + a.ws.ebase[cx.t];
+    float *Et = a.ws.E + a.ws.ebase[t];
+    const bool okm = li < D12;
     for (int e = w; e < np; e += 4) {
-        int j = 0;
-        while (j < 3 && e >= cx.pstart[j + 1]) ++j;
-        const int rfirst = cx.cfirst[j] + (e - cx.pstart[j]) * P;
-        int cnt = cx.cfirst[j] + cx.ccnt[j] - rfirst;
-        cnt = cnt < P ? cnt : P;
-        const int ufirst = cx.ustart[j] + rfirst;
-        const bool okm = li < D12;
+        float bcur[KQ];
+#pragma unroll
+        for (int s = 0; s < KQ; ++s) bcur[s] = bnext[s];
+        if (e + 4 < np) load_b(e + 4, bnext);
+        int j, rb, cnt;
+        piece(e, j, rb, cnt);
         const float *ca = Cs + j * kCUnit + (okm ? li : 0) * kCStride + kq * KQ;
-        float a2[KQ];
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
         if constexpr (KQ % 4 == 0) {
 #pragma unroll
             for (int s = 0; s < KQ; s += 4) {
-                float4 v = *reinterpret_cast<const float4 *>(ca + s);
-                a2[s] = okm ? v.x : 0.f;
-                a2[s + 1] = okm ? v.y : 0.f;
-                a2[s + 2] = okm ? v.z : 0.f;
-                a2[s + 3] = okm ? v.w : 0.f;
+                const float4 v = *reinterpret_cast<const float4 *>(ca + s);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(okm ? v.x : 0.f, bcur[s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(okm ? v.y : 0.f, bcur[s + 1], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(okm ? v.z : 0.f, bcur[s + 2], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(okm ? v.w : 0.f, bcur[s + 3], acc, 0, 0, 0);
             }
         } else {
 #pragma unroll
-            for (int s = 0; s < KQ; ++s) a2[s] = okm ? ca[s] : 0.f;
+            for (int s = 0; s < KQ; ++s)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(okm ? ca[s] : 0.f, bcur[s], acc, 0, 0, 0);
         }
-        const int slot = li / d3, j3 = li - slot * d3;
-        const bool okb = slot < cnt;
-        const int u = ufirst + (okb ? slot : 0);
-        const int i3 = okb ? a.ws.uniq_row[u] % n3 : 0;
-        const float *gb = G3 + ((int64_t)i3 * R + kq * KQ) * d3 + (okb ? j3 : 0);
-        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KQ; ++s) {
-            const float b = okb ? gb[s * d3] : 0.f;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[s], b, acc, 0, 0, 0);
-        }
-        if (okb) {
-            float *Erow = Et + (int64_t)u * tb.Dp;
+        if (slot < cnt) {
+            const int u = rec.ustart[j] + (rb - rec.rowoff[j]) + slot;
+            float *Erow = Et + (int64_t)u * Dp;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int m2 = kq * 4 + v;
@@ -226,102 +299,63 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkCtx &cx,
     }
 }
 
-// Persistent contraction kernel for every table of an MFMA rank class.
+// Persistent contraction kernel for every table of an MFMA rank class.  Wave 0
+// keeps two chunks claimed ahead: while chunk i runs, the record of chunk i+1
+// is in flight and the claim of chunk i+2 is outstanding.
 __global__ __launch_bounds__(kThreads, 2) void k_contract(FwdArgs a)
 {
     __shared__ __attribute__((aligned(16))) float Cs[kCTile];
-    __shared__ ChunkCtx cx;
-    __shared__ int s_c, s_flag;
+    __shared__ ChunkRec rbuf[2];
+    __shared__ int s_cur, s_next, s_flag;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int nb = gridDim.x, me = blockIdx.x;
-    const int64_t C = a.ws.ctrl[CTRL_CHUNKS];
+    const Ws &ws = a.ws;
+    const int64_t C = ws.ctrl[CTRL_CHUNKS];
     const int nvict = a.sched == kSchedStatic ? 1 : nb;
     float breg[64];
 #pragma unroll
     for (int i = 0; i < 64; ++i) breg[i] = 0.f;
     int bkey = -1, lds_tile = -1, vi = 0;
+    if (w == 0) {
+        const int c0 = claim_finish(ws, me, vi, nb, nvict, C, claim_start(ws, me, vi, nb, nvict));
+        const int c1 = c0 < 0 ? -1 : claim_finish(ws, me, vi, nb, nvict, C, claim_start(ws, me, vi, nb, nvict));
+        if (c0 >= 0) reinterpret_cast<int *>(&rbuf[0])[lane] = reinterpret_cast<const int *>(&ws.crec[c0])[lane];
+        if (lane == 0) {
+            s_cur = c0;
+            s_next = c1;
+        }
+    }
+    __syncthreads();
+    int buf = 0;
     for (;;) {
-        // ---- claim the next chunk: own range first, then steal
-        if (w == 0) {
-            int c = -1;
-            while (vi < nvict) {
-                int got = -1;
-                if (lane == 0) {
-                    const int v = victim_of(me, vi, nb);
-                    const int idx = atomicAdd(&a.ws.heads[v], 1);
-                    if (idx < range_begin(v + 1, C, nb)) got = idx;
-                }
-                got = __shfl(got, 0, 64);
-                if (got >= 0) {
-                    c = got;
-                    if (vi != 0 && lane == 0) atomicAdd(&a.ws.ctrl[CTRL_STEALS], 1);
-                    break;
-                }
-                // the current victim is drained: probe the next 64 in parallel
-                const int cand = vi + 1 + lane;
-                bool avail = false;
-                if (cand < nvict) {
-                    const int v = victim_of(me, cand, nb);
-                    avail = __hip_atomic_load(&a.ws.heads[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                            range_begin(v + 1, C, nb);
-                }
-                const uint64_t m = __ballot(avail);
-                vi = m ? vi + 1 + (__ffsll((unsigned long long)m) - 1) : vi + 65;
-            }
-            if (lane == 0) s_c = c;
-        }
-        __syncthreads();
-        const int c = s_c;
+        const int c = s_cur, cn = s_next;
         if (c < 0) break;
-        // ---- chunk context
-        if (threadIdx.x == 0) {
-            const Ws &ws = a.ws;
-            const int tile = ws.chunk_tile[c];
-            const int rbeg = ws.chunk_rbeg[c], rend = ws.chunk_rend[c];
-            const int ubeg = ws.tile_ubeg[tile], nu = ws.tile_nu[tile];
-            const int u0 = ws.uorder[ubeg];
-            const int t = segment_of(ws.tab_unit_start, a.T, u0);
-            const TableDesc &tb = a.tab[t];
-            cx.tile = tile;
-            cx.t = t;
-            cx.nu = nu;
-            cx.rbeg = rbeg;
-            cx.rend = rend;
-            cx.slot = ws.tile_slot[tile];
-            cx.cls = tb.cls;
-            cx.i2 = ws.unit_prefix[u0] % tb.n2;
-            const int P = 16 / (tb.d3 > 0 && tb.d3 <= 16 ? tb.d3 : 16);
-            int off = 0;
-            cx.pstart[0] = 0;
-            for (int j = 0; j < 4; ++j) {
-                int cf = 0, cc = 0, us = 0, i1 = 0;
-                if (j < nu) {
-                    const int u = ws.uorder[ubeg + j];
-                    us = ws.unit_start[u];
-                    const int cnt = ws.unit_start[u + 1] - us;
-                    i1 = ws.unit_prefix[u] / tb.n2;
-                    const int lo = rbeg > off ? rbeg : off;
-                    const int hi = rend < off + cnt ? rend : off + cnt;
-                    cf = lo - off;
-                    cc = hi > lo ? hi - lo : 0;
-                    off += cnt;
-                }
-                cx.i1[j] = i1;
-                cx.ustart[j] = us;
-                cx.cfirst[j] = cf;
-                cx.ccnt[j] = cc;
-                cx.pstart[j + 1] = cx.pstart[j] + (cc + P - 1) / P;
+        int pre = 0, raw = 0x7fffffff;
+        if (w == 0) {
+            if (cn >= 0) {
+                pre = reinterpret_cast<const int *>(&ws.crec[cn])[lane];
+                raw = claim_start(ws, me, vi, nb, nvict);
             }
         }
-        __syncthreads();
-        switch (cx.cls) {
-        case 0: chunk_mfma<8>(a, cx, Cs, breg, bkey, lds_tile, &s_flag); break;
-        case 1: chunk_mfma<16>(a, cx, Cs, breg, bkey, lds_tile, &s_flag); break;
-        case 2: chunk_mfma<32>(a, cx, Cs, breg, bkey, lds_tile, &s_flag); break;
-        case 3: chunk_mfma<64>(a, cx, Cs, breg, bkey, lds_tile, &s_flag); break;
+        const ChunkRec &rec = rbuf[buf];
+        switch (rec.cls) {
+        case 0: chunk_mfma<8>(a, rec, Cs, breg, bkey, lds_tile, &s_flag); break;
+        case 1: chunk_mfma<16>(a, rec, Cs, breg, bkey, lds_tile, &s_flag); break;
+        case 2: chunk_mfma<32>(a, rec, Cs, breg, bkey, lds_tile, &s_flag); break;
+        case 3: chunk_mfma<64>(a, rec, Cs, breg, bkey, lds_tile, &s_flag); break;
         default: break; // tables outside the rank classes run in k_contract_generic
         }
+        __syncthreads(); // everyone is done with rbuf[buf], s_cur and s_next
+        if (w == 0) {
+            const int c2 = cn < 0 ? -1 : claim_finish(ws, me, vi, nb, nvict, C, raw);
+            if (cn >= 0) reinterpret_cast<int *>(&rbuf[buf ^ 1])[lane] = pre;
+            if (lane == 0) {
+                s_cur = cn;
+                s_next = c2;
+            }
+        }
         __syncthreads();
+        buf ^= 1;
     }
 }
 
@@ -438,8 +472,10 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
     timer_begin(p.timing, TM_CONTRACT, s);
     if (p.nnz > 0) {
         hipLaunchKernelGGL(k_queue_init, dim3(1), dim3(kThreads), 0, s, p.ws, p.num_blocks);
-        if (!p.force_generic)
+        if (!p.force_generic) {
+            hipLaunchKernelGGL(k_g3t, dim3(64, p.T), dim3(kThreads), 0, s, a);
             hipLaunchKernelGGL(k_contract, dim3(p.num_blocks), dim3(kThreads), 0, s, a);
+        }
         if (p.force_generic || p.any_generic)
             hipLaunchKernelGGL(k_contract_generic, dim3(p.num_blocks * 4), dim3(kThreads), 0, s, a,
                                p.force_generic ? 1 : 0);

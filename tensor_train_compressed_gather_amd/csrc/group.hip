@@ -451,6 +451,7 @@ struct ChunkOp {
         ws.tile_rows[tile] = r;
         ws.tile_slot[tile] = (nch > 1 && hi < (uint32_t)kMaxCkptSlots) ? (int32_t)hi : -1;
         for (uint32_t c = 0; c < nch; ++c) {
+            if ((int64_t)lo + c >= ws.chunk_cap) break; // reported by total()
             ws.chunk_tile[lo + c] = (int32_t)tile;
             ws.chunk_rbeg[lo + c] = (int32_t)(c * S);
             const int32_t e = (int32_t)((c + 1) * S);
@@ -459,10 +460,68 @@ struct ChunkOp {
     }
     __device__ void total(uint64_t tot, int64_t) const
     {
-        ws.ctrl[CTRL_CHUNKS] = (int32_t)(tot & 0xffffffffu);
+        int64_t c = (int64_t)(tot & 0xffffffffu);
+        if (c > ws.chunk_cap) {
+            atomicOr(&ws.ctrl[CTRL_ERR], (int)ERRB_CAPACITY);
+            c = ws.chunk_cap;
+        }
+        ws.ctrl[CTRL_CHUNKS] = (int32_t)c;
         ws.ctrl[CTRL_SPLIT] = (int32_t)(tot >> 32);
     }
 };
+
+// One record per chunk: the digits, row ranges and per-row i3 the persistent
+// contraction kernel needs, gathered here in parallel.
+__global__ __launch_bounds__(kThreads) void k_chunk_records(const TableDesc *tab, int T, Ws ws)
+{
+    const int64_t C = ws.ctrl[CTRL_CHUNKS];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < C; c += stride) {
+        ChunkRec rec;
+        const int tile = ws.chunk_tile[c];
+        const int rbeg = ws.chunk_rbeg[c], rend = ws.chunk_rend[c];
+        const int ubeg = ws.tile_ubeg[tile], nu = ws.tile_nu[tile];
+        const int u0 = ws.uorder[ubeg];
+        const int t = segment_of(ws.tab_unit_start, T, u0);
+        const TableDesc &tb = tab[t];
+        rec.tile = tile;
+        rec.t = t;
+        rec.nu = nu;
+        rec.rbeg = rbeg;
+        rec.rend = rend;
+        rec.slot = ws.tile_slot[tile];
+        rec.i2 = ws.unit_prefix[u0] % tb.n2;
+        rec.cls = tb.cls;
+        rec.pad[0] = rec.pad[1] = 0;
+        const int P = (tb.d3 > 0 && tb.d3 <= 16) ? 16 / tb.d3 : 1;
+        int off = 0, coff = 0;
+        rec.pstart[0] = 0;
+        for (int j = 0; j < 4; ++j) {
+            int i1 = 0, us = 0, cc = 0;
+            if (j < nu) {
+                const int u = ws.uorder[ubeg + j];
+                const int s0 = ws.unit_start[u], cnt = ws.unit_start[u + 1] - s0;
+                const int lo = rbeg > off ? rbeg : off;
+                const int hi = rend < off + cnt ? rend : off + cnt;
+                cc = hi > lo ? hi - lo : 0;
+                us = s0 + (lo - off);
+                i1 = ws.unit_prefix[u] / tb.n2;
+                off += cnt;
+            }
+            rec.i1[j] = i1;
+            rec.ustart[j] = us;
+            rec.ccnt[j] = cc;
+            rec.rowoff[j] = coff;
+            for (int r = 0; r < cc && coff + r < kMaxChunkRows; ++r)
+                rec.i3[coff + r] = ws.uniq_row[us + r] % tb.n3;
+            coff += cc;
+            rec.pstart[j + 1] = rec.pstart[j] + (cc + P - 1) / P;
+        }
+        rec.rowoff[4] = coff;
+        for (int r = coff; r < kMaxChunkRows; ++r) rec.i3[r] = 0;
+        ws.crec[c] = rec;
+    }
+}
 
 hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t *offsets,
                            hipStream_t s)
@@ -533,6 +592,9 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
         ChunkOp cop{ws, p.chunk_rows};
         e = run_scan(cop, ws.part, scan_blocks(nnz), s);
         if (e != hipSuccess) return e;
+        int gc = ceil_div(ws.chunk_cap, kThreads);
+        if (gc > 4096) gc = 4096;
+        hipLaunchKernelGGL(k_chunk_records, dim3(gc), dim3(kThreads), 0, s, p.dtab, T, ws);
     }
     timer_end(p.timing, TM_GROUP_RLE, s);
     return hipGetLastError();

@@ -41,7 +41,7 @@ enum CtrlSlot {
     CTRL_BWD_NEXT = 12,  // next run of the backward contraction (work counter)
     CTRL_N = 64
 };
-enum ErrBits { ERRB_INDEX = 1, ERRB_OFFSETS = 2 };
+enum ErrBits { ERRB_INDEX = 1, ERRB_OFFSETS = 2, ERRB_CAPACITY = 4 };
 
 // Per-table descriptor, copied to the device at create time.
 struct TableDesc {
@@ -57,7 +57,24 @@ struct TableDesc {
     uint32_t i3_base;  // sum of n3 over earlier tables
     int32_t cls;       // MFMA rank class (0: R=8, 1: 16, 2: 32, 3: 64) or -1
     int32_t Dp;        // row stride of the unique-row buffer E (D rounded up to 4)
+    int64_t g3t_off;   // offset of this table's transposed G3 copy ([n3][d3][R2]) in Ws::g3t
 };
+
+constexpr int kMaxChunkRows = 32; // rows per forward work chunk (upper limit)
+
+// Context of one forward work chunk, built once per grouping (one 256-byte
+// record so the persistent kernel fetches it with a single wave-wide load).
+struct ChunkRec {
+    int32_t tile, t, nu, rbeg, rend, slot, i2, cls;
+    int32_t i1[4];      // first digit of each unit
+    int32_t ustart[4];  // unique id of each unit's first row inside the chunk
+    int32_t ccnt[4];    // rows of each unit inside the chunk
+    int32_t pstart[5];  // prefix of output tiles (16/d3 rows each) per unit
+    int32_t rowoff[5];  // prefix of ccnt
+    int32_t pad[2];
+    int32_t i3[kMaxChunkRows]; // third digit of every row of the chunk
+};
+static_assert(sizeof(ChunkRec) == 256, "chunk record is one 256-byte line");
 
 struct CorePtrs {
     const float *g[kMaxTables][3];
@@ -103,6 +120,9 @@ struct Ws {
     int32_t *chunk_tile;     // [2*nnz]
     int32_t *chunk_rbeg;     // [2*nnz]
     int32_t *chunk_rend;     // [2*nnz]
+    ChunkRec *crec;          // [chunk_cap]
+    int64_t chunk_cap;       // capacity of the chunk arrays
+    float *g3t;              // transposed G3 copies of the MFMA-class tables
     int32_t *heads;          // [num_blocks] queue heads
     int32_t *flags;          // [kMaxCkptSlots] checkpoint ready flags
     float *ckpt;             // [kMaxCkptSlots][4][16][max R2 + 4]
