@@ -181,6 +181,10 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
     ap.add_argument("--sched", type=int, default=0, help="0 default, 1 static, 2 steal, 3 steal+L2")
     ap.add_argument("--group", type=int, default=0, help="0 default, 1 prefix, 2 unique-only")
+    ap.add_argument("--mode", default="train", choices=("train", "fwd", "copy"),
+                    help="train: the full step (default); fwd: forward only on --config; "
+                         "copy: a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--config", type=int, default=4, help="workload of --mode fwd (1..4)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -193,11 +197,38 @@ def main():
     import tensor_train_compressed_gather_amd as tt
     from tensor_train_compressed_gather_amd import workloads as W
 
+    if args.mode == "copy":
+        n = 1 << 28  # 1 GiB of fp32
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"mode": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n, "ms": dt * 1e3,
+                          "GBps": 8 * n / dt / 1e9}), flush=True)
+        return
+
     opts = None
     if args.sched or args.group:
         opts = tt.tt_emb_options()
         opts.sched_mode = args.sched
         opts.group_mode = args.group
+
+    if args.mode == "fwd":
+        wf = W.make_workload(args.config)
+        bf = Bench(wf, torch, tt, opts)
+        fms, _, fph = bf.timed(bf.fwd, args.steps, args.warmup)
+        ur, up, nz, fc = bf.counts()
+        ff, _, _ = phase_flops(wf.tables, ur, up, nz)
+        fphase = {k: round(v[0] / max(v[1], 1), 4) for k, v in fph.items() if v[1]}
+        print(json.dumps({"mode": "fwd", "workload": W.CONFIG_NAMES[args.config], "ms": fms,
+                          "lookups_per_s": wf.nnz / (fms * 1e-3), "phases_ms": fphase,
+                          "contract_flops": ff, "unique_rows": sum(ur), "prefix_groups": sum(up),
+                          "sched_stats": fc}), flush=True)
+        return
 
     w = W.make_workload(5)
     b = Bench(w, torch, tt, opts)

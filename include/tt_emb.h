@@ -84,7 +84,7 @@ typedef struct {
     int32_t sched_mode;    /* TT_EMB_SCHED_* */
     int32_t group_mode;    /* TT_EMB_GROUP_* */
     int32_t chunk_rows;    /* max rows per forward work chunk, 1..32 (0 = 32) */
-    int32_t num_blocks;    /* persistent grid size (0 = 2 per compute unit) */
+    int32_t num_blocks;    /* persistent grid size (0 = one block per compute unit) */
     int32_t check_indices; /* 0 = on (default), 1 = on, -1 = off (caller guarantees) */
     int32_t force_generic; /* 1 = use the plain (non-MFMA) contraction kernels (testing) */
     int32_t reserved[2];

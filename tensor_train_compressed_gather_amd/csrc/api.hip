@@ -45,6 +45,7 @@ struct tt_emb {
     int sum_n[3];
     int64_t max_d1R1, max_R2d3, max_Dp;
     int64_t g3t_elems;
+    int cls_mask;
 };
 
 namespace {
@@ -126,7 +127,8 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.crec = (ChunkRec *)take(sizeof(ChunkRec) * chunks);
     w.chunk_cap = chunks;
     w.g3t = (float *)take(4 * (size_t)h->g3t_elems);
-    w.heads = (int32_t *)take(4 * (size_t)h->num_blocks);
+    // 4 classes x up to 4 blocks per CU, one 128-byte line each
+    w.heads = (int32_t *)take(4 * (size_t)h->num_blocks * 16 * 32);
     w.flags = (int32_t *)take(4 * (size_t)kMaxCkptSlots);
     w.ckpt = (float *)take(4 * (size_t)kMaxCkptSlots * (4 * (16 * 68 + 16)));
     // bounds on unique rows / units per table that do not depend on values
@@ -175,6 +177,7 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
         p->check_indices = h->check_indices;
         p->force_generic = h->force_generic;
         p->any_generic = h->any_generic;
+        p->cls_mask = h->cls_mask;
         p->key_bits = h->key_bits;
         p->key2_bits = h->key2_bits;
         p->key3_bits = h->key3_bits;
@@ -309,6 +312,21 @@ int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const in
             delete h;
             return rc;
         }
+        // work order is class-major: i2 bases follow the tables grouped by MFMA
+        // rank class (generic tables last), so each class owns a contiguous
+        // range of chunks and runs
+        h->cls_mask = 0;
+        {
+            uint64_t base = 0;
+            for (int c = 0; c <= 4; ++c)
+                for (auto &td : h->tabs) {
+                    const int rank = td.cls < 0 ? 4 : td.cls;
+                    if (rank != c) continue;
+                    td.i2_base = (uint32_t)base;
+                    base += (uint64_t)td.n2;
+                    if (td.cls >= 0) h->cls_mask |= 1 << td.cls;
+                }
+        }
         h->sumD = col;
         h->sum_n[0] = (int)b1;
         h->sum_n[1] = (int)b2;
@@ -326,7 +344,9 @@ int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const in
             int cus = 0;
             if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess || cus <= 0)
                 cus = 256;
-            h->num_blocks = (2 * cus + 7) / 8 * 8;
+            // one resident persistent block per CU: the contraction kernels
+            // need more than 256 registers per lane (one wave per SIMD)
+            h->num_blocks = (cus + 7) / 8 * 8;
         }
         if (hipMalloc((void **)&h->dtab, sizeof(TableDesc) * T) != hipSuccess) {
             delete h;

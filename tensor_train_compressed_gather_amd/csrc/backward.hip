@@ -733,8 +733,7 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
     timer_begin(p.timing, TM_BWD_CONTRACT, s);
     if (p.nnz > 0) {
         if (!p.force_generic) {
-            int cus = p.num_blocks / 2;
-            hipLaunchKernelGGL(k_bwd_mfma, dim3(cus > 0 ? cus : 1), dim3(kThreads), 0, s, a);
+            hipLaunchKernelGGL(k_bwd_mfma, dim3(p.num_blocks), dim3(kThreads), 0, s, a);
         }
         if (p.force_generic || p.any_generic)
             hipLaunchKernelGGL(k_bwd_runs, dim3(p.num_blocks * 2), dim3(kThreads), 0, s, a);

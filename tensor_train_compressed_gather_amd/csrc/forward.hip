@@ -50,13 +50,42 @@ __device__ __forceinline__ int victim_of(int me, int vi, int nb)
 
 __device__ __forceinline__ int range_begin(int v, int64_t C, int nb) { return (int)((int64_t)v * C / nb); }
 
-__global__ __launch_bounds__(kThreads) void k_queue_init(Ws ws, int nb)
+// Chunks are class-major (rank class 0..3, generic tables last).  Find the
+// first chunk of every class and give each class its own static ranges.
+// Queue heads sit on their own 128-byte lines (atomics on a shared line
+// serialise in L2).
+constexpr int kHeadPad = 32;
+
+// Blocks per CU of each rank class's persistent kernel (register-limited).
+constexpr int kClsOcc[4] = {4, 4, 3, 2};
+struct ClassGrid {
+    int nb[4];
+};
+
+__global__ __launch_bounds__(kThreads) void k_queue_init(Ws ws, ClassGrid g, int stride)
 {
+    __shared__ int cstart[6];
     const int64_t C = ws.ctrl[CTRL_CHUNKS];
     int split = ws.ctrl[CTRL_SPLIT];
     if (split > kMaxCkptSlots) split = kMaxCkptSlots;
-    for (int b = threadIdx.x; b < nb; b += blockDim.x) ws.heads[b] = range_begin(b, C, nb);
+    if (threadIdx.x <= 5) {
+        const int c = threadIdx.x; // first chunk whose class rank is >= c
+        int lo = 0, hi = (int)C;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            const int cls = ws.crec[mid].cls;
+            const int rank = cls < 0 ? 4 : cls;
+            if (rank < c) lo = mid + 1;
+            else hi = mid;
+        }
+        cstart[c] = c == 5 ? (int)C : lo;
+    }
+    __syncthreads();
+    for (int c = 0; c < 4; ++c)
+        for (int b = threadIdx.x; b < g.nb[c]; b += blockDim.x)
+            ws.heads[(c * stride + b) * kHeadPad] = cstart[c] + range_begin(b, cstart[c + 1] - cstart[c], g.nb[c]);
     for (int i = threadIdx.x; i < split; i += blockDim.x) ws.flags[i] = 0;
+    if (threadIdx.x < 5) ws.ctrl[CTRL_CLS_START + threadIdx.x] = cstart[threadIdx.x];
     if (threadIdx.x == 0) {
         ws.ctrl[CTRL_STEALS] = 0;
         ws.ctrl[CTRL_CKPT_HIT] = 0;
@@ -87,43 +116,78 @@ __global__ __launch_bounds__(kThreads) void k_g3t(FwdArgs a)
 // drained, probes the next 64 victims in parallel and retries.  Every chunk is
 // handed out exactly once (heads only grow) and the loop ends once every
 // victim has been seen drained.
-__device__ __forceinline__ int claim_start(const Ws &ws, int me, int vi, int nb, int nvict)
+__device__ __forceinline__ int claim_start(int32_t *heads, int me, int vi, int nb, int nvict)
 {
     int raw = 0x7fffffff;
-    if (vi < nvict && (threadIdx.x & 63) == 0) raw = atomicAdd(&ws.heads[victim_of(me, vi, nb)], 1);
+    if (vi < nvict && (threadIdx.x & 63) == 0) raw = atomicAdd(&heads[victim_of(me, vi, nb) * kHeadPad], 1);
     return raw;
 }
 
-__device__ int claim_finish(const Ws &ws, int me, int &vi, int nb, int nvict, int64_t C, int raw)
+// heads / chunk ids are offset by `base`, the class's first chunk; C = its count
+__device__ int claim_finish(int32_t *heads, int base, int me, int &vi, int nb, int nvict, int64_t C, int raw,
+                            int &steals)
 {
     const int lane = threadIdx.x & 63;
     for (;;) {
         if (vi >= nvict) return -1;
         const int v = victim_of(me, vi, nb);
         int got = -1;
-        if (lane == 0 && raw < range_begin(v + 1, C, nb)) got = raw;
+        if (lane == 0 && raw < base + range_begin(v + 1, C, nb)) got = raw;
         got = __shfl(got, 0, 64);
         if (got >= 0) {
-            if (vi != 0 && lane == 0) atomicAdd(&ws.ctrl[CTRL_STEALS], 1);
+            steals += vi != 0;
             return got;
         }
         const int cand = vi + 1 + lane;
         bool avail = false;
         if (cand < nvict) {
             const int vv = victim_of(me, cand, nb);
-            avail = __hip_atomic_load(&ws.heads[vv], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                    range_begin(vv + 1, C, nb);
+            avail = __hip_atomic_load(&heads[vv * kHeadPad], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                    base + range_begin(vv + 1, C, nb);
         }
         const uint64_t m = __ballot(avail);
         vi = m ? vi + 1 + (__ffsll((unsigned long long)m) - 1) : vi + 65;
-        raw = claim_start(ws, me, vi, nb, nvict);
+        raw = claim_start(heads, me, vi, nb, nvict);
     }
 }
 
 // One chunk of a tile on the matrix cores, R1 = R2 = R.
+// A operand of the next chunk's prefix tile (its G1 slices), issued before the
+// current chunk's E stores: on gfx9 loads and stores share one in-order
+// counter, so a load issued after the stores would also wait for them.
+__device__ __forceinline__ void prefetch_a(const FwdArgs &a, const ChunkRec &nr, float (&apf)[16], int &apf_tile)
+{
+    apf_tile = -1;
+    if (nr.cls < 0) return;
+    const int R = 8 << nr.cls, KQ = R >> 2;
+    const TableDesc &tb = a.tab[nr.t];
+    const int d1 = tb.d1;
+    const int lane = threadIdx.x & 63, li = lane & 15, kq = lane >> 4;
+    const int g = li >> 2, j1 = li & 3;
+    const bool ok = g < nr.nu && j1 < d1;
+    const float *src = a.cores.g[nr.t][0] + ((int64_t)(ok ? nr.i1[g] : 0) * d1 + (ok ? j1 : 0)) * R + kq * KQ;
+    if (KQ >= 4) {
+#pragma unroll
+        for (int s = 0; s < 16; s += 4) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (ok && s < KQ) v = *reinterpret_cast<const float4 *>(src + s);
+            apf[s] = v.x;
+            apf[s + 1] = v.y;
+            apf[s + 2] = v.z;
+            apf[s + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) apf[s] = (ok && s < KQ) ? src[s] : 0.f;
+    }
+    apf_tile = nr.tile;
+}
+
 template <int R>
 __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec, float *Cs,
-                                           float (&breg)[64], int &bkey, int &lds_tile, int *s_flag)
+                                           float (&breg)[64], int &bkey, int &lds_tile, int *s_flag,
+                                           float (&apf)[16], int &apf_tile, ChunkRec *rnext, bool has_next,
+                                           int pre, int &hits, int &misses, int c, int cn)
 {
     constexpr int KQ = R / 4;           // K values each lane feeds per output tile
     constexpr int NT = R / 4;           // 16-column tiles of the padded d2*R2 (d2 <= 4)
@@ -185,14 +249,18 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
                 for (int i = threadIdx.x; i < kCTile / 4; i += kThreads) dst[i] = src[i];
                 have = true;
             }
-            if (threadIdx.x == 0) atomicAdd(&a.ws.ctrl[have ? CTRL_CKPT_HIT : CTRL_CKPT_MISS], 1);
+            if (have) ++hits;
+            else ++misses;
         }
         if (!have) {
             const int g = li >> 2, j1 = li & 3;
             const bool oka = g < rec.nu && j1 < d1;
             const float *srcA = G1 + ((int64_t)(oka ? rec.i1[g] : 0) * d1 + (oka ? j1 : 0)) * R + kq * KQ;
             float areg[KQ];
-            if constexpr (KQ % 4 == 0) {
+            if (apf_tile == rec.tile) {
+#pragma unroll
+                for (int s = 0; s < KQ; ++s) areg[s] = apf[s];
+            } else if constexpr (KQ % 4 == 0) {
 #pragma unroll
                 for (int s = 0; s < KQ; s += 4) {
                     const float4 v = oka ? *reinterpret_cast<const float4 *>(srcA + s) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -247,7 +315,11 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
                 }
             }
             __syncthreads();
-            if (split && rec.rbeg == 0) {
+            // publish only when another block may run a later chunk of this tile:
+            // this block already holds the next claimed chunk, so a two-chunk
+            // tile whose second chunk is that one never needs the checkpoint
+            // (an agent-scope release writes back L2, which is not free)
+            if (split && rec.rbeg == 0 && (rec.nch > 2 || cn != c + 1)) {
                 float4 *dst = reinterpret_cast<float4 *>(a.ws.ckpt + (size_t)rec.slot * kCTile);
                 const float4 *src = reinterpret_cast<const float4 *>(Cs);
                 for (int i = threadIdx.x; i < kCTile / 4; i += kThreads) dst[i] = src[i];
@@ -260,6 +332,10 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
         lds_tile = rec.tile;
     }
     __syncthreads();
+    // the next chunk's record (its load was issued when this chunk started)
+    if (has_next && w == 0) reinterpret_cast<int *>(rnext)[lane] = pre;
+    __syncthreads();
+    if (has_next && rnext->tile != rec.tile) prefetch_a(a, *rnext, apf, apf_tile);
 
     // -------- unique rows E_u = C_unit . G3[i3_u], 16/d3 rows per output tile
     float *Et = a.ws.E + a.ws.ebase[t];
@@ -299,26 +375,34 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
     }
 }
 
-// Persistent contraction kernel for every table of an MFMA rank class.  Wave 0
-// keeps two chunks claimed ahead: while chunk i runs, the record of chunk i+1
-// is in flight and the claim of chunk i+2 is outstanding.
-__global__ __launch_bounds__(kThreads, 2) void k_contract(FwdArgs a)
+// Persistent contraction kernel for the tables of one MFMA rank class
+// (R1 = R2 = R).  Wave 0 keeps two chunks claimed ahead: while chunk i runs,
+// the record of chunk i+1 is in flight and the claim of chunk i+2 is
+// outstanding; the next chunk's A operand is loaded before this chunk's stores.
+template <int R>
+__global__ __launch_bounds__(kThreads, 2) void k_contract(FwdArgs a, int heads_stride)
 {
+    constexpr int CLS = R == 8 ? 0 : R == 16 ? 1 : R == 32 ? 2 : 3;
     __shared__ __attribute__((aligned(16))) float Cs[kCTile];
     __shared__ ChunkRec rbuf[2];
     __shared__ int s_cur, s_next, s_flag;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int nb = gridDim.x, me = blockIdx.x;
     const Ws &ws = a.ws;
-    const int64_t C = ws.ctrl[CTRL_CHUNKS];
+    const int base = ws.ctrl[CTRL_CLS_START + CLS];
+    const int64_t C = ws.ctrl[CTRL_CLS_START + CLS + 1] - base;
+    int32_t *heads = ws.heads + CLS * heads_stride * kHeadPad;
     const int nvict = a.sched == kSchedStatic ? 1 : nb;
-    float breg[64];
+    float breg[64], apf[16];
 #pragma unroll
     for (int i = 0; i < 64; ++i) breg[i] = 0.f;
-    int bkey = -1, lds_tile = -1, vi = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) apf[i] = 0.f;
+    int bkey = -1, lds_tile = -1, vi = 0, apf_tile = -1, steals = 0, hits = 0, misses = 0;
     if (w == 0) {
-        const int c0 = claim_finish(ws, me, vi, nb, nvict, C, claim_start(ws, me, vi, nb, nvict));
-        const int c1 = c0 < 0 ? -1 : claim_finish(ws, me, vi, nb, nvict, C, claim_start(ws, me, vi, nb, nvict));
+        const int c0 = claim_finish(heads, base, me, vi, nb, nvict, C, claim_start(heads, me, vi, nb, nvict), steals);
+        const int c1 = c0 < 0 ? -1
+                              : claim_finish(heads, base, me, vi, nb, nvict, C, claim_start(heads, me, vi, nb, nvict), steals);
         if (c0 >= 0) reinterpret_cast<int *>(&rbuf[0])[lane] = reinterpret_cast<const int *>(&ws.crec[c0])[lane];
         if (lane == 0) {
             s_cur = c0;
@@ -331,24 +415,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_contract(FwdArgs a)
         const int c = s_cur, cn = s_next;
         if (c < 0) break;
         int pre = 0, raw = 0x7fffffff;
-        if (w == 0) {
-            if (cn >= 0) {
-                pre = reinterpret_cast<const int *>(&ws.crec[cn])[lane];
-                raw = claim_start(ws, me, vi, nb, nvict);
-            }
+        if (w == 0 && cn >= 0) {
+            pre = reinterpret_cast<const int *>(&ws.crec[cn])[lane];
+            raw = claim_start(heads, me, vi, nb, nvict);
         }
-        const ChunkRec &rec = rbuf[buf];
-        switch (rec.cls) {
-        case 0: chunk_mfma<8>(a, rec, Cs, breg, bkey, lds_tile, &s_flag); break;
-        case 1: chunk_mfma<16>(a, rec, Cs, breg, bkey, lds_tile, &s_flag); break;
-        case 2: chunk_mfma<32>(a, rec, Cs, breg, bkey, lds_tile, &s_flag); break;
-        case 3: chunk_mfma<64>(a, rec, Cs, breg, bkey, lds_tile, &s_flag); break;
-        default: break; // tables outside the rank classes run in k_contract_generic
-        }
+        chunk_mfma<R>(a, rbuf[buf], Cs, breg, bkey, lds_tile, &s_flag, apf, apf_tile, &rbuf[buf ^ 1], cn >= 0, pre,
+                      hits, misses, c, cn);
         __syncthreads(); // everyone is done with rbuf[buf], s_cur and s_next
         if (w == 0) {
-            const int c2 = cn < 0 ? -1 : claim_finish(ws, me, vi, nb, nvict, C, raw);
-            if (cn >= 0) reinterpret_cast<int *>(&rbuf[buf ^ 1])[lane] = pre;
+            const int c2 = cn < 0 ? -1 : claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals);
             if (lane == 0) {
                 s_cur = cn;
                 s_next = c2;
@@ -356,6 +431,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_contract(FwdArgs a)
         }
         __syncthreads();
         buf ^= 1;
+    }
+    // scheduling statistics, one atomic per block
+    if (threadIdx.x == 0) {
+        if (steals) atomicAdd(&ws.ctrl[CTRL_STEALS], steals);
+        if (hits) atomicAdd(&ws.ctrl[CTRL_CKPT_HIT], hits);
+        if (misses) atomicAdd(&ws.ctrl[CTRL_CKPT_MISS], misses);
     }
 }
 
@@ -471,10 +552,16 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
     FwdArgs a{p.dtab, p.T, p.ws, cores, p.sched_mode};
     timer_begin(p.timing, TM_CONTRACT, s);
     if (p.nnz > 0) {
-        hipLaunchKernelGGL(k_queue_init, dim3(1), dim3(kThreads), 0, s, p.ws, p.num_blocks);
+        ClassGrid cg;
+        for (int c = 0; c < 4; ++c) cg.nb[c] = p.num_blocks * kClsOcc[c];
+        const int hs = p.num_blocks * 4;
+        hipLaunchKernelGGL(k_queue_init, dim3(1), dim3(kThreads), 0, s, p.ws, cg, hs);
         if (!p.force_generic) {
             hipLaunchKernelGGL(k_g3t, dim3(64, p.T), dim3(kThreads), 0, s, a);
-            hipLaunchKernelGGL(k_contract, dim3(p.num_blocks), dim3(kThreads), 0, s, a);
+            if (p.cls_mask & 1) hipLaunchKernelGGL(k_contract<8>, dim3(cg.nb[0]), dim3(kThreads), 0, s, a, hs);
+            if (p.cls_mask & 2) hipLaunchKernelGGL(k_contract<16>, dim3(cg.nb[1]), dim3(kThreads), 0, s, a, hs);
+            if (p.cls_mask & 4) hipLaunchKernelGGL(k_contract<32>, dim3(cg.nb[2]), dim3(kThreads), 0, s, a, hs);
+            if (p.cls_mask & 8) hipLaunchKernelGGL(k_contract<64>, dim3(cg.nb[3]), dim3(kThreads), 0, s, a, hs);
         }
         if (p.force_generic || p.any_generic)
             hipLaunchKernelGGL(k_contract_generic, dim3(p.num_blocks * 4), dim3(kThreads), 0, s, a,

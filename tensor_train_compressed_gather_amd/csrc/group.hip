@@ -472,7 +472,7 @@ struct ChunkOp {
 
 // One record per chunk: the digits, row ranges and per-row i3 the persistent
 // contraction kernel needs, gathered here in parallel.
-__global__ __launch_bounds__(kThreads) void k_chunk_records(const TableDesc *tab, int T, Ws ws)
+__global__ __launch_bounds__(kThreads) void k_chunk_records(const TableDesc *tab, int T, int S, Ws ws)
 {
     const int64_t C = ws.ctrl[CTRL_CHUNKS];
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -492,7 +492,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_records(const TableDesc *tab
         rec.slot = ws.tile_slot[tile];
         rec.i2 = ws.unit_prefix[u0] % tb.n2;
         rec.cls = tb.cls;
-        rec.pad[0] = rec.pad[1] = 0;
+        rec.nch = (ws.tile_rows[tile] + S - 1) / S;
+        rec.pad = 0;
         const int P = (tb.d3 > 0 && tb.d3 <= 16) ? 16 / tb.d3 : 1;
         int off = 0, coff = 0;
         rec.pstart[0] = 0;
@@ -594,7 +595,7 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
         if (e != hipSuccess) return e;
         int gc = ceil_div(ws.chunk_cap, kThreads);
         if (gc > 4096) gc = 4096;
-        hipLaunchKernelGGL(k_chunk_records, dim3(gc), dim3(kThreads), 0, s, p.dtab, T, ws);
+        hipLaunchKernelGGL(k_chunk_records, dim3(gc), dim3(kThreads), 0, s, p.dtab, T, p.chunk_rows, ws);
     }
     timer_end(p.timing, TM_GROUP_RLE, s);
     return hipGetLastError();

@@ -39,6 +39,7 @@ enum CtrlSlot {
     CTRL_CKPT_HIT = 10,  // split-tile chunks that found a published checkpoint
     CTRL_CKPT_MISS = 11, // split-tile chunks that recomputed the prefix tile
     CTRL_BWD_NEXT = 12,  // next run of the backward contraction (work counter)
+    CTRL_CLS_START = 16, // 5 words: first chunk of each MFMA rank class (chunks are class-major)
     CTRL_N = 64
 };
 enum ErrBits { ERRB_INDEX = 1, ERRB_OFFSETS = 2, ERRB_CAPACITY = 4 };
@@ -71,7 +72,8 @@ struct ChunkRec {
     int32_t ccnt[4];    // rows of each unit inside the chunk
     int32_t pstart[5];  // prefix of output tiles (16/d3 rows each) per unit
     int32_t rowoff[5];  // prefix of ccnt
-    int32_t pad[2];
+    int32_t nch;        // chunks of this chunk's tile
+    int32_t pad;
     int32_t i3[kMaxChunkRows]; // third digit of every row of the chunk
 };
 static_assert(sizeof(ChunkRec) == 256, "chunk record is one 256-byte line");
@@ -157,6 +159,7 @@ struct Plan {
     int num_blocks;
     int sched_mode, group_mode, chunk_rows, check_indices, force_generic;
     bool any_generic;
+    int cls_mask; // bit c set when some table is in MFMA rank class c
     int key_bits, key2_bits, key3_bits;
     int Dmax, R2max, sumD;
     int sum_n[3]; // sum over tables of n1, n2, n3
