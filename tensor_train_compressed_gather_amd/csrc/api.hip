@@ -94,7 +94,6 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.tab_grp_start = (int32_t *)take(4 * (T + 1));
     w.ebase = (int64_t *)take(8 * T);
     w.p3base = (int64_t *)take(8 * T);
-    w.g1base = (int64_t *)take(8 * T);
     if (h->group_mode == TT_EMB_GROUP_UNIQUE_ONLY) {
         w.unit_prefix = (int32_t *)take(4 * n);
         w.unit_start = (int32_t *)take(4 * (n + 1));
@@ -121,6 +120,8 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     if (units_bound > n) units_bound = n;
     int64_t chunks = n / h->chunk_rows + 1 + units_bound / 4 + 1 + h->sum_n[1] + 1;
     if (chunks > 2 * n + 1) chunks = 2 * n + 1;
+    w.tile_cstart = (int32_t *)take(4 * (n + 1));
+    w.uinv = (int32_t *)take(4 * n);
     w.chunk_tile = (int32_t *)take(4 * chunks);
     w.chunk_rbeg = (int32_t *)take(4 * chunks);
     w.chunk_rend = (int32_t *)take(4 * chunks);
@@ -132,19 +133,17 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.flags = (int32_t *)take(4 * (size_t)kMaxCkptSlots);
     w.ckpt = (float *)take(4 * (size_t)kMaxCkptSlots * (4 * (16 * 68 + 16)));
     // bounds on unique rows / units per table that do not depend on values
-    int64_t e_elems = 0, p3_elems = 0, g1_elems = 0;
+    int64_t e_elems = 0, p3_elems = 0;
     for (int t = 0; t < T; ++t) {
         const TableDesc &d = h->tabs[t];
         const int64_t urows = d.N < n ? d.N : n;
         const int64_t pre = (int64_t)d.n1 * d.n2;
-        const int64_t units = h->group_mode == TT_EMB_GROUP_UNIQUE_ONLY ? urows : (pre < n ? pre : n);
         e_elems += urows * d.Dp;
         p3_elems += urows * (int64_t)d.R2 * d.d3;
-        g1_elems += units * (int64_t)d.d1 * d.R1;
+        (void)pre;
     }
     if (e_elems > n * h->max_Dp) e_elems = n * h->max_Dp;
     if (p3_elems > n * h->max_R2d3) p3_elems = n * h->max_R2d3;
-    if (g1_elems > n * h->max_d1R1) g1_elems = n * h->max_d1R1;
     const int64_t pieces = n + n / kGuPiece + 1;
     const int64_t piece_elems = pieces * h->Dmax;
     w.E = (float *)take(4 * e_elems);
@@ -154,7 +153,8 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.u_piece_start = (int32_t *)take(4 * (n + 1));
     w.P3 = (float *)take(4 * (p3_elems > piece_elems ? p3_elems : piece_elems));
     w.piece_sum = w.P3;
-    w.G1P = (float *)take(4 * g1_elems);
+    // G1 partials are indexed by work position (< units) with a uniform stride
+    w.G1P = (float *)take(4 * (size_t)units_bound * h->max_d1R1);
     // buffers where the sorts end
     const int fm = sort_passes(nnz, h->key_bits) & 1;
     const int fu = sort_passes(nnz, h->key2_bits) & 1;
@@ -185,6 +185,7 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
         p->R2max = h->R2max;
         p->sumD = h->sumD;
         for (int k = 0; k < 3; ++k) p->sum_n[k] = h->sum_n[k];
+        p->g1stride = (int)h->max_d1R1;
         p->dtab = h->dtab;
         p->ws = w;
     }

@@ -36,6 +36,7 @@ struct BwdArgs {
     int SD;
     int Dmax; // row stride of the gather partials
     int force_generic;
+    int g1stride; // row stride of the G1 partials (max d1*R1)
 };
 
 // bag_of[l] for every lookup (clamped ranges; used only through clamps).
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_runs(BwdArgs a)
                 for (int j2 = 0; j2 < d2; ++j2)
                     for (int r2 = 0; r2 < R2; ++r2)
                         c = fmaf(dCl[(j1 * d2 + j2) * R2 + r2], G2[((int64_t)r1 * d2 + j2) * R2 + r2], c);
-                ws.G1P[ws.g1base[t] + (int64_t)unit * d1 * R1 + e] = c;
+                ws.G1P[(int64_t)k * a.g1stride + e] = c;
             }
             // dG2 slice: sum_j1 G1[i1][j1][r1] dC[j1*d2+j2][r2]
 #pragma unroll
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_g1(BwdArgs a, int total_slo
         float *dst = a.grads.g[t][0] + (int64_t)i1 * per;
         for (int e = threadIdx.x; e < per; e += kThreads) {
             float c = 0.f;
-            for (int unit = first; unit < last; ++unit) c += ws.G1P[ws.g1base[t] + (int64_t)unit * per + e];
+            for (int unit = first; unit < last; ++unit) c += ws.G1P[(int64_t)ws.uinv[unit] * a.g1stride + e];
             dst[e] = c;
         }
     }
@@ -379,329 +380,389 @@ __global__ __launch_bounds__(kThreads) void k_reduce_g3(BwdArgs a, const uint32_
 // ------------------------------------------------ matrix-core reverse contraction
 //
 // One block per (table, i2) run of a rank class R (R1 = R2 = R, d1, d2 <= 4,
-// d3 <= 16), runs taken from a shared counter.  The G2[i2] slice is staged in
-// LDS once per run with an XOR swizzle (column ^ (row & 31)), so it can be read
-// both along columns (recomputing C and accumulating dG2) and along rows
-// (forming the dG1 partials) without bank conflicts.  Per tile of <= 4 units:
+// d3 <= 16), one kernel per class, runs taken from a per-class counter.  The
+// run is walked through the forward's chunk records (tiles of <= 4 units,
+// chunks of <= 32 rows with their i3 digits), so no dependent index chasing
+// happens in the loop.  The G2[i2] slice is staged in LDS once per run with an
+// XOR swizzle (column ^ (row & 31)) so it can be read along columns (C and dG2)
+// and along rows (dG1 partials) without bank conflicts.  Per chunk the G1
+// slices of the tile, the output-gradient rows g_u and the transposed G3
+// slices of the rows are staged in LDS with one burst of independent loads.
+// Per tile of <= 4 units (g) and column col = j2*R + r2:
 //   (1) C[(g,j1)][col]  = sum_r1 G1[i1_g][j1][r1] G2[r1][col]          -> LDS
-//   (2) per row u:  dC_g += g_u . G3[i3_u]^T ;  P3_u = C_g^T . g_u     (g_u staged in LDS)
+//   (2) per row u:  dC_g += g_u . G3[i3_u]^T ;  P3_u = C_g^T . g_u     (P3 -> partial buffer)
 //   (3) G1P_g[j1][r1]   = sum_col dC[(g,j1)][col] G2[r1][col]           -> partial buffer
-//   (4) dG2[r1][col]   += sum_(g,j1) G1[i1_g][j1][r1] dC[(g,j1)][col]  (registers)
-// where col = j2*R + r2.  All products are v_mfma_f32_16x16x4_f32 tiles.
+//   (4) dG2[r1][col]   += sum_(g,j1) G1[i1_g][j1][r1] dC[(g,j1)][col]  (registers for the run)
+// All products are v_mfma_f32_16x16x4_f32 tiles.
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-constexpr int kBCStride = 68;                   // LDS row stride of C / dC tiles
-constexpr int kBCUnit = 16 * kBCStride + 16;    // floats per unit
-constexpr int kBGs = 8192;                      // floats of staged output-gradient rows
-
-struct BTileCtx {
-    int nu;
-    int unit[4], i1[4], ustart[4], rowoff[5];
-};
 
 __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// LDS layout (floats) of the class kernel for rank R.
 template <int R>
-__device__ __forceinline__ void bwd_run_mfma(const BwdArgs &a, int t, int i2, int k0, int k1, float *G2s,
-                                             float *Cs, float *dCs, float *Gs, BTileCtx *cx)
+struct BwdLds {
+    static constexpr int CLS = R == 8 ? 0 : R == 16 ? 1 : R == 32 ? 2 : 3;
+    static constexpr int NCOL = 4 * R;                 // columns (j2, r2), d2 padded to 4
+    static constexpr int CSTR = R + 4;                 // row stride of C / dC
+    static constexpr int CUNIT = 16 * CSTR + 16;       // floats per unit
+    static constexpr int G2S = R * NCOL;
+    static constexpr int CS = 4 * CUNIT;
+    static constexpr int G1ST = R + 1;                 // odd row stride: (1) reads rows across lanes
+    static constexpr int G1S = 16 * G1ST;              // [unit][j1][r1]
+    static constexpr int DTST = 17;                    // transposed dC: [col][(g, j1)], stride 17
+    static constexpr int STAGE = CLS == 3 ? 14336 : CLS == 2 ? 10240 : 6144;
+    static constexpr int TOTAL = G2S + 2 * CS + G1S + STAGE;
+    static constexpr int OCC = CLS == 3 ? 1 : CLS == 2 ? 2 : 4; // blocks per CU
+    static constexpr int NW = CLS == 3 ? 8 : 4;                  // waves per block
+};
+
+template <int R>
+__global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_class(BwdArgs a)
 {
-    constexpr int NCOL = 4 * R;          // columns (j2, r2) with d2 padded to 4
-    constexpr int NT = NCOL / 16;        // 16-column blocks
-    constexpr int NTW = (NT + 3) / 4;    // blocks per wave
-    constexpr int MT = (R + 15) / 16;    // 16-row blocks of r1 or r2
-    constexpr int KQ = R / 4;            // K values per lane for K = R
-    constexpr int KS = 4 / MT;           // K split of the dG1 partial over waves
-    constexpr int SPL = R / KS;
-    const TableDesc &tb = a.tab[t];
-    const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, n2 = tb.n2, n3 = tb.n3, D12 = d1 * d2, Dp = tb.Dp;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, kq = lane >> 4;
-    const float *G1 = a.cores.g[t][0];
-    const float *G3 = a.cores.g[t][2];
+    using L = BwdLds<R>;
+    constexpr int NW = L::NW, BT = NW * 64;
+    constexpr int NCOL = L::NCOL, NT = NCOL / 16, NTW = (NT + NW - 1) / NW, MT = (R + 15) / 16, KQ = R / 4;
+    constexpr int NIT = (4 * MT + NW - 1) / NW;  // (unit, r-block) items per wave
+    constexpr int KS = NW / MT, SPL = R / KS, CSTR = L::CSTR, CUNIT = L::CUNIT;
+    static_assert((SPL & (SPL - 1)) == 0, "k-split length is a power of two");
+    __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
+    __shared__ ChunkRec recs[2];
+    __shared__ int s_run;
+    // Cs holds C during a tile and dC at its end (C is dead by then); dT holds
+    // dC transposed ([col][(g, j1)]) for the dG1 partials
+    float *G2s = lds, *Cs = lds + L::G2S, *dT = Cs + L::CS, *G1s = dT + L::CS, *Sg = G1s + L::G1S;
+    static_assert(L::NCOL * L::DTST <= L::CS, "transposed dC fits in its region");
+    constexpr int G1ST = L::G1ST, DTST = L::DTST;
     const Ws &ws = a.ws;
-
-    {   // stage G2[i2] as G2s[r][col ^ (r & 31)], zero-padded to NCOL columns
-        const float *src = a.cores.g[t][1] + (int64_t)i2 * R * d2 * R;
-        for (int e = tid; e < R * NCOL; e += kThreads) {
-            const int r = e / NCOL, c = e - r * NCOL;
-            G2s[r * NCOL + (c ^ (r & 31))] = c < d2 * R ? src[r * d2 * R + c] : 0.f;
-        }
-    }
-    floatx4 g2acc[MT][NTW];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) g2acc[mt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    for (int k = k0; k < k1; k += 4) {
-        if (tid == 0) {
-            const int nu = k1 - k < 4 ? k1 - k : 4;
-            int off = 0;
-            for (int j = 0; j < 4; ++j) {
-                int unit = 0, i1 = 0, us = 0, cnt = 0;
-                if (j < nu) {
-                    unit = ws.uorder[k + j];
-                    i1 = ws.unit_prefix[unit] / n2;
-                    us = ws.unit_start[unit];
-                    cnt = ws.unit_start[unit + 1] - us;
-                }
-                cx->unit[j] = unit;
-                cx->i1[j] = i1;
-                cx->ustart[j] = us;
-                cx->rowoff[j] = off;
-                off += cnt;
-            }
-            cx->rowoff[4] = off;
-            cx->nu = nu;
-        }
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, kq = lane >> 4;
+    const int rbeg = ws.ctrl[CTRL_RUN_CLS + L::CLS], rend = ws.ctrl[CTRL_RUN_CLS + L::CLS + 1];
+    for (;;) {
+        if (tid == 0) s_run = rbeg + atomicAdd(&ws.ctrl[CTRL_BWD_NEXT + L::CLS], 1);
         __syncthreads();
-        const int nu = cx->nu;
-
-        // ---- (1) prefix tile C of the <= 4 units
-        {
-            const int g = li >> 2, j1 = li & 3;
-            const bool oka = g < nu && j1 < d1;
-            const float *srcA = G1 + ((int64_t)(oka ? cx->i1[g] : 0) * d1 + (oka ? j1 : 0)) * R + kq * KQ;
-            float areg[KQ];
-#pragma unroll
-            for (int s = 0; s < KQ; ++s) areg[s] = oka ? srcA[s] : 0.f;
-            floatx4 acc[NTW];
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KQ; ++s) {
-                const int r = kq * KQ + s;
-#pragma unroll
-                for (int j = 0; j < NTW; ++j) {
-                    const int ntg = w + 4 * j;
-                    if (ntg < NT) {
-                        const int col = ntg * 16 + li;
-                        acc[j] = mfma4(areg[s], G2s[r * NCOL + (col ^ (r & 31))], acc[j]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const int ntg = w + 4 * j;
-                if (ntg < NT) {
-                    const int col = ntg * 16 + li, j2 = col / R, r2 = col % R;
-                    if (j2 < d2) {
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            if (v < d1) Cs[kq * kBCUnit + (v * d2 + j2) * kBCStride + r2] = acc[j][v];
-                    }
-                }
+        const int run = s_run;
+        if (run >= rend) break;
+        const int c0 = ws.tile_cstart[ws.run_tile_start[run]], c1 = ws.tile_cstart[ws.run_tile_start[run + 1]];
+        if (w == 0) reinterpret_cast<int *>(&recs[0])[lane] = reinterpret_cast<const int *>(&ws.crec[c0])[lane];
+        __syncthreads();
+        const int t = recs[0].t, i2 = recs[0].i2;
+        const TableDesc &tb = a.tab[t];
+        const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, D12 = d1 * d2, Dp = tb.Dp, P = 16 / d3;
+        const float *G1 = a.cores.g[t][0];
+        const float *G3t = ws.g3t + tb.g3t_off;
+        // staged rows: g_u at stride Dp + 4, G3 slices as [j3][R + 16] (bank-spread)
+        const int GST = Dp + 4, G3J = R + 16, G3ST = d3 * G3J;
+        int rb = L::STAGE / (GST + G3ST);
+        rb = rb < kMaxChunkRows ? rb : kMaxChunkRows;
+        float *Gs = Sg, *G3s = Sg + rb * GST;
+        {   // stage G2[i2] as G2s[r][col ^ (r & 31)], zero-padded to NCOL columns
+            const float *src = a.cores.g[t][1] + (int64_t)i2 * R * d2 * R;
+            for (int e = tid; e < R * NCOL; e += BT) {
+                const int r = e / NCOL, c = e - r * NCOL;
+                G2s[r * NCOL + (c ^ (r & 31))] = c < d2 * R ? src[r * d2 * R + c] : 0.f;
             }
         }
-
-        // ---- (2) rows: dC accumulation and G3 partials, items (unit g, r2 block mb)
-        floatx4 dacc[MT];
+        floatx4 g2acc[MT][NTW], dacc[NIT];
 #pragma unroll
-        for (int ii = 0; ii < MT; ++ii) dacc[ii] = floatx4{0.f, 0.f, 0.f, 0.f};
-        const int nrows = cx->rowoff[4];
-        const int rch = kBGs / Dp;
-        const int P = 16 / d3;
-        for (int q0 = 0; q0 < nrows; q0 += rch) {
-            const int qn = nrows - q0 < rch ? nrows - q0 : rch;
-            __syncthreads(); // C tile complete; previous staged rows consumed
-            {
-                const int c4n = Dp >> 2;
-                for (int e = tid; e < qn * c4n; e += kThreads) {
-                    const int qq = e / c4n, c4 = e - qq * c4n, q = q0 + qq;
-                    int g = 0;
-                    while (g < 3 && q >= cx->rowoff[g + 1]) ++g;
-                    const int u = cx->ustart[g] + (q - cx->rowoff[g]);
-                    reinterpret_cast<float4 *>(Gs)[qq * c4n + c4] =
-                        reinterpret_cast<const float4 *>(ws.E + ws.ebase[t] + (int64_t)u * Dp)[c4];
-                }
-            }
-            __syncthreads();
+        for (int ii = 0; ii < NIT; ++ii) dacc[ii] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ii = 0; ii < MT; ++ii) {
-                const int item = w + 4 * ii, g = item / MT, mb = item % MT;
-                if (g >= nu) continue;
-                const int r2 = mb * 16 + li;
-                const bool okr = r2 < R;
-                const int qa = q0 > cx->rowoff[g] ? q0 : cx->rowoff[g];
-                const int qb = q0 + qn < cx->rowoff[g + 1] ? q0 + qn : cx->rowoff[g + 1];
-                // (2a) dC_g[m2][r2] += sum_j3 g_u[m2][j3] G3[i3_u][r2][j3]
-                for (int q = qa; q < qb; ++q) {
-                    const int u = cx->ustart[g] + (q - cx->rowoff[g]);
-                    const int i3 = ws.uniq_row[u] % n3;
-                    const float *g3 = G3 + ((int64_t)i3 * R + (okr ? r2 : 0)) * d3;
-                    const float *gq = Gs + (q - q0) * Dp;
-                    for (int j0 = 0; j0 < d3; j0 += 4) {
-                        const int j3 = j0 + kq;
-                        const float av = (li < D12 && j3 < d3) ? gq[li * d3 + j3] : 0.f;
-                        const float bv = (okr && j3 < d3) ? g3[j3] : 0.f;
-                        dacc[ii] = mfma4(av, bv, dacc[ii]);
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) g2acc[mt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+        int cur_tile = -1, buf = 0;
+        for (int c = c0; c < c1; ++c) {
+            const ChunkRec &rec = recs[buf];
+            // the next record travels while this chunk runs
+            int pre = 0;
+            if (w == 0 && c + 1 < c1) pre = reinterpret_cast<const int *>(&ws.crec[c + 1])[lane];
+            const int nu = rec.nu;
+            const bool new_tile = rec.tile != cur_tile;
+            const int nrows = rec.rowoff[4];
+            // ---- one burst of independent loads: the tile's G1 slices (new tile
+            // only, G1s[(g*4 + j1)*G1ST + r1], zeros outside) and the first batch of rows
+            const int c4g = Dp >> 2, c4t = (d3 * R) >> 2;
+            auto stage_rows = [&](int sb, int n) {
+                for (int e = tid; e < n * (c4g + c4t); e += BT) {
+                    const int qq = e / (c4g + c4t), rem = e - qq * (c4g + c4t), q = sb + qq;
+                    int j = 0;
+                    while (j < 3 && q >= rec.rowoff[j + 1]) ++j;
+                    if (rem < c4g) {
+                        const int u = rec.ustart[j] + (q - rec.rowoff[j]);
+                        *reinterpret_cast<float4 *>(Gs + qq * GST + 4 * rem) =
+                            reinterpret_cast<const float4 *>(ws.E + ws.ebase[t] + (int64_t)u * Dp)[rem];
+                    } else {
+                        const int r4 = rem - c4g, j3 = (4 * r4) / R, r = 4 * r4 - j3 * R;
+                        *reinterpret_cast<float4 *>(G3s + qq * G3ST + j3 * G3J + r) =
+                            reinterpret_cast<const float4 *>(G3t + (int64_t)rec.i3[q] * d3 * R)[r4];
                     }
                 }
-                // (2b) P3_u[r2][j3] = sum_m2 C_g[m2][r2] g_u[m2][j3], P rows per output tile
-                float ca[4];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int m2 = kq * 4 + s;
-                    ca[s] = (m2 < D12 && okr) ? Cs[g * kBCUnit + m2 * kBCStride + r2] : 0.f;
+            };
+            if (new_tile) {
+                for (int e = tid; e < 4 * R; e += BT) {
+                    const int gj = e / (R / 4), r4 = e - gj * (R / 4), g = gj >> 2, j1 = gj & 3;
+                    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (g < nu && j1 < d1) v = reinterpret_cast<const float4 *>(G1 + ((int64_t)rec.i1[g] * d1 + j1) * R)[r4];
+                    float *d = G1s + gj * G1ST + 4 * r4;
+                    d[0] = v.x;
+                    d[1] = v.y;
+                    d[2] = v.z;
+                    d[3] = v.w;
                 }
-                const int slot = li / d3, j3 = li - slot * d3;
-                for (int qs = qa; qs < qb; qs += P) {
-                    const int cnt = qb - qs < P ? qb - qs : P;
-                    const bool okb = slot < cnt;
-                    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+            stage_rows(0, nrows < rb ? nrows : rb);
+            __syncthreads();
+            if (new_tile) {
+                // ---- (1) prefix tile C
+                {
+                    const int g = li >> 2, j1 = li & 3;
+                    floatx4 acc[NTW];
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KQ; ++s) {
+                        const int r = kq * KQ + s;
+                        const float av = G1s[(g * 4 + j1) * G1ST + r];
+#pragma unroll
+                        for (int j = 0; j < NTW; ++j) {
+                            const int ntg = w + NW * j;
+                            if (ntg < NT) {
+                                const int col = ntg * 16 + li;
+                                acc[j] = mfma4(av, G2s[r * NCOL + (col ^ (r & 31))], acc[j]);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j) {
+                        const int ntg = w + NW * j;
+                        if (ntg < NT) {
+                            const int col = ntg * 16 + li, j2 = col / R, r2 = col % R;
+                            if (j2 < d2) {
+#pragma unroll
+                                for (int v = 0; v < 4; ++v)
+                                    if (v < d1) Cs[kq * CUNIT + (v * d2 + j2) * CSTR + r2] = acc[j][v];
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int ii = 0; ii < NIT; ++ii) dacc[ii] = floatx4{0.f, 0.f, 0.f, 0.f};
+                cur_tile = rec.tile;
+            }
+            // ---- (2) rows of this chunk, in staged batches of rb rows (the first is staged)
+            for (int sb = 0; sb < nrows; sb += rb) {
+                const int n = nrows - sb < rb ? nrows - sb : rb;
+                __syncthreads(); // C tile written; previous batch consumed
+                if (sb > 0) {
+                    stage_rows(sb, n);
+                    __syncthreads();
+                }
+#pragma unroll
+                for (int ii = 0; ii < NIT; ++ii) {
+                    const int item = w + NW * ii, g = item / MT, mb = item % MT;
+                    if (item >= 4 * MT || g >= nu) continue;
+                    const int r2 = mb * 16 + li;
+                    const bool okr = r2 < R;
+                    const int qa = sb > rec.rowoff[g] ? sb : rec.rowoff[g];
+                    const int qe = rec.rowoff[g] + rec.ccnt[g];
+                    const int qb = sb + n < qe ? sb + n : qe;
+                    // (2a) dC_g[m2][r2] += sum_j3 g_u[m2][j3] G3[i3_u][r2][j3]
+                    for (int q = qa; q < qb; ++q) {
+                        const float *gq = Gs + (q - sb) * GST;
+                        const float *g3 = G3s + (q - sb) * G3ST + (okr ? r2 : 0);
+                        for (int j0 = 0; j0 < d3; j0 += 4) {
+                            const int j3 = j0 + kq;
+                            const float av = (li < D12 && j3 < d3) ? gq[li * d3 + j3] : 0.f;
+                            const float bv = (okr && j3 < d3) ? g3[j3 * G3J] : 0.f;
+                            dacc[ii] = mfma4(av, bv, dacc[ii]);
+                        }
+                    }
+                    // (2b) P3_u[r2][j3] = sum_m2 C_g[m2][r2] g_u[m2][j3], P rows per output tile
+                    float ca[4];
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
                         const int m2 = kq * 4 + s;
-                        const float bv = (okb && m2 < D12) ? Gs[(qs + slot - q0) * Dp + m2 * d3 + j3] : 0.f;
-                        acc = mfma4(ca[s], bv, acc);
+                        ca[s] = (m2 < D12 && okr) ? Cs[g * CUNIT + m2 * CSTR + r2] : 0.f;
                     }
-                    if (okb) {
-                        const int u = cx->ustart[g] + (qs + slot - cx->rowoff[g]);
-                        float *dst = ws.P3 + ws.p3base[t] + (int64_t)u * R * d3 + j3;
+                    const int slot = li / d3, j3 = li - slot * d3;
+                    for (int qs = qa; qs < qb; qs += P) {
+                        const int cnt = qb - qs < P ? qb - qs : P;
+                        const bool okb = slot < cnt;
+                        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int rr = mb * 16 + 4 * kq + v;
-                            if (rr < R) dst[rr * d3] = acc[v];
+                        for (int s = 0; s < 4; ++s) {
+                            const int m2 = kq * 4 + s;
+                            const float bv = (okb && m2 < D12) ? Gs[(qs + slot - sb) * GST + m2 * d3 + j3] : 0.f;
+                            acc = mfma4(ca[s], bv, acc);
+                        }
+                        if (okb) {
+                            const int u = rec.ustart[g] + (qs + slot - rec.rowoff[g]);
+                            float *dst = ws.P3 + ws.p3base[t] + (int64_t)u * R * d3 + j3;
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const int rr = mb * 16 + 4 * kq + v;
+                                if (rr < R) dst[rr * d3] = acc[v];
+                            }
                         }
                     }
                 }
             }
-        }
-        __syncthreads(); // staged rows and C consumed
+            // ---- the record of the next chunk, and whether this tile ends here
+            __syncthreads();
+            if (w == 0 && c + 1 < c1) reinterpret_cast<int *>(&recs[buf ^ 1])[lane] = pre;
+            __syncthreads();
+            const bool tile_end = c + 1 == c1 || recs[buf ^ 1].tile != rec.tile;
+            if (tile_end) {
 #pragma unroll
-        for (int ii = 0; ii < MT; ++ii) {
-            const int item = w + 4 * ii, g = item / MT, mb = item % MT;
-            const int r2 = mb * 16 + li;
-            if (r2 < R) {
+                for (int ii = 0; ii < NIT; ++ii) {
+                    const int item = w + NW * ii, g = item / MT, mb = item % MT;
+                    const int r2 = mb * 16 + li;
+                    if (item < 4 * MT && r2 < R) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) dCs[g * kBCUnit + (4 * kq + v) * kBCStride + r2] = dacc[ii][v];
-            }
-        }
-        __syncthreads();
-
-        // ---- (3) G1 partial of each unit: sum_col dC[(g,j1)][col] G2[r1][col]
-        {
-            const int mb = w % MT, ks = w / MT;
-            const int g = li >> 2, j1 = li & 3;
-            const bool oka = kq < d2 && j1 < d1;
-            const float *arow = dCs + g * kBCUnit + (oka ? j1 * d2 + kq : 0) * kBCStride;
-            const int r1 = mb * 16 + li;
-            const bool okr = r1 < R;
-            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = ks * SPL; s < (ks + 1) * SPL; ++s) {
-                const int col = kq * R + s;
-                const float av = oka ? arow[s] : 0.f;
-                const float bv = okr ? G2s[r1 * NCOL + (col ^ (r1 & 31))] : 0.f;
-                acc = mfma4(av, bv, acc);
-            }
-            if constexpr (KS > 1) {
-                float *red = Gs; // staged rows are no longer needed
-#pragma unroll
-                for (int v = 0; v < 4; ++v) red[(w * 64 + lane) * 4 + v] = acc[v];
-                __syncthreads();
-                if (ks == 0) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        float sum = 0.f;
-#pragma unroll
-                        for (int kk = 0; kk < KS; ++kk) sum += red[((mb + kk * MT) * 64 + lane) * 4 + v];
-                        acc[v] = sum;
+                        for (int v = 0; v < 4; ++v) {
+                            const int m2 = 4 * kq + v;
+                            Cs[g * CUNIT + m2 * CSTR + r2] = dacc[ii][v];
+                            if (m2 < D12) dT[((m2 % d2) * R + r2) * DTST + g * 4 + m2 / d2] = dacc[ii][v];
+                        }
                     }
                 }
-            }
-            if (ks == 0 && okr && kq < nu) {
-                float *dst = ws.G1P + ws.g1base[t] + (int64_t)cx->unit[kq] * d1 * R + r1;
+                __syncthreads();
+                // ---- (3) G1 partial of each unit: sum_col dC[(g,j1)][col] G2[r1][col]
+                {
+                    const int mb = w % MT, ks = w / MT;
+                    const int g = li >> 2, j1 = li & 3;
+                    const bool oka = kq < d2 && j1 < d1;
+                    const float *acol = dT + kq * R * DTST + li; // dT[(kq*R + s)][(g, j1) = li]
+                    const int r1 = mb * 16 + li;
+                    const bool okr = r1 < R;
+                    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+                    // lanes of the two k-quarters sharing a half-wave walk their
+                    // columns 16 apart, so dT and G2s reads land in distinct banks
+                    const int rot = SPL >= 32 ? 16 * (kq & 1) : 0;
+#pragma unroll 8
+                    for (int sl = 0; sl < SPL; ++sl) {
+                        const int s = ks * SPL + ((sl + rot) & (SPL - 1));
+                        const int col = kq * R + s;
+                        const float av = oka ? acol[s * DTST] : 0.f;
+                        const float bv = okr ? G2s[r1 * NCOL + (col ^ (r1 & 31))] : 0.f;
+                        acc = mfma4(av, bv, acc);
+                    }
+                    if constexpr (KS > 1) {
+                        float *red = Sg; // staged rows are no longer needed
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (v < d1) dst[v * R] = acc[v];
-            }
-        }
-
-        // ---- (4) dG2 += G1^T dC over (g, j1)
-        {
-            float ga[MT][4];
+                        for (int v = 0; v < 4; ++v) red[(w * 64 + lane) * 4 + v] = acc[v];
+                        __syncthreads();
+                        if (ks == 0) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+                            for (int v = 0; v < 4; ++v) {
+                                float sum = 0.f;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int r1 = mt * 16 + li;
-                    const bool ok = kq < nu && s < d1 && r1 < R;
-                    ga[mt][s] = ok ? G1[((int64_t)cx->i1[kq] * d1 + s) * R + r1] : 0.f;
+                                for (int kk = 0; kk < KS; ++kk) sum += red[((mb + kk * MT) * 64 + lane) * 4 + v];
+                                acc[v] = sum;
+                            }
+                        }
+                    }
+                    if (ks == 0 && okr && kq < nu) {
+                        // partials are indexed by the unit's position in the work order
+                        float *dst = ws.G1P + (int64_t)(rec.ubeg + kq) * a.g1stride + r1;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (v < d1) dst[v * R] = acc[v];
+                    }
                 }
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const int ntg = w + 4 * j;
-                if (ntg < NT) {
-                    const int col = ntg * 16 + li, j2 = col / R, r2 = col % R;
-                    float bv[4];
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        bv[s] = (j2 < d2 && s < d1) ? dCs[kq * kBCUnit + (s * d2 + j2) * kBCStride + r2] : 0.f;
+                // ---- (4) dG2 += G1^T dC over (g, j1)
+                {
+                    float ga[MT][4];
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                        for (int s = 0; s < 4; ++s) g2acc[mt][j] = mfma4(ga[mt][s], bv[s], g2acc[mt][j]);
+                        for (int s = 0; s < 4; ++s) {
+                            const int r1 = mt * 16 + li;
+                            ga[mt][s] = r1 < R ? G1s[(kq * 4 + s) * G1ST + r1] : 0.f;
+                        }
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j) {
+                        const int ntg = w + NW * j;
+                        if (ntg < NT) {
+                            const int col = ntg * 16 + li, j2 = col / R, r2 = col % R;
+                            float bv[4];
+#pragma unroll
+                            for (int s = 0; s < 4; ++s)
+                                bv[s] = (j2 < d2 && s < d1) ? Cs[kq * CUNIT + (s * d2 + j2) * CSTR + r2] : 0.f;
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                                for (int s = 0; s < 4; ++s) g2acc[mt][j] = mfma4(ga[mt][s], bv[s], g2acc[mt][j]);
+                        }
+                    }
                 }
+                __syncthreads(); // before the next tile reuses G1s / Cs / dT
             }
+            buf ^= 1;
         }
-        __syncthreads(); // before the next tile reuses the LDS buffers
-    }
-    float *dst = a.grads.g[t][1] + (int64_t)i2 * R * d2 * R;
+        float *dst = a.grads.g[t][1] + (int64_t)i2 * R * d2 * R;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-        const int ntg = w + 4 * j;
-        if (ntg >= NT) continue;
-        const int col = ntg * 16 + li;
-        if (col >= d2 * R) continue;
+        for (int j = 0; j < NTW; ++j) {
+            const int ntg = w + NW * j;
+            if (ntg >= NT) continue;
+            const int col = ntg * 16 + li;
+            if (col >= d2 * R) continue;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r1 = mt * 16 + 4 * kq + v;
-                if (r1 < R) dst[(int64_t)r1 * d2 * R + col] = g2acc[mt][j][v];
-            }
+                for (int v = 0; v < 4; ++v) {
+                    const int r1 = mt * 16 + 4 * kq + v;
+                    if (r1 < R) dst[(int64_t)r1 * d2 * R + col] = g2acc[mt][j][v];
+                }
+        }
+        __syncthreads();
     }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void k_bwd_mfma(BwdArgs a)
+// Run-class boundaries (runs are class-major like the units) and counters.
+__global__ void k_bwd_prep(BwdArgs a)
 {
-    __shared__ __attribute__((aligned(16))) float G2s[64 * 256];
-    __shared__ __attribute__((aligned(16))) float Cs[4 * kBCUnit];
-    __shared__ __attribute__((aligned(16))) float dCs[4 * kBCUnit];
-    __shared__ __attribute__((aligned(16))) float Gs[kBGs];
-    __shared__ BTileCtx cx;
-    __shared__ int s_run;
     const Ws &ws = a.ws;
     const int nruns = ws.ctrl[CTRL_RUNS];
-    for (;;) {
-        if (threadIdx.x == 0) s_run = atomicAdd(&ws.ctrl[CTRL_BWD_NEXT], 1);
-        __syncthreads();
-        const int run = s_run;
-        if (run >= nruns) break;
-        const int k0 = ws.run_start[run], k1 = ws.run_start[run + 1];
-        const int u0 = ws.uorder[k0];
-        const int t = segment_of(ws.tab_unit_start, a.T, u0);
-        const TableDesc &tb = a.tab[t];
-        const int i2 = ws.unit_prefix[u0] % tb.n2;
-        switch (a.force_generic ? -1 : tb.cls) {
-        case 0: bwd_run_mfma<8>(a, t, i2, k0, k1, G2s, Cs, dCs, Gs, &cx); break;
-        case 1: bwd_run_mfma<16>(a, t, i2, k0, k1, G2s, Cs, dCs, Gs, &cx); break;
-        case 2: bwd_run_mfma<32>(a, t, i2, k0, k1, G2s, Cs, dCs, Gs, &cx); break;
-        case 3: bwd_run_mfma<64>(a, t, i2, k0, k1, G2s, Cs, dCs, Gs, &cx); break;
-        default: break; // handled by k_bwd_runs
+    const int c = threadIdx.x;
+    if (c <= 4) {
+        int lo = 0, hi = nruns;
+        while (lo < hi) { // first run whose class rank is >= c
+            const int mid = (lo + hi) >> 1;
+            const int t = segment_of(ws.tab_unit_start, a.T, ws.uorder[ws.run_start[mid]]);
+            const int cls = a.tab[t].cls, rank = cls < 0 ? 4 : cls;
+            if (rank < c) lo = mid + 1;
+            else hi = mid;
         }
-        __syncthreads();
+        ws.ctrl[CTRL_RUN_CLS + c] = lo;
+    }
+    if (c == 5) ws.ctrl[CTRL_RUN_CLS + 5] = nruns;
+    if (c < 4) ws.ctrl[CTRL_BWD_NEXT + c] = 0;
+}
+
+// Transposed G3 copies of the MFMA-class tables (G3t[i3][j3][r2]).
+__global__ __launch_bounds__(kThreads) void k_bwd_g3t(BwdArgs a)
+{
+    const int t = blockIdx.y;
+    const TableDesc &tb = a.tab[t];
+    if (tb.cls < 0) return;
+    const int R2 = tb.R2, d3 = tb.d3, per = R2 * d3;
+    const int64_t n = (int64_t)tb.n3 * per;
+    const float *src = a.cores.g[t][2];
+    float *dst = a.ws.g3t + tb.g3t_off;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i3 = i / per;
+        const int rem = (int)(i - i3 * per), j3 = rem / R2, r2 = rem - j3 * R2;
+        dst[i] = src[(i3 * R2 + r2) * d3 + j3];
     }
 }
 
 // Zero every dG2 core (runs overwrite the slices they own) and the run counter.
 __global__ __launch_bounds__(kThreads) void k_zero_g2(BwdArgs a)
 {
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.ws.ctrl[CTRL_BWD_NEXT] = 0;
     const int t = blockIdx.y;
     const TableDesc &tb = a.tab[t];
     const int64_t n = (int64_t)tb.n2 * tb.R1 * tb.d2 * tb.R2;
@@ -713,7 +774,8 @@ __global__ __launch_bounds__(kThreads) void k_zero_g2(BwdArgs a)
 hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs &cores,
                            const int64_t *offsets, const GradPtrs &grads, hipStream_t s)
 {
-    BwdArgs a{p.dtab, p.T, p.B, p.ws, cores, grads, grad_out, offsets, p.nnz, p.sumD, p.Dmax, p.force_generic};
+    BwdArgs a{p.dtab, p.T, p.B, p.ws, cores, grads, grad_out, offsets, p.nnz, p.sumD, p.Dmax, p.force_generic,
+              p.g1stride};
     const int T = p.T;
     const int sum_n1 = p.sum_n[0], sum_n3 = p.sum_n[2];
     timer_begin(p.timing, TM_BWD_GATHER, s);
@@ -733,7 +795,19 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
     timer_begin(p.timing, TM_BWD_CONTRACT, s);
     if (p.nnz > 0) {
         if (!p.force_generic) {
-            hipLaunchKernelGGL(k_bwd_mfma, dim3(p.num_blocks), dim3(kThreads), 0, s, a);
+            hipLaunchKernelGGL(k_bwd_prep, dim3(1), dim3(64), 0, s, a);
+            hipLaunchKernelGGL(k_bwd_g3t, dim3(64, T), dim3(kThreads), 0, s, a);
+            if (p.cls_mask & 1)
+                hipLaunchKernelGGL(k_bwd_class<8>, dim3(p.num_blocks * BwdLds<8>::OCC), dim3(BwdLds<8>::NW * 64), 0, s, a);
+            if (p.cls_mask & 2)
+                hipLaunchKernelGGL(k_bwd_class<16>, dim3(p.num_blocks * BwdLds<16>::OCC), dim3(BwdLds<16>::NW * 64), 0,
+                                   s, a);
+            if (p.cls_mask & 4)
+                hipLaunchKernelGGL(k_bwd_class<32>, dim3(p.num_blocks * BwdLds<32>::OCC), dim3(BwdLds<32>::NW * 64), 0,
+                                   s, a);
+            if (p.cls_mask & 8)
+                hipLaunchKernelGGL(k_bwd_class<64>, dim3(p.num_blocks * BwdLds<64>::OCC), dim3(BwdLds<64>::NW * 64), 0,
+                                   s, a);
         }
         if (p.force_generic || p.any_generic)
             hipLaunchKernelGGL(k_bwd_runs, dim3(p.num_blocks * 2), dim3(kThreads), 0, s, a);

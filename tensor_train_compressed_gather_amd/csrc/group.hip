@@ -355,17 +355,14 @@ __global__ void k_finalize_bases(const TableDesc *tab, int T, int unique_only, W
 {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
     if (!unique_only) ws.ctrl[CTRL_UNITS] = ws.ctrl[CTRL_G];
-    int64_t e = 0, p3 = 0, g1 = 0;
+    int64_t e = 0, p3 = 0;
     for (int t = 0; t < T; ++t) {
         const TableDesc &d = tab[t];
         const int64_t u0 = ws.tab_uniq_start[t], u1 = ws.tab_uniq_start[t + 1];
-        const int64_t n0 = ws.tab_unit_start[t], n1 = ws.tab_unit_start[t + 1];
         ws.ebase[t] = e - u0 * d.Dp;
         e += (u1 - u0) * d.Dp;
         ws.p3base[t] = p3 - u0 * (int64_t)d.R2 * d.d3;
         p3 += (u1 - u0) * (int64_t)d.R2 * d.d3;
-        ws.g1base[t] = g1 - n0 * (int64_t)d.d1 * d.R1;
-        g1 += (n1 - n0) * (int64_t)d.d1 * d.R1;
     }
 }
 
@@ -380,6 +377,14 @@ __global__ __launch_bounds__(kThreads) void k_unit_keys(const TableDesc *tab, in
         ws.keys0[k] = tab[t].i2_base + (uint32_t)(ws.unit_prefix[k] % tab[t].n2);
         ws.uvals0[k] = (int32_t)k;
     }
+}
+
+// Position of every unit in the work order.
+__global__ __launch_bounds__(kThreads) void k_uinv(Ws ws, const int32_t *uo)
+{
+    const int64_t Un = ws.ctrl[CTRL_UNITS];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < Un; k += stride) ws.uinv[uo[k]] = (int32_t)k;
 }
 
 struct RunOp {
@@ -449,6 +454,7 @@ struct ChunkOp {
         const uint32_t nch = (uint32_t)(v & 0xffffffffu);
         const uint32_t lo = (uint32_t)(excl & 0xffffffffu), hi = (uint32_t)(excl >> 32);
         ws.tile_rows[tile] = r;
+        ws.tile_cstart[tile] = (int32_t)lo;
         ws.tile_slot[tile] = (nch > 1 && hi < (uint32_t)kMaxCkptSlots) ? (int32_t)hi : -1;
         for (uint32_t c = 0; c < nch; ++c) {
             if ((int64_t)lo + c >= ws.chunk_cap) break; // reported by total()
@@ -467,6 +473,7 @@ struct ChunkOp {
         }
         ws.ctrl[CTRL_CHUNKS] = (int32_t)c;
         ws.ctrl[CTRL_SPLIT] = (int32_t)(tot >> 32);
+        ws.tile_cstart[ws.ctrl[CTRL_TILES]] = (int32_t)c;
     }
 };
 
@@ -493,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_records(const TableDesc *tab
         rec.i2 = ws.unit_prefix[u0] % tb.n2;
         rec.cls = tb.cls;
         rec.nch = (ws.tile_rows[tile] + S - 1) / S;
-        rec.pad = 0;
+        rec.ubeg = ubeg;
         const int P = (tb.d3 > 0 && tb.d3 <= 16) ? 16 / tb.d3 : 1;
         int off = 0, coff = 0;
         rec.pstart[0] = 0;
@@ -584,6 +591,7 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
         const uint32_t *k2 = u1 ? ws.keys1 : ws.keys0;
         const int32_t *uo = u1 ? ws.uvals1 : ws.uvals0;
         if (k2 != ws.ukey2 || uo != ws.uorder) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_uinv, dim3(g), dim3(kThreads), 0, s, ws, uo);
         RunOp rop{k2, ws};
         e = run_scan(rop, ws.part, scan_blocks(nnz), s);
         if (e != hipSuccess) return e;

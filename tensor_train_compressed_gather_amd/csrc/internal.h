@@ -38,8 +38,9 @@ enum CtrlSlot {
     CTRL_STEALS = 9,  // chunks taken from another block's range (statistics)
     CTRL_CKPT_HIT = 10,  // split-tile chunks that found a published checkpoint
     CTRL_CKPT_MISS = 11, // split-tile chunks that recomputed the prefix tile
-    CTRL_BWD_NEXT = 12,  // next run of the backward contraction (work counter)
+    CTRL_BWD_NEXT = 40,  // 4 words: next run of each class's backward contraction
     CTRL_CLS_START = 16, // 5 words: first chunk of each MFMA rank class (chunks are class-major)
+    CTRL_RUN_CLS = 24,   // 6 words: first run of each class, then the run count
     CTRL_N = 64
 };
 enum ErrBits { ERRB_INDEX = 1, ERRB_OFFSETS = 2, ERRB_CAPACITY = 4 };
@@ -73,7 +74,7 @@ struct ChunkRec {
     int32_t pstart[5];  // prefix of output tiles (16/d3 rows each) per unit
     int32_t rowoff[5];  // prefix of ccnt
     int32_t nch;        // chunks of this chunk's tile
-    int32_t pad;
+    int32_t ubeg;       // position of the tile's first unit in the work order
     int32_t i3[kMaxChunkRows]; // third digit of every row of the chunk
 };
 static_assert(sizeof(ChunkRec) == 256, "chunk record is one 256-byte line");
@@ -106,7 +107,6 @@ struct Ws {
     int32_t *tab_grp_start;  // [T+1]
     int64_t *ebase;     // [T] element offset of table t's unique rows in E, minus tab_uniq_start*D
     int64_t *p3base;    // [T] same for the backward G3 partials
-    int64_t *g1base;    // [T] same for the backward G1 partials (per unit)
     // work units and the B-stationary work list
     int32_t *unit_prefix;    // [nnz]   (aliases grp_prefix in PREFIX mode)
     int32_t *unit_start;     // [nnz+1] (aliases grp_start in PREFIX mode)
@@ -119,6 +119,8 @@ struct Ws {
     int32_t *tile_nu;        // [nnz]
     int32_t *tile_rows;      // [nnz]
     int32_t *tile_slot;      // [nnz] checkpoint slot or -1
+    int32_t *tile_cstart;    // [tiles+1] first chunk of each tile
+    int32_t *uinv;           // [units] position of each unit in the work order
     int32_t *chunk_tile;     // [2*nnz]
     int32_t *chunk_rbeg;     // [2*nnz]
     int32_t *chunk_rend;     // [2*nnz]
@@ -163,6 +165,7 @@ struct Plan {
     int key_bits, key2_bits, key3_bits;
     int Dmax, R2max, sumD;
     int sum_n[3]; // sum over tables of n1, n2, n3
+    int g1stride; // row stride of the G1 partials (max d1*R1 over tables)
     const TableDesc *dtab; // device copy
     Ws ws;
 };
