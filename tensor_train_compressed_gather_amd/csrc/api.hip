@@ -45,7 +45,7 @@ struct tt_emb {
     int sum_n[3];
     int64_t max_d1R1, max_R2d3, max_Dp;
     int64_t g3t_elems;
-    int cls_mask;
+    int cls_mask, gcls_mask;
 };
 
 namespace {
@@ -144,15 +144,14 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     }
     if (e_elems > n * h->max_Dp) e_elems = n * h->max_Dp;
     if (p3_elems > n * h->max_R2d3) p3_elems = n * h->max_R2d3;
-    const int64_t pieces = n + n / kGuPiece + 1;
-    const int64_t piece_elems = pieces * h->Dmax;
+    // gradient gather: tasks of kGuTask sorted positions per table, two partial rows each
+    const int64_t tasks = n / kGuTask + T + 1;
+    const int64_t part_elems = tasks * 2 * h->Dpmax;
     w.E = (float *)take(4 * e_elems);
-    w.bag_of = (int32_t *)take(4 * n);
-    w.piece_u = (int32_t *)take(4 * pieces);
-    w.piece_k = (int32_t *)take(4 * pieces);
-    w.u_piece_start = (int32_t *)take(4 * (n + 1));
-    w.P3 = (float *)take(4 * (p3_elems > piece_elems ? p3_elems : piece_elems));
-    w.piece_sum = w.P3;
+    w.lk = (int2 *)take(8 * n);
+    w.gu_ml = (int32_t *)take(4 * tasks);
+    w.gu_mr = (int32_t *)take(4 * tasks);
+    w.P3 = (float *)take(4 * (p3_elems > part_elems ? p3_elems : part_elems));
     // G1 partials are indexed by work position (< units) with a uniform stride
     w.G1P = (float *)take(4 * (size_t)units_bound * h->max_d1R1);
     // buffers where the sorts end
@@ -178,10 +177,12 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
         p->force_generic = h->force_generic;
         p->any_generic = h->any_generic;
         p->cls_mask = h->cls_mask;
+        p->gcls_mask = h->gcls_mask;
         p->key_bits = h->key_bits;
         p->key2_bits = h->key2_bits;
         p->key3_bits = h->key3_bits;
         p->Dmax = h->Dmax;
+        p->Dpmax = h->Dpmax;
         p->R2max = h->R2max;
         p->sumD = h->sumD;
         for (int k = 0; k < 3; ++k) p->sum_n[k] = h->sum_n[k];
@@ -329,6 +330,18 @@ int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const in
                 }
         }
         h->sumD = col;
+        // gradient-gather class: rows move as float4 when every row of the
+        // table's columns starts 16-byte aligned; lanes per row = columns
+        // (float4 or float) rounded up to a power of two, at most 64
+        h->gcls_mask = 0;
+        for (auto &td : h->tabs) {
+            const bool vec = ((col | td.col_off) & 3) == 0;
+            const int cn = vec ? (td.D + 3) / 4 : td.D;
+            int lg = 0;
+            while (lg < 6 && (1 << lg) < cn) ++lg;
+            td.gcls = lg + (vec ? 8 : 0);
+            h->gcls_mask |= 1 << td.gcls;
+        }
         h->sum_n[0] = (int)b1;
         h->sum_n[1] = (int)b2;
         h->sum_n[2] = (int)b3;
@@ -479,15 +492,14 @@ int tt_emb_sgd_update(tt_emb_t h, float *const *cores, const float *const *core_
     hipStream_t s = (hipStream_t)stream;
     Timing *tm = (h->timing && h->timing->on) ? h->timing : nullptr;
     timer_begin(tm, TM_SGD, s);
+    std::vector<int64_t> cnt(3 * (size_t)h->T);
     for (int t = 0; t < h->T; ++t) {
         const TableDesc &d = h->tabs[t];
-        const int64_t cnt[3] = {(int64_t)d.n1 * d.d1 * d.R1, (int64_t)d.n2 * d.R1 * d.d2 * d.R2,
-                                (int64_t)d.n3 * d.R2 * d.d3};
-        for (int k = 0; k < 3; ++k) {
-            hipError_t e = launch_sgd(cores[3 * t + k], core_grads[3 * t + k], cnt[k], lr, s);
-            if (e != hipSuccess) return TT_EMB_ERR_HIP;
-        }
+        cnt[3 * t + 0] = (int64_t)d.n1 * d.d1 * d.R1;
+        cnt[3 * t + 1] = (int64_t)d.n2 * d.R1 * d.d2 * d.R2;
+        cnt[3 * t + 2] = (int64_t)d.n3 * d.R2 * d.d3;
     }
+    if (launch_sgd(cores, core_grads, cnt.data(), 3 * h->T, lr, s) != hipSuccess) return TT_EMB_ERR_HIP;
     timer_end(tm, TM_SGD, s);
     return TT_EMB_OK;
 }

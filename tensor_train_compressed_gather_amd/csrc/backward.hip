@@ -12,8 +12,9 @@
 //   dG2[i2]    += G1[i1]^T . dC_p         over units with that i2
 // Every sum runs in a fixed order and no floating-point atomic touches a
 // result, so the gradients are bit-reproducible:
-//   * g_u is summed over the sorted lookup run of u; runs longer than one
-//     piece are cut into fixed pieces whose partials are added in order;
+//   * g_u is summed over the sorted lookup run of u; the sorted positions are
+//     cut into fixed tasks and the parts of a run cut by task edges are added
+//     in task order;
 //   * one block owns one run of units sharing (table, i2) and keeps dG2[i2] in
 //     registers, writing it once;
 //   * dG1 and dG3 contributions go to per-unit / per-row partial buffers and
@@ -34,143 +35,248 @@ struct BwdArgs {
     const int64_t *offsets;
     int64_t nnz;
     int SD;
-    int Dmax; // row stride of the gather partials
+    int gstride; // row stride of the gather partial slots (max Dp)
     int force_generic;
     int g1stride; // row stride of the G1 partials (max d1*R1)
 };
 
-// bag_of[l] for every lookup (clamped ranges; used only through clamps).
-__global__ __launch_bounds__(kThreads) void k_bag_of(BwdArgs a)
+// (bag within its table, unique row) of every lookup, in lookup order, so the
+// gather reads both with one load per sorted position.  A block takes
+// kThreads bags; their lookups are contiguous, so lanes walk them coalesced
+// and find their bag by binary search over the block's offsets in LDS.
+__global__ __launch_bounds__(kThreads) void k_lookup_meta(BwdArgs a)
 {
+    __shared__ int64_t so[kThreads + 1];
     const int64_t nbags = (int64_t)a.T * a.B;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nbags; b += stride) {
-        int64_t lo = a.offsets[b], hi = a.offsets[b + 1];
-        lo = lo < 0 ? 0 : (lo > a.nnz ? a.nnz : lo);
-        hi = hi < lo ? lo : (hi > a.nnz ? a.nnz : hi);
-        for (int64_t l = lo; l < hi; ++l) a.ws.bag_of[l] = (int32_t)b;
+    for (int64_t b0 = (int64_t)blockIdx.x * kThreads; b0 < nbags; b0 += (int64_t)gridDim.x * kThreads) {
+        const int nb = nbags - b0 < kThreads ? (int)(nbags - b0) : kThreads;
+        for (int i = threadIdx.x; i <= nb; i += kThreads) {
+            const int64_t o = a.offsets[b0 + i];
+            so[i] = o < 0 ? 0 : (o > a.nnz ? a.nnz : o);
+        }
+        __syncthreads();
+        const int64_t lo = so[0], hi = so[nb];
+        for (int64_t l = lo + threadIdx.x; l < hi; l += kThreads) {
+            int i0 = 0, i1 = nb; // last i < nb with so[i] <= l
+            while (i1 - i0 > 1) {
+                const int mid = (i0 + i1) >> 1;
+                if (so[mid] <= l) i0 = mid;
+                else i1 = mid;
+            }
+            const int64_t b = b0 + i0;
+            a.ws.lk[l] = make_int2((int)(b - (b / a.B) * a.B), a.ws.inv[l]);
+        }
+        __syncthreads();
     }
 }
 
-// Pieces of the gradient gather: run u is cut into ceil(len / kGuPiece) pieces.
-struct PieceOp {
-    Ws ws;
-    __device__ int64_t count() const { return ws.ctrl[CTRL_U]; }
-    __device__ uint64_t value(int64_t u) const
-    {
-        const int64_t len = ws.uniq_start[u + 1] - ws.uniq_start[u];
-        return (uint64_t)((len + kGuPiece - 1) / kGuPiece);
-    }
-    __device__ void emit(int64_t u, uint64_t excl, uint64_t v) const
-    {
-        ws.u_piece_start[u] = (int32_t)excl;
-        for (uint64_t j = 0; j < v; ++j) {
-            ws.piece_u[excl + j] = (int32_t)u;
-            ws.piece_k[excl + j] = ws.uniq_start[u] + (int32_t)j * kGuPiece;
-        }
-    }
-    __device__ void total(uint64_t tot, int64_t U) const
-    {
-        ws.ctrl[CTRL_PIECES] = (int32_t)tot;
-        ws.u_piece_start[U] = (int32_t)tot;
-    }
+// Gather task numbering.  The sorted positions of table t,
+// [tstart[t], tstart[t+1]), are cut into tasks of kGuTask positions; table t
+// owns tasks [base[t], base[t+1]) of the global order (partial slots, cut-run
+// records) and [cbase[t], cbase[t+1]) of the order of gather class gcls (all
+// tables when gcls < 0).  Both prefixes are built in LDS by wave 0.
+// Per-table values a gather task needs, copied to LDS once per block so that
+// no global load issued between a worker's stores has to wait for them.
+struct GuTab {
+    int64_t ebase;
+    int ts, te, u0, u1, D, Dp, col_off, pad;
 };
 
-// One wave per piece: sum grad_out rows of the piece's lookups (sorted order).
-// Single-piece runs write g_u straight into the unique-row buffer (E's space);
-// longer runs write a partial, combined in piece order by k_gu_combine.
-__global__ __launch_bounds__(kThreads) void k_gu_pieces(BwdArgs a)
+__device__ void gu_bases(const BwdArgs &a, int gcls, int *base, int *cbase, GuTab *gt)
 {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (threadIdx.x < 64) {
+        const int t = threadIdx.x;
+        int n = 0, c = 0;
+        if (t < a.T) {
+            const TableDesc &tb = a.tab[t];
+            gt[t] = GuTab{a.ws.ebase[t], a.ws.tstart[t], a.ws.tstart[t + 1], a.ws.tab_uniq_start[t],
+                          a.ws.tab_uniq_start[t + 1], tb.D, tb.Dp, tb.col_off, 0};
+            const int len = a.ws.tstart[t + 1] - a.ws.tstart[t];
+            n = len > 0 ? (len + kGuTask - 1) / kGuTask : 0;
+            c = (gcls < 0 || a.tab[t].gcls == gcls) ? n : 0;
+        }
+        for (int o = 1; o < 64; o <<= 1) {
+            const int yn = __shfl_up(n, o, 64), yc = __shfl_up(c, o, 64);
+            if (t >= o) {
+                n += yn;
+                c += yc;
+            }
+        }
+        if (t == 0) base[0] = cbase[0] = 0;
+        if (t < a.T) {
+            base[t + 1] = n;
+            cbase[t + 1] = c;
+        }
+    }
+    __syncthreads();
+}
+
+// Last table t < T with pre[t] <= id (pre non-decreasing, pre[0] = 0 <= id).
+__device__ inline int gu_table(const int *pre, int T, int id)
+{
+    int lo = 0, hi = T;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= id) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Gradient gather g_u = sum of grad_out rows over the lookups of unique row u,
+// for the tables of one gather class.  A worker is a group of LPR lanes (one
+// grad_out row per instruction, a float4 or a float per lane); it walks the
+// positions of its task in sorted order, kGuBatch rows in flight, summing
+// runs of equal u.  A run that lies inside the task goes straight to u's slot
+// of the unique-row buffer (E's space); a run cut by the task's left or right
+// edge leaves its sum in the task's left or right partial slot, recorded in
+// gu_ml / gu_mr, and k_gu_join adds the parts in task order.  The order of
+// every sum is fixed by the task cut alone.
+template <int LPR, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_gu_gather(BwdArgs a, int gcls)
+{
+    constexpr int G = 64 / LPR;                                // workers per wave
+    constexpr int NS = LPR >= kGuBatch ? 1 : kGuBatch / LPR;   // metadata slots per lane
+    __shared__ int base[kMaxTables + 1], cbase[kMaxTables + 1];
+    __shared__ GuTab gt[kMaxTables];
+    gu_bases(a, gcls, base, cbase, gt);
     const Ws &ws = a.ws;
-    const int64_t np = ws.ctrl[CTRL_PIECES];
-    const int64_t nbags = (int64_t)a.T * a.B;
-    for (int64_t p = (int64_t)blockIdx.x * 4 + w; p < np; p += (int64_t)gridDim.x * 4) {
-        const int u = ws.piece_u[p];
-        const int k0 = ws.piece_k[p];
-        const int kend = ws.uniq_start[u + 1];
-        const int k1 = k0 + kGuPiece < kend ? k0 + kGuPiece : kend;
-        const int t = segment_of(ws.tab_uniq_start, a.T, u);
-        const TableDesc &tb = a.tab[t];
-        const int D = tb.D;
-        const bool single = (ws.u_piece_start[u + 1] - ws.u_piece_start[u]) == 1;
-        float *dst = single ? ws.E + ws.ebase[t] + (int64_t)u * tb.Dp : ws.P3 + p * (int64_t)a.Dmax;
-        const float *go = a.grad_out + tb.col_off;
-        // lanes per row: float4 columns rounded up to a power of two; rows in flight
-        const int c4n = (D + 3) >> 2;
-        int lpr = 1;
-        while (lpr < c4n) lpr <<= 1;
-        const bool vec = lpr <= 64 && ((a.SD | tb.col_off) & 3) == 0;
-        if (vec) {
-            const int rf = 64 / lpr, c4 = lane & (lpr - 1), r = lane / lpr;
-            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int kb = k0; kb < k1; kb += 64) {
-                const int nk = k1 - kb < 64 ? k1 - kb : 64;
-                // the bag (row of grad_out) of lookups kb .. kb+63, one per lane
-                int64_t bb = 0;
-                if (lane < nk) {
-                    int64_t bag = ws.bag_of[ws.perm[kb + lane]];
-                    bag = bag < 0 ? 0 : (bag >= nbags ? nbags - 1 : bag);
-                    const int64_t b = bag - (int64_t)t * a.B;
-                    bb = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
-                }
-#pragma unroll 4
-                for (int i = 0; i < nk; i += rf) {
-                    const int64_t row = __shfl(bb, i + r < 64 ? i + r : 0, 64);
-                    if (i + r < nk && c4 < c4n) {
-                        const float4 v = reinterpret_cast<const float4 *>(go + row * a.SD)[c4];
-                        acc.x += v.x;
-                        acc.y += v.y;
-                        acc.z += v.z;
-                        acc.w += v.w;
+    const int T = a.T, ntask = cbase[T];
+    const int lane = threadIdx.x & 63, grp = lane / LPR, gl = lane - grp * LPR;
+    const int gwave = (blockIdx.x * kThreads + threadIdx.x) >> 6;
+    const int nworkers = gridDim.x * (kThreads / 64) * G;
+    const int64_t SD = a.SD;
+    for (int id = gwave * G + grp; id < ntask; id += nworkers) {
+        const int t = gu_table(cbase, T, id);
+        const int task = base[t] + (id - cbase[t]);
+        const GuTab tb = gt[t];
+        const int ts = tb.ts, te = tb.te;
+        const int k0 = ts + (id - cbase[t]) * kGuTask;
+        const int k1 = k0 + kGuTask < te ? k0 + kGuTask : te;
+        const int u0 = tb.u0, u1 = tb.u1;
+        int mL = -1, mR = -1;
+        if (u1 > u0) {
+            auto clampu = [&](int u) { return u < u0 ? u0 : (u >= u1 ? u1 - 1 : u); };
+            const int D = tb.D, Dp = tb.Dp;
+            float *Eu = ws.E + tb.ebase;
+            const float *go = a.grad_out + tb.col_off;
+            float *slotL = ws.P3 + (int64_t)(2 * task) * a.gstride, *slotR = slotL + a.gstride;
+            // unique rows of the positions just outside the task (-1: table edge)
+            const int uleft = k0 > ts ? clampu(ws.lk[ws.perm[k0 - 1]].y) : -1;
+            const int uright = k1 < te ? clampu(ws.lk[ws.perm[k1]].y) : -1;
+            const int cn = VEC ? (D + 3) >> 2 : D; // columns in float4 (or float) units
+            for (int cb = 0; cb < cn; cb += LPR) {
+                const int c = cb + gl;
+                const bool okc = c < cn;
+                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+                int ucur = -1;
+                bool first = true;
+                auto flush = [&](bool last) {
+                    const bool cutl = first && ucur == uleft;
+                    const bool cutr = last && ucur == uright;
+                    if (cutl) mL = ucur;
+                    if (cutr) mR = ucur;
+                    float *dst = cutl ? slotL : (cutr ? slotR : Eu + (int64_t)ucur * Dp);
+                    if (!okc) return;
+                    if (VEC) {
+                        const int j = 4 * c;
+                        if (j + 3 < D) {
+                            *reinterpret_cast<float4 *>(dst + j) = acc;
+                        } else {
+                            if (j + 0 < D) dst[j + 0] = acc.x;
+                            if (j + 1 < D) dst[j + 1] = acc.y;
+                            if (j + 2 < D) dst[j + 2] = acc.z;
+                        }
+                    } else {
+                        dst[c] = acc.x;
+                    }
+                };
+                for (int kb = k0; kb < k1; kb += kGuBatch) {
+                    // metadata of the batch: position kb + e sits in lane e % LPR, slot e / LPR
+                    int bg[NS], uu[NS];
+#pragma unroll
+                    for (int sl = 0; sl < NS; ++sl) {
+                        const int e = sl * LPR + gl, pos = kb + e;
+                        bg[sl] = 0;
+                        uu[sl] = -1;
+                        if (e < kGuBatch && pos < k1) {
+                            const int2 m = ws.lk[ws.perm[pos]];
+                            bg[sl] = m.x < 0 ? 0 : (m.x >= a.B ? (int)a.B - 1 : m.x);
+                            uu[sl] = clampu(m.y);
+                        }
+                    }
+                    float4 row[kGuBatch];
+#pragma unroll
+                    for (int ii = 0; ii < kGuBatch; ++ii) {
+                        const int src = grp * LPR + ii % LPR;
+                        const int b = __shfl(bg[ii / LPR < NS ? ii / LPR : 0], src, 64);
+                        row[ii] = make_float4(0.f, 0.f, 0.f, 0.f);
+                        if (okc && kb + ii < k1) {
+                            const float *gr = go + (int64_t)b * SD;
+                            if (VEC) row[ii] = reinterpret_cast<const float4 *>(gr)[c];
+                            else row[ii].x = gr[c];
+                        }
+                    }
+#pragma unroll
+                    for (int ii = 0; ii < kGuBatch; ++ii) {
+                        const int src = grp * LPR + ii % LPR;
+                        const int u = __shfl(uu[ii / LPR < NS ? ii / LPR : 0], src, 64);
+                        if (kb + ii < k1) {
+                            if (u != ucur) {
+                                if (ucur >= 0) {
+                                    flush(false);
+                                    first = false;
+                                }
+                                ucur = u;
+                                acc = make_float4(0.f, 0.f, 0.f, 0.f);
+                            }
+                            acc.x += row[ii].x;
+                            if (VEC) {
+                                acc.y += row[ii].y;
+                                acc.z += row[ii].z;
+                                acc.w += row[ii].w;
+                            }
+                        }
                     }
                 }
+                if (ucur >= 0) flush(true);
             }
-            for (int m = lpr; m < 64; m <<= 1) {
-                acc.x += __shfl_xor(acc.x, m, 64);
-                acc.y += __shfl_xor(acc.y, m, 64);
-                acc.z += __shfl_xor(acc.z, m, 64);
-                acc.w += __shfl_xor(acc.w, m, 64);
-            }
-            if (r == 0 && c4 < c4n) {
-                const int j = 4 * c4;
-                if (j + 0 < D) dst[j + 0] = acc.x;
-                if (j + 1 < D) dst[j + 1] = acc.y;
-                if (j + 2 < D) dst[j + 2] = acc.z;
-                if (j + 3 < D) dst[j + 3] = acc.w;
-            }
-        } else {
-            for (int j0 = 0; j0 < D; j0 += 64) {
-                const int j = j0 + lane;
-                float acc = 0.f;
-                for (int k = k0; k < k1; ++k) {
-                    int64_t bag = ws.bag_of[ws.perm[k]];
-                    bag = bag < 0 ? 0 : (bag >= nbags ? nbags - 1 : bag);
-                    const int64_t b = bag - (int64_t)t * a.B;
-                    const int64_t bb = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
-                    if (j < D) acc += go[bb * a.SD + j];
-                }
-                if (j < D) dst[j] = acc;
-            }
+        }
+        if (gl == 0) {
+            ws.gu_ml[task] = mL;
+            ws.gu_mr[task] = mR;
         }
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_gu_combine(BwdArgs a)
+// Cut runs: the task where a cut run starts (its right edge cuts run u, which
+// does not also enter from the left) adds its right partial and the left
+// partials of the following tasks up to the one holding u's last position, in
+// that order, into u's slot.  One wave per task, lanes over columns.
+__global__ __launch_bounds__(kThreads) void k_gu_join(BwdArgs a)
 {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __shared__ int base[kMaxTables + 1], cbase[kMaxTables + 1];
+    __shared__ GuTab gt[kMaxTables];
+    gu_bases(a, -1, base, cbase, gt);
     const Ws &ws = a.ws;
-    const int64_t U = ws.ctrl[CTRL_U];
-    for (int64_t u = (int64_t)blockIdx.x * 4 + w; u < U; u += (int64_t)gridDim.x * 4) {
-        const int p0 = ws.u_piece_start[u], p1 = ws.u_piece_start[u + 1];
-        if (p1 - p0 <= 1) continue;
-        const int t = segment_of(ws.tab_uniq_start, a.T, u);
-        const TableDesc &tb = a.tab[t];
-        float *dst = ws.E + ws.ebase[t] + u * (int64_t)tb.Dp;
+    const int T = a.T, ntask = base[T];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int task = blockIdx.x * (kThreads / 64) + w; task < ntask; task += gridDim.x * (kThreads / 64)) {
+        const int u = ws.gu_mr[task];
+        if (u < 0 || ws.gu_ml[task] == u) continue;
+        const int t = gu_table(base, T, task);
+        const GuTab tb = gt[t];
+        const int e = ws.uniq_start[u + 1] - 1; // u's last sorted position
+        int last = base[t] + (e - tb.ts) / kGuTask;
+        last = last > base[t + 1] - 1 ? base[t + 1] - 1 : last;
+        float *dst = ws.E + tb.ebase + (int64_t)u * tb.Dp;
+        const float *part = ws.P3;
+        const int64_t gs = a.gstride;
         for (int j = lane; j < tb.D; j += 64) {
-            float acc = 0.f;
-            for (int p = p0; p < p1; ++p) acc += ws.P3[p * (int64_t)a.Dmax + j];
-            dst[j] = acc;
+            float s = part[(2 * (int64_t)task + 1) * gs + j];
+#pragma unroll 8
+            for (int k = task + 1; k <= last; ++k) s += part[2 * (int64_t)k * gs + j];
+            dst[j] = s;
         }
     }
 }
@@ -416,8 +522,11 @@ struct BwdLds {
     static constexpr int DTST = 17;                    // transposed dC: [col][(g, j1)], stride 17
     static constexpr int STAGE = CLS == 3 ? 14336 : CLS == 2 ? 10240 : 6144;
     static constexpr int TOTAL = G2S + 2 * CS + G1S + STAGE;
-    static constexpr int OCC = CLS == 3 ? 1 : CLS == 2 ? 2 : 4; // blocks per CU
+    static constexpr int OCC = CLS == 3 ? 1 : 2; // blocks per CU
     static constexpr int NW = CLS == 3 ? 8 : 4;                  // waves per block
+    // float4 registers per thread that carry the next chunk's first rows while
+    // this chunk computes (the rows of a 64-column table at chunk_rows 32)
+    static constexpr int PF = CLS == 3 ? 2 : CLS == 2 ? 6 : CLS == 1 ? 4 : 2;
 };
 
 template <int R>
@@ -426,11 +535,23 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
     using L = BwdLds<R>;
     constexpr int NW = L::NW, BT = NW * 64;
     constexpr int NCOL = L::NCOL, NT = NCOL / 16, NTW = (NT + NW - 1) / NW, MT = (R + 15) / 16, KQ = R / 4;
-    constexpr int NIT = (4 * MT + NW - 1) / NW;  // (unit, r-block) items per wave
-    constexpr int KS = NW / MT, SPL = R / KS, CSTR = L::CSTR, CUNIT = L::CUNIT;
-    static_assert((SPL & (SPL - 1)) == 0, "k-split length is a power of two");
+    // (2) rows: at ranks <= 32 wave (mb, rg) takes every RG-th row of every
+    // unit for r2 block mb and the wave partials of dC are added at tile end
+    // (balanced whatever the unit sizes); at rank 64, where units hold few
+    // rows, wave w owns the (unit, r2 block) items w + NW*i whole
+    constexpr bool kBal = R <= 32;
+    constexpr int RG = NW / MT;                    // row groups (waves per r2 block)
+    constexpr int NIT = (4 * MT + NW - 1) / NW;    // items per wave (rank 64)
+    constexpr int NACC = kBal ? 4 : NIT;           // dC accumulators per wave
+    static_assert(RG * MT == NW && RG * 4 * MT * 256 <= L::STAGE, "(2) wave partials fit in the staging region");
+    // (3): waves form NP groups of MTW r1 blocks times KG groups of SPW columns
+    constexpr int MTW = MT >= 2 ? 2 : 1, NP = MT / MTW, KG = NW / NP, SPW = R / KG;
+    constexpr int CSTR = L::CSTR, CUNIT = L::CUNIT, PF = L::PF;
+    static_assert(NP * KG == NW && SPW * KG == R && (R & (R - 1)) == 0, "(3) splits the columns evenly");
+    static_assert(KG * MT * 256 <= L::STAGE, "(3) partials fit in the staging region");
+    static_assert(4 * R <= BT, "one G1 float4 per thread");
     __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
-    __shared__ ChunkRec recs[2];
+    __shared__ ChunkRec recs[3]; // records of chunks c, c+1 and (arriving) c+2
     __shared__ int s_run;
     // Cs holds C during a tile and dC at its end (C is dead by then); dT holds
     // dC transposed ([col][(g, j1)]) for the dG1 partials
@@ -439,6 +560,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
     constexpr int G1ST = L::G1ST, DTST = L::DTST;
     const Ws &ws = a.ws;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, kq = lane >> 4;
+    const int mb = w % MT, rg = w / MT; // (2): this wave's r2 block and row group
     const int rbeg = ws.ctrl[CTRL_RUN_CLS + L::CLS], rend = ws.ctrl[CTRL_RUN_CLS + L::CLS + 1];
     for (;;) {
         if (tid == 0) s_run = rbeg + atomicAdd(&ws.ctrl[CTRL_BWD_NEXT + L::CLS], 1);
@@ -446,13 +568,22 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
         const int run = s_run;
         if (run >= rend) break;
         const int c0 = ws.tile_cstart[ws.run_tile_start[run]], c1 = ws.tile_cstart[ws.run_tile_start[run + 1]];
-        if (w == 0) reinterpret_cast<int *>(&recs[0])[lane] = reinterpret_cast<const int *>(&ws.crec[c0])[lane];
+        if (w == 0) {
+            reinterpret_cast<int *>(&recs[0])[lane] = reinterpret_cast<const int *>(&ws.crec[c0])[lane];
+            if (c0 + 1 < c1)
+                reinterpret_cast<int *>(&recs[1])[lane] = reinterpret_cast<const int *>(&ws.crec[c0 + 1])[lane];
+        }
         __syncthreads();
-        const int t = recs[0].t, i2 = recs[0].i2;
+        // wave-uniform: the table data below become scalar loads
+        const int t = __builtin_amdgcn_readfirstlane(recs[0].t), i2 = __builtin_amdgcn_readfirstlane(recs[0].i2);
         const TableDesc &tb = a.tab[t];
         const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, D12 = d1 * d2, Dp = tb.Dp, P = 16 / d3;
         const float *G1 = a.cores.g[t][0];
         const float *G3t = ws.g3t + tb.g3t_off;
+        // per-table bases read once per run: a global load issued after this
+        // run's stores would wait for all of them (stores and loads share one counter)
+        const float *Et = ws.E + ws.ebase[t];
+        float *P3t = ws.P3 + ws.p3base[t];
         // staged rows: g_u at stride Dp + 4, G3 slices as [j3][R + 16] (bank-spread)
         const int GST = Dp + 4, G3J = R + 16, G3ST = d3 * G3J;
         int rb = L::STAGE / (GST + G3ST);
@@ -465,76 +596,139 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                 G2s[r * NCOL + (c ^ (r & 31))] = c < d2 * R ? src[r * d2 * R + c] : 0.f;
             }
         }
-        floatx4 g2acc[MT][NTW], dacc[NIT];
+        floatx4 g2acc[MT][NTW], dacc[NACC]; // this wave's part of the units' dC
 #pragma unroll
-        for (int ii = 0; ii < NIT; ++ii) dacc[ii] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < NACC; ++i) dacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
             for (int j = 0; j < NTW; ++j) g2acc[mt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
-        int cur_tile = -1, buf = 0;
+        const int c4g = Dp >> 2, c4t = (d3 * R) >> 2, c4r = c4g + c4t; // float4 per staged row
+        const int pf_cap = PF * BT / c4r;                                // rows the prefetch carries
+        auto first_rows = [&](const ChunkRec &r) __attribute__((always_inline)) {
+            const int n = r.rowoff[4] < rb ? r.rowoff[4] : rb;
+            return n < pf_cap ? n : pf_cap;
+        };
+        // Stage rows q0 .. q0+n-1 of chunk r into the batch that starts at row sb.
+        auto stage_rows = [&](const ChunkRec &r, int sb, int q0, int n) __attribute__((always_inline)) {
+            for (int e = tid; e < n * c4r; e += BT) {
+                const int qq = e / c4r, rem = e - qq * c4r, q = q0 + qq;
+                const int j = (q >= r.rowoff[1]) + (q >= r.rowoff[2]) + (q >= r.rowoff[3]); // unit of row q
+                if (rem < c4g) {
+                    const int u = r.ustart[j] + (q - r.rowoff[j]);
+                    *reinterpret_cast<float4 *>(Gs + (q - sb) * GST + 4 * rem) =
+                        reinterpret_cast<const float4 *>(Et + (int64_t)u * Dp)[rem];
+                } else {
+                    const int r4 = rem - c4g, j3 = (4 * r4) / R, rr = 4 * r4 - j3 * R;
+                    *reinterpret_cast<float4 *>(G3s + (q - sb) * G3ST + j3 * G3J + rr) =
+                        reinterpret_cast<const float4 *>(G3t + (int64_t)r.i3[q] * d3 * R)[r4];
+                }
+            }
+        };
+        // The next chunk's first rows (and its tile's G1 slices, G1s[(g*4 + j1)*G1ST
+        // + r1], zeros outside) travel in registers while this chunk computes.
+        // Loads are unconditional (clamped to the chunk's first row when out of
+        // range) and validity is applied when committing: zeroing a register that
+        // a load may still target makes the compiler wait for every outstanding
+        // load and store of the wave.
+        floatx4 pfv[PF], pg1; // native vectors (a struct copy here would live in scratch)
+        auto pf_issue = [&](const ChunkRec &r, bool tile_start) __attribute__((always_inline)) {
+            const int n = first_rows(r);
+#pragma unroll
+            for (int i = 0; i < PF; ++i) {
+                int e = tid + i * BT;
+                e = e < n * c4r ? e : 0;
+                const int q = e / c4r, rem = e - q * c4r;
+                const int j = (q >= r.rowoff[1]) + (q >= r.rowoff[2]) + (q >= r.rowoff[3]); // unit of row q
+                const floatx4 *src = rem < c4g
+                    ? reinterpret_cast<const floatx4 *>(Et + (int64_t)(r.ustart[j] + (q - r.rowoff[j])) * Dp) + rem
+                    : reinterpret_cast<const floatx4 *>(G3t + (int64_t)r.i3[q] * d3 * R) + (rem - c4g);
+                pfv[i] = *src;
+            }
+            if (tile_start) {
+                const int e = tid < 4 * R ? tid : 0;
+                const int gj = e / (R / 4), r4 = e - gj * (R / 4), g = gj >> 2, j1 = gj & 3;
+                const bool ok = g < r.nu && j1 < d1;
+                pg1 = reinterpret_cast<const floatx4 *>(G1 + ((int64_t)(ok ? r.i1[g] : r.i1[0]) * d1 + (ok ? j1 : 0)) * R)[r4];
+            }
+        };
+        auto pf_commit = [&](const ChunkRec &r, bool tile_start) __attribute__((always_inline)) {
+            const int n = first_rows(r);
+#pragma unroll
+            for (int i = 0; i < PF; ++i) {
+                const int e = tid + i * BT;
+                if (e < n * c4r) {
+                    const int q = e / c4r, rem = e - q * c4r;
+                    if (rem < c4g) {
+                        *reinterpret_cast<floatx4 *>(Gs + q * GST + 4 * rem) = pfv[i];
+                    } else {
+                        const int r4 = rem - c4g, j3 = (4 * r4) / R, rr = 4 * r4 - j3 * R;
+                        *reinterpret_cast<floatx4 *>(G3s + q * G3ST + j3 * G3J + rr) = pfv[i];
+                    }
+                }
+            }
+            if (tile_start && tid < 4 * R) {
+                const int gj = tid / (R / 4), r4 = tid - gj * (R / 4), g = gj >> 2, j1 = gj & 3;
+                const bool ok = g < r.nu && j1 < d1;
+                float *d = G1s + gj * G1ST + 4 * r4;
+                d[0] = ok ? pg1[0] : 0.f;
+                d[1] = ok ? pg1[1] : 0.f;
+                d[2] = ok ? pg1[2] : 0.f;
+                d[3] = ok ? pg1[3] : 0.f;
+            }
+        };
+        pf_issue(recs[0], true);
+        pf_commit(recs[0], true);
+        int cur_tile = -1;
         for (int c = c0; c < c1; ++c) {
-            const ChunkRec &rec = recs[buf];
-            // the next record travels while this chunk runs
-            int pre = 0;
-            if (w == 0 && c + 1 < c1) pre = reinterpret_cast<const int *>(&ws.crec[c + 1])[lane];
+            const int slot = (c - c0) % 3;
+            __syncthreads(); // staged rows, G1 slices and the record of chunk c+1 are visible
+            const ChunkRec &rec = recs[slot];
+            const ChunkRec &nrec = recs[slot == 2 ? 0 : slot + 1];
+            const bool has_next = c + 1 < c1;
+            const bool next_new = has_next && nrec.tile != rec.tile;
+            const bool tile_end = !has_next || next_new;
+            // record c+2 and the rows of chunk c+1 travel while this chunk runs
+            const int pre = reinterpret_cast<const int *>(&ws.crec[c + 2 < c1 ? c + 2 : c])[lane];
+            if (has_next) pf_issue(nrec, next_new);
             const int nu = rec.nu;
             const bool new_tile = rec.tile != cur_tile;
             const int nrows = rec.rowoff[4];
-            // ---- one burst of independent loads: the tile's G1 slices (new tile
-            // only, G1s[(g*4 + j1)*G1ST + r1], zeros outside) and the first batch of rows
-            const int c4g = Dp >> 2, c4t = (d3 * R) >> 2;
-            auto stage_rows = [&](int sb, int n) {
-                for (int e = tid; e < n * (c4g + c4t); e += BT) {
-                    const int qq = e / (c4g + c4t), rem = e - qq * (c4g + c4t), q = sb + qq;
-                    int j = 0;
-                    while (j < 3 && q >= rec.rowoff[j + 1]) ++j;
-                    if (rem < c4g) {
-                        const int u = rec.ustart[j] + (q - rec.rowoff[j]);
-                        *reinterpret_cast<float4 *>(Gs + qq * GST + 4 * rem) =
-                            reinterpret_cast<const float4 *>(ws.E + ws.ebase[t] + (int64_t)u * Dp)[rem];
-                    } else {
-                        const int r4 = rem - c4g, j3 = (4 * r4) / R, r = 4 * r4 - j3 * R;
-                        *reinterpret_cast<float4 *>(G3s + qq * G3ST + j3 * G3J + r) =
-                            reinterpret_cast<const float4 *>(G3t + (int64_t)rec.i3[q] * d3 * R)[r4];
-                    }
-                }
-            };
-            if (new_tile) {
-                for (int e = tid; e < 4 * R; e += BT) {
-                    const int gj = e / (R / 4), r4 = e - gj * (R / 4), g = gj >> 2, j1 = gj & 3;
-                    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (g < nu && j1 < d1) v = reinterpret_cast<const float4 *>(G1 + ((int64_t)rec.i1[g] * d1 + j1) * R)[r4];
-                    float *d = G1s + gj * G1ST + 4 * r4;
-                    d[0] = v.x;
-                    d[1] = v.y;
-                    d[2] = v.z;
-                    d[3] = v.w;
+            {   // rows of the first batch the prefetch could not carry
+                const int n0 = nrows < rb ? nrows : rb, npf = first_rows(rec);
+                if (npf < n0) {
+                    stage_rows(rec, 0, npf, n0 - npf);
+                    __syncthreads();
                 }
             }
-            stage_rows(0, nrows < rb ? nrows : rb);
-            __syncthreads();
             if (new_tile) {
                 // ---- (1) prefix tile C
                 {
+                    // two independent chains per output tile (even and odd k steps)
                     const int g = li >> 2, j1 = li & 3;
-                    floatx4 acc[NTW];
+                    floatx4 acc[NTW], acc2[NTW];
 #pragma unroll
-                    for (int j = 0; j < NTW; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    for (int j = 0; j < NTW; ++j) acc[j] = acc2[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < KQ; ++s) {
+                    for (int s = 0; s < KQ; s += 2) {
                         const int r = kq * KQ + s;
                         const float av = G1s[(g * 4 + j1) * G1ST + r];
+                        const float av2 = G1s[(g * 4 + j1) * G1ST + r + 1];
 #pragma unroll
                         for (int j = 0; j < NTW; ++j) {
                             const int ntg = w + NW * j;
                             if (ntg < NT) {
                                 const int col = ntg * 16 + li;
                                 acc[j] = mfma4(av, G2s[r * NCOL + (col ^ (r & 31))], acc[j]);
+                                acc2[j] = mfma4(av2, G2s[(r + 1) * NCOL + (col ^ ((r + 1) & 31))], acc2[j]);
                             }
                         }
                     }
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[j][v] += acc2[j][v];
 #pragma unroll
                     for (int j = 0; j < NTW; ++j) {
                         const int ntg = w + NW * j;
@@ -549,128 +743,164 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                     }
                 }
 #pragma unroll
-                for (int ii = 0; ii < NIT; ++ii) dacc[ii] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int i = 0; i < NACC; ++i) dacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
                 cur_tile = rec.tile;
+                __syncthreads(); // C tile written
             }
-            // ---- (2) rows of this chunk, in staged batches of rb rows (the first is staged)
+            // ---- (2) rows of this chunk, in staged batches of rb rows (the first is
+            // staged).  Wave (mb, rg) covers r2 block mb for every RG-th row of each
+            // unit, so the waves share the rows evenly whatever the unit sizes.
             for (int sb = 0; sb < nrows; sb += rb) {
                 const int n = nrows - sb < rb ? nrows - sb : rb;
-                __syncthreads(); // C tile written; previous batch consumed
                 if (sb > 0) {
-                    stage_rows(sb, n);
+                    __syncthreads(); // previous batch consumed
+                    stage_rows(rec, sb, sb, n);
                     __syncthreads();
                 }
 #pragma unroll
-                for (int ii = 0; ii < NIT; ++ii) {
-                    const int item = w + NW * ii, g = item / MT, mb = item % MT;
+                for (int i = 0; i < (kBal ? 4 : NIT); ++i) {
+                    // (unit g, r2 block bm) of accumulator i, and the rows it takes
+                    const int item = kBal ? 0 : w + NW * i;
+                    const int g = kBal ? i : item / MT, bm = kBal ? mb : item % MT;
+                    const int r0 = kBal ? rg : 0, rs = kBal ? RG : 1;
                     if (item >= 4 * MT || g >= nu) continue;
-                    const int r2 = mb * 16 + li;
+                    const int r2 = bm * 16 + li;
                     const bool okr = r2 < R;
                     const int qa = sb > rec.rowoff[g] ? sb : rec.rowoff[g];
                     const int qe = rec.rowoff[g] + rec.ccnt[g];
                     const int qb = sb + n < qe ? sb + n : qe;
                     // (2a) dC_g[m2][r2] += sum_j3 g_u[m2][j3] G3[i3_u][r2][j3]
-                    for (int q = qa; q < qb; ++q) {
+                    for (int q = qa + r0; q < qb; q += rs) {
                         const float *gq = Gs + (q - sb) * GST;
                         const float *g3 = G3s + (q - sb) * G3ST + (okr ? r2 : 0);
                         for (int j0 = 0; j0 < d3; j0 += 4) {
                             const int j3 = j0 + kq;
                             const float av = (li < D12 && j3 < d3) ? gq[li * d3 + j3] : 0.f;
                             const float bv = (okr && j3 < d3) ? g3[j3 * G3J] : 0.f;
-                            dacc[ii] = mfma4(av, bv, dacc[ii]);
+                            dacc[i] = mfma4(av, bv, dacc[i]);
                         }
                     }
-                    // (2b) P3_u[r2][j3] = sum_m2 C_g[m2][r2] g_u[m2][j3], P rows per output tile
-                    float ca[4];
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const int m2 = kq * 4 + s;
-                        ca[s] = (m2 < D12 && okr) ? Cs[g * CUNIT + m2 * CSTR + r2] : 0.f;
-                    }
-                    const int slot = li / d3, j3 = li - slot * d3;
-                    for (int qs = qa; qs < qb; qs += P) {
-                        const int cnt = qb - qs < P ? qb - qs : P;
-                        const bool okb = slot < cnt;
-                        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+                    // (2b) P3_u[r2][j3] = sum_m2 C_g[m2][r2] g_u[m2][j3], P rows per output
+                    // tile, the row groups dealt round-robin over the row-group waves
+                    if (qa + r0 * P < qb) {
+                        float ca[4];
 #pragma unroll
                         for (int s = 0; s < 4; ++s) {
                             const int m2 = kq * 4 + s;
-                            const float bv = (okb && m2 < D12) ? Gs[(qs + slot - sb) * GST + m2 * d3 + j3] : 0.f;
-                            acc = mfma4(ca[s], bv, acc);
+                            ca[s] = (m2 < D12 && okr) ? Cs[g * CUNIT + m2 * CSTR + r2] : 0.f;
                         }
-                        if (okb) {
-                            const int u = rec.ustart[g] + (qs + slot - rec.rowoff[g]);
-                            float *dst = ws.P3 + ws.p3base[t] + (int64_t)u * R * d3 + j3;
+                        const int slot_r = li / d3, j3 = li - slot_r * d3;
+                        for (int qs = qa + r0 * P; qs < qb; qs += rs * P) {
+                            const int cnt = qb - qs < P ? qb - qs : P;
+                            const bool okb = slot_r < cnt;
+                            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                const int rr = mb * 16 + 4 * kq + v;
-                                if (rr < R) dst[rr * d3] = acc[v];
+                            for (int s = 0; s < 4; ++s) {
+                                const int m2 = kq * 4 + s;
+                                const float bv = (okb && m2 < D12) ? Gs[(qs + slot_r - sb) * GST + m2 * d3 + j3] : 0.f;
+                                acc = mfma4(ca[s], bv, acc);
+                            }
+                            if (okb) {
+                                const int u = rec.ustart[g] + (qs + slot_r - rec.rowoff[g]);
+                                float *dst = P3t + (int64_t)u * R * d3 + j3;
+#pragma unroll
+                                for (int v = 0; v < 4; ++v) {
+                                    const int rr = bm * 16 + 4 * kq + v;
+                                    if (rr < R) dst[rr * d3] = acc[v];
+                                }
                             }
                         }
                     }
                 }
             }
-            // ---- the record of the next chunk, and whether this tile ends here
-            __syncthreads();
-            if (w == 0 && c + 1 < c1) reinterpret_cast<int *>(&recs[buf ^ 1])[lane] = pre;
-            __syncthreads();
-            const bool tile_end = c + 1 == c1 || recs[buf ^ 1].tile != rec.tile;
+            __syncthreads(); // rows done: C and the staged rows are free
             if (tile_end) {
+                if constexpr (kBal) {
+                    // dC of each unit = the RG wave partials added in order; it goes
+                    // to Cs (C is dead) and, transposed, to dT
+                    float *part = Sg; // [rg][g][mb][v][lane]
 #pragma unroll
-                for (int ii = 0; ii < NIT; ++ii) {
-                    const int item = w + NW * ii, g = item / MT, mb = item % MT;
-                    const int r2 = mb * 16 + li;
-                    if (item < 4 * MT && r2 < R) {
+                    for (int g = 0; g < 4; ++g)
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int m2 = 4 * kq + v;
-                            Cs[g * CUNIT + m2 * CSTR + r2] = dacc[ii][v];
-                            if (m2 < D12) dT[((m2 % d2) * R + r2) * DTST + g * 4 + m2 / d2] = dacc[ii][v];
+                        for (int v = 0; v < 4; ++v) part[(((rg * 4 + g) * MT + mb) * 4 + v) * 64 + lane] = dacc[g][v];
+                    __syncthreads();
+                    for (int e = tid; e < 4 * MT * 256; e += BT) {
+                        float sum = 0.f;
+#pragma unroll
+                        for (int k = 0; k < RG; ++k) sum += part[k * 4 * MT * 256 + e];
+                        const int g = e / (MT * 256), bm = (e >> 8) % MT, v = (e >> 6) & 3, ln = e & 63;
+                        const int rr = bm * 16 + (ln & 15), m2 = 4 * (ln >> 4) + v;
+                        if (rr < R) {
+                            Cs[g * CUNIT + m2 * CSTR + rr] = sum;
+                            if (m2 < D12) dT[((m2 % d2) * R + rr) * DTST + g * 4 + m2 / d2] = sum;
+                        }
+                    }
+                } else {
+                    // each item's dC block is whole in one wave
+#pragma unroll
+                    for (int i = 0; i < NIT; ++i) {
+                        const int item = w + NW * i, g = item / MT, bm = item % MT;
+                        const int rr = bm * 16 + li;
+                        if (item < 4 * MT && rr < R) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const int m2 = 4 * kq + v;
+                                Cs[g * CUNIT + m2 * CSTR + rr] = dacc[i][v];
+                                if (m2 < D12) dT[((m2 % d2) * R + rr) * DTST + g * 4 + m2 / d2] = dacc[i][v];
+                            }
                         }
                     }
                 }
                 __syncthreads();
-                // ---- (3) G1 partial of each unit: sum_col dC[(g,j1)][col] G2[r1][col]
+                // ---- (3) G1 partial of each unit: sum over the columns (j2, r2) of
+                // dC[(g,j1)][col] G2[r1][col].  A wave takes MTW r1 blocks over
+                // one of KG column groups (independent accumulator chains of
+                // SPW steps); the group partials are added in group order.
                 {
-                    const int mb = w % MT, ks = w / MT;
-                    const int g = li >> 2, j1 = li & 3;
+                    const int g = li >> 2, j1 = li & 3, kg = w % KG, mt0 = (w / KG) * MTW;
                     const bool oka = kq < d2 && j1 < d1;
                     const float *acol = dT + kq * R * DTST + li; // dT[(kq*R + s)][(g, j1) = li]
-                    const int r1 = mb * 16 + li;
-                    const bool okr = r1 < R;
-                    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-                    // lanes of the two k-quarters sharing a half-wave walk their
-                    // columns 16 apart, so dT and G2s reads land in distinct banks
-                    const int rot = SPL >= 32 ? 16 * (kq & 1) : 0;
-#pragma unroll 8
-                    for (int sl = 0; sl < SPL; ++sl) {
-                        const int s = ks * SPL + ((sl + rot) & (SPL - 1));
-                        const int col = kq * R + s;
+                    // the two k-quarters sharing a half-wave walk columns 16 apart
+                    // so their dT and G2s reads fall in distinct banks
+                    const int rot = R >= 32 ? 16 * (kq & 1) : 0;
+                    // two independent chains per output tile (even and odd steps)
+                    floatx4 acc[MTW], acc2[MTW];
+#pragma unroll
+                    for (int m = 0; m < MTW; ++m) acc[m] = acc2[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+                    for (int sl = 0; sl < SPW; sl += 2) {
+                        const int s = (kg * SPW + sl + rot) & (R - 1);
+                        const int s2 = (kg * SPW + sl + 1 + rot) & (R - 1);
                         const float av = oka ? acol[s * DTST] : 0.f;
-                        const float bv = okr ? G2s[r1 * NCOL + (col ^ (r1 & 31))] : 0.f;
-                        acc = mfma4(av, bv, acc);
-                    }
-                    if constexpr (KS > 1) {
-                        float *red = Sg; // staged rows are no longer needed
+                        const float av2 = oka ? acol[s2 * DTST] : 0.f;
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) red[(w * 64 + lane) * 4 + v] = acc[v];
-                        __syncthreads();
-                        if (ks == 0) {
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                float sum = 0.f;
-#pragma unroll
-                                for (int kk = 0; kk < KS; ++kk) sum += red[((mb + kk * MT) * 64 + lane) * 4 + v];
-                                acc[v] = sum;
-                            }
+                        for (int m = 0; m < MTW; ++m) {
+                            const int r1 = (mt0 + m) * 16 + li;
+                            const float bv = r1 < R ? G2s[r1 * NCOL + ((kq * R + s) ^ (r1 & 31))] : 0.f;
+                            const float bv2 = r1 < R ? G2s[r1 * NCOL + ((kq * R + s2) ^ (r1 & 31))] : 0.f;
+                            acc[m] = mfma4(av, bv, acc[m]);
+                            acc2[m] = mfma4(av2, bv2, acc2[m]);
                         }
                     }
-                    if (ks == 0 && okr && kq < nu) {
-                        // partials are indexed by the unit's position in the work order
-                        float *dst = ws.G1P + (int64_t)(rec.ubeg + kq) * a.g1stride + r1;
 #pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            if (v < d1) dst[v * R] = acc[v];
+                    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[m][v] += acc2[m][v];
+                    float *red = Sg; // [kg][mt][v][lane]; the staged rows are no longer needed
+#pragma unroll
+                    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) red[((kg * MT + mt0 + m) * 4 + v) * 64 + lane] = acc[m][v];
+                    __syncthreads();
+                    for (int e = tid; e < MT * 256; e += BT) {
+                        float sum = 0.f;
+#pragma unroll
+                        for (int k = 0; k < KG; ++k) sum += red[k * MT * 256 + e];
+                        // e = (mt*4 + v)*64 + lane: row (g = lane/16, j1 = v), r1 = mt*16 + lane%16
+                        const int mt = e >> 8, v = (e >> 6) & 3, ln = e & 63;
+                        const int r1 = mt * 16 + (ln & 15), gg = ln >> 4;
+                        if (r1 < R && gg < nu && v < d1)
+                            ws.G1P[(int64_t)(rec.ubeg + gg) * a.g1stride + v * R + r1] = sum;
                     }
                 }
                 // ---- (4) dG2 += G1^T dC over (g, j1)
@@ -699,9 +929,10 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                         }
                     }
                 }
-                __syncthreads(); // before the next tile reuses G1s / Cs / dT
+                __syncthreads(); // (3) partials read, G1s and dC read before they are replaced
             }
-            buf ^= 1;
+            if (has_next) pf_commit(nrec, next_new);
+            if (w == 0 && c + 2 < c1) reinterpret_cast<int *>(&recs[slot == 0 ? 2 : slot - 1])[lane] = pre;
         }
         float *dst = a.grads.g[t][1] + (int64_t)i2 * R * d2 * R;
 #pragma unroll
@@ -774,7 +1005,7 @@ __global__ __launch_bounds__(kThreads) void k_zero_g2(BwdArgs a)
 hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs &cores,
                            const int64_t *offsets, const GradPtrs &grads, hipStream_t s)
 {
-    BwdArgs a{p.dtab, p.T, p.B, p.ws, cores, grads, grad_out, offsets, p.nnz, p.sumD, p.Dmax, p.force_generic,
+    BwdArgs a{p.dtab, p.T, p.B, p.ws, cores, grads, grad_out, offsets, p.nnz, p.sumD, p.Dpmax, p.force_generic,
               p.g1stride};
     const int T = p.T;
     const int sum_n1 = p.sum_n[0], sum_n3 = p.sum_n[2];
@@ -784,12 +1015,34 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
         const int64_t nbags = (int64_t)T * p.B;
         int g = ceil_div(nbags, kThreads);
         if (g > 4096) g = 4096;
-        hipLaunchKernelGGL(k_bag_of, dim3(g), dim3(kThreads), 0, s, a);
-        PieceOp pop{p.ws};
-        hipError_t e = run_scan(pop, p.ws.part, scan_blocks(p.nnz), s);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_gu_pieces, dim3(4096), dim3(kThreads), 0, s, a);
-        hipLaunchKernelGGL(k_gu_combine, dim3(2048), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(k_lookup_meta, dim3(g), dim3(kThreads), 0, s, a);
+        const int64_t tasks = p.nnz / kGuTask + T + 1;
+        for (int c = 0; c < 16; ++c) {
+            if (!(p.gcls_mask & (1 << c))) continue;
+            const int lpr = 1 << (c & 7), G = 64 / lpr;
+            int gb = ceil_div(tasks, (int64_t)G * (kThreads / 64));
+            gb = gb < 1 ? 1 : (gb > 8192 ? 8192 : gb);
+            switch (c) {
+            case 0: hipLaunchKernelGGL((k_gu_gather<1, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 1: hipLaunchKernelGGL((k_gu_gather<2, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 2: hipLaunchKernelGGL((k_gu_gather<4, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 3: hipLaunchKernelGGL((k_gu_gather<8, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 4: hipLaunchKernelGGL((k_gu_gather<16, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 5: hipLaunchKernelGGL((k_gu_gather<32, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 6: hipLaunchKernelGGL((k_gu_gather<64, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 8: hipLaunchKernelGGL((k_gu_gather<1, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 9: hipLaunchKernelGGL((k_gu_gather<2, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 10: hipLaunchKernelGGL((k_gu_gather<4, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 11: hipLaunchKernelGGL((k_gu_gather<8, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 12: hipLaunchKernelGGL((k_gu_gather<16, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 13: hipLaunchKernelGGL((k_gu_gather<32, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            case 14: hipLaunchKernelGGL((k_gu_gather<64, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
+            default: return hipErrorInvalidValue;
+            }
+        }
+        int gj = ceil_div(tasks, kThreads / 64);
+        gj = gj > 4096 ? 4096 : gj;
+        hipLaunchKernelGGL(k_gu_join, dim3(gj), dim3(kThreads), 0, s, a);
     }
     timer_end(p.timing, TM_BWD_GATHER, s);
     timer_begin(p.timing, TM_BWD_CONTRACT, s);

@@ -158,14 +158,17 @@ __device__ int claim_finish(int32_t *heads, int base, int me, int &vi, int nb, i
 __device__ __forceinline__ void prefetch_a(const FwdArgs &a, const ChunkRec &nr, float (&apf)[16], int &apf_tile)
 {
     apf_tile = -1;
-    if (nr.cls < 0) return;
-    const int R = 8 << nr.cls, KQ = R >> 2;
-    const TableDesc &tb = a.tab[nr.t];
+    // record fields are wave-uniform: scalar loads of the table data then stay
+    // off the vector memory counter
+    const int cls = __builtin_amdgcn_readfirstlane(nr.cls), t = __builtin_amdgcn_readfirstlane(nr.t);
+    if (cls < 0) return;
+    const int R = 8 << cls, KQ = R >> 2;
+    const TableDesc &tb = a.tab[t];
     const int d1 = tb.d1;
     const int lane = threadIdx.x & 63, li = lane & 15, kq = lane >> 4;
     const int g = li >> 2, j1 = li & 3;
     const bool ok = g < nr.nu && j1 < d1;
-    const float *src = a.cores.g[nr.t][0] + ((int64_t)(ok ? nr.i1[g] : 0) * d1 + (ok ? j1 : 0)) * R + kq * KQ;
+    const float *src = a.cores.g[t][0] + ((int64_t)(ok ? nr.i1[g] : 0) * d1 + (ok ? j1 : 0)) * R + kq * KQ;
     if (KQ >= 4) {
 #pragma unroll
         for (int s = 0; s < 16; s += 4) {
@@ -192,9 +195,12 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
     constexpr int KQ = R / 4;           // K values each lane feeds per output tile
     constexpr int NT = R / 4;           // 16-column tiles of the padded d2*R2 (d2 <= 4)
     constexpr int NTW = (NT + 3) / 4;   // per wave
-    const int t = rec.t;
+    // wave-uniform table index: the table data below become scalar loads,
+    // which do not wait behind this wave's outstanding vector loads and stores
+    const int t = __builtin_amdgcn_readfirstlane(rec.t);
     const TableDesc &tb = a.tab[t];
     const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, D12 = d1 * d2, Dp = tb.Dp;
+    float *Et = a.ws.E + a.ws.ebase[t];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, kq = lane >> 4;
     const float *G1 = a.cores.g[t][0];
     const float *G2 = a.cores.g[t][1];
@@ -338,7 +344,6 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
     if (has_next && rnext->tile != rec.tile) prefetch_a(a, *rnext, apf, apf_tile);
 
     // -------- unique rows E_u = C_unit . G3[i3_u], 16/d3 rows per output tile
-    float *Et = a.ws.E + a.ws.ebase[t];
     const bool okm = li < D12;
     for (int e = w; e < np; e += 4) {
         float bcur[KQ];

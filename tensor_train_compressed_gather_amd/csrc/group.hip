@@ -47,11 +47,22 @@ __global__ __launch_bounds__(kThreads) void k_check_offsets(const int64_t *offse
     }
     if (__any(bad) && lane_id() == 0) atomicOr(&ws.ctrl[CTRL_ERR], (int)ERRB_OFFSETS);
     if (blockIdx.x == 0) {
+        // table starts, clamped into [0, nnz] and made non-decreasing so the
+        // table ranges never overlap even when the offsets are malformed
+        __shared__ int32_t st[kMaxTables + 1];
         for (int t = threadIdx.x; t <= T; t += blockDim.x) {
             int64_t o = nbags > 0 ? offsets[(int64_t)t * B] : 0;
             if (t == T) o = nnz;
             o = o < 0 ? 0 : (o > nnz ? nnz : o);
-            ws.tstart[t] = (int32_t)o;
+            st[t] = (int32_t)o;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int32_t m = 0;
+            for (int t = 0; t <= T; ++t) {
+                m = st[t] > m ? st[t] : m;
+                ws.tstart[t] = m;
+            }
         }
     }
 }

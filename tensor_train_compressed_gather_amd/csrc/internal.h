@@ -22,7 +22,8 @@ constexpr int kSortTile = 4096;     // keys per radix-sort block (256 threads x 
 constexpr int kSortItems = kSortTile / kThreads;
 constexpr int kMaxCkptSlots = 4096; // L2 checkpoint slots for split prefix tiles
 constexpr int kUnitsPerTile = 4;    // prefix units sharing (table, i2) per tile
-constexpr int kGuPiece = 256;       // lookups per piece of a gradient gather run
+constexpr int kGuTask = 256;        // sorted lookup positions per gradient-gather task
+constexpr int kGuBatch = 16;        // positions whose grad_out rows a gather worker has in flight
 
 // Control words at the head of the workspace.
 enum CtrlSlot {
@@ -34,7 +35,6 @@ enum CtrlSlot {
     CTRL_TILES = 5,   // tiles of <= 4 units
     CTRL_CHUNKS = 6,  // forward work chunks
     CTRL_SPLIT = 7,   // tiles split over several chunks
-    CTRL_PIECES = 8,  // pieces of the backward gradient gather
     CTRL_STEALS = 9,  // chunks taken from another block's range (statistics)
     CTRL_CKPT_HIT = 10,  // split-tile chunks that found a published checkpoint
     CTRL_CKPT_MISS = 11, // split-tile chunks that recomputed the prefix tile
@@ -59,6 +59,7 @@ struct TableDesc {
     uint32_t i3_base;  // sum of n3 over earlier tables
     int32_t cls;       // MFMA rank class (0: R=8, 1: 16, 2: 32, 3: 64) or -1
     int32_t Dp;        // row stride of the unique-row buffer E (D rounded up to 4)
+    int32_t gcls;      // gradient-gather class: log2(lanes per row) + 8 when rows move as float4
     int64_t g3t_off;   // offset of this table's transposed G3 copy ([n3][d3][R2]) in Ws::g3t
 };
 
@@ -132,11 +133,10 @@ struct Ws {
     float *ckpt;             // [kMaxCkptSlots][4][16][max R2 + 4]
     float *E;                // unique rows, per-table segments
     // backward
-    int32_t *bag_of;         // [nnz]
-    int32_t *piece_u;        // [nnz] unique row of each gather piece
-    int32_t *piece_k;        // [nnz] first sorted position of each piece
-    int32_t *u_piece_start;  // [nnz+1] first piece of each unique row
-    float *piece_sum;        // [nnz/kGuPiece + U][Dmax] partial sums of split runs
+    int2 *lk;                // [nnz] (bag within its table, unique row) of each lookup
+    int32_t *gu_ml;          // [gather tasks] unique row of the run cut at the task's left edge, or -1
+    int32_t *gu_mr;          // [gather tasks] unique row of the run cut at its right edge, or -1
+    // the partial sums of cut runs ([task][left, right][gstride]) live in P3's space
     float *P3;               // per-unique-row G3 partials
     float *G1P;              // per-unit G1 partials
     uint32_t *key3;          // sorted (i3_base + i3) of unique rows
@@ -162,8 +162,9 @@ struct Plan {
     int sched_mode, group_mode, chunk_rows, check_indices, force_generic;
     bool any_generic;
     int cls_mask; // bit c set when some table is in MFMA rank class c
+    int gcls_mask; // bit c set when some table is in gradient-gather class c
     int key_bits, key2_bits, key3_bits;
-    int Dmax, R2max, sumD;
+    int Dmax, Dpmax, R2max, sumD;
     int sum_n[3]; // sum over tables of n1, n2, n3
     int g1stride; // row stride of the G1 partials (max d1*R1 over tables)
     const TableDesc *dtab; // device copy
@@ -181,7 +182,16 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
 hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs &cores,
                            const int64_t *offsets, const GradPtrs &grads, hipStream_t s);
 // SGD and fills (misc.hip)
-hipError_t launch_sgd(float *g, const float *dg, int64_t count, float lr, hipStream_t s);
+constexpr int kSgdMaxCores = 32; // cores per SGD launch (kernel-argument batch)
+struct SgdBatch {
+    int n;                       // cores in the batch
+    int blk[kSgdMaxCores + 1];   // first block of each core
+    float *g[kSgdMaxCores];
+    const float *dg[kSgdMaxCores];
+    int64_t cnt[kSgdMaxCores];
+};
+hipError_t launch_sgd(float *const *g, const float *const *dg, const int64_t *count, int ncores, float lr,
+                      hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, int64_t count, hipStream_t s);
 hipError_t launch_fill_f32(float *p, float v, int64_t count, hipStream_t s);
 

@@ -153,7 +153,7 @@ def test_edge_cases_empty_bags_single_prefix_and_no_lookups():
     assert all(not g.any().item() for g in grads)
 
 
-def test_hot_row_longer_than_a_gather_piece():
+def test_hot_row_longer_than_a_gather_task():
     tab = W.Table(1000, (10, 10, 10), (2, 2, 4), (1, 8, 8, 1), 0.1, "uniform")
     rng = np.random.default_rng(9)
     lens = [rng.integers(20, 60, size=64)]
@@ -165,6 +165,33 @@ def test_hot_row_longer_than_a_gather_piece():
     assert_out_close(w, run.forward().cpu().numpy(), oracle.forward(w))
     got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
     assert_grads_close(got, oracle.backward(w))
+
+
+def test_gradient_gather_runs_at_task_edges():
+    # Sorted lookup runs (one per distinct row) laid against the 256-position
+    # gather tasks: a run ending exactly on a task edge, one filling a task, one
+    # crossing two edges (a whole task in the middle), single lookups; plus a
+    # 512-column table whose rows take two column passes of a lane group.
+    counts = [100, 156, 256, 600, 1, 300, 3, 255, 2]
+    tab_a = W.Table(1000, (10, 10, 10), (2, 2, 4), (1, 8, 8, 1), 0.1, "uniform")
+    tab_b = W.Table(64, (4, 4, 4), (4, 4, 32), (1, 4, 4, 1), 0.1, "uniform")
+    rng = np.random.default_rng(11)
+    rows_a = np.repeat(np.arange(len(counts)) * 37, counts)
+    rng.shuffle(rows_a)
+    B = 64
+    cut = np.sort(rng.choice(np.arange(1, rows_a.size), size=B - 1, replace=False))
+    len_a = np.diff(np.concatenate([[0], cut, [rows_a.size]]))
+    len_b = rng.integers(0, 30, size=B)
+    nb = int(len_b.sum())
+    rows_b = np.where(rng.random(nb) < 0.5, 13, rng.integers(0, 64, nb))
+    w = W.make_custom([tab_a, tab_b], [len_a, len_b], [rows_a, rows_b], seed=11)
+    w.grad_out = rng.standard_normal((w.B, w.sum_D)).astype(np.float32)
+    run = Run(w)
+    assert_out_close(w, run.forward().cpu().numpy(), oracle.forward(w))
+    got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
+    assert_grads_close(got, oracle.backward(w))
+    again = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
+    assert all(np.array_equal(a, b) for a, b in zip(got, again))
 
 
 @pytest.mark.parametrize("cfg,bags", [(1, None), (3, 256), (5, 64)])
