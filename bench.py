@@ -31,6 +31,33 @@ PEAK_FP32_TFLOPS = 157.3   # MI355X dense FP32 (matrix cores; also the vector fi
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 
+def mfma_rank(tb):
+    """Rank of the matrix-core kernel class a table falls in (R1 = R2 in
+    {8, 16, 32, 64}, d1, d2 <= 4, d3 <= 16), else None (generic kernels)."""
+    R1, R2 = tb.R[1], tb.R[2]
+    d1, d2, d3 = tb.d
+    if R1 == R2 and R1 in (8, 16, 32, 64) and d1 <= 4 and d2 <= 4 and d3 <= 16:
+        return R1
+    return None
+
+
+def kernel_flops(tabs, U_r, U_p):
+    """Algorithmic flops of each matrix-core contraction kernel: forward
+    (C once per prefix unit, E once per unique row) and backward (C, dG1 and
+    dG2 per unit; dC and the dG3 partial per unique row)."""
+    out = {}
+    for tb, ur, up in zip(tabs, U_r, U_p):
+        R = mfma_rank(tb)
+        if R is None:
+            continue
+        d1, d2, d3 = tb.d
+        step1 = 2.0 * d1 * R * d2 * R
+        step2 = 2.0 * d1 * d2 * d3 * R
+        out[f"fwd_r{R}"] = out.get(f"fwd_r{R}", 0.0) + up * step1 + ur * step2
+        out[f"bwd_r{R}"] = out.get(f"bwd_r{R}", 0.0) + up * 3 * step1 + ur * 2 * step2
+    return out
+
+
 def phase_flops(tabs, U_r, U_p, nnz_t):
     """Algorithmic flops of the contraction phases (prefix reuse counted once)."""
     fwd = bwd = pool = 0.0
@@ -75,6 +102,56 @@ def load_traffic(kernel, workload, sha):
     if r.get("workload") != workload or r.get("src_sha") != sha:
         return None
     return r.get("bytes_per_launch")
+
+
+# kernel symbol -> (timer name, sources it is built from)
+TRAFFIC_KERNELS = {
+    "k_bwd_class<64>": ("bwd_r64", ["backward.hip", "internal.h"]),
+    "k_bwd_class<32>": ("bwd_r32", ["backward.hip", "internal.h"]),
+    "k_bwd_class<16>": ("bwd_r16", ["backward.hip", "internal.h"]),
+    "k_contract<64>": ("fwd_r64", ["forward.hip", "internal.h"]),
+    "k_contract<32>": ("fwd_r32", ["forward.hip", "internal.h"]),
+    "k_contract<16>": ("fwd_r16", ["forward.hip", "internal.h"]),
+    "k_pool(": ("pool", ["forward.hip", "internal.h"]),
+}
+
+
+def write_traffic(d):
+    """HBM bytes per launch of the contraction and pooling kernels from four
+    rocprofv3 counter runs: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the
+    training step, and the same counters on a plain 1 GiB device copy, whose
+    readings fix the scale of each counter (bytes moved / bytes counted)."""
+    import csv
+
+    def per_kernel(sub):
+        acc = {}
+        with open(os.path.join(d, sub, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return acc
+
+    def copy_scale(sub):
+        vals = [v for k, vs in per_kernel(sub).items() if "copyBuffer" in k for v in vs]
+        return (1 << 30) / (sum(vals) / len(vals))
+
+    fs, ws = copy_scale("cfetch"), copy_scale("cwrite")
+    fetch, write = per_kernel("fetch"), per_kernel("write")
+    from tensor_train_compressed_gather_amd import workloads as W
+    out = {"_calibration": {"fetch_scale": fs, "write_scale": ws,
+                            "copy": "1 GiB fp32 device-to-device copy (bench.py --mode copy)"}}
+    for sym, (name, srcs) in TRAFFIC_KERNELS.items():
+        fk = [k for k in fetch if sym in k]
+        wk = [k for k in write if sym in k]
+        if not fk or not wk:
+            continue
+        fb = sum(fetch[fk[0]]) / len(fetch[fk[0]]) * fs
+        wb = sum(write[wk[0]]) / len(write[wk[0]]) * ws
+        out[name] = {"workload": W.CONFIG_NAMES[5], "src_sha": kernel_sources_sha(srcs), "fetch_bytes": fb,
+                     "write_bytes": wb, "bytes_per_launch": fb + wb}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1, sort_keys=True))
 
 
 class Bench:
@@ -181,9 +258,12 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
     ap.add_argument("--sched", type=int, default=0, help="0 default, 1 static, 2 steal, 3 steal+L2")
     ap.add_argument("--group", type=int, default=0, help="0 default, 1 prefix, 2 unique-only")
-    ap.add_argument("--mode", default="train", choices=("train", "fwd", "copy"),
+    ap.add_argument("--mode", default="train", choices=("train", "fwd", "copy", "traffic"),
                     help="train: the full step (default); fwd: forward only on --config; "
-                         "copy: a plain 1 GiB device copy (counter calibration)")
+                         "copy: a plain 1 GiB device copy (counter calibration); "
+                         "traffic: turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json")
+    ap.add_argument("--pmc-dir", default="gpurun_out/m",
+                    help="traffic: directory with the fetch/, write/, cfetch/, cwrite/ counter runs")
     ap.add_argument("--config", type=int, default=4, help="workload of --mode fwd (1..4)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -191,6 +271,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.mode == "traffic":
+        write_traffic(args.pmc_dir)
+        return
 
     import torch
 
@@ -236,23 +320,31 @@ def main():
     U_r, U_p, nnz_t, cnt = b.counts()
     F_fwd, F_bwd, F_pool = phase_flops(w.tables, U_r, U_p, nnz_t)
     value = w.nnz / (ms * 1e-3)
-    phases = {k: round(v[0] / max(v[1], 1), 4) for k, v in ph.items() if v[1]}
-    # dominant kernel of the step and its roofline
-    dom = max(phases, key=phases.get)
+    per_step = {k: (v[0] / max(v[1], 1), v[1]) for k, v in ph.items() if v[1]}
+    phases = {k: round(v[0], 4) for k, v in per_step.items() if not k[-1].isdigit()}
+    # single-kernel timers (one HIP event pair per launch, on the library's stream)
+    kern_ms = {k: v[0] for k, v in per_step.items() if k[-1].isdigit()}
+    kern_ms["pool"] = per_step["pool"][0]  # the pooling phase is one kernel
+    kflops = kernel_flops(w.tables, U_r, U_p)
     wl = W.CONFIG_NAMES[5]
-    if dom in ("contract", "bwd_contract"):
-        flops = F_fwd if dom == "contract" else F_bwd
-        src = "forward.hip" if dom == "contract" else "backward.hip"
-        achieved = flops / (phases[dom] * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved,
-                "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
-                "algorithmic": flops,
-                "traffic": load_traffic(dom, wl, kernel_sources_sha([src]))}
+    # dominant kernel of the step and its roofline
+    dom = max(kern_ms, key=kern_ms.get)
+    if dom != "pool":
+        flops = kflops[dom]
+        src = "forward.hip" if dom.startswith("fwd") else "backward.hip"
+        achieved = flops / (kern_ms[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "algorithmic_flops": flops,
+                "launch_ms": kern_ms[dom],
+                "traffic": load_traffic(dom, wl, kernel_sources_sha([src, "internal.h"]))}
     else:
         byts = phase_bytes(w, U_r)
-        achieved = byts / (phases[dom] * 1e-3) / 1e9
+        achieved = byts / (kern_ms[dom] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "algorithmic": byts, "traffic": None}
+                "frac": achieved / PEAK_HBM_GBS, "algorithmic_bytes": byts, "launch_ms": kern_ms[dom],
+                "traffic": load_traffic(dom, wl, kernel_sources_sha(["forward.hip", "internal.h"]))}
+    kernels = {k: {"ms": round(v, 4), "tflops": round(kflops[k] / (v * 1e-3) / 1e12, 2) if k in kflops else None}
+               for k, v in sorted(kern_ms.items(), key=lambda kv: -kv[1])}
     res = {
         "metric": METRIC, "value": value, "unit": "lookups/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -261,6 +353,7 @@ def main():
                    "unique_rows": sum(U_r), "prefix_groups": sum(U_p), "sched": args.sched,
                    "group": args.group, "wall_s": wall},
         "phases_ms": phases,
+        "kernels": kernels,
         "flops": {"fwd_contract": F_fwd, "bwd_contract": F_bwd, "pool_adds": F_pool},
         "sched_stats": cnt,
         "roofline": roof,
@@ -276,7 +369,7 @@ def main():
             fms, _, fph = bf.timed(bf.fwd, args.steps, args.warmup)
             ur, up, nz, fc = bf.counts()
             ff, _, _ = phase_flops(wf.tables, ur, up, nz)
-            fphase = {k: round(v[0] / max(v[1], 1), 4) for k, v in fph.items() if v[1]}
+            fphase = {k: round(v[0] / max(v[1], 1), 4) for k, v in fph.items() if v[1] and not k[-1].isdigit()}
             post = fphase.get("contract", 0) + fphase.get("pool", 0)
             cms = fphase.get("contract", 0)
             fwd[W.CONFIG_NAMES[cfg]] = {

@@ -184,6 +184,11 @@ enum {
     TT_EMB_TIMER_BWD_CONTRACT,   /* reverse contraction per (table, i2) run */
     TT_EMB_TIMER_BWD_REDUCE,     /* fixed-order dG1 / dG3 reductions */
     TT_EMB_TIMER_SGD,            /* in-place SGD update */
+    /* single kernels inside CONTRACT and BWD_CONTRACT: the matrix-core
+     * contraction of the tables of rank 8, 16, 32 and 64 (R1 = R2, d1, d2 <= 4,
+     * d3 <= 16); one interval per launch */
+    TT_EMB_TIMER_FWD_R8, TT_EMB_TIMER_FWD_R16, TT_EMB_TIMER_FWD_R32, TT_EMB_TIMER_FWD_R64,
+    TT_EMB_TIMER_BWD_R8, TT_EMB_TIMER_BWD_R16, TT_EMB_TIMER_BWD_R32, TT_EMB_TIMER_BWD_R64,
     TT_EMB_NUM_TIMERS
 };
 

@@ -34,7 +34,8 @@ EXPORTED = (
     "tt_emb_status_string", "tt_emb_timing_enable", "tt_emb_timing_read", "tt_emb_timer_name",
 )
 TIMER_NAMES = ("group_sort", "group_rle", "contract", "pool", "bwd_gather", "bwd_contract",
-               "bwd_reduce", "sgd")
+               "bwd_reduce", "sgd", "fwd_r8", "fwd_r16", "fwd_r32", "fwd_r64",
+               "bwd_r8", "bwd_r16", "bwd_r32", "bwd_r64")
 
 
 class tt_emb_options(C.Structure):

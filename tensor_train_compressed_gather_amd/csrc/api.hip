@@ -558,7 +558,9 @@ int tt_emb_timing_read(tt_emb_t h, double *ms, int32_t *count)
 const char *tt_emb_timer_name(int32_t id)
 {
     static const char *names[TM_COUNT] = {"group_sort", "group_rle", "contract", "pool",
-                                          "bwd_gather", "bwd_contract", "bwd_reduce", "sgd"};
+                                          "bwd_gather", "bwd_contract", "bwd_reduce", "sgd",
+                                          "fwd_r8", "fwd_r16", "fwd_r32", "fwd_r64",
+                                          "bwd_r8", "bwd_r16", "bwd_r32", "bwd_r64"};
     return (id >= 0 && id < TM_COUNT) ? names[id] : nullptr;
 }
 

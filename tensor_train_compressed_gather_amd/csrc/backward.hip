@@ -1050,17 +1050,29 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
         if (!p.force_generic) {
             hipLaunchKernelGGL(k_bwd_prep, dim3(1), dim3(64), 0, s, a);
             hipLaunchKernelGGL(k_bwd_g3t, dim3(64, T), dim3(kThreads), 0, s, a);
-            if (p.cls_mask & 1)
-                hipLaunchKernelGGL(k_bwd_class<8>, dim3(p.num_blocks * BwdLds<8>::OCC), dim3(BwdLds<8>::NW * 64), 0, s, a);
-            if (p.cls_mask & 2)
-                hipLaunchKernelGGL(k_bwd_class<16>, dim3(p.num_blocks * BwdLds<16>::OCC), dim3(BwdLds<16>::NW * 64), 0,
-                                   s, a);
-            if (p.cls_mask & 4)
-                hipLaunchKernelGGL(k_bwd_class<32>, dim3(p.num_blocks * BwdLds<32>::OCC), dim3(BwdLds<32>::NW * 64), 0,
-                                   s, a);
-            if (p.cls_mask & 8)
-                hipLaunchKernelGGL(k_bwd_class<64>, dim3(p.num_blocks * BwdLds<64>::OCC), dim3(BwdLds<64>::NW * 64), 0,
-                                   s, a);
+            for (int c = 0; c < 4; ++c) {
+                if (!(p.cls_mask & (1 << c))) continue;
+                timer_begin(p.timing, TM_BWD_CLS0 + c, s);
+                switch (c) {
+                case 0:
+                    hipLaunchKernelGGL(k_bwd_class<8>, dim3(p.num_blocks * BwdLds<8>::OCC), dim3(BwdLds<8>::NW * 64), 0,
+                                       s, a);
+                    break;
+                case 1:
+                    hipLaunchKernelGGL(k_bwd_class<16>, dim3(p.num_blocks * BwdLds<16>::OCC), dim3(BwdLds<16>::NW * 64),
+                                       0, s, a);
+                    break;
+                case 2:
+                    hipLaunchKernelGGL(k_bwd_class<32>, dim3(p.num_blocks * BwdLds<32>::OCC), dim3(BwdLds<32>::NW * 64),
+                                       0, s, a);
+                    break;
+                default:
+                    hipLaunchKernelGGL(k_bwd_class<64>, dim3(p.num_blocks * BwdLds<64>::OCC), dim3(BwdLds<64>::NW * 64),
+                                       0, s, a);
+                    break;
+                }
+                timer_end(p.timing, TM_BWD_CLS0 + c, s);
+            }
         }
         if (p.force_generic || p.any_generic)
             hipLaunchKernelGGL(k_bwd_runs, dim3(p.num_blocks * 2), dim3(kThreads), 0, s, a);

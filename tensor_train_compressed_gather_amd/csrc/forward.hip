@@ -563,10 +563,17 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
         hipLaunchKernelGGL(k_queue_init, dim3(1), dim3(kThreads), 0, s, p.ws, cg, hs);
         if (!p.force_generic) {
             hipLaunchKernelGGL(k_g3t, dim3(64, p.T), dim3(kThreads), 0, s, a);
-            if (p.cls_mask & 1) hipLaunchKernelGGL(k_contract<8>, dim3(cg.nb[0]), dim3(kThreads), 0, s, a, hs);
-            if (p.cls_mask & 2) hipLaunchKernelGGL(k_contract<16>, dim3(cg.nb[1]), dim3(kThreads), 0, s, a, hs);
-            if (p.cls_mask & 4) hipLaunchKernelGGL(k_contract<32>, dim3(cg.nb[2]), dim3(kThreads), 0, s, a, hs);
-            if (p.cls_mask & 8) hipLaunchKernelGGL(k_contract<64>, dim3(cg.nb[3]), dim3(kThreads), 0, s, a, hs);
+            for (int c = 0; c < 4; ++c) {
+                if (!(p.cls_mask & (1 << c))) continue;
+                timer_begin(p.timing, TM_FWD_CLS0 + c, s);
+                switch (c) {
+                case 0: hipLaunchKernelGGL(k_contract<8>, dim3(cg.nb[0]), dim3(kThreads), 0, s, a, hs); break;
+                case 1: hipLaunchKernelGGL(k_contract<16>, dim3(cg.nb[1]), dim3(kThreads), 0, s, a, hs); break;
+                case 2: hipLaunchKernelGGL(k_contract<32>, dim3(cg.nb[2]), dim3(kThreads), 0, s, a, hs); break;
+                default: hipLaunchKernelGGL(k_contract<64>, dim3(cg.nb[3]), dim3(kThreads), 0, s, a, hs); break;
+                }
+                timer_end(p.timing, TM_FWD_CLS0 + c, s);
+            }
         }
         if (p.force_generic || p.any_generic)
             hipLaunchKernelGGL(k_contract_generic, dim3(p.num_blocks * 4), dim3(kThreads), 0, s, a,

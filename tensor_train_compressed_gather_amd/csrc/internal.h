@@ -148,7 +148,7 @@ struct Ws {
 
 enum TimerId {
     TM_GROUP_SORT = 0, TM_GROUP_RLE, TM_CONTRACT, TM_POOL, TM_BWD_GATHER, TM_BWD_CONTRACT,
-    TM_BWD_REDUCE, TM_SGD, TM_COUNT
+    TM_BWD_REDUCE, TM_SGD, TM_FWD_CLS0, TM_BWD_CLS0 = TM_FWD_CLS0 + 4, TM_COUNT = TM_BWD_CLS0 + 4
 };
 struct Timing; // host-side event rings (api.hip)
 void timer_begin(Timing *tm, int id, hipStream_t s);
