@@ -543,10 +543,15 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
     constexpr int RG = NW / MT;                    // row groups (waves per r2 block)
     constexpr int NIT = (4 * MT + NW - 1) / NW;    // items per wave (rank 64)
     constexpr int NACC = kBal ? 4 : NIT;           // dC accumulators per wave
-    static_assert(RG * MT == NW && RG * 4 * MT * 256 <= L::STAGE, "(2) wave partials fit in the staging region");
+    static_assert(RG * MT == NW && (!kBal || RG * 4 * MT * 256 <= L::STAGE), "(2) wave partials fit in the staging region");
     // (3): waves form NP groups of MTW r1 blocks times KG groups of SPW columns
     constexpr int MTW = MT >= 2 ? 2 : 1, NP = MT / MTW, KG = NW / NP, SPW = R / KG;
     constexpr int CSTR = L::CSTR, CUNIT = L::CUNIT, PF = L::PF;
+    // guards that hold for every lane are folded at compile time, and LDS
+    // operand loads are unconditional (clamped addresses, then a select):
+    // a branch around each load would keep the scheduler from hoisting loads
+    // ahead of the MFMAs that consume them
+    constexpr bool kAllNT = NT % NW == 0, kAllR = R % 16 == 0;
     static_assert(NP * KG == NW && SPW * KG == R && (R & (R - 1)) == 0, "(3) splits the columns evenly");
     static_assert(KG * MT * 256 <= L::STAGE, "(3) partials fit in the staging region");
     static_assert(4 * R <= BT, "one G1 float4 per thread");
@@ -718,7 +723,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
 #pragma unroll
                         for (int j = 0; j < NTW; ++j) {
                             const int ntg = w + NW * j;
-                            if (ntg < NT) {
+                            if (kAllNT || ntg < NT) {
                                 const int col = ntg * 16 + li;
                                 acc[j] = mfma4(av, G2s[r * NCOL + (col ^ (r & 31))], acc[j]);
                                 acc2[j] = mfma4(av2, G2s[(r + 1) * NCOL + (col ^ ((r + 1) & 31))], acc2[j]);
@@ -732,7 +737,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
 #pragma unroll
                     for (int j = 0; j < NTW; ++j) {
                         const int ntg = w + NW * j;
-                        if (ntg < NT) {
+                        if (kAllNT || ntg < NT) {
                             const int col = ntg * 16 + li, j2 = col / R, r2 = col % R;
                             if (j2 < d2) {
 #pragma unroll
@@ -775,9 +780,10 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                         const float *g3 = G3s + (q - sb) * G3ST + (okr ? r2 : 0);
                         for (int j0 = 0; j0 < d3; j0 += 4) {
                             const int j3 = j0 + kq;
-                            const float av = (li < D12 && j3 < d3) ? gq[li * d3 + j3] : 0.f;
-                            const float bv = (okr && j3 < d3) ? g3[j3 * G3J] : 0.f;
-                            dacc[i] = mfma4(av, bv, dacc[i]);
+                            const bool okj = j3 < d3;
+                            const float ga = gq[(li < D12 ? li : 0) * d3 + (okj ? j3 : 0)];
+                            const float gb = g3[(okj ? j3 : 0) * G3J];
+                            dacc[i] = mfma4((li < D12 && okj) ? ga : 0.f, (okr && okj) ? gb : 0.f, dacc[i]);
                         }
                     }
                     // (2b) P3_u[r2][j3] = sum_m2 C_g[m2][r2] g_u[m2][j3], P rows per output
@@ -787,7 +793,8 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
 #pragma unroll
                         for (int s = 0; s < 4; ++s) {
                             const int m2 = kq * 4 + s;
-                            ca[s] = (m2 < D12 && okr) ? Cs[g * CUNIT + m2 * CSTR + r2] : 0.f;
+                            const float cv = Cs[g * CUNIT + m2 * CSTR + (okr ? r2 : 0)];
+                            ca[s] = (m2 < D12 && okr) ? cv : 0.f;
                         }
                         const int slot_r = li / d3, j3 = li - slot_r * d3;
                         for (int qs = qa + r0 * P; qs < qb; qs += rs * P) {
@@ -797,8 +804,8 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
 #pragma unroll
                             for (int s = 0; s < 4; ++s) {
                                 const int m2 = kq * 4 + s;
-                                const float bv = (okb && m2 < D12) ? Gs[(qs + slot_r - sb) * GST + m2 * d3 + j3] : 0.f;
-                                acc = mfma4(ca[s], bv, acc);
+                                const float gv = Gs[(qs + (okb ? slot_r : 0) - sb) * GST + (m2 < D12 ? m2 : 0) * d3 + j3];
+                                acc = mfma4(ca[s], (okb && m2 < D12) ? gv : 0.f, acc);
                             }
                             if (okb) {
                                 const int u = rec.ustart[g] + (qs + slot_r - rec.rowoff[g]);
@@ -871,15 +878,17 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                     for (int sl = 0; sl < SPW; sl += 2) {
                         const int s = (kg * SPW + sl + rot) & (R - 1);
                         const int s2 = (kg * SPW + sl + 1 + rot) & (R - 1);
-                        const float av = oka ? acol[s * DTST] : 0.f;
-                        const float av2 = oka ? acol[s2 * DTST] : 0.f;
+                        const float a1 = acol[s * DTST], a2 = acol[s2 * DTST];
+                        const float av = oka ? a1 : 0.f, av2 = oka ? a2 : 0.f;
 #pragma unroll
                         for (int m = 0; m < MTW; ++m) {
                             const int r1 = (mt0 + m) * 16 + li;
-                            const float bv = r1 < R ? G2s[r1 * NCOL + ((kq * R + s) ^ (r1 & 31))] : 0.f;
-                            const float bv2 = r1 < R ? G2s[r1 * NCOL + ((kq * R + s2) ^ (r1 & 31))] : 0.f;
-                            acc[m] = mfma4(av, bv, acc[m]);
-                            acc2[m] = mfma4(av2, bv2, acc2[m]);
+                            const bool okr1 = kAllR || r1 < R;
+                            const int rr1 = okr1 ? r1 : 0;
+                            const float b1 = G2s[rr1 * NCOL + ((kq * R + s) ^ (rr1 & 31))];
+                            const float b2 = G2s[rr1 * NCOL + ((kq * R + s2) ^ (rr1 & 31))];
+                            acc[m] = mfma4(av, okr1 ? b1 : 0.f, acc[m]);
+                            acc2[m] = mfma4(av2, okr1 ? b2 : 0.f, acc2[m]);
                         }
                     }
 #pragma unroll
@@ -911,17 +920,20 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
 #pragma unroll
                         for (int s = 0; s < 4; ++s) {
                             const int r1 = mt * 16 + li;
-                            ga[mt][s] = r1 < R ? G1s[(kq * 4 + s) * G1ST + r1] : 0.f;
+                            const float gv = G1s[(kq * 4 + s) * G1ST + ((kAllR || r1 < R) ? r1 : 0)];
+                            ga[mt][s] = (kAllR || r1 < R) ? gv : 0.f;
                         }
 #pragma unroll
                     for (int j = 0; j < NTW; ++j) {
                         const int ntg = w + NW * j;
-                        if (ntg < NT) {
+                        if (kAllNT || ntg < NT) {
                             const int col = ntg * 16 + li, j2 = col / R, r2 = col % R;
                             float bv[4];
 #pragma unroll
-                            for (int s = 0; s < 4; ++s)
-                                bv[s] = (j2 < d2 && s < d1) ? Cs[kq * CUNIT + (s * d2 + j2) * CSTR + r2] : 0.f;
+                            for (int s = 0; s < 4; ++s) {
+                                const float cv = Cs[kq * CUNIT + (s * d2 + (j2 < d2 ? j2 : 0)) * CSTR + r2];
+                                bv[s] = (j2 < d2 && s < d1) ? cv : 0.f;
+                            }
 #pragma unroll
                             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll

@@ -29,6 +29,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kCStride = 68;                   // LDS row stride of a prefix tile (R2 <= 64)
 constexpr int kCUnit = 16 * kCStride + 16;     // floats per unit (extra 16 rotates banks)
 constexpr int kCTile = kUnitsPerTile * kCUnit; // floats per prefix tile
+constexpr int kEsFloats = 32 * 68;              // E rows staged per chunk (32 rows of D <= 64)
 constexpr int kSchedStatic = 1, kSchedSteal = 2, kSchedStealL2 = 3;
 
 struct FwdArgs {
@@ -167,30 +168,32 @@ __device__ __forceinline__ void prefetch_a(const FwdArgs &a, const ChunkRec &nr,
     const int d1 = tb.d1;
     const int lane = threadIdx.x & 63, li = lane & 15, kq = lane >> 4;
     const int g = li >> 2, j1 = li & 3;
+    // out-of-range lanes read the first unit's slice (always valid) and are
+    // zeroed when used: zeroing a register a load may still target would make
+    // the wave wait for all of its outstanding stores
     const bool ok = g < nr.nu && j1 < d1;
-    const float *src = a.cores.g[t][0] + ((int64_t)(ok ? nr.i1[g] : 0) * d1 + (ok ? j1 : 0)) * R + kq * KQ;
+    const float *src = a.cores.g[t][0] + ((int64_t)(ok ? nr.i1[g] : nr.i1[0]) * d1 + (ok ? j1 : 0)) * R + kq * KQ;
     if (KQ >= 4) {
 #pragma unroll
         for (int s = 0; s < 16; s += 4) {
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (ok && s < KQ) v = *reinterpret_cast<const float4 *>(src + s);
-            apf[s] = v.x;
-            apf[s + 1] = v.y;
-            apf[s + 2] = v.z;
-            apf[s + 3] = v.w;
+            const floatx4 v = *reinterpret_cast<const floatx4 *>(src + (s < KQ ? s : 0));
+            apf[s] = v[0];
+            apf[s + 1] = v[1];
+            apf[s + 2] = v[2];
+            apf[s + 3] = v[3];
         }
     } else {
 #pragma unroll
-        for (int s = 0; s < 16; ++s) apf[s] = (ok && s < KQ) ? src[s] : 0.f;
+        for (int s = 0; s < 16; ++s) apf[s] = src[s < KQ ? s : 0];
     }
     apf_tile = nr.tile;
 }
 
-template <int R>
-__device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec, float *Cs,
+template <int R, class Mid>
+__device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec, float *Cs, float *Es,
                                            float (&breg)[64], int &bkey, int &lds_tile, int *s_flag,
                                            float (&apf)[16], int &apf_tile, ChunkRec *rnext, bool has_next,
-                                           int pre, int &hits, int &misses, int c, int cn)
+                                           int pre, int &hits, int &misses, int c, int cn, Mid &&mid)
 {
     constexpr int KQ = R / 4;           // K values each lane feeds per output tile
     constexpr int NT = R / 4;           // 16-column tiles of the padded d2*R2 (d2 <= 4)
@@ -221,20 +224,22 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
     auto load_b = [&](int e, float (&b)[KQ]) {
         int j, rb, cnt;
         piece(e, j, rb, cnt);
+        // lanes past the tile's rows read the tile's first row; their outputs
+        // are never stored (no zeroing: see prefetch_a)
         const bool ok = slot < cnt;
-        const float *src = G3t + ((int64_t)(ok ? rec.i3[rb + slot] : 0) * d3 + (ok ? j3 : 0)) * R + kq * KQ;
+        const float *src = G3t + ((int64_t)rec.i3[rb + (ok ? slot : 0)] * d3 + j3) * R + kq * KQ;
         if constexpr (KQ % 4 == 0) {
 #pragma unroll
             for (int s = 0; s < KQ; s += 4) {
-                const float4 v = ok ? *reinterpret_cast<const float4 *>(src + s) : make_float4(0.f, 0.f, 0.f, 0.f);
-                b[s] = v.x;
-                b[s + 1] = v.y;
-                b[s + 2] = v.z;
-                b[s + 3] = v.w;
+                const floatx4 v = *reinterpret_cast<const floatx4 *>(src + s);
+                b[s] = v[0];
+                b[s + 1] = v[1];
+                b[s + 2] = v[2];
+                b[s + 3] = v[3];
             }
         } else {
 #pragma unroll
-            for (int s = 0; s < KQ; ++s) b[s] = ok ? src[s] : 0.f;
+            for (int s = 0; s < KQ; ++s) b[s] = src[s];
         }
     };
     float bnext[KQ];
@@ -261,7 +266,7 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
         if (!have) {
             const int g = li >> 2, j1 = li & 3;
             const bool oka = g < rec.nu && j1 < d1;
-            const float *srcA = G1 + ((int64_t)(oka ? rec.i1[g] : 0) * d1 + (oka ? j1 : 0)) * R + kq * KQ;
+            const float *srcA = G1 + ((int64_t)(oka ? rec.i1[g] : rec.i1[0]) * d1 + (oka ? j1 : 0)) * R + kq * KQ;
             float areg[KQ];
             if (apf_tile == rec.tile) {
 #pragma unroll
@@ -269,16 +274,19 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
             } else if constexpr (KQ % 4 == 0) {
 #pragma unroll
                 for (int s = 0; s < KQ; s += 4) {
-                    const float4 v = oka ? *reinterpret_cast<const float4 *>(srcA + s) : make_float4(0.f, 0.f, 0.f, 0.f);
-                    areg[s] = v.x;
-                    areg[s + 1] = v.y;
-                    areg[s + 2] = v.z;
-                    areg[s + 3] = v.w;
+                    const floatx4 v = *reinterpret_cast<const floatx4 *>(srcA + s);
+                    areg[s] = v[0];
+                    areg[s + 1] = v[1];
+                    areg[s + 2] = v[2];
+                    areg[s + 3] = v[3];
                 }
             } else {
 #pragma unroll
-                for (int s = 0; s < KQ; ++s) areg[s] = oka ? srcA[s] : 0.f;
+                for (int s = 0; s < KQ; ++s) areg[s] = srcA[s];
             }
+            // rows of absent units / j1 contribute zeros to C (their C rows are never read)
+#pragma unroll
+            for (int s = 0; s < KQ; ++s) areg[s] = oka ? areg[s] : 0.f;
             const int key = (int)(tb.i2_base + (uint32_t)rec.i2);
             if (bkey != key) {
 #pragma unroll
@@ -343,7 +351,12 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
     __syncthreads();
     if (has_next && rnext->tile != rec.tile) prefetch_a(a, *rnext, apf, apf_tile);
 
-    // -------- unique rows E_u = C_unit . G3[i3_u], 16/d3 rows per output tile
+    // -------- unique rows E_u = C_unit . G3[i3_u], 16/d3 rows per output tile,
+    // staged in LDS (Es, row stride Dp + 4) and stored coalesced once every
+    // load of the chunk has been waited for
+    mid();
+    const int EST = Dp + 4;
+    const bool staged = rec.rowoff[4] * EST <= kEsFloats; // else rows go straight to E
     const bool okm = li < D12;
     for (int e = w; e < np; e += 4) {
         float bcur[KQ];
@@ -369,8 +382,8 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(okm ? ca[s] : 0.f, bcur[s], acc, 0, 0, 0);
         }
         if (slot < cnt) {
-            const int u = rec.ustart[j] + (rb - rec.rowoff[j]) + slot;
-            float *Erow = Et + (int64_t)u * Dp;
+            float *Erow = staged ? Es + (rb + slot) * EST
+                                 : Et + (int64_t)(rec.ustart[j] + (rb - rec.rowoff[j]) + slot) * Dp;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int m2 = kq * 4 + v;
@@ -378,19 +391,26 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
             }
         }
     }
+    if (staged) {
+        __syncthreads();
+        const int nrows = rec.rowoff[4], c4 = Dp >> 2;
+        for (int e = threadIdx.x; e < nrows * c4; e += kThreads) {
+            const int q = e / c4, r4 = e - q * c4;
+            const int j = (q >= rec.rowoff[1]) + (q >= rec.rowoff[2]) + (q >= rec.rowoff[3]);
+            const int u = rec.ustart[j] + (q - rec.rowoff[j]);
+            reinterpret_cast<floatx4 *>(Et + (int64_t)u * Dp)[r4] = *reinterpret_cast<const floatx4 *>(Es + q * EST + 4 * r4);
+        }
+    }
 }
 
-// Persistent contraction kernel for the tables of one MFMA rank class
-// (R1 = R2 = R).  Wave 0 keeps two chunks claimed ahead: while chunk i runs,
-// the record of chunk i+1 is in flight and the claim of chunk i+2 is
-// outstanding; the next chunk's A operand is loaded before this chunk's stores.
 template <int R>
 __global__ __launch_bounds__(kThreads, 2) void k_contract(FwdArgs a, int heads_stride)
 {
     constexpr int CLS = R == 8 ? 0 : R == 16 ? 1 : R == 32 ? 2 : 3;
     __shared__ __attribute__((aligned(16))) float Cs[kCTile];
+    __shared__ __attribute__((aligned(16))) float Es[kEsFloats];
     __shared__ ChunkRec rbuf[2];
-    __shared__ int s_cur, s_next, s_flag;
+    __shared__ int s_cur, s_next, s_next2, s_flag;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int nb = gridDim.x, me = blockIdx.x;
     const Ws &ws = a.ws;
@@ -424,15 +444,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_contract(FwdArgs a, int heads_s
             pre = reinterpret_cast<const int *>(&ws.crec[cn])[lane];
             raw = claim_start(heads, me, vi, nb, nvict);
         }
-        chunk_mfma<R>(a, rbuf[buf], Cs, breg, bkey, lds_tile, &s_flag, apf, apf_tile, &rbuf[buf ^ 1], cn >= 0, pre,
-                      hits, misses, c, cn);
-        __syncthreads(); // everyone is done with rbuf[buf], s_cur and s_next
-        if (w == 0) {
-            const int c2 = cn < 0 ? -1 : claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals);
-            if (lane == 0) {
-                s_cur = cn;
-                s_next = c2;
+        // the claim of chunk c+2 completes before this chunk's stores are issued
+        // (a wait on the atomic issued after them would also wait for them)
+        auto mid = [&]() {
+            if (w == 0) {
+                const int c2 = cn < 0 ? -1 : claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals);
+                if (lane == 0) s_next2 = c2;
             }
+        };
+        chunk_mfma<R>(a, rbuf[buf], Cs, Es, breg, bkey, lds_tile, &s_flag, apf, apf_tile, &rbuf[buf ^ 1], cn >= 0,
+                      pre, hits, misses, c, cn, mid);
+        __syncthreads(); // everyone is done with rbuf[buf], s_cur and s_next
+        if (threadIdx.x == 0) {
+            s_cur = cn;
+            s_next = s_next2;
         }
         __syncthreads();
         buf ^= 1;
