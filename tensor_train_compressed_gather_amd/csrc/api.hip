@@ -154,6 +154,8 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.P3 = (float *)take(4 * (p3_elems > part_elems ? p3_elems : part_elems));
     // G1 partials are indexed by work position (< units) with a uniform stride
     w.G1P = (float *)take(4 * (size_t)units_bound * h->max_d1R1);
+    // [first, last) unique-row range (in (table, i3) order) of every G3 slice
+    w.g3rng = (int32_t *)take(4 * 2 * ((size_t)h->sum_n[2] + 1));
     // buffers where the sorts end
     const int fm = sort_passes(nnz, h->key_bits) & 1;
     const int fu = sort_passes(nnz, h->key2_bits) & 1;

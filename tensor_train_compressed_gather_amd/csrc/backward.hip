@@ -404,11 +404,33 @@ __global__ __launch_bounds__(kThreads) void k_reduce_g1(BwdArgs a, int total_slo
         const int last = lo;
         const int per = tb.d1 * tb.R1;
         float *dst = a.grads.g[t][0] + (int64_t)i1 * per;
-        for (int e = threadIdx.x; e < per; e += kThreads) {
-            float c = 0.f;
-            for (int unit = first; unit < last; ++unit) c += ws.G1P[(int64_t)ws.uinv[unit] * a.g1stride + e];
-            dst[e] = c;
+        // partial rows of the slot's units (in unit order) staged kThreads at a
+        // time in LDS, then summed in that order with 8 loads in flight
+        __shared__ int rows[kThreads];
+        for (int e0 = 0; e0 < per; e0 += 4 * kThreads) {
+            float c[4] = {0.f, 0.f, 0.f, 0.f}; // elements e0 + threadIdx.x + k*kThreads
+            for (int u0 = first; u0 < last; u0 += kThreads) {
+                const int n = last - u0 < kThreads ? last - u0 : kThreads;
+                __syncthreads();
+                if ((int)threadIdx.x < n) rows[threadIdx.x] = ws.uinv[u0 + threadIdx.x];
+                __syncthreads();
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int e = e0 + threadIdx.x + k * kThreads;
+                    if (e >= per) break;
+                    float s = c[k];
+#pragma unroll 8
+                    for (int i = 0; i < n; ++i) s += ws.G1P[(int64_t)rows[i] * a.g1stride + e];
+                    c[k] = s;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int e = e0 + threadIdx.x + k * kThreads;
+                if (e < per) dst[e] = c[k];
+            }
         }
+        __syncthreads();
     }
 }
 
@@ -425,47 +447,61 @@ __global__ __launch_bounds__(kThreads) void k_key3(BwdArgs a, uint32_t *k, int32
     }
 }
 
-// dG3[t][i3] = sum over unique rows of table t with that i3, in unique-id
-// order, of their partials; zero when none.
-__global__ __launch_bounds__(kThreads) void k_reduce_g3(BwdArgs a, const uint32_t *k3,
-                                                        const int32_t *order, int total_slots)
+// Row range of every G3 slice in the (table, i3)-sorted unique rows: run
+// edges of the sorted keys (slots without rows keep the empty range 0..0).
+__global__ __launch_bounds__(kThreads) void k_g3_bounds(BwdArgs a, const uint32_t *k3, int total_slots)
 {
     const Ws &ws = a.ws;
     const int64_t U = ws.ctrl[CTRL_U];
+    int32_t *first = ws.g3rng, *last = ws.g3rng + total_slots;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < U; q += stride) {
+        const uint32_t key = k3[q];
+        if (key >= (uint32_t)total_slots) continue;
+        if (q == 0 || k3[q - 1] != key) first[key] = (int32_t)q;
+        if (q == U - 1 || k3[q + 1] != key) last[key] = (int32_t)(q + 1);
+    }
+}
+
+// dG3[t][i3] = sum over unique rows of table t with that i3, in unique-id
+// order, of their partials; zero when none.  Each (phase, element) thread
+// keeps kG3Acc interleaved partial sums over its rows, added in order, and
+// the phases are added in order: a fixed order with several loads in flight.
+constexpr int kG3Acc = 8;
+
+__global__ __launch_bounds__(kThreads) void k_reduce_g3(BwdArgs a, const int32_t *order, int total_slots)
+{
+    const Ws &ws = a.ws;
+    __shared__ float part[kThreads];
     for (int slot = blockIdx.x; slot < total_slots; slot += gridDim.x) {
         int t = 0;
         while (t + 1 < a.T && a.tab[t + 1].i3_base <= (uint32_t)slot) ++t;
         const TableDesc &tb = a.tab[t];
         const int i3 = slot - (int)tb.i3_base;
         if (i3 >= tb.n3) continue;
-        int64_t lo = 0, hi = U;
-        while (lo < hi) {
-            const int64_t mid = (lo + hi) >> 1;
-            if (k3[mid] < (uint32_t)slot) lo = mid + 1;
-            else hi = mid;
-        }
-        const int64_t first = lo;
-        hi = U;
-        while (lo < hi) {
-            const int64_t mid = (lo + hi) >> 1;
-            if (k3[mid] <= (uint32_t)slot) lo = mid + 1;
-            else hi = mid;
-        }
-        const int64_t last = lo;
+        const int64_t first = ws.g3rng[slot], last = ws.g3rng[total_slots + slot];
         const int per = tb.R2 * tb.d3;
         float *dst = a.grads.g[t][2] + (int64_t)i3 * per;
         const float *src = ws.P3 + ws.p3base[t];
-        // rp row phases of per-element threads; phase ph sums rows first+ph,
-        // first+ph+rp, ... in order, then the phases are added in order.
         const int rp = per >= kThreads ? 1 : kThreads / per;
         const int ph = threadIdx.x / per < rp ? threadIdx.x / per : rp; // rp = idle
-        __shared__ float part[kThreads];
         for (int e0 = 0; e0 < per; e0 += kThreads) {
             const int e = e0 + (rp == 1 ? threadIdx.x : threadIdx.x - ph * per);
             float c = 0.f;
             if (ph < rp && e < per) {
-#pragma unroll 8
-                for (int64_t q = first + ph; q < last; q += rp) c += src[(int64_t)order[q] * per + e];
+                float acc[kG3Acc];
+#pragma unroll
+                for (int k = 0; k < kG3Acc; ++k) acc[k] = 0.f;
+                int64_t q = first + ph;
+                for (; q + (kG3Acc - 1) * rp < last; q += kG3Acc * rp) {
+#pragma unroll
+                    for (int k = 0; k < kG3Acc; ++k) acc[k] += src[(int64_t)order[q + k * rp] * per + e];
+                }
+#pragma unroll
+                for (int k = 0; k < kG3Acc; ++k)
+                    if (q + k * rp < last) acc[k] += src[(int64_t)order[q + k * rp] * per + e];
+#pragma unroll
+                for (int k = 0; k < kG3Acc; ++k) c += acc[k];
             }
             if (rp == 1) {
                 if (e < per) dst[e] = c;
@@ -1110,8 +1146,15 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
         k3 = p.ws.keys0;
         o3 = p.ws.u3order;
     }
+    {
+        hipError_t e = launch_fill_i32(p.ws.g3rng, 0, 2 * (int64_t)sum_n3, s);
+        if (e != hipSuccess) return e;
+        int g = ceil_div(p.nnz > 0 ? p.nnz : 1, kThreads);
+        if (g > 8192) g = 8192;
+        hipLaunchKernelGGL(k_g3_bounds, dim3(g), dim3(kThreads), 0, s, a, k3, sum_n3);
+    }
     hipLaunchKernelGGL(k_reduce_g3, dim3(sum_n3 > 0 ? (sum_n3 < 65535 ? sum_n3 : 65535) : 1), dim3(kThreads), 0,
-                       s, a, k3, o3, sum_n3);
+                       s, a, o3, sum_n3);
     timer_end(p.timing, TM_BWD_REDUCE, s);
     return hipGetLastError();
 }

@@ -538,16 +538,31 @@ __global__ __launch_bounds__(kThreads) void k_pool(const TableDesc *tab, int T, 
         while (lpr < c4n) lpr <<= 1;
         const int rf = 64 / lpr;
         const int c4 = lane & (lpr - 1), r = lane / lpr;
+        const int cc = c4 < c4n ? c4 : 0;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (c4 < c4n) {
-            for (int64_t l = lo + r; l < hi; l += rf) {
-                int u = ws.inv[l];
-                u = u < u0 ? u0 : (u >= u1 ? u1 - 1 : u);
-                const float4 v = *reinterpret_cast<const float4 *>(Et + (int64_t)u * tb.Dp + 4 * c4);
-                acc.x += v.x;
-                acc.y += v.y;
-                acc.z += v.z;
-                acc.w += v.w;
+        // 64 lookups at a time: one coalesced load of their unique rows, then
+        // the E rows in flight together (rf rows per instruction, 4 deep)
+        for (int64_t l0 = lo; l0 < hi; l0 += 64) {
+            const int n = hi - l0 < 64 ? (int)(hi - l0) : 64;
+            int uu = ws.inv[l0 + (lane < n ? lane : 0)];
+            uu = uu < u0 ? u0 : (uu >= u1 ? u1 - 1 : uu);
+            const int nk = (n + rf - 1) / rf; // row steps, uniform over the wave
+            for (int k0 = 0; k0 < nk; k0 += 4) {
+                float4 v[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int i = r + (k0 + kk) * rf;
+                    const int u = __shfl(uu, i < n ? i : 0, 64);
+                    v[kk] = *reinterpret_cast<const float4 *>(Et + (int64_t)u * tb.Dp + 4 * cc);
+                    if (!(i < n && k0 + kk < nk && c4 < c4n)) v[kk] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    acc.x += v[kk].x;
+                    acc.y += v[kk].y;
+                    acc.z += v[kk].z;
+                    acc.w += v[kk].w;
+                }
             }
         }
         for (int m = lpr; m < 64; m <<= 1) {

@@ -139,6 +139,7 @@ struct Ws {
     // the partial sums of cut runs ([task][left, right][gstride]) live in P3's space
     float *P3;               // per-unique-row G3 partials
     float *G1P;              // per-unit G1 partials
+    int32_t *g3rng;          // [2][sum n3] row range of each G3 slice in the (table, i3) order
     uint32_t *key3;          // sorted (i3_base + i3) of unique rows
     int32_t *u3order;        // unique rows in (table, i3, unique id) order
     // sort buffers of the unit order (kept apart from the canonical perm)
