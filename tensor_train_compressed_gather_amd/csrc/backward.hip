@@ -551,7 +551,8 @@ struct BwdLds {
     static constexpr int NCOL = 4 * R;                 // columns (j2, r2), d2 padded to 4
     static constexpr int CSTR = R + 4;                 // row stride of C / dC
     static constexpr int CUNIT = 16 * CSTR + 16;       // floats per unit
-    static constexpr int G2S = R * NCOL;
+    static constexpr int G2ST = NCOL + 1;              // odd row stride of the G2 slice
+    static constexpr int G2S = R * G2ST;
     static constexpr int CS = 4 * CUNIT;
     static constexpr int G1ST = R + 1;                 // odd row stride: (1) reads rows across lanes
     static constexpr int G1S = 16 * G1ST;              // [unit][j1][r1]
@@ -598,7 +599,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
     // dC transposed ([col][(g, j1)]) for the dG1 partials
     float *G2s = lds, *Cs = lds + L::G2S, *dT = Cs + L::CS, *G1s = dT + L::CS, *Sg = G1s + L::G1S;
     static_assert(L::NCOL * L::DTST <= L::CS, "transposed dC fits in its region");
-    constexpr int G1ST = L::G1ST, DTST = L::DTST;
+    constexpr int G1ST = L::G1ST, DTST = L::DTST, G2ST = L::G2ST;
     const Ws &ws = a.ws;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, kq = lane >> 4;
     const int mb = w % MT, rg = w / MT; // (2): this wave's r2 block and row group
@@ -630,11 +631,11 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
         int rb = L::STAGE / (GST + G3ST);
         rb = rb < kMaxChunkRows ? rb : kMaxChunkRows;
         float *Gs = Sg, *G3s = Sg + rb * GST;
-        {   // stage G2[i2] as G2s[r][col ^ (r & 31)], zero-padded to NCOL columns
+        {   // stage G2[i2] as G2s[r][col] (row stride NCOL + 1), zero-padded to NCOL columns
             const float *src = a.cores.g[t][1] + (int64_t)i2 * R * d2 * R;
             for (int e = tid; e < R * NCOL; e += BT) {
                 const int r = e / NCOL, c = e - r * NCOL;
-                G2s[r * NCOL + (c ^ (r & 31))] = c < d2 * R ? src[r * d2 * R + c] : 0.f;
+                G2s[r * G2ST + c] = c < d2 * R ? src[r * d2 * R + c] : 0.f;
             }
         }
         floatx4 g2acc[MT][NTW], dacc[NACC]; // this wave's part of the units' dC
@@ -761,8 +762,8 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                             const int ntg = w + NW * j;
                             if (kAllNT || ntg < NT) {
                                 const int col = ntg * 16 + li;
-                                acc[j] = mfma4(av, G2s[r * NCOL + (col ^ (r & 31))], acc[j]);
-                                acc2[j] = mfma4(av2, G2s[(r + 1) * NCOL + (col ^ ((r + 1) & 31))], acc2[j]);
+                                acc[j] = mfma4(av, G2s[r * G2ST + col], acc[j]);
+                                acc2[j] = mfma4(av2, G2s[(r + 1) * G2ST + col], acc2[j]);
                             }
                         }
                     }
@@ -903,28 +904,34 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                     const int g = li >> 2, j1 = li & 3, kg = w % KG, mt0 = (w / KG) * MTW;
                     const bool oka = kq < d2 && j1 < d1;
                     const float *acol = dT + kq * R * DTST + li; // dT[(kq*R + s)][(g, j1) = li]
-                    // the two k-quarters sharing a half-wave walk columns 16 apart
-                    // so their dT and G2s reads fall in distinct banks
-                    const int rot = R >= 32 ? 16 * (kq & 1) : 0;
+                    // the two k-quarters sharing a half-wave walk column blocks 16
+                    // apart (bit 4 of the column flipped for odd kq), so their dT
+                    // and G2s reads fall in distinct banks; the addresses stay
+                    // base + constant along the loop
+                    static_assert(SPW <= 16 || R < 32, "the column flip must not touch the step index");
+                    const int sbase = (kg * SPW) ^ (R >= 32 ? 16 * (kq & 1) : 0);
+                    const float *ab = acol + sbase * DTST;
+                    const float *g2r[MTW];
+                    bool okr1[MTW];
+#pragma unroll
+                    for (int m = 0; m < MTW; ++m) {
+                        const int r1 = (mt0 + m) * 16 + li;
+                        okr1[m] = kAllR || r1 < R;
+                        g2r[m] = G2s + (okr1[m] ? r1 : 0) * G2ST + kq * R + sbase;
+                    }
                     // two independent chains per output tile (even and odd steps)
                     floatx4 acc[MTW], acc2[MTW];
 #pragma unroll
                     for (int m = 0; m < MTW; ++m) acc[m] = acc2[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+#pragma unroll
                     for (int sl = 0; sl < SPW; sl += 2) {
-                        const int s = (kg * SPW + sl + rot) & (R - 1);
-                        const int s2 = (kg * SPW + sl + 1 + rot) & (R - 1);
-                        const float a1 = acol[s * DTST], a2 = acol[s2 * DTST];
+                        const float a1 = ab[sl * DTST], a2 = ab[(sl + 1) * DTST];
                         const float av = oka ? a1 : 0.f, av2 = oka ? a2 : 0.f;
 #pragma unroll
                         for (int m = 0; m < MTW; ++m) {
-                            const int r1 = (mt0 + m) * 16 + li;
-                            const bool okr1 = kAllR || r1 < R;
-                            const int rr1 = okr1 ? r1 : 0;
-                            const float b1 = G2s[rr1 * NCOL + ((kq * R + s) ^ (rr1 & 31))];
-                            const float b2 = G2s[rr1 * NCOL + ((kq * R + s2) ^ (rr1 & 31))];
-                            acc[m] = mfma4(av, okr1 ? b1 : 0.f, acc[m]);
-                            acc2[m] = mfma4(av2, okr1 ? b2 : 0.f, acc2[m]);
+                            const float b1 = g2r[m][sl], b2 = g2r[m][sl + 1];
+                            acc[m] = mfma4(av, okr1[m] ? b1 : 0.f, acc[m]);
+                            acc2[m] = mfma4(av2, okr1[m] ? b2 : 0.f, acc2[m]);
                         }
                     }
 #pragma unroll
