@@ -559,11 +559,11 @@ struct BwdLds {
     static constexpr int DTST = 17;                    // transposed dC: [col][(g, j1)], stride 17
     static constexpr int STAGE = CLS == 3 ? 14336 : CLS == 2 ? 10240 : 6144;
     static constexpr int TOTAL = G2S + 2 * CS + G1S + STAGE;
-    static constexpr int OCC = CLS == 3 ? 1 : 2; // blocks per CU
+    static constexpr int OCC = CLS == 3 ? 1 : CLS == 1 ? 3 : 2; // blocks per CU
     static constexpr int NW = CLS == 3 ? 8 : 4;                  // waves per block
     // float4 registers per thread that carry the next chunk's first rows while
     // this chunk computes (the rows of a 64-column table at chunk_rows 32)
-    static constexpr int PF = CLS == 3 ? 2 : CLS == 2 ? 6 : CLS == 1 ? 4 : 2;
+    static constexpr int PF = CLS == 3 ? 2 : CLS == 2 ? 6 : CLS == 1 ? 3 : 2;
 };
 
 template <int R>
