@@ -638,9 +638,14 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                 G2s[r * G2ST + c] = c < d2 * R ? src[r * d2 * R + c] : 0.f;
             }
         }
-        floatx4 g2acc[MT][NTW], dacc[NACC]; // this wave's part of the units' dC
+        // this wave's part of the units' dC; at rank 64 (few rows per wave
+        // and unit) a second chain takes every other row
+        constexpr int NACC2 = kBal ? 1 : NACC;
+        floatx4 g2acc[MT][NTW], dacc[NACC], dacc2[NACC2];
 #pragma unroll
         for (int i = 0; i < NACC; ++i) dacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NACC2; ++i) dacc2[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -786,6 +791,8 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                 }
 #pragma unroll
                 for (int i = 0; i < NACC; ++i) dacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < NACC2; ++i) dacc2[i] = floatx4{0.f, 0.f, 0.f, 0.f};
                 cur_tile = rec.tile;
                 __syncthreads(); // C tile written
             }
@@ -811,16 +818,35 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                     const int qa = sb > rec.rowoff[g] ? sb : rec.rowoff[g];
                     const int qe = rec.rowoff[g] + rec.ccnt[g];
                     const int qb = sb + n < qe ? sb + n : qe;
-                    // (2a) dC_g[m2][r2] += sum_j3 g_u[m2][j3] G3[i3_u][r2][j3]
-                    for (int q = qa + r0; q < qb; q += rs) {
+                    // (2a) dC_g[m2][r2] += sum_j3 g_u[m2][j3] G3[i3_u][r2][j3]; with
+                    // d3 = 4 (one k step per row) two rows per step into two chains
+                    auto row_ops = [&](int q, int j0, float &av, float &bv) {
                         const float *gq = Gs + (q - sb) * GST;
                         const float *g3 = G3s + (q - sb) * G3ST + (okr ? r2 : 0);
+                        const int j3 = j0 + kq;
+                        const bool okj = j3 < d3;
+                        const float ga = gq[(li < D12 ? li : 0) * d3 + (okj ? j3 : 0)];
+                        const float gb = g3[(okj ? j3 : 0) * G3J];
+                        av = (li < D12 && okj) ? ga : 0.f;
+                        bv = (okr && okj) ? gb : 0.f;
+                    };
+                    int q = qa + r0;
+                    if constexpr (!kBal) {
+                        if (d3 == 4) {
+                            for (; q + rs < qb; q += 2 * rs) {
+                                float a0, b0, a1, b1;
+                                row_ops(q, 0, a0, b0);
+                                row_ops(q + rs, 0, a1, b1);
+                                dacc[i] = mfma4(a0, b0, dacc[i]);
+                                dacc2[i < NACC2 ? i : 0] = mfma4(a1, b1, dacc2[i < NACC2 ? i : 0]);
+                            }
+                        }
+                    }
+                    for (; q < qb; q += rs) {
                         for (int j0 = 0; j0 < d3; j0 += 4) {
-                            const int j3 = j0 + kq;
-                            const bool okj = j3 < d3;
-                            const float ga = gq[(li < D12 ? li : 0) * d3 + (okj ? j3 : 0)];
-                            const float gb = g3[(okj ? j3 : 0) * G3J];
-                            dacc[i] = mfma4((li < D12 && okj) ? ga : 0.f, (okr && okj) ? gb : 0.f, dacc[i]);
+                            float a0, b0;
+                            row_ops(q, j0, a0, b0);
+                            dacc[i] = mfma4(a0, b0, dacc[i]);
                         }
                     }
                     // (2b) P3_u[r2][j3] = sum_m2 C_g[m2][r2] g_u[m2][j3], P rows per output
@@ -859,6 +885,12 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
             }
             __syncthreads(); // rows done: C and the staged rows are free
             if (tile_end) {
+                if constexpr (!kBal) {
+#pragma unroll
+                    for (int i = 0; i < NACC; ++i)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) dacc[i][v] += dacc2[i < NACC2 ? i : 0][v];
+                }
                 if constexpr (kBal) {
                     // dC of each unit = the RG wave partials added in order; it goes
                     // to Cs (C is dead) and, transposed, to dT

@@ -311,14 +311,14 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
             for (int s = 0; s < KQ; ++s) {
 #pragma unroll
                 for (int j = 0; j < NTW; ++j)
-                    if (w + 4 * j < NT)
+                    if (NT % 4 == 0 || w + 4 * j < NT) // folded when every wave has NTW tiles
                         acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(areg[s], breg[j * KQ + s], acc[j], 0, 0, 0);
             }
             // lane (kq, li) holds rows 4*kq + v = (unit kq, j1 = v), column ntg*16 + li
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 const int ntg = w + 4 * j;
-                if (ntg < NT) {
+                if (NT % 4 == 0 || ntg < NT) {
                     const int col = ntg * 16 + li;
                     const int j2 = col / R, r2 = col % R;
                     if (j2 < d2 && kq < rec.nu) {
