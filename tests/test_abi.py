@@ -36,6 +36,23 @@ def test_status_strings():
     assert tt.tt_emb_status_string(-99) == "unknown status"
 
 
+def test_timer_names_match_the_binding():
+    n = len(tt.TIMER_NAMES)
+    assert [tt.tt_emb_timer_name(i) for i in range(n)] == list(tt.TIMER_NAMES)
+    assert tt.tt_emb_timer_name(n) is None and tt.tt_emb_timer_name(-1) is None
+    # one timer per matrix-core contraction kernel, forward and backward
+    assert all(f"{p}_r{r}" in tt.TIMER_NAMES for p in ("fwd", "bwd") for r in (8, 16, 32, 64))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
 def _create(N, n, d, R, opt=None):
     h = C.c_void_p()
     NN = np.asarray(N, np.int64)

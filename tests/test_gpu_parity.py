@@ -230,6 +230,29 @@ def test_sgd_update_matches_oracle_delta():
         assert np.abs(delta - ref).max() <= TOL * scale + ulp, k
 
 
+def test_kernel_timers_record_every_launch():
+    # the per-kernel timers behind the bench's roofline: one interval per call
+    # of each rank class present, inside its phase
+    w = W.make_workload(5, bags=64)
+    run = Run(w)
+    h = run.emb.handle
+    tt.tt_emb_timing_read(h)
+    tt.tt_emb_timing_enable(h, True)
+    for _ in range(3):
+        run.forward()
+        run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)
+    tt.tt_emb_timing_enable(h, False)
+    ph = tt.tt_emb_timing_read(h)
+    ranks = {t.R[1] for t in w.tables}
+    for r in (8, 16, 32, 64):
+        for p in ("fwd", "bwd"):
+            ms, n = ph[f"{p}_r{r}"]
+            assert n == (3 if r in ranks else 0), (p, r, n)
+            if n:
+                assert 0 < ms <= ph["contract" if p == "fwd" else "bwd_contract"][0]
+    assert ph["contract"][1] == 3 and ph["bwd_contract"][1] == 3
+
+
 def test_bit_reproducible_forward_and_backward():
     w = W.make_workload(5, bags=64)
     run = Run(w)
