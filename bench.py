@@ -81,6 +81,17 @@ def phase_bytes(w, U_r):
     return e + 4 * w.nnz + 8 * (w.T * w.B + 1) + 4 * w.B * w.sum_D
 
 
+def split_timers(per_step):
+    """Per-step timer readings -> (phases, single-kernel timers, grouping
+    stages).  Kernel timers (names ending in the rank) and grouping stages
+    (stage_*) are nested inside the phases."""
+    phases = {k: round(v[0], 4) for k, v in per_step.items()
+              if not k[-1].isdigit() and not k.startswith("stage_")}
+    kern = {k: v[0] for k, v in per_step.items() if k[-1].isdigit()}
+    stages = {k[6:]: round(v[0], 4) for k, v in per_step.items() if k.startswith("stage_")}
+    return phases, kern, stages
+
+
 def kernel_sources_sha(files):
     h = hashlib.sha256()
     for f in files:
@@ -249,6 +260,45 @@ def cpu_baseline(w, target_s=12.0):
                       f"{kind}, per-index fp64, {t:.1f} s"}
 
 
+def run_sweep(args, torch, tt, W, opts):
+    """Batch sweep on the 26-table shapes (same tables, bag-length law and
+    index laws as the training workload, B bags per table): training step
+    (group + forward + backward + SGD) and forward-only (group + forward)
+    throughput, the grouping share of each, the workspace the library asks
+    for (upper bounds that do not depend on index values) and the peak device
+    memory of the step (inputs, cores, gradients, output and workspace)."""
+    rows = []
+    for B in [int(x) for x in args.batches.split(",") if x]:
+        w = W.make_workload(5, bags=B)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        b = Bench(w, torch, tt, opts)
+        ws_bytes = tt.tt_emb_workspace_size(b.emb.handle, w.B, w.nnz)
+        tms, _, tph = b.timed(b.train_step, args.steps, args.warmup)
+        fms, _, fph = b.timed(b.fwd, args.steps, args.warmup)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        tphase, _, tst = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in tph.items() if v[1]})
+        fphase, _, fst = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in fph.items() if v[1]})
+        tgroup = tphase.get("group_sort", 0) + tphase.get("group_rle", 0)
+        fgroup = fphase.get("group_sort", 0) + fphase.get("group_rle", 0)
+        row = {"batch": B, "nnz": w.nnz,
+               "train_ms": round(tms, 4), "train_lookups_per_s": w.nnz / (tms * 1e-3),
+               "fwd_ms": round(fms, 4), "fwd_lookups_per_s": w.nnz / (fms * 1e-3),
+               "grouping_share_train": round(tgroup / tms, 4), "grouping_share_fwd": round(fgroup / fms, 4),
+               "train_phases_ms": tphase, "fwd_phases_ms": fphase, "grouping_stages_ms": fst,
+               "workspace_bytes": ws_bytes, "peak_device_bytes": int(peak)}
+        rows.append(row)
+        print(f"[sweep] B={B} nnz={w.nnz} train {tms:.3f} ms fwd {fms:.3f} ms ws {ws_bytes / 2**30:.2f} GiB",
+              file=sys.stderr, flush=True)
+        del b
+        torch.cuda.empty_cache()
+    print(json.dumps({"mode": "sweep", "workload": "26 tables (the training workload's shapes), B bags per table",
+                      "data": "synthetic", "steps": args.steps, "warmup": args.warmup, "sweep": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,13 +308,16 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
     ap.add_argument("--sched", type=int, default=0, help="0 default, 1 static, 2 steal, 3 steal+L2")
     ap.add_argument("--group", type=int, default=0, help="0 default, 1 prefix, 2 unique-only")
-    ap.add_argument("--mode", default="train", choices=("train", "fwd", "copy", "traffic"),
+    ap.add_argument("--mode", default="train", choices=("train", "fwd", "copy", "traffic", "sweep"),
                     help="train: the full step (default); fwd: forward only on --config; "
                          "copy: a plain 1 GiB device copy (counter calibration); "
-                         "traffic: turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json")
+                         "traffic: turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json; "
+                         "sweep: training step and forward over --batches on the 26-table shapes")
     ap.add_argument("--pmc-dir", default="gpurun_out/m",
                     help="traffic: directory with the fetch/, write/, cfetch/, cwrite/ counter runs")
     ap.add_argument("--config", type=int, default=4, help="workload of --mode fwd (1..4)")
+    ap.add_argument("--batches", default="2048,4096,8192,16384,32768,65536,131072",
+                    help="sweep: bags per table, comma separated")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -301,15 +354,20 @@ def main():
         opts.sched_mode = args.sched
         opts.group_mode = args.group
 
+    if args.mode == "sweep":
+        run_sweep(args, torch, tt, W, opts)
+        return
+
     if args.mode == "fwd":
         wf = W.make_workload(args.config)
         bf = Bench(wf, torch, tt, opts)
         fms, _, fph = bf.timed(bf.fwd, args.steps, args.warmup)
         ur, up, nz, fc = bf.counts()
         ff, _, _ = phase_flops(wf.tables, ur, up, nz)
-        fphase = {k: round(v[0] / max(v[1], 1), 4) for k, v in fph.items() if v[1]}
+        fphase, fkern, fstages = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in fph.items() if v[1]})
         print(json.dumps({"mode": "fwd", "workload": W.CONFIG_NAMES[args.config], "ms": fms,
                           "lookups_per_s": wf.nnz / (fms * 1e-3), "phases_ms": fphase,
+                          "grouping_stages_ms": fstages, "kernels_ms": fkern,
                           "contract_flops": ff, "unique_rows": sum(ur), "prefix_groups": sum(up),
                           "sched_stats": fc}), flush=True)
         return
@@ -321,9 +379,8 @@ def main():
     F_fwd, F_bwd, F_pool = phase_flops(w.tables, U_r, U_p, nnz_t)
     value = w.nnz / (ms * 1e-3)
     per_step = {k: (v[0] / max(v[1], 1), v[1]) for k, v in ph.items() if v[1]}
-    phases = {k: round(v[0], 4) for k, v in per_step.items() if not k[-1].isdigit()}
-    # single-kernel timers (one HIP event pair per launch, on the library's stream)
-    kern_ms = {k: v[0] for k, v in per_step.items() if k[-1].isdigit()}
+    # single-kernel timers: one HIP event pair per launch, on the library's stream
+    phases, kern_ms, stages = split_timers(per_step)
     kern_ms["pool"] = per_step["pool"][0]  # the pooling phase is one kernel
     kflops = kernel_flops(w.tables, U_r, U_p)
     wl = W.CONFIG_NAMES[5]
@@ -353,6 +410,7 @@ def main():
                    "unique_rows": sum(U_r), "prefix_groups": sum(U_p), "sched": args.sched,
                    "group": args.group, "wall_s": wall},
         "phases_ms": phases,
+        "grouping_stages_ms": stages,
         "kernels": kernels,
         "flops": {"fwd_contract": F_fwd, "bwd_contract": F_bwd, "pool_adds": F_pool},
         "sched_stats": cnt,
@@ -369,13 +427,14 @@ def main():
             fms, _, fph = bf.timed(bf.fwd, args.steps, args.warmup)
             ur, up, nz, fc = bf.counts()
             ff, _, _ = phase_flops(wf.tables, ur, up, nz)
-            fphase = {k: round(v[0] / max(v[1], 1), 4) for k, v in fph.items() if v[1] and not k[-1].isdigit()}
+            fphase, _, fstages = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in fph.items() if v[1]})
             post = fphase.get("contract", 0) + fphase.get("pool", 0)
             cms = fphase.get("contract", 0)
             fwd[W.CONFIG_NAMES[cfg]] = {
                 "lookups_per_s": wf.nnz / (fms * 1e-3), "ms": fms,
                 "post_grouping_ms": post, "post_grouping_lookups_per_s": wf.nnz / (post * 1e-3) if post else None,
-                "phases_ms": fphase, "nnz": wf.nnz, "unique_rows": sum(ur), "prefix_groups": sum(up),
+                "phases_ms": fphase, "grouping_stages_ms": fstages, "nnz": wf.nnz, "unique_rows": sum(ur),
+                "prefix_groups": sum(up),
                 "contract_tflops": ff / (cms * 1e-3) / 1e12 if cms else None,
                 "contract_frac_fp32_peak": ff / (cms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS if cms else None,
                 "roofline_ms_fp32": ff / (PEAK_FP32_TFLOPS * 1e12) * 1e3,

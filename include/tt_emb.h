@@ -189,6 +189,12 @@ enum {
      * d3 <= 16); one interval per launch */
     TT_EMB_TIMER_FWD_R8, TT_EMB_TIMER_FWD_R16, TT_EMB_TIMER_FWD_R32, TT_EMB_TIMER_FWD_R64,
     TT_EMB_TIMER_BWD_R8, TT_EMB_TIMER_BWD_R16, TT_EMB_TIMER_BWD_R32, TT_EMB_TIMER_BWD_R64,
+    /* stages inside GROUP_SORT and GROUP_RLE (the grouping overhead the
+     * FlowTT page breaks down in section 4): validation and key build, the
+     * (table, row) sort, unique extraction, mixed-radix prefix extraction and
+     * run-length encoding, the (table, i2) unit order, and the work list */
+    TT_EMB_TIMER_STAGE_DECODE, TT_EMB_TIMER_STAGE_SORT, TT_EMB_TIMER_STAGE_UNIQUE,
+    TT_EMB_TIMER_STAGE_PREFIX, TT_EMB_TIMER_STAGE_ORDER, TT_EMB_TIMER_STAGE_WORKLIST,
     TT_EMB_NUM_TIMERS
 };
 

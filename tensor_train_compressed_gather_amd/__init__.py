@@ -35,7 +35,8 @@ EXPORTED = (
 )
 TIMER_NAMES = ("group_sort", "group_rle", "contract", "pool", "bwd_gather", "bwd_contract",
                "bwd_reduce", "sgd", "fwd_r8", "fwd_r16", "fwd_r32", "fwd_r64",
-               "bwd_r8", "bwd_r16", "bwd_r32", "bwd_r64")
+               "bwd_r8", "bwd_r16", "bwd_r32", "bwd_r64",
+               "stage_decode", "stage_sort", "stage_unique", "stage_prefix", "stage_order", "stage_worklist")
 
 
 class tt_emb_options(C.Structure):

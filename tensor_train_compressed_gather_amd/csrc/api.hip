@@ -128,8 +128,8 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.crec = (ChunkRec *)take(sizeof(ChunkRec) * chunks);
     w.chunk_cap = chunks;
     w.g3t = (float *)take(4 * (size_t)h->g3t_elems);
-    // 4 classes x up to 4 blocks per CU, one 128-byte line each
-    w.heads = (int32_t *)take(4 * (size_t)h->num_blocks * 16 * 32);
+    // 4 classes x up to 8 blocks per CU, one 128-byte line each
+    w.heads = (int32_t *)take(4 * (size_t)h->num_blocks * 4 * 8 * 32);
     w.flags = (int32_t *)take(4 * (size_t)kMaxCkptSlots);
     w.ckpt = (float *)take(4 * (size_t)kMaxCkptSlots * (4 * (16 * 68 + 16)));
     // bounds on unique rows / units per table that do not depend on values
@@ -148,6 +148,7 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     const int64_t tasks = n / kGuTask + T + 1;
     const int64_t part_elems = tasks * 2 * h->Dpmax;
     w.E = (float *)take(4 * e_elems);
+    w.sink = (float *)take(4 * (size_t)kSinkFloats);
     w.lk = (int2 *)take(8 * n);
     w.gu_ml = (int32_t *)take(4 * tasks);
     w.gu_mr = (int32_t *)take(4 * tasks);
@@ -562,7 +563,10 @@ const char *tt_emb_timer_name(int32_t id)
     static const char *names[TM_COUNT] = {"group_sort", "group_rle", "contract", "pool",
                                           "bwd_gather", "bwd_contract", "bwd_reduce", "sgd",
                                           "fwd_r8", "fwd_r16", "fwd_r32", "fwd_r64",
-                                          "bwd_r8", "bwd_r16", "bwd_r32", "bwd_r64"};
+                                          "bwd_r8", "bwd_r16", "bwd_r32", "bwd_r64",
+                                          "stage_decode", "stage_sort", "stage_unique", "stage_prefix",
+                                          "stage_order", "stage_worklist"};
+    static_assert(TM_COUNT == TT_EMB_NUM_TIMERS, "one name per timer");
     return (id >= 0 && id < TM_COUNT) ? names[id] : nullptr;
 }
 

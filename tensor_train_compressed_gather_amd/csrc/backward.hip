@@ -618,14 +618,14 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
         __syncthreads();
         // wave-uniform: the table data below become scalar loads
         const int t = __builtin_amdgcn_readfirstlane(recs[0].t), i2 = __builtin_amdgcn_readfirstlane(recs[0].i2);
-        const TableDesc &tb = a.tab[t];
+        const auto &tb = kconst(a.tab)[t];
         const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, D12 = d1 * d2, Dp = tb.Dp, P = 16 / d3;
         const float *G1 = a.cores.g[t][0];
         const float *G3t = ws.g3t + tb.g3t_off;
         // per-table bases read once per run: a global load issued after this
         // run's stores would wait for all of them (stores and loads share one counter)
-        const float *Et = ws.E + ws.ebase[t];
-        float *P3t = ws.P3 + ws.p3base[t];
+        const float *Et = ws.E + kconst(ws.ebase)[t];
+        float *P3t = ws.P3 + kconst(ws.p3base)[t];
         // staged rows: g_u at stride Dp + 4, G3 slices as [j3][R + 16] (bank-spread)
         const int GST = Dp + 4, G3J = R + 16, G3ST = d3 * G3J;
         int rb = L::STAGE / (GST + G3ST);

@@ -25,11 +25,25 @@
 namespace ttemb {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) float lds_float;
 
-constexpr int kCStride = 68;                   // LDS row stride of a prefix tile (R2 <= 64)
-constexpr int kCUnit = 16 * kCStride + 16;     // floats per unit (extra 16 rotates banks)
-constexpr int kCTile = kUnitsPerTile * kCUnit; // floats per prefix tile
-constexpr int kEsFloats = 32 * 68;              // E rows staged per chunk (32 rows of D <= 64)
+constexpr int kCTile = kUnitsPerTile * (16 * 68 + 16); // floats per checkpoint slot (R2 <= 64)
+
+// Per-rank layout of a class kernel: LDS row stride of the prefix tile
+// (R + 4), floats per unit (an extra 16 rotates banks between units), E rows
+// staged per chunk, and blocks per CU (measured: six rank-16 blocks per CU
+// ran slower than four, the chunk loop being bound by instruction issue).
+template <int R>
+struct FwdCfg {
+    static constexpr int CSTR = R + 4;
+    static constexpr int CUNIT = 16 * CSTR + 16;
+    static constexpr int CTILE = kUnitsPerTile * CUNIT;
+    static constexpr int ES = R <= 16 ? 32 * 68 : 32 * 132; // 32 rows of D <= 64, or <= 128
+    static constexpr int OCC = R <= 16 ? 4 : R == 32 ? 3 : 2;
+    static constexpr int BREG = ((R / 4 + 3) / 4) * (R / 4); // G2 slice registers per lane
+};
+static_assert(FwdCfg<64>::CTILE == kCTile, "checkpoint slot holds the largest prefix tile");
+constexpr int kMaxClsOcc = 8; // queue heads per CU reserved for each class
 constexpr int kSchedStatic = 1, kSchedSteal = 2, kSchedStealL2 = 3;
 
 struct FwdArgs {
@@ -58,7 +72,7 @@ __device__ __forceinline__ int range_begin(int v, int64_t C, int nb) { return (i
 constexpr int kHeadPad = 32;
 
 // Blocks per CU of each rank class's persistent kernel (register-limited).
-constexpr int kClsOcc[4] = {4, 4, 3, 2};
+constexpr int kClsOcc[4] = {FwdCfg<8>::OCC, FwdCfg<16>::OCC, FwdCfg<32>::OCC, FwdCfg<64>::OCC};
 struct ClassGrid {
     int nb[4];
 };
@@ -129,15 +143,21 @@ __device__ int claim_finish(int32_t *heads, int base, int me, int &vi, int nb, i
                             int &steals)
 {
     const int lane = threadIdx.x & 63;
+    int res;
     for (;;) {
-        if (vi >= nvict) return -1;
-        const int v = victim_of(me, vi, nb);
+        const bool live = vi < nvict;
+        const int v = victim_of(me, live ? vi : 0, nb);
         int got = -1;
-        if (lane == 0 && raw < base + range_begin(v + 1, C, nb)) got = raw;
-        got = __shfl(got, 0, 64);
+        if ((lane == 0) & live & (raw < base + range_begin(v + 1, C, nb))) got = raw;
+        got = uni(got); // lane 0's value (every lane of the wave is active here)
         if (got >= 0) {
             steals += vi != 0;
-            return got;
+            res = got;
+            break;
+        }
+        if (!live) {
+            res = -1;
+            break;
         }
         const int cand = vi + 1 + lane;
         bool avail = false;
@@ -148,154 +168,209 @@ __device__ int claim_finish(int32_t *heads, int base, int me, int &vi, int nb, i
         }
         const uint64_t m = __ballot(avail);
         vi = m ? vi + 1 + (__ffsll((unsigned long long)m) - 1) : vi + 65;
-        raw = claim_start(heads, me, vi, nb, nvict);
+        if (vi >= nvict) {
+            res = -1;
+            break;
+        }
+        // a retry (a drained victim, rare) waits for its claim right here, so
+        // no claim is ever left in flight past this function: a register that
+        // a load may still target makes later writes to it wait for every
+        // load and store the wave has in flight
+        raw = uni(claim_start(heads, me, vi, nb, nvict));
     }
+    return res;
 }
 
-// One chunk of a tile on the matrix cores, R1 = R2 = R.
-// A operand of the next chunk's prefix tile (its G1 slices), issued before the
-// current chunk's E stores: on gfx9 loads and stores share one in-order
-// counter, so a load issued after the stores would also wait for them.
-__device__ __forceinline__ void prefetch_a(const FwdArgs &a, const ChunkRec &nr, float (&apf)[16], int &apf_tile)
+// Output tile e of a chunk (16/d3 rows of one unit, P rows per tile) -> unit
+// j, first row in chunk numbering and row count.
+__device__ __forceinline__ void chunk_piece(const ChunkRec &r, int P, int e, int &j, int &rb, int &cnt)
 {
-    apf_tile = -1;
-    // record fields are wave-uniform: scalar loads of the table data then stay
-    // off the vector memory counter
-    const int cls = __builtin_amdgcn_readfirstlane(nr.cls), t = __builtin_amdgcn_readfirstlane(nr.t);
-    if (cls < 0) return;
-    const int R = 8 << cls, KQ = R >> 2;
-    const TableDesc &tb = a.tab[t];
-    const int d1 = tb.d1;
+    j = 0;
+    while (j < 3 && e >= r.pstart[j + 1]) ++j;
+    rb = r.rowoff[j] + (e - r.pstart[j]) * P;
+    const int rem = r.rowoff[j] + r.ccnt[j] - rb;
+    cnt = rem < P ? rem : P;
+}
+
+// Pieces of a chunk whose B operands a wave keeps in registers from one chunk
+// to the next: they are loaded while the previous chunk finishes.
+template <int R> constexpr int fwd_nq() { return R <= 32 ? 3 : 2; }
+
+// B operand of output tile e of chunk r: G3t[i3][j3][kq*KQ .. kq*KQ+KQ-1] of
+// the lane's row.  Lanes past the tile's rows read its first row; their
+// outputs are never stored (and never zeroed: see load_a).
+template <int R>
+__device__ __forceinline__ void load_b_piece(const FwdArgs &a, const ChunkRec &r, int e, float (&b)[R / 4])
+{
+    constexpr int KQ = R / 4;
+    const int t = __builtin_amdgcn_readfirstlane(r.t);
+    const auto &tb = kconst(a.tab)[t];
+    const int d3 = tb.d3;
     const int lane = threadIdx.x & 63, li = lane & 15, kq = lane >> 4;
-    const int g = li >> 2, j1 = li & 3;
-    // out-of-range lanes read the first unit's slice (always valid) and are
-    // zeroed when used: zeroing a register a load may still target would make
-    // the wave wait for all of its outstanding stores
-    const bool ok = g < nr.nu && j1 < d1;
-    const float *src = a.cores.g[t][0] + ((int64_t)(ok ? nr.i1[g] : nr.i1[0]) * d1 + (ok ? j1 : 0)) * R + kq * KQ;
-    if (KQ >= 4) {
+    const int slot = li / d3, j3 = li - slot * d3;
+    int j, rb, cnt;
+    chunk_piece(r, 16 / d3, e, j, rb, cnt);
+    const bool ok = slot < cnt;
+    const float *src = a.ws.g3t + tb.g3t_off + ((int64_t)r.i3[rb + (ok ? slot : 0)] * d3 + j3) * R + kq * KQ;
+    if constexpr (KQ % 4 == 0) {
 #pragma unroll
-        for (int s = 0; s < 16; s += 4) {
-            const floatx4 v = *reinterpret_cast<const floatx4 *>(src + (s < KQ ? s : 0));
-            apf[s] = v[0];
-            apf[s + 1] = v[1];
-            apf[s + 2] = v[2];
-            apf[s + 3] = v[3];
+        for (int s = 0; s < KQ; s += 4) {
+            const floatx4 v = *reinterpret_cast<const floatx4 *>(src + s);
+            b[s] = v[0];
+            b[s + 1] = v[1];
+            b[s + 2] = v[2];
+            b[s + 3] = v[3];
         }
     } else {
 #pragma unroll
-        for (int s = 0; s < 16; ++s) apf[s] = src[s < KQ ? s : 0];
+        for (int s = 0; s < KQ; ++s) b[s] = src[s];
     }
-    apf_tile = nr.tile;
 }
 
-template <int R, class Mid>
+// A operand of a chunk's prefix tile: the G1[i1] slices of its units, lane
+// (kq, li) holding row 4*unit + j1 = li, K values kq*KQ .. kq*KQ+KQ-1.  Lanes
+// outside the tile read the first unit's slice (always valid) and are masked
+// where the operand is used: zeroing a register that a load may still target
+// would make the wave wait for every load and store it has in flight.
+template <int R>
+__device__ __forceinline__ void load_a(const FwdArgs &a, const ChunkRec &r, float (&av)[R / 4])
+{
+    constexpr int KQ = R / 4;
+    const int t = __builtin_amdgcn_readfirstlane(r.t);
+    const auto &tb = kconst(a.tab)[t];
+    const int d1 = tb.d1;
+    const int lane = threadIdx.x & 63, li = lane & 15, kq = lane >> 4;
+    const int g = li >> 2, j1 = li & 3;
+    const bool ok = g < r.nu && j1 < d1;
+    const float *src = a.cores.g[t][0] + ((int64_t)(ok ? r.i1[g] : r.i1[0]) * d1 + (ok ? j1 : 0)) * R + kq * KQ;
+    if constexpr (KQ % 4 == 0) {
+#pragma unroll
+        for (int s = 0; s < KQ; s += 4) {
+            const floatx4 v = *reinterpret_cast<const floatx4 *>(src + s);
+            av[s] = v[0];
+            av[s + 1] = v[1];
+            av[s + 2] = v[2];
+            av[s + 3] = v[3];
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < KQ; ++s) av[s] = src[s];
+    }
+}
+
+// Every operand a chunk loads from memory except its G2 slice: the A operand
+// and the B operands of the wave's first NQ output tiles.  Issued while the
+// previous chunk finishes, before its E stores.
+template <int R>
+__device__ __forceinline__ void load_operands(const FwdArgs &a, const ChunkRec &r, float (&av)[R / 4],
+                                              float (&bq)[fwd_nq<R>()][R / 4])
+{
+    load_a<R>(a, r, av);
+    const int w = uni(threadIdx.x >> 6);
+    const int np = r.pstart[r.nu];
+#pragma unroll
+    for (int k = 0; k < fwd_nq<R>(); ++k) load_b_piece<R>(a, r, w + 4 * k < np ? w + 4 * k : (np > 0 ? np - 1 : 0), bq[k]);
+}
+
+// E rows of a chunk staged in LDS are written out with this many float4
+// stores per thread, always the same number (the last element is written
+// again by the threads past the end, with the same value).  A fixed count of
+// stores lets the next chunk wait for its operands, loaded before these
+// stores, without waiting for the stores.
+constexpr int kFlushPerThread = 4; // 32 rows of D <= 128
+static_assert(kFlushPerThread * kThreads * 4 <= kSinkFloats, "scratch line holds one flush");
+
+// One chunk of a tile on the matrix cores, R1 = R2 = R.  On entry the chunk's
+// A operand (apf) and first B operands (bq) are loaded or in flight; on exit
+// those of the next chunk are.
+template <int R, class Mid, class End>
 __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec, float *Cs, float *Es,
-                                           float (&breg)[64], int &bkey, int &lds_tile, int *s_flag,
-                                           float (&apf)[16], int &apf_tile, ChunkRec *rnext, bool has_next,
-                                           int pre, int &hits, int &misses, int c, int cn, Mid &&mid)
+                                           float (&breg)[FwdCfg<R>::BREG], int &bkey, int &lds_tile, int *s_flag,
+                                           float (&apf)[R / 4], float (&bq)[fwd_nq<R>()][R / 4], ChunkRec *rnext,
+                                           bool has_next, int pre, int &hits, int &misses, int c, int cn,
+                                           Mid &&mid, End &&endc)
 {
     constexpr int KQ = R / 4;           // K values each lane feeds per output tile
     constexpr int NT = R / 4;           // 16-column tiles of the padded d2*R2 (d2 <= 4)
     constexpr int NTW = (NT + 3) / 4;   // per wave
+    constexpr int NQ = fwd_nq<R>();     // output tiles per wave with B operands loaded ahead
+    using L = FwdCfg<R>;
     // wave-uniform table index: the table data below become scalar loads,
     // which do not wait behind this wave's outstanding vector loads and stores
     const int t = __builtin_amdgcn_readfirstlane(rec.t);
-    const TableDesc &tb = a.tab[t];
+    const auto &tb = kconst(a.tab)[t];
     const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, D12 = d1 * d2, Dp = tb.Dp;
-    float *Et = a.ws.E + a.ws.ebase[t];
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, kq = lane >> 4;
-    const float *G1 = a.cores.g[t][0];
+    float *Et = a.ws.E + kconst(a.ws.ebase)[t];
+    const int w = uni(threadIdx.x >> 6), lane = threadIdx.x & 63, li = lane & 15, kq = lane >> 4;
     const float *G2 = a.cores.g[t][1];
-    const float *G3t = a.ws.g3t + tb.g3t_off;
     const int P = 16 / d3;
-    const int np = rec.pstart[rec.nu];
+    // record fields that steer control flow, made wave-uniform: a branch on a
+    // value the compiler takes as per-lane runs both sides under exec masks,
+    // and the waits of one side then apply to the other
+    const int tile = uni(rec.tile), nu = uni(rec.nu), i2 = uni(rec.i2), cslot = uni(rec.slot);
+    const int rbeg = uni(rec.rbeg), nch = uni(rec.nch);
+    const int np = uni(rec.pstart[nu]);
     const int slot = li / d3, j3 = li - slot * d3;
 
-    // output tile e -> unit j, first row (chunk numbering) and row count
-    auto piece = [&](int e, int &j, int &rb, int &cnt) {
-        j = 0;
-        while (j < 3 && e >= rec.pstart[j + 1]) ++j;
-        rb = rec.rowoff[j] + (e - rec.pstart[j]) * P;
-        const int rem = rec.rowoff[j] + rec.ccnt[j] - rb;
-        cnt = rem < P ? rem : P;
-    };
-    // B operand of an output tile: G3t[i3][j3][kq*KQ .. kq*KQ+KQ-1] of the lane's row
-    auto load_b = [&](int e, float (&b)[KQ]) {
-        int j, rb, cnt;
-        piece(e, j, rb, cnt);
-        // lanes past the tile's rows read the tile's first row; their outputs
-        // are never stored (no zeroing: see prefetch_a)
-        const bool ok = slot < cnt;
-        const float *src = G3t + ((int64_t)rec.i3[rb + (ok ? slot : 0)] * d3 + j3) * R + kq * KQ;
-        if constexpr (KQ % 4 == 0) {
-#pragma unroll
-            for (int s = 0; s < KQ; s += 4) {
-                const floatx4 v = *reinterpret_cast<const floatx4 *>(src + s);
-                b[s] = v[0];
-                b[s + 1] = v[1];
-                b[s + 2] = v[2];
-                b[s + 3] = v[3];
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < KQ; ++s) b[s] = src[s];
-        }
-    };
-    float bnext[KQ];
-    if (w < np) load_b(w, bnext); // in flight while the prefix tile is computed
-
     // -------- prefix tile C_u = G1[i1_u] . G2[i2] for the (<= 4) units
-    if (lds_tile != rec.tile) {
+    if (uni(lds_tile) != tile) {
         bool have = false;
-        const bool split = rec.slot >= 0 && a.sched == kSchedStealL2;
-        if (split && rec.rbeg > 0) {
+        const bool split = cslot >= 0 && a.sched == kSchedStealL2;
+        if (split && rbeg > 0) {
             if (threadIdx.x == 0)
-                *s_flag = __hip_atomic_load(&a.ws.flags[rec.slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+                *s_flag = __hip_atomic_load(&a.ws.flags[cslot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
-            if (*s_flag) {
+            if (uni(*s_flag)) {
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                const float4 *src = reinterpret_cast<const float4 *>(a.ws.ckpt + (size_t)rec.slot * kCTile);
+                const float4 *src = reinterpret_cast<const float4 *>(a.ws.ckpt + (size_t)cslot * kCTile);
                 float4 *dst = reinterpret_cast<float4 *>(Cs);
-                for (int i = threadIdx.x; i < kCTile / 4; i += kThreads) dst[i] = src[i];
+                for (int i = threadIdx.x; i < L::CTILE / 4; i += kThreads) dst[i] = src[i];
                 have = true;
             }
             if (have) ++hits;
             else ++misses;
         }
         if (!have) {
-            const int g = li >> 2, j1 = li & 3;
-            const bool oka = g < rec.nu && j1 < d1;
-            const float *srcA = G1 + ((int64_t)(oka ? rec.i1[g] : rec.i1[0]) * d1 + (oka ? j1 : 0)) * R + kq * KQ;
-            float areg[KQ];
-            if (apf_tile == rec.tile) {
+            auto step1 = [&]() {
+                floatx4 acc[NTW];
 #pragma unroll
-                for (int s = 0; s < KQ; ++s) areg[s] = apf[s];
-            } else if constexpr (KQ % 4 == 0) {
+                for (int j = 0; j < NTW; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < KQ; s += 4) {
-                    const floatx4 v = *reinterpret_cast<const floatx4 *>(srcA + s);
-                    areg[s] = v[0];
-                    areg[s + 1] = v[1];
-                    areg[s + 2] = v[2];
-                    areg[s + 3] = v[3];
+                for (int s = 0; s < KQ; ++s) {
+                    // rows of absent units / j1 hold the first unit's slice: C
+                    // rows are independent and theirs are never stored
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j)
+                        if (NT % 4 == 0 || w + 4 * j < NT) // folded when every wave has NTW tiles
+                            acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(apf[s], breg[j * KQ + s], acc[j], 0, 0, 0);
                 }
+                // lane (kq, li) holds rows 4*kq + v = (unit kq, j1 = v), column ntg*16 + li
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    const int ntg = w + 4 * j;
+                    if (NT % 4 == 0 || ntg < NT) {
+                        const int col = ntg * 16 + li;
+                        const int j2 = col / R, r2 = col % R;
+                        if (j2 < d2 && kq < nu) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                if (v < d1) Cs[kq * L::CUNIT + (v * d2 + j2) * L::CSTR + r2] = acc[j][v];
+                        }
+                    }
+                }
+            };
+            const int key = (int)(tb.i2_base + (uint32_t)i2);
+            if (uni(bkey) == key) {
+                step1(); // every operand was loaded before the previous chunk's stores
             } else {
-#pragma unroll
-                for (int s = 0; s < KQ; ++s) areg[s] = srcA[s];
-            }
-            // rows of absent units / j1 contribute zeros to C (their C rows are never read)
-#pragma unroll
-            for (int s = 0; s < KQ; ++s) areg[s] = oka ? areg[s] : 0.f;
-            const int key = (int)(tb.i2_base + (uint32_t)rec.i2);
-            if (bkey != key) {
+                // a new G2 slice: this copy of the tile waits for its loads
 #pragma unroll
                 for (int j = 0; j < NTW; ++j) {
                     const int ntg = w + 4 * j;
                     const int col = ntg * 16 + li;
                     const int j2 = col / R, r2 = col % R;
                     const bool ok = ntg < NT && j2 < d2;
-                    const float *src = G2 + ((int64_t)rec.i2 * R * d2 + (ok ? j2 : 0)) * R + r2;
+                    const float *src = G2 + ((int64_t)i2 * R * d2 + (ok ? j2 : 0)) * R + r2;
 #pragma unroll
                     for (int s = 0; s < KQ; ++s) {
                         const int k = kq * KQ + s;
@@ -303,69 +378,40 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
                     }
                 }
                 bkey = key;
-            }
-            floatx4 acc[NTW];
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KQ; ++s) {
-#pragma unroll
-                for (int j = 0; j < NTW; ++j)
-                    if (NT % 4 == 0 || w + 4 * j < NT) // folded when every wave has NTW tiles
-                        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(areg[s], breg[j * KQ + s], acc[j], 0, 0, 0);
-            }
-            // lane (kq, li) holds rows 4*kq + v = (unit kq, j1 = v), column ntg*16 + li
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const int ntg = w + 4 * j;
-                if (NT % 4 == 0 || ntg < NT) {
-                    const int col = ntg * 16 + li;
-                    const int j2 = col / R, r2 = col % R;
-                    if (j2 < d2 && kq < rec.nu) {
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            if (v < d1) Cs[kq * kCUnit + (v * d2 + j2) * kCStride + r2] = acc[j][v];
-                    }
-                }
+                step1();
             }
             __syncthreads();
             // publish only when another block may run a later chunk of this tile:
             // this block already holds the next claimed chunk, so a two-chunk
             // tile whose second chunk is that one never needs the checkpoint
             // (an agent-scope release writes back L2, which is not free)
-            if (split && rec.rbeg == 0 && (rec.nch > 2 || cn != c + 1)) {
-                float4 *dst = reinterpret_cast<float4 *>(a.ws.ckpt + (size_t)rec.slot * kCTile);
+            if (split && rbeg == 0 && (nch > 2 || cn != c + 1)) {
+                float4 *dst = reinterpret_cast<float4 *>(a.ws.ckpt + (size_t)cslot * kCTile);
                 const float4 *src = reinterpret_cast<const float4 *>(Cs);
-                for (int i = threadIdx.x; i < kCTile / 4; i += kThreads) dst[i] = src[i];
+                for (int i = threadIdx.x; i < L::CTILE / 4; i += kThreads) dst[i] = src[i];
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
                 __syncthreads();
                 if (threadIdx.x == 0)
-                    __hip_atomic_store(&a.ws.flags[rec.slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&a.ws.flags[cslot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        lds_tile = rec.tile;
+        lds_tile = tile;
     }
     __syncthreads();
-    // the next chunk's record (its load was issued when this chunk started)
+    // the next chunk's record (loaded while the previous chunk finished)
     if (has_next && w == 0) reinterpret_cast<int *>(rnext)[lane] = pre;
     __syncthreads();
-    if (has_next && rnext->tile != rec.tile) prefetch_a(a, *rnext, apf, apf_tile);
+    mid();
 
     // -------- unique rows E_u = C_unit . G3[i3_u], 16/d3 rows per output tile,
-    // staged in LDS (Es, row stride Dp + 4) and stored coalesced once every
-    // load of the chunk has been waited for
-    mid();
-    const int EST = Dp + 4;
-    const bool staged = rec.rowoff[4] * EST <= kEsFloats; // else rows go straight to E
+    // staged in LDS (Es, row stride Dp + 4) and written out at the chunk's end
+    const int EST = Dp + 4, nrows = uni(rec.rowoff[4]), c4 = Dp >> 2;
+    const bool staged = nrows >= 1 && nrows * EST <= L::ES && nrows * c4 <= kFlushPerThread * kThreads;
     const bool okm = li < D12;
-    for (int e = w; e < np; e += 4) {
-        float bcur[KQ];
-#pragma unroll
-        for (int s = 0; s < KQ; ++s) bcur[s] = bnext[s];
-        if (e + 4 < np) load_b(e + 4, bnext);
+    auto piece_mfma = [&](int e, const float (&bcur)[KQ]) {
         int j, rb, cnt;
-        piece(e, j, rb, cnt);
-        const float *ca = Cs + j * kCUnit + (okm ? li : 0) * kCStride + kq * KQ;
+        chunk_piece(rec, P, e, j, rb, cnt);
+        const float *ca = Cs + j * L::CUNIT + (okm ? li : 0) * L::CSTR + kq * KQ;
         floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
         if constexpr (KQ % 4 == 0) {
 #pragma unroll
@@ -381,86 +427,135 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
             for (int s = 0; s < KQ; ++s)
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(okm ? ca[s] : 0.f, bcur[s], acc, 0, 0, 0);
         }
-        if (slot < cnt) {
-            float *Erow = staged ? Es + (rb + slot) * EST
-                                 : Et + (int64_t)(rec.ustart[j] + (rb - rec.rowoff[j]) + slot) * Dp;
+        // two separate stores (LDS or global): a pointer that may be either
+        // would be a flat store, counted by both the LDS and the memory counter
+        if (slot < cnt && staged) {
+            lds_float *Erow = (lds_float *)(Es + (rb + slot) * EST);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m2 = kq * 4 + v;
+                if (m2 < D12) Erow[m2 * d3 + j3] = acc[v];
+            }
+        } else if (slot < cnt) {
+            float *Erow = Et + (int64_t)(rec.ustart[j] + (rb - rec.rowoff[j]) + slot) * Dp;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int m2 = kq * 4 + v;
                 if (m2 < D12) Erow[m2 * d3 + j3] = acc[v];
             }
         }
+    };
+#pragma unroll
+    for (int k = 0; k < NQ; ++k)
+        if (w + 4 * k < np) piece_mfma(w + 4 * k, bq[k]);
+    // later tiles (chunks of more than 4*NQ output tiles, d3 >= 8): loaded
+    // and used in turn, so no load is left in flight past the loop (a
+    // register that may still be a load's target makes any later write to it
+    // wait for every outstanding load and store)
+    for (int e = w + 4 * NQ; e < np; e += 4) {
+        float bcur[KQ];
+        load_b_piece<R>(a, rec, e, bcur);
+        piece_mfma(e, bcur);
     }
-    if (staged) {
-        __syncthreads();
-        const int nrows = rec.rowoff[4], c4 = Dp >> 2;
-        for (int e = threadIdx.x; e < nrows * c4; e += kThreads) {
-            const int q = e / c4, r4 = e - q * c4;
-            const int j = (q >= rec.rowoff[1]) + (q >= rec.rowoff[2]) + (q >= rec.rowoff[3]);
+
+    // -------- end of the chunk: the next chunk's record, claim and operands
+    // (the last chunk reloads its own, so every chunk issues the same
+    // loads), then this chunk's E rows
+    endc();
+    load_operands<R>(a, has_next ? *rnext : rec, apf, bq);
+    if (staged) __syncthreads();
+    {
+        const int tot = nrows * c4;
+        const int r1 = rec.rowoff[1], r2 = rec.rowoff[2], r3 = rec.rowoff[3];
+#pragma unroll
+        for (int k = 0; k < kFlushPerThread; ++k) {
+            int e = threadIdx.x + k * kThreads;
+            e = e < tot ? e : tot - 1;
+            e = e > 0 ? e : 0;
+            const int q = e / (c4 > 0 ? c4 : 1), r4 = e - q * c4;
+            const int j = (q >= r1) + (q >= r2) + (q >= r3);
             const int u = rec.ustart[j] + (q - rec.rowoff[j]);
-            reinterpret_cast<floatx4 *>(Et + (int64_t)u * Dp)[r4] = *reinterpret_cast<const floatx4 *>(Es + q * EST + 4 * r4);
+            // chunks not staged (wide rows) store into a scratch line instead
+            floatx4 *dst = staged ? reinterpret_cast<floatx4 *>(Et + (int64_t)u * Dp) + r4
+                                  : reinterpret_cast<floatx4 *>(a.ws.sink) + threadIdx.x + k * kThreads;
+            *dst = *reinterpret_cast<const floatx4 *>(Es + (staged ? q * EST + 4 * r4 : 0));
         }
     }
 }
 
 template <int R>
-__global__ __launch_bounds__(kThreads, 2) void k_contract(FwdArgs a, int heads_stride)
+__global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a, int heads_stride)
 {
     constexpr int CLS = R == 8 ? 0 : R == 16 ? 1 : R == 32 ? 2 : 3;
-    __shared__ __attribute__((aligned(16))) float Cs[kCTile];
-    __shared__ __attribute__((aligned(16))) float Es[kEsFloats];
+    __shared__ __attribute__((aligned(16))) float Cs[FwdCfg<R>::CTILE];
+    __shared__ __attribute__((aligned(16))) float Es[FwdCfg<R>::ES];
     __shared__ ChunkRec rbuf[2];
     __shared__ int s_cur, s_next, s_next2, s_flag;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = uni(threadIdx.x >> 6); // wave index, in a scalar register
     const int nb = gridDim.x, me = blockIdx.x;
     const Ws &ws = a.ws;
     const int base = ws.ctrl[CTRL_CLS_START + CLS];
     const int64_t C = ws.ctrl[CTRL_CLS_START + CLS + 1] - base;
     int32_t *heads = ws.heads + CLS * heads_stride * kHeadPad;
     const int nvict = a.sched == kSchedStatic ? 1 : nb;
-    float breg[64], apf[16];
+    float breg[FwdCfg<R>::BREG], apf[R / 4], bq[fwd_nq<R>()][R / 4];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) breg[i] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) apf[i] = 0.f;
-    int bkey = -1, lds_tile = -1, vi = 0, apf_tile = -1, steals = 0, hits = 0, misses = 0;
+    for (int i = 0; i < FwdCfg<R>::BREG; ++i) breg[i] = 0.f;
+    int bkey = -1, lds_tile = -1, vi = 0, steals = 0, hits = 0, misses = 0;
+    // wave 0 runs the claims two chunks ahead: chunk c+2 is claimed while
+    // chunk c runs, and the record of chunk c+1 is loaded at the end of chunk c-1
+    int pre = 0, raw = 0x7fffffff, c2w = -1;
     if (w == 0) {
         const int c0 = claim_finish(heads, base, me, vi, nb, nvict, C, claim_start(heads, me, vi, nb, nvict), steals);
         const int c1 = c0 < 0 ? -1
                               : claim_finish(heads, base, me, vi, nb, nvict, C, claim_start(heads, me, vi, nb, nvict), steals);
         if (c0 >= 0) reinterpret_cast<int *>(&rbuf[0])[lane] = reinterpret_cast<const int *>(&ws.crec[c0])[lane];
+        if (c1 >= 0) {
+            pre = reinterpret_cast<const int *>(&ws.crec[c1])[lane];
+            raw = claim_start(heads, me, vi, nb, nvict);
+        }
         if (lane == 0) {
             s_cur = c0;
             s_next = c1;
         }
     }
     __syncthreads();
-    int buf = 0;
-    for (;;) {
-        const int c = s_cur, cn = s_next;
-        if (c < 0) break;
-        int pre = 0, raw = 0x7fffffff;
-        if (w == 0 && cn >= 0) {
-            pre = reinterpret_cast<const int *>(&ws.crec[cn])[lane];
-            raw = claim_start(heads, me, vi, nb, nvict);
-        }
-        // the claim of chunk c+2 completes before this chunk's stores are issued
-        // (a wait on the atomic issued after them would also wait for them)
-        auto mid = [&]() {
-            if (w == 0) {
-                const int c2 = cn < 0 ? -1 : claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals);
-                if (lane == 0) s_next2 = c2;
+    // the first chunk's operands, then as many stores as every chunk's end
+    // issues (the loop is entered only from here, so the compiler's count of
+    // loads and stores in flight is the same on every path into it)
+    if (uni(s_cur) >= 0) {
+        load_operands<R>(a, rbuf[0], apf, bq);
+#pragma unroll
+        for (int k = 0; k < kFlushPerThread; ++k)
+            reinterpret_cast<floatx4 *>(ws.sink)[threadIdx.x + k * kThreads] = floatx4{0.f, 0.f, 0.f, 0.f};
+        int buf = 0;
+        for (;;) {
+            const int c = uni(s_cur), cn = uni(s_next);
+            if (c < 0) break;
+            // claim of chunk c+2 (started at the end of chunk c-1)
+            auto mid = [&]() {
+                if (w == 0) {
+                    c2w = cn < 0 ? -1 : claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals);
+                    if (lane == 0) s_next2 = c2w;
+                }
+            };
+            // record of chunk c+2 and the claim of chunk c+3
+            auto endc = [&]() {
+                if (w == 0 && c2w >= 0) {
+                    pre = reinterpret_cast<const int *>(&ws.crec[c2w])[lane];
+                    raw = claim_start(heads, me, vi, nb, nvict);
+                }
+            };
+            chunk_mfma<R>(a, rbuf[buf], Cs, Es, breg, bkey, lds_tile, &s_flag, apf, bq, &rbuf[buf ^ 1], cn >= 0,
+                          pre, hits, misses, c, cn, mid, endc);
+            __syncthreads(); // everyone is done with rbuf[buf], s_cur and s_next
+            if (threadIdx.x == 0) {
+                s_cur = cn;
+                s_next = s_next2;
             }
-        };
-        chunk_mfma<R>(a, rbuf[buf], Cs, Es, breg, bkey, lds_tile, &s_flag, apf, apf_tile, &rbuf[buf ^ 1], cn >= 0,
-                      pre, hits, misses, c, cn, mid);
-        __syncthreads(); // everyone is done with rbuf[buf], s_cur and s_next
-        if (threadIdx.x == 0) {
-            s_cur = cn;
-            s_next = s_next2;
+            __syncthreads();
+            buf ^= 1;
         }
-        __syncthreads();
-        buf ^= 1;
     }
     // scheduling statistics, one atomic per block
     if (threadIdx.x == 0) {
@@ -599,7 +694,7 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
     if (p.nnz > 0) {
         ClassGrid cg;
         for (int c = 0; c < 4; ++c) cg.nb[c] = p.num_blocks * kClsOcc[c];
-        const int hs = p.num_blocks * 4;
+        const int hs = p.num_blocks * kMaxClsOcc;
         hipLaunchKernelGGL(k_queue_init, dim3(1), dim3(kThreads), 0, s, p.ws, cg, hs);
         if (!p.force_generic) {
             hipLaunchKernelGGL(k_g3t, dim3(64, p.T), dim3(kThreads), 0, s, a);

@@ -549,6 +549,7 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
     const int T = p.T;
     const int64_t nnz = p.nnz, nbags = (int64_t)T * p.B;
     timer_begin(p.timing, TM_GROUP_SORT, s);
+    timer_begin(p.timing, TM_STAGE_DECODE, s);
     hipLaunchKernelGGL(k_init_ctrl, dim3(1), dim3(kThreads), 0, s, ws, T);
     {
         int g = ceil_div(nbags > 0 ? nbags : 1, kThreads);
@@ -561,9 +562,11 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
         hipLaunchKernelGGL(k_decode, dim3(g), dim3(kThreads), 0, s, indices, nnz, p.dtab, T,
                            p.check_indices ? 1 : 0, ws);
     }
+    timer_end(p.timing, TM_STAGE_DECODE, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // 1. index sorting by (table, row), stable
+    timer_begin(p.timing, TM_STAGE_SORT, s);
     bool in1 = false;
     e = radix_sort_pairs(p, ws.keys0, ws.vals0, ws.keys1, ws.vals1, nnz, nullptr, p.key_bits, &in1, s);
     if (e != hipSuccess) return e;
@@ -571,13 +574,19 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
     const int32_t *sv = in1 ? ws.vals1 : ws.vals0;
     // the plan points skeys/perm at the buffers the sort ends in
     if (sk != ws.skeys || sv != ws.perm) return hipErrorInvalidValue;
+    timer_end(p.timing, TM_STAGE_SORT, s);
     timer_end(p.timing, TM_GROUP_SORT, s);
     timer_begin(p.timing, TM_GROUP_RLE, s);
     // 2. unique extraction
+    timer_begin(p.timing, TM_STAGE_UNIQUE, s);
     if (nnz > 0) {
         UniqueOp uop{sk, sv, ws, nnz};
         e = run_scan(uop, ws.part, scan_blocks(nnz), s);
         if (e != hipSuccess) return e;
+    }
+    timer_end(p.timing, TM_STAGE_UNIQUE, s);
+    timer_begin(p.timing, TM_STAGE_PREFIX, s);
+    if (nnz > 0) {
         // 3.-4. mixed-radix conversion, prefix extraction, run-length encoding
         GroupOp gop{p.dtab, T, ws};
         e = run_scan(gop, ws.part, scan_blocks(nnz), s);
@@ -590,8 +599,10 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
         hipLaunchKernelGGL(k_units_unique, dim3(g), dim3(kThreads), 0, s, p.dtab, T, ws);
     }
     hipLaunchKernelGGL(k_finalize_bases, dim3(1), dim3(64), 0, s, p.dtab, T, unique_only ? 1 : 0, ws);
+    timer_end(p.timing, TM_STAGE_PREFIX, s);
     if (nnz > 0) {
         // B-stationary order of units: stable sort by (table, i2)
+        timer_begin(p.timing, TM_STAGE_ORDER, s);
         int g = ceil_div(nnz, kThreads * 4);
         if (g > 8192) g = 8192;
         hipLaunchKernelGGL(k_unit_keys, dim3(g), dim3(kThreads), 0, s, p.dtab, T, ws);
@@ -603,6 +614,9 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
         const int32_t *uo = u1 ? ws.uvals1 : ws.uvals0;
         if (k2 != ws.ukey2 || uo != ws.uorder) return hipErrorInvalidValue;
         hipLaunchKernelGGL(k_uinv, dim3(g), dim3(kThreads), 0, s, ws, uo);
+        timer_end(p.timing, TM_STAGE_ORDER, s);
+        // 5. work list: runs of equal (table, i2), tiles of <= 4 units, chunks
+        timer_begin(p.timing, TM_STAGE_WORKLIST, s);
         RunOp rop{k2, ws};
         e = run_scan(rop, ws.part, scan_blocks(nnz), s);
         if (e != hipSuccess) return e;
@@ -615,6 +629,7 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
         int gc = ceil_div(ws.chunk_cap, kThreads);
         if (gc > 4096) gc = 4096;
         hipLaunchKernelGGL(k_chunk_records, dim3(gc), dim3(kThreads), 0, s, p.dtab, T, p.chunk_rows, ws);
+        timer_end(p.timing, TM_STAGE_WORKLIST, s);
     }
     timer_end(p.timing, TM_GROUP_RLE, s);
     return hipGetLastError();

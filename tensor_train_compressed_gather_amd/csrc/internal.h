@@ -64,6 +64,7 @@ struct TableDesc {
 };
 
 constexpr int kMaxChunkRows = 32; // rows per forward work chunk (upper limit)
+constexpr int kSinkFloats = 4 * 4 * 256; // 4 float4 stores per thread of a 256-thread block
 
 // Context of one forward work chunk, built once per grouping (one 256-byte
 // record so the persistent kernel fetches it with a single wave-wide load).
@@ -132,6 +133,7 @@ struct Ws {
     int32_t *flags;          // [kMaxCkptSlots] checkpoint ready flags
     float *ckpt;             // [kMaxCkptSlots][4][16][max R2 + 4]
     float *E;                // unique rows, per-table segments
+    float *sink;             // [kSinkFloats] scratch target of stores that carry no result
     // backward
     int2 *lk;                // [nnz] (bag within its table, unique row) of each lookup
     int32_t *gu_ml;          // [gather tasks] unique row of the run cut at the task's left edge, or -1
@@ -149,7 +151,8 @@ struct Ws {
 
 enum TimerId {
     TM_GROUP_SORT = 0, TM_GROUP_RLE, TM_CONTRACT, TM_POOL, TM_BWD_GATHER, TM_BWD_CONTRACT,
-    TM_BWD_REDUCE, TM_SGD, TM_FWD_CLS0, TM_BWD_CLS0 = TM_FWD_CLS0 + 4, TM_COUNT = TM_BWD_CLS0 + 4
+    TM_BWD_REDUCE, TM_SGD, TM_FWD_CLS0, TM_BWD_CLS0 = TM_FWD_CLS0 + 4, TM_STAGE_DECODE = TM_BWD_CLS0 + 4,
+    TM_STAGE_SORT, TM_STAGE_UNIQUE, TM_STAGE_PREFIX, TM_STAGE_ORDER, TM_STAGE_WORKLIST, TM_COUNT
 };
 struct Timing; // host-side event rings (api.hip)
 void timer_begin(Timing *tm, int id, hipStream_t s);

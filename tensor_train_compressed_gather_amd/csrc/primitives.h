@@ -7,6 +7,19 @@ namespace ttemb {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// A value every lane of the wave holds, moved to a scalar register.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Read-only view of device data that no kernel of the current launch writes
+// (table descriptors, per-table bases set by an earlier kernel).  Through the
+// constant address space, wave-uniform reads become scalar loads, which do not
+// wait behind the wave's outstanding vector loads and stores.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T *kconst(const T *p)
+{
+    return (const __attribute__((address_space(4))) T *)p;
+}
+
 // Inclusive scan inside one 64-lane wave.
 template <class T>
 __device__ __forceinline__ T wave_inclusive_scan(T x)
