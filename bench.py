@@ -41,35 +41,38 @@ def mfma_rank(tb):
     return None
 
 
-def kernel_flops(tabs, U_r, U_p):
+def kernel_flops(tabs, U_r, U_p, kept=False):
     """Algorithmic flops of each matrix-core contraction kernel: forward
-    (C once per prefix unit, E once per unique row) and backward (C, dG1 and
-    dG2 per unit; dC and the dG3 partial per unique row)."""
+    (C once per prefix unit, E once per unique row) and backward (dG1 and dG2
+    per unit, plus C again unless the forward kept it; dC and the dG3 partial
+    per unique row)."""
     out = {}
     for tb, ur, up in zip(tabs, U_r, U_p):
         R = mfma_rank(tb)
         if R is None:
             continue
+        n1 = 2 if kept and R >= 32 else 3  # the library keeps C_p at ranks >= 32
         d1, d2, d3 = tb.d
         step1 = 2.0 * d1 * R * d2 * R
         step2 = 2.0 * d1 * d2 * d3 * R
         out[f"fwd_r{R}"] = out.get(f"fwd_r{R}", 0.0) + up * step1 + ur * step2
-        out[f"bwd_r{R}"] = out.get(f"bwd_r{R}", 0.0) + up * 3 * step1 + ur * 2 * step2
+        out[f"bwd_r{R}"] = out.get(f"bwd_r{R}", 0.0) + up * n1 * step1 + ur * 2 * step2
     return out
 
 
-def phase_flops(tabs, U_r, U_p, nnz_t):
+def phase_flops(tabs, U_r, U_p, nnz_t, kept=False):
     """Algorithmic flops of the contraction phases (prefix reuse counted once)."""
     fwd = bwd = pool = 0.0
     for tb, ur, up, nz in zip(tabs, U_r, U_p, nnz_t):
+        n1 = 2 if kept and mfma_rank(tb) is not None and mfma_rank(tb) >= 32 else 3
         d1, d2, d3 = tb.d
         R1, R2 = tb.R[1], tb.R[2]
         D = d1 * d2 * d3
         step1 = 2.0 * d1 * R1 * d2 * R2
         step2 = 2.0 * D * R2
         fwd += up * step1 + ur * step2
-        # recompute C, dG1 and dG2 per unit; dC and the dG3 term per unique row
-        bwd += up * 3 * step1 + ur * 2 * step2
+        # dG1 and dG2 (and C unless kept) per unit; dC and the dG3 term per unique row
+        bwd += up * n1 * step1 + ur * 2 * step2
         pool += nz * D
     return fwd, bwd, pool
 
@@ -166,8 +169,12 @@ def write_traffic(d):
 
 
 class Bench:
-    def __init__(self, w, torch, tt, options=None):
+    def __init__(self, w, torch, tt, options=None, keep=False):
         self.w, self.torch, self.tt = w, torch, tt
+        self.keep = keep
+        if keep:
+            options = options or tt.tt_emb_options()
+            options.keep_prefix = 1
         dev = "cuda"
         self.emb = tt.TTEmbeddingBag(w.tables, dev, options)
         self.cores = [torch.from_numpy(c).to(dev) for c in w.cores]
@@ -182,9 +189,11 @@ class Bench:
         self.emb.forward(self.cores, self.idx, self.off, self.w.B, out=self.out)
 
     def train_step(self):
-        self.emb.forward(self.cores, self.idx, self.off, self.w.B, out=self.out)
+        tt = self.tt
+        self.emb.forward(self.cores, self.idx, self.off, self.w.B, out=self.out,
+                         flags=tt.TT_EMB_KEEP_PREFIX if self.keep else 0)
         self.emb.backward(self.gout, self.cores, self.idx, self.off, self.w.B, core_grads=self.grads,
-                          flags=self.tt.TT_EMB_REUSE_GROUPING)
+                          flags=tt.TT_EMB_REUSE_GROUPING | (tt.TT_EMB_REUSE_PREFIX if self.keep else 0))
         self.emb.sgd_update(self.cores, self.grads, self.w.lr)
 
     def timed(self, fn, steps, warmup):
@@ -274,7 +283,7 @@ def run_sweep(args, torch, tt, W, opts):
         torch.cuda.empty_cache()
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
-        b = Bench(w, torch, tt, opts)
+        b = Bench(w, torch, tt, opts, keep=args.prefix == "keep")
         ws_bytes = tt.tt_emb_workspace_size(b.emb.handle, w.B, w.nnz)
         tms, _, tph = b.timed(b.train_step, args.steps, args.warmup)
         fms, _, fph = b.timed(b.fwd, args.steps, args.warmup)
@@ -316,6 +325,9 @@ def main():
     ap.add_argument("--pmc-dir", default="gpurun_out/m",
                     help="traffic: directory with the fetch/, write/, cfetch/, cwrite/ counter runs")
     ap.add_argument("--config", type=int, default=4, help="workload of --mode fwd (1..4)")
+    ap.add_argument("--prefix", default="keep", choices=("keep", "recompute"),
+                    help="training step: the forward keeps C_p for the backward (default) or the "
+                         "backward recomputes it")
     ap.add_argument("--batches", default="2048,4096,8192,16384,32768,65536,131072",
                     help="sweep: bags per table, comma separated")
     args = ap.parse_args()
@@ -372,17 +384,18 @@ def main():
                           "sched_stats": fc}), flush=True)
         return
 
+    keep = args.prefix == "keep"
     w = W.make_workload(5)
-    b = Bench(w, torch, tt, opts)
+    b = Bench(w, torch, tt, opts, keep=keep)
     ms, wall, ph = b.timed(b.train_step, args.steps, args.warmup)
     U_r, U_p, nnz_t, cnt = b.counts()
-    F_fwd, F_bwd, F_pool = phase_flops(w.tables, U_r, U_p, nnz_t)
+    F_fwd, F_bwd, F_pool = phase_flops(w.tables, U_r, U_p, nnz_t, kept=keep)
     value = w.nnz / (ms * 1e-3)
     per_step = {k: (v[0] / max(v[1], 1), v[1]) for k, v in ph.items() if v[1]}
     # single-kernel timers: one HIP event pair per launch, on the library's stream
     phases, kern_ms, stages = split_timers(per_step)
     kern_ms["pool"] = per_step["pool"][0]  # the pooling phase is one kernel
-    kflops = kernel_flops(w.tables, U_r, U_p)
+    kflops = kernel_flops(w.tables, U_r, U_p, kept=keep)
     wl = W.CONFIG_NAMES[5]
     # dominant kernel of the step and its roofline
     dom = max(kern_ms, key=kern_ms.get)
@@ -407,7 +420,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl, "step": "group+fwd+bwd+sgd", "tables": w.T, "batch": w.B, "nnz": w.nnz,
-                   "unique_rows": sum(U_r), "prefix_groups": sum(U_p), "sched": args.sched,
+                   "unique_rows": sum(U_r), "prefix_groups": sum(U_p),
+                   "prefix_intermediates": "kept by the forward" if keep else "recomputed by the backward",
+                   "sched": args.sched,
                    "group": args.group, "wall_s": wall},
         "phases_ms": phases,
         "grouping_stages_ms": stages,

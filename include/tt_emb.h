@@ -87,12 +87,29 @@ typedef struct {
     int32_t num_blocks;    /* persistent grid size (0 = one block per compute unit) */
     int32_t check_indices; /* 0 = on (default), 1 = on, -1 = off (caller guarantees) */
     int32_t force_generic; /* 1 = use the plain (non-MFMA) contraction kernels (testing) */
-    int32_t reserved[2];
+    int32_t keep_prefix;   /* 1 = the workspace also has room for the prefix intermediates
+                              C_p of the matrix-core tables (TT_EMB_KEEP_PREFIX and
+                              TT_EMB_REUSE_PREFIX below); 0 = no room, flags rejected */
+    int32_t reserved;
 } tt_emb_options;
 
 /* tt_emb_forward / tt_emb_backward flags. */
 #define TT_EMB_REUSE_GROUPING 1u /* ws already holds the grouping of these exact
                                     (indices, offsets, B, nnz); skip rebuilding it */
+/* Training mode (FlowTT section 3.2: the backward reverses the forward's
+ * contraction flow).  TT_EMB_KEEP_PREFIX (forward): also store every prefix
+ * unit's C_p = G1[i1] . G2[i2] of the matrix-core tables of rank >= 32 in ws
+ * (smaller ranks recompute it: cheaper than storing and reading it).
+ * TT_EMB_REUSE_PREFIX (backward): read C_p from ws instead of recomputing it;
+ * valid only with TT_EMB_REUSE_GROUPING, after a forward on the same ws, the
+ * same grouping and the same cores with TT_EMB_KEEP_PREFIX (the caller
+ * asserts this, as with the grouping).  Both need a handle created with
+ * keep_prefix = 1, else TT_EMB_ERR_ARG (checked before any device work).
+ * The backward's gradients then use the forward's C_p, which the forward sums
+ * over r1 in one chain where the recomputing backward uses two: results
+ * agree to rounding, not bit for bit, and each path is itself deterministic. */
+#define TT_EMB_KEEP_PREFIX 2u
+#define TT_EMB_REUSE_PREFIX 4u
 
 /* Device pointers to the grouping arrays held in a workspace (for tests and
  * tools), all int32, ids global over tables in table order:

@@ -27,6 +27,8 @@ TT_EMB_ERR_OFFSETS = -7
 TT_EMB_SCHED_DEFAULT, TT_EMB_SCHED_STATIC, TT_EMB_SCHED_STEAL, TT_EMB_SCHED_STEAL_L2 = 0, 1, 2, 3
 TT_EMB_GROUP_DEFAULT, TT_EMB_GROUP_PREFIX, TT_EMB_GROUP_UNIQUE_ONLY = 0, 1, 2
 TT_EMB_REUSE_GROUPING = 1
+TT_EMB_KEEP_PREFIX = 2
+TT_EMB_REUSE_PREFIX = 4
 
 EXPORTED = (
     "tt_emb_create", "tt_emb_destroy", "tt_emb_workspace_size", "tt_emb_group", "tt_emb_forward",
@@ -42,7 +44,7 @@ TIMER_NAMES = ("group_sort", "group_rle", "contract", "pool", "bwd_gather", "bwd
 class tt_emb_options(C.Structure):
     _fields_ = [("sched_mode", C.c_int32), ("group_mode", C.c_int32), ("chunk_rows", C.c_int32),
                 ("num_blocks", C.c_int32), ("check_indices", C.c_int32), ("force_generic", C.c_int32),
-                ("reserved", C.c_int32 * 2)]
+                ("keep_prefix", C.c_int32), ("reserved", C.c_int32)]
 
 
 class tt_emb_grouping(C.Structure):

@@ -38,7 +38,7 @@ struct tt_emb {
     std::vector<TableDesc> tabs;
     TableDesc *dtab = nullptr;
     int device = 0;
-    int sched_mode, group_mode, chunk_rows, num_blocks, check_indices, force_generic;
+    int sched_mode, group_mode, chunk_rows, num_blocks, check_indices, force_generic, keep_prefix;
     bool any_generic;
     int key_bits, key2_bits, key3_bits;
     int Dmax, Dpmax, R2max, sumD;
@@ -149,6 +149,22 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     const int64_t part_elems = tasks * 2 * h->Dpmax;
     w.E = (float *)take(4 * e_elems);
     w.sink = (float *)take(4 * (size_t)kSinkFloats);
+    w.cbase = (int64_t *)take(8 * T);
+    // kept prefix intermediates (keep_prefix handles only): 16 x R2 floats per
+    // unit of every table of the kept rank classes, at most min(units of the
+    // table, nnz) units
+    int64_t cg_elems = 0;
+    if (h->keep_prefix) {
+        for (int t = 0; t < T; ++t) {
+            const TableDesc &d = h->tabs[t];
+            if (d.cls < kKeepMinCls) continue;
+            const int64_t pre = (int64_t)d.n1 * d.n2;
+            int64_t ub = h->group_mode == TT_EMB_GROUP_UNIQUE_ONLY ? d.N : (pre < d.N ? pre : d.N);
+            ub = ub < n ? ub : n;
+            cg_elems += ub * 16 * (int64_t)d.R2;
+        }
+    }
+    w.Cg = (float *)take(4 * (cg_elems > 0 ? cg_elems : 4));
     w.lk = (int2 *)take(8 * n);
     w.gu_ml = (int32_t *)take(4 * tasks);
     w.gu_mr = (int32_t *)take(4 * tasks);
@@ -178,6 +194,7 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
         p->chunk_rows = h->chunk_rows;
         p->check_indices = h->check_indices;
         p->force_generic = h->force_generic;
+        p->keep_c = p->reuse_c = 0;
         p->any_generic = h->any_generic;
         p->cls_mask = h->cls_mask;
         p->gcls_mask = h->gcls_mask;
@@ -247,6 +264,7 @@ int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const in
         h->g3t_elems = 0;
         h->check_indices = o.check_indices >= 0 ? 1 : 0;
         h->force_generic = o.force_generic ? 1 : 0;
+        h->keep_prefix = o.keep_prefix ? 1 : 0;
         uint64_t key = 0, b1 = 0, b2 = 0, b3 = 0;
         int col = 0;
         h->any_generic = false;
@@ -444,6 +462,8 @@ int tt_emb_forward(tt_emb_t h, const float *const *cores, const int64_t *indices
         if (B > 0 && !out) return TT_EMB_ERR_ARG;
         CorePtrs cp{};
         if ((rc = core_ptrs(h, cores, &cp))) return rc;
+        if ((flags & TT_EMB_KEEP_PREFIX) && !h->keep_prefix) return TT_EMB_ERR_ARG;
+        p.keep_c = (flags & TT_EMB_KEEP_PREFIX) ? 1 : 0;
         if ((rc = set_device(h))) return rc;
         hipStream_t s = (hipStream_t)stream;
         if (!(flags & TT_EMB_REUSE_GROUPING)) {
@@ -474,6 +494,9 @@ int tt_emb_backward(tt_emb_t h, const float *grad_out, const float *const *cores
                 if (bad_ptr(g)) return TT_EMB_ERR_ARG;
                 gp.g[t][k] = g;
             }
+        if ((flags & TT_EMB_REUSE_PREFIX) && (!h->keep_prefix || !(flags & TT_EMB_REUSE_GROUPING)))
+            return TT_EMB_ERR_ARG;
+        p.reuse_c = (flags & TT_EMB_REUSE_PREFIX) ? 1 : 0;
         if ((rc = set_device(h))) return rc;
         hipStream_t s = (hipStream_t)stream;
         if (!(flags & TT_EMB_REUSE_GROUPING)) {

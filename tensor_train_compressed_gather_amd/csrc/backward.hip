@@ -566,7 +566,8 @@ struct BwdLds {
     static constexpr int PF = CLS == 3 ? 2 : CLS == 2 ? 6 : CLS == 1 ? 3 : 2;
 };
 
-template <int R>
+// REUSE: the prefix tiles C come from the forward (Ws::Cg) instead of step (1).
+template <int R, bool REUSE>
 __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_class(BwdArgs a)
 {
     using L = BwdLds<R>;
@@ -680,6 +681,11 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
         // a load may still target makes the compiler wait for every outstanding
         // load and store of the wave.
         floatx4 pfv[PF], pg1; // native vectors (a struct copy here would live in scratch)
+        // with REUSE, the next tile's kept C (4 units x 16 rows x R floats,
+        // compact in Cg by work position) travels with them
+        constexpr int CPB = REUSE ? (16 * R + BT - 1) / BT : 1;
+        floatx4 pc[CPB];
+        const float *Cgt = ws.Cg + kconst(ws.cbase)[t];
         auto pf_issue = [&](const ChunkRec &r, bool tile_start) __attribute__((always_inline)) {
             const int n = first_rows(r);
 #pragma unroll
@@ -698,6 +704,17 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                 const int gj = e / (R / 4), r4 = e - gj * (R / 4), g = gj >> 2, j1 = gj & 3;
                 const bool ok = g < r.nu && j1 < d1;
                 pg1 = reinterpret_cast<const floatx4 *>(G1 + ((int64_t)(ok ? r.i1[g] : r.i1[0]) * d1 + (ok ? j1 : 0)) * R)[r4];
+                if constexpr (REUSE) {
+                    const floatx4 *src = reinterpret_cast<const floatx4 *>(Cgt + (int64_t)r.ubeg * 16 * R);
+#pragma unroll
+                    for (int i = 0; i < CPB; ++i) {
+                        // float4 e of the tile = (unit * 16 + row) * R/4 + col4; units
+                        // past the tile's read unit 0 (their C rows are never used)
+                        const int e = tid + i * BT;
+                        const bool in = e < 16 * R && e / (4 * R) < r.nu;
+                        pc[i] = src[in ? e : 0];
+                    }
+                }
             }
         };
         auto pf_commit = [&](const ChunkRec &r, bool tile_start) __attribute__((always_inline)) {
@@ -712,6 +729,18 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                     } else {
                         const int r4 = rem - c4g, j3 = (4 * r4) / R, rr = 4 * r4 - j3 * R;
                         *reinterpret_cast<floatx4 *>(G3s + q * G3ST + j3 * G3J + rr) = pfv[i];
+                    }
+                }
+            }
+            if constexpr (REUSE) {
+                if (tile_start) {
+#pragma unroll
+                    for (int i = 0; i < CPB; ++i) {
+                        const int e = tid + i * BT;
+                        if (e < 16 * R) {
+                            const int j = e / (4 * R), f = e - j * (4 * R), m = f / (R / 4), c4q = f - m * (R / 4);
+                            *reinterpret_cast<floatx4 *>(Cs + j * CUNIT + m * CSTR + 4 * c4q) = pc[i];
+                        }
                     }
                 }
             }
@@ -750,8 +779,9 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                 }
             }
             if (new_tile) {
-                // ---- (1) prefix tile C
-                {
+                // ---- (1) prefix tile C (with REUSE it is already in Cs, committed
+                // with the tile's first rows)
+                if constexpr (!REUSE) {
                     // two independent chains per output tile (even and odd k steps)
                     const int g = li >> 2, j1 = li & 3;
                     floatx4 acc[NTW], acc2[NTW];
@@ -1140,23 +1170,17 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
             for (int c = 0; c < 4; ++c) {
                 if (!(p.cls_mask & (1 << c))) continue;
                 timer_begin(p.timing, TM_BWD_CLS0 + c, s);
-                switch (c) {
-                case 0:
-                    hipLaunchKernelGGL(k_bwd_class<8>, dim3(p.num_blocks * BwdLds<8>::OCC), dim3(BwdLds<8>::NW * 64), 0,
-                                       s, a);
-                    break;
-                case 1:
-                    hipLaunchKernelGGL(k_bwd_class<16>, dim3(p.num_blocks * BwdLds<16>::OCC), dim3(BwdLds<16>::NW * 64),
-                                       0, s, a);
-                    break;
-                case 2:
-                    hipLaunchKernelGGL(k_bwd_class<32>, dim3(p.num_blocks * BwdLds<32>::OCC), dim3(BwdLds<32>::NW * 64),
-                                       0, s, a);
-                    break;
-                default:
-                    hipLaunchKernelGGL(k_bwd_class<64>, dim3(p.num_blocks * BwdLds<64>::OCC), dim3(BwdLds<64>::NW * 64),
-                                       0, s, a);
-                    break;
+                switch (c * 2 + (p.reuse_c && c >= kKeepMinCls ? 1 : 0)) {
+#define TT_BWD_CLASS(RR, RU)                                                                                    \
+    hipLaunchKernelGGL((k_bwd_class<RR, RU>), dim3(p.num_blocks * BwdLds<RR>::OCC), dim3(BwdLds<RR>::NW * 64), 0, \
+                       s, a)
+                case 0: TT_BWD_CLASS(8, false); break;
+                case 2: TT_BWD_CLASS(16, false); break;
+                case 4: TT_BWD_CLASS(32, false); break;
+                case 5: TT_BWD_CLASS(32, true); break;
+                case 6: TT_BWD_CLASS(64, false); break;
+                default: TT_BWD_CLASS(64, true); break;
+#undef TT_BWD_CLASS
                 }
                 timer_end(p.timing, TM_BWD_CLS0 + c, s);
             }

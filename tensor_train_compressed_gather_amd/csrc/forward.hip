@@ -194,7 +194,9 @@ __device__ __forceinline__ void chunk_piece(const ChunkRec &r, int P, int e, int
 
 // Pieces of a chunk whose B operands a wave keeps in registers from one chunk
 // to the next: they are loaded while the previous chunk finishes.
-template <int R> constexpr int fwd_nq() { return R <= 32 ? 3 : 2; }
+// (one fewer at rank 64 when the prefix intermediates are kept: its C stores
+// need the registers)
+template <int R, bool KEEP> constexpr int fwd_nq() { return R <= 32 ? 3 : KEEP ? 1 : 2; }
 
 // B operand of output tile e of chunk r: G3t[i3][j3][kq*KQ .. kq*KQ+KQ-1] of
 // the lane's row.  Lanes past the tile's rows read its first row; their
@@ -261,15 +263,15 @@ __device__ __forceinline__ void load_a(const FwdArgs &a, const ChunkRec &r, floa
 // Every operand a chunk loads from memory except its G2 slice: the A operand
 // and the B operands of the wave's first NQ output tiles.  Issued while the
 // previous chunk finishes, before its E stores.
-template <int R>
+template <int R, bool KEEP>
 __device__ __forceinline__ void load_operands(const FwdArgs &a, const ChunkRec &r, float (&av)[R / 4],
-                                              float (&bq)[fwd_nq<R>()][R / 4])
+                                              float (&bq)[fwd_nq<R, KEEP>()][R / 4])
 {
     load_a<R>(a, r, av);
     const int w = uni(threadIdx.x >> 6);
     const int np = r.pstart[r.nu];
 #pragma unroll
-    for (int k = 0; k < fwd_nq<R>(); ++k) load_b_piece<R>(a, r, w + 4 * k < np ? w + 4 * k : (np > 0 ? np - 1 : 0), bq[k]);
+    for (int k = 0; k < fwd_nq<R, KEEP>(); ++k) load_b_piece<R>(a, r, w + 4 * k < np ? w + 4 * k : (np > 0 ? np - 1 : 0), bq[k]);
 }
 
 // E rows of a chunk staged in LDS are written out with this many float4
@@ -278,22 +280,27 @@ __device__ __forceinline__ void load_operands(const FwdArgs &a, const ChunkRec &
 // stores lets the next chunk wait for its operands, loaded before these
 // stores, without waiting for the stores.
 constexpr int kFlushPerThread = 4; // 32 rows of D <= 128
-static_assert(kFlushPerThread * kThreads * 4 <= kSinkFloats, "scratch line holds one flush");
+// With the prefix intermediates kept for the backward, the tile's first chunk
+// also writes its C tile (4 units x 16 rows x R, compact), again with a fixed
+// number of float4 stores per thread.
+template <int R> constexpr int keep_per_thread() { return (16 * R + kThreads - 1) / kThreads; }
+static_assert((kFlushPerThread + keep_per_thread<64>()) * kThreads * 4 <= kSinkFloats,
+              "scratch line holds one flush");
 
 // One chunk of a tile on the matrix cores, R1 = R2 = R.  On entry the chunk's
 // A operand (apf) and first B operands (bq) are loaded or in flight; on exit
 // those of the next chunk are.
-template <int R, class Mid, class End>
+template <int R, bool KEEP, class Mid, class End>
 __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec, float *Cs, float *Es,
                                            float (&breg)[FwdCfg<R>::BREG], int &bkey, int &lds_tile, int *s_flag,
-                                           float (&apf)[R / 4], float (&bq)[fwd_nq<R>()][R / 4], ChunkRec *rnext,
+                                           float (&apf)[R / 4], float (&bq)[fwd_nq<R, KEEP>()][R / 4], ChunkRec *rnext,
                                            bool has_next, int pre, int &hits, int &misses, int c, int cn,
                                            Mid &&mid, End &&endc)
 {
     constexpr int KQ = R / 4;           // K values each lane feeds per output tile
     constexpr int NT = R / 4;           // 16-column tiles of the padded d2*R2 (d2 <= 4)
     constexpr int NTW = (NT + 3) / 4;   // per wave
-    constexpr int NQ = fwd_nq<R>();     // output tiles per wave with B operands loaded ahead
+    constexpr int NQ = fwd_nq<R, KEEP>();     // output tiles per wave with B operands loaded ahead
     using L = FwdCfg<R>;
     // wave-uniform table index: the table data below become scalar loads,
     // which do not wait behind this wave's outstanding vector loads and stores
@@ -462,7 +469,7 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
     // (the last chunk reloads its own, so every chunk issues the same
     // loads), then this chunk's E rows
     endc();
-    load_operands<R>(a, has_next ? *rnext : rec, apf, bq);
+    load_operands<R, KEEP>(a, has_next ? *rnext : rec, apf, bq);
     if (staged) __syncthreads();
     {
         const int tot = nrows * c4;
@@ -481,9 +488,27 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
             *dst = *reinterpret_cast<const floatx4 *>(Es + (staged ? q * EST + 4 * r4 : 0));
         }
     }
+    if constexpr (KEEP) {
+        // C_u of the tile's units, [unit position in the work order][16][R]:
+        // the tile's first chunk writes them (lanes past the tile's units
+        // write element 0 again, with the same value), other chunks write the
+        // scratch line (a wave-uniform base, 32-bit offsets per lane)
+        const bool first = rbeg == 0;
+        floatx4 *base = first ? reinterpret_cast<floatx4 *>(a.ws.Cg + kconst(a.ws.cbase)[t] +
+                                                              (int64_t)rec.ubeg * 16 * R)
+                              : reinterpret_cast<floatx4 *>(a.ws.sink) + kFlushPerThread * kThreads;
+#pragma unroll
+        for (int k = 0; k < keep_per_thread<R>(); ++k) {
+            const int e = threadIdx.x + k * kThreads; // float4 of the tile, = (j * 16 + m) * R/4 + c4q
+            const bool in = e < 16 * R && e / (4 * R) < nu;
+            const int ec = in ? e : 0;
+            const int j = ec / (4 * R), f = ec - j * (4 * R), m = f / (R / 4), c4q = f - m * (R / 4);
+            base[first ? ec : e] = *reinterpret_cast<const floatx4 *>(Cs + j * L::CUNIT + m * L::CSTR + 4 * c4q);
+        }
+    }
 }
 
-template <int R>
+template <int R, bool KEEP>
 __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a, int heads_stride)
 {
     constexpr int CLS = R == 8 ? 0 : R == 16 ? 1 : R == 32 ? 2 : 3;
@@ -498,7 +523,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
     const int64_t C = ws.ctrl[CTRL_CLS_START + CLS + 1] - base;
     int32_t *heads = ws.heads + CLS * heads_stride * kHeadPad;
     const int nvict = a.sched == kSchedStatic ? 1 : nb;
-    float breg[FwdCfg<R>::BREG], apf[R / 4], bq[fwd_nq<R>()][R / 4];
+    float breg[FwdCfg<R>::BREG], apf[R / 4], bq[fwd_nq<R, KEEP>()][R / 4];
 #pragma unroll
     for (int i = 0; i < FwdCfg<R>::BREG; ++i) breg[i] = 0.f;
     int bkey = -1, lds_tile = -1, vi = 0, steals = 0, hits = 0, misses = 0;
@@ -524,9 +549,10 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
     // issues (the loop is entered only from here, so the compiler's count of
     // loads and stores in flight is the same on every path into it)
     if (uni(s_cur) >= 0) {
-        load_operands<R>(a, rbuf[0], apf, bq);
+        load_operands<R, KEEP>(a, rbuf[0], apf, bq);
+        constexpr int NST = kFlushPerThread + (KEEP ? keep_per_thread<R>() : 0);
 #pragma unroll
-        for (int k = 0; k < kFlushPerThread; ++k)
+        for (int k = 0; k < NST; ++k)
             reinterpret_cast<floatx4 *>(ws.sink)[threadIdx.x + k * kThreads] = floatx4{0.f, 0.f, 0.f, 0.f};
         int buf = 0;
         for (;;) {
@@ -546,7 +572,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
                     raw = claim_start(heads, me, vi, nb, nvict);
                 }
             };
-            chunk_mfma<R>(a, rbuf[buf], Cs, Es, breg, bkey, lds_tile, &s_flag, apf, bq, &rbuf[buf ^ 1], cn >= 0,
+            chunk_mfma<R, KEEP>(a, rbuf[buf], Cs, Es, breg, bkey, lds_tile, &s_flag, apf, bq, &rbuf[buf ^ 1], cn >= 0,
                           pre, hits, misses, c, cn, mid, endc);
             __syncthreads(); // everyone is done with rbuf[buf], s_cur and s_next
             if (threadIdx.x == 0) {
@@ -701,11 +727,18 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
             for (int c = 0; c < 4; ++c) {
                 if (!(p.cls_mask & (1 << c))) continue;
                 timer_begin(p.timing, TM_FWD_CLS0 + c, s);
-                switch (c) {
-                case 0: hipLaunchKernelGGL(k_contract<8>, dim3(cg.nb[0]), dim3(kThreads), 0, s, a, hs); break;
-                case 1: hipLaunchKernelGGL(k_contract<16>, dim3(cg.nb[1]), dim3(kThreads), 0, s, a, hs); break;
-                case 2: hipLaunchKernelGGL(k_contract<32>, dim3(cg.nb[2]), dim3(kThreads), 0, s, a, hs); break;
-                default: hipLaunchKernelGGL(k_contract<64>, dim3(cg.nb[3]), dim3(kThreads), 0, s, a, hs); break;
+                const dim3 grid(cg.nb[c]), block(kThreads);
+                static_assert(kKeepMinCls == 2, "kept-prefix kernels exist for ranks 32 and 64");
+                if (p.keep_c && c >= kKeepMinCls) {
+                    if (c == 2) hipLaunchKernelGGL((k_contract<32, true>), grid, block, 0, s, a, hs);
+                    else hipLaunchKernelGGL((k_contract<64, true>), grid, block, 0, s, a, hs);
+                } else {
+                    switch (c) {
+                    case 0: hipLaunchKernelGGL((k_contract<8, false>), grid, block, 0, s, a, hs); break;
+                    case 1: hipLaunchKernelGGL((k_contract<16, false>), grid, block, 0, s, a, hs); break;
+                    case 2: hipLaunchKernelGGL((k_contract<32, false>), grid, block, 0, s, a, hs); break;
+                    default: hipLaunchKernelGGL((k_contract<64, false>), grid, block, 0, s, a, hs); break;
+                    }
                 }
                 timer_end(p.timing, TM_FWD_CLS0 + c, s);
             }

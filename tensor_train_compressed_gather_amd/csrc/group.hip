@@ -375,6 +375,21 @@ __global__ void k_finalize_bases(const TableDesc *tab, int T, int unique_only, W
         ws.p3base[t] = p3 - u0 * (int64_t)d.R2 * d.d3;
         p3 += (u1 - u0) * (int64_t)d.R2 * d.d3;
     }
+    // kept prefix intermediates: 16 x R2 per unit of a table of the kept rank
+    // classes, by position in the work order.  That order is class-major (tables grouped
+    // by rank class, in table order within a class, as their i2 bases), so a
+    // table's units are contiguous there but not at tab_unit_start.
+    int64_t cg = 0, pos = 0;
+    for (int c = 0; c <= 4; ++c)
+        for (int t = 0; t < T; ++t) {
+            const TableDesc &d = tab[t];
+            if ((d.cls < 0 ? 4 : d.cls) != c) continue;
+            const int64_t units = ws.tab_unit_start[t + 1] - ws.tab_unit_start[t];
+            const int64_t per = d.cls >= kKeepMinCls ? 16 * (int64_t)d.R2 : 0;
+            ws.cbase[t] = cg - pos * per;
+            cg += units * per;
+            pos += units;
+        }
 }
 
 // ------------------------------------------------ B-stationary work list

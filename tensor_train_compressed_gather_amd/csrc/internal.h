@@ -64,7 +64,11 @@ struct TableDesc {
 };
 
 constexpr int kMaxChunkRows = 32; // rows per forward work chunk (upper limit)
-constexpr int kSinkFloats = 4 * 4 * 256; // 4 float4 stores per thread of a 256-thread block
+constexpr int kSinkFloats = 8 * 4 * 256; // 8 float4 stores per thread of a 256-thread block
+// Prefix intermediates are kept from forward to backward for the rank classes
+// from this one up (ranks >= 32).  Measured: at rank 16 the forward's extra C
+// stores cost what the backward's saved recompute gained.
+constexpr int kKeepMinCls = 2;
 
 // Context of one forward work chunk, built once per grouping (one 256-byte
 // record so the persistent kernel fetches it with a single wave-wide load).
@@ -133,6 +137,8 @@ struct Ws {
     int32_t *flags;          // [kMaxCkptSlots] checkpoint ready flags
     float *ckpt;             // [kMaxCkptSlots][4][16][max R2 + 4]
     float *E;                // unique rows, per-table segments
+    float *Cg;               // kept prefix intermediates: [work position][16][R2] per table (keep_prefix)
+    int64_t *cbase;          // [T] offset of table t's units in Cg, minus tab_unit_start[t]*16*R2
     float *sink;             // [kSinkFloats] scratch target of stores that carry no result
     // backward
     int2 *lk;                // [nnz] (bag within its table, unique row) of each lookup
@@ -164,6 +170,7 @@ struct Plan {
     int64_t B, nnz;
     int num_blocks;
     int sched_mode, group_mode, chunk_rows, check_indices, force_generic;
+    int keep_c, reuse_c; // forward stores C_p in Ws::Cg / backward reads it
     bool any_generic;
     int cls_mask; // bit c set when some table is in MFMA rank class c
     int gcls_mask; // bit c set when some table is in gradient-gather class c

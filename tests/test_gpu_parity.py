@@ -298,6 +298,56 @@ def test_host_detected_errors():
     assert e.value.status == tt.TT_EMB_ERR_ARG
 
 
+# ------------------------------------------------ kept prefix intermediates
+
+REUSE = tt.TT_EMB_REUSE_GROUPING | tt.TT_EMB_REUSE_PREFIX
+
+
+@pytest.mark.parametrize("cfg,bags,opt", [
+    (3, 256, {}),
+    (5, 64, {}),
+    (5, 64, {"chunk_rows": 3}),                   # many tiles split over chunks (checkpoints)
+    (5, 64, {"chunk_rows": 2, "sched_mode": 1}),  # split tiles, static ranges
+    (4, 128, {"group_mode": 2}),                  # one unit per unique row
+])
+def test_kept_prefix_backward_matches_oracle(cfg, bags, opt):
+    # training mode: the forward keeps every prefix unit's C_p, the backward
+    # reads it instead of recomputing it
+    w = W.make_workload(cfg, bags=bags)
+    if w.grad_out is None:
+        w.grad_out = W.make_grad_out(w, 200 + cfg)
+    run = Run(w, keep_prefix=1, **opt)
+    out = run.forward(flags=tt.TT_EMB_KEEP_PREFIX).cpu().numpy()
+    assert_out_close(w, out, oracle.forward(w))
+    got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=REUSE)]
+    assert_grads_close(got, oracle.backward(w))
+    # the recomputing backward on the same grouping sums C in another order:
+    # equal to rounding
+    rec = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
+    for k, (a, b) in enumerate(zip(got, rec)):
+        scale = np.abs(b).max()
+        assert np.abs(a.astype(np.float64) - b).max() <= 1e-5 * max(scale, 1e-30), k
+    again = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=REUSE)]
+    for a, b in zip(got, again):
+        assert np.array_equal(a, b)
+
+
+def test_prefix_flags_need_a_keep_prefix_handle():
+    w = W.make_workload(1)
+    w.grad_out = W.make_grad_out(w, 7)
+    run = Run(w)
+    with pytest.raises(tt.TTEmbError) as e:
+        run.forward(flags=tt.TT_EMB_KEEP_PREFIX)
+    assert e.value.status == tt.TT_EMB_ERR_ARG
+    run = Run(w, keep_prefix=1)
+    run.forward(flags=tt.TT_EMB_KEEP_PREFIX)
+    with pytest.raises(tt.TTEmbError) as e:  # the kept prefixes need the kept grouping
+        run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_PREFIX)
+    assert e.value.status == tt.TT_EMB_ERR_ARG
+    got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=REUSE)]
+    assert_grads_close(got, oracle.backward(w))
+
+
 # ------------------------------------------------------------ full sizes
 
 @pytest.mark.parametrize("cfg", [2, 3, 4])
@@ -313,11 +363,12 @@ def test_full_size_forward_sampled_bags(cfg):
     assert_out_close(w, out[bags], ref)
 
 
-def test_full_size_training_step_sampled_slices():
+@pytest.mark.parametrize("keep", [False, True])
+def test_full_size_training_step_sampled_slices(keep):
     w = W.make_workload(5)
-    run = Run(w)
-    run.forward()
-    grads = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
+    run = Run(w, keep_prefix=1) if keep else Run(w)
+    run.forward(flags=tt.TT_EMB_KEEP_PREFIX if keep else 0)
+    grads = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=REUSE if keep else tt.TT_EMB_REUSE_GROUPING)]
     rng = np.random.default_rng(55)
     tabs = [0, 7, 13, 25]
     sel = np.full((w.T, 3), -2, np.int64)
