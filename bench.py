@@ -188,6 +188,10 @@ class Bench:
     def fwd(self):
         self.emb.forward(self.cores, self.idx, self.off, self.w.B, out=self.out)
 
+    def fwd_fused(self):
+        # pooling inside the contraction with float atomics (not bit-reproducible)
+        self.emb.forward(self.cores, self.idx, self.off, self.w.B, out=self.out, flags=self.tt.TT_EMB_ATOMIC_POOL)
+
     def train_step(self):
         tt = self.tt
         self.emb.forward(self.cores, self.idx, self.off, self.w.B, out=self.out,
@@ -456,6 +460,14 @@ def main():
                 "post_grouping_frac_of_roofline": (ff / (PEAK_FP32_TFLOPS * 1e12) * 1e3) / post if post else None,
                 "sched_stats": fc,
             }
+            # the non-deterministic fast mode: pooling fused into the contraction
+            ums, _, uph = bf.timed(bf.fwd_fused, args.steps, args.warmup)
+            uphase, _, _ = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in uph.items() if v[1]})
+            upost = uphase.get("contract", 0) + uphase.get("pool", 0)
+            fwd[W.CONFIG_NAMES[cfg]]["fused_atomic_pool"] = {
+                "ms": ums, "lookups_per_s": wf.nnz / (ums * 1e-3), "post_grouping_ms": round(upost, 4),
+                "post_grouping_frac_of_roofline": (ff / (PEAK_FP32_TFLOPS * 1e12) * 1e3) / upost if upost else None,
+                "bit_reproducible": False}
             del bf
             torch.cuda.empty_cache()
         res["fwd"] = fwd

@@ -110,6 +110,14 @@ typedef struct {
  * agree to rounding, not bit for bit, and each path is itself deterministic. */
 #define TT_EMB_KEEP_PREFIX 2u
 #define TT_EMB_REUSE_PREFIX 4u
+/* Forward: fused pooling with float atomics (FlowTT section 3.2 pools inside
+ * the contraction, batching in on-chip memory and adding into the output with
+ * atomics).  Each unique row, still on chip, is added into the bag of every
+ * lookup of it; out is zeroed first.  The summation order then depends on
+ * scheduling, so the output is NOT bit-reproducible (within fp32 rounding of
+ * the deterministic path); the default bag-major pooling is.  Not with
+ * TT_EMB_KEEP_PREFIX (TT_EMB_ERR_ARG). */
+#define TT_EMB_ATOMIC_POOL 8u
 
 /* Device pointers to the grouping arrays held in a workspace (for tests and
  * tools), all int32, ids global over tables in table order:

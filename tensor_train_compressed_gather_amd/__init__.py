@@ -29,6 +29,7 @@ TT_EMB_GROUP_DEFAULT, TT_EMB_GROUP_PREFIX, TT_EMB_GROUP_UNIQUE_ONLY = 0, 1, 2
 TT_EMB_REUSE_GROUPING = 1
 TT_EMB_KEEP_PREFIX = 2
 TT_EMB_REUSE_PREFIX = 4
+TT_EMB_ATOMIC_POOL = 8
 
 EXPORTED = (
     "tt_emb_create", "tt_emb_destroy", "tt_emb_workspace_size", "tt_emb_group", "tt_emb_forward",

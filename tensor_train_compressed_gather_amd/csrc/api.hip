@@ -194,7 +194,7 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
         p->chunk_rows = h->chunk_rows;
         p->check_indices = h->check_indices;
         p->force_generic = h->force_generic;
-        p->keep_c = p->reuse_c = 0;
+        p->keep_c = p->reuse_c = p->pool_atomic = 0;
         p->any_generic = h->any_generic;
         p->cls_mask = h->cls_mask;
         p->gcls_mask = h->gcls_mask;
@@ -463,7 +463,9 @@ int tt_emb_forward(tt_emb_t h, const float *const *cores, const int64_t *indices
         CorePtrs cp{};
         if ((rc = core_ptrs(h, cores, &cp))) return rc;
         if ((flags & TT_EMB_KEEP_PREFIX) && !h->keep_prefix) return TT_EMB_ERR_ARG;
+        if ((flags & TT_EMB_KEEP_PREFIX) && (flags & TT_EMB_ATOMIC_POOL)) return TT_EMB_ERR_ARG;
         p.keep_c = (flags & TT_EMB_KEEP_PREFIX) ? 1 : 0;
+        p.pool_atomic = (flags & TT_EMB_ATOMIC_POOL) ? 1 : 0;
         if ((rc = set_device(h))) return rc;
         hipStream_t s = (hipStream_t)stream;
         if (!(flags & TT_EMB_REUSE_GROUPING)) {

@@ -1119,6 +1119,19 @@ __global__ __launch_bounds__(kThreads) void k_zero_g2(BwdArgs a)
         g[i] = 0.f;
 }
 
+hipError_t launch_lookup_meta(const Plan &p, const int64_t *offsets, hipStream_t s)
+{
+    BwdArgs a{p.dtab, p.T, p.B, p.ws, CorePtrs{}, GradPtrs{}, nullptr, offsets, p.nnz, p.sumD, p.Dpmax,
+              p.force_generic, p.g1stride};
+    const int64_t nbags = (int64_t)p.T * p.B;
+    if (p.nnz > 0 && nbags > 0) {
+        int g = ceil_div(nbags, kThreads);
+        if (g > 4096) g = 4096;
+        hipLaunchKernelGGL(k_lookup_meta, dim3(g), dim3(kThreads), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs &cores,
                            const int64_t *offsets, const GradPtrs &grads, hipStream_t s)
 {

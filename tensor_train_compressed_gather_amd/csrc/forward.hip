@@ -44,6 +44,7 @@ struct FwdCfg {
 };
 static_assert(FwdCfg<64>::CTILE == kCTile, "checkpoint slot holds the largest prefix tile");
 constexpr int kMaxClsOcc = 8; // queue heads per CU reserved for each class
+constexpr int kPoolCap = 64;  // fused pooling: lookups of a row pooled by the contraction itself
 constexpr int kSchedStatic = 1, kSchedSteal = 2, kSchedStealL2 = 3;
 
 struct FwdArgs {
@@ -52,6 +53,9 @@ struct FwdArgs {
     Ws ws;
     CorePtrs cores;
     int sched;
+    float *out; // fused pooling only: the pooled output [B][SD]
+    int SD;
+    int64_t B;
 };
 
 // Victim order for stealing: own range, then blocks on the same XCD (blocks
@@ -290,7 +294,7 @@ static_assert((kFlushPerThread + keep_per_thread<64>()) * kThreads * 4 <= kSinkF
 // One chunk of a tile on the matrix cores, R1 = R2 = R.  On entry the chunk's
 // A operand (apf) and first B operands (bq) are loaded or in flight; on exit
 // those of the next chunk are.
-template <int R, bool KEEP, class Mid, class End>
+template <int R, bool KEEP, bool POOL, class Mid, class End>
 __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec, float *Cs, float *Es,
                                            float (&breg)[FwdCfg<R>::BREG], int &bkey, int &lds_tile, int *s_flag,
                                            float (&apf)[R / 4], float (&bq)[fwd_nq<R, KEEP>()][R / 4], ChunkRec *rnext,
@@ -470,6 +474,41 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
     // loads), then this chunk's E rows
     endc();
     load_operands<R, KEEP>(a, has_next ? *rnext : rec, apf, bq);
+    if constexpr (POOL) {
+        // fused pooling (the pages' pooling inside the contraction): every
+        // lookup of each unique row of the chunk adds the row into its bag's
+        // output with float atomics; the summation order is not fixed, so the
+        // output is not bit-reproducible.  A wave takes rows, lanes columns;
+        // the bags of 64 lookups are loaded at once and broadcast.
+        __syncthreads(); // rows complete in Es (staged) or in E (written directly)
+        const int D = tb.D, col_off = tb.col_off;
+        const int r1 = rec.rowoff[1], r2 = rec.rowoff[2], r3 = rec.rowoff[3];
+        for (int q = w; q < nrows; q += 4) {
+            const int j = (q >= r1) + (q >= r2) + (q >= r3);
+            const int u = rec.ustart[j] + (q - rec.rowoff[j]);
+            const int s0 = a.ws.uniq_start[u], s1 = a.ws.uniq_start[u + 1];
+            // a row's first kPoolCap lookups are pooled here; a hot row (skewed
+            // indices) leaves its other lookups to k_pool_tail, which spreads
+            // them over the whole grid, and so keeps its row in E
+            const int se = s1 - s0 > kPoolCap ? s0 + kPoolCap : s1;
+            for (int cb = 0; cb < D; cb += 64) {
+                const int c = cb + lane;
+                float v = 0.f;
+                if (c < D) v = staged ? Es[q * EST + c] : Et[(int64_t)u * Dp + c];
+                if (staged && se < s1 && c < D) Et[(int64_t)u * Dp + c] = v;
+                for (int sb = s0; sb < se; sb += 64) {
+                    const int n = se - sb < 64 ? se - sb : 64;
+                    const int bag = lane < n ? a.ws.lk[a.ws.perm[sb + lane]].x : 0;
+                    for (int k = 0; k < n; ++k) {
+                        const int b = __shfl(bag, k, 64);
+                        // (a lookup outside every bag, from malformed offsets, is skipped)
+                        if (c < D && (uint64_t)b < (uint64_t)a.B) atomicAdd(a.out + (int64_t)b * a.SD + col_off + c, v);
+                    }
+                }
+            }
+        }
+        return;
+    }
     if (staged) __syncthreads();
     {
         const int tot = nrows * c4;
@@ -508,7 +547,7 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
     }
 }
 
-template <int R, bool KEEP>
+template <int R, bool KEEP, bool POOL>
 __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a, int heads_stride)
 {
     constexpr int CLS = R == 8 ? 0 : R == 16 ? 1 : R == 32 ? 2 : 3;
@@ -572,7 +611,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
                     raw = claim_start(heads, me, vi, nb, nvict);
                 }
             };
-            chunk_mfma<R, KEEP>(a, rbuf[buf], Cs, Es, breg, bkey, lds_tile, &s_flag, apf, bq, &rbuf[buf ^ 1], cn >= 0,
+            chunk_mfma<R, KEEP, POOL>(a, rbuf[buf], Cs, Es, breg, bkey, lds_tile, &s_flag, apf, bq, &rbuf[buf ^ 1], cn >= 0,
                           pre, hits, misses, c, cn, mid, endc);
             __syncthreads(); // everyone is done with rbuf[buf], s_cur and s_next
             if (threadIdx.x == 0) {
@@ -636,7 +675,7 @@ __global__ __launch_bounds__(kThreads) void k_contract_generic(FwdArgs a, int fo
 // xor-tree order.  Empty bags write zeros.
 __global__ __launch_bounds__(kThreads) void k_pool(const TableDesc *tab, int T, int64_t B,
                                                    const int64_t *offsets, int64_t nnz, Ws ws,
-                                                   float *out, int SD)
+                                                   float *out, int SD, int skip_mfma)
 {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t bag = (int64_t)blockIdx.x * (kThreads / 64) + w;
@@ -644,6 +683,7 @@ __global__ __launch_bounds__(kThreads) void k_pool(const TableDesc *tab, int T, 
     const int t = (int)(bag / B);
     const int64_t b = bag - (int64_t)t * B;
     const TableDesc &tb = tab[t];
+    if (skip_mfma && tb.cls >= 0) return; // pooled inside the contraction
     int64_t lo = offsets[bag], hi = offsets[bag + 1];
     lo = lo < 0 ? 0 : (lo > nnz ? nnz : lo);
     hi = hi < lo ? lo : (hi > nnz ? nnz : hi);
@@ -712,11 +752,52 @@ __global__ __launch_bounds__(kThreads) void k_pool(const TableDesc *tab, int T, 
     }
 }
 
+// Fused pooling: the remaining lookups of hot rows (those past a row's first
+// kPoolCap), one wave per 64 sorted positions over the whole grid; each such
+// lookup adds its row (kept in E) into its bag with float atomics.
+__global__ __launch_bounds__(kThreads) void k_pool_tail(FwdArgs a, int64_t nnz)
+{
+    const Ws &ws = a.ws;
+    const int lane = threadIdx.x & 63;
+    const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t s0 = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 64; s0 < nnz; s0 += nw * 64) {
+        const int64_t sp = s0 + lane;
+        int u = 0, bag = 0;
+        bool tail = false;
+        if (sp < nnz) {
+            const int l = ws.perm[sp];
+            u = ws.inv[l];
+            tail = sp - ws.uniq_start[u] >= kPoolCap;
+            bag = ws.lk[l].x;
+        }
+        uint64_t m = __ballot(tail);
+        while (m) {
+            const int k = __ffsll((unsigned long long)m) - 1;
+            m &= m - 1;
+            const int uk = __shfl(u, k, 64), bk = __shfl(bag, k, 64);
+            const int t = segment_of(ws.tab_uniq_start, a.T, uk);
+            const auto &tb = kconst(a.tab)[t];
+            if (tb.cls < 0 || (uint64_t)bk >= (uint64_t)a.B) continue; // generic tables: pooled by k_pool
+            const float *Erow = ws.E + kconst(ws.ebase)[t] + (int64_t)uk * tb.Dp;
+            for (int c = lane; c < tb.D; c += 64) atomicAdd(a.out + (int64_t)bk * a.SD + tb.col_off + c, Erow[c]);
+        }
+    }
+}
+
 hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *offsets, float *out,
                           hipStream_t s)
 {
-    FwdArgs a{p.dtab, p.T, p.ws, cores, p.sched_mode};
+    FwdArgs a{p.dtab, p.T, p.ws, cores, p.sched_mode, out, p.sumD, p.B};
+    const int64_t nbags = (int64_t)p.T * p.B;
+    // fused pooling: out accumulates from zero, and every lookup's bag is
+    // looked up once before the contraction
+    const bool fused = p.pool_atomic && !p.force_generic;
     timer_begin(p.timing, TM_CONTRACT, s);
+    if (fused && nbags > 0) {
+        hipError_t e = launch_fill_f32(out, 0.f, p.B * (int64_t)p.sumD, s);
+        if (e != hipSuccess) return e;
+        if ((e = launch_lookup_meta(p, offsets, s)) != hipSuccess) return e;
+    }
     if (p.nnz > 0) {
         ClassGrid cg;
         for (int c = 0; c < 4; ++c) cg.nb[c] = p.num_blocks * kClsOcc[c];
@@ -729,19 +810,33 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
                 timer_begin(p.timing, TM_FWD_CLS0 + c, s);
                 const dim3 grid(cg.nb[c]), block(kThreads);
                 static_assert(kKeepMinCls == 2, "kept-prefix kernels exist for ranks 32 and 64");
-                if (p.keep_c && c >= kKeepMinCls) {
-                    if (c == 2) hipLaunchKernelGGL((k_contract<32, true>), grid, block, 0, s, a, hs);
-                    else hipLaunchKernelGGL((k_contract<64, true>), grid, block, 0, s, a, hs);
+#define TT_FWD_CLASS(RR, KK, PP) hipLaunchKernelGGL((k_contract<RR, KK, PP>), grid, block, 0, s, a, hs)
+                if (fused) {
+                    switch (c) {
+                    case 0: TT_FWD_CLASS(8, false, true); break;
+                    case 1: TT_FWD_CLASS(16, false, true); break;
+                    case 2: TT_FWD_CLASS(32, false, true); break;
+                    default: TT_FWD_CLASS(64, false, true); break;
+                    }
+                } else if (p.keep_c && c >= kKeepMinCls) {
+                    if (c == 2) TT_FWD_CLASS(32, true, false);
+                    else TT_FWD_CLASS(64, true, false);
                 } else {
                     switch (c) {
-                    case 0: hipLaunchKernelGGL((k_contract<8, false>), grid, block, 0, s, a, hs); break;
-                    case 1: hipLaunchKernelGGL((k_contract<16, false>), grid, block, 0, s, a, hs); break;
-                    case 2: hipLaunchKernelGGL((k_contract<32, false>), grid, block, 0, s, a, hs); break;
-                    default: hipLaunchKernelGGL((k_contract<64, false>), grid, block, 0, s, a, hs); break;
+                    case 0: TT_FWD_CLASS(8, false, false); break;
+                    case 1: TT_FWD_CLASS(16, false, false); break;
+                    case 2: TT_FWD_CLASS(32, false, false); break;
+                    default: TT_FWD_CLASS(64, false, false); break;
                     }
                 }
+#undef TT_FWD_CLASS
                 timer_end(p.timing, TM_FWD_CLS0 + c, s);
             }
+        }
+        if (fused) {
+            int g = ceil_div(p.nnz, kThreads);
+            g = g > 8192 ? 8192 : g;
+            hipLaunchKernelGGL(k_pool_tail, dim3(g), dim3(kThreads), 0, s, a, p.nnz);
         }
         if (p.force_generic || p.any_generic)
             hipLaunchKernelGGL(k_contract_generic, dim3(p.num_blocks * 4), dim3(kThreads), 0, s, a,
@@ -749,11 +844,11 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
     }
     timer_end(p.timing, TM_CONTRACT, s);
     timer_begin(p.timing, TM_POOL, s);
-    const int64_t nbags = (int64_t)p.T * p.B;
-    if (nbags > 0) {
+    if (nbags > 0 && (!fused || p.any_generic)) {
+        // with fused pooling only the tables of the generic kernels are left
         const int64_t g = (nbags + 3) / 4;
         hipLaunchKernelGGL(k_pool, dim3((unsigned)g), dim3(kThreads), 0, s, p.dtab, p.T, p.B, offsets,
-                           p.nnz, p.ws, out, p.sumD);
+                           p.nnz, p.ws, out, p.sumD, fused ? 1 : 0);
     }
     timer_end(p.timing, TM_POOL, s);
     return hipGetLastError();

@@ -171,6 +171,7 @@ struct Plan {
     int num_blocks;
     int sched_mode, group_mode, chunk_rows, check_indices, force_generic;
     int keep_c, reuse_c; // forward stores C_p in Ws::Cg / backward reads it
+    int pool_atomic;     // forward pools inside the contraction with float atomics
     bool any_generic;
     int cls_mask; // bit c set when some table is in MFMA rank class c
     int gcls_mask; // bit c set when some table is in gradient-gather class c
@@ -192,6 +193,8 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
 // Backward (backward.hip)
 hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs &cores,
                            const int64_t *offsets, const GradPtrs &grads, hipStream_t s);
+// Bag (within its table) and unique row of every lookup position, Ws::lk.
+hipError_t launch_lookup_meta(const Plan &p, const int64_t *offsets, hipStream_t s);
 // SGD and fills (misc.hip)
 constexpr int kSgdMaxCores = 32; // cores per SGD launch (kernel-argument batch)
 struct SgdBatch {

@@ -298,6 +298,51 @@ def test_host_detected_errors():
     assert e.value.status == tt.TT_EMB_ERR_ARG
 
 
+# ------------------------------------------------ fused atomic pooling
+
+def _close_to(a, b, rel):
+    scale = np.abs(b).max()
+    assert np.abs(a.astype(np.float64) - b).max() <= rel * max(scale, 1e-30)
+
+
+@pytest.mark.parametrize("cfg,bags,opt", [
+    (1, None, {}), (2, 4096, {}), (3, 512, {}), (4, 128, {}),
+    (4, 128, {"chunk_rows": 2}),                  # split tiles
+    (4, 128, {"group_mode": 2, "sched_mode": 1}),  # one unit per unique row, static ranges
+])
+def test_fused_atomic_pooling_matches_oracle(cfg, bags, opt):
+    # the non-deterministic fast mode: rows pooled inside the contraction with
+    # float atomics; equal to the bag-major result up to summation order
+    w = W.make_workload(cfg, bags=bags)
+    run = Run(w, **opt)
+    fused = run.forward(flags=tt.TT_EMB_ATOMIC_POOL).cpu().numpy()
+    assert_out_close(w, fused, oracle.forward(w))
+    det = run.forward(flags=tt.TT_EMB_REUSE_GROUPING).cpu().numpy()
+    _close_to(fused, det, 1e-5)
+    assert run.emb.poll_error() == 0
+
+
+def test_fused_atomic_pooling_with_generic_tables_and_empty_bags():
+    tables = [W.Table(57, (3, 4, 5), (2, 3, 2), (1, 3, 2, 1), 0.3, "uniform"),      # generic kernels
+              W.Table(1000, (10, 10, 10), (2, 2, 4), (1, 8, 8, 1), 0.1, "zipf", 1.1),
+              W.Table(1000, (10, 10, 10), (4, 4, 16), (1, 16, 16, 1), 0.1, "uniform")]  # D = 256
+    rng = np.random.default_rng(11)
+    lens = [rng.integers(0, 9, size=48) for _ in tables]
+    lens[1][:5] = 0
+    idx = [rng.integers(0, t.N, size=int(l.sum())) for t, l in zip(tables, lens)]
+    idx[1] = rng.integers(0, 12, size=idx[1].size)  # hot rows, repeated within bags
+    w = W.make_custom(tables, lens, idx, seed=11)
+    for opt in ({}, {"force_generic": 1}):
+        run = Run(w, **opt)
+        out = run.forward(flags=tt.TT_EMB_ATOMIC_POOL).cpu().numpy()
+        assert_out_close(w, out, oracle.forward(w))
+        col = w.col_offsets()
+        assert not out[:5, col[1]:col[2]].any()
+    with pytest.raises(tt.TTEmbError) as e:  # not with kept prefixes
+        Run(w, keep_prefix=1).forward(flags=tt.TT_EMB_ATOMIC_POOL | tt.TT_EMB_KEEP_PREFIX)
+    assert e.value.status == tt.TT_EMB_ERR_ARG
+
+
 # ------------------------------------------------ kept prefix intermediates
 
 REUSE = tt.TT_EMB_REUSE_GROUPING | tt.TT_EMB_REUSE_PREFIX
