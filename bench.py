@@ -119,13 +119,13 @@ def load_traffic(kernel, workload, sha):
 
 
 # kernel symbol -> (timer name, sources it is built from)
-TRAFFIC_KERNELS = {
-    "k_bwd_class<64>": ("bwd_r64", ["backward.hip", "internal.h"]),
-    "k_bwd_class<32>": ("bwd_r32", ["backward.hip", "internal.h"]),
-    "k_bwd_class<16>": ("bwd_r16", ["backward.hip", "internal.h"]),
-    "k_contract<64>": ("fwd_r64", ["forward.hip", "internal.h"]),
-    "k_contract<32>": ("fwd_r32", ["forward.hip", "internal.h"]),
-    "k_contract<16>": ("fwd_r16", ["forward.hip", "internal.h"]),
+TRAFFIC_KERNELS = {  # (the training step runs one instantiation per rank)
+    "k_bwd_class<64,": ("bwd_r64", ["backward.hip", "internal.h"]),
+    "k_bwd_class<32,": ("bwd_r32", ["backward.hip", "internal.h"]),
+    "k_bwd_class<16,": ("bwd_r16", ["backward.hip", "internal.h"]),
+    "k_contract<64,": ("fwd_r64", ["forward.hip", "internal.h"]),
+    "k_contract<32,": ("fwd_r32", ["forward.hip", "internal.h"]),
+    "k_contract<16,": ("fwd_r16", ["forward.hip", "internal.h"]),
     "k_pool(": ("pool", ["forward.hip", "internal.h"]),
 }
 
