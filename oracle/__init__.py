@@ -55,6 +55,8 @@ def _load():
             lib.orc_grouping.argtypes = [i32, p, p, p, p, i64, i64, p, p, p, p, p, p, p, p, p]
             lib.orc_forward_grouped.argtypes = [i32, p, p, p, p, p, p, p, i64, i64, p]
             lib.orc_backward.argtypes = [i32, p, p, p, p, p, p, p, i64, i64, p, p, p, i32]
+            lib.orc_forward_k.argtypes = [i32, i32, p, p, p, p, p, p, p, i64, i64, p, i32]
+            lib.orc_forward_k_grouped.argtypes = [i32, i32, p, p, p, p, p, p, p, i64, i64, p]
             lib.orc_sgd_delta.argtypes = [p, i64, C.c_double, p]
             lib.orc_sgd_delta.restype = None
             lib.orc_max_threads.restype = C.c_int
@@ -205,4 +207,27 @@ def sgd_delta(dG: np.ndarray, lr: float) -> np.ndarray:
     src = np.ascontiguousarray(dG, dtype=np.float64)
     out = np.empty_like(src)
     lib.orc_sgd_delta(_ptr(src), src.size, float(lr), _ptr(out))
+    return out
+
+
+def forward_k(w, grouped: bool = False, threads: int = 0) -> np.ndarray:
+    """Pooled forward of K-core tables (every table of w has K = len(n)
+    cores), fp64 [B][sum D]: per-index chains, or (grouped) every distinct
+    leading-digit prefix computed once and reused."""
+    lib = _load()
+    K = len(w.tables[0].n)
+    assert all(len(t.n) == K for t in w.tables)
+    N, n, d, R = _shape_args(w)
+    cs, carr = _cores_arg(w.cores)
+    out = np.zeros((w.B, w.sum_D), dtype=np.float64)
+    idx = np.ascontiguousarray(w.indices, dtype=np.int64)
+    off = np.ascontiguousarray(w.offsets, dtype=np.int64)
+    if grouped:
+        rc = lib.orc_forward_k_grouped(w.T, K, _ptr(N), _ptr(n), _ptr(d), _ptr(R), carr, _ptr(idx), _ptr(off),
+                                       w.B, idx.shape[0], _ptr(out))
+    else:
+        rc = lib.orc_forward_k(w.T, K, _ptr(N), _ptr(n), _ptr(d), _ptr(R), carr, _ptr(idx), _ptr(off),
+                               w.B, idx.shape[0], _ptr(out), int(threads))
+    if rc:
+        raise OracleError(rc)
     return out

@@ -518,3 +518,255 @@ int orc_max_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------ K >= 2 TT cores */
+
+/* The general case of the same statement (FlowTT summary, section 2.4: a row
+ * is rebuilt by sequential TT-core contractions; section 3.3: rows sharing
+ * their leading digits share every prefix of that chain).  Each table has K
+ * cores; n, d are [T][K], R is [T][K+1] with R_0 = R_K = 1; digits are
+ * big-endian (i = ((i1*n2 + i2)*n3 + ...)*nK + iK) and output column
+ * j = ((j1*d2 + j2)*d3 + ...)*dK + jK, the 3-core readings extended. */
+
+#define ORC_MAXK 8
+
+static int check_tables_k(int32_t T, int32_t K, const int64_t *N, const int32_t *n, const int32_t *d,
+                          const int32_t *R)
+{
+    if (T <= 0 || K < 2 || K > ORC_MAXK) return ORC_ERR_ARG;
+    for (int t = 0; t < T; ++t) {
+        const int32_t *nt = n + K * t, *dt = d + K * t, *Rt = R + (K + 1) * t;
+        if (N[t] <= 0 || Rt[0] != 1 || Rt[K] != 1) return ORC_ERR_ARG;
+        int64_t prod = 1;
+        for (int k = 0; k < K; ++k) {
+            if (nt[k] <= 0 || dt[k] <= 0 || Rt[k + 1] <= 0) return ORC_ERR_ARG;
+            prod *= nt[k];
+            if (prod > ((int64_t)1 << 40)) prod = (int64_t)1 << 40;
+        }
+        if (prod < N[t]) return ORC_ERR_ARG;
+    }
+    return ORC_OK;
+}
+
+/* Digits of row i, most significant first. */
+static void decode_k(int64_t i, int32_t K, const int32_t *n, int64_t *dig)
+{
+    for (int k = K - 1; k >= 0; --k) {
+        dig[k] = i % n[k];
+        i /= n[k];
+    }
+}
+
+/* One step of the chain: V is [P][Rin] (row-major); the result W is
+ * [P*dk][Rout] with W[p*dk + j][r] = sum_{r'} V[p][r'] * G[ik][r'][j][r],
+ * r' ascending. */
+static void chain_step(const double *V, int64_t P, int32_t Rin, const float *Gk, int32_t dk, int32_t Rout,
+                       int64_t ik, double *Wv)
+{
+    const float *g = Gk + (size_t)ik * Rin * dk * Rout;
+    for (int64_t p = 0; p < P; ++p)
+        for (int32_t j = 0; j < dk; ++j)
+            for (int32_t r = 0; r < Rout; ++r) {
+                double acc = 0.0;
+                for (int32_t q = 0; q < Rin; ++q) acc += V[p * Rin + q] * (double)g[((size_t)q * dk + j) * Rout + r];
+                Wv[(p * dk + j) * Rout + r] = acc;
+            }
+}
+
+/* Row i of a K-core table, no reuse: V_1 = G1[i1] ([d1][R1]), V_k = V_{k-1} .
+ * G_k[i_k] for k = 2..K; the row is V_K ([D][1]).  work holds 2*maxP doubles
+ * where maxP bounds every intermediate (product of d's times the rank). */
+static void row_k(int32_t K, const int32_t *nt, const int32_t *dt, const int32_t *Rt, const float *const *G,
+                  int64_t i, double *work, int64_t maxP, double *E)
+{
+    int64_t dig[ORC_MAXK];
+    decode_k(i, K, nt, dig);
+    double *V = work, *Wv = work + maxP;
+    int64_t P = dt[0];
+    const float *g1 = G[0] + (size_t)dig[0] * dt[0] * Rt[1];
+    for (int64_t e = 0; e < P * Rt[1]; ++e) V[e] = (double)g1[e];
+    for (int k = 1; k < K; ++k) {
+        chain_step(V, P, Rt[k], G[k], dt[k], Rt[k + 1], dig[k], Wv);
+        P *= dt[k];
+        double *tmp = V;
+        V = Wv;
+        Wv = tmp;
+    }
+    for (int64_t j = 0; j < P; ++j) E[j] = V[j];
+}
+
+static int64_t maxp_k(int32_t T, int32_t K, const int32_t *d, const int32_t *R, int64_t *maxD)
+{
+    int64_t m = 1;
+    *maxD = 1;
+    for (int t = 0; t < T; ++t) {
+        int64_t P = 1;
+        for (int k = 0; k < K; ++k) {
+            P *= d[K * t + k];
+            const int64_t c = P * R[(K + 1) * t + k + 1];
+            if (c > m) m = c;
+        }
+        if (P > *maxD) *maxD = P;
+    }
+    return m;
+}
+
+static int check_csr_k(int32_t T, const int64_t *N, const int64_t *indices, const int64_t *offsets, int64_t B,
+                       int64_t nnz)
+{
+    return check_csr(T, N, indices, offsets, B, nnz);
+}
+
+/* Pooled forward of K-core tables with NO reuse (every index recomputes its
+ * whole chain), bags summed in CSR order; out fp64 [B][sum D]. */
+int orc_forward_k(int32_t T, int32_t K, const int64_t *N, const int32_t *n, const int32_t *d, const int32_t *R,
+                  const float *const *cores, const int64_t *indices, const int64_t *offsets, int64_t B,
+                  int64_t nnz, double *out, int32_t nthreads)
+{
+    int rc = check_tables_k(T, K, N, n, d, R);
+    if (rc) return rc;
+    rc = check_csr_k(T, N, indices, offsets, B, nnz);
+    if (rc) return rc;
+    int64_t maxD;
+    const int64_t maxP = maxp_k(T, K, d, R, &maxD);
+    int64_t *col_off = (int64_t *)malloc(sizeof(int64_t) * T);
+    if (!col_off) return ORC_ERR_NOMEM;
+    int64_t SD = 0;
+    for (int t = 0; t < T; ++t) {
+        col_off[t] = SD;
+        int64_t D = 1;
+        for (int k = 0; k < K; ++k) D *= d[K * t + k];
+        SD += D;
+    }
+    memset(out, 0, sizeof(double) * (size_t)(B * SD));
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel reduction(| : failed)
+#endif
+    {
+        double *work = (double *)malloc(sizeof(double) * (size_t)(2 * maxP));
+        double *E = (double *)malloc(sizeof(double) * (size_t)maxD);
+        if (!work || !E) failed = 1;
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 16)
+#endif
+        for (int64_t b = 0; b < B; ++b) {
+            if (!work || !E) continue;
+            for (int t = 0; t < T; ++t) {
+                const int32_t *nt = n + K * t, *dt = d + K * t, *Rt = R + (K + 1) * t;
+                int64_t D = 1;
+                for (int k = 0; k < K; ++k) D *= dt[k];
+                double *acc = out + b * SD + col_off[t];
+                for (int64_t l = offsets[(int64_t)t * B + b]; l < offsets[(int64_t)t * B + b + 1]; ++l) {
+                    row_k(K, nt, dt, Rt, cores + (size_t)K * t, indices[l], work, maxP, E);
+                    for (int64_t j = 0; j < D; ++j) acc[j] += E[j];
+                }
+            }
+        }
+        free(work);
+        free(E);
+    }
+    free(col_off);
+    return failed ? ORC_ERR_NOMEM : ORC_OK;
+}
+
+/* Unique rows of one table's lookups and, for every prefix length m = 1..K-1,
+ * the intermediate V_m computed once per distinct leading-digit prefix and
+ * reused by every row that shares it (FlowTT 3.3, generalised to every prefix
+ * length); rows are V_K = V_{K-1}[prefix] . G_K[i_K].  Bags are then summed in
+ * CSR order from the unique rows.  Same products in the same order as
+ * orc_forward_k, so the result is identical. */
+static int cmp_i64(const void *a, const void *b)
+{
+    const int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
+    return (x > y) - (x < y);
+}
+
+int orc_forward_k_grouped(int32_t T, int32_t K, const int64_t *N, const int32_t *n, const int32_t *d,
+                          const int32_t *R, const float *const *cores, const int64_t *indices,
+                          const int64_t *offsets, int64_t B, int64_t nnz, double *out)
+{
+    int rc = check_tables_k(T, K, N, n, d, R);
+    if (rc) return rc;
+    rc = check_csr_k(T, N, indices, offsets, B, nnz);
+    if (rc) return rc;
+    int64_t maxD;
+    const int64_t maxP = maxp_k(T, K, d, R, &maxD);
+    int64_t SD = 0;
+    for (int t = 0; t < T; ++t) {
+        int64_t D = 1;
+        for (int k = 0; k < K; ++k) D *= d[K * t + k];
+        SD += D;
+    }
+    memset(out, 0, sizeof(double) * (size_t)(B * SD));
+    int64_t col = 0;
+    for (int t = 0; t < T; ++t) {
+        const int32_t *nt = n + K * t, *dt = d + K * t, *Rt = R + (K + 1) * t;
+        const float *const *G = cores + (size_t)K * t;
+        int64_t D = 1;
+        for (int k = 0; k < K; ++k) D *= dt[k];
+        const int64_t l0 = offsets[(int64_t)t * B], l1 = offsets[(int64_t)(t + 1) * B], m = l1 - l0;
+        int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(m > 0 ? m : 1));
+        double *Erows = NULL, *lev = NULL;
+        int64_t U = 0;
+        if (!rows) return ORC_ERR_NOMEM;
+        for (int64_t l = 0; l < m; ++l) rows[l] = indices[l0 + l];
+        qsort(rows, (size_t)m, sizeof(int64_t), cmp_i64);
+        for (int64_t l = 0; l < m; ++l)
+            if (l == 0 || rows[l] != rows[l - 1]) rows[U++] = rows[l];
+        Erows = (double *)malloc(sizeof(double) * (size_t)((U > 0 ? U : 1) * D));
+        /* one current intermediate per prefix length, recomputed only when
+         * the row's prefix of that length changes (rows are sorted, so equal
+         * prefixes are consecutive) */
+        lev = (double *)malloc(sizeof(double) * (size_t)(K * maxP));
+        if (!Erows || !lev) {
+            free(rows);
+            free(Erows);
+            free(lev);
+            return ORC_ERR_NOMEM;
+        }
+        int64_t prevdig[ORC_MAXK];
+        for (int k = 0; k < K; ++k) prevdig[k] = -1;
+        for (int64_t u = 0; u < U; ++u) {
+            int64_t dig[ORC_MAXK];
+            decode_k(rows[u], K, nt, dig);
+            int same = 1; /* prefix of length k+1 unchanged so far */
+            int64_t P = dt[0];
+            for (int k = 0; k < K; ++k) {
+                same = same && dig[k] == prevdig[k];
+                double *Vk = lev + (size_t)k * maxP;
+                if (k == 0) {
+                    if (!same) {
+                        const float *g1 = G[0] + (size_t)dig[0] * dt[0] * Rt[1];
+                        for (int64_t e = 0; e < P * Rt[1]; ++e) Vk[e] = (double)g1[e];
+                    }
+                } else {
+                    if (!same) chain_step(lev + (size_t)(k - 1) * maxP, P, Rt[k], G[k], dt[k], Rt[k + 1], dig[k], Vk);
+                    P *= dt[k];
+                }
+            }
+            for (int k = 0; k < K; ++k) prevdig[k] = dig[k];
+            const double *VK = lev + (size_t)(K - 1) * maxP;
+            for (int64_t j = 0; j < D; ++j) Erows[u * D + j] = VK[j];
+        }
+        for (int64_t b = 0; b < B; ++b) {
+            double *acc = out + b * SD + col;
+            for (int64_t l = offsets[(int64_t)t * B + b]; l < offsets[(int64_t)t * B + b + 1]; ++l) {
+                /* unique id of the row: binary search in the sorted unique rows */
+                int64_t lo = 0, hi = U - 1;
+                while (lo < hi) {
+                    const int64_t mid = (lo + hi) / 2;
+                    if (rows[mid] < indices[l]) lo = mid + 1;
+                    else hi = mid;
+                }
+                for (int64_t j = 0; j < D; ++j) acc[j] += Erows[lo * D + j];
+            }
+        }
+        col += D;
+        free(rows);
+        free(Erows);
+        free(lev);
+    }
+    return ORC_OK;
+}

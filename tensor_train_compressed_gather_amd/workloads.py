@@ -46,12 +46,16 @@ class Table:
     alpha: float = 0.0
 
     @property
+    def K(self) -> int:
+        return len(self.n)
+
+    @property
     def D(self) -> int:
-        return int(self.d[0] * self.d[1] * self.d[2])
+        return int(np.prod(self.d))
 
     def core_shapes(self):
         n, d, R = self.n, self.d, self.R
-        return [(n[k], R[k], d[k], R[k + 1]) for k in range(3)]
+        return [(n[k], R[k], d[k], R[k + 1]) for k in range(len(n))]
 
 
 @dataclass
@@ -252,3 +256,41 @@ def make_fd_instance(seed: int = SEED_BASE + 55) -> Workload:
     w = _assemble("fd_1000rows_rank8", [tab], 64, "poisson20", rng, {"seed": seed})
     w.grad_out = rng.standard_normal((w.B, w.sum_D), dtype=np.float32)
     return w
+
+
+# --------------------------------------------------------- K >= 4 TT cores
+
+def near_equal_factors_k(N: int, K: int):
+    """K factors, the first K-1 equal to ceil(N^(1/K)) (then lowered while the
+    product still covers N), the last covering the rest."""
+    c = max(1, int(round(N ** (1.0 / K))))
+    while c ** K < N:
+        c += 1
+    while c > 1 and (c - 1) ** K >= N:
+        c -= 1
+    last = -(-N // (c ** (K - 1)))
+    return tuple([c] * (K - 1) + [int(last)])
+
+
+KCORE_NAMES = {
+    "k4": "tt10m_k4_d128_r32_b32768_len1-64_zipf1.2",
+    "k5": "tt10m_k5_d64_r16_b32768_len1-64_zipf1.2",
+}
+
+
+def make_kcore_workload(name: str, bags: int | None = None) -> Workload:
+    """Seeded K-core workloads (more than three TT cores per table): the
+    10^7-row, Zipf(1.2), bag length U[1, 64] shape of the single-table
+    workload with K = 4 (d = 2x4x4x4 = 128, ranks 32) or K = 5 (d = 2x2x2x2x4
+    = 64, ranks 16), sigma 0.05; same draw order as the 3-core recipe, seed
+    20270 + K."""
+    K = {"k4": 4, "k5": 5}[name]
+    rng = np.random.default_rng(np.random.PCG64(SEED_BASE + 10 + K))
+    B = 32768 if bags is None else int(bags)
+    N = 10 ** 7
+    if K == 4:
+        d, R = (2, 4, 4, 4), (1, 32, 32, 32, 1)
+    else:
+        d, R = (2, 2, 2, 2, 4), (1, 16, 16, 16, 16, 1)
+    tab = Table(N, near_equal_factors_k(N, K), d, R, 0.05, "zipf", 1.2)
+    return _assemble(KCORE_NAMES[name], [tab], B, "u1_64", rng, {"kcores": K, "seed": SEED_BASE + 10 + K})

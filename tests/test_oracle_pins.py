@@ -406,3 +406,69 @@ def test_generator_is_reproducible_and_shaped():
     for t, tab in enumerate(w4.tables):
         seg = w4.indices[w4.offsets[t * 16]:w4.offsets[(t + 1) * 16]]
         assert seg.min() >= 0 and seg.max() < tab.N
+
+
+# ------------------------------------------------------- K >= 4 TT cores
+
+def _dense_table_k(tab, cores):
+    """Full table [N][D] of a K-core table by one numpy einsum over the whole
+    cores (a different route from the oracle's per-row chain)."""
+    K = len(cores)
+    I, J, Rl = "abcdefgh"[:K], "ijklmnop"[:K], "qrstuvwxy"[: K + 1]
+    subs = ",".join(f"{I[k]}{Rl[k]}{J[k]}{Rl[k + 1]}" for k in range(K))
+    full = np.einsum(f"{subs}->{I}{J}", *[c.astype(np.float64) for c in cores])
+    n = [c.shape[0] for c in cores]
+    d = [c.shape[2] for c in cores]
+    return full.reshape(int(np.prod(n)), int(np.prod(d)))[: tab.N]
+
+
+@pytest.mark.parametrize("n,d,R", [
+    ((3, 2, 4, 2), (2, 3, 2, 2), (1, 3, 2, 4, 1)),
+    ((2, 3, 2, 2, 3), (2, 2, 1, 3, 2), (1, 2, 3, 2, 2, 1)),
+])
+def test_kcore_forward_matches_dense_table(n, d, R):
+    tab = _table(int(np.prod(n)) - 1, n, d, R, sigma=0.4)
+    w = _random_workload([tab], 24, seed=31)
+    dense = _dense_table_k(tab, w.cores)
+    ref = np.zeros((w.B, tab.D))
+    for b in range(w.B):
+        for l in range(w.offsets[b], w.offsets[b + 1]):
+            ref[b] += dense[w.indices[l]]
+    got = oracle.forward_k(w)
+    assert np.abs(got - ref).max() <= 1e-12 * max(np.abs(ref).max(), 1.0)
+
+
+def test_kcore_rank1_rows_are_kronecker_products():
+    n, d, R = (3, 2, 2, 3), (2, 3, 2, 2), (1, 1, 1, 1, 1)
+    tab = _table(36, n, d, R, sigma=0.5)
+    lens = [np.ones(36, np.int64)]
+    w = W.make_custom([tab], lens, [np.arange(36)], seed=32)
+    got = oracle.forward_k(w)
+    for i in range(36):
+        dig = np.unravel_index(i, n)
+        v = np.ones(1)
+        for k in range(4):
+            v = np.kron(v, w.cores[k][dig[k], 0, :, 0].astype(np.float64))
+        assert np.allclose(got[i], v, rtol=0, atol=1e-14)
+
+
+def test_kcore_with_three_cores_equals_the_three_core_oracle():
+    w = W.make_workload(3, bags=64)
+    a = oracle.forward_k(w)
+    b = oracle.forward(w)
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(b).max()
+
+
+@pytest.mark.parametrize("name,bags", [("k4", 64), ("k5", 64)])
+def test_kcore_grouped_is_bit_identical_to_ungrouped(name, bags):
+    w = W.make_kcore_workload(name, bags=bags)
+    assert np.array_equal(oracle.forward_k(w, grouped=True), oracle.forward_k(w))
+
+
+def test_kcore_workload_factors_cover_the_rows():
+    for name in ("k4", "k5"):
+        w = W.make_kcore_workload(name, bags=8)
+        t = w.tables[0]
+        assert np.prod(t.n) >= t.N and len(t.n) == t.K == len(t.d) == len(t.R) - 1
+        assert [c.shape for c in w.cores] == t.core_shapes()
+        assert w.indices.min() >= 0 and w.indices.max() < t.N
