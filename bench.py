@@ -168,6 +168,50 @@ def write_traffic(d):
     print(json.dumps(out, indent=1, sort_keys=True))
 
 
+def kcore_flops(tables, indices, offsets, B):
+    """Contraction flops of the K-core forward with prefix reuse at every
+    length (one intermediate per distinct prefix of length 2..K-1, one last
+    contraction per distinct row) and without it (the chain per lookup)."""
+    import numpy as np
+
+    grouped = dense = 0
+    for t, tab in enumerate(tables):
+        K, n, d, R = len(tab.n), tab.n, tab.d, tab.R
+        rows = indices[offsets[t * B]:offsets[(t + 1) * B]]
+        u = np.unique(rows)
+        P = [1]
+        for k in range(K):
+            P.append(P[-1] * d[k])
+        for m in range(2, K + 1):
+            per = 2 * P[m - 1] * R[m - 1] * d[m - 1] * R[m]
+            div = int(np.prod(n[m:])) if m < K else 1
+            grouped += per * (np.unique(u // div).size if m < K else u.size)
+            dense += per * rows.size
+    return float(grouped), float(dense)
+
+
+def kcore_extras(torch, tt, W, opts, args):
+    out = {}
+    for name in ("k4", "k5"):
+        wk = W.make_kcore_workload(name)
+        bk = Bench(wk, torch, tt, opts)
+        ms, _, ph = bk.timed(bk.fwd, args.steps, args.warmup)
+        phase, _, stages = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in ph.items() if v[1]})
+        fg, fd = kcore_flops(wk.tables, wk.indices, wk.offsets, wk.B)
+        cms = phase.get("contract", 0)
+        post = cms + phase.get("pool", 0)
+        out[wk.name] = {
+            "K": len(wk.tables[0].n), "lookups_per_s": wk.nnz / (ms * 1e-3), "ms": ms, "nnz": wk.nnz,
+            "post_grouping_ms": post, "phases_ms": phase, "grouping_stages_ms": stages,
+            "contract_flops": fg, "contract_flops_without_reuse": fd,
+            "contract_tflops": fg / (cms * 1e-3) / 1e12 if cms else None,
+            "contract_frac_fp32_peak": fg / (cms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS if cms else None,
+        }
+        del bk
+        torch.cuda.empty_cache()
+    return out
+
+
 class Bench:
     def __init__(self, w, torch, tt, options=None, keep=False):
         self.w, self.torch, self.tt = w, torch, tt
@@ -321,11 +365,12 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
     ap.add_argument("--sched", type=int, default=0, help="0 default, 1 static, 2 steal, 3 steal+L2")
     ap.add_argument("--group", type=int, default=0, help="0 default, 1 prefix, 2 unique-only")
-    ap.add_argument("--mode", default="train", choices=("train", "fwd", "copy", "traffic", "sweep"),
+    ap.add_argument("--mode", default="train", choices=("train", "fwd", "copy", "traffic", "sweep", "kcores"),
                     help="train: the full step (default); fwd: forward only on --config; "
                          "copy: a plain 1 GiB device copy (counter calibration); "
                          "traffic: turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json; "
-                         "sweep: training step and forward over --batches on the 26-table shapes")
+                         "sweep: training step and forward over --batches on the 26-table shapes; "
+                         "kcores: forward of the 4- and 5-core 10^7-row tables")
     ap.add_argument("--pmc-dir", default="gpurun_out/m",
                     help="traffic: directory with the fetch/, write/, cfetch/, cwrite/ counter runs")
     ap.add_argument("--config", type=int, default=4, help="workload of --mode fwd (1..4)")
@@ -372,6 +417,10 @@ def main():
 
     if args.mode == "sweep":
         run_sweep(args, torch, tt, W, opts)
+        return
+
+    if args.mode == "kcores":
+        print(json.dumps({"mode": "kcores", "fwd_kcores": kcore_extras(torch, tt, W, opts, args)}), flush=True)
         return
 
     if args.mode == "fwd":
@@ -471,6 +520,7 @@ def main():
             del bf
             torch.cuda.empty_cache()
         res["fwd"] = fwd
+        res["fwd_kcores"] = kcore_extras(torch, tt, W, opts, args)
 
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w)

@@ -146,6 +146,25 @@ typedef struct {
 int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const int32_t *d,
                   const int32_t *R, const tt_emb_options *opt, tt_emb_t *out);
 
+/* Tables of K TT cores, K = 3 .. 8, the same K for every table (FlowTT
+ * section 2.4 states the lookup as sequential TT-core contractions; section
+ * 3.3 reuses the intermediate of rows sharing their leading digits -- here
+ * at every prefix length).  n, d are host [T][K] arrays, R is [T][K+1] with
+ * R_0 = R_K = 1; core k is [n_k][R_k][d_k][R_{k+1}]; digits are big-endian
+ * (i = ((i_0 n_1 + i_1) n_2 + ...) n_{K-1} + i_{K-1}) and so are output
+ * columns.  K = 3 is exactly tt_emb_create.  For K >= 4 the forward takes a
+ * host array of T*K core pointers and computes every distinct prefix of
+ * length 2 .. K-1 once (plain fp32, no matrix cores); tt_emb_backward and
+ * tt_emb_sgd_update return TT_EMB_ERR_UNSUPPORTED, and the forward flags
+ * TT_EMB_KEEP_PREFIX / TT_EMB_ATOMIC_POOL give TT_EMB_ERR_ARG.  Beyond the
+ * three-core limits: TT_EMB_ERR_UNSUPPORTED when T*K > 192, K = 2, K > 8,
+ * the leading K-1 digits of all tables span 2^31 or more prefixes, or an
+ * intermediate or core slice of some level exceeds 8192 floats; K < 2 is
+ * TT_EMB_ERR_ARG.  The grouping view of such a handle groups unique rows by
+ * their leading K-1 digits (grp_prefix = row div n_{K-1}). */
+int tt_emb_create_k(int32_t T, int32_t K, const int64_t *num_rows, const int32_t *n, const int32_t *d,
+                    const int32_t *R, const tt_emb_options *opt, tt_emb_t *out);
+
 /* Release a handle (NULL is accepted). */
 int tt_emb_destroy(tt_emb_t h);
 

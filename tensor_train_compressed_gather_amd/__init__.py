@@ -9,6 +9,7 @@ is no CPU fallback -- if the library is missing, loading it raises.
 from __future__ import annotations
 
 import ctypes as C
+import math
 import os
 import threading
 
@@ -32,7 +33,7 @@ TT_EMB_REUSE_PREFIX = 4
 TT_EMB_ATOMIC_POOL = 8
 
 EXPORTED = (
-    "tt_emb_create", "tt_emb_destroy", "tt_emb_workspace_size", "tt_emb_group", "tt_emb_forward",
+    "tt_emb_create", "tt_emb_create_k", "tt_emb_destroy", "tt_emb_workspace_size", "tt_emb_group", "tt_emb_forward",
     "tt_emb_backward", "tt_emb_sgd_update", "tt_emb_grouping_view", "tt_emb_poll_error",
     "tt_emb_status_string", "tt_emb_timing_enable", "tt_emb_timing_read", "tt_emb_timer_name",
 )
@@ -73,6 +74,7 @@ def lib():
             L = C.CDLL(LIB_PATH)
             p, i32, i64, u32 = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32
             L.tt_emb_create.argtypes = [i32, p, p, p, p, C.POINTER(tt_emb_options), C.POINTER(p)]
+            L.tt_emb_create_k.argtypes = [i32, i32, p, p, p, p, C.POINTER(tt_emb_options), C.POINTER(p)]
             L.tt_emb_destroy.argtypes = [p]
             L.tt_emb_workspace_size.argtypes = [p, i64, i64, C.POINTER(C.c_size_t)]
             L.tt_emb_group.argtypes = [p, p, p, i64, i64, p, C.c_size_t, p]
@@ -126,6 +128,24 @@ def _ptr_array(tensors):
 
 def tt_emb_status_string(status: int) -> str:
     return lib().tt_emb_status_string(int(status)).decode()
+
+
+def tt_emb_create_k(K: int, num_rows, n, d, R, options: tt_emb_options | None = None):
+    """K-core tables: num_rows [T], n [T][K], d [T][K], R [T][K+1] -> handle."""
+    import numpy as np
+
+    N = np.ascontiguousarray(np.asarray(num_rows, dtype=np.int64).reshape(-1))
+    nn = np.ascontiguousarray(np.asarray(n, dtype=np.int32).reshape(-1))
+    dd = np.ascontiguousarray(np.asarray(d, dtype=np.int32).reshape(-1))
+    RR = np.ascontiguousarray(np.asarray(R, dtype=np.int32).reshape(-1))
+    T = N.shape[0]
+    if nn.shape[0] != K * T or dd.shape[0] != K * T or RR.shape[0] != (K + 1) * T:
+        raise ValueError("shape arrays must have KT, KT and (K+1)T entries")
+    h = C.c_void_p()
+    rc = lib().tt_emb_create_k(T, int(K), N.ctypes.data, nn.ctypes.data, dd.ctypes.data, RR.ctypes.data,
+                               C.byref(options) if options is not None else None, C.byref(h))
+    _check(rc, "tt_emb_create_k")
+    return h
 
 
 def tt_emb_create(num_rows, n, d, R, options: tt_emb_options | None = None):
@@ -241,10 +261,15 @@ class TTEmbeddingBag:
     def __init__(self, tables, device="cuda", options: tt_emb_options | None = None):
         self.tables = list(tables)
         self.T = len(self.tables)
-        self.handle = tt_emb_create([t.N for t in self.tables], [t.n for t in self.tables],
-                                    [t.d for t in self.tables], [t.R for t in self.tables], options)
+        self.K = len(self.tables[0].n)
+        if self.K == 3:
+            self.handle = tt_emb_create([t.N for t in self.tables], [t.n for t in self.tables],
+                                        [t.d for t in self.tables], [t.R for t in self.tables], options)
+        else:
+            self.handle = tt_emb_create_k(self.K, [t.N for t in self.tables], [t.n for t in self.tables],
+                                          [t.d for t in self.tables], [t.R for t in self.tables], options)
         self.device = device
-        self.sum_D = sum(int(t.d[0] * t.d[1] * t.d[2]) for t in self.tables)
+        self.sum_D = sum(int(math.prod(t.d)) for t in self.tables)
         self._ws = None
         self._ws_key = None
 

@@ -46,6 +46,9 @@ struct tt_emb {
     int64_t max_d1R1, max_R2d3, max_Dp;
     int64_t g3t_elems;
     int cls_mask, gcls_mask;
+    int K = 3;                 // TT cores per table
+    std::vector<KTab> ktabs;   // K >= 4 only
+    KTab *dkt = nullptr;
 };
 
 namespace {
@@ -210,6 +213,30 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
         p->dtab = h->dtab;
         p->ws = w;
     }
+    // K >= 4 cores: per prefix length m = 2..K-1, the group of each unique
+    // row, the groups' first rows, and one intermediate per group (at most
+    // min(prefixes of length m, rows, nnz) groups per table)
+    KPlan kp{};
+    if (h->K >= 4) {
+        kp.K = h->K;
+        kp.dkt = h->dkt;
+        for (int m = 2; m <= h->K - 1; ++m) {
+            int64_t gb = 0, sm = 1;
+            for (int t = 0; t < T; ++t) {
+                const KTab &kt = h->ktabs[t];
+                int64_t prod = 1;
+                for (int j = 0; j < m; ++j) prod = std::min<int64_t>(prod * kt.n[j], (int64_t)1 << 40);
+                gb += std::min<int64_t>(std::min<int64_t>(prod, h->tabs[t].N), n);
+                sm = std::max<int64_t>(sm, (int64_t)kt.P[m] * kt.R[m]);
+            }
+            gb = std::min<int64_t>(gb, n);
+            kp.ugrp[m] = (int32_t *)take(4 * n);
+            kp.gfirst[m] = (int32_t *)take(4 * (n + 1));
+            kp.V[m] = (float *)take(4 * (size_t)(gb * sm));
+            kp.smax[m] = sm;
+        }
+    }
+    if (p) p->kp = kp;
     return off;
 }
 
@@ -409,12 +436,83 @@ static void free_timing(tt_emb *h)
     h->timing = nullptr;
 }
 
+int tt_emb_create_k(int32_t T, int32_t K, const int64_t *num_rows, const int32_t *n, const int32_t *d,
+                    const int32_t *R, const tt_emb_options *opt, tt_emb_t *out)
+{
+    try {
+        if (!out) return TT_EMB_ERR_ARG;
+        *out = nullptr;
+        if (T <= 0 || !num_rows || !n || !d || !R) return TT_EMB_ERR_ARG;
+        if (K == 3) return tt_emb_create(T, num_rows, n, d, R, opt, out);
+        if (K < 2) return TT_EMB_ERR_ARG;
+        if (K < 4 || K > kMaxK || T > kMaxTables || T * K > kMaxKPtrs) return TT_EMB_ERR_UNSUPPORTED;
+        std::vector<KTab> kts((size_t)T);
+        std::vector<int32_t> n3(3 * (size_t)T), d3(3 * (size_t)T, 1), R3(4 * (size_t)T, 1);
+        int rc = TT_EMB_OK;
+        for (int t = 0; t < T; ++t) {
+            const int32_t *nt = n + (size_t)K * t, *dt = d + (size_t)K * t, *Rt = R + (size_t)(K + 1) * t;
+            KTab &kt = kts[t];
+            kt = KTab{};
+            kt.K = K;
+            if (num_rows[t] <= 0 || Rt[0] != 1 || Rt[K] != 1) return TT_EMB_ERR_ARG;
+            int64_t prod = 1, D = 1;
+            for (int k = 0; k < K; ++k) {
+                if (nt[k] <= 0 || dt[k] <= 0 || Rt[k + 1] <= 0) return TT_EMB_ERR_ARG;
+                kt.n[k] = nt[k];
+                kt.d[k] = dt[k];
+                kt.R[k] = Rt[k];
+                prod = std::min<int64_t>(prod * nt[k], (int64_t)1 << 40);
+                D *= dt[k];
+                if (D > 1024) rc = TT_EMB_ERR_UNSUPPORTED;
+                if (Rt[k + 1] > 256) rc = TT_EMB_ERR_UNSUPPORTED;
+            }
+            kt.R[K] = 1;
+            if (prod < num_rows[t]) return TT_EMB_ERR_ARG;
+            if (prod >= ((int64_t)1 << 40)) rc = TT_EMB_ERR_UNSUPPORTED;
+            int64_t dv = 1;
+            for (int k = K - 1; k >= 0; --k) {
+                kt.div[k] = dv;
+                dv = std::min<int64_t>(dv * nt[k], (int64_t)1 << 40);
+            }
+            kt.P[0] = 1;
+            for (int m = 1; m <= K; ++m) kt.P[m] = kt.P[m - 1] * dt[m - 1];
+            // staged operands of every level must fit in LDS
+            for (int m = 2; m <= K - 1; ++m)
+                if ((int64_t)kt.P[m - 1] * kt.R[m - 1] > kKLds || (int64_t)kt.R[m - 1] * dt[m - 1] * Rt[m] > kKLds)
+                    rc = TT_EMB_ERR_UNSUPPORTED;
+            if ((int64_t)kt.P[K - 1] * kt.R[K - 1] > kKLds) rc = TT_EMB_ERR_UNSUPPORTED;
+            // the three-core view the grouping uses: digits (1, leading, last)
+            const int64_t lead = kt.div[0] * nt[0] / nt[K - 1];
+            if (lead >= 0x7fffffff) rc = TT_EMB_ERR_UNSUPPORTED;
+            n3[3 * t] = 1;
+            n3[3 * t + 1] = (int32_t)std::min<int64_t>(lead, 0x7fffffff);
+            n3[3 * t + 2] = nt[K - 1];
+            d3[3 * t + 2] = (int32_t)std::min<int64_t>(D, 1 << 20);
+        }
+        if (rc != TT_EMB_OK) return rc;
+        if ((rc = tt_emb_create(T, num_rows, n3.data(), d3.data(), R3.data(), opt, out)) != TT_EMB_OK) return rc;
+        tt_emb *h = *out;
+        h->K = K;
+        h->ktabs = kts;
+        if (hipMalloc((void **)&h->dkt, sizeof(KTab) * T) != hipSuccess ||
+            hipMemcpy(h->dkt, kts.data(), sizeof(KTab) * T, hipMemcpyHostToDevice) != hipSuccess) {
+            tt_emb_destroy(h);
+            *out = nullptr;
+            return TT_EMB_ERR_HIP;
+        }
+        return TT_EMB_OK;
+    } catch (...) {
+        return TT_EMB_ERR_NOMEM;
+    }
+}
+
 int tt_emb_destroy(tt_emb_t h)
 {
     if (!h) return TT_EMB_OK;
     int rc = TT_EMB_OK;
     free_timing(h);
     if (h->dtab && hipFree(h->dtab) != hipSuccess) rc = TT_EMB_ERR_HIP;
+    if (h->dkt && hipFree(h->dkt) != hipSuccess) rc = TT_EMB_ERR_HIP;
     delete h;
     return rc;
 }
@@ -440,6 +538,16 @@ int tt_emb_group(tt_emb_t h, const int64_t *indices, const int64_t *offsets, int
     }
 }
 
+static int kcore_ptrs(const tt_emb *h, const float *const *cores, KCorePtrs *cp)
+{
+    if (!cores) return TT_EMB_ERR_ARG;
+    for (int i = 0; i < h->T * h->K; ++i) {
+        if (bad_ptr(cores[i])) return TT_EMB_ERR_ARG;
+        cp->g[i] = cores[i];
+    }
+    return TT_EMB_OK;
+}
+
 static int core_ptrs(const tt_emb *h, const float *const *cores, CorePtrs *cp)
 {
     if (!cores) return TT_EMB_ERR_ARG;
@@ -460,6 +568,18 @@ int tt_emb_forward(tt_emb_t h, const float *const *cores, const int64_t *indices
         int rc = check_call(h, B, nnz, indices, offsets, ws, ws_bytes, &p);
         if (rc) return rc;
         if (B > 0 && !out) return TT_EMB_ERR_ARG;
+        if (h->K >= 4) {
+            // tables of K >= 4 cores: prefix reuse at every prefix length
+            if (flags & (TT_EMB_KEEP_PREFIX | TT_EMB_ATOMIC_POOL)) return TT_EMB_ERR_ARG;
+            KCorePtrs kc{};
+            if ((rc = kcore_ptrs(h, cores, &kc))) return rc;
+            if ((rc = set_device(h))) return rc;
+            hipStream_t s = (hipStream_t)stream;
+            if (!(flags & TT_EMB_REUSE_GROUPING)) {
+                if ((rc = hip_status(launch_grouping(p, indices, offsets, s)))) return rc;
+            }
+            return hip_status(launch_forward_k(p, kc, offsets, out, s));
+        }
         CorePtrs cp{};
         if ((rc = core_ptrs(h, cores, &cp))) return rc;
         if ((flags & TT_EMB_KEEP_PREFIX) && !h->keep_prefix) return TT_EMB_ERR_ARG;
@@ -486,6 +606,7 @@ int tt_emb_backward(tt_emb_t h, const float *grad_out, const float *const *cores
         int rc = check_call(h, B, nnz, indices, offsets, ws, ws_bytes, &p);
         if (rc) return rc;
         if (B > 0 && !grad_out) return TT_EMB_ERR_ARG;
+        if (h->K != 3) return TT_EMB_ERR_UNSUPPORTED; // the backward covers three cores
         CorePtrs cp{};
         if ((rc = core_ptrs(h, cores, &cp))) return rc;
         if (!core_grads) return TT_EMB_ERR_ARG;
@@ -513,6 +634,7 @@ int tt_emb_backward(tt_emb_t h, const float *grad_out, const float *const *cores
 int tt_emb_sgd_update(tt_emb_t h, float *const *cores, const float *const *core_grads, float lr, void *stream)
 {
     if (!h || !cores || !core_grads) return TT_EMB_ERR_ARG;
+    if (h->K != 3) return TT_EMB_ERR_UNSUPPORTED;
     for (int i = 0; i < 3 * h->T; ++i)
         if (bad_ptr(cores[i]) || bad_ptr(core_grads[i])) return TT_EMB_ERR_ARG;
     int rc = set_device(h);

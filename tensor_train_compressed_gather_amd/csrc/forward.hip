@@ -784,6 +784,17 @@ __global__ __launch_bounds__(kThreads) void k_pool_tail(FwdArgs a, int64_t nnz)
     }
 }
 
+hipError_t launch_pool(const Plan &p, const int64_t *offsets, float *out, hipStream_t s)
+{
+    const int64_t nbags = (int64_t)p.T * p.B;
+    if (nbags > 0) {
+        const int64_t g = (nbags + 3) / 4;
+        hipLaunchKernelGGL(k_pool, dim3((unsigned)g), dim3(kThreads), 0, s, p.dtab, p.T, p.B, offsets, p.nnz,
+                           p.ws, out, p.sumD, 0);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *offsets, float *out,
                           hipStream_t s)
 {

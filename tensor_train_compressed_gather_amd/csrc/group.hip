@@ -615,6 +615,10 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
     }
     hipLaunchKernelGGL(k_finalize_bases, dim3(1), dim3(64), 0, s, p.dtab, T, unique_only ? 1 : 0, ws);
     timer_end(p.timing, TM_STAGE_PREFIX, s);
+    if (p.kp.K > 0) { // K >= 4 cores: the prefix levels are built by the forward itself
+        timer_end(p.timing, TM_GROUP_RLE, s);
+        return hipGetLastError();
+    }
     if (nnz > 0) {
         // B-stationary order of units: stable sort by (table, i2)
         timer_begin(p.timing, TM_STAGE_ORDER, s);

@@ -41,6 +41,7 @@ enum CtrlSlot {
     CTRL_BWD_NEXT = 40,  // 4 words: next run of each class's backward contraction
     CTRL_CLS_START = 16, // 5 words: first chunk of each MFMA rank class (chunks are class-major)
     CTRL_RUN_CLS = 24,   // 6 words: first run of each class, then the run count
+    CTRL_KLEV = 48,      // 8 words: groups of each prefix length (tables of K >= 4 cores)
     CTRL_N = 64
 };
 enum ErrBits { ERRB_INDEX = 1, ERRB_OFFSETS = 2, ERRB_CAPACITY = 4 };
@@ -164,6 +165,29 @@ struct Timing; // host-side event rings (api.hip)
 void timer_begin(Timing *tm, int id, hipStream_t s);
 void timer_end(Timing *tm, int id, hipStream_t s);
 
+// Tables of K >= 4 TT cores (one K per handle).  Core k of a table is
+// [n_k][R_k][d_k][R_{k+1}] (R_0 = R_K = 1); digits are big-endian.
+constexpr int kMaxK = 8;
+constexpr int kMaxKPtrs = 3 * kMaxTables; // core pointers of a K-core handle, T * K of them
+constexpr int kKLds = 8192;               // floats of each staged operand of a prefix level
+struct KTab {
+    int32_t K;
+    int32_t n[kMaxK], d[kMaxK], R[kMaxK + 1];
+    int64_t div[kMaxK]; // product of n_j over j > k: digit k = row / div[k] % n[k]
+    int32_t P[kMaxK + 1]; // product of d_j over j < m: rows of the prefix-m intermediate
+};
+struct KCorePtrs {
+    const float *g[kMaxKPtrs]; // table t, core k at t * K + k
+};
+struct KPlan {
+    int K;
+    const KTab *dkt;            // device copy, one per table
+    int32_t *ugrp[kMaxK];       // prefix length m: [U] group of each unique row
+    int32_t *gfirst[kMaxK];     // [U + 1] first unique row of each group
+    float *V[kMaxK];            // [groups][smax[m]] prefix-m intermediates
+    int64_t smax[kMaxK];        // floats per group of prefix length m
+};
+
 struct Plan {
     Timing *timing; // nullptr unless phase timing is enabled
     int32_t T;
@@ -172,6 +196,7 @@ struct Plan {
     int sched_mode, group_mode, chunk_rows, check_indices, force_generic;
     int keep_c, reuse_c; // forward stores C_p in Ws::Cg / backward reads it
     int pool_atomic;     // forward pools inside the contraction with float atomics
+    KPlan kp;            // K >= 4 cores (kp.K == 0 for three-core handles)
     bool any_generic;
     int cls_mask; // bit c set when some table is in MFMA rank class c
     int gcls_mask; // bit c set when some table is in gradient-gather class c
@@ -195,6 +220,11 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
                            const int64_t *offsets, const GradPtrs &grads, hipStream_t s);
 // Bag (within its table) and unique row of every lookup position, Ws::lk.
 hipError_t launch_lookup_meta(const Plan &p, const int64_t *offsets, hipStream_t s);
+// Bag-major pooling of the unique rows of every table (forward.hip).
+hipError_t launch_pool(const Plan &p, const int64_t *offsets, float *out, hipStream_t s);
+// Forward of K >= 4 cores: every prefix length's intermediates, rows, pooling (kcores.hip).
+hipError_t launch_forward_k(const Plan &p, const KCorePtrs &cores, const int64_t *offsets, float *out,
+                            hipStream_t s);
 // SGD and fills (misc.hip)
 constexpr int kSgdMaxCores = 32; // cores per SGD launch (kernel-argument batch)
 struct SgdBatch {

@@ -80,6 +80,36 @@ def test_create_rejects_bad_shapes_before_touching_the_device(N, n, d, R, code):
     assert not h.value
 
 
+def _create_k(K, N, n, d, R):
+    h = C.c_void_p()
+    NN = np.asarray(N, np.int64)
+    nn = np.asarray(n, np.int32).reshape(-1)
+    dd = np.asarray(d, np.int32).reshape(-1)
+    RR = np.asarray(R, np.int32).reshape(-1)
+    rc = tt.lib().tt_emb_create_k(len(NN), K, NN.ctypes.data, nn.ctypes.data, dd.ctypes.data, RR.ctypes.data,
+                                  None, C.byref(h))
+    return rc, h
+
+
+@pytest.mark.parametrize("K,N,n,d,R,code", [
+    (1, [10], [10], [4], [1, 1], tt.TT_EMB_ERR_ARG),                                   # K < 2
+    (2, [100], [10, 10], [2, 4], [1, 8, 1], tt.TT_EMB_ERR_UNSUPPORTED),                # two cores
+    (9, [512], [2] * 9, [1] * 9, [1] * 10, tt.TT_EMB_ERR_UNSUPPORTED),                 # K > 8
+    (3, [1000], [10, 10, 10], [2, 2, 4], [2, 8, 8, 1], tt.TT_EMB_ERR_ARG),             # K = 3 -> 3-core checks
+    (4, [1000], [5, 5, 5, 8], [2, 2, 2, 2], [2, 8, 8, 8, 1], tt.TT_EMB_ERR_ARG),       # R0 != 1
+    (4, [1000], [5, 5, 5, 8], [2, 2, 2, 2], [1, 8, 8, 8, 3], tt.TT_EMB_ERR_ARG),       # RK != 1
+    (4, [1001], [5, 5, 5, 8], [2, 2, 2, 2], [1, 8, 8, 8, 1], tt.TT_EMB_ERR_ARG),       # prod n < N
+    (4, [1000], [5, 5, 5, 8], [2, 0, 2, 2], [1, 8, 8, 8, 1], tt.TT_EMB_ERR_ARG),       # zero dim
+    (4, [1000], [5, 5, 5, 8], [8, 8, 8, 4], [1, 8, 8, 8, 1], tt.TT_EMB_ERR_UNSUPPORTED),  # D > 1024
+    (4, [1000], [5, 5, 5, 8], [2, 2, 2, 2], [1, 8, 300, 8, 1], tt.TT_EMB_ERR_UNSUPPORTED),  # rank > 256
+    (4, [1000], [5, 5, 5, 8], [16, 4, 4, 4], [1, 8, 256, 8, 1], tt.TT_EMB_ERR_UNSUPPORTED),  # LDS
+])
+def test_create_k_rejects_bad_shapes_before_touching_the_device(K, N, n, d, R, code):
+    rc, h = _create_k(K, N, n, d, R)
+    assert rc == code
+    assert not h.value
+
+
 def test_create_rejects_bad_options():
     opt = tt.tt_emb_options()
     opt.sched_mode = 7

@@ -430,3 +430,103 @@ def test_full_size_training_step_sampled_slices(keep):
             scale = np.abs(r).max()
             assert scale > 0
             assert np.abs(g - r).max() <= TOL * scale, (t, k)
+
+
+# ------------------------------------------------------ K >= 4 TT cores
+
+def _three_digit_view(w):
+    """The same lookups over tables whose rows split into (1, leading K-1
+    digits, last digit): the grouping a K-core table set is sorted by."""
+    tabs = []
+    for t in w.tables:
+        lead = int(np.prod(t.n[:-1]))
+        tabs.append(W.Table(t.N, (1, lead, t.n[-1]), (1, 1, t.D), (1, 1, 1, 1), t.sigma, t.dist, t.alpha))
+    return W.Workload(name=w.name + "_view", tables=tabs, B=w.B, cores=[], indices=w.indices,
+                      offsets=w.offsets)
+
+
+def _sub_bags(w, bags):
+    """The lookups of the chosen bags of every table, as a workload of its own."""
+    lens, idx = [], []
+    for t in range(w.T):
+        lo = w.offsets[t * w.B + bags]
+        hi = w.offsets[t * w.B + bags + 1]
+        lens.append(hi - lo)
+        idx.append(np.concatenate([w.indices[a:b] for a, b in zip(lo, hi)]) if len(bags) else
+                   np.zeros(0, np.int64))
+    off = np.zeros(w.T * len(bags) + 1, np.int64)
+    np.cumsum(np.concatenate(lens), out=off[1:])
+    return W.Workload(name=w.name + "_sub", tables=w.tables, B=len(bags), cores=w.cores,
+                      indices=np.concatenate(idx), offsets=off)
+
+
+def _check_kcore(w, run):
+    out = run.forward().cpu().numpy()
+    assert out.shape == (w.B, w.sum_D)
+    assert_out_close(w, out, oracle.forward_k(w))
+    ref = oracle.grouping(_three_digit_view(w))
+    got = run.grouping()
+    for k in ref:
+        assert np.array_equal(got[k], ref[k]), k
+    return out
+
+
+@pytest.mark.parametrize("name,bags", [("k4", 256), ("k5", 256), ("k4", 3)])
+def test_kcore_forward_matches_oracle(name, bags):
+    w = W.make_kcore_workload(name, bags=bags)
+    run = Run(w)
+    out = _check_kcore(w, run)
+    # bit-reproducible, and the same again from the kept grouping
+    assert np.array_equal(out, run.forward().cpu().numpy())
+    assert np.array_equal(out, run.forward(flags=tt.TT_EMB_REUSE_GROUPING).cpu().numpy())
+
+
+def test_kcore_mixed_shapes_empty_bags_and_no_lookups():
+    # K = 4 tables of unequal ranks and widths: a wide row (D = 512), ranks
+    # that are no MFMA class, a table with a single leading prefix, empty bags
+    tables = [W.Table(5000, (4, 5, 6, 50), (4, 4, 4, 8), (1, 8, 24, 12, 1), 0.2, "uniform"),
+              W.Table(77, (2, 3, 2, 7), (3, 1, 2, 5), (1, 5, 3, 7, 1), 0.3, "uniform"),
+              W.Table(999, (10, 10, 10, 1), (2, 2, 2, 2), (1, 16, 16, 16, 1), 0.2, "uniform"),
+              W.Table(40000, (20, 20, 20, 5), (2, 4, 4, 4), (1, 32, 32, 32, 1), 0.05, "zipf", 1.1)]
+    rng = np.random.default_rng(41)
+    lens = [rng.integers(0, 12, size=50) for _ in tables]
+    lens[1][:] = 0
+    lens[2][5:] = 0
+    idx = [rng.integers(0, t.N, size=int(l.sum())) for t, l in zip(tables, lens)]
+    idx[0][: len(idx[0]) // 2] = 4321  # one hot row
+    idx[3] = np.minimum(idx[3], 37)    # a single leading prefix (rows 0..37)
+    w = W.make_custom(tables, lens, idx, seed=41)
+    run = Run(w)
+    out = _check_kcore(w, run)
+    col = w.col_offsets()
+    assert not out[:, col[1]:col[2]].any()
+    assert not out[5:, col[2]:col[3]].any()
+    w0 = W.make_custom(tables[:2], [np.zeros(4, np.int64)] * 2, [np.zeros(0, np.int64)] * 2, seed=42)
+    run0 = Run(w0)
+    out0 = run0.forward().cpu().numpy()
+    assert out0.shape == (4, w0.sum_D) and not out0.any()
+
+
+def test_kcore_full_size_sampled_bags():
+    w = W.make_kcore_workload("k4")
+    run = Run(w)
+    out = run.forward().cpu().numpy()
+    rng = np.random.default_rng(44)
+    bags = np.unique(np.concatenate([[0, w.B - 1], rng.integers(0, w.B, 300)]))
+    sub = _sub_bags(w, bags)
+    assert_out_close(sub, out[bags], oracle.forward_k(sub))
+
+
+def test_kcore_unsupported_calls_are_rejected():
+    w = W.make_kcore_workload("k5", bags=8)
+    run = Run(w)
+    with pytest.raises(tt.TTEmbError) as e:
+        run.forward(flags=tt.TT_EMB_KEEP_PREFIX)
+    assert e.value.status == tt.TT_EMB_ERR_ARG
+    with pytest.raises(tt.TTEmbError) as e:
+        run.forward(flags=tt.TT_EMB_ATOMIC_POOL)
+    assert e.value.status == tt.TT_EMB_ERR_ARG
+    run.forward()
+    with pytest.raises(tt.TTEmbError) as e:
+        run.backward(np.zeros((w.B, w.sum_D), np.float32))
+    assert e.value.status == tt.TT_EMB_ERR_UNSUPPORTED
