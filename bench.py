@@ -266,6 +266,15 @@ class Bench:
         assert self.emb.poll_error() == 0
         return ev0.elapsed_time(ev1) / steps, wall, phases
 
+    def balance(self):
+        tt = self.tt
+        out = {}
+        for k in tt.BLOCK_STAT_KERNELS:
+            r = tt.block_balance(self.emb.block_stats(self.w.B, self.w.nnz, k))
+            if r is not None:
+                out[k] = r
+        return out
+
     def counts(self):
         g = self.emb.grouping(self.w.B, self.w.nnz)
         tu = g["tab_uniq_start"].cpu().numpy()
@@ -317,6 +326,34 @@ def cpu_baseline(w, target_s=12.0):
                       f"{kind}, per-index fp64, {t:.1f} s"}
 
 
+def run_ablation(args, torch, tt, W):
+    """The scheduling / reuse ablation of the FlowTT evaluation (static prefix
+    mapping, persistent blocks with stealing, stealing plus L2 checkpoints;
+    prefix reuse against unique-row-only reuse) on the 26-table forward at
+    batch 32768: latency normalised to the static mode, and how evenly each
+    persistent launch spread over blocks and compute units."""
+    w = W.make_workload(4)
+    modes = [("static", 1, 1), ("steal", 2, 1), ("steal_l2", 3, 1), ("steal_l2_unique_only", 3, 2)]
+    res = {}
+    for name, sched, group in modes:
+        o = tt.tt_emb_options()
+        o.sched_mode, o.group_mode = sched, group
+        bf = Bench(w, torch, tt, o)
+        fms, _, fph = bf.timed(bf.fwd, args.steps, args.warmup)
+        fphase, fkern, _ = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in fph.items() if v[1]})
+        _, _, _, fc = bf.counts()
+        res[name] = {"ms": round(fms, 4), "contract_ms": fphase.get("contract"), "kernels_ms": fkern,
+                     "sched_stats": fc, "balance": bf.balance()}
+        del bf
+        torch.cuda.empty_cache()
+    base, cbase = res["static"]["ms"], res["static"]["contract_ms"]
+    for r in res.values():
+        r["norm_latency"] = round(r["ms"] / base, 4)
+        r["norm_contract"] = round(r["contract_ms"] / cbase, 4) if cbase else None
+    print(json.dumps({"mode": "ablation", "workload": W.CONFIG_NAMES[4], "nnz": w.nnz, "steps": args.steps,
+                      "results": res}), flush=True)
+
+
 def run_sweep(args, torch, tt, W, opts):
     """Batch sweep on the 26-table shapes (same tables, bag-length law and
     index laws as the training workload, B bags per table): training step
@@ -365,12 +402,13 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
     ap.add_argument("--sched", type=int, default=0, help="0 default, 1 static, 2 steal, 3 steal+L2")
     ap.add_argument("--group", type=int, default=0, help="0 default, 1 prefix, 2 unique-only")
-    ap.add_argument("--mode", default="train", choices=("train", "fwd", "copy", "traffic", "sweep", "kcores"),
+    ap.add_argument("--mode", default="train", choices=("train", "fwd", "copy", "traffic", "sweep", "kcores", "ablation"),
                     help="train: the full step (default); fwd: forward only on --config; "
                          "copy: a plain 1 GiB device copy (counter calibration); "
                          "traffic: turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json; "
                          "sweep: training step and forward over --batches on the 26-table shapes; "
-                         "kcores: forward of the 4- and 5-core 10^7-row tables")
+                         "kcores: forward of the 4- and 5-core 10^7-row tables; "
+                         "ablation: the 26-table forward under each scheduling and grouping mode")
     ap.add_argument("--pmc-dir", default="gpurun_out/m",
                     help="traffic: directory with the fetch/, write/, cfetch/, cwrite/ counter runs")
     ap.add_argument("--config", type=int, default=4, help="workload of --mode fwd (1..4)")
@@ -417,6 +455,10 @@ def main():
 
     if args.mode == "sweep":
         run_sweep(args, torch, tt, W, opts)
+        return
+
+    if args.mode == "ablation":
+        run_ablation(args, torch, tt, W)
         return
 
     if args.mode == "kcores":
@@ -468,6 +510,8 @@ def main():
                 "traffic": load_traffic(dom, wl, kernel_sources_sha(["forward.hip", "internal.h"]))}
     kernels = {k: {"ms": round(v, 4), "tflops": round(kflops[k] / (v * 1e-3) / 1e12, 2) if k in kflops else None}
                for k, v in sorted(kern_ms.items(), key=lambda kv: -kv[1])}
+    # how evenly the last step's persistent launches spread over blocks and CUs
+    balance = b.balance()
     res = {
         "metric": METRIC, "value": value, "unit": "lookups/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -482,6 +526,7 @@ def main():
         "kernels": kernels,
         "flops": {"fwd_contract": F_fwd, "bwd_contract": F_bwd, "pool_adds": F_pool},
         "sched_stats": cnt,
+        "balance": balance,
         "roofline": roof,
     }
     del b

@@ -209,6 +209,31 @@ int tt_emb_sgd_update(tt_emb_t h, float *const *cores, const float *const *core_
 int tt_emb_grouping_view(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B, int64_t nnz,
                          void *stream, tt_emb_grouping *view);
 
+/* Per-block scheduling records of the persistent matrix-core kernels: the
+ * evidence for how evenly the work-stealing scheduler (FlowTT section 3.4,
+ * persistent blocks with chunk stealing; section 4 reports the load
+ * imbalance it removes) spreads one launch over blocks and compute units.
+ * kernel: 0..3 = forward contraction of the rank-8/16/32/64 tables,
+ * 4..7 = backward contraction of the same classes.  Each record holds the
+ * block's start and end on the device's constant-rate wall clock
+ * (t_start, t_end in ticks of *clock_khz kHz), the chunks (forward) or
+ * (table, i2) runs (backward) it processed (work), the unique rows
+ * (forward) or chunks (backward) in them (rows), the compute unit it ran on
+ * (cu: xcc id << 7 | shader engine << 5 | cu id << 1 | shader array) and
+ * the grid size.
+ * Synchronises the stream, then copies min(grid, cap, 2048) records of the
+ * last launch of that kernel on this workspace into the host array out
+ * (caller-owned) and sets *nblocks to that count (0 when the last forward
+ * (kernels 0..3) or backward (4..7) on ws did not launch it).  Tools and
+ * tests only; TT_EMB_ERR_ARG for a bad kernel id or null pointers. */
+typedef struct {
+    int64_t t_start, t_end;
+    int32_t work, rows, cu, grid;
+} tt_emb_block_stat;
+int tt_emb_block_stats(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B, int64_t nnz, int32_t kernel,
+                       void *stream, tt_emb_block_stat *out, int32_t cap, int32_t *nblocks,
+                       int64_t *clock_khz);
+
 /* Synchronise the stream and report a device-detected error recorded in ws
  * since the last grouping (TT_EMB_OK, TT_EMB_ERR_INDEX or TT_EMB_ERR_OFFSETS). */
 int tt_emb_poll_error(tt_emb_t h, const void *ws, void *stream);

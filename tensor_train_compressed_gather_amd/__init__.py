@@ -36,7 +36,9 @@ EXPORTED = (
     "tt_emb_create", "tt_emb_create_k", "tt_emb_destroy", "tt_emb_workspace_size", "tt_emb_group", "tt_emb_forward",
     "tt_emb_backward", "tt_emb_sgd_update", "tt_emb_grouping_view", "tt_emb_poll_error",
     "tt_emb_status_string", "tt_emb_timing_enable", "tt_emb_timing_read", "tt_emb_timer_name",
+    "tt_emb_block_stats",
 )
+BLOCK_STAT_KERNELS = ("fwd_r8", "fwd_r16", "fwd_r32", "fwd_r64", "bwd_r8", "bwd_r16", "bwd_r32", "bwd_r64")
 TIMER_NAMES = ("group_sort", "group_rle", "contract", "pool", "bwd_gather", "bwd_contract",
                "bwd_reduce", "sgd", "fwd_r8", "fwd_r16", "fwd_r32", "fwd_r64",
                "bwd_r8", "bwd_r16", "bwd_r32", "bwd_r64",
@@ -57,6 +59,11 @@ class tt_emb_grouping(C.Structure):
                 ("num_units", C.c_int64), ("num_tiles", C.c_int64), ("num_chunks", C.c_int64),
                 ("num_split_tiles", C.c_int64), ("num_steals", C.c_int64),
                 ("num_ckpt_hits", C.c_int64), ("num_ckpt_misses", C.c_int64)]
+
+
+class tt_emb_block_stat(C.Structure):
+    _fields_ = [("t_start", C.c_int64), ("t_end", C.c_int64), ("work", C.c_int32), ("rows", C.c_int32),
+                ("cu", C.c_int32), ("grid", C.c_int32)]
 
 
 _lib = None
@@ -83,6 +90,7 @@ def lib():
             L.tt_emb_sgd_update.argtypes = [p, p, p, C.c_float, p]
             L.tt_emb_grouping_view.argtypes = [p, p, C.c_size_t, i64, i64, p, C.POINTER(tt_emb_grouping)]
             L.tt_emb_poll_error.argtypes = [p, p, p]
+            L.tt_emb_block_stats.argtypes = [p, p, C.c_size_t, i64, i64, i32, p, p, i32, p, p]
             L.tt_emb_status_string.argtypes = [C.c_int]
             L.tt_emb_status_string.restype = C.c_char_p
             L.tt_emb_timing_enable.argtypes = [p, i32]
@@ -233,6 +241,64 @@ def tt_emb_grouping_view(h, ws, B: int, nnz: int, T: int, stream=None) -> dict:
     }
 
 
+def tt_emb_block_stats(h, ws, B: int, nnz: int, kernel, stream=None):
+    """Per-block records of the last launch of a persistent matrix-core kernel
+    (kernel: index or name in BLOCK_STAT_KERNELS) as numpy arrays (t0, t1 in
+    microseconds from the earliest start, work, rows, cu); None when it did
+    not run.  Synchronises the stream."""
+    import numpy as np
+
+    k = BLOCK_STAT_KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    cap = 2048
+    recs = (tt_emb_block_stat * cap)()
+    n = C.c_int32()
+    khz = C.c_int64()
+    rc = lib().tt_emb_block_stats(h, _ptr(ws), ws.numel(), int(B), int(nnz), k, _stream(stream), recs, cap,
+                                  C.byref(n), C.byref(khz))
+    _check(rc, "tt_emb_block_stats")
+    if n.value == 0:
+        return None
+    m = n.value
+    t0 = np.array([recs[i].t_start for i in range(m)], dtype=np.int64)
+    t1 = np.array([recs[i].t_end for i in range(m)], dtype=np.int64)
+    us = 1e3 / float(khz.value)
+    base = t0.min()
+    return {"t0_us": (t0 - base) * us, "t1_us": (t1 - base) * us,
+            "work": np.array([recs[i].work for i in range(m)], dtype=np.int64),
+            "rows": np.array([recs[i].rows for i in range(m)], dtype=np.int64),
+            "cu": np.array([recs[i].cu for i in range(m)], dtype=np.int64),
+            "grid": int(recs[0].grid), "clock_khz": int(khz.value)}
+
+
+def block_balance(st) -> dict | None:
+    """Load-balance summary of one launch's per-block records (host logic).
+
+    eff_blocks = total block busy time / (blocks x launch span): 1.0 when
+    every block works until the launch ends; eff_cus = the same over compute
+    units (busy time of the blocks a CU ran, against the busiest CU);
+    work_max_over_mean / rows_max_over_mean = how unevenly the chunks and
+    rows were handed out."""
+    if st is None:
+        return None
+    import numpy as np
+
+    t0, t1 = st["t0_us"], st["t1_us"]
+    busy = t1 - t0
+    span = float(t1.max() - t0.min())
+    n = len(busy)
+    cus, inv = np.unique(st["cu"], return_inverse=True)
+    cu_busy = np.bincount(inv, weights=busy)
+    work, rows = st["work"].astype(np.float64), st["rows"].astype(np.float64)
+    return {"blocks": n, "cus": int(len(cus)), "span_us": round(span, 2),
+            "eff_blocks": round(float(busy.sum() / (n * span)), 4) if span > 0 else None,
+            "eff_cus": round(float(cu_busy.mean() / cu_busy.max()), 4) if cu_busy.max() > 0 else None,
+            "busy_us_min_mean_max": [round(float(busy.min()), 2), round(float(busy.mean()), 2),
+                                     round(float(busy.max()), 2)],
+            "start_spread_us": round(float(t0.max() - t0.min()), 2),
+            "work_max_over_mean": round(float(work.max() / work.mean()), 3) if work.mean() > 0 else None,
+            "rows_max_over_mean": round(float(rows.max() / rows.mean()), 3) if rows.mean() > 0 else None}
+
+
 def tt_emb_timing_enable(h, enable: bool = True):
     _check(lib().tt_emb_timing_enable(h, 1 if enable else 0), "tt_emb_timing_enable")
 
@@ -312,6 +378,9 @@ class TTEmbeddingBag:
 
     def grouping(self, B: int, nnz: int, stream=None) -> dict:
         return tt_emb_grouping_view(self.handle, self._ws, B, nnz, self.T, stream)
+
+    def block_stats(self, B: int, nnz: int, kernel, stream=None):
+        return tt_emb_block_stats(self.handle, self._ws, B, nnz, kernel, stream)
 
     def close(self):
         if self.handle is not None:

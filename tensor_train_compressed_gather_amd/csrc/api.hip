@@ -152,6 +152,7 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     const int64_t part_elems = tasks * 2 * h->Dpmax;
     w.E = (float *)take(4 * e_elems);
     w.sink = (float *)take(4 * (size_t)kSinkFloats);
+    w.bstat = (BlockStat *)take(sizeof(BlockStat) * (size_t)kStatKernels * kStatBlocks);
     w.cbase = (int64_t *)take(8 * T);
     // kept prefix intermediates (keep_prefix handles only): 16 x R2 floats per
     // unit of every table of the kept rank classes, at most min(units of the
@@ -747,6 +748,32 @@ int tt_emb_grouping_view(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B,
     view->num_steals = ctrl[CTRL_STEALS];
     view->num_ckpt_hits = ctrl[CTRL_CKPT_HIT];
     view->num_ckpt_misses = ctrl[CTRL_CKPT_MISS];
+    return TT_EMB_OK;
+}
+
+int tt_emb_block_stats(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B, int64_t nnz, int32_t kernel,
+                       void *stream, tt_emb_block_stat *out, int32_t cap, int32_t *nblocks, int64_t *clock_khz)
+{
+    static_assert(sizeof(tt_emb_block_stat) == sizeof(BlockStat), "public block record mirrors BlockStat");
+    if (!out || !nblocks || !clock_khz || cap < 0 || kernel < 0 || kernel >= kStatKernels) return TT_EMB_ERR_ARG;
+    Plan p;
+    int64_t dummy_off[1] = {0};
+    int rc = check_call(h, B, nnz, nnz > 0 ? dummy_off : nullptr, dummy_off, const_cast<void *>(ws), ws_bytes, &p);
+    if (rc) return rc;
+    if ((rc = set_device(h))) return rc;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TT_EMB_ERR_HIP;
+    int rate = 0;
+    if (hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, h->device) != hipSuccess) return TT_EMB_ERR_HIP;
+    *clock_khz = rate;
+    const BlockStat *src = p.ws.bstat + (size_t)kernel * kStatBlocks;
+    BlockStat first;
+    if (hipMemcpy(&first, src, sizeof(first), hipMemcpyDeviceToHost) != hipSuccess) return TT_EMB_ERR_HIP;
+    int n = first.nb < 0 ? 0 : first.nb;
+    if (n > kStatBlocks) n = kStatBlocks;
+    if (n > cap) n = cap;
+    *nblocks = n;
+    if (n > 0 && hipMemcpy(out, src, sizeof(BlockStat) * (size_t)n, hipMemcpyDeviceToHost) != hipSuccess)
+        return TT_EMB_ERR_HIP;
     return TT_EMB_OK;
 }
 

@@ -596,6 +596,9 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
     __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
     __shared__ ChunkRec recs[3]; // records of chunks c, c+1 and (arriving) c+2
     __shared__ int s_run;
+    __shared__ long long s_t0;
+    if (threadIdx.x == 0) s_t0 = wall_clock64();
+    int nwork = 0, nchunks = 0; // scheduling record (thread 0)
     // Cs holds C during a tile and dC at its end (C is dead by then); dT holds
     // dC transposed ([col][(g, j1)]) for the dG1 partials
     float *G2s = lds, *Cs = lds + L::G2S, *dT = Cs + L::CS, *G1s = dT + L::CS, *Sg = G1s + L::G1S;
@@ -611,6 +614,10 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
         const int run = s_run;
         if (run >= rend) break;
         const int c0 = ws.tile_cstart[ws.run_tile_start[run]], c1 = ws.tile_cstart[ws.run_tile_start[run + 1]];
+        if (tid == 0) {
+            ++nwork;
+            nchunks += c1 - c0;
+        }
         if (w == 0) {
             reinterpret_cast<int *>(&recs[0])[lane] = reinterpret_cast<const int *>(&ws.crec[c0])[lane];
             if (c0 + 1 < c1)
@@ -1068,6 +1075,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
         }
         __syncthreads();
     }
+    if (tid == 0) block_stat_write(ws.bstat + (4 + L::CLS) * kStatBlocks, s_t0, nwork, nchunks);
 }
 
 // Run-class boundaries (runs are class-major like the units) and counters.
@@ -1088,7 +1096,10 @@ __global__ void k_bwd_prep(BwdArgs a)
         ws.ctrl[CTRL_RUN_CLS + c] = lo;
     }
     if (c == 5) ws.ctrl[CTRL_RUN_CLS + 5] = nruns;
-    if (c < 4) ws.ctrl[CTRL_BWD_NEXT + c] = 0;
+    if (c < 4) {
+        ws.ctrl[CTRL_BWD_NEXT + c] = 0;
+        ws.bstat[(4 + c) * kStatBlocks].nb = 0; // backward class records
+    }
 }
 
 // Transposed G3 copies of the MFMA-class tables (G3t[i3][j3][r2]).

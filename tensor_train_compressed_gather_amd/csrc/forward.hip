@@ -105,6 +105,7 @@ __global__ __launch_bounds__(kThreads) void k_queue_init(Ws ws, ClassGrid g, int
             ws.heads[(c * stride + b) * kHeadPad] = cstart[c] + range_begin(b, cstart[c + 1] - cstart[c], g.nb[c]);
     for (int i = threadIdx.x; i < split; i += blockDim.x) ws.flags[i] = 0;
     if (threadIdx.x < 5) ws.ctrl[CTRL_CLS_START + threadIdx.x] = cstart[threadIdx.x];
+    if (threadIdx.x < 4) ws.bstat[threadIdx.x * kStatBlocks].nb = 0; // forward class records
     if (threadIdx.x == 0) {
         ws.ctrl[CTRL_STEALS] = 0;
         ws.ctrl[CTRL_CKPT_HIT] = 0;
@@ -555,6 +556,8 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
     __shared__ __attribute__((aligned(16))) float Es[FwdCfg<R>::ES];
     __shared__ ChunkRec rbuf[2];
     __shared__ int s_cur, s_next, s_next2, s_flag;
+    __shared__ long long s_t0;
+    if (threadIdx.x == 0) s_t0 = wall_clock64();
     const int lane = threadIdx.x & 63, w = uni(threadIdx.x >> 6); // wave index, in a scalar register
     const int nb = gridDim.x, me = blockIdx.x;
     const Ws &ws = a.ws;
@@ -565,7 +568,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
     float breg[FwdCfg<R>::BREG], apf[R / 4], bq[fwd_nq<R, KEEP>()][R / 4];
 #pragma unroll
     for (int i = 0; i < FwdCfg<R>::BREG; ++i) breg[i] = 0.f;
-    int bkey = -1, lds_tile = -1, vi = 0, steals = 0, hits = 0, misses = 0;
+    int bkey = -1, lds_tile = -1, vi = 0, steals = 0, hits = 0, misses = 0, nwork = 0, nrows = 0;
     // wave 0 runs the claims two chunks ahead: chunk c+2 is claimed while
     // chunk c runs, and the record of chunk c+1 is loaded at the end of chunk c-1
     int pre = 0, raw = 0x7fffffff, c2w = -1;
@@ -615,6 +618,8 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
                           pre, hits, misses, c, cn, mid, endc);
             __syncthreads(); // everyone is done with rbuf[buf], s_cur and s_next
             if (threadIdx.x == 0) {
+                ++nwork;
+                nrows += rbuf[buf].rend - rbuf[buf].rbeg;
                 s_cur = cn;
                 s_next = s_next2;
             }
@@ -622,8 +627,9 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
             buf ^= 1;
         }
     }
-    // scheduling statistics, one atomic per block
+    // scheduling statistics, one atomic per block, and the block's record
     if (threadIdx.x == 0) {
+        block_stat_write(ws.bstat + CLS * kStatBlocks, s_t0, nwork, nrows);
         if (steals) atomicAdd(&ws.ctrl[CTRL_STEALS], steals);
         if (hits) atomicAdd(&ws.ctrl[CTRL_CKPT_HIT], hits);
         if (misses) atomicAdd(&ws.ctrl[CTRL_CKPT_MISS], misses);

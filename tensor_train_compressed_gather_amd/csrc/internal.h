@@ -86,6 +86,20 @@ struct ChunkRec {
 };
 static_assert(sizeof(ChunkRec) == 256, "chunk record is one 256-byte line");
 
+// Per-block record of the persistent matrix-core kernels (scheduling
+// evidence: how the work of one launch spread over blocks and compute units).
+// Kernel slots 0..3 are the forward rank classes, 4..7 the backward ones.
+constexpr int kStatKernels = 8;
+constexpr int kStatBlocks = 2048; // blocks past this many leave no record
+struct BlockStat {
+    int64_t t0, t1;  // wall clock (constant-rate counter) at block start / end
+    int32_t work;    // chunks (forward) or (table, i2) runs (backward) processed
+    int32_t rows;    // unique rows computed (forward) or chunks (backward)
+    int32_t cu;      // compute unit the block ran on (XCC, SE and CU ids)
+    int32_t nb;      // grid size of the launch; entry 0 is cleared before each launch
+};
+static_assert(sizeof(BlockStat) == 32, "block record is 32 bytes");
+
 struct CorePtrs {
     const float *g[kMaxTables][3];
 };
@@ -141,6 +155,7 @@ struct Ws {
     float *Cg;               // kept prefix intermediates: [work position][16][R2] per table (keep_prefix)
     int64_t *cbase;          // [T] offset of table t's units in Cg, minus tab_unit_start[t]*16*R2
     float *sink;             // [kSinkFloats] scratch target of stores that carry no result
+    BlockStat *bstat;        // [kStatKernels][kStatBlocks] per-block scheduling records
     // backward
     int2 *lk;                // [nnz] (bag within its table, unique row) of each lookup
     int32_t *gu_ml;          // [gather tasks] unique row of the run cut at the task's left edge, or -1

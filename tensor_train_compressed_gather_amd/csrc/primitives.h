@@ -20,6 +20,25 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T *kconst(con
     return (const __attribute__((address_space(4))) T *)p;
 }
 
+// Scheduling record of one persistent block (thread 0 only): start and end
+// on the constant-rate wall clock, work done, the compute unit it ran on
+// (xcc, shader engine, cu and shader-array ids) and the grid size.  Plain
+// vector stores.
+__device__ __forceinline__ void block_stat_write(BlockStat *slot, int64_t t0, int work, int rows)
+{
+    if (blockIdx.x >= (unsigned)kStatBlocks) return;
+    BlockStat r;
+    r.t0 = t0;
+    r.t1 = wall_clock64();
+    r.work = work;
+    r.rows = rows;
+    // __smid() = xcc << 6 | se << 4 | cu; the shader-array bit (HW_ID bit 12)
+    // is appended so that CUs of the two arrays of an engine stay apart
+    r.cu = (int32_t)((__smid() << 1) | __builtin_amdgcn_s_getreg(GETREG_IMMED(0, 12, HW_ID)));
+    r.nb = (int32_t)gridDim.x;
+    slot[blockIdx.x] = r;
+}
+
 // Inclusive scan inside one 64-lane wave.
 template <class T>
 __device__ __forceinline__ T wave_inclusive_scan(T x)

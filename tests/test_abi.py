@@ -142,3 +142,15 @@ def test_product_path_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "tt_oracle" not in text and "liboracle" not in text, f
+
+
+def test_block_balance_summary():
+    # host-side summary of per-block records: two CUs, one busy twice as long
+    st = {"t0_us": np.array([0.0, 0.0, 0.0, 0.0]), "t1_us": np.array([10.0, 10.0, 5.0, 5.0]),
+          "work": np.array([4, 4, 2, 2]), "rows": np.array([8, 8, 4, 4]), "cu": np.array([1, 1, 2, 2])}
+    b = tt.block_balance(st)
+    assert b["blocks"] == 4 and b["cus"] == 2 and b["span_us"] == 10.0
+    assert b["eff_blocks"] == 0.75          # 30 busy of 40 block-microseconds
+    assert b["eff_cus"] == 0.75             # CU busy 20 and 10: mean 15 over max 20
+    assert b["work_max_over_mean"] == round(4 / 3, 3) and b["rows_max_over_mean"] == round(8 / 6, 3)
+    assert tt.block_balance(None) is None

@@ -253,6 +253,43 @@ def test_kernel_timers_record_every_launch():
     assert ph["contract"][1] == 3 and ph["bwd_contract"][1] == 3
 
 
+@pytest.mark.parametrize("sched", [1, 3])
+def test_block_records_account_for_every_chunk(sched):
+    # the per-block scheduling records: one per block of each persistent
+    # launch, and between them every forward chunk and unique row (each is
+    # computed exactly once) and every backward chunk
+    w = W.make_workload(5, bags=64)
+    run = Run(w, sched_mode=sched)
+    run.forward()
+    run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)
+    cnt = run.grouping()["counts"]
+    ranks = {t.R[1] for t in w.tables}
+    fwork = frows = bchunks = 0
+    for r in (8, 16, 32, 64):
+        for p in ("fwd", "bwd"):
+            st = run.emb.block_stats(w.B, w.nnz, f"{p}_r{r}")
+            assert (st is not None) == (r in ranks), (p, r)
+            if st is None:
+                continue
+            n = len(st["work"])
+            assert n == st["grid"] and n >= 256, (p, r, n)
+            assert np.all(st["t1_us"] >= st["t0_us"]) and st["clock_khz"] > 0
+            assert np.all(st["work"] >= 0) and np.all(st["rows"] >= 0)
+            # hardware ids decode into at most 8 XCDs of 4 engines
+            assert np.all((st["cu"] >> 7) < 8)
+            if p == "fwd":
+                fwork += int(st["work"].sum())
+                frows += int(st["rows"].sum())
+            else:
+                bchunks += int(st["rows"].sum())
+            bal = tt.block_balance(st)
+            assert 0 < bal["eff_blocks"] <= 1 and 0 < bal["eff_cus"] <= 1
+    assert fwork == cnt["num_chunks"] and bchunks == cnt["num_chunks"]
+    assert frows == cnt["num_unique"]
+    with pytest.raises(tt.TTEmbError):
+        run.emb.block_stats(w.B, w.nnz, 8)
+
+
 def test_bit_reproducible_forward_and_backward():
     w = W.make_workload(5, bags=64)
     run = Run(w)
