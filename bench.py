@@ -168,6 +168,52 @@ def write_traffic(d):
     print(json.dumps(out, indent=1, sort_keys=True))
 
 
+COUNTER_KERNELS = (("k_contract<16", "fwd_r16"), ("k_contract<32", "fwd_r32"), ("k_contract<64", "fwd_r64"),
+                   ("k_bwd_class<16", "bwd_r16"), ("k_bwd_class<32", "bwd_r32"), ("k_bwd_class<64", "bwd_r64"),
+                   ("k_pool(", "pool"), ("k_gu_gather", "bwd_gather"))
+
+
+def write_counters(d, trace_csv=None):
+    """Per-kernel hardware counters of the training step from two rocprofv3
+    --pmc runs (lds/: LdsBankConflict = bank-conflict cycles per conflict-free
+    indexed LDS cycle, SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE; mfma/: MfmaUtil =
+    % of SIMD cycles the matrix core is busy, MfmaFlopsF32 = fp32 MFMA flops
+    issued), averaged over the dispatches of each kernel, as a markdown table.
+    With the kernel-trace csv, issued flops are also divided by the average
+    launch duration."""
+    import csv
+
+    vals = {}
+    for sub in ("lds", "mfma"):
+        with open(os.path.join(d, sub, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    dur = {}
+    if trace_csv and os.path.exists(trace_csv):
+        with open(trace_csv) as f:
+            for r in csv.DictReader(f):
+                dur.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+
+    def avg(sym, counter):
+        xs = [v for (k, c), vs in vals.items() if sym in k and c == counter for v in vs]
+        return sum(xs) / len(xs) if xs else None
+
+    rows = []
+    for sym, name in COUNTER_KERNELS:
+        ds = [v for k, vs in dur.items() if sym in k for v in vs]
+        t = sum(ds) / len(ds) if ds else None
+        fl = avg(sym, "MfmaFlopsF32")
+        rows.append({"kernel": name, "lds_bank_conflict_ratio": avg(sym, "LdsBankConflict"),
+                     "lds_conflict_cycles": avg(sym, "SQ_LDS_BANK_CONFLICT"),
+                     "lds_active_cycles": avg(sym, "SQ_LDS_IDX_ACTIVE"),
+                     "mfma_util_pct": avg(sym, "MfmaUtil"), "mfma_f32_flops": fl,
+                     "launch_ms": t * 1e3 if t else None,
+                     "mfma_issued_tflops": fl / t / 1e12 if (fl and t) else None})
+    print(json.dumps(rows, indent=1))
+    return rows
+
+
 def kcore_flops(tables, indices, offsets, B):
     """Contraction flops of the K-core forward with prefix reuse at every
     length (one intermediate per distinct prefix of length 2..K-1, one last
@@ -333,7 +379,8 @@ def run_ablation(args, torch, tt, W):
     batch 32768: latency normalised to the static mode, and how evenly each
     persistent launch spread over blocks and compute units."""
     w = W.make_workload(4)
-    modes = [("static", 1, 1), ("steal", 2, 1), ("steal_l2", 3, 1), ("steal_l2_unique_only", 3, 2)]
+    modes = [("static", 1, 1), ("steal", 2, 1), ("steal_l2", 3, 1), ("default", 0, 1),
+             ("default_unique_only", 0, 2)]
     res = {}
     for name, sched, group in modes:
         o = tt.tt_emb_options()
@@ -402,10 +449,12 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
     ap.add_argument("--sched", type=int, default=0, help="0 default, 1 static, 2 steal, 3 steal+L2")
     ap.add_argument("--group", type=int, default=0, help="0 default, 1 prefix, 2 unique-only")
-    ap.add_argument("--mode", default="train", choices=("train", "fwd", "copy", "traffic", "sweep", "kcores", "ablation"),
+    ap.add_argument("--mode", default="train", choices=("train", "fwd", "copy", "traffic", "counters", "sweep", "kcores",
+                                                     "ablation"),
                     help="train: the full step (default); fwd: forward only on --config; "
                          "copy: a plain 1 GiB device copy (counter calibration); "
                          "traffic: turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json; "
+                         "counters: summarise the LDS bank-conflict and MFMA-utilisation counter runs; "
                          "sweep: training step and forward over --batches on the 26-table shapes; "
                          "kcores: forward of the 4- and 5-core 10^7-row tables; "
                          "ablation: the 26-table forward under each scheduling and grouping mode")
@@ -426,6 +475,9 @@ def main():
 
     if args.mode == "traffic":
         write_traffic(args.pmc_dir)
+        return
+    if args.mode == "counters":
+        write_counters(args.pmc_dir, os.path.join(args.pmc_dir, "trace", "run_kernel_trace.csv"))
         return
 
     import torch
@@ -553,6 +605,7 @@ def main():
                 "roofline_ms_fp32": ff / (PEAK_FP32_TFLOPS * 1e12) * 1e3,
                 "post_grouping_frac_of_roofline": (ff / (PEAK_FP32_TFLOPS * 1e12) * 1e3) / post if post else None,
                 "sched_stats": fc,
+                "balance": bf.balance(),
             }
             # the non-deterministic fast mode: pooling fused into the contraction
             ums, _, uph = bf.timed(bf.fwd_fused, args.steps, args.warmup)

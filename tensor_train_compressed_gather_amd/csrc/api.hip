@@ -177,6 +177,14 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.G1P = (float *)take(4 * (size_t)units_bound * h->max_d1R1);
     // [first, last) unique-row range (in (table, i3) order) of every G3 slice
     w.g3rng = (int32_t *)take(4 * 2 * ((size_t)h->sum_n[2] + 1));
+    // run claim order of the backward: runs <= min(units, sum n2)
+    // (the backward's launch computes the same bound from nnz and sum n2)
+    const int64_t runs_bound = (nnz < h->sum_n[1] ? nnz : h->sum_n[1]) + 1;
+    w.rkey0 = (uint32_t *)take(4 * runs_bound);
+    w.rkey1 = (uint32_t *)take(4 * runs_bound);
+    w.rval0 = (int32_t *)take(4 * runs_bound);
+    w.rval1 = (int32_t *)take(4 * runs_bound);
+    w.rorder = w.rval0;
     // buffers where the sorts end
     const int fm = sort_passes(nnz, h->key_bits) & 1;
     const int fu = sort_passes(nnz, h->key2_bits) & 1;
@@ -286,7 +294,7 @@ int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const in
         tt_emb *h = new (std::nothrow) tt_emb();
         if (!h) return TT_EMB_ERR_NOMEM;
         h->T = T;
-        h->sched_mode = o.sched_mode == 0 ? TT_EMB_SCHED_STEAL_L2 : o.sched_mode;
+        h->sched_mode = o.sched_mode; // 0: the per-rank-class default of the forward launch
         h->group_mode = o.group_mode == 0 ? TT_EMB_GROUP_PREFIX : o.group_mode;
         h->chunk_rows = o.chunk_rows == 0 ? kMaxChunkRows : o.chunk_rows;
         h->g3t_elems = 0;

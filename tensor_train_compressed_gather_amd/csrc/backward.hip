@@ -609,10 +609,14 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
     const int mb = w % MT, rg = w / MT; // (2): this wave's r2 block and row group
     const int rbeg = ws.ctrl[CTRL_RUN_CLS + L::CLS], rend = ws.ctrl[CTRL_RUN_CLS + L::CLS + 1];
     for (;;) {
-        if (tid == 0) s_run = rbeg + atomicAdd(&ws.ctrl[CTRL_BWD_NEXT + L::CLS], 1);
+        if (tid == 0) {
+            // runs are claimed longest first (the class's slice of the sorted order)
+            const int k = rbeg + atomicAdd(&ws.ctrl[CTRL_BWD_NEXT + L::CLS], 1);
+            s_run = k < rend ? ws.rorder[k] : -1;
+        }
         __syncthreads();
         const int run = s_run;
-        if (run >= rend) break;
+        if (run < 0) break;
         const int c0 = ws.tile_cstart[ws.run_tile_start[run]], c1 = ws.tile_cstart[ws.run_tile_start[run + 1]];
         if (tid == 0) {
             ++nwork;
@@ -1102,6 +1106,28 @@ __global__ void k_bwd_prep(BwdArgs a)
     }
 }
 
+// Claim order of the runs (longest-processing-time first, so that the long
+// runs of Zipf-hot i2 digits do not start last and leave a tail): key =
+// class rank (runs are class-major, so each class keeps its slice of
+// positions) above the run's chunk count, descending; the stable sort keeps
+// equal runs in run order.  The order changes only which block computes a
+// run: every run writes its own results, so the output does not depend on it.
+constexpr int kRunKeyBits = 16, kRunCostBits = 13;
+__global__ __launch_bounds__(kThreads) void k_run_keys(BwdArgs a)
+{
+    const Ws &ws = a.ws;
+    const int nruns = ws.ctrl[CTRL_RUNS];
+    for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < nruns; r += gridDim.x * blockDim.x) {
+        const int t = segment_of(ws.tab_unit_start, a.T, ws.uorder[ws.run_start[r]]);
+        const int cls = a.tab[t].cls, rank = cls < 0 ? 4 : cls;
+        int nch = ws.tile_cstart[ws.run_tile_start[r + 1]] - ws.tile_cstart[ws.run_tile_start[r]];
+        constexpr int cmax = (1 << kRunCostBits) - 1;
+        nch = nch < cmax ? nch : cmax;
+        ws.rkey0[r] = ((uint32_t)rank << kRunCostBits) | (uint32_t)(cmax - nch);
+        ws.rval0[r] = r;
+    }
+}
+
 // Transposed G3 copies of the MFMA-class tables (G3t[i3][j3][r2]).
 __global__ __launch_bounds__(kThreads) void k_bwd_g3t(BwdArgs a)
 {
@@ -1191,6 +1217,17 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
         if (!p.force_generic) {
             hipLaunchKernelGGL(k_bwd_prep, dim3(1), dim3(64), 0, s, a);
             hipLaunchKernelGGL(k_bwd_g3t, dim3(64, T), dim3(kThreads), 0, s, a);
+            {
+                const int64_t runs_bound = (p.nnz < p.sum_n[1] ? p.nnz : p.sum_n[1]) + 1;
+                int g = ceil_div(runs_bound, kThreads);
+                g = g > 1024 ? 1024 : g;
+                hipLaunchKernelGGL(k_run_keys, dim3(g), dim3(kThreads), 0, s, a);
+                bool in1 = false;
+                hipError_t e = radix_sort_pairs(p, p.ws.rkey0, p.ws.rval0, p.ws.rkey1, p.ws.rval1, runs_bound,
+                                                &p.ws.ctrl[CTRL_RUNS], kRunKeyBits, &in1, s);
+                if (e != hipSuccess) return e;
+                a.ws.rorder = in1 ? p.ws.rval1 : p.ws.rval0;
+            }
             for (int c = 0; c < 4; ++c) {
                 if (!(p.cls_mask & (1 << c))) continue;
                 timer_begin(p.timing, TM_BWD_CLS0 + c, s);

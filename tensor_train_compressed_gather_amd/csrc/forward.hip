@@ -46,6 +46,15 @@ static_assert(FwdCfg<64>::CTILE == kCTile, "checkpoint slot holds the largest pr
 constexpr int kMaxClsOcc = 8; // queue heads per CU reserved for each class
 constexpr int kPoolCap = 64;  // fused pooling: lookups of a row pooled by the contraction itself
 constexpr int kSchedStatic = 1, kSchedSteal = 2, kSchedStealL2 = 3;
+// Default scheduling per rank class (8, 16, 32, 64), from the scheduling
+// ablation on the 26-table batch-32768 forward: static ranges are already
+// balanced to within 0.82-0.85 of the span, and a claimed chunk of a rank-16
+// or rank-32 tile is short enough that stealing's extra claims and broken
+// (table, i2) continuity cost more than the idle tail they remove (rank 16:
+// 0.16 ms static, 0.22 ms stealing, 0.42 ms with checkpoints); rank-64 chunks
+// are long and stealing pays (1.15 -> 1.04 ms).  Checkpoints were consulted
+// by under 1 % of the chunks of split tiles and are left to the explicit mode.
+constexpr int kDefaultSched[4] = {kSchedStatic, kSchedStatic, kSchedStatic, kSchedSteal};
 
 struct FwdArgs {
     const TableDesc *tab;
@@ -827,7 +836,9 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
                 timer_begin(p.timing, TM_FWD_CLS0 + c, s);
                 const dim3 grid(cg.nb[c]), block(kThreads);
                 static_assert(kKeepMinCls == 2, "kept-prefix kernels exist for ranks 32 and 64");
-#define TT_FWD_CLASS(RR, KK, PP) hipLaunchKernelGGL((k_contract<RR, KK, PP>), grid, block, 0, s, a, hs)
+                FwdArgs ac = a;
+                ac.sched = p.sched_mode != 0 ? p.sched_mode : kDefaultSched[c];
+#define TT_FWD_CLASS(RR, KK, PP) hipLaunchKernelGGL((k_contract<RR, KK, PP>), grid, block, 0, s, ac, hs)
                 if (fused) {
                     switch (c) {
                     case 0: TT_FWD_CLASS(8, false, true); break;

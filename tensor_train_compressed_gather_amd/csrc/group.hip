@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void k_sort_upsweep(const uint32_t *keys,
     __shared__ uint32_t cnt[kRadix];
     for (int i = threadIdx.x; i < kRadix; i += kThreads) cnt[i] = 0;
     __syncthreads();
-    const int64_t n = n_dev ? (int64_t)*n_dev : n_max;
+    const int64_t nd = n_dev ? (int64_t)*n_dev : n_max, n = nd < n_max ? nd : n_max; // never past the buffers
     const int64_t base = (int64_t)blockIdx.x * kSortTile;
 #pragma unroll 4
     for (int j = 0; j < kSortItems; ++j) {
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void k_sort_downsweep(const uint32_t *kin
     __shared__ uint32_t ssum[W];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t n = n_dev ? (int64_t)*n_dev : n_max;
+    const int64_t nd = n_dev ? (int64_t)*n_dev : n_max, n = nd < n_max ? nd : n_max; // never past the buffers
     const int64_t base = (int64_t)blockIdx.x * kSortTile;
     if (base >= n) return;
     for (int i = tid; i < W * kRadix; i += kThreads) (&wcnt[0][0])[i] = 0;

@@ -166,6 +166,10 @@ struct Ws {
     int32_t *g3rng;          // [2][sum n3] row range of each G3 slice in the (table, i3) order
     uint32_t *key3;          // sorted (i3_base + i3) of unique rows
     int32_t *u3order;        // unique rows in (table, i3, unique id) order
+    // backward claim order of the (table, i2) runs: class-major, longest first
+    uint32_t *rkey0, *rkey1;
+    int32_t *rval0, *rval1;
+    const int32_t *rorder;   // the sorted run ids (one of rval0 / rval1, set at launch)
     // sort buffers of the unit order (kept apart from the canonical perm)
     int32_t *uvals0, *uvals1;
     int32_t *uvals_free; // the unit-sort value buffer that does not hold uorder
