@@ -159,7 +159,8 @@ int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const in
  * tt_emb_sgd_update return TT_EMB_ERR_UNSUPPORTED, and the forward flags
  * TT_EMB_KEEP_PREFIX / TT_EMB_ATOMIC_POOL give TT_EMB_ERR_ARG.  Beyond the
  * three-core limits: TT_EMB_ERR_UNSUPPORTED when T*K > 192, K = 2, K > 8,
- * the leading K-1 digits of all tables span 2^31 or more prefixes, or an
+ * the leading K-1 digits of all tables span 2^31 or more prefixes, the
+ * product n_1 .. n_{K-1} of some table exceeds 2^32 - 1, or an
  * intermediate or core slice of some level exceeds 8192 floats; K < 2 is
  * TT_EMB_ERR_ARG.  The grouping view of such a handle groups unique rows by
  * their leading K-1 digits (grp_prefix = row div n_{K-1}). */

@@ -64,6 +64,16 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 int sort_passes(int64_t n, int bits) { return (n <= 0 || bits <= 0) ? 0 : (bits + 7) / 8; }
 
+// dG2 partial slots for split backward runs: split runs take fewer than
+// 2 * tiles / kPieceTiles <= 2 * nnz / kPieceTiles slots, capped (the backward
+// then cuts longer pieces).
+int64_t g2p_slots_for(int64_t nnz)
+{
+    const int64_t n = nnz > 0 ? nnz : 1;
+    const int64_t v = 2 * n / kPieceTiles + 1;
+    return v < kMaxG2Slots ? v : kMaxG2Slots;
+}
+
 // Carve the workspace.  With base == nullptr only the size is computed.
 size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan *p)
 {
@@ -177,13 +187,22 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.G1P = (float *)take(4 * (size_t)units_bound * h->max_d1R1);
     // [first, last) unique-row range (in (table, i3) order) of every G3 slice
     w.g3rng = (int32_t *)take(4 * 2 * ((size_t)h->sum_n[2] + 1));
-    // run claim order of the backward: runs <= min(units, sum n2)
-    // (the backward's launch computes the same bound from nnz and sum n2)
+    // backward pieces and their claim order: runs <= min(nnz, sum n2); split
+    // runs take at most 2 * tiles / kPieceTiles <= 2 * nnz / kPieceTiles slots
+    // (the backward's launch computes the same bounds from nnz and sum n2)
     const int64_t runs_bound = (nnz < h->sum_n[1] ? nnz : h->sum_n[1]) + 1;
-    w.rkey0 = (uint32_t *)take(4 * runs_bound);
-    w.rkey1 = (uint32_t *)take(4 * runs_bound);
-    w.rval0 = (int32_t *)take(4 * runs_bound);
-    w.rval1 = (int32_t *)take(4 * runs_bound);
+    const int64_t slots_cap = g2p_slots_for(nnz);
+    const int64_t pieces_bound = runs_bound + slots_cap;
+    w.run_pbase = (int32_t *)take(4 * runs_bound);
+    w.run_sbase = (int32_t *)take(4 * runs_bound);
+    w.piece_tb = (int32_t *)take(4 * pieces_bound);
+    w.piece_te = (int32_t *)take(4 * pieces_bound);
+    w.piece_slot = (int32_t *)take(4 * pieces_bound);
+    w.G2P = (float *)take(4 * (size_t)slots_cap * kG2PStride);
+    w.rkey0 = (uint32_t *)take(4 * pieces_bound);
+    w.rkey1 = (uint32_t *)take(4 * pieces_bound);
+    w.rval0 = (int32_t *)take(4 * pieces_bound);
+    w.rval1 = (int32_t *)take(4 * pieces_bound);
     w.rorder = w.rval0;
     // buffers where the sorts end
     const int fm = sort_passes(nnz, h->key_bits) & 1;
@@ -219,6 +238,7 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
         p->sumD = h->sumD;
         for (int k = 0; k < 3; ++k) p->sum_n[k] = h->sum_n[k];
         p->g1stride = (int)h->max_d1R1;
+        p->g2p_slots = (int)g2p_slots_for(nnz);
         p->dtab = h->dtab;
         p->ws = w;
     }
@@ -483,6 +503,9 @@ int tt_emb_create_k(int32_t T, int32_t K, const int64_t *num_rows, const int32_t
                 kt.div[k] = dv;
                 dv = std::min<int64_t>(dv * nt[k], (int64_t)1 << 40);
             }
+            // digit strides fit 32 bits (the kernels decode rows < 2^31 with
+            // 32-bit division; div[0] is the largest stride)
+            if (kt.div[0] > (int64_t)0xffffffff) rc = TT_EMB_ERR_UNSUPPORTED;
             kt.P[0] = 1;
             for (int m = 1; m <= K; ++m) kt.P[m] = kt.P[m - 1] * dt[m - 1];
             // staged operands of every level must fit in LDS

@@ -38,6 +38,7 @@ struct BwdArgs {
     int gstride; // row stride of the gather partial slots (max Dp)
     int force_generic;
     int g1stride; // row stride of the G1 partials (max d1*R1)
+    int g2p_slots; // dG2 partial slots in the workspace (pieces of split runs)
 };
 
 // (bag within its table, unique row) of every lookup, in lookup order, so the
@@ -607,17 +608,19 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
     const Ws &ws = a.ws;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, kq = lane >> 4;
     const int mb = w % MT, rg = w / MT; // (2): this wave's r2 block and row group
-    const int rbeg = ws.ctrl[CTRL_RUN_CLS + L::CLS], rend = ws.ctrl[CTRL_RUN_CLS + L::CLS + 1];
+    const int rbeg = ws.ctrl[CTRL_PIECE_CLS + L::CLS], rend = ws.ctrl[CTRL_PIECE_CLS + L::CLS + 1];
     for (;;) {
         if (tid == 0) {
-            // runs are claimed longest first (the class's slice of the sorted order)
+            // pieces (whole runs, or tile-aligned parts of long ones) are
+            // claimed longest first: the class's slice of the sorted order
             const int k = rbeg + atomicAdd(&ws.ctrl[CTRL_BWD_NEXT + L::CLS], 1);
             s_run = k < rend ? ws.rorder[k] : -1;
         }
         __syncthreads();
-        const int run = s_run;
-        if (run < 0) break;
-        const int c0 = ws.tile_cstart[ws.run_tile_start[run]], c1 = ws.tile_cstart[ws.run_tile_start[run + 1]];
+        const int piece = s_run;
+        if (piece < 0) break;
+        const int c0 = ws.tile_cstart[ws.piece_tb[piece]], c1 = ws.tile_cstart[ws.piece_te[piece]];
+        const int slot = __builtin_amdgcn_readfirstlane(ws.piece_slot[piece]);
         if (tid == 0) {
             ++nwork;
             nchunks += c1 - c0;
@@ -1062,7 +1065,8 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
             if (has_next) pf_commit(nrec, next_new);
             if (w == 0 && c + 2 < c1) reinterpret_cast<int *>(&recs[slot == 0 ? 2 : slot - 1])[lane] = pre;
         }
-        float *dst = a.grads.g[t][1] + (int64_t)i2 * R * d2 * R;
+        // a whole run writes its dG2 slice; a piece of a split run its partial
+        float *dst = slot < 0 ? a.grads.g[t][1] + (int64_t)i2 * R * d2 * R : ws.G2P + (int64_t)slot * kG2PStride;
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const int ntg = w + NW * j;
@@ -1100,31 +1104,105 @@ __global__ void k_bwd_prep(BwdArgs a)
         ws.ctrl[CTRL_RUN_CLS + c] = lo;
     }
     if (c == 5) ws.ctrl[CTRL_RUN_CLS + 5] = nruns;
+    if (c == 6) { // tiles per piece of a split run: >= kPieceTiles and >= 2 * tiles / slots
+        const int64_t tiles = ws.ctrl[CTRL_TILES];
+        const int64_t need = (2 * tiles + a.g2p_slots - 1) / a.g2p_slots;
+        ws.ctrl[CTRL_PIECE_TILES] = (int)(need > kPieceTiles ? need : kPieceTiles);
+    }
     if (c < 4) {
         ws.ctrl[CTRL_BWD_NEXT + c] = 0;
         ws.bstat[(4 + c) * kStatBlocks].nb = 0; // backward class records
     }
 }
 
-// Claim order of the runs (longest-processing-time first, so that the long
-// runs of Zipf-hot i2 digits do not start last and leave a tail): key =
-// class rank (runs are class-major, so each class keeps its slice of
-// positions) above the run's chunk count, descending; the stable sort keeps
-// equal runs in run order.  The order changes only which block computes a
-// run: every run writes its own results, so the output does not depend on it.
+// Backward pieces.  A (table, i2) run accumulates its dG2 slice in registers
+// from its first tile to its last, so one long run (a Zipf-hot i2 digit of a
+// large table) is a single block's work; at ranks <= 32 such runs are longer
+// than a block's fair share.  A run of those classes with more than PT tiles
+// is cut into ceil(tiles / PT) tile-aligned pieces of near-equal size; each
+// piece writes its dG2 partial to a slot of its own and k_reduce_g2p adds the
+// slots of a run in piece order (fixed order, no atomics).  PT >= 16 and
+// PT >= 2 * tiles / slots, so the slots in the workspace always suffice.
+struct PieceOp {
+    BwdArgs a;
+    __device__ int64_t count() const { return a.ws.ctrl[CTRL_RUNS]; }
+    __device__ uint64_t value(int64_t r) const
+    {
+        const Ws &ws = a.ws;
+        const int t = segment_of(ws.tab_unit_start, a.T, ws.uorder[ws.run_start[r]]);
+        const int cls = a.tab[t].cls;
+        const int nt = ws.run_tile_start[r + 1] - ws.run_tile_start[r];
+        const int PT = ws.ctrl[CTRL_PIECE_TILES];
+        if (cls < 0 || cls > kSplitMaxCls || nt <= PT) return (uint64_t)1 << 32; // one piece, no slot
+        const uint64_t np = (uint64_t)((nt + PT - 1) / PT);
+        return (np << 32) | np; // pieces (high word) and slots (low word)
+    }
+    __device__ void emit(int64_t r, uint64_t excl, uint64_t) const
+    {
+        a.ws.run_pbase[r] = (int32_t)(excl >> 32);
+        a.ws.run_sbase[r] = (int32_t)(excl & 0xffffffffu);
+    }
+    __device__ void total(uint64_t tot, int64_t n) const
+    {
+        a.ws.ctrl[CTRL_PIECES] = (int32_t)(tot >> 32);
+        a.ws.ctrl[CTRL_SLOTS] = (int32_t)(tot & 0xffffffffu);
+        a.ws.run_pbase[n] = (int32_t)(tot >> 32);
+        a.ws.run_sbase[n] = (int32_t)(tot & 0xffffffffu);
+    }
+};
+
+// Pieces of every run, and their claim order keys (longest-processing-time
+// first, so that long pieces do not start last and leave a tail): key = class
+// rank (runs, hence pieces, are class-major, so each class keeps its slice of
+// positions) above the piece's chunk count, descending; the stable sort keeps
+// equal pieces in piece order.  The order changes only which block computes a
+// piece: every piece writes its own results, so the output does not depend on it.
 constexpr int kRunKeyBits = 16, kRunCostBits = 13;
-__global__ __launch_bounds__(kThreads) void k_run_keys(BwdArgs a)
+__global__ __launch_bounds__(kThreads) void k_piece_fill(BwdArgs a)
 {
     const Ws &ws = a.ws;
     const int nruns = ws.ctrl[CTRL_RUNS];
+    if (blockIdx.x == 0 && threadIdx.x < 6) // first piece of each class, then the total
+        ws.ctrl[CTRL_PIECE_CLS + threadIdx.x] = ws.run_pbase[ws.ctrl[CTRL_RUN_CLS + threadIdx.x]];
     for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < nruns; r += gridDim.x * blockDim.x) {
         const int t = segment_of(ws.tab_unit_start, a.T, ws.uorder[ws.run_start[r]]);
         const int cls = a.tab[t].cls, rank = cls < 0 ? 4 : cls;
-        int nch = ws.tile_cstart[ws.run_tile_start[r + 1]] - ws.tile_cstart[ws.run_tile_start[r]];
+        const int pb = ws.run_pbase[r], np = ws.run_pbase[r + 1] - pb, sb = ws.run_sbase[r];
+        const int tb0 = ws.run_tile_start[r], nt = ws.run_tile_start[r + 1] - tb0;
         constexpr int cmax = (1 << kRunCostBits) - 1;
-        nch = nch < cmax ? nch : cmax;
-        ws.rkey0[r] = ((uint32_t)rank << kRunCostBits) | (uint32_t)(cmax - nch);
-        ws.rval0[r] = r;
+        for (int j = 0; j < np; ++j) {
+            const int k = pb + j;
+            const int tb = tb0 + (int)((int64_t)j * nt / np), te = tb0 + (int)((int64_t)(j + 1) * nt / np);
+            ws.piece_tb[k] = tb;
+            ws.piece_te[k] = te;
+            ws.piece_slot[k] = np > 1 ? sb + j : -1;
+            int nch = ws.tile_cstart[te] - ws.tile_cstart[tb];
+            nch = nch < cmax ? nch : cmax;
+            ws.rkey0[k] = ((uint32_t)rank << kRunCostBits) | (uint32_t)(cmax - nch);
+            ws.rval0[k] = k;
+        }
+    }
+}
+
+// dG2[i2] of every split run = its pieces' partials added in piece order.
+__global__ __launch_bounds__(kThreads) void k_reduce_g2p(BwdArgs a)
+{
+    const Ws &ws = a.ws;
+    const int nruns = ws.ctrl[CTRL_RUNS];
+    for (int r = blockIdx.x; r < nruns; r += gridDim.x) {
+        const int pb = ws.run_pbase[r], np = ws.run_pbase[r + 1] - pb;
+        if (np <= 1) continue;
+        const int sb = ws.run_sbase[r];
+        const ChunkRec &rec = ws.crec[ws.tile_cstart[ws.run_tile_start[r]]];
+        const int t = rec.t, i2 = rec.i2;
+        const TableDesc &tb = a.tab[t];
+        const int n = tb.R1 * tb.d2 * tb.R2;
+        float *dst = a.grads.g[t][1] + (int64_t)i2 * n;
+        for (int e = threadIdx.x; e < n; e += blockDim.x) {
+            float acc = ws.G2P[(int64_t)sb * kG2PStride + e];
+            for (int j = 1; j < np; ++j) acc += ws.G2P[(int64_t)(sb + j) * kG2PStride + e];
+            dst[e] = acc;
+        }
     }
 }
 
@@ -1173,7 +1251,7 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
                            const int64_t *offsets, const GradPtrs &grads, hipStream_t s)
 {
     BwdArgs a{p.dtab, p.T, p.B, p.ws, cores, grads, grad_out, offsets, p.nnz, p.sumD, p.Dpmax, p.force_generic,
-              p.g1stride};
+              p.g1stride, p.g2p_slots};
     const int T = p.T;
     const int sum_n1 = p.sum_n[0], sum_n3 = p.sum_n[2];
     timer_begin(p.timing, TM_BWD_GATHER, s);
@@ -1217,14 +1295,18 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
         if (!p.force_generic) {
             hipLaunchKernelGGL(k_bwd_prep, dim3(1), dim3(64), 0, s, a);
             hipLaunchKernelGGL(k_bwd_g3t, dim3(64, T), dim3(kThreads), 0, s, a);
-            {
+            {   // pieces of the runs and their claim order (bounds as in the workspace plan)
                 const int64_t runs_bound = (p.nnz < p.sum_n[1] ? p.nnz : p.sum_n[1]) + 1;
+                const int64_t pieces_bound = runs_bound + p.g2p_slots;
+                PieceOp op{a};
+                hipError_t e = run_scan(op, p.ws.part, scan_blocks(runs_bound), s);
+                if (e != hipSuccess) return e;
                 int g = ceil_div(runs_bound, kThreads);
                 g = g > 1024 ? 1024 : g;
-                hipLaunchKernelGGL(k_run_keys, dim3(g), dim3(kThreads), 0, s, a);
+                hipLaunchKernelGGL(k_piece_fill, dim3(g), dim3(kThreads), 0, s, a);
                 bool in1 = false;
-                hipError_t e = radix_sort_pairs(p, p.ws.rkey0, p.ws.rval0, p.ws.rkey1, p.ws.rval1, runs_bound,
-                                                &p.ws.ctrl[CTRL_RUNS], kRunKeyBits, &in1, s);
+                e = radix_sort_pairs(p, p.ws.rkey0, p.ws.rval0, p.ws.rkey1, p.ws.rval1, pieces_bound,
+                                     &p.ws.ctrl[CTRL_PIECES], kRunKeyBits, &in1, s);
                 if (e != hipSuccess) return e;
                 a.ws.rorder = in1 ? p.ws.rval1 : p.ws.rval0;
             }
@@ -1245,6 +1327,8 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
                 }
                 timer_end(p.timing, TM_BWD_CLS0 + c, s);
             }
+            int g = p.sum_n[1] < 4096 ? p.sum_n[1] : 4096;
+            hipLaunchKernelGGL(k_reduce_g2p, dim3(g > 0 ? g : 1), dim3(kThreads), 0, s, a);
         }
         if (p.force_generic || p.any_generic)
             hipLaunchKernelGGL(k_bwd_runs, dim3(p.num_blocks * 2), dim3(kThreads), 0, s, a);

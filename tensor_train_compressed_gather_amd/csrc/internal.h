@@ -24,6 +24,10 @@ constexpr int kMaxCkptSlots = 4096; // L2 checkpoint slots for split prefix tile
 constexpr int kUnitsPerTile = 4;    // prefix units sharing (table, i2) per tile
 constexpr int kGuTask = 256;        // sorted lookup positions per gradient-gather task
 constexpr int kGuBatch = 16;        // positions whose grad_out rows a gather worker has in flight
+constexpr int kPieceTiles = 16;     // least tiles per piece of a split backward run
+constexpr int kSplitMaxCls = 2;     // runs of the rank classes 8, 16, 32 may be split
+constexpr int kMaxG2Slots = 8192;   // dG2 partial slots (pieces of split runs)
+constexpr int kG2PStride = 32 * 4 * 32; // floats per slot: R1 * d2 * R2 of a splittable table
 
 // Control words at the head of the workspace.
 enum CtrlSlot {
@@ -42,6 +46,10 @@ enum CtrlSlot {
     CTRL_CLS_START = 16, // 5 words: first chunk of each MFMA rank class (chunks are class-major)
     CTRL_RUN_CLS = 24,   // 6 words: first run of each class, then the run count
     CTRL_KLEV = 48,      // 8 words: groups of each prefix length (tables of K >= 4 cores)
+    CTRL_PIECE_CLS = 32, // 6 words: first backward piece of each class, then the piece count
+    CTRL_PIECE_TILES = 56, // tiles per piece of a split backward run
+    CTRL_PIECES = 57,    // backward pieces
+    CTRL_SLOTS = 58,     // dG2 partial slots of split runs
     CTRL_N = 64
 };
 enum ErrBits { ERRB_INDEX = 1, ERRB_OFFSETS = 2, ERRB_CAPACITY = 4 };
@@ -166,10 +174,17 @@ struct Ws {
     int32_t *g3rng;          // [2][sum n3] row range of each G3 slice in the (table, i3) order
     uint32_t *key3;          // sorted (i3_base + i3) of unique rows
     int32_t *u3order;        // unique rows in (table, i3, unique id) order
-    // backward claim order of the (table, i2) runs: class-major, longest first
+    // backward pieces: a (table, i2) run of the rank classes up to kSplitMaxCls
+    // with more than CTRL_PIECE_TILES tiles is cut into tile-aligned pieces
+    // whose dG2 partials (G2P slots) are summed in piece order afterwards
+    int32_t *run_pbase;      // [runs + 1] first piece of each run
+    int32_t *run_sbase;      // [runs + 1] first G2P slot of each run
+    int32_t *piece_tb, *piece_te, *piece_slot; // [pieces] tile range, slot or -1
+    float *G2P;              // [g2p_slots][kG2PStride] dG2 partials of split runs
+    // backward claim order of the pieces: class-major, longest first
     uint32_t *rkey0, *rkey1;
     int32_t *rval0, *rval1;
-    const int32_t *rorder;   // the sorted run ids (one of rval0 / rval1, set at launch)
+    const int32_t *rorder;   // the sorted piece ids (one of rval0 / rval1, set at launch)
     // sort buffers of the unit order (kept apart from the canonical perm)
     int32_t *uvals0, *uvals1;
     int32_t *uvals_free; // the unit-sort value buffer that does not hold uorder
@@ -223,6 +238,7 @@ struct Plan {
     int Dmax, Dpmax, R2max, sumD;
     int sum_n[3]; // sum over tables of n1, n2, n3
     int g1stride; // row stride of the G1 partials (max d1*R1 over tables)
+    int g2p_slots; // G2P slots in the workspace
     const TableDesc *dtab; // device copy
     Ws ws;
 };

@@ -12,9 +12,9 @@
 // each group's intermediate built from its parent group's one level up.
 //
 // gfx950 mapping: plain fp32 FMAs (shapes vary per level and table), one
-// block per group with the parent intermediate and the core slice staged in
-// LDS; the rows of the last level are formed per group of length K-1 and
-// pooled by the bag-major pooling kernel.
+// wave per group of a level and one wave per unique row of the last step,
+// operands read from L2 with no LDS staging; the rows are pooled by the
+// bag-major pooling kernel.
 #include "primitives.h"
 
 namespace ttemb {
@@ -36,7 +36,7 @@ struct KLevOp {
     __device__ void info(int64_t u, int *t, int64_t *q) const
     {
         *t = segment_of(a.ws.tab_uniq_start, a.T, u);
-        *q = (int64_t)a.ws.uniq_row[u] / a.kp.dkt[*t].div[m - 1];
+        *q = (uint32_t)a.ws.uniq_row[u] / (uint32_t)a.kp.dkt[*t].div[m - 1];
     }
     __device__ uint64_t value(int64_t u) const
     {
@@ -61,77 +61,94 @@ struct KLevOp {
 };
 
 // Level m (2 <= m <= K-1): V_m[g] = V_{m-1}[parent] . G_{m-1}[i_{m-1}], one
-// block per group; V_1 is the core slice G_0[i_0] itself.
+// wave per group; V_1 is the core slice G_0[i_0] itself.  The lanes take 64
+// output columns (j, r) at a time and up to 8 rows p: the core slice is read
+// coalesced straight from L2 (a core is small and shared by many groups), the
+// parent's entries are wave-uniform and come through scalar loads.  No LDS,
+// so many waves per SIMD hide the load latency.
+constexpr int kKRowBlk = 8;
 __global__ __launch_bounds__(kThreads) void k_klevel(KArgs a, int m)
 {
-    __shared__ float Vp[kKLds];
-    __shared__ float Gs[kKLds];
     const Ws &ws = a.ws;
-    const int K = a.kp.K;
+    const int K = a.kp.K, lane = threadIdx.x & 63;
     const int64_t ng = ws.ctrl[CTRL_KLEV + m];
-    for (int64_t g = blockIdx.x; g < ng; g += gridDim.x) {
-        const int u0 = a.kp.gfirst[m][g];
-        const int t = segment_of(ws.tab_uniq_start, a.T, u0);
-        const KTab &kt = a.kp.dkt[t];
-        const int64_t row = ws.uniq_row[u0];
+    const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + uni(threadIdx.x >> 6); g < ng; g += nw) {
+        const int u0 = uni(a.kp.gfirst[m][g]);
+        const int t = uni(segment_of(ws.tab_uniq_start, a.T, u0));
+        const auto &kt = kconst(a.kp.dkt)[t];
+        const int64_t row = uni((int)ws.uniq_row[u0]);
         const int c = m - 1; // core applied at this level
         const int P = kt.P[m - 1], Rin = kt.R[m - 1], dk = kt.d[c], Rout = kt.R[m];
-        const int64_t ic = row / kt.div[c] % kt.n[c];
-        // parent intermediate [P][Rin]
+        // rows and digit strides are below 2^31 (checked at create): 32-bit division
+        const uint32_t urow = (uint32_t)row;
+        const int64_t ic = urow / (uint32_t)kt.div[c] % (uint32_t)kt.n[c];
         const float *par;
         if (m == 2) {
-            const int64_t i0 = row / kt.div[0] % kt.n[0];
+            const int64_t i0 = urow / (uint32_t)kt.div[0] % (uint32_t)kt.n[0];
             par = a.cores.g[t * K] + i0 * (int64_t)kt.d[0] * kt.R[1];
         } else {
-            par = a.kp.V[m - 1] + (int64_t)a.kp.ugrp[m - 1][u0] * a.kp.smax[m - 1];
+            par = a.kp.V[m - 1] + (int64_t)uni(a.kp.ugrp[m - 1][u0]) * a.kp.smax[m - 1];
         }
-        for (int e = threadIdx.x; e < P * Rin; e += kThreads) Vp[e] = par[e];
-        const float *gsl = a.cores.g[t * K + c] + ic * (int64_t)Rin * dk * Rout;
-        for (int e = threadIdx.x; e < Rin * dk * Rout; e += kThreads) Gs[e] = gsl[e];
-        __syncthreads();
-        float *out = a.kp.V[m] + g * a.kp.smax[m];
+        const auto *pc = kconst(par); // [P][Rin], wave-uniform reads
+        const float *gsl = a.cores.g[t * K + c] + ic * (int64_t)Rin * dk * Rout; // [Rin][dk * Rout]
+        float *out = a.kp.V[m] + g * a.kp.smax[m];                            // [P][dk * Rout]
         const int cols = dk * Rout;
-        for (int e = threadIdx.x; e < P * cols; e += kThreads) {
-            const int p = e / cols, jr = e - p * cols; // jr = j * Rout + r
-            float acc = 0.f;
-            for (int q = 0; q < Rin; ++q) acc = fmaf(Vp[p * Rin + q], Gs[q * cols + jr], acc);
-            out[e] = acc; // row p * dk + j, column r
+        for (int c0 = 0; c0 < cols; c0 += 64) {
+            const int jr = c0 + lane;
+            const bool ok = jr < cols;
+            const int jrc = ok ? jr : cols - 1; // clamped: loads stay inside the slice
+            for (int p0 = 0; p0 < P; p0 += kKRowBlk) {
+                const int np = P - p0 < kKRowBlk ? P - p0 : kKRowBlk;
+                float acc[kKRowBlk];
+#pragma unroll
+                for (int i = 0; i < kKRowBlk; ++i) acc[i] = 0.f;
+#pragma unroll 8
+                for (int q = 0; q < Rin; ++q) {
+                    const float gv = gsl[(int64_t)q * cols + jrc];
+#pragma unroll
+                    for (int i = 0; i < kKRowBlk; ++i)
+                        if (i < np) acc[i] = fmaf(pc[(p0 + i) * Rin + q], gv, acc[i]);
+                }
+                if (ok) {
+#pragma unroll
+                    for (int i = 0; i < kKRowBlk; ++i)
+                        if (i < np) out[(int64_t)(p0 + i) * cols + jr] = acc[i]; // row (p, j), column r
+                }
+            }
         }
-        __syncthreads();
     }
 }
 
-// Rows: E[u] = V_{K-1}[group of u] . G_{K-1}[i_{K-1}(u)] for the unique rows
-// of each group of length K-1 (contiguous in the unique-row order).
+// Rows: E[u] = V_{K-1}[group of u] . G_{K-1}[i_{K-1}(u)], one wave per unique
+// row, lanes over the D = P * d_{K-1} columns (p, j); the group's intermediate
+// and the last core slice are read from L2 / L1 (both shared by many lanes).
 __global__ __launch_bounds__(kThreads) void k_krows(KArgs a)
 {
-    __shared__ float Vp[kKLds];
     const Ws &ws = a.ws;
-    const int K = a.kp.K, m = K - 1;
-    const int64_t ng = ws.ctrl[CTRL_KLEV + m];
-    for (int64_t g = blockIdx.x; g < ng; g += gridDim.x) {
-        const int u0 = a.kp.gfirst[m][g], u1 = a.kp.gfirst[m][g + 1];
-        const int t = segment_of(ws.tab_uniq_start, a.T, u0);
-        const KTab &kt = a.kp.dkt[t];
-        const TableDesc &tb = a.tab[t];
-        const int P = kt.P[m], Rin = kt.R[m], dk = kt.d[K - 1];
-        const float *par = a.kp.V[m] + g * a.kp.smax[m];
-        for (int e = threadIdx.x; e < P * Rin; e += kThreads) Vp[e] = par[e];
-        __syncthreads();
-        const float *GK = a.cores.g[t * K + K - 1];
-        float *Et = ws.E + ws.ebase[t];
-        const int D = P * dk;
-        for (int64_t e = threadIdx.x; e < (int64_t)(u1 - u0) * D; e += kThreads) {
-            const int r = (int)(e / D), col = (int)(e - (int64_t)r * D);
-            const int u = u0 + r;
-            const int64_t ik = ws.uniq_row[u] % kt.n[K - 1];
-            const int p = col / dk, j = col - p * dk;
-            const float *gk = GK + ik * (int64_t)Rin * dk + j; // [Rin][dk][1]
+    const int K = a.kp.K, m = K - 1, lane = threadIdx.x & 63;
+    const int64_t U = ws.ctrl[CTRL_U];
+    const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t u = (int64_t)blockIdx.x * (kThreads / 64) + uni(threadIdx.x >> 6); u < U; u += nw) {
+        const int t = uni(segment_of(ws.tab_uniq_start, a.T, u));
+        const auto &kt = kconst(a.kp.dkt)[t];
+        const int P = kt.P[m], Rin = kt.R[m], dk = kt.d[K - 1], D = P * dk;
+        const int g = uni(a.kp.ugrp[m][u]);
+        const int64_t ik = (uint32_t)uni((int)ws.uniq_row[u]) % (uint32_t)kt.n[K - 1];
+        const float *V = a.kp.V[m] + (int64_t)g * a.kp.smax[m];          // [P][Rin]
+        const float *gk = a.cores.g[t * K + K - 1] + ik * (int64_t)Rin * dk; // [Rin][dk]
+        float *Er = ws.E + kconst(ws.ebase)[t] + u * (int64_t)kconst(a.tab)[t].Dp;
+        for (int c0 = 0; c0 < D; c0 += 64) {
+            const int col = c0 + lane;
+            const bool ok = col < D;
+            const int cc = ok ? col : D - 1;
+            const int p = cc / dk, j = cc - p * dk;
+            const float *vr = V + (int64_t)p * Rin;
             float acc = 0.f;
-            for (int q = 0; q < Rin; ++q) acc = fmaf(Vp[p * Rin + q], gk[q * dk], acc);
-            Et[(int64_t)u * tb.Dp + col] = acc;
+#pragma unroll 8
+            for (int q = 0; q < Rin; ++q) acc = fmaf(vr[q], gk[q * dk + j], acc);
+            if (ok) Er[col] = acc;
         }
-        __syncthreads();
     }
 }
 
@@ -147,7 +164,7 @@ hipError_t launch_forward_k(const Plan &p, const KCorePtrs &cores, const int64_t
             hipError_t e = run_scan(op, p.ws.part, scan_blocks(p.nnz), s);
             if (e != hipSuccess) return e;
         }
-        const int g = p.num_blocks * 8;
+        const int g = p.num_blocks * 16; // 64 waves per compute unit, grid-stride
         for (int m = 2; m <= K - 1; ++m) hipLaunchKernelGGL(k_klevel, dim3(g), dim3(kThreads), 0, s, a, m);
         hipLaunchKernelGGL(k_krows, dim3(g), dim3(kThreads), 0, s, a);
     }

@@ -132,6 +132,31 @@ def test_shapes_outside_the_mfma_classes():
     assert_grads_close(got, oracle.backward(w))
 
 
+def test_backward_with_split_runs():
+    # n2 = 2 and n1 = 200: each (table, i2) run holds ~200 prefix units (~50
+    # tiles), more than a backward piece (16 tiles), so the rank-16 and
+    # rank-32 runs are cut into pieces whose dG2 partials are summed in order;
+    # the rank-64 table keeps whole runs
+    tables = [W.Table(3200, (200, 2, 8), (4, 4, 4), (1, R, R, 1), 0.1, "uniform") for R in (16, 32, 64)]
+    rng = np.random.default_rng(11)
+    lens = [rng.integers(16, 33, size=256) for _ in tables]
+    idx = [rng.integers(0, t.N, size=int(l.sum())) for t, l in zip(tables, lens)]
+    w = W.make_custom(tables, lens, idx, seed=11)
+    w.grad_out = np.random.default_rng(12).standard_normal((w.B, w.sum_D)).astype(np.float32)
+    run = Run(w)
+    assert_out_close(w, run.forward().cpu().numpy(), oracle.forward(w))
+    got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
+    assert_grads_close(got, oracle.backward(w))
+    # the split classes ran more pieces than runs (2 runs per table)
+    for r in (16, 32):
+        st = run.emb.block_stats(w.B, w.nnz, f"bwd_r{r}")
+        assert int(st["work"].sum()) > 2, (r, int(st["work"].sum()))
+    assert int(run.emb.block_stats(w.B, w.nnz, "bwd_r64")["work"].sum()) == 2
+    again = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
+    for g0, g1 in zip(got, again):
+        assert np.array_equal(g0, g1)
+
+
 def test_edge_cases_empty_bags_single_prefix_and_no_lookups():
     tab = W.Table(1000, (10, 10, 10), (2, 2, 4), (1, 8, 8, 1), 0.1, "uniform")
     rows = (3 * 10 + 7) * 10 + np.arange(10)
