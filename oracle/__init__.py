@@ -57,6 +57,7 @@ def _load():
             lib.orc_backward.argtypes = [i32, p, p, p, p, p, p, p, i64, i64, p, p, p, i32]
             lib.orc_forward_k.argtypes = [i32, i32, p, p, p, p, p, p, p, i64, i64, p, i32]
             lib.orc_forward_k_grouped.argtypes = [i32, i32, p, p, p, p, p, p, p, i64, i64, p]
+            lib.orc_backward_k.argtypes = [i32, i32, p, p, p, p, p, p, p, i64, i64, p, p]
             lib.orc_sgd_delta.argtypes = [p, i64, C.c_double, p]
             lib.orc_sgd_delta.restype = None
             lib.orc_max_threads.restype = C.c_int
@@ -210,7 +211,7 @@ def sgd_delta(dG: np.ndarray, lr: float) -> np.ndarray:
     return out
 
 
-def forward_k(w, grouped: bool = False, threads: int = 0) -> np.ndarray:
+def forward_k(w, grouped: bool = False, threads: int = 0, cores=None) -> np.ndarray:
     """Pooled forward of K-core tables (every table of w has K = len(n)
     cores), fp64 [B][sum D]: per-index chains, or (grouped) every distinct
     leading-digit prefix computed once and reused."""
@@ -218,7 +219,7 @@ def forward_k(w, grouped: bool = False, threads: int = 0) -> np.ndarray:
     K = len(w.tables[0].n)
     assert all(len(t.n) == K for t in w.tables)
     N, n, d, R = _shape_args(w)
-    cs, carr = _cores_arg(w.cores)
+    cs, carr = _cores_arg(w.cores if cores is None else cores)
     out = np.zeros((w.B, w.sum_D), dtype=np.float64)
     idx = np.ascontiguousarray(w.indices, dtype=np.int64)
     off = np.ascontiguousarray(w.offsets, dtype=np.int64)
@@ -231,3 +232,26 @@ def forward_k(w, grouped: bool = False, threads: int = 0) -> np.ndarray:
     if rc:
         raise OracleError(rc)
     return out
+
+
+def backward_k(w, grad_out=None) -> list:
+    """Core gradients of sum(grad_out * out) for K-core tables, fp64, shaped
+    like the cores (T*K of them): every index's chain reversed on its own,
+    lookups in CSR order."""
+    lib = _load()
+    K = len(w.tables[0].n)
+    assert all(len(t.n) == K for t in w.tables)
+    N, n, d, R = _shape_args(w)
+    cs, carr = _cores_arg(w.cores)
+    g = np.ascontiguousarray(w.grad_out if grad_out is None else grad_out, dtype=np.float32)
+    if g.shape != (w.B, w.sum_D):
+        raise ValueError("grad_out must be [B][sum D]")
+    dG = [np.zeros(c.shape, dtype=np.float64) for c in cs]
+    darr = (C.c_void_p * len(dG))(*[x.ctypes.data for x in dG])
+    idx = np.ascontiguousarray(w.indices, dtype=np.int64)
+    off = np.ascontiguousarray(w.offsets, dtype=np.int64)
+    rc = lib.orc_backward_k(w.T, K, _ptr(N), _ptr(n), _ptr(d), _ptr(R), carr, _ptr(idx), _ptr(off), w.B,
+                            idx.shape[0], _ptr(g), darr)
+    if rc:
+        raise OracleError(rc)
+    return dG

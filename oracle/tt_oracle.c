@@ -770,3 +770,96 @@ int orc_forward_k_grouped(int32_t T, int32_t K, const int64_t *N, const int32_t 
     }
     return ORC_OK;
 }
+
+/* Backward of the pooled K-core forward for L = sum(grad_out * out), every
+ * index on its own (no reuse), lookups in CSR order.  The chain of one index
+ * is kept (V_1 .. V_K), then reversed (FlowTT 3.2: the backward reverses the
+ * contraction structure), core K-1 first:
+ *   V_{k+1}[p*d_k + j][r] = sum_q V_k[p][q] G_k[i_k][q][j][r]
+ *   dG_k[i_k][q][j][r]   += sum_p V_k[p][q] dV_{k+1}[p*d_k + j][r]
+ *   dV_k[p][q]            = sum_{j,r} dV_{k+1}[p*d_k + j][r] G_k[i_k][q][j][r]
+ * with dV_K = the index's bag row of grad_out and, since V_1 = G_0[i_0],
+ * dG_0[i_0] += dV_1.  dG (fp64, shaped like the cores, [T*K]) is overwritten;
+ * untouched slices are 0. */
+int orc_backward_k(int32_t T, int32_t K, const int64_t *N, const int32_t *n, const int32_t *d, const int32_t *R,
+                   const float *const *cores, const int64_t *indices, const int64_t *offsets, int64_t B,
+                   int64_t nnz, const float *grad_out, double *const *dG)
+{
+    int rc = check_tables_k(T, K, N, n, d, R);
+    if (rc) return rc;
+    rc = check_csr_k(T, N, indices, offsets, B, nnz);
+    if (rc) return rc;
+    int64_t maxD;
+    const int64_t maxP = maxp_k(T, K, d, R, &maxD);
+    int64_t SD = 0;
+    for (int t = 0; t < T; ++t) {
+        int64_t D = 1;
+        for (int k = 0; k < K; ++k) D *= d[K * t + k];
+        SD += D;
+    }
+    double *chain = (double *)malloc(sizeof(double) * (size_t)(K * maxP));
+    double *dv = (double *)malloc(sizeof(double) * (size_t)(2 * maxP));
+    if (!chain || !dv) {
+        free(chain);
+        free(dv);
+        return ORC_ERR_NOMEM;
+    }
+    int64_t col = 0;
+    for (int t = 0; t < T; ++t) {
+        const int32_t *nt = n + K * t, *dt = d + K * t, *Rt = R + (K + 1) * t;
+        const float *const *G = cores + (size_t)K * t;
+        double *const *dGt = dG + (size_t)K * t;
+        int64_t P[ORC_MAXK + 1];
+        P[0] = 1;
+        for (int k = 0; k < K; ++k) P[k + 1] = P[k] * dt[k];
+        for (int k = 0; k < K; ++k)
+            memset(dGt[k], 0, sizeof(double) * (size_t)nt[k] * Rt[k] * dt[k] * Rt[k + 1]);
+        for (int64_t b = 0; b < B; ++b) {
+            const float *g = grad_out + (size_t)(b * SD + col);
+            for (int64_t l = offsets[(int64_t)t * B + b]; l < offsets[(int64_t)t * B + b + 1]; ++l) {
+                int64_t dig[ORC_MAXK];
+                decode_k(indices[l], K, nt, dig);
+                /* forward chain: chain + (m-1)*maxP holds V_m ([P_m][R_m]) */
+                const float *g0 = G[0] + (size_t)dig[0] * dt[0] * Rt[1];
+                for (int64_t e = 0; e < P[1] * Rt[1]; ++e) chain[e] = (double)g0[e];
+                for (int k = 1; k < K; ++k)
+                    chain_step(chain + (size_t)(k - 1) * maxP, P[k], Rt[k], G[k], dt[k], Rt[k + 1], dig[k],
+                               chain + (size_t)k * maxP);
+                /* reverse: dV_K = g */
+                double *dcur = dv, *dnext = dv + maxP;
+                for (int64_t e = 0; e < P[K]; ++e) dcur[e] = (double)g[e];
+                for (int k = K - 1; k >= 1; --k) {
+                    const double *Vk = chain + (size_t)(k - 1) * maxP; /* [P_k][R_k] */
+                    const float *gs = G[k] + (size_t)dig[k] * Rt[k] * dt[k] * Rt[k + 1];
+                    double *dgs = dGt[k] + (size_t)dig[k] * Rt[k] * dt[k] * Rt[k + 1];
+                    const int32_t Rin = Rt[k], dk = dt[k], Rout = Rt[k + 1];
+                    for (int32_t q = 0; q < Rin; ++q)
+                        for (int32_t j = 0; j < dk; ++j)
+                            for (int32_t r = 0; r < Rout; ++r) {
+                                double acc = 0.0;
+                                for (int64_t p = 0; p < P[k]; ++p)
+                                    acc += Vk[p * Rin + q] * dcur[(p * dk + j) * Rout + r];
+                                dgs[((size_t)q * dk + j) * Rout + r] += acc;
+                            }
+                    for (int64_t p = 0; p < P[k]; ++p)
+                        for (int32_t q = 0; q < Rin; ++q) {
+                            double acc = 0.0;
+                            for (int32_t j = 0; j < dk; ++j)
+                                for (int32_t r = 0; r < Rout; ++r)
+                                    acc += dcur[(p * dk + j) * Rout + r] * (double)gs[((size_t)q * dk + j) * Rout + r];
+                            dnext[p * Rin + q] = acc;
+                        }
+                    double *tmp = dcur;
+                    dcur = dnext;
+                    dnext = tmp;
+                }
+                double *dg0 = dGt[0] + (size_t)dig[0] * dt[0] * Rt[1];
+                for (int64_t e = 0; e < P[1] * Rt[1]; ++e) dg0[e] += dcur[e];
+            }
+        }
+        col += P[K];
+    }
+    free(chain);
+    free(dv);
+    return ORC_OK;
+}

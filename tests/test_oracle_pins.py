@@ -472,3 +472,69 @@ def test_kcore_workload_factors_cover_the_rows():
         assert np.prod(t.n) >= t.N and len(t.n) == t.K == len(t.d) == len(t.R) - 1
         assert [c.shape for c in w.cores] == t.core_shapes()
         assert w.indices.min() >= 0 and w.indices.max() < t.N
+
+
+def _torch_grads_k(w):
+    """Gradients of sum(grad_out * out) for K-core tables through a dense
+    torch.einsum table and embedding_bag, float64 on the CPU."""
+    K = len(w.tables[0].n)
+    I, J, Rl = "abcdefgh"[:K], "ijklmnop"[:K], "qrstuvwxy"[: K + 1]
+    subs = ",".join(f"{I[k]}{Rl[k]}{J[k]}{Rl[k + 1]}" for k in range(K))
+    grads = []
+    col = w.col_offsets()
+    go = torch.from_numpy(w.grad_out.astype(np.float64))
+    for t, tab in enumerate(w.tables):
+        G = [torch.tensor(c.astype(np.float64), requires_grad=True) for c in w.cores[K * t:K * t + K]]
+        dense = torch.einsum(f"{subs}->{I}{J}", *G).reshape(int(np.prod(tab.n)), tab.D)[: tab.N]
+        lo, hi = w.offsets[t * w.B], w.offsets[(t + 1) * w.B]
+        out = torch.nn.functional.embedding_bag(torch.from_numpy(w.indices[lo:hi]), dense,
+                                                torch.from_numpy(w.offsets[t * w.B:(t + 1) * w.B] - lo),
+                                                mode="sum")
+        (out * go[:, col[t]:col[t + 1]]).sum().backward()
+        grads.extend(g.grad.numpy() for g in G)
+    return grads
+
+
+@pytest.mark.parametrize("n,d,R", [
+    ((3, 2, 4, 2), (2, 3, 2, 2), (1, 3, 2, 4, 1)),
+    ((2, 3, 2, 2, 3), (2, 2, 1, 3, 2), (1, 2, 3, 2, 2, 1)),
+])
+def test_kcore_backward_matches_torch_autograd_dense(n, d, R):
+    tabs = [_table(int(np.prod(n)) - 1, n, d, R, sigma=0.4), _table(int(np.prod(n)) // 2, n, d, R, sigma=0.3)]
+    w = _random_workload(tabs, 19, seed=41)
+    w.grad_out = np.random.default_rng(42).standard_normal((w.B, w.sum_D)).astype(np.float32)
+    got = oracle.backward_k(w)
+    ref = _torch_grads_k(w)
+    assert len(got) == len(ref) == 2 * len(n)
+    for g, r in zip(got, ref):
+        assert g.shape == r.shape
+        assert np.abs(g - r).max() <= 1e-12 * max(np.abs(r).max(), 1e-300)
+
+
+def test_kcore_backward_matches_exact_finite_differences():
+    """The pooled loss is affine in each core entry: a central difference over
+    the stored fp32 perturbation equals the gradient up to fp64 rounding."""
+    n, d, R = (3, 2, 4, 2), (2, 3, 2, 2), (1, 3, 2, 4, 1)
+    w = _random_workload([_table(40, n, d, R, sigma=0.4)], 12, seed=43)
+    w.grad_out = np.random.default_rng(44).standard_normal((w.B, w.sum_D)).astype(np.float32)
+    dG = oracle.backward_k(w)
+    go = w.grad_out.astype(np.float64)
+    rng = np.random.default_rng(45)
+    for k in range(4):
+        c = w.cores[k]
+        for f in rng.choice(c.size, size=min(c.size, 25), replace=False):
+            pos = np.unravel_index(int(f), c.shape)
+            cp, cm = [x.copy() for x in w.cores], [x.copy() for x in w.cores]
+            cp[k][pos] = np.float32(c[pos] + np.float32(0.01))
+            cm[k][pos] = np.float32(c[pos] - np.float32(0.01))
+            step = float(cp[k][pos]) - float(cm[k][pos])
+            fd = ((oracle.forward_k(w, cores=cp) - oracle.forward_k(w, cores=cm)) * go).sum() / step
+            assert abs(fd - dG[k][pos]) <= 1e-9 * max(1.0, abs(dG[k][pos])), (k, pos)
+
+
+def test_kcore_backward_with_three_cores_equals_the_three_core_oracle():
+    w = W.make_workload(5, bags=8)
+    a = oracle.backward_k(w)
+    b = oracle.backward(w)
+    for x, y in zip(a, b):
+        assert np.abs(x - y).max() <= 1e-12 * max(np.abs(y).max(), 1e-300)
