@@ -240,7 +240,11 @@ def kcore_extras(torch, tt, W, opts, args):
     out = {}
     for name in ("k4", "k5"):
         wk = W.make_kcore_workload(name)
+        wk.grad_out = W.make_grad_out(wk, 20300 + len(wk.tables[0].n))
         bk = Bench(wk, torch, tt, opts)
+        # training step on the K-core tables: forward, backward to all K cores, SGD
+        tms, _, tph = bk.timed(bk.train_step, args.steps, args.warmup)
+        tphase, _, _ = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in tph.items() if v[1]})
         ms, _, ph = bk.timed(bk.fwd, args.steps, args.warmup)
         phase, _, stages = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in ph.items() if v[1]})
         fg, fd = kcore_flops(wk.tables, wk.indices, wk.offsets, wk.B)
@@ -252,6 +256,7 @@ def kcore_extras(torch, tt, W, opts, args):
             "contract_flops": fg, "contract_flops_without_reuse": fd,
             "contract_tflops": fg / (cms * 1e-3) / 1e12 if cms else None,
             "contract_frac_fp32_peak": fg / (cms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS if cms else None,
+            "train_step": {"ms": tms, "lookups_per_s": wk.nnz / (tms * 1e-3), "phases_ms": tphase},
         }
         del bk
         torch.cuda.empty_cache()

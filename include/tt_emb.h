@@ -155,12 +155,18 @@ int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const in
  * (i = ((i_0 n_1 + i_1) n_2 + ...) n_{K-1} + i_{K-1}) and so are output
  * columns.  K = 3 is exactly tt_emb_create.  For K >= 4 the forward takes a
  * host array of T*K core pointers and computes every distinct prefix of
- * length 2 .. K-1 once (plain fp32, no matrix cores); tt_emb_backward and
- * tt_emb_sgd_update return TT_EMB_ERR_UNSUPPORTED, and the forward flags
- * TT_EMB_KEEP_PREFIX / TT_EMB_ATOMIC_POOL give TT_EMB_ERR_ARG.  Beyond the
+ * length 2 .. K-1 once (plain fp32, no matrix cores).  tt_emb_backward takes
+ * the same T*K core pointers and T*K gradient pointers (overwritten, shaped
+ * like the cores): the chain is reversed with the same prefix sharing, each
+ * group's intermediate gradient formed once from its children, and every core
+ * slice's gradient summed from per-row / per-group partials in a fixed order
+ * (no atomics, bit-reproducible); tt_emb_sgd_update updates the T*K cores.
+ * The forward flags TT_EMB_KEEP_PREFIX / TT_EMB_ATOMIC_POOL and the backward
+ * flag TT_EMB_REUSE_PREFIX give TT_EMB_ERR_ARG.  Beyond the
  * three-core limits: TT_EMB_ERR_UNSUPPORTED when T*K > 192, K = 2, K > 8,
  * the leading K-1 digits of all tables span 2^31 or more prefixes, the
- * product n_1 .. n_{K-1} of some table exceeds 2^32 - 1, or an
+ * product n_1 .. n_{K-1} of some table exceeds 2^32 - 1, some n_k summed
+ * over the tables exceeds 2^30 - 1, or an
  * intermediate or core slice of some level exceeds 8192 floats; K < 2 is
  * TT_EMB_ERR_ARG.  The grouping view of such a handle groups unique rows by
  * their leading K-1 digits (grp_prefix = row div n_{K-1}). */

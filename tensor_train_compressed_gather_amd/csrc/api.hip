@@ -48,6 +48,7 @@ struct tt_emb {
     int cls_mask, gcls_mask;
     int K = 3;                 // TT cores per table
     std::vector<KTab> ktabs;   // K >= 4 only
+    std::vector<int32_t> kn;   // K >= 4 only: n_k of every table, [T*K]
     KTab *dkt = nullptr;
 };
 
@@ -264,8 +265,49 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
             kp.V[m] = (float *)take(4 * (size_t)(gb * sm));
             kp.smax[m] = sm;
         }
+        // backward: groups of the first digit, the intermediates' gradients and
+        // the per-group / per-row core partials
+        for (int m = 1; m <= h->K - 1; ++m) {
+            int64_t gb = 0, sm = 1, qm = 1;
+            for (int t = 0; t < T; ++t) {
+                const KTab &kt = h->ktabs[t];
+                int64_t prod = 1;
+                for (int j = 0; j < m; ++j) prod = std::min<int64_t>(prod * kt.n[j], (int64_t)1 << 40);
+                gb += std::min<int64_t>(std::min<int64_t>(prod, h->tabs[t].N), n);
+                sm = std::max<int64_t>(sm, (int64_t)kt.P[m] * kt.R[m]);
+                if (m >= 2) qm = std::max<int64_t>(qm, (int64_t)kt.R[m - 1] * kt.d[m - 1] * kt.R[m]);
+            }
+            gb = std::min<int64_t>(gb, n);
+            if (m == 1) {
+                kp.ugrp[1] = (int32_t *)take(4 * n);
+                kp.gfirst[1] = (int32_t *)take(4 * (n + 1));
+                kp.smax[1] = sm;
+            }
+            kp.dV[m] = (float *)take(4 * (size_t)(gb * sm));
+            if (m >= 2) {
+                kp.Q[m] = (float *)take(4 * (size_t)(gb * qm));
+                kp.qmax[m] = qm;
+            }
+        }
+        int64_t pk = 1;
+        for (int t = 0; t < T; ++t) {
+            const KTab &kt = h->ktabs[t];
+            pk = std::max<int64_t>(pk, (int64_t)kt.R[h->K - 1] * kt.d[h->K - 1]);
+        }
+        kp.pkmax = pk;
+        kp.PK = (float *)take(4 * (size_t)(n * pk));
+        for (int k = 0; k < h->K; ++k) {
+            int64_t tot = 0;
+            for (int t = 0; t < T; ++t) tot += h->ktabs[t].n[k];
+            int bits = 1;
+            while (((int64_t)1 << bits) <= tot) ++bits;
+            kp.key_bits[k] = bits;
+        }
     }
-    if (p) p->kp = kp;
+    if (p) {
+        p->kp = kp;
+        p->kp_n = h->K >= 4 ? h->kn.data() : nullptr;
+    }
     return off;
 }
 
@@ -508,6 +550,7 @@ int tt_emb_create_k(int32_t T, int32_t K, const int64_t *num_rows, const int32_t
             if (kt.div[0] > (int64_t)0xffffffff) rc = TT_EMB_ERR_UNSUPPORTED;
             kt.P[0] = 1;
             for (int m = 1; m <= K; ++m) kt.P[m] = kt.P[m - 1] * dt[m - 1];
+            for (int k = 0; k < K; ++k) kt.nbase[k] = t == 0 ? 0 : kts[t - 1].nbase[k] + kts[t - 1].n[k];
             // staged operands of every level must fit in LDS
             for (int m = 2; m <= K - 1; ++m)
                 if ((int64_t)kt.P[m - 1] * kt.R[m - 1] > kKLds || (int64_t)kt.R[m - 1] * dt[m - 1] * Rt[m] > kKLds)
@@ -521,11 +564,14 @@ int tt_emb_create_k(int32_t T, int32_t K, const int64_t *num_rows, const int32_t
             n3[3 * t + 2] = nt[K - 1];
             d3[3 * t + 2] = (int32_t)std::min<int64_t>(D, 1 << 20);
         }
+        for (int k = 0; k < K; ++k) // backward sort keys of core-k slices fit 31 bits
+            if ((int64_t)kts[T - 1].nbase[k] + kts[T - 1].n[k] > 0x3fffffff) rc = TT_EMB_ERR_UNSUPPORTED;
         if (rc != TT_EMB_OK) return rc;
         if ((rc = tt_emb_create(T, num_rows, n3.data(), d3.data(), R3.data(), opt, out)) != TT_EMB_OK) return rc;
         tt_emb *h = *out;
         h->K = K;
         h->ktabs = kts;
+        h->kn.assign(n, n + (size_t)T * K);
         if (hipMalloc((void **)&h->dkt, sizeof(KTab) * T) != hipSuccess ||
             hipMemcpy(h->dkt, kts.data(), sizeof(KTab) * T, hipMemcpyHostToDevice) != hipSuccess) {
             tt_emb_destroy(h);
@@ -638,7 +684,21 @@ int tt_emb_backward(tt_emb_t h, const float *grad_out, const float *const *cores
         int rc = check_call(h, B, nnz, indices, offsets, ws, ws_bytes, &p);
         if (rc) return rc;
         if (B > 0 && !grad_out) return TT_EMB_ERR_ARG;
-        if (h->K != 3) return TT_EMB_ERR_UNSUPPORTED; // the backward covers three cores
+        if (h->K >= 4) {
+            // tables of K >= 4 cores: the chain reversed with prefix sharing
+            if (flags & TT_EMB_REUSE_PREFIX) return TT_EMB_ERR_ARG;
+            KCorePtrs kc{};
+            if ((rc = kcore_ptrs(h, cores, &kc))) return rc;
+            if (!core_grads) return TT_EMB_ERR_ARG;
+            for (int i = 0; i < h->T * h->K; ++i)
+                if (bad_ptr(core_grads[i])) return TT_EMB_ERR_ARG;
+            if ((rc = set_device(h))) return rc;
+            hipStream_t s = (hipStream_t)stream;
+            if (!(flags & TT_EMB_REUSE_GROUPING)) {
+                if ((rc = hip_status(launch_grouping(p, indices, offsets, s)))) return rc;
+            }
+            return hip_status(launch_backward_k(p, grad_out, kc, offsets, core_grads, s));
+        }
         CorePtrs cp{};
         if ((rc = core_ptrs(h, cores, &cp))) return rc;
         if (!core_grads) return TT_EMB_ERR_ARG;
@@ -666,22 +726,27 @@ int tt_emb_backward(tt_emb_t h, const float *grad_out, const float *const *cores
 int tt_emb_sgd_update(tt_emb_t h, float *const *cores, const float *const *core_grads, float lr, void *stream)
 {
     if (!h || !cores || !core_grads) return TT_EMB_ERR_ARG;
-    if (h->K != 3) return TT_EMB_ERR_UNSUPPORTED;
-    for (int i = 0; i < 3 * h->T; ++i)
+    const int nc = h->K * h->T; // cores of the handle (three per table, or K)
+    for (int i = 0; i < nc; ++i)
         if (bad_ptr(cores[i]) || bad_ptr(core_grads[i])) return TT_EMB_ERR_ARG;
     int rc = set_device(h);
     if (rc) return rc;
     hipStream_t s = (hipStream_t)stream;
     Timing *tm = (h->timing && h->timing->on) ? h->timing : nullptr;
     timer_begin(tm, TM_SGD, s);
-    std::vector<int64_t> cnt(3 * (size_t)h->T);
+    std::vector<int64_t> cnt((size_t)nc);
     for (int t = 0; t < h->T; ++t) {
+        if (h->K >= 4) {
+            const KTab &kt = h->ktabs[t];
+            for (int k = 0; k < h->K; ++k) cnt[(size_t)h->K * t + k] = (int64_t)kt.n[k] * kt.R[k] * kt.d[k] * kt.R[k + 1];
+            continue;
+        }
         const TableDesc &d = h->tabs[t];
         cnt[3 * t + 0] = (int64_t)d.n1 * d.d1 * d.R1;
         cnt[3 * t + 1] = (int64_t)d.n2 * d.R1 * d.d2 * d.R2;
         cnt[3 * t + 2] = (int64_t)d.n3 * d.R2 * d.d3;
     }
-    if (launch_sgd(cores, core_grads, cnt.data(), 3 * h->T, lr, s) != hipSuccess) return TT_EMB_ERR_HIP;
+    if (launch_sgd(cores, core_grads, cnt.data(), nc, lr, s) != hipSuccess) return TT_EMB_ERR_HIP;
     timer_end(tm, TM_SGD, s);
     return TT_EMB_OK;
 }

@@ -1247,15 +1247,11 @@ hipError_t launch_lookup_meta(const Plan &p, const int64_t *offsets, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs &cores,
-                           const int64_t *offsets, const GradPtrs &grads, hipStream_t s)
+hipError_t launch_gu_gather(const Plan &p, const float *grad_out, const int64_t *offsets, hipStream_t s)
 {
-    BwdArgs a{p.dtab, p.T, p.B, p.ws, cores, grads, grad_out, offsets, p.nnz, p.sumD, p.Dpmax, p.force_generic,
-              p.g1stride, p.g2p_slots};
+    BwdArgs a{p.dtab, p.T, p.B, p.ws, CorePtrs{}, GradPtrs{}, grad_out, offsets, p.nnz, p.sumD, p.Dpmax,
+              p.force_generic, p.g1stride, p.g2p_slots};
     const int T = p.T;
-    const int sum_n1 = p.sum_n[0], sum_n3 = p.sum_n[2];
-    timer_begin(p.timing, TM_BWD_GATHER, s);
-    hipLaunchKernelGGL(k_zero_g2, dim3(256, T), dim3(kThreads), 0, s, a);
     if (p.nnz > 0) {
         const int64_t nbags = (int64_t)T * p.B;
         int g = ceil_div(nbags, kThreads);
@@ -1288,6 +1284,22 @@ hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs 
         int gj = ceil_div(tasks, kThreads / 64);
         gj = gj > 4096 ? 4096 : gj;
         hipLaunchKernelGGL(k_gu_join, dim3(gj), dim3(kThreads), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs &cores,
+                           const int64_t *offsets, const GradPtrs &grads, hipStream_t s)
+{
+    BwdArgs a{p.dtab, p.T, p.B, p.ws, cores, grads, grad_out, offsets, p.nnz, p.sumD, p.Dpmax, p.force_generic,
+              p.g1stride, p.g2p_slots};
+    const int T = p.T;
+    const int sum_n1 = p.sum_n[0], sum_n3 = p.sum_n[2];
+    timer_begin(p.timing, TM_BWD_GATHER, s);
+    hipLaunchKernelGGL(k_zero_g2, dim3(256, T), dim3(kThreads), 0, s, a);
+    {
+        hipError_t e = launch_gu_gather(p, grad_out, offsets, s);
+        if (e != hipSuccess) return e;
     }
     timer_end(p.timing, TM_BWD_GATHER, s);
     timer_begin(p.timing, TM_BWD_CONTRACT, s);

@@ -209,6 +209,7 @@ struct KTab {
     int32_t n[kMaxK], d[kMaxK], R[kMaxK + 1];
     int64_t div[kMaxK]; // product of n_j over j > k: digit k = row / div[k] % n[k]
     int32_t P[kMaxK + 1]; // product of d_j over j < m: rows of the prefix-m intermediate
+    int32_t nbase[kMaxK]; // sum of n_k over earlier tables (backward sort key of a core-k slice)
 };
 struct KCorePtrs {
     const float *g[kMaxKPtrs]; // table t, core k at t * K + k
@@ -220,6 +221,13 @@ struct KPlan {
     int32_t *gfirst[kMaxK];     // [U + 1] first unique row of each group
     float *V[kMaxK];            // [groups][smax[m]] prefix-m intermediates
     int64_t smax[kMaxK];        // floats per group of prefix length m
+    // backward (prefix lengths m = 1 .. K-1; m = 1 groups share the first digit)
+    float *dV[kMaxK];           // [groups][smax[m]] gradient of each group's intermediate
+    float *Q[kMaxK];            // [groups][qmax[m]] core m-1 partial of each prefix-m group
+    int64_t qmax[kMaxK];        // R_{m-1} * d_{m-1} * R_m, max over tables
+    float *PK;                  // [unique rows][pkmax] last-core partial of each unique row
+    int64_t pkmax;              // R_{K-1} * d_{K-1}, max over tables
+    int key_bits[kMaxK];        // sort key bits of the core-k slices (sum over tables of n_k)
 };
 
 struct Plan {
@@ -231,6 +239,7 @@ struct Plan {
     int keep_c, reuse_c; // forward stores C_p in Ws::Cg / backward reads it
     int pool_atomic;     // forward pools inside the contraction with float atomics
     KPlan kp;            // K >= 4 cores (kp.K == 0 for three-core handles)
+    const int32_t *kp_n; // host copy of n_k of every table, [T*K] (K >= 4 cores)
     bool any_generic;
     int cls_mask; // bit c set when some table is in MFMA rank class c
     int gcls_mask; // bit c set when some table is in gradient-gather class c
@@ -260,6 +269,11 @@ hipError_t launch_pool(const Plan &p, const int64_t *offsets, float *out, hipStr
 // Forward of K >= 4 cores: every prefix length's intermediates, rows, pooling (kcores.hip).
 hipError_t launch_forward_k(const Plan &p, const KCorePtrs &cores, const int64_t *offsets, float *out,
                             hipStream_t s);
+// Backward of K >= 4 cores into core_grads [T*K] (kcores.hip).
+hipError_t launch_backward_k(const Plan &p, const float *grad_out, const KCorePtrs &cores, const int64_t *offsets,
+                             float *const *core_grads, hipStream_t s);
+// Output-gradient rows g_u of every unique row into Ws::E (backward.hip).
+hipError_t launch_gu_gather(const Plan &p, const float *grad_out, const int64_t *offsets, hipStream_t s);
 // SGD and fills (misc.hip)
 constexpr int kSgdMaxCores = 32; // cores per SGD launch (kernel-argument batch)
 struct SgdBatch {

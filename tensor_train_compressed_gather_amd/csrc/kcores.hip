@@ -152,6 +152,214 @@ __global__ __launch_bounds__(kThreads) void k_krows(KArgs a)
     }
 }
 
+// ------------------------------------------------------------------ backward
+//
+// The backward reverses the chain (FlowTT section 3.2) with the same prefix
+// sharing as the forward: a group's intermediate gradient dV_m is formed once
+// from its children and passed up, and each core slice's gradient is the sum of
+// per-item partials (one per unique row for the last core, one per prefix
+// group for the middle cores, one per first-digit group for core 0) taken in
+// a fixed order -- the items sorted stably by (table, digit) -- with no atomics.
+
+// Last core (k = K-1), one wave per group g of prefix length K-1, its unique
+// rows u in order, g_u the output-gradient row of u ([P][d] with P = P_{K-1}):
+//   dV_{K-1}[g][p][q] = sum_u sum_j g_u[p][j] G_{K-1}[i(u)][q][j]
+//   partial of u:  PK[u][q][j] = sum_p V_{K-1}[g][p][q] g_u[p][j]
+__global__ __launch_bounds__(kThreads) void k_kb_last(KArgs a)
+{
+    const Ws &ws = a.ws;
+    const int K = a.kp.K, m = K - 1, lane = threadIdx.x & 63;
+    const int64_t ng = ws.ctrl[CTRL_KLEV + m];
+    const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + uni(threadIdx.x >> 6); g < ng; g += nw) {
+        const int u0 = uni(a.kp.gfirst[m][g]), u1 = uni(a.kp.gfirst[m][g + 1]);
+        const int t = uni(segment_of(ws.tab_uniq_start, a.T, u0));
+        const auto &kt = kconst(a.kp.dkt)[t];
+        const int P = kt.P[m], Rin = kt.R[m], dk = kt.d[K - 1], Dp = kconst(a.tab)[t].Dp;
+        const float *V = a.kp.V[m] + g * a.kp.smax[m];            // [P][Rin]
+        const float *GK = a.cores.g[t * K + K - 1];                // [n][Rin][dk]
+        const float *Et = ws.E + kconst(ws.ebase)[t];             // g_u rows, stride Dp
+        float *dV = a.kp.dV[m] + g * a.kp.smax[m];
+        for (int e0 = 0; e0 < P * Rin; e0 += 64) {
+            const int e = e0 + lane;
+            const int ec = e < P * Rin ? e : P * Rin - 1;
+            const int p = ec / Rin, q = ec - p * Rin;
+            float acc = 0.f;
+            for (int u = u0; u < u1; ++u) {
+                const float *gu = Et + (int64_t)u * Dp + p * dk;
+                const float *gs = GK + (int64_t)((uint32_t)ws.uniq_row[u] % (uint32_t)kt.n[K - 1]) * Rin * dk + q * dk;
+                for (int j = 0; j < dk; ++j) acc = fmaf(gu[j], gs[j], acc);
+            }
+            if (e < P * Rin) dV[e] = acc;
+        }
+        for (int u = u0; u < u1; ++u) {
+            const float *gu = Et + (int64_t)u * Dp;
+            float *pk = a.kp.PK + (int64_t)u * a.kp.pkmax;
+            for (int e0 = 0; e0 < Rin * dk; e0 += 64) {
+                const int e = e0 + lane;
+                const int ec = e < Rin * dk ? e : Rin * dk - 1;
+                const int q = ec / dk, j = ec - q * dk;
+                float acc = 0.f;
+                for (int p = 0; p < P; ++p) acc = fmaf(V[p * Rin + q], gu[p * dk + j], acc);
+                if (e < Rin * dk) pk[e] = acc;
+            }
+        }
+    }
+}
+
+// Level m (K-1 down to 2), one wave per parent group pg of prefix length m-1
+// and its children g (the prefix-m groups inside it, consecutive), core c =
+// m-1 with slice G = G_c[i_c(g)] ([Rin][dk * Rout]):
+//   dV_{m-1}[pg][p][q] = sum_g sum_{(j,r)} dV_m[g][p][(j,r)] G[q][(j,r)]
+//   partial of g:  Q_m[g][q][(j,r)] = sum_p V_{m-1}[pg][p][q] dV_m[g][p][(j,r)]
+// V_1 of a first-digit group is the core slice G_0[i_0].
+__global__ __launch_bounds__(kThreads) void k_kb_level(KArgs a, int m)
+{
+    const Ws &ws = a.ws;
+    const int K = a.kp.K, lane = threadIdx.x & 63, c = m - 1;
+    const int64_t np = ws.ctrl[CTRL_KLEV + m - 1];
+    const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t pg = (int64_t)blockIdx.x * (kThreads / 64) + uni(threadIdx.x >> 6); pg < np; pg += nw) {
+        const int r0 = uni(a.kp.gfirst[m - 1][pg]), r1 = uni(a.kp.gfirst[m - 1][pg + 1]);
+        const int g0 = uni(a.kp.ugrp[m][r0]), g1 = uni(a.kp.ugrp[m][r1 - 1]) + 1; // children [g0, g1)
+        const int t = uni(segment_of(ws.tab_uniq_start, a.T, r0));
+        const auto &kt = kconst(a.kp.dkt)[t];
+        const int P = kt.P[m - 1], Rin = kt.R[m - 1], dk = kt.d[c], Rout = kt.R[m], cols = dk * Rout;
+        const float *Vp;
+        if (m == 2) {
+            const uint32_t i0 = (uint32_t)ws.uniq_row[r0] / (uint32_t)kt.div[0] % (uint32_t)kt.n[0];
+            Vp = a.cores.g[t * K] + (int64_t)i0 * kt.d[0] * kt.R[1];
+        } else {
+            Vp = a.kp.V[m - 1] + pg * a.kp.smax[m - 1];
+        }
+        const float *Gc = a.cores.g[t * K + c];
+        float *dVp = a.kp.dV[m - 1] + pg * a.kp.smax[m - 1];
+        for (int e0 = 0; e0 < P * Rin; e0 += 64) {
+            const int e = e0 + lane;
+            const int ec = e < P * Rin ? e : P * Rin - 1;
+            const int p = ec / Rin, q = ec - p * Rin;
+            float acc = 0.f;
+            for (int g = g0; g < g1; ++g) {
+                const uint32_t ic = (uint32_t)ws.uniq_row[a.kp.gfirst[m][g]] / (uint32_t)kt.div[c] % (uint32_t)kt.n[c];
+                const float *gs = Gc + (int64_t)ic * Rin * cols + q * cols;
+                const float *dv = a.kp.dV[m] + g * a.kp.smax[m] + p * cols;
+                for (int jr = 0; jr < cols; ++jr) acc = fmaf(dv[jr], gs[jr], acc);
+            }
+            if (e < P * Rin) dVp[e] = acc;
+        }
+        for (int g = g0; g < g1; ++g) {
+            const float *dv = a.kp.dV[m] + g * a.kp.smax[m];
+            float *qo = a.kp.Q[m] + g * a.kp.qmax[m];
+            for (int e0 = 0; e0 < Rin * cols; e0 += 64) {
+                const int e = e0 + lane;
+                const int ec = e < Rin * cols ? e : Rin * cols - 1;
+                const int q = ec / cols, jr = ec - q * cols;
+                float acc = 0.f;
+                for (int p = 0; p < P; ++p) acc = fmaf(Vp[p * Rin + q], dv[p * cols + jr], acc);
+                if (e < Rin * cols) qo[e] = acc;
+            }
+        }
+    }
+}
+
+// Sort keys of the items whose partials make up core k's slices: item i is a
+// unique row (k = K-1) or a group of prefix length m (k = m-1; m = 1 for
+// k = 0); key = the slice (table base + digit k of the item's first row).
+__global__ __launch_bounds__(kThreads) void k_kb_keys(KArgs a, int k, int m, uint32_t *keys, int32_t *vals)
+{
+    const Ws &ws = a.ws;
+    const int64_t n = m == 0 ? ws.ctrl[CTRL_U] : ws.ctrl[CTRL_KLEV + m];
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int u = m == 0 ? (int)i : a.kp.gfirst[m][i];
+        const int t = segment_of(ws.tab_uniq_start, a.T, u);
+        const KTab &kt = a.kp.dkt[t];
+        const uint32_t dig = (uint32_t)ws.uniq_row[u] / (uint32_t)kt.div[k] % (uint32_t)kt.n[k];
+        keys[i] = (uint32_t)kt.nbase[k] + dig;
+        vals[i] = (int32_t)i;
+    }
+}
+
+// dG_k of table t, one block per slice: the partials of its items in sorted
+// (stable) order, summed; 0 where no item has that digit (m < 0: no items).
+__global__ __launch_bounds__(kThreads) void k_kb_reduce(KArgs a, int t, int k, int m, const uint32_t *keys,
+                                                        const int32_t *vals, const float *part, int64_t pstride,
+                                                        float *dG)
+{
+    const Ws &ws = a.ws;
+    const KTab &kt = a.kp.dkt[t];
+    const int64_t n = m < 0 ? 0 : (m == 0 ? ws.ctrl[CTRL_U] : ws.ctrl[CTRL_KLEV + m]);
+    const int S = kt.R[k] * kt.d[k] * kt.R[k + 1];
+    for (int i = blockIdx.x; i < kt.n[k]; i += gridDim.x) {
+        const uint32_t key = (uint32_t)kt.nbase[k] + (uint32_t)i;
+        int64_t lo = 0, hi = n; // first item with key >= key
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (keys[mid] < key) lo = mid + 1;
+            else hi = mid;
+        }
+        int64_t end = lo;
+        while (end < n && keys[end] == key) ++end;
+        for (int e = threadIdx.x; e < S; e += blockDim.x) {
+            float acc = 0.f;
+            for (int64_t j = lo; j < end; ++j) acc += part[(int64_t)vals[j] * pstride + e];
+            dG[(int64_t)i * S + e] = acc;
+        }
+    }
+}
+
+hipError_t launch_backward_k(const Plan &p, const float *grad_out, const KCorePtrs &cores, const int64_t *offsets,
+                             float *const *core_grads, hipStream_t s)
+{
+    KArgs a{p.dtab, p.T, p.ws, p.kp, cores};
+    const int K = p.kp.K;
+    timer_begin(p.timing, TM_BWD_GATHER, s);
+    hipError_t e = launch_gu_gather(p, grad_out, offsets, s);
+    if (e != hipSuccess) return e;
+    timer_end(p.timing, TM_BWD_GATHER, s);
+    timer_begin(p.timing, TM_BWD_CONTRACT, s);
+    const int g = p.num_blocks * 16;
+    if (p.nnz > 0) {
+        // groups of every prefix length 1..K-1 and the forward intermediates
+        for (int m = 1; m <= K - 1; ++m) {
+            KLevOp op{a, m};
+            if ((e = run_scan(op, p.ws.part, scan_blocks(p.nnz), s)) != hipSuccess) return e;
+        }
+        for (int m = 2; m <= K - 1; ++m) hipLaunchKernelGGL(k_klevel, dim3(g), dim3(kThreads), 0, s, a, m);
+        hipLaunchKernelGGL(k_kb_last, dim3(g), dim3(kThreads), 0, s, a);
+        for (int m = K - 1; m >= 2; --m) hipLaunchKernelGGL(k_kb_level, dim3(g), dim3(kThreads), 0, s, a, m);
+    }
+    timer_end(p.timing, TM_BWD_CONTRACT, s);
+    timer_begin(p.timing, TM_BWD_REDUCE, s);
+    for (int k = 0; k < K; ++k) {
+        // items of core k: first-digit groups (k = 0), prefix-(k+1) groups, unique rows (k = K-1)
+        const int m = k == K - 1 ? 0 : k + 1;
+        const float *part = k == K - 1 ? p.kp.PK : (k == 0 ? p.kp.dV[1] : p.kp.Q[k + 1]);
+        const int64_t pstride = k == K - 1 ? p.kp.pkmax : (k == 0 ? p.kp.smax[1] : p.kp.qmax[k + 1]);
+        const uint32_t *keys = p.ws.keys0;
+        const int32_t *vals = p.ws.u3order;
+        if (p.nnz > 0) {
+            int gk = ceil_div(p.nnz, kThreads);
+            gk = gk > 4096 ? 4096 : gk;
+            hipLaunchKernelGGL(k_kb_keys, dim3(gk), dim3(kThreads), 0, s, a, k, m, p.ws.keys0, p.ws.u3order);
+            bool in1 = false;
+            const int32_t *cnt = m == 0 ? &p.ws.ctrl[CTRL_U] : &p.ws.ctrl[CTRL_KLEV + m];
+            if ((e = radix_sort_pairs(p, p.ws.keys0, p.ws.u3order, p.ws.keys1, p.ws.uvals_free, p.nnz, cnt,
+                                      p.kp.key_bits[k], &in1, s)) != hipSuccess)
+                return e;
+            keys = in1 ? p.ws.keys1 : p.ws.keys0;
+            vals = in1 ? p.ws.uvals_free : p.ws.u3order;
+        }
+        // a call with no lookups reads no item and zeroes every slice
+        for (int t = 0; t < p.T; ++t) {
+            const int ns = p.kp_n[t * K + k];
+            hipLaunchKernelGGL(k_kb_reduce, dim3(ns < 1024 ? ns : 1024), dim3(kThreads), 0, s, a, t, k,
+                               p.nnz > 0 ? m : -1, keys, vals, part, pstride, core_grads[t * K + k]);
+        }
+    }
+    timer_end(p.timing, TM_BWD_REDUCE, s);
+    return hipGetLastError();
+}
+
 hipError_t launch_forward_k(const Plan &p, const KCorePtrs &cores, const int64_t *offsets, float *out,
                             hipStream_t s)
 {

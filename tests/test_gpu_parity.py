@@ -590,5 +590,71 @@ def test_kcore_unsupported_calls_are_rejected():
     assert e.value.status == tt.TT_EMB_ERR_ARG
     run.forward()
     with pytest.raises(tt.TTEmbError) as e:
-        run.backward(np.zeros((w.B, w.sum_D), np.float32))
-    assert e.value.status == tt.TT_EMB_ERR_UNSUPPORTED
+        run.backward(np.zeros((w.B, w.sum_D), np.float32),
+                     flags=tt.TT_EMB_REUSE_GROUPING | tt.TT_EMB_REUSE_PREFIX)
+    assert e.value.status == tt.TT_EMB_ERR_ARG
+
+
+@pytest.mark.parametrize("name,bags", [("k4", 256), ("k5", 256)])
+def test_kcore_backward_matches_oracle(name, bags):
+    w = W.make_kcore_workload(name, bags=bags)
+    w.grad_out = np.random.default_rng(51).standard_normal((w.B, w.sum_D)).astype(np.float32)
+    run = Run(w)
+    run.forward()
+    got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
+    assert len(got) == len(w.cores)
+    assert_grads_close(got, oracle.backward_k(w))
+    # bit-reproducible, with or without the kept grouping
+    again = [g.cpu().numpy() for g in run.backward(w.grad_out)]
+    for a, b in zip(got, again):
+        assert np.array_equal(a, b)
+
+
+def test_kcore_backward_mixed_shapes_and_sgd():
+    tables = [W.Table(5000, (4, 5, 6, 50), (4, 4, 4, 8), (1, 8, 24, 12, 1), 0.2, "uniform"),
+              W.Table(77, (2, 3, 2, 7), (3, 1, 2, 5), (1, 5, 3, 7, 1), 0.3, "uniform"),
+              W.Table(999, (10, 10, 10, 1), (2, 2, 2, 2), (1, 16, 16, 16, 1), 0.2, "uniform"),
+              W.Table(40000, (20, 20, 20, 5), (2, 4, 4, 4), (1, 32, 32, 32, 1), 0.05, "zipf", 1.1)]
+    rng = np.random.default_rng(52)
+    lens = [rng.integers(0, 12, size=50) for _ in tables]
+    lens[1][:] = 0  # a table with no lookups: zero gradients
+    idx = [rng.integers(0, t.N, size=int(l.sum())) for t, l in zip(tables, lens)]
+    idx[0][: len(idx[0]) // 2] = 4321
+    w = W.make_custom(tables, lens, idx, seed=52)
+    w.grad_out = rng.standard_normal((w.B, w.sum_D)).astype(np.float32)
+    run = Run(w)
+    got = [g.cpu().numpy() for g in run.backward(w.grad_out)]
+    ref = oracle.backward_k(w)
+    assert_grads_close(got, ref)
+    for k in range(4):
+        assert not got[4 + k].any()
+    # SGD on the T*K cores: the applied update is -lr * dG
+    before = [c.cpu().numpy().astype(np.float64) for c in run.cores]
+    grads = run.emb.backward(torch.from_numpy(w.grad_out).to(DEV), run.cores, run.idx, run.off, w.B)
+    run.emb.sgd_update(run.cores, grads, 0.01)
+    torch.cuda.synchronize()
+    for c, b0, r in zip(run.cores, before, ref):
+        delta = c.cpu().numpy().astype(np.float64) - b0
+        want = oracle.sgd_delta(r, 0.01)
+        ulp = np.spacing(np.abs(b0).astype(np.float32)).max()  # the update lands on the fp32 grid
+        assert np.abs(delta - want).max() <= TOL * np.abs(want).max() + ulp
+    # no lookups at all: every gradient is zero
+    w0 = W.make_custom(tables[:2], [np.zeros(4, np.int64)] * 2, [np.zeros(0, np.int64)] * 2, seed=53)
+    run0 = Run(w0)
+    g0 = run0.backward(np.zeros((4, w0.sum_D), np.float32))
+    assert all(not g.cpu().numpy().any() for g in g0)
+
+
+def test_kcore_full_size_backward_sampled_bags():
+    # the gradient is linear in grad_out: with grad_out zero outside a sample
+    # of bags, the full-size backward equals the oracle's on those bags alone
+    w = W.make_kcore_workload("k4")
+    rng = np.random.default_rng(54)
+    bags = np.unique(np.concatenate([[0, w.B - 1], rng.integers(0, w.B, 200)]))
+    go = np.zeros((w.B, w.sum_D), np.float32)
+    go[bags] = rng.standard_normal((len(bags), w.sum_D)).astype(np.float32)
+    run = Run(w)
+    got = [g.cpu().numpy() for g in run.backward(go)]
+    sub = _sub_bags(w, bags)
+    sub.grad_out = go[bags]
+    assert_grads_close(got, oracle.backward_k(sub))
