@@ -296,6 +296,14 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
         }
         kp.pkmax = pk;
         kp.PK = (float *)take(4 * (size_t)(n * pk));
+        // split sums of the per-slice reduction: 16 per slice of the largest core
+        int64_t red = 1;
+        for (int t = 0; t < T; ++t) {
+            const KTab &kt = h->ktabs[t];
+            for (int k = 0; k < h->K; ++k)
+                red = std::max<int64_t>(red, (int64_t)kt.n[k] * kt.R[k] * kt.d[k] * kt.R[k + 1] * 16);
+        }
+        kp.red = (float *)take(4 * (size_t)red);
         for (int k = 0; k < h->K; ++k) {
             int64_t tot = 0;
             for (int t = 0; t < T; ++t) tot += h->ktabs[t].n[k];

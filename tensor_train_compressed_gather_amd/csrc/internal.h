@@ -228,6 +228,7 @@ struct KPlan {
     float *PK;                  // [unique rows][pkmax] last-core partial of each unique row
     int64_t pkmax;              // R_{K-1} * d_{K-1}, max over tables
     int key_bits[kMaxK];        // sort key bits of the core-k slices (sum over tables of n_k)
+    float *red;                 // [n_k][16][slice] split sums of one (table, core) reduction
 };
 
 struct Plan {

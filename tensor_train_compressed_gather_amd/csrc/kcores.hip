@@ -211,8 +211,8 @@ __global__ __launch_bounds__(kThreads) void k_kb_last(KArgs a)
 // and its children g (the prefix-m groups inside it, consecutive), core c =
 // m-1 with slice G = G_c[i_c(g)] ([Rin][dk * Rout]):
 //   dV_{m-1}[pg][p][q] = sum_g sum_{(j,r)} dV_m[g][p][(j,r)] G[q][(j,r)]
-//   partial of g:  Q_m[g][q][(j,r)] = sum_p V_{m-1}[pg][p][q] dV_m[g][p][(j,r)]
-// V_1 of a first-digit group is the core slice G_0[i_0].
+// (the children's core partials are k_kb_q's).  V_1 of a first-digit group is
+// the core slice G_0[i_0].
 __global__ __launch_bounds__(kThreads) void k_kb_level(KArgs a, int m)
 {
     const Ws &ws = a.ws;
@@ -225,13 +225,6 @@ __global__ __launch_bounds__(kThreads) void k_kb_level(KArgs a, int m)
         const int t = uni(segment_of(ws.tab_uniq_start, a.T, r0));
         const auto &kt = kconst(a.kp.dkt)[t];
         const int P = kt.P[m - 1], Rin = kt.R[m - 1], dk = kt.d[c], Rout = kt.R[m], cols = dk * Rout;
-        const float *Vp;
-        if (m == 2) {
-            const uint32_t i0 = (uint32_t)ws.uniq_row[r0] / (uint32_t)kt.div[0] % (uint32_t)kt.n[0];
-            Vp = a.cores.g[t * K] + (int64_t)i0 * kt.d[0] * kt.R[1];
-        } else {
-            Vp = a.kp.V[m - 1] + pg * a.kp.smax[m - 1];
-        }
         const float *Gc = a.cores.g[t * K + c];
         float *dVp = a.kp.dV[m - 1] + pg * a.kp.smax[m - 1];
         for (int e0 = 0; e0 < P * Rin; e0 += 64) {
@@ -243,21 +236,44 @@ __global__ __launch_bounds__(kThreads) void k_kb_level(KArgs a, int m)
                 const uint32_t ic = (uint32_t)ws.uniq_row[a.kp.gfirst[m][g]] / (uint32_t)kt.div[c] % (uint32_t)kt.n[c];
                 const float *gs = Gc + (int64_t)ic * Rin * cols + q * cols;
                 const float *dv = a.kp.dV[m] + g * a.kp.smax[m] + p * cols;
+#pragma unroll 8
                 for (int jr = 0; jr < cols; ++jr) acc = fmaf(dv[jr], gs[jr], acc);
             }
             if (e < P * Rin) dVp[e] = acc;
         }
-        for (int g = g0; g < g1; ++g) {
-            const float *dv = a.kp.dV[m] + g * a.kp.smax[m];
-            float *qo = a.kp.Q[m] + g * a.kp.qmax[m];
-            for (int e0 = 0; e0 < Rin * cols; e0 += 64) {
-                const int e = e0 + lane;
-                const int ec = e < Rin * cols ? e : Rin * cols - 1;
-                const int q = ec / cols, jr = ec - q * cols;
-                float acc = 0.f;
-                for (int p = 0; p < P; ++p) acc = fmaf(Vp[p * Rin + q], dv[p * cols + jr], acc);
-                if (e < Rin * cols) qo[e] = acc;
-            }
+    }
+}
+
+// The core-(m-1) partial of every prefix-m group g, one wave per group:
+//   Q_m[g][q][(j,r)] = sum_p V_{m-1}[parent][p][q] dV_m[g][p][(j,r)]
+__global__ __launch_bounds__(kThreads) void k_kb_q(KArgs a, int m)
+{
+    const Ws &ws = a.ws;
+    const int K = a.kp.K, lane = threadIdx.x & 63, c = m - 1;
+    const int64_t ng = ws.ctrl[CTRL_KLEV + m];
+    const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + uni(threadIdx.x >> 6); g < ng; g += nw) {
+        const int r0 = uni(a.kp.gfirst[m][g]);
+        const int t = uni(segment_of(ws.tab_uniq_start, a.T, r0));
+        const auto &kt = kconst(a.kp.dkt)[t];
+        const int P = kt.P[m - 1], Rin = kt.R[m - 1], dk = kt.d[c], Rout = kt.R[m], cols = dk * Rout;
+        const float *Vp;
+        if (m == 2) {
+            const uint32_t i0 = (uint32_t)ws.uniq_row[r0] / (uint32_t)kt.div[0] % (uint32_t)kt.n[0];
+            Vp = a.cores.g[t * K] + (int64_t)i0 * kt.d[0] * kt.R[1];
+        } else {
+            Vp = a.kp.V[m - 1] + (int64_t)uni(a.kp.ugrp[m - 1][r0]) * a.kp.smax[m - 1];
+        }
+        const float *dv = a.kp.dV[m] + g * a.kp.smax[m];
+        float *qo = a.kp.Q[m] + g * a.kp.qmax[m];
+        for (int e0 = 0; e0 < Rin * cols; e0 += 64) {
+            const int e = e0 + lane;
+            const int ec = e < Rin * cols ? e : Rin * cols - 1;
+            const int q = ec / cols, jr = ec - q * cols;
+            float acc = 0.f;
+#pragma unroll 4
+            for (int p = 0; p < P; ++p) acc = fmaf(Vp[p * Rin + q], dv[p * cols + jr], acc);
+            if (e < Rin * cols) qo[e] = acc;
         }
     }
 }
@@ -279,16 +295,22 @@ __global__ __launch_bounds__(kThreads) void k_kb_keys(KArgs a, int k, int m, uin
     }
 }
 
-// dG_k of table t, one block per slice: the partials of its items in sorted
-// (stable) order, summed; 0 where no item has that digit (m < 0: no items).
-__global__ __launch_bounds__(kThreads) void k_kb_reduce(KArgs a, int t, int k, int m, const uint32_t *keys,
-                                                        const int32_t *vals, const float *part, int64_t pstride,
-                                                        float *dG)
+// dG_k of table t from the sorted partials, in two fixed-order passes so that
+// a slice with many items is spread over kKbSplit blocks: pass 1, block
+// (slice i, part c) sums part c of the slice's items (its stable sorted order,
+// cut into kKbSplit near-equal ranges, four interleaved accumulators added in a
+// fixed order) into red[i][c]; pass 2 adds the kKbSplit sums of each slice in
+// order.  A slice no item touches gets 0 (m < 0: no items at all).
+constexpr int kKbSplit = 16;
+__global__ __launch_bounds__(kThreads) void k_kb_reduce1(KArgs a, int t, int k, int m, const uint32_t *keys,
+                                                         const int32_t *vals, const float *part, int64_t pstride,
+                                                         float *red)
 {
     const Ws &ws = a.ws;
     const KTab &kt = a.kp.dkt[t];
     const int64_t n = m < 0 ? 0 : (m == 0 ? ws.ctrl[CTRL_U] : ws.ctrl[CTRL_KLEV + m]);
     const int S = kt.R[k] * kt.d[k] * kt.R[k + 1];
+    const int c = blockIdx.y;
     for (int i = blockIdx.x; i < kt.n[k]; i += gridDim.x) {
         const uint32_t key = (uint32_t)kt.nbase[k] + (uint32_t)i;
         int64_t lo = 0, hi = n; // first item with key >= key
@@ -297,14 +319,37 @@ __global__ __launch_bounds__(kThreads) void k_kb_reduce(KArgs a, int t, int k, i
             if (keys[mid] < key) lo = mid + 1;
             else hi = mid;
         }
-        int64_t end = lo;
-        while (end < n && keys[end] == key) ++end;
+        int64_t lo2 = lo, hi2 = n; // first item with key > key
+        while (lo2 < hi2) {
+            const int64_t mid = (lo2 + hi2) >> 1;
+            if (keys[mid] <= key) lo2 = mid + 1;
+            else hi2 = mid;
+        }
+        const int64_t len = lo2 - lo;
+        const int64_t b = lo + len * c / kKbSplit, e1 = lo + len * (c + 1) / kKbSplit;
         for (int e = threadIdx.x; e < S; e += blockDim.x) {
-            float acc = 0.f;
-            for (int64_t j = lo; j < end; ++j) acc += part[(int64_t)vals[j] * pstride + e];
-            dG[(int64_t)i * S + e] = acc;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            int64_t j = b;
+            for (; j + 4 <= e1; j += 4) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) acc[x] += part[(int64_t)vals[j + x] * pstride + e];
+            }
+            for (; j < e1; ++j) acc[0] += part[(int64_t)vals[j] * pstride + e];
+            red[((int64_t)i * kKbSplit + c) * S + e] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         }
     }
+}
+
+__global__ __launch_bounds__(kThreads) void k_kb_reduce2(KArgs a, int t, int k, const float *red, float *dG)
+{
+    const KTab &kt = a.kp.dkt[t];
+    const int S = kt.R[k] * kt.d[k] * kt.R[k + 1];
+    for (int i = blockIdx.x; i < kt.n[k]; i += gridDim.x)
+        for (int e = threadIdx.x; e < S; e += blockDim.x) {
+            float acc = 0.f;
+            for (int c = 0; c < kKbSplit; ++c) acc += red[((int64_t)i * kKbSplit + c) * S + e];
+            dG[(int64_t)i * S + e] = acc;
+        }
 }
 
 hipError_t launch_backward_k(const Plan &p, const float *grad_out, const KCorePtrs &cores, const int64_t *offsets,
@@ -326,7 +371,10 @@ hipError_t launch_backward_k(const Plan &p, const float *grad_out, const KCorePt
         }
         for (int m = 2; m <= K - 1; ++m) hipLaunchKernelGGL(k_klevel, dim3(g), dim3(kThreads), 0, s, a, m);
         hipLaunchKernelGGL(k_kb_last, dim3(g), dim3(kThreads), 0, s, a);
-        for (int m = K - 1; m >= 2; --m) hipLaunchKernelGGL(k_kb_level, dim3(g), dim3(kThreads), 0, s, a, m);
+        for (int m = K - 1; m >= 2; --m) {
+            hipLaunchKernelGGL(k_kb_level, dim3(g), dim3(kThreads), 0, s, a, m);
+            hipLaunchKernelGGL(k_kb_q, dim3(g), dim3(kThreads), 0, s, a, m);
+        }
     }
     timer_end(p.timing, TM_BWD_CONTRACT, s);
     timer_begin(p.timing, TM_BWD_REDUCE, s);
@@ -351,9 +399,10 @@ hipError_t launch_backward_k(const Plan &p, const float *grad_out, const KCorePt
         }
         // a call with no lookups reads no item and zeroes every slice
         for (int t = 0; t < p.T; ++t) {
-            const int ns = p.kp_n[t * K + k];
-            hipLaunchKernelGGL(k_kb_reduce, dim3(ns < 1024 ? ns : 1024), dim3(kThreads), 0, s, a, t, k,
-                               p.nnz > 0 ? m : -1, keys, vals, part, pstride, core_grads[t * K + k]);
+            const int ns = p.kp_n[t * K + k], gb = ns < 1024 ? ns : 1024;
+            hipLaunchKernelGGL(k_kb_reduce1, dim3(gb, kKbSplit), dim3(kThreads), 0, s, a, t, k, p.nnz > 0 ? m : -1,
+                               keys, vals, part, pstride, p.kp.red);
+            hipLaunchKernelGGL(k_kb_reduce2, dim3(gb), dim3(kThreads), 0, s, a, t, k, p.kp.red, core_grads[t * K + k]);
         }
     }
     timer_end(p.timing, TM_BWD_REDUCE, s);
