@@ -287,6 +287,7 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
             if (m >= 2) {
                 kp.Q[m] = (float *)take(4 * (size_t)(gb * qm));
                 kp.qmax[m] = qm;
+                kp.Cc[m] = (float *)take(4 * (size_t)(gb * kp.smax[m - 1]));
             }
         }
         int64_t pk = 1;

@@ -224,6 +224,7 @@ struct KPlan {
     // backward (prefix lengths m = 1 .. K-1; m = 1 groups share the first digit)
     float *dV[kMaxK];           // [groups][smax[m]] gradient of each group's intermediate
     float *Q[kMaxK];            // [groups][qmax[m]] core m-1 partial of each prefix-m group
+    float *Cc[kMaxK];           // [groups][smax[m-1]] each prefix-m group's share of its parent's dV
     int64_t qmax[kMaxK];        // R_{m-1} * d_{m-1} * R_m, max over tables
     float *PK;                  // [unique rows][pkmax] last-core partial of each unique row
     int64_t pkmax;              // R_{K-1} * d_{K-1}, max over tables

@@ -207,45 +207,14 @@ __global__ __launch_bounds__(kThreads) void k_kb_last(KArgs a)
     }
 }
 
-// Level m (K-1 down to 2), one wave per parent group pg of prefix length m-1
-// and its children g (the prefix-m groups inside it, consecutive), core c =
-// m-1 with slice G = G_c[i_c(g)] ([Rin][dk * Rout]):
+// Level m (K-1 down to 2), core c = m-1, per prefix-m group g with parent pg
+// (its prefix-(m-1) group) and core slice G = G_c[i_c(g)] ([Rin][dk * Rout]):
 //   dV_{m-1}[pg][p][q] = sum_g sum_{(j,r)} dV_m[g][p][(j,r)] G[q][(j,r)]
-// (the children's core partials are k_kb_q's).  V_1 of a first-digit group is
-// the core slice G_0[i_0].
-__global__ __launch_bounds__(kThreads) void k_kb_level(KArgs a, int m)
-{
-    const Ws &ws = a.ws;
-    const int K = a.kp.K, lane = threadIdx.x & 63, c = m - 1;
-    const int64_t np = ws.ctrl[CTRL_KLEV + m - 1];
-    const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
-    for (int64_t pg = (int64_t)blockIdx.x * (kThreads / 64) + uni(threadIdx.x >> 6); pg < np; pg += nw) {
-        const int r0 = uni(a.kp.gfirst[m - 1][pg]), r1 = uni(a.kp.gfirst[m - 1][pg + 1]);
-        const int g0 = uni(a.kp.ugrp[m][r0]), g1 = uni(a.kp.ugrp[m][r1 - 1]) + 1; // children [g0, g1)
-        const int t = uni(segment_of(ws.tab_uniq_start, a.T, r0));
-        const auto &kt = kconst(a.kp.dkt)[t];
-        const int P = kt.P[m - 1], Rin = kt.R[m - 1], dk = kt.d[c], Rout = kt.R[m], cols = dk * Rout;
-        const float *Gc = a.cores.g[t * K + c];
-        float *dVp = a.kp.dV[m - 1] + pg * a.kp.smax[m - 1];
-        for (int e0 = 0; e0 < P * Rin; e0 += 64) {
-            const int e = e0 + lane;
-            const int ec = e < P * Rin ? e : P * Rin - 1;
-            const int p = ec / Rin, q = ec - p * Rin;
-            float acc = 0.f;
-            for (int g = g0; g < g1; ++g) {
-                const uint32_t ic = (uint32_t)ws.uniq_row[a.kp.gfirst[m][g]] / (uint32_t)kt.div[c] % (uint32_t)kt.n[c];
-                const float *gs = Gc + (int64_t)ic * Rin * cols + q * cols;
-                const float *dv = a.kp.dV[m] + g * a.kp.smax[m] + p * cols;
-#pragma unroll 8
-                for (int jr = 0; jr < cols; ++jr) acc = fmaf(dv[jr], gs[jr], acc);
-            }
-            if (e < P * Rin) dVp[e] = acc;
-        }
-    }
-}
-
-// The core-(m-1) partial of every prefix-m group g, one wave per group:
-//   Q_m[g][q][(j,r)] = sum_p V_{m-1}[parent][p][q] dV_m[g][p][(j,r)]
+//   partial of g:  Q_m[g][q][(j,r)] = sum_p V_{m-1}[pg][p][q] dV_m[g][p][(j,r)]
+// k_kb_q takes one wave per group g and forms its partial Q_m[g] and its
+// contribution Cc_m[g] = dV_m[g] . G^T to the parent; k_kb_level then adds the
+// contributions of each parent's children (consecutive groups) in order.
+// V_1 of a first-digit group is the core slice G_0[i_0].
 __global__ __launch_bounds__(kThreads) void k_kb_q(KArgs a, int m)
 {
     const Ws &ws = a.ws;
@@ -257,14 +226,17 @@ __global__ __launch_bounds__(kThreads) void k_kb_q(KArgs a, int m)
         const int t = uni(segment_of(ws.tab_uniq_start, a.T, r0));
         const auto &kt = kconst(a.kp.dkt)[t];
         const int P = kt.P[m - 1], Rin = kt.R[m - 1], dk = kt.d[c], Rout = kt.R[m], cols = dk * Rout;
+        const uint32_t urow = (uint32_t)ws.uniq_row[r0];
         const float *Vp;
         if (m == 2) {
-            const uint32_t i0 = (uint32_t)ws.uniq_row[r0] / (uint32_t)kt.div[0] % (uint32_t)kt.n[0];
+            const uint32_t i0 = urow / (uint32_t)kt.div[0] % (uint32_t)kt.n[0];
             Vp = a.cores.g[t * K] + (int64_t)i0 * kt.d[0] * kt.R[1];
         } else {
             Vp = a.kp.V[m - 1] + (int64_t)uni(a.kp.ugrp[m - 1][r0]) * a.kp.smax[m - 1];
         }
-        const float *dv = a.kp.dV[m] + g * a.kp.smax[m];
+        const uint32_t ic = urow / (uint32_t)kt.div[c] % (uint32_t)kt.n[c];
+        const float *gsl = a.cores.g[t * K + c] + (int64_t)ic * Rin * cols; // [Rin][cols]
+        const float *dv = a.kp.dV[m] + g * a.kp.smax[m];                   // [P][cols]
         float *qo = a.kp.Q[m] + g * a.kp.qmax[m];
         for (int e0 = 0; e0 < Rin * cols; e0 += 64) {
             const int e = e0 + lane;
@@ -274,6 +246,38 @@ __global__ __launch_bounds__(kThreads) void k_kb_q(KArgs a, int m)
 #pragma unroll 4
             for (int p = 0; p < P; ++p) acc = fmaf(Vp[p * Rin + q], dv[p * cols + jr], acc);
             if (e < Rin * cols) qo[e] = acc;
+        }
+        float *cc = a.kp.Cc[m] + g * a.kp.smax[m - 1];
+        for (int e0 = 0; e0 < P * Rin; e0 += 64) {
+            const int e = e0 + lane;
+            const int ec = e < P * Rin ? e : P * Rin - 1;
+            const int p = ec / Rin, q = ec - p * Rin;
+            const float *dvr = dv + p * cols, *gr = gsl + q * cols;
+            float acc = 0.f;
+#pragma unroll 8
+            for (int jr = 0; jr < cols; ++jr) acc = fmaf(dvr[jr], gr[jr], acc);
+            if (e < P * Rin) cc[e] = acc;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_kb_level(KArgs a, int m)
+{
+    const Ws &ws = a.ws;
+    const int lane = threadIdx.x & 63;
+    const int64_t np = ws.ctrl[CTRL_KLEV + m - 1];
+    const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t pg = (int64_t)blockIdx.x * (kThreads / 64) + uni(threadIdx.x >> 6); pg < np; pg += nw) {
+        const int r0 = uni(a.kp.gfirst[m - 1][pg]), r1 = uni(a.kp.gfirst[m - 1][pg + 1]);
+        const int g0 = uni(a.kp.ugrp[m][r0]), g1 = uni(a.kp.ugrp[m][r1 - 1]) + 1; // children [g0, g1)
+        const int t = uni(segment_of(ws.tab_uniq_start, a.T, r0));
+        const auto &kt = kconst(a.kp.dkt)[t];
+        const int n = kt.P[m - 1] * kt.R[m - 1];
+        float *dVp = a.kp.dV[m - 1] + pg * a.kp.smax[m - 1];
+        for (int e = lane; e < n; e += 64) {
+            float acc = 0.f;
+            for (int g = g0; g < g1; ++g) acc += a.kp.Cc[m][g * a.kp.smax[m - 1] + e];
+            dVp[e] = acc;
         }
     }
 }
@@ -372,8 +376,8 @@ hipError_t launch_backward_k(const Plan &p, const float *grad_out, const KCorePt
         for (int m = 2; m <= K - 1; ++m) hipLaunchKernelGGL(k_klevel, dim3(g), dim3(kThreads), 0, s, a, m);
         hipLaunchKernelGGL(k_kb_last, dim3(g), dim3(kThreads), 0, s, a);
         for (int m = K - 1; m >= 2; --m) {
-            hipLaunchKernelGGL(k_kb_level, dim3(g), dim3(kThreads), 0, s, a, m);
             hipLaunchKernelGGL(k_kb_q, dim3(g), dim3(kThreads), 0, s, a, m);
+            hipLaunchKernelGGL(k_kb_level, dim3(g), dim3(kThreads), 0, s, a, m);
         }
     }
     timer_end(p.timing, TM_BWD_CONTRACT, s);
