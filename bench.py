@@ -289,10 +289,11 @@ class Bench:
 
     def train_step(self):
         tt = self.tt
+        kcore = len(self.w.tables[0].n) > 3  # K-core forwards always leave their intermediates in ws
         self.emb.forward(self.cores, self.idx, self.off, self.w.B, out=self.out,
-                         flags=tt.TT_EMB_KEEP_PREFIX if self.keep else 0)
+                         flags=tt.TT_EMB_KEEP_PREFIX if (self.keep and not kcore) else 0)
         self.emb.backward(self.gout, self.cores, self.idx, self.off, self.w.B, core_grads=self.grads,
-                          flags=tt.TT_EMB_REUSE_GROUPING | (tt.TT_EMB_REUSE_PREFIX if self.keep else 0))
+                          flags=tt.TT_EMB_REUSE_GROUPING | (tt.TT_EMB_REUSE_PREFIX if (self.keep or kcore) else 0))
         self.emb.sgd_update(self.cores, self.grads, self.w.lr)
 
     def timed(self, fn, steps, warmup):

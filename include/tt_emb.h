@@ -161,8 +161,11 @@ int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const in
  * group's intermediate gradient formed once from its children, and every core
  * slice's gradient summed from per-row / per-group partials in a fixed order
  * (no atomics, bit-reproducible); tt_emb_sgd_update updates the T*K cores.
- * The forward flags TT_EMB_KEEP_PREFIX / TT_EMB_ATOMIC_POOL and the backward
- * flag TT_EMB_REUSE_PREFIX give TT_EMB_ERR_ARG.  Beyond the
+ * The forward leaves every prefix intermediate in ws: a backward with
+ * TT_EMB_REUSE_GROUPING | TT_EMB_REUSE_PREFIX right after a forward on the
+ * same ws, grouping and cores uses them instead of recomputing (REUSE_PREFIX
+ * alone gives TT_EMB_ERR_ARG).  The forward flags TT_EMB_KEEP_PREFIX /
+ * TT_EMB_ATOMIC_POOL give TT_EMB_ERR_ARG.  Beyond the
  * three-core limits: TT_EMB_ERR_UNSUPPORTED when T*K > 192, K = 2, K > 8,
  * the leading K-1 digits of all tables span 2^31 or more prefixes, the
  * product n_1 .. n_{K-1} of some table exceeds 2^32 - 1, some n_k summed

@@ -694,8 +694,10 @@ int tt_emb_backward(tt_emb_t h, const float *grad_out, const float *const *cores
         if (rc) return rc;
         if (B > 0 && !grad_out) return TT_EMB_ERR_ARG;
         if (h->K >= 4) {
-            // tables of K >= 4 cores: the chain reversed with prefix sharing
-            if (flags & TT_EMB_REUSE_PREFIX) return TT_EMB_ERR_ARG;
+            // tables of K >= 4 cores: the chain reversed with prefix sharing;
+            // REUSE_PREFIX: the level intermediates in ws are the forward's
+            if ((flags & TT_EMB_REUSE_PREFIX) && !(flags & TT_EMB_REUSE_GROUPING)) return TT_EMB_ERR_ARG;
+            p.reuse_c = (flags & TT_EMB_REUSE_PREFIX) ? 1 : 0;
             KCorePtrs kc{};
             if ((rc = kcore_ptrs(h, cores, &kc))) return rc;
             if (!core_grads) return TT_EMB_ERR_ARG;

@@ -369,11 +369,13 @@ hipError_t launch_backward_k(const Plan &p, const float *grad_out, const KCorePt
     const int g = p.num_blocks * 16;
     if (p.nnz > 0) {
         // groups of every prefix length 1..K-1 and the forward intermediates
-        for (int m = 1; m <= K - 1; ++m) {
+        // (lengths 2..K-1 kept from the forward when the caller says so)
+        for (int m = 1; m <= (p.reuse_c ? 1 : K - 1); ++m) {
             KLevOp op{a, m};
             if ((e = run_scan(op, p.ws.part, scan_blocks(p.nnz), s)) != hipSuccess) return e;
         }
-        for (int m = 2; m <= K - 1; ++m) hipLaunchKernelGGL(k_klevel, dim3(g), dim3(kThreads), 0, s, a, m);
+        if (!p.reuse_c)
+            for (int m = 2; m <= K - 1; ++m) hipLaunchKernelGGL(k_klevel, dim3(g), dim3(kThreads), 0, s, a, m);
         hipLaunchKernelGGL(k_kb_last, dim3(g), dim3(kThreads), 0, s, a);
         for (int m = K - 1; m >= 2; --m) {
             hipLaunchKernelGGL(k_kb_q, dim3(g), dim3(kThreads), 0, s, a, m);

@@ -590,8 +590,7 @@ def test_kcore_unsupported_calls_are_rejected():
     assert e.value.status == tt.TT_EMB_ERR_ARG
     run.forward()
     with pytest.raises(tt.TTEmbError) as e:
-        run.backward(np.zeros((w.B, w.sum_D), np.float32),
-                     flags=tt.TT_EMB_REUSE_GROUPING | tt.TT_EMB_REUSE_PREFIX)
+        run.backward(np.zeros((w.B, w.sum_D), np.float32), flags=tt.TT_EMB_REUSE_PREFIX)
     assert e.value.status == tt.TT_EMB_ERR_ARG
 
 
@@ -604,9 +603,15 @@ def test_kcore_backward_matches_oracle(name, bags):
     got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
     assert len(got) == len(w.cores)
     assert_grads_close(got, oracle.backward_k(w))
-    # bit-reproducible, with or without the kept grouping
+    # bit-reproducible, with or without the kept grouping, and with the
+    # forward's prefix intermediates in place of recomputed ones
     again = [g.cpu().numpy() for g in run.backward(w.grad_out)]
     for a, b in zip(got, again):
+        assert np.array_equal(a, b)
+    run.forward(flags=tt.TT_EMB_REUSE_GROUPING)
+    kept = [g.cpu().numpy() for g in run.backward(w.grad_out,
+                                                  flags=tt.TT_EMB_REUSE_GROUPING | tt.TT_EMB_REUSE_PREFIX)]
+    for a, b in zip(got, kept):
         assert np.array_equal(a, b)
 
 
