@@ -1121,7 +1121,7 @@ __global__ void k_bwd_prep(BwdArgs a)
 // than a block's fair share.  A run of those classes with more than PT tiles
 // is cut into ceil(tiles / PT) tile-aligned pieces of near-equal size; each
 // piece writes its dG2 partial to a slot of its own and k_reduce_g2p adds the
-// slots of a run in piece order (fixed order, no atomics).  PT >= 16 and
+// slots of a run in piece order (fixed order, no atomics).  PT >= 8 and
 // PT >= 2 * tiles / slots, so the slots in the workspace always suffice.
 struct PieceOp {
     BwdArgs a;
