@@ -67,6 +67,7 @@ struct KLevOp {
 // parent's entries are wave-uniform and come through scalar loads.  No LDS,
 // so many waves per SIMD hide the load latency.
 constexpr int kKRowBlk = 8;
+constexpr int kKLastP = 32, kKLastD = 8; // register fast path of the last level's dV
 __global__ __launch_bounds__(kThreads) void k_klevel(KArgs a, int m)
 {
     const Ws &ws = a.ws;
@@ -180,17 +181,46 @@ __global__ __launch_bounds__(kThreads) void k_kb_last(KArgs a)
         const float *GK = a.cores.g[t * K + K - 1];                // [n][Rin][dk]
         const float *Et = ws.E + kconst(ws.ebase)[t];             // g_u rows, stride Dp
         float *dV = a.kp.dV[m] + g * a.kp.smax[m];
-        for (int e0 = 0; e0 < P * Rin; e0 += 64) {
-            const int e = e0 + lane;
-            const int ec = e < P * Rin ? e : P * Rin - 1;
-            const int p = ec / Rin, q = ec - p * Rin;
-            float acc = 0.f;
+        if (P <= kKLastP && Rin <= 64 && dk <= kKLastD) {
+            // lane q keeps the P sums of column q; the rows' g_u entries are
+            // wave-uniform (scalar loads), the lane's G slice column in
+            // registers; same sums, same order (rows, then j)
+            const int q = lane < Rin ? lane : Rin - 1;
+            float acc[kKLastP];
+#pragma unroll
+            for (int p = 0; p < kKLastP; ++p) acc[p] = 0.f;
             for (int u = u0; u < u1; ++u) {
-                const float *gu = Et + (int64_t)u * Dp + p * dk;
-                const float *gs = GK + (int64_t)((uint32_t)ws.uniq_row[u] % (uint32_t)kt.n[K - 1]) * Rin * dk + q * dk;
-                for (int j = 0; j < dk; ++j) acc = fmaf(gu[j], gs[j], acc);
+                const auto *gu = kconst(Et + (int64_t)u * Dp);
+                const float *gs = GK + (int64_t)((uint32_t)uni(ws.uniq_row[u]) % (uint32_t)kt.n[K - 1]) * Rin * dk + q * dk;
+                float gq[kKLastD];
+#pragma unroll
+                for (int j = 0; j < kKLastD; ++j) gq[j] = j < dk ? gs[j] : 0.f;
+#pragma unroll
+                for (int p = 0; p < kKLastP; ++p) {
+                    if (p >= P) break;
+#pragma unroll
+                    for (int j = 0; j < kKLastD; ++j)
+                        if (j < dk) acc[p] = fmaf(gu[p * dk + j], gq[j], acc[p]);
+                }
             }
-            if (e < P * Rin) dV[e] = acc;
+            if (lane < Rin) {
+#pragma unroll
+                for (int p = 0; p < kKLastP; ++p)
+                    if (p < P) dV[p * Rin + lane] = acc[p];
+            }
+        } else {
+            for (int e0 = 0; e0 < P * Rin; e0 += 64) {
+                const int e = e0 + lane;
+                const int ec = e < P * Rin ? e : P * Rin - 1;
+                const int p = ec / Rin, q = ec - p * Rin;
+                float acc = 0.f;
+                for (int u = u0; u < u1; ++u) {
+                    const float *gu = Et + (int64_t)u * Dp + p * dk;
+                    const float *gs = GK + (int64_t)((uint32_t)ws.uniq_row[u] % (uint32_t)kt.n[K - 1]) * Rin * dk + q * dk;
+                    for (int j = 0; j < dk; ++j) acc = fmaf(gu[j], gs[j], acc);
+                }
+                if (e < P * Rin) dV[e] = acc;
+            }
         }
         for (int u = u0; u < u1; ++u) {
             const float *gu = Et + (int64_t)u * Dp;
@@ -238,14 +268,35 @@ __global__ __launch_bounds__(kThreads) void k_kb_q(KArgs a, int m)
         const float *gsl = a.cores.g[t * K + c] + (int64_t)ic * Rin * cols; // [Rin][cols]
         const float *dv = a.kp.dV[m] + g * a.kp.smax[m];                   // [P][cols]
         float *qo = a.kp.Q[m] + g * a.kp.qmax[m];
-        for (int e0 = 0; e0 < Rin * cols; e0 += 64) {
-            const int e = e0 + lane;
-            const int ec = e < Rin * cols ? e : Rin * cols - 1;
-            const int q = ec / cols, jr = ec - q * cols;
-            float acc = 0.f;
+        if (P <= kKRowBlk) {
+            // lanes over the columns (j, r): the P entries of dV_m in registers,
+            // the parent's entries wave-uniform (scalar loads); same sums, same order
+            const auto *vpc = kconst(Vp);
+            for (int j0 = 0; j0 < cols; j0 += 64) {
+                const int jr = j0 + lane;
+                const bool ok = jr < cols;
+                const int jc = ok ? jr : cols - 1;
+                float dvr[kKRowBlk];
+#pragma unroll
+                for (int i = 0; i < kKRowBlk; ++i) dvr[i] = i < P ? dv[i * cols + jc] : 0.f;
+                for (int q = 0; q < Rin; ++q) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int i = 0; i < kKRowBlk; ++i)
+                        if (i < P) acc = fmaf(vpc[i * Rin + q], dvr[i], acc);
+                    if (ok) qo[q * cols + jr] = acc;
+                }
+            }
+        } else {
+            for (int e0 = 0; e0 < Rin * cols; e0 += 64) {
+                const int e = e0 + lane;
+                const int ec = e < Rin * cols ? e : Rin * cols - 1;
+                const int q = ec / cols, jr = ec - q * cols;
+                float acc = 0.f;
 #pragma unroll 4
-            for (int p = 0; p < P; ++p) acc = fmaf(Vp[p * Rin + q], dv[p * cols + jr], acc);
-            if (e < Rin * cols) qo[e] = acc;
+                for (int p = 0; p < P; ++p) acc = fmaf(Vp[p * Rin + q], dv[p * cols + jr], acc);
+                if (e < Rin * cols) qo[e] = acc;
+            }
         }
         float *cc = a.kp.Cc[m] + g * a.kp.smax[m - 1];
         for (int e0 = 0; e0 < P * Rin; e0 += 64) {
