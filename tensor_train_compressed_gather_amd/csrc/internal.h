@@ -23,7 +23,7 @@ constexpr int kSortItems = kSortTile / kThreads;
 constexpr int kMaxCkptSlots = 4096; // L2 checkpoint slots for split prefix tiles
 constexpr int kUnitsPerTile = 4;    // prefix units sharing (table, i2) per tile
 constexpr int kGuTask = 256;        // sorted lookup positions per gradient-gather task
-constexpr int kGuBatch = 16;        // positions whose grad_out rows a gather worker has in flight
+constexpr int kGuBatch = 32;        // positions whose grad_out rows a gather worker has in flight
 constexpr int kPieceTiles = 8;      // least tiles per piece of a split backward run
 constexpr int kSplitMaxCls = 2;     // runs of the rank classes 8, 16, 32 may be split
 constexpr int kMaxG2Slots = 32768;  // dG2 partial slots (pieces of split runs)
