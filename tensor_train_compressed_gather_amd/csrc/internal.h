@@ -17,7 +17,7 @@ namespace ttemb {
 
 constexpr int kMaxTables = 64;
 constexpr int kThreads = 256;       // threads per block for every kernel
-constexpr int kScanBlocks = 1024;   // blocks of the 3-phase scans
+constexpr int kScanBlocks = 4096;   // blocks of the 3-phase scans (at most)
 constexpr int kSortTile = 4096;     // keys per radix-sort block (256 threads x 16)
 constexpr int kSortItems = kSortTile / kThreads;
 constexpr int kMaxCkptSlots = 4096; // L2 checkpoint slots for split prefix tiles

@@ -116,13 +116,22 @@ __global__ __launch_bounds__(kThreads) void scan_phase1(Op op, uint64_t *part)
     }
 }
 
-// One block of 1024 threads scans the nparts (<= 1024) partials.
+// One block of 1024 threads scans the nparts (<= kScanBlocks) partials,
+// kScanBlocks / 1024 consecutive ones per thread.
 template <class Op>
 __global__ __launch_bounds__(1024) void scan_phase2(Op op, uint64_t *part, int nparts)
 {
+    constexpr int PER = kScanBlocks / 1024;
+    static_assert(PER * 1024 == kScanBlocks, "partials split evenly over the threads");
     __shared__ uint64_t sm[16];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    uint64_t v = tid < nparts ? part[tid] : 0;
+    uint64_t pv[PER], v = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int i = tid * PER + j;
+        pv[j] = i < nparts ? part[i] : 0;
+        v += pv[j];
+    }
     uint64_t x = wave_inclusive_scan(v);
     if (lane == 63) sm[w] = x;
     __syncthreads();
@@ -131,7 +140,13 @@ __global__ __launch_bounds__(1024) void scan_phase2(Op op, uint64_t *part, int n
         if (i < w) wpre += sm[i];
         tot += sm[i];
     }
-    if (tid < nparts) part[tid] = wpre + x - v;
+    uint64_t ex = wpre + x - v;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int i = tid * PER + j;
+        if (i < nparts) part[i] = ex;
+        ex += pv[j];
+    }
     if (tid == 0) op.total(tot, op.count());
 }
 
