@@ -39,7 +39,7 @@ struct FwdCfg {
     static constexpr int CUNIT = 16 * CSTR + 16;
     static constexpr int CTILE = kUnitsPerTile * CUNIT;
     static constexpr int ES = R <= 16 ? 32 * 68 : 32 * 132; // 32 rows of D <= 64, or <= 128
-    static constexpr int OCC = R <= 16 ? 4 : R == 32 ? 4 : 2;
+    static constexpr int OCC = R <= 16 ? 5 : R == 32 ? 4 : 2;
     static constexpr int BREG = ((R / 4 + 3) / 4) * (R / 4); // G2 slice registers per lane
 };
 static_assert(FwdCfg<64>::CTILE == kCTile, "checkpoint slot holds the largest prefix tile");
