@@ -90,8 +90,14 @@ struct ClassGrid {
     int nb[4];
 };
 
-__global__ __launch_bounds__(kThreads) void k_queue_init(Ws ws, ClassGrid g, int stride)
+// Queue heads and counters of the persistent kernels (block (0, 0)), and the
+// transposed G3 copies (all blocks, when g3t != 0): one launch for both.
+__device__ void g3t_copy(const FwdArgs &a);
+__global__ __launch_bounds__(kThreads) void k_queue_init(FwdArgs a, ClassGrid g, int stride, int g3t)
 {
+    if (g3t) g3t_copy(a);
+    if (blockIdx.x != 0 || blockIdx.y != 0) return;
+    const Ws &ws = a.ws;
     __shared__ int cstart[6];
     const int64_t C = ws.ctrl[CTRL_CHUNKS];
     int split = ws.ctrl[CTRL_SPLIT];
@@ -122,9 +128,9 @@ __global__ __launch_bounds__(kThreads) void k_queue_init(Ws ws, ClassGrid g, int
     }
 }
 
-// Transposed copy G3t[i3][j3][r2] = G3[i3][r2][j3] of every MFMA-class table,
-// so a lane's run of r2 values is contiguous (float4 loads).
-__global__ __launch_bounds__(kThreads) void k_g3t(FwdArgs a)
+// Transposed copy G3t[i3][j3][r2] = G3[i3][r2][j3] of every MFMA-class table
+// (table blockIdx.y), so a lane's run of r2 values is contiguous (float4 loads).
+__device__ void g3t_copy(const FwdArgs &a)
 {
     const int t = blockIdx.y;
     const TableDesc &tb = a.tab[t];
@@ -828,9 +834,9 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
         ClassGrid cg;
         for (int c = 0; c < 4; ++c) cg.nb[c] = p.num_blocks * kClsOcc[c];
         const int hs = p.num_blocks * kMaxClsOcc;
-        hipLaunchKernelGGL(k_queue_init, dim3(1), dim3(kThreads), 0, s, p.ws, cg, hs);
+        if (p.force_generic) hipLaunchKernelGGL(k_queue_init, dim3(1), dim3(kThreads), 0, s, a, cg, hs, 0);
+        else hipLaunchKernelGGL(k_queue_init, dim3(64, p.T), dim3(kThreads), 0, s, a, cg, hs, 1);
         if (!p.force_generic) {
-            hipLaunchKernelGGL(k_g3t, dim3(64, p.T), dim3(kThreads), 0, s, a);
             for (int c = 0; c < 4; ++c) {
                 if (!(p.cls_mask & (1 << c))) continue;
                 timer_begin(p.timing, TM_FWD_CLS0 + c, s);
