@@ -14,7 +14,9 @@
 // gfx950 mapping: plain fp32 FMAs (shapes vary per level and table), one
 // wave per group of a level and one wave per unique row of the last step,
 // operands read from L2 with no LDS staging; the rows are pooled by the
-// bag-major pooling kernel.
+// bag-major pooling kernel.  The backward (second half of this file) walks
+// the same levels in reverse, again one wave per group, and sums every core
+// slice's gradient from per-row / per-group partials in a fixed order.
 #include "primitives.h"
 
 namespace ttemb {
