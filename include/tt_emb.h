@@ -234,8 +234,9 @@ int tt_emb_grouping_view(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B,
  * the grid size.
  * Synchronises the stream, then copies min(grid, cap, 2048) records of the
  * last launch of that kernel on this workspace into the host array out
- * (caller-owned) and sets *nblocks to that count (0 when the last forward
- * (kernels 0..3) or backward (4..7) on ws did not launch it).  Tools and
+ * (caller-owned) and sets *nblocks to that count (0 when the kernel has not
+ * run since the last grouping of ws, or the last forward (kernels 0..3) or
+ * backward (4..7) did not launch it; always 0 for K >= 4 cores).  Tools and
  * tests only; TT_EMB_ERR_ARG for a bad kernel id or null pointers. */
 typedef struct {
     int64_t t_start, t_end;

@@ -30,6 +30,8 @@ __global__ __launch_bounds__(kThreads) void k_init_ctrl(Ws ws, int T)
         ws.uniq_start[0] = 0;
         ws.grp_start[0] = 0;
     }
+    // no persistent launch has left records on this grouping yet
+    if (threadIdx.x < kStatKernels) ws.bstat[threadIdx.x * kStatBlocks].nb = 0;
 }
 
 // Offsets must start at 0, never decrease and end at nnz.  Malformed offsets

@@ -579,6 +579,23 @@ def test_kcore_full_size_sampled_bags():
     assert_out_close(sub, out[bags], oracle.forward_k(sub))
 
 
+def test_block_records_empty_before_any_persistent_launch():
+    # a grouping clears the records; a K-core handle never launches the
+    # persistent class kernels
+    w = W.make_workload(5, bags=16)
+    run = Run(w)
+    ws = run.emb.workspace(w.B, w.nnz)
+    tt.tt_emb_group(run.emb.handle, run.idx, run.off, w.B, ws)
+    for k in tt.BLOCK_STAT_KERNELS:
+        assert run.emb.block_stats(w.B, w.nnz, k) is None, k
+    wk = W.make_kcore_workload("k4", bags=16)
+    runk = Run(wk)
+    runk.forward()
+    runk.backward(np.zeros((wk.B, wk.sum_D), np.float32), flags=tt.TT_EMB_REUSE_GROUPING)
+    for k in tt.BLOCK_STAT_KERNELS:
+        assert runk.emb.block_stats(wk.B, wk.nnz, k) is None, k
+
+
 def test_kcore_unsupported_calls_are_rejected():
     w = W.make_kcore_workload("k5", bags=8)
     run = Run(w)
