@@ -154,3 +154,17 @@ def test_block_balance_summary():
     assert b["eff_cus"] == 0.75             # CU busy 20 and 10: mean 15 over max 20
     assert b["work_max_over_mean"] == round(4 / 3, 3) and b["rows_max_over_mean"] == round(8 / 6, 3)
     assert tt.block_balance(None) is None
+
+
+def test_block_stats_rejects_bad_arguments_on_the_host():
+    # argument checks come before any device work
+    L = tt.lib()
+    recs = (tt.tt_emb_block_stat * 4)()
+    n, khz = C.c_int32(), C.c_int64()
+    for kernel in (-1, 8):
+        rc = L.tt_emb_block_stats(None, None, 0, 1, 1, kernel, None, recs, 4, C.byref(n), C.byref(khz))
+        assert rc == tt.TT_EMB_ERR_ARG
+    rc = L.tt_emb_block_stats(None, None, 0, 1, 1, 0, None, None, 4, C.byref(n), C.byref(khz))
+    assert rc == tt.TT_EMB_ERR_ARG
+    rc = L.tt_emb_block_stats(None, None, 0, 1, 1, 0, None, recs, 4, C.byref(n), C.byref(khz))
+    assert rc == tt.TT_EMB_ERR_ARG  # no handle
