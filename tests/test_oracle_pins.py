@@ -392,6 +392,22 @@ def test_sgd_delta_closed_form():
 
 # ----------------------------------------------------------------- generator
 
+def test_generator_matches_the_recorded_digests():
+    # sha256 of every generated array of each workload, recorded by
+    # tests/golden/make_workload_digests.py: any change to the seeded inputs
+    # (draw order, distributions, shapes) shows up here
+    import json
+    import os
+    import sys
+
+    golden = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    sys.path.insert(0, golden)
+    import make_workload_digests as mk
+
+    want = json.load(open(os.path.join(golden, "workload_digests.json")))
+    assert mk.digests() == want
+
+
 def test_generator_is_reproducible_and_shaped():
     a, b = W.make_workload(3, bags=256), W.make_workload(3, bags=256)
     assert a.digest() == b.digest()
