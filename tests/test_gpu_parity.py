@@ -327,6 +327,29 @@ def test_bit_reproducible_forward_and_backward():
             assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("opt", [dict(), dict(sched_mode=2), dict(sched_mode=3, chunk_rows=4),
+                                 dict(num_blocks=16, sched_mode=2)])
+def test_bit_identical_over_ten_runs(opt):
+    # the whole training step (kept prefix intermediates, split backward runs,
+    # stealing or not) hashed over ten runs of each configuration
+    import hashlib
+
+    w = W.make_workload(5, bags=96)
+    run = Run(w, keep_prefix=1, **opt)
+    go = torch.from_numpy(w.grad_out).to(DEV)
+    digests = set()
+    for _ in range(10):
+        out = run.emb.forward(run.cores, run.idx, run.off, w.B, flags=tt.TT_EMB_KEEP_PREFIX)
+        grads = run.emb.backward(go, run.cores, run.idx, run.off, w.B,
+                                 flags=tt.TT_EMB_REUSE_GROUPING | tt.TT_EMB_REUSE_PREFIX)
+        torch.cuda.synchronize()
+        h = hashlib.sha256(out.cpu().numpy().tobytes())
+        for g in grads:
+            h.update(g.cpu().numpy().tobytes())
+        digests.add(h.hexdigest())
+    assert len(digests) == 1
+
+
 def test_device_detected_errors():
     w = W.make_workload(1)
     bad = w.indices.copy()
