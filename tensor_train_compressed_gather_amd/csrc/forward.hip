@@ -68,9 +68,14 @@ struct FwdArgs {
 };
 
 // Victim order for stealing: own range, then blocks on the same XCD (blocks
-// are dispatched round-robin over the 8 XCDs), then the other XCDs.
+// are dispatched round-robin over the 8 XCDs), then the other XCDs.  For any
+// grid size vi -> victim is a permutation of the blocks with victim 0 = me,
+// so every static range is claimed by its owner first.
 __device__ __forceinline__ int victim_of(int me, int vi, int nb)
 {
+    // a grid that is not a whole number of rounds over the 8 XCDs: plain
+    // rotation (still a permutation that starts with the block itself)
+    if (nb < 8 || (nb & 7)) return (me + vi) % nb;
     const int per = nb >> 3;
     const int xo = vi / per, k = vi - xo * per;
     return ((me & 7) + xo) % 8 + 8 * (((me >> 3) + k) % per);

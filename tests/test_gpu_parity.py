@@ -100,6 +100,10 @@ def test_forward_matches_oracle(cfg, bags):
 @pytest.mark.parametrize("opt", [
     dict(sched_mode=1), dict(sched_mode=2), dict(sched_mode=3, chunk_rows=1), dict(sched_mode=3, chunk_rows=3),
     dict(num_blocks=8), dict(group_mode=2), dict(sched_mode=1, num_blocks=8, chunk_rows=2),
+    # grids that are not a whole number of rounds over the 8 XCDs (fewer than
+    # 8 blocks, or 3 per CU x OCC): every static range is still claimed
+    dict(num_blocks=1), dict(num_blocks=1, sched_mode=2), dict(num_blocks=3, sched_mode=1),
+    dict(num_blocks=3, sched_mode=3, chunk_rows=2),
 ])
 def test_scheduling_modes_are_bit_identical(opt):
     w = W.make_workload(4, bags=64)
