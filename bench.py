@@ -184,8 +184,11 @@ def write_counters(d, trace_csv=None):
     import csv
 
     vals = {}
-    for sub in ("lds", "mfma"):
-        with open(os.path.join(d, sub, "run_counter_collection.csv")) as f:
+    for sub in ("lds", "mfma", "busy"):  # busy/ (optional): SQ_BUSY_CU_CYCLES, GRBM_GUI_ACTIVE, OccupancyPercent
+        path = os.path.join(d, sub, "run_counter_collection.csv")
+        if sub == "busy" and not os.path.exists(path):
+            continue
+        with open(path) as f:
             for r in csv.DictReader(f):
                 vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
     dur = {}
@@ -204,7 +207,14 @@ def write_counters(d, trace_csv=None):
         ds = [v for k, vs in dur.items() if sym in k for v in vs]
         t = sum(ds) / len(ds) if ds else None
         fl = avg(sym, "MfmaFlopsF32")
+        busy, gui = avg(sym, "SQ_BUSY_CU_CYCLES"), avg(sym, "GRBM_GUI_ACTIVE")
         rows.append({"kernel": name, "lds_bank_conflict_ratio": avg(sym, "LdsBankConflict"),
+                     # busy cycles of the CUs summed, against the launch's GPU-active
+                     # cycles (GRBM_GUI_ACTIVE, summed over the 8 XCDs) x 256 CUs; on
+                     # gfx950 the counter reads cycles (its description says
+                     # quad-cycles, which would put every kernel near 390 %)
+                     "cu_busy_pct": 100.0 * busy / (gui / 8 * 256) if (busy and gui) else None,
+                     "occupancy_pct": avg(sym, "OccupancyPercent"),
                      "lds_conflict_cycles": avg(sym, "SQ_LDS_BANK_CONFLICT"),
                      "lds_active_cycles": avg(sym, "SQ_LDS_IDX_ACTIVE"),
                      "mfma_util_pct": avg(sym, "MfmaUtil"), "mfma_f32_flops": fl,
