@@ -69,7 +69,9 @@ enum {
     TT_EMB_SCHED_DEFAULT = 0,  /* per rank class: STATIC for ranks 8, 16 and 32, STEAL for
                                   rank 64 (the fastest of each, measured) */
     TT_EMB_SCHED_STATIC = 1,   /* each block runs only its static range of chunks */
-    TT_EMB_SCHED_STEAL = 2,    /* static range first, then steal chunks; no checkpoints */
+    TT_EMB_SCHED_STEAL = 2,    /* static range first, then steal chunks of blocks on the same
+                                  XCD (grids a multiple of 8 blocks; otherwise of any block);
+                                  no checkpoints */
     TT_EMB_SCHED_STEAL_L2 = 3  /* stealing plus L2 checkpoints of split prefix tiles */
 };
 

@@ -584,7 +584,9 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
     const int base = ws.ctrl[CTRL_CLS_START + CLS];
     const int64_t C = ws.ctrl[CTRL_CLS_START + CLS + 1] - base;
     int32_t *heads = ws.heads + CLS * heads_stride * kHeadPad;
-    const int nvict = a.sched == kSchedStatic ? 1 : nb;
+    // stealing stays on the block's own XCD (victims 0 .. nb/8 - 1 of victim_of):
+    // the scan a drained block makes before it exits is an eighth as long
+    const int nvict = a.sched == kSchedStatic ? 1 : ((nb >= 8 && !(nb & 7)) ? nb >> 3 : nb);
     float breg[FwdCfg<R>::BREG], apf[R / 4], bq[fwd_nq<R, KEEP>()][R / 4];
 #pragma unroll
     for (int i = 0; i < FwdCfg<R>::BREG; ++i) breg[i] = 0.f;
