@@ -144,7 +144,7 @@ typedef struct {
  * gather over sequential core contractions).  num_rows[T] = N_t; n[3T], d[3T]
  * = row and column factors; R[4T] = ranks with R0 = R3 = 1.  All are host
  * arrays, copied.  Returns TT_EMB_ERR_ARG for inconsistent shapes and
- * TT_EMB_ERR_UNSUPPORTED beyond this build's limits (T <= 64, sum N_t < 2^31,
+ * TT_EMB_ERR_UNSUPPORTED beyond this build's limits (T <= 64, sum N_t <= 2^31 - 2,
  * ranks <= 256, D_t <= 1024).  *out receives the handle. */
 int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const int32_t *d,
                   const int32_t *R, const tt_emb_options *opt, tt_emb_t *out);

@@ -73,6 +73,8 @@ def _create(N, n, d, R, opt=None):
     ([1000], [10, 10, 10], [16, 16, 8], [1, 8, 8, 1], tt.TT_EMB_ERR_UNSUPPORTED),  # D > 1024
     ([1000], [10, 10, 10], [2, 2, 4], [1, 512, 8, 1], tt.TT_EMB_ERR_UNSUPPORTED),  # rank > 256
     ([2 ** 31], [2 ** 11, 2 ** 10, 2 ** 10], [2, 2, 4], [1, 8, 8, 1], tt.TT_EMB_ERR_UNSUPPORTED),
+    ([2 ** 31 - 1000, 999], [2 ** 11, 2 ** 10, 2 ** 10, 10, 10, 10], [2, 2, 4, 2, 2, 4], [1, 8, 8, 1, 1, 8, 8, 1],
+     tt.TT_EMB_ERR_UNSUPPORTED),  # rows summed over the tables = 2^31 - 1
 ])
 def test_create_rejects_bad_shapes_before_touching_the_device(N, n, d, R, code):
     rc, h = _create(N, n, d, R)

@@ -707,3 +707,34 @@ def test_kcore_full_size_backward_sampled_bags():
     sub = _sub_bags(w, bags)
     sub.grad_out = go[bags]
     assert_grads_close(got, oracle.backward_k(sub))
+
+
+def test_largest_row_space():
+    # Rows summed over the tables at the handle's limit (2^31 - 2), so that the
+    # (table, row) sort keys fill 31 bits and the first table's row numbers
+    # reach 2^31 - 1003: lookups at the first and last rows of each table,
+    # rows near the top of the first and uniform rows, with empty bags.
+    big = 2 ** 31 - 2 - 1000
+    tabs = [W.Table(big, (2048, 1024, 1024), (2, 2, 4), (1, 8, 8, 1), 0.1, "uniform"),
+            W.Table(1000, (10, 10, 10), (4, 4, 4), (1, 16, 16, 1), 0.1, "uniform")]
+    rng = np.random.default_rng(31)
+    B = 64
+    lens, idx = [], []
+    for t in tabs:
+        ln = rng.integers(0, 40, size=B)
+        ln[[3, 17]] = 0
+        n = int(ln.sum())
+        pick = rng.integers(0, 3, n)
+        ix = np.where(pick == 0, rng.integers(max(t.N - 2 ** 20, 0), t.N, n), rng.integers(0, t.N, n))
+        ix[:4] = [0, t.N - 1, t.N - 2, 0]
+        lens.append(ln)
+        idx.append(ix.astype(np.int64))
+    w = W.make_custom(tabs, lens, idx, seed=31)
+    w.grad_out = rng.standard_normal((w.B, w.sum_D)).astype(np.float32)
+    run = Run(w)
+    out = run.forward().cpu().numpy()
+    assert_out_close(w, out, oracle.forward(w))
+    assert not out[[3, 17]].any()
+    check_grouping(run)
+    got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
+    assert_grads_close(got, oracle.backward(w))
