@@ -738,3 +738,27 @@ def test_largest_row_space():
     check_grouping(run)
     got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
     assert_grads_close(got, oracle.backward(w))
+
+
+def test_largest_supported_shapes():
+    # Tables at the create-time shape limits, all outside the matrix-core
+    # classes: D = 1024 columns with R1 d2 R2 = 16384 (the whole dG2 slice of a
+    # unit in the generic backward's registers), R1 = 256 and R2 = 256, each
+    # against the oracle forward and backward, with empty bags.
+    tables = [W.Table(500, (8, 8, 8), (4, 4, 64), (1, 64, 64, 1), 0.05, "uniform"),
+              W.Table(300, (7, 7, 7), (2, 2, 4), (1, 256, 32, 1), 0.05, "uniform"),
+              W.Table(300, (7, 7, 7), (4, 2, 4), (1, 32, 256, 1), 0.05, "uniform")]
+    rng = np.random.default_rng(41)
+    lens = [rng.integers(0, 9, size=40) for _ in tables]
+    for ln in lens:
+        ln[[0, 7]] = 0
+    idx = [rng.integers(0, t.N, size=int(l.sum())) for t, l in zip(tables, lens)]
+    w = W.make_custom(tables, lens, idx, seed=41)
+    w.grad_out = rng.standard_normal((w.B, w.sum_D)).astype(np.float32)
+    run = Run(w)
+    out = run.forward().cpu().numpy()
+    assert_out_close(w, out, oracle.forward(w))
+    assert not out[[0, 7]].any()
+    check_grouping(run)
+    got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
+    assert_grads_close(got, oracle.backward(w))
