@@ -762,3 +762,30 @@ def test_largest_supported_shapes():
     check_grouping(run)
     got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
     assert_grads_close(got, oracle.backward(w))
+
+
+def test_kcore_eight_cores():
+    # K = 8, the largest core count: unequal ranks and digit widths (some
+    # d_k = 1), a hot row, forward and backward against the oracle, each
+    # with the level intermediates kept from the forward and recomputed.
+    tables = [W.Table(2000, (2, 3, 2, 3, 2, 3, 2, 5), (2, 1, 2, 1, 2, 1, 2, 2), (1, 4, 6, 8, 5, 7, 3, 4, 1), 0.3,
+                      "uniform"),
+              W.Table(60000, (4, 4, 4, 4, 4, 4, 4, 4), (1, 2, 1, 2, 1, 2, 1, 2), (1, 8, 8, 8, 8, 8, 8, 8, 1), 0.3,
+                      "uniform")]
+    rng = np.random.default_rng(61)
+    lens = [rng.integers(0, 16, size=48) for _ in tables]
+    lens[0][5] = 0
+    idx = [rng.integers(0, t.N, size=int(l.sum())) for t, l in zip(tables, lens)]
+    idx[1][::3] = 59999
+    w = W.make_custom(tables, lens, idx, seed=61)
+    w.grad_out = rng.standard_normal((w.B, w.sum_D)).astype(np.float32)
+    run = Run(w)
+    out = run.forward().cpu().numpy()
+    assert_out_close(w, out, oracle.forward_k(w))
+    assert not out[5, :w.col_offsets()[1]].any()
+    ref = oracle.backward_k(w)
+    got = [g.cpu().numpy() for g in run.backward(w.grad_out,
+                                                  flags=tt.TT_EMB_REUSE_GROUPING | tt.TT_EMB_REUSE_PREFIX)]
+    assert_grads_close(got, ref)
+    got = [g.cpu().numpy() for g in run.backward(w.grad_out)]
+    assert_grads_close(got, ref)
