@@ -789,3 +789,25 @@ def test_kcore_eight_cores():
     assert_grads_close(got, ref)
     got = [g.cpu().numpy() for g in run.backward(w.grad_out)]
     assert_grads_close(got, ref)
+
+
+def test_sixty_four_tables():
+    # T = 64, the most tables a handle takes: every matrix-core rank class and
+    # generic shapes side by side, some tables without lookups, forward,
+    # grouping and backward against the oracle.
+    shapes = [((10, 10, 10), (2, 2, 4), (1, 8, 8, 1)), ((10, 10, 10), (4, 4, 4), (1, 16, 16, 1)),
+              ((10, 10, 10), (4, 4, 4), (1, 32, 32, 1)), ((10, 10, 10), (4, 4, 4), (1, 64, 64, 1)),
+              ((9, 9, 9), (3, 2, 5), (1, 6, 10, 1))]
+    tables = [W.Table(600 + 2 * i, *shapes[i % 5], 0.1, "uniform") for i in range(64)]
+    rng = np.random.default_rng(64)
+    lens = [rng.integers(0, 7, size=16) for _ in tables]
+    for t in (5, 33, 63):
+        lens[t][:] = 0
+    idx = [rng.integers(0, t.N, size=int(l.sum())) for t, l in zip(tables, lens)]
+    w = W.make_custom(tables, lens, idx, seed=64)
+    w.grad_out = rng.standard_normal((w.B, w.sum_D)).astype(np.float32)
+    run = Run(w)
+    assert_out_close(w, run.forward().cpu().numpy(), oracle.forward(w))
+    check_grouping(run)
+    got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
+    assert_grads_close(got, oracle.backward(w))
