@@ -811,3 +811,24 @@ def test_sixty_four_tables():
     check_grouping(run)
     got = [g.cpu().numpy() for g in run.backward(w.grad_out, flags=tt.TT_EMB_REUSE_GROUPING)]
     assert_grads_close(got, oracle.backward(w))
+
+
+def test_kcore_most_cores_per_handle():
+    # T * K = 192, the most cores a handle takes (48 tables of four cores),
+    # with ranks and widths that differ between tables and tables without
+    # lookups: forward and backward against the oracle.
+    shapes = [((6, 6, 6, 6), (2, 2, 2, 2), (1, 8, 8, 8, 1)), ((5, 5, 5, 8), (2, 4, 4, 4), (1, 16, 16, 16, 1)),
+              ((4, 6, 5, 7), (3, 1, 2, 5), (1, 5, 3, 7, 1))]
+    tables = [W.Table(780 + i, *shapes[i % 3], 0.2, "uniform") for i in range(48)]
+    rng = np.random.default_rng(192)
+    lens = [rng.integers(0, 6, size=12) for _ in tables]
+    for t in (0, 47):
+        lens[t][:] = 0
+    idx = [rng.integers(0, t.N, size=int(l.sum())) for t, l in zip(tables, lens)]
+    w = W.make_custom(tables, lens, idx, seed=192)
+    w.grad_out = rng.standard_normal((w.B, w.sum_D)).astype(np.float32)
+    run = Run(w)
+    assert_out_close(w, run.forward().cpu().numpy(), oracle.forward_k(w))
+    got = [g.cpu().numpy() for g in run.backward(w.grad_out,
+                                                  flags=tt.TT_EMB_REUSE_GROUPING | tt.TT_EMB_REUSE_PREFIX)]
+    assert_grads_close(got, oracle.backward_k(w))
