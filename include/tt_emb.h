@@ -248,6 +248,17 @@ int tt_emb_block_stats(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B, i
                        void *stream, tt_emb_block_stat *out, int32_t cap, int32_t *nblocks,
                        int64_t *clock_khz);
 
+/* Victim order of the persistent kernels' chunk stealing (FlowTT section 3.4:
+ * a block that has finished its own range takes chunks from others).  For a
+ * grid of nb blocks (nb a positive multiple of 8, as every persistent launch
+ * of this library is: blocks per CU times a multiple of 8 CUs) writes
+ * order[vi] = the vi-th block whose range block `me` claims from, vi = 0 ..
+ * nb-1 (caller-owned host array of nb entries): itself first, then the blocks
+ * of its own XCD, then those of the other XCDs.  The kernels use the same
+ * function; host only, no device work.  TT_EMB_ERR_ARG for a null array,
+ * nb < 8, nb not a multiple of 8, or me outside [0, nb). */
+int tt_emb_victim_order(int32_t me, int32_t nb, int32_t *order);
+
 /* Synchronise the stream and report a device-detected error recorded in ws
  * since the last grouping (TT_EMB_OK, TT_EMB_ERR_INDEX or TT_EMB_ERR_OFFSETS). */
 int tt_emb_poll_error(tt_emb_t h, const void *ws, void *stream);

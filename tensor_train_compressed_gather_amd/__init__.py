@@ -36,7 +36,7 @@ EXPORTED = (
     "tt_emb_create", "tt_emb_create_k", "tt_emb_destroy", "tt_emb_workspace_size", "tt_emb_group", "tt_emb_forward",
     "tt_emb_backward", "tt_emb_sgd_update", "tt_emb_grouping_view", "tt_emb_poll_error",
     "tt_emb_status_string", "tt_emb_timing_enable", "tt_emb_timing_read", "tt_emb_timer_name",
-    "tt_emb_block_stats",
+    "tt_emb_block_stats", "tt_emb_victim_order",
 )
 BLOCK_STAT_KERNELS = ("fwd_r8", "fwd_r16", "fwd_r32", "fwd_r64", "bwd_r8", "bwd_r16", "bwd_r32", "bwd_r64")
 TIMER_NAMES = ("group_sort", "group_rle", "contract", "pool", "bwd_gather", "bwd_contract",
@@ -91,6 +91,7 @@ def lib():
             L.tt_emb_grouping_view.argtypes = [p, p, C.c_size_t, i64, i64, p, C.POINTER(tt_emb_grouping)]
             L.tt_emb_poll_error.argtypes = [p, p, p]
             L.tt_emb_block_stats.argtypes = [p, p, C.c_size_t, i64, i64, i32, p, p, i32, p, p]
+            L.tt_emb_victim_order.argtypes = [i32, i32, p]
             L.tt_emb_status_string.argtypes = [C.c_int]
             L.tt_emb_status_string.restype = C.c_char_p
             L.tt_emb_timing_enable.argtypes = [p, i32]
@@ -129,9 +130,36 @@ def _ptr(t):
     return C.c_void_p(0 if t is None else t.data_ptr())
 
 
-def _ptr_array(tensors):
-    arr = (C.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
-    return arr
+def _need(specs):
+    """Reject tensors the kernels would misread: the library takes raw
+    pointers and cannot tell an int32 index array, a strided view or a host
+    tensor from the int64 / fp32 contiguous device buffers it expects (reading
+    8 bytes per index from a 4-byte array would run past the allocation).
+    specs: (tensor or list of tensors, name, dtype name).  Types and layouts
+    are checked first, then that every tensor is on one and the same GPU."""
+    import torch
+
+    kinds = {"int64": torch.int64, "float32": torch.float32, "uint8": torch.uint8}
+    flat = []
+    for ts, what, dtype in specs:
+        if isinstance(ts, (list, tuple)):
+            flat += [(t, f"{what}[{i}]", dtype) for i, t in enumerate(ts)]
+        else:
+            flat.append((ts, what, dtype))
+    for t, what, dtype in flat:
+        if not torch.is_tensor(t):
+            raise TTEmbError(TT_EMB_ERR_ARG, f"{what}: expected a torch tensor, got {type(t).__name__}")
+        if t.dtype != kinds[dtype]:
+            raise TTEmbError(TT_EMB_ERR_ARG, f"{what}: dtype {t.dtype}, expected {kinds[dtype]}")
+        if not t.is_contiguous():
+            raise TTEmbError(TT_EMB_ERR_ARG, f"{what}: not contiguous")
+    device = None
+    for t, what, _ in flat:
+        if t.device.type != "cuda":
+            raise TTEmbError(TT_EMB_ERR_ARG, f"{what}: on {t.device}, expected a GPU tensor")
+        if device is not None and t.device != device:
+            raise TTEmbError(TT_EMB_ERR_ARG, f"{what}: on {t.device}, expected {device} like the others")
+        device = t.device
 
 
 def tt_emb_status_string(status: int) -> str:
@@ -185,12 +213,15 @@ def tt_emb_workspace_size(h, B: int, nnz: int) -> int:
 
 
 def tt_emb_group(h, indices, offsets, B: int, ws, stream=None):
+    _need([(indices, "indices", "int64"), (offsets, "offsets", "int64"), (ws, "workspace", "uint8")])
     rc = lib().tt_emb_group(h, _ptr(indices), _ptr(offsets), int(B), int(indices.numel()), _ptr(ws),
                             ws.numel(), _stream(stream))
     _check(rc, "tt_emb_group")
 
 
 def tt_emb_forward(h, cores, indices, offsets, B: int, out, ws, flags: int = 0, stream=None):
+    _need([(indices, "indices", "int64"), (offsets, "offsets", "int64"), (cores, "cores", "float32"),
+           (out, "out", "float32"), (ws, "workspace", "uint8")])
     rc = lib().tt_emb_forward(h, _ptr_array(cores), _ptr(indices), _ptr(offsets), int(B),
                               int(indices.numel()), _ptr(out), _ptr(ws), ws.numel(), int(flags),
                               _stream(stream))
@@ -199,6 +230,8 @@ def tt_emb_forward(h, cores, indices, offsets, B: int, out, ws, flags: int = 0, 
 
 def tt_emb_backward(h, grad_out, cores, indices, offsets, B: int, core_grads, ws, flags: int = 0,
                     stream=None):
+    _need([(indices, "indices", "int64"), (offsets, "offsets", "int64"), (grad_out, "grad_out", "float32"),
+           (cores, "cores", "float32"), (core_grads, "core_grads", "float32"), (ws, "workspace", "uint8")])
     rc = lib().tt_emb_backward(h, _ptr(grad_out), _ptr_array(cores), _ptr(indices), _ptr(offsets),
                                int(B), int(indices.numel()), _ptr_array(core_grads), _ptr(ws),
                                ws.numel(), int(flags), _stream(stream))
@@ -206,6 +239,7 @@ def tt_emb_backward(h, grad_out, cores, indices, offsets, B: int, core_grads, ws
 
 
 def tt_emb_sgd_update(h, cores, core_grads, lr: float, stream=None):
+    _need([(cores, "cores", "float32"), (core_grads, "core_grads", "float32")])
     rc = lib().tt_emb_sgd_update(h, _ptr_array(cores), _ptr_array(core_grads), float(lr), _stream(stream))
     _check(rc, "tt_emb_sgd_update")
 
@@ -299,6 +333,17 @@ def block_balance(st) -> dict | None:
             "rows_max_over_mean": round(float(rows.max() / rows.mean()), 3) if rows.mean() > 0 else None}
 
 
+def tt_emb_victim_order(me: int, nb: int):
+    """Blocks that block `me` of an nb-block persistent grid claims chunks
+    from, in order (host-side; the kernels use the same function)."""
+    import numpy as np
+
+    order = np.empty(max(int(nb), 0), dtype=np.int32)
+    _check(lib().tt_emb_victim_order(int(me), int(nb), order.ctypes.data if order.size else None),
+           "tt_emb_victim_order")
+    return order
+
+
 def tt_emb_timing_enable(h, enable: bool = True):
     _check(lib().tt_emb_timing_enable(h, 1 if enable else 0), "tt_emb_timing_enable")
 
@@ -351,11 +396,42 @@ class TTEmbeddingBag:
             self._ws_key = key
         return self._ws
 
+    def _core_sizes(self):
+        sizes = []
+        for t in self.tables:
+            for k in range(self.K):
+                sizes.append(int(t.n[k]) * int(t.R[k]) * int(t.d[k]) * int(t.R[k + 1]))
+        return sizes
+
+    def _check_shapes(self, cores, indices, offsets, B: int, out=None, grad_out=None, core_grads=None):
+        """Sizes the kernels index by: K*T cores of n_k*R_k*d_k*R_{k+1}
+        elements, T*B+1 offsets, [B][sum D] outputs and output gradients."""
+        sizes = self._core_sizes()
+        if len(cores) != len(sizes):
+            raise TTEmbError(TT_EMB_ERR_ARG, f"cores: {len(cores)} tensors, expected {len(sizes)}")
+        for i, (c, n) in enumerate(zip(cores, sizes)):
+            if c.numel() != n:
+                raise TTEmbError(TT_EMB_ERR_ARG, f"cores[{i}]: {c.numel()} elements, expected {n}")
+        if core_grads is not None:
+            if len(core_grads) != len(sizes):
+                raise TTEmbError(TT_EMB_ERR_ARG, f"core_grads: {len(core_grads)} tensors, expected {len(sizes)}")
+            for i, (g, n) in enumerate(zip(core_grads, sizes)):
+                if g.numel() != n:
+                    raise TTEmbError(TT_EMB_ERR_ARG, f"core_grads[{i}]: {g.numel()} elements, expected {n}")
+        if offsets.numel() != self.T * int(B) + 1:
+            raise TTEmbError(TT_EMB_ERR_ARG, f"offsets: {offsets.numel()} entries, expected T*B+1 = "
+                                             f"{self.T * int(B) + 1}")
+        for name, x in (("out", out), ("grad_out", grad_out)):
+            if x is not None and x.numel() != int(B) * self.sum_D:
+                raise TTEmbError(TT_EMB_ERR_ARG, f"{name}: {x.numel()} elements, expected B*sum(D) = "
+                                                 f"{int(B) * self.sum_D}")
+
     def forward(self, cores, indices, offsets, B: int, out=None, flags: int = 0, stream=None):
         import torch
 
         if out is None:
             out = torch.empty((B, self.sum_D), dtype=torch.float32, device=self.device)
+        self._check_shapes(cores, indices, offsets, B, out=out)
         ws = self.workspace(B, indices.numel())
         tt_emb_forward(self.handle, cores, indices, offsets, B, out, ws, flags, stream)
         return out
@@ -366,11 +442,16 @@ class TTEmbeddingBag:
 
         if core_grads is None:
             core_grads = [torch.empty_like(c) for c in cores]
+        self._check_shapes(cores, indices, offsets, B, grad_out=grad_out, core_grads=core_grads)
         ws = self.workspace(B, indices.numel())
         tt_emb_backward(self.handle, grad_out, cores, indices, offsets, B, core_grads, ws, flags, stream)
         return core_grads
 
     def sgd_update(self, cores, core_grads, lr: float, stream=None):
+        sizes = self._core_sizes()
+        if len(cores) != len(sizes) or len(core_grads) != len(sizes) or any(
+                c.numel() != n or g.numel() != n for c, g, n in zip(cores, core_grads, sizes)):
+            raise TTEmbError(TT_EMB_ERR_ARG, "sgd_update: cores and gradients must match the tables' core sizes")
         tt_emb_sgd_update(self.handle, cores, core_grads, lr, stream)
 
     def poll_error(self, stream=None) -> int:

@@ -884,6 +884,13 @@ int tt_emb_block_stats(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B, i
     return TT_EMB_OK;
 }
 
+int tt_emb_victim_order(int32_t me, int32_t nb, int32_t *order)
+{
+    if (!order || nb < 8 || (nb & 7) || me < 0 || me >= nb) return TT_EMB_ERR_ARG;
+    for (int vi = 0; vi < nb; ++vi) order[vi] = victim_of(me, vi, nb);
+    return TT_EMB_OK;
+}
+
 int tt_emb_poll_error(tt_emb_t h, const void *ws, void *stream)
 {
     if (!h || !ws) return TT_EMB_ERR_ARG;

@@ -67,20 +67,6 @@ struct FwdArgs {
     int64_t B;
 };
 
-// Victim order for stealing: own range, then blocks on the same XCD (blocks
-// are dispatched round-robin over the 8 XCDs), then the other XCDs.  For any
-// grid size vi -> victim is a permutation of the blocks with victim 0 = me,
-// so every static range is claimed by its owner first.
-__device__ __forceinline__ int victim_of(int me, int vi, int nb)
-{
-    // a grid that is not a whole number of rounds over the 8 XCDs: plain
-    // rotation (still a permutation that starts with the block itself)
-    if (nb < 8 || (nb & 7)) return (me + vi) % nb;
-    const int per = nb >> 3;
-    const int xo = vi / per, k = vi - xo * per;
-    return ((me & 7) + xo) % 8 + 8 * (((me >> 3) + k) % per);
-}
-
 __device__ __forceinline__ int range_begin(int v, int64_t C, int nb) { return (int)((int64_t)v * C / nb); }
 
 // Chunks are class-major (rank class 0..3, generic tables last).  Find the
@@ -586,7 +572,9 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
     int32_t *heads = ws.heads + CLS * heads_stride * kHeadPad;
     // stealing stays on the block's own XCD (victims 0 .. nb/8 - 1 of victim_of):
     // the scan a drained block makes before it exits is an eighth as long
-    const int nvict = a.sched == kSchedStatic ? 1 : ((nb >= 8 && !(nb & 7)) ? nb >> 3 : nb);
+    // (the grid is a whole number of rounds over the 8 XCDs: blocks per CU
+    // times a multiple of 8 compute units)
+    const int nvict = a.sched == kSchedStatic ? 1 : nb >> 3;
     float breg[FwdCfg<R>::BREG], apf[R / 4], bq[fwd_nq<R, KEEP>()][R / 4];
 #pragma unroll
     for (int i = 0; i < FwdCfg<R>::BREG; ++i) breg[i] = 0.f;

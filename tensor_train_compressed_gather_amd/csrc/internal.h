@@ -298,4 +298,18 @@ hipError_t radix_sort_pairs(const Plan &p, uint32_t *k0, int32_t *v0, uint32_t *
 
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// Victim order of the persistent kernels' work stealing: for a grid of nb
+// blocks (nb a positive multiple of 8: blocks are dispatched round-robin over
+// the 8 XCDs, so block b runs on XCD b mod 8), the vi-th victim of block me is
+// its own range first, then the other blocks of its own XCD, then those of the
+// other XCDs, one XCD after another.  For every such nb, vi -> victim is a
+// permutation of the blocks with victim 0 = me, so each static range is
+// claimed by its owner first and every range has a thief.
+__host__ __device__ inline int victim_of(int me, int vi, int nb)
+{
+    const int per = nb >> 3;
+    const int xo = vi / per, k = vi - xo * per;
+    return ((me & 7) + xo) % 8 + 8 * (((me >> 3) + k) % per);
+}
+
 } // namespace ttemb

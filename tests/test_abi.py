@@ -170,3 +170,51 @@ def test_block_stats_rejects_bad_arguments_on_the_host():
     assert rc == tt.TT_EMB_ERR_ARG
     rc = L.tt_emb_block_stats(None, None, 0, 1, 1, 0, None, recs, 4, C.byref(n), C.byref(khz))
     assert rc == tt.TT_EMB_ERR_ARG  # no handle
+
+
+def test_victim_order_is_a_permutation_for_every_grid():
+    # every persistent grid is a multiple of 8 blocks; for each such size up
+    # to 4096 and every block, the stealing order starts with the block's own
+    # range, visits every block exactly once, and keeps to the block's own XCD
+    # (block mod 8) for its first nb/8 victims (the thieves' range)
+    for nb in range(8, 4097, 8):
+        mes = range(nb) if nb <= 256 else sorted({0, 1, 7, 8, nb // 2, nb - 9, nb - 1})
+        for me in mes:
+            order = tt.tt_emb_victim_order(me, nb)
+            assert order[0] == me
+            assert np.array_equal(np.sort(order), np.arange(nb)), (nb, me)
+            assert np.all(order[: nb // 8] % 8 == me % 8), (nb, me)
+    for nb, me in ((0, 0), (4, 0), (12, 0), (16, 16), (16, -1)):
+        with pytest.raises(tt.TTEmbError) as e:
+            tt.tt_emb_victim_order(me, nb)
+        assert e.value.status == tt.TT_EMB_ERR_ARG
+
+
+def test_binding_rejects_wrong_dtype_layout_or_device():
+    # the library takes raw pointers: the binding must refuse what the
+    # kernels would misread before any call reaches it
+    import torch
+
+    idx64 = torch.zeros(4, dtype=torch.int64)
+    off64 = torch.zeros(3, dtype=torch.int64)
+    core = torch.zeros(8, dtype=torch.float32)
+    out = torch.zeros(2, 4, dtype=torch.float32)
+    ws = torch.zeros(256, dtype=torch.uint8)
+    cases = [
+        dict(indices=idx64.to(torch.int32), msg="dtype"),
+        dict(offsets=off64.to(torch.int32), msg="dtype"),
+        dict(cores=[core.double()], msg="dtype"),
+        dict(cores=[torch.zeros(4, 4)[:, 1]], msg="contiguous"),
+        dict(out=out.t(), msg="contiguous"),
+        dict(msg="GPU"),  # host tensors throughout
+    ]
+    for c in cases:
+        args = dict(indices=idx64, offsets=off64, cores=[core], out=out)
+        args.update({k: v for k, v in c.items() if k != "msg"})
+        with pytest.raises(tt.TTEmbError) as e:
+            tt.tt_emb_forward(None, args["cores"], args["indices"], args["offsets"], 2, args["out"], ws)
+        assert e.value.status == tt.TT_EMB_ERR_ARG and c["msg"] in str(e.value), c
+    with pytest.raises(tt.TTEmbError):
+        tt.tt_emb_backward(None, out.double(), [core], idx64, off64, 2, [core], ws)
+    with pytest.raises(tt.TTEmbError):
+        tt.tt_emb_sgd_update(None, [core.double()], [core], 0.01)

@@ -100,16 +100,37 @@ def test_forward_matches_oracle(cfg, bags):
 @pytest.mark.parametrize("opt", [
     dict(sched_mode=1), dict(sched_mode=2), dict(sched_mode=3, chunk_rows=1), dict(sched_mode=3, chunk_rows=3),
     dict(num_blocks=8), dict(group_mode=2), dict(sched_mode=1, num_blocks=8, chunk_rows=2),
-    # grids that are not a whole number of rounds over the 8 XCDs (fewer than
-    # 8 blocks, or 3 per CU x OCC): every static range is still claimed
+    # the smallest grids: a num_blocks of 1 or 3 is rounded up to 8 (one
+    # round over the 8 XCDs), so each class kernel runs 8 x its blocks per CU
     dict(num_blocks=1), dict(num_blocks=1, sched_mode=2), dict(num_blocks=3, sched_mode=1),
     dict(num_blocks=3, sched_mode=3, chunk_rows=2),
 ])
 def test_scheduling_modes_are_bit_identical(opt):
+    # every mode matches the oracle on its own, and the default path bit for bit
     w = W.make_workload(4, bags=64)
     base = Run(w).forward().cpu().numpy()
     other = Run(w, **opt).forward().cpu().numpy()
+    assert_out_close(w, other, oracle.forward(w))
     assert np.array_equal(base, other)
+
+
+def test_l2_checkpoints_are_consumed_at_full_size():
+    # stealing with L2 checkpoints on the 26-table batch with short chunks (many
+    # split prefix tiles): some chunks of split tiles must find a published
+    # checkpoint and use it, and the output must still match the oracle and
+    # the default path
+    w = W.make_workload(4)
+    base = Run(w).forward().cpu().numpy()
+    run = Run(w, sched_mode=3, chunk_rows=4)
+    out = run.forward().cpu().numpy()
+    c = run.grouping()["counts"]
+    print(f"[ckpt] split tiles {c['num_split_tiles']} steals {c['num_steals']} "
+          f"hits {c['num_ckpt_hits']} misses {c['num_ckpt_misses']}", flush=True)
+    assert c["num_split_tiles"] > 0 and c["num_ckpt_hits"] > 0
+    assert np.array_equal(base, out)
+    rng = np.random.default_rng(44)
+    bags = np.unique(np.concatenate([[0, w.B - 1], rng.integers(0, w.B, 300)]))
+    assert_out_close(w, out[bags], oracle.forward(w, bags=bags))
 
 
 def test_generic_kernels_match_oracle():

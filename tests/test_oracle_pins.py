@@ -385,9 +385,25 @@ def test_untouched_gradient_slices_are_zero():
             assert dG[k][s].any() == (s in used[k])
 
 
-def test_sgd_delta_closed_form():
-    dG = np.random.default_rng(13).standard_normal((5, 7))
-    assert np.array_equal(oracle.sgd_delta(dG, 0.01), -0.01 * dG)
+def test_sgd_delta_matches_torch_sgd_step():
+    # an independent statement of plain SGD: one torch.optim.SGD step (no
+    # momentum, no weight decay) on an fp64 parameter whose gradient is dG;
+    # the oracle's delta must be the parameter's change, sign and scale
+    # included, for several learning rates and gradient scales
+    import torch
+
+    rng = np.random.default_rng(13)
+    for lr, scale in ((0.01, 1.0), (0.5, 1e-3), (3.0, 1e4)):
+        p0 = rng.standard_normal((5, 7))
+        dG = rng.standard_normal((5, 7)) * scale
+        p = torch.nn.Parameter(torch.from_numpy(p0.copy()))
+        p.grad = torch.from_numpy(dG.copy())
+        torch.optim.SGD([p], lr=lr).step()
+        moved = p.detach().numpy() - p0
+        got = oracle.sgd_delta(dG, lr)
+        assert np.allclose(got, moved, rtol=1e-12, atol=1e-15 * np.abs(p0).max()), lr
+        # descent direction: the step never increases the linear loss <dG, p>
+        assert float(np.sum(got * dG)) < 0
 
 
 # ----------------------------------------------------------------- generator
