@@ -41,12 +41,26 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+def build_sanitized(path: str) -> str:
+    """The same oracle built for the CPU sanitizer check: AddressSanitizer and
+    UndefinedBehaviorSanitizer (any report aborts), same fp64
+    arithmetic flags."""
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fopenmp", "-fPIC", "-shared", "-o", path, _SRC]
+    subprocess.run(cmd, check=True)
+    return path
+
+
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            lib = C.CDLL(_LIB)
+            # TT_ORACLE_LIB: a sanitizer build of the same source (CPU tests only)
+            path = os.environ.get("TT_ORACLE_LIB")
+            if not path:
+                build()
+                path = _LIB
+            lib = C.CDLL(path)
             p = C.c_void_p
             i32, i64 = C.c_int32, C.c_int64
             lib.orc_decode.argtypes = [i64, p, p]

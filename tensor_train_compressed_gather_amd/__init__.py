@@ -14,7 +14,9 @@ import os
 import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtt_emb.so")
+# TT_EMB_LIB names another build of the same library (the host-sanitizer build
+# the CPU tests make); there is no fallback either way
+LIB_PATH = os.environ.get("TT_EMB_LIB") or os.path.join(_HERE, "libtt_emb.so")
 
 TT_EMB_OK = 0
 TT_EMB_ERR_ARG = -1

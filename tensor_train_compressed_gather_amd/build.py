@@ -46,5 +46,42 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# The host-side code of the C ABI (argument checks, the workspace plan, launch
+# sequencing) built with AddressSanitizer and UndefinedBehaviorSanitizer for a
+# CPU check; the sanitizers apply to the host pass only (-Xarch_host), the
+# device code is the ordinary build's.
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime the host-sanitizer build links to
+    (to be preloaded into a Python process that loads that build)."""
+    import glob
+
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang", "*",
+                                         "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise FileNotFoundError("libclang_rt.asan-x86_64.so not found under the ROCm LLVM")
+    return hits[-1]
+
+
+def build_host_sanitized(path: str) -> str:
+    """libtt_emb.so with api.hip's host code under ASan + UBSan, written to path."""
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(f)[0] + ".o")) for f in SOURCES):
+        build(verbose=False)
+    obj = path + ".api.o"
+    cmd = [HIPCC, *FLAGS, "-O1", "-g", *SAN_HOST, "-c", os.path.join(CSRC, "api.hip"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc (sanitized api.hip) failed:\n{r.stderr[-4000:]}")
+    objs = [obj] + [os.path.join(BUILD, os.path.splitext(f)[0] + ".o") for f in SOURCES if f != "api.hip"]
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *SAN_HOST[:4], "-shared-libsan", "-o", path, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (sanitized) failed:\n{r.stderr[-4000:]}")
+    return path
+
+
 if __name__ == "__main__":
     build()
