@@ -164,6 +164,11 @@ def _need(specs):
         device = t.device
 
 
+def _ptr_array(tensors):
+    arr = (C.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    return arr
+
+
 def tt_emb_status_string(status: int) -> str:
     return lib().tt_emb_status_string(int(status)).decode()
 

@@ -218,3 +218,27 @@ def test_binding_rejects_wrong_dtype_layout_or_device():
         tt.tt_emb_backward(None, out.double(), [core], idx64, off64, 2, [core], ws)
     with pytest.raises(tt.TTEmbError):
         tt.tt_emb_sgd_update(None, [core.double()], [core], 0.01)
+
+
+def test_binding_module_names_resolve():
+    # every global name the binding reads is defined in it or a builtin (a
+    # static check: the marshalling paths that reach the library need a GPU)
+    import ast
+    import builtins
+
+    src = open(os.path.join(ROOT, "tensor_train_compressed_gather_amd", "__init__.py")).read()
+    tree = ast.parse(src)
+    defined = set(dir(builtins)) | {"__file__"}
+    for node in ast.walk(tree):
+        if isinstance(node, (ast.FunctionDef, ast.ClassDef)):
+            defined.add(node.name)
+        elif isinstance(node, (ast.Import, ast.ImportFrom)):
+            defined |= {(a.asname or a.name).split(".")[0] for a in node.names}
+        elif isinstance(node, ast.arg):
+            defined.add(node.arg)
+        elif isinstance(node, ast.Name) and isinstance(node.ctx, ast.Store):
+            defined.add(node.id)
+        elif isinstance(node, ast.ExceptHandler) and node.name:
+            defined.add(node.name)
+    used = {n.id for n in ast.walk(tree) if isinstance(n, ast.Name) and isinstance(n.ctx, ast.Load)}
+    assert not (used - defined), sorted(used - defined)
