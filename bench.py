@@ -124,9 +124,9 @@ TRAFFIC_KERNELS = {  # (the training step runs one instantiation per rank)
     "k_bwd_class<32,": ("bwd_r32", ["backward.hip", "internal.h"]),
     "k_bwd_class<16,": ("bwd_r16", ["backward.hip", "internal.h"]),
     "k_contract<64,": ("fwd_r64", ["forward.hip", "internal.h"]),
-    "k_contract<32,": ("fwd_r32", ["forward.hip", "internal.h"]),
-    "k_contract<16,": ("fwd_r16", ["forward.hip", "internal.h"]),
-    "k_pool(": ("pool", ["forward.hip", "internal.h"]),
+    "k_contract_w<32,": ("fwd_r32", ["forward.hip", "internal.h"]),
+    "k_contract_w<16,": ("fwd_r16", ["forward.hip", "internal.h"]),
+    "k_pool<": ("pool", ["forward.hip", "internal.h"]),
 }
 
 
@@ -168,9 +168,9 @@ def write_traffic(d):
     print(json.dumps(out, indent=1, sort_keys=True))
 
 
-COUNTER_KERNELS = (("k_contract<16", "fwd_r16"), ("k_contract<32", "fwd_r32"), ("k_contract<64", "fwd_r64"),
+COUNTER_KERNELS = (("k_contract_w<16", "fwd_r16"), ("k_contract_w<32", "fwd_r32"), ("k_contract<64", "fwd_r64"),
                    ("k_bwd_class<16", "bwd_r16"), ("k_bwd_class<32", "bwd_r32"), ("k_bwd_class<64", "bwd_r64"),
-                   ("k_pool(", "pool"), ("k_gu_gather", "bwd_gather"))
+                   ("k_pool<", "pool"), ("k_gu_gather", "bwd_gather"))
 
 
 def write_counters(d, trace_csv=None):
@@ -274,24 +274,28 @@ def kcore_extras(torch, tt, W, opts, args):
 
 
 class Bench:
-    def __init__(self, w, torch, tt, options=None, keep=False):
+    def __init__(self, w, torch, tt, options=None, keep=False, forward_only=False):
         self.w, self.torch, self.tt = w, torch, tt
         self.keep = keep
         if keep:
             options = options or tt.tt_emb_options()
             options.keep_prefix = 1
         dev = "cuda"
-        self.emb = tt.TTEmbeddingBag(w.tables, dev, options)
+        self.emb = tt.TTEmbeddingBag(w.tables, dev, options, forward_only=forward_only)
         self.cores = [torch.from_numpy(c).to(dev) for c in w.cores]
         self.idx = torch.from_numpy(w.indices).to(dev)
         self.off = torch.from_numpy(w.offsets).to(dev)
         self.out = torch.empty((w.B, w.sum_D), dtype=torch.float32, device=dev)
-        self.grads = [torch.empty_like(c) for c in self.cores]
-        self.gout = torch.from_numpy(w.grad_out).to(dev) if w.grad_out is not None else None
+        self.grads = None if forward_only else [torch.empty_like(c) for c in self.cores]
+        self.gout = torch.from_numpy(w.grad_out).to(dev) if (w.grad_out is not None and not forward_only) else None
         self.emb.workspace(w.B, w.nnz)
 
     def fwd(self):
         self.emb.forward(self.cores, self.idx, self.off, self.w.B, out=self.out)
+
+    def fwd_post(self):
+        # contraction + pooling only: the grouping of the same inputs is already in the workspace
+        self.emb.forward(self.cores, self.idx, self.off, self.w.B, out=self.out, flags=self.tt.TT_EMB_REUSE_GROUPING)
 
     def fwd_fused(self):
         # pooling inside the contraction with float atomics (not bit-reproducible)
@@ -395,7 +399,65 @@ def cpu_baseline(w, target_s=12.0):
     kind = "fwd+bwd" if s.grad_out is not None else "fwd"
     return {"value": s.nnz / t, "unit": "lookups/s", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"first {S} of {w.B} bags of each of the {w.T} tables ({s.nnz} lookups), "
-                      f"{kind}, per-index fp64, {t:.1f} s"}
+                      f"{kind}, per-index fp64, {t:.1f} s",
+            "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_single_thread(W):
+    """The oracle's pooled forward on one host thread over the whole of the
+    three single-table workloads (1000 rows; 10^6 rows, bags of one; 10^7
+    rows, bags of 1-64): lookups/s and seconds."""
+    import oracle
+
+    out = {}
+    for cfg in (1, 2, 3):
+        w = W.make_workload(cfg)
+        t0 = time.perf_counter()
+        oracle.forward(w, threads=1)
+        dt = time.perf_counter() - t0
+        out[W.CONFIG_NAMES[cfg]] = {"lookups": w.nnz, "s": round(dt, 3), "lookups_per_s": w.nnz / dt,
+                                    "kind": "oracle fwd, per-index fp64, 1 thread"}
+    return out
+
+
+def measure_peaks(torch, tt):
+    """The device's own FP32 matrix-core rate (tt_emb_peak_mfma: independent
+    MFMA chains, no memory traffic) and device-to-device copy bandwidth (1 GiB
+    fp32 copy, read + write), timed on the current stream."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = cus * 4, 20000
+    buf = torch.empty(blocks, dtype=torch.float32, device="cuda")
+    tt.tt_emb_peak_mfma(blocks, 200, buf)  # warm-up
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    tt.tt_emb_peak_mfma(blocks, iters, buf)
+    ev1.record()
+    torch.cuda.synchronize()
+    mfma = blocks * 4 * 8 * iters * 2048.0 / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    copy = 5 * 8.0 * n / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst, buf
+    return {"mfma_f32_tflops": round(mfma, 2), "copy_gbs": round(copy, 1),
+            "datasheet": {"fp32_tflops": PEAK_FP32_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}}
 
 
 def run_ablation(args, torch, tt, W):
@@ -447,6 +509,18 @@ def run_sweep(args, torch, tt, W, opts):
         fms, _, fph = b.timed(b.fwd, args.steps, args.warmup)
         torch.cuda.synchronize()
         peak = torch.cuda.max_memory_allocated() - base
+        del b
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        # inference only: a forward-only workspace, no gradients
+        base_i = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        bi = Bench(w, torch, tt, opts, forward_only=True)
+        fws_bytes = tt.tt_emb_forward_workspace_size(bi.emb.handle, w.B, w.nnz)
+        ims, _, _ = bi.timed(bi.fwd, args.steps, args.warmup)
+        torch.cuda.synchronize()
+        ipeak = torch.cuda.max_memory_allocated() - base_i
+        del bi
         tphase, _, tst = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in tph.items() if v[1]})
         fphase, _, fst = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in fph.items() if v[1]})
         tgroup = tphase.get("group_sort", 0) + tphase.get("group_rle", 0)
@@ -456,11 +530,12 @@ def run_sweep(args, torch, tt, W, opts):
                "fwd_ms": round(fms, 4), "fwd_lookups_per_s": w.nnz / (fms * 1e-3),
                "grouping_share_train": round(tgroup / tms, 4), "grouping_share_fwd": round(fgroup / fms, 4),
                "train_phases_ms": tphase, "fwd_phases_ms": fphase, "grouping_stages_ms": fst,
-               "workspace_bytes": ws_bytes, "peak_device_bytes": int(peak)}
+               "workspace_bytes": ws_bytes, "peak_device_bytes_train": int(peak),
+               "inference": {"fwd_ms": round(ims, 4), "workspace_bytes": fws_bytes,
+                             "peak_device_bytes": int(ipeak)}}
         rows.append(row)
-        print(f"[sweep] B={B} nnz={w.nnz} train {tms:.3f} ms fwd {fms:.3f} ms ws {ws_bytes / 2**30:.2f} GiB",
-              file=sys.stderr, flush=True)
-        del b
+        print(f"[sweep] B={B} nnz={w.nnz} train {tms:.3f} ms fwd {fms:.3f} ms ws {ws_bytes / 2**30:.2f} GiB "
+              f"inference ws {fws_bytes / 2**30:.2f} GiB peak {ipeak / 2**30:.2f} GiB", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     print(json.dumps({"mode": "sweep", "workload": "26 tables (the training workload's shapes), B bags per table",
                       "data": "synthetic", "steps": args.steps, "warmup": args.warmup, "sweep": rows}), flush=True)
@@ -547,10 +622,13 @@ def main():
         wf = W.make_workload(args.config)
         bf = Bench(wf, torch, tt, opts)
         fms, _, fph = bf.timed(bf.fwd, args.steps, args.warmup)
+        post, _, _ = bf.timed(bf.fwd_post, args.steps, args.warmup)
         ur, up, nz, fc = bf.counts()
         ff, _, _ = phase_flops(wf.tables, ur, up, nz)
         fphase, fkern, fstages = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in fph.items() if v[1]})
+        roof = ff / (PEAK_FP32_TFLOPS * 1e12) * 1e3
         print(json.dumps({"mode": "fwd", "workload": W.CONFIG_NAMES[args.config], "ms": fms,
+                          "post_grouping_ms": post, "post_grouping_frac_of_roofline": roof / post,
                           "lookups_per_s": wf.nnz / (fms * 1e-3), "phases_ms": fphase,
                           "grouping_stages_ms": fstages, "kernels_ms": fkern,
                           "contract_flops": ff, "unique_rows": sum(ur), "prefix_groups": sum(up),
@@ -613,19 +691,23 @@ def main():
 
     if not args.no_extra:
         fwd = {}
-        for cfg in (4, 3):
+        for cfg in (4, 3, 2):
             wf = W.make_workload(cfg)
             bf = Bench(wf, torch, tt, opts)
             fms, _, fph = bf.timed(bf.fwd, args.steps, args.warmup)
             ur, up, nz, fc = bf.counts()
             ff, _, _ = phase_flops(wf.tables, ur, up, nz)
-            fphase, _, fstages = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in fph.items() if v[1]})
-            post = fphase.get("contract", 0) + fphase.get("pool", 0)
+            fphase, fkern, fstages = split_timers({k: (v[0] / max(v[1], 1), v[1]) for k, v in fph.items() if v[1]})
+            # the forward after grouping (contraction + pooling), timed on its own
+            # with the phase timers off (their events would add to it)
+            post, _, _ = bf.timed(bf.fwd_post, args.steps, args.warmup)
             cms = fphase.get("contract", 0)
+            ws_fwd = tt.tt_emb_forward_workspace_size(bf.emb.handle, wf.B, wf.nnz)
             fwd[W.CONFIG_NAMES[cfg]] = {
-                "lookups_per_s": wf.nnz / (fms * 1e-3), "ms": fms,
+                "lookups_per_s": wf.nnz / (fms * 1e-3), "ms": fms, "forward_workspace_bytes": ws_fwd,
                 "post_grouping_ms": post, "post_grouping_lookups_per_s": wf.nnz / (post * 1e-3) if post else None,
-                "phases_ms": fphase, "grouping_stages_ms": fstages, "nnz": wf.nnz, "unique_rows": sum(ur),
+                "phases_ms": fphase, "kernels_ms": {k: round(v, 4) for k, v in fkern.items()},
+                "grouping_stages_ms": fstages, "nnz": wf.nnz, "unique_rows": sum(ur),
                 "prefix_groups": sum(up),
                 "contract_tflops": ff / (cms * 1e-3) / 1e12 if cms else None,
                 "contract_frac_fp32_peak": ff / (cms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS if cms else None,
@@ -647,8 +729,20 @@ def main():
         res["fwd"] = fwd
         res["fwd_kcores"] = kcore_extras(torch, tt, W, opts, args)
 
+    peaks = measure_peaks(torch, tt)
+    res["measured_peaks"] = peaks
+    if roof["unit"] == "TFLOP/s":
+        roof["frac_of_measured_peak"] = roof["achieved"] / peaks["mfma_f32_tflops"]
+    else:
+        roof["frac_of_measured_peak"] = roof["achieved"] / peaks["copy_gbs"]
+    if "fwd" in res:
+        for v in res["fwd"].values():
+            if v.get("post_grouping_ms"):
+                v["post_grouping_frac_of_measured_roofline"] = (
+                    v["roofline_ms_fp32"] * PEAK_FP32_TFLOPS / peaks["mfma_f32_tflops"] / v["post_grouping_ms"])
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w)
+        res["cpu_single_thread"] = cpu_single_thread(W)
     print(json.dumps(res), flush=True)
 
 

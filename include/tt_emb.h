@@ -185,6 +185,17 @@ int tt_emb_destroy(tt_emb_t h);
  * and nnz lookups (an upper bound that does not depend on the index values). */
 int tt_emb_workspace_size(tt_emb_t h, int64_t B, int64_t nnz, size_t *bytes);
 
+/* Bytes of device workspace that an inference-only caller needs: the
+ * grouping and a forward without TT_EMB_KEEP_PREFIX (the FlowTT page,
+ * Abstract and Conclusion, reports the method's inference peak memory).  A
+ * workspace of this size (smaller than tt_emb_workspace_size's) is accepted
+ * by tt_emb_group, tt_emb_forward without TT_EMB_KEEP_PREFIX,
+ * tt_emb_grouping_view, tt_emb_block_stats and tt_emb_poll_error; the
+ * backward and a forward with TT_EMB_KEEP_PREFIX return TT_EMB_ERR_WORKSPACE
+ * on it.  The forward part is a prefix of the full layout, so a full
+ * workspace serves both. */
+int tt_emb_forward_workspace_size(tt_emb_t h, int64_t B, int64_t nnz, size_t *bytes);
+
 /* Build the grouping of (indices, offsets) into ws: validation and key build,
  * stable radix sort by (table, row), unique extraction, prefix run-length
  * encoding and the work list (FlowTT section 4, grouping breakdown). */
@@ -258,6 +269,15 @@ int tt_emb_block_stats(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B, i
  * function; host only, no device work.  TT_EMB_ERR_ARG for a null array,
  * nb < 8, nb not a multiple of 8, or me outside [0, nb). */
 int tt_emb_victim_order(int32_t me, int32_t nb, int32_t *order);
+
+/* Measurement aid (not part of the hot path): launches `blocks` blocks of
+ * four waves, each wave running eight independent chains of `iters` FP32
+ * matrix-core instructions (v_mfma_f32_16x16x4_f32, 2048 flops each) with no
+ * memory traffic, and writes one float per block to out (device, caller-owned,
+ * `blocks` floats).  Timing it on the stream gives the device's measured FP32
+ * matrix peak: blocks * 4 * 8 * iters * 2048 flops per launch.  Stream-ordered,
+ * no synchronisation; TT_EMB_ERR_ARG for non-positive sizes or a null out. */
+int tt_emb_peak_mfma(int32_t blocks, int32_t iters, float *out, void *stream);
 
 /* Synchronise the stream and report a device-detected error recorded in ws
  * since the last grouping (TT_EMB_OK, TT_EMB_ERR_INDEX or TT_EMB_ERR_OFFSETS). */

@@ -35,10 +35,11 @@ TT_EMB_REUSE_PREFIX = 4
 TT_EMB_ATOMIC_POOL = 8
 
 EXPORTED = (
-    "tt_emb_create", "tt_emb_create_k", "tt_emb_destroy", "tt_emb_workspace_size", "tt_emb_group", "tt_emb_forward",
+    "tt_emb_create", "tt_emb_create_k", "tt_emb_destroy", "tt_emb_workspace_size", "tt_emb_forward_workspace_size",
+    "tt_emb_group", "tt_emb_forward",
     "tt_emb_backward", "tt_emb_sgd_update", "tt_emb_grouping_view", "tt_emb_poll_error",
     "tt_emb_status_string", "tt_emb_timing_enable", "tt_emb_timing_read", "tt_emb_timer_name",
-    "tt_emb_block_stats", "tt_emb_victim_order",
+    "tt_emb_block_stats", "tt_emb_victim_order", "tt_emb_peak_mfma",
 )
 BLOCK_STAT_KERNELS = ("fwd_r8", "fwd_r16", "fwd_r32", "fwd_r64", "bwd_r8", "bwd_r16", "bwd_r32", "bwd_r64")
 TIMER_NAMES = ("group_sort", "group_rle", "contract", "pool", "bwd_gather", "bwd_contract",
@@ -86,6 +87,7 @@ def lib():
             L.tt_emb_create_k.argtypes = [i32, i32, p, p, p, p, C.POINTER(tt_emb_options), C.POINTER(p)]
             L.tt_emb_destroy.argtypes = [p]
             L.tt_emb_workspace_size.argtypes = [p, i64, i64, C.POINTER(C.c_size_t)]
+            L.tt_emb_forward_workspace_size.argtypes = [p, i64, i64, C.POINTER(C.c_size_t)]
             L.tt_emb_group.argtypes = [p, p, p, i64, i64, p, C.c_size_t, p]
             L.tt_emb_forward.argtypes = [p, p, p, p, i64, i64, p, p, C.c_size_t, u32, p]
             L.tt_emb_backward.argtypes = [p, p, p, p, p, i64, i64, p, p, C.c_size_t, u32, p]
@@ -94,6 +96,7 @@ def lib():
             L.tt_emb_poll_error.argtypes = [p, p, p]
             L.tt_emb_block_stats.argtypes = [p, p, C.c_size_t, i64, i64, i32, p, p, i32, p, p]
             L.tt_emb_victim_order.argtypes = [i32, i32, p]
+            L.tt_emb_peak_mfma.argtypes = [i32, i32, p, p]
             L.tt_emb_status_string.argtypes = [C.c_int]
             L.tt_emb_status_string.restype = C.c_char_p
             L.tt_emb_timing_enable.argtypes = [p, i32]
@@ -216,6 +219,12 @@ def tt_emb_destroy(h):
 def tt_emb_workspace_size(h, B: int, nnz: int) -> int:
     out = C.c_size_t()
     _check(lib().tt_emb_workspace_size(h, int(B), int(nnz), C.byref(out)), "tt_emb_workspace_size")
+    return int(out.value)
+
+
+def tt_emb_forward_workspace_size(h, B: int, nnz: int) -> int:
+    out = C.c_size_t()
+    _check(lib().tt_emb_forward_workspace_size(h, int(B), int(nnz), C.byref(out)), "tt_emb_forward_workspace_size")
     return int(out.value)
 
 
@@ -351,6 +360,13 @@ def tt_emb_victim_order(me: int, nb: int):
     return order
 
 
+def tt_emb_peak_mfma(blocks: int, iters: int, out, stream=None):
+    """Launch the FP32 matrix-core peak kernel (measurement aid): blocks x 4
+    waves x 8 chains x iters instructions of 2048 flops."""
+    _need([(out, "out", "float32")])
+    _check(lib().tt_emb_peak_mfma(int(blocks), int(iters), _ptr(out), _stream(stream)), "tt_emb_peak_mfma")
+
+
 def tt_emb_timing_enable(h, enable: bool = True):
     _check(lib().tt_emb_timing_enable(h, 1 if enable else 0), "tt_emb_timing_enable")
 
@@ -376,7 +392,7 @@ class TTEmbeddingBag:
     [n_k][R_{k-1}][d_k][R_k]; indices/offsets are int64 device tensors in
     table-major CSR (T*B+1 offsets)."""
 
-    def __init__(self, tables, device="cuda", options: tt_emb_options | None = None):
+    def __init__(self, tables, device="cuda", options: tt_emb_options | None = None, forward_only: bool = False):
         self.tables = list(tables)
         self.T = len(self.tables)
         self.K = len(self.tables[0].n)
@@ -390,13 +406,17 @@ class TTEmbeddingBag:
         self.sum_D = sum(int(math.prod(t.d)) for t in self.tables)
         self._ws = None
         self._ws_key = None
+        # inference only: the smaller forward workspace (no backward, no
+        # TT_EMB_KEEP_PREFIX)
+        self.forward_only = bool(forward_only)
 
     def workspace(self, B: int, nnz: int):
         import torch
 
         key = (int(B), int(nnz))
         if self._ws_key != key:
-            need = tt_emb_workspace_size(self.handle, B, nnz)
+            size = tt_emb_forward_workspace_size if self.forward_only else tt_emb_workspace_size
+            need = size(self.handle, B, nnz)
             if self._ws is None or self._ws.numel() < need:
                 self._ws = None
                 self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtt_emb.so")
-SOURCES = ["api.hip", "group.hip", "forward.hip", "backward.hip", "kcores.hip", "misc.hip"]
+SOURCES = ["api.hip", "group.hip", "forward.hip", "backward.hip", "kcores.hip", "misc.hip", "peak.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17",

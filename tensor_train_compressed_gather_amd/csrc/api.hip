@@ -75,8 +75,12 @@ int64_t g2p_slots_for(int64_t nnz)
     return v < kMaxG2Slots ? v : kMaxG2Slots;
 }
 
-// Carve the workspace.  With base == nullptr only the size is computed.
-size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan *p)
+// Carve the workspace.  With base == nullptr only the size is computed.  The
+// regions a forward without TT_EMB_KEEP_PREFIX uses come first; *fwd_bytes
+// (optional) receives their size.  With fwd_only the backward's pointers in
+// the plan are left null (the caller's buffer ends before them).
+size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan *p, size_t *fwd_bytes = nullptr,
+                      bool fwd_only = false)
 {
     size_t off = 0;
     auto take = [&](size_t bytes) -> char * {
@@ -142,10 +146,13 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.crec = (ChunkRec *)take(sizeof(ChunkRec) * chunks);
     w.chunk_cap = chunks;
     w.g3t = (float *)take(4 * (size_t)h->g3t_elems);
-    // 4 classes x up to 8 blocks per CU, one 128-byte line each
-    w.heads = (int32_t *)take(4 * (size_t)h->num_blocks * 4 * 8 * 32);
-    w.flags = (int32_t *)take(4 * (size_t)kMaxCkptSlots);
-    w.ckpt = (float *)take(4 * (size_t)kMaxCkptSlots * (4 * (16 * 68 + 16)));
+    // 4 classes x up to kMaxWorkersPerCu workers per CU, one 128-byte line each
+    w.heads = (int32_t *)take(4 * (size_t)h->num_blocks * 4 * kMaxWorkersPerCu * 32);
+    // checkpoint slots: one per split tile, at most one per chunk
+    const int64_t ckpt_slots = chunks < kMaxCkptSlots ? chunks : kMaxCkptSlots;
+    w.ckpt_slots = (int32_t)ckpt_slots;
+    w.flags = (int32_t *)take(4 * (size_t)ckpt_slots);
+    w.ckpt = (float *)take(4 * (size_t)ckpt_slots * (4 * (16 * 68 + 16)));
     // bounds on unique rows / units per table that do not depend on values
     int64_t e_elems = 0, p3_elems = 0;
     for (int t = 0; t < T; ++t) {
@@ -165,6 +172,35 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.sink = (float *)take(4 * (size_t)kSinkFloats);
     w.bstat = (BlockStat *)take(sizeof(BlockStat) * (size_t)kStatKernels * kStatBlocks);
     w.cbase = (int64_t *)take(8 * T);
+    w.ftab = (FwdTab *)take(sizeof(FwdTab) * (size_t)T);
+    w.lk = (int2 *)take(8 * n);
+    // K >= 4 cores: per prefix length m = 2..K-1, the group of each unique
+    // row, the groups' first rows, and one intermediate per group (at most
+    // min(prefixes of length m, rows, nnz) groups per table)
+    KPlan kp{};
+    if (h->K >= 4) {
+        kp.K = h->K;
+        kp.dkt = h->dkt;
+        for (int m = 2; m <= h->K - 1; ++m) {
+            int64_t gb = 0, sm = 1;
+            for (int t = 0; t < T; ++t) {
+                const KTab &kt = h->ktabs[t];
+                int64_t prod = 1;
+                for (int j = 0; j < m; ++j) prod = std::min<int64_t>(prod * kt.n[j], (int64_t)1 << 40);
+                gb += std::min<int64_t>(std::min<int64_t>(prod, h->tabs[t].N), n);
+                sm = std::max<int64_t>(sm, (int64_t)kt.P[m] * kt.R[m]);
+            }
+            gb = std::min<int64_t>(gb, n);
+            kp.ugrp[m] = (int32_t *)take(4 * n);
+            kp.gfirst[m] = (int32_t *)take(4 * (n + 1));
+            kp.V[m] = (float *)take(4 * (size_t)(gb * sm));
+            kp.smax[m] = sm;
+        }
+    }
+    // everything a forward without TT_EMB_KEEP_PREFIX (and the grouping, its
+    // views and the block records) touches lies before this point; the
+    // backward's regions and the kept prefix intermediates follow
+    const size_t fwd_end = off;
     // kept prefix intermediates (keep_prefix handles only): 16 x R2 floats per
     // unit of every table of the kept rank classes, at most min(units of the
     // table, nnz) units
@@ -180,7 +216,6 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
         }
     }
     w.Cg = (float *)take(4 * (cg_elems > 0 ? cg_elems : 4));
-    w.lk = (int2 *)take(8 * n);
     w.gu_ml = (int32_t *)take(4 * tasks);
     w.gu_mr = (int32_t *)take(4 * tasks);
     w.P3 = (float *)take(4 * (p3_elems > part_elems ? p3_elems : part_elems));
@@ -243,28 +278,7 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
         p->dtab = h->dtab;
         p->ws = w;
     }
-    // K >= 4 cores: per prefix length m = 2..K-1, the group of each unique
-    // row, the groups' first rows, and one intermediate per group (at most
-    // min(prefixes of length m, rows, nnz) groups per table)
-    KPlan kp{};
     if (h->K >= 4) {
-        kp.K = h->K;
-        kp.dkt = h->dkt;
-        for (int m = 2; m <= h->K - 1; ++m) {
-            int64_t gb = 0, sm = 1;
-            for (int t = 0; t < T; ++t) {
-                const KTab &kt = h->ktabs[t];
-                int64_t prod = 1;
-                for (int j = 0; j < m; ++j) prod = std::min<int64_t>(prod * kt.n[j], (int64_t)1 << 40);
-                gb += std::min<int64_t>(std::min<int64_t>(prod, h->tabs[t].N), n);
-                sm = std::max<int64_t>(sm, (int64_t)kt.P[m] * kt.R[m]);
-            }
-            gb = std::min<int64_t>(gb, n);
-            kp.ugrp[m] = (int32_t *)take(4 * n);
-            kp.gfirst[m] = (int32_t *)take(4 * (n + 1));
-            kp.V[m] = (float *)take(4 * (size_t)(gb * sm));
-            kp.smax[m] = sm;
-        }
         // backward: groups of the first digit, the intermediates' gradients and
         // the per-group / per-row core partials
         for (int m = 1; m <= h->K - 1; ++m) {
@@ -316,23 +330,40 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     if (p) {
         p->kp = kp;
         p->kp_n = h->K >= 4 ? h->kn.data() : nullptr;
+        if (fwd_only) {
+            Ws &v = p->ws;
+            v.Cg = nullptr;
+            v.gu_ml = v.gu_mr = nullptr;
+            v.P3 = v.G1P = v.G2P = nullptr;
+            v.g3rng = v.run_pbase = v.run_sbase = v.piece_tb = v.piece_te = v.piece_slot = nullptr;
+            v.rkey0 = v.rkey1 = nullptr;
+            v.rval0 = v.rval1 = nullptr;
+            v.rorder = nullptr;
+            for (int m = 0; m < kMaxK; ++m) p->kp.dV[m] = p->kp.Q[m] = p->kp.Cc[m] = nullptr;
+            p->kp.ugrp[1] = p->kp.gfirst[1] = nullptr;
+            p->kp.PK = p->kp.red = nullptr;
+        }
     }
+    if (fwd_bytes) *fwd_bytes = fwd_end;
     return off;
 }
 
 bool bad_ptr(const void *ptr) { return ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
 
+// full: the call needs the whole workspace (backward, or a forward that keeps
+// the prefix intermediates); otherwise the forward part is enough.
 int check_call(const tt_emb *h, int64_t B, int64_t nnz, const int64_t *indices, const int64_t *offsets,
-               void *ws, size_t ws_bytes, Plan *p)
+               void *ws, size_t ws_bytes, Plan *p, bool full)
 {
     if (!h || B < 0 || nnz < 0 || nnz >= (int64_t)0x7fffffff) return TT_EMB_ERR_ARG;
     if ((int64_t)h->T * B >= (int64_t)0x7fffffff) return TT_EMB_ERR_ARG;
     if (!offsets) return TT_EMB_ERR_ARG;
     if (nnz > 0 && !indices) return TT_EMB_ERR_ARG;
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return TT_EMB_ERR_WORKSPACE;
-    const size_t need = plan_workspace(h, B, nnz, nullptr, nullptr);
-    if (ws_bytes < need) return TT_EMB_ERR_WORKSPACE;
-    plan_workspace(h, B, nnz, static_cast<char *>(ws), p);
+    size_t fwd = 0;
+    const size_t all = plan_workspace(h, B, nnz, nullptr, nullptr, &fwd);
+    if (ws_bytes < (full ? all : fwd)) return TT_EMB_ERR_WORKSPACE;
+    plan_workspace(h, B, nnz, static_cast<char *>(ws), p, nullptr, ws_bytes < all);
     return TT_EMB_OK;
 }
 
@@ -611,12 +642,19 @@ int tt_emb_workspace_size(tt_emb_t h, int64_t B, int64_t nnz, size_t *bytes)
     return TT_EMB_OK;
 }
 
+int tt_emb_forward_workspace_size(tt_emb_t h, int64_t B, int64_t nnz, size_t *bytes)
+{
+    if (!h || !bytes || B < 0 || nnz < 0 || nnz >= (int64_t)0x7fffffff) return TT_EMB_ERR_ARG;
+    plan_workspace(h, B, nnz, nullptr, nullptr, bytes);
+    return TT_EMB_OK;
+}
+
 int tt_emb_group(tt_emb_t h, const int64_t *indices, const int64_t *offsets, int64_t B, int64_t nnz, void *ws,
                  size_t ws_bytes, void *stream)
 {
     try {
         Plan p;
-        int rc = check_call(h, B, nnz, indices, offsets, ws, ws_bytes, &p);
+        int rc = check_call(h, B, nnz, indices, offsets, ws, ws_bytes, &p, false);
         if (rc) return rc;
         if ((rc = set_device(h))) return rc;
         return hip_status(launch_grouping(p, indices, offsets, (hipStream_t)stream));
@@ -652,7 +690,7 @@ int tt_emb_forward(tt_emb_t h, const float *const *cores, const int64_t *indices
 {
     try {
         Plan p;
-        int rc = check_call(h, B, nnz, indices, offsets, ws, ws_bytes, &p);
+        int rc = check_call(h, B, nnz, indices, offsets, ws, ws_bytes, &p, (flags & TT_EMB_KEEP_PREFIX) != 0);
         if (rc) return rc;
         if (B > 0 && !out) return TT_EMB_ERR_ARG;
         if (h->K >= 4) {
@@ -690,7 +728,7 @@ int tt_emb_backward(tt_emb_t h, const float *grad_out, const float *const *cores
 {
     try {
         Plan p;
-        int rc = check_call(h, B, nnz, indices, offsets, ws, ws_bytes, &p);
+        int rc = check_call(h, B, nnz, indices, offsets, ws, ws_bytes, &p, true);
         if (rc) return rc;
         if (B > 0 && !grad_out) return TT_EMB_ERR_ARG;
         if (h->K >= 4) {
@@ -831,7 +869,7 @@ int tt_emb_grouping_view(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B,
     if (!view) return TT_EMB_ERR_ARG;
     Plan p;
     int64_t dummy_off[1] = {0};
-    int rc = check_call(h, B, nnz, nnz > 0 ? dummy_off : nullptr, dummy_off, const_cast<void *>(ws), ws_bytes, &p);
+    int rc = check_call(h, B, nnz, nnz > 0 ? dummy_off : nullptr, dummy_off, const_cast<void *>(ws), ws_bytes, &p, false);
     if (rc) return rc;
     if ((rc = set_device(h))) return rc;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TT_EMB_ERR_HIP;
@@ -865,7 +903,7 @@ int tt_emb_block_stats(tt_emb_t h, const void *ws, size_t ws_bytes, int64_t B, i
     if (!out || !nblocks || !clock_khz || cap < 0 || kernel < 0 || kernel >= kStatKernels) return TT_EMB_ERR_ARG;
     Plan p;
     int64_t dummy_off[1] = {0};
-    int rc = check_call(h, B, nnz, nnz > 0 ? dummy_off : nullptr, dummy_off, const_cast<void *>(ws), ws_bytes, &p);
+    int rc = check_call(h, B, nnz, nnz > 0 ? dummy_off : nullptr, dummy_off, const_cast<void *>(ws), ws_bytes, &p, false);
     if (rc) return rc;
     if ((rc = set_device(h))) return rc;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TT_EMB_ERR_HIP;

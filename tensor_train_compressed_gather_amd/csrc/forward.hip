@@ -43,7 +43,7 @@ struct FwdCfg {
     static constexpr int BREG = ((R / 4 + 3) / 4) * (R / 4); // G2 slice registers per lane
 };
 static_assert(FwdCfg<64>::CTILE == kCTile, "checkpoint slot holds the largest prefix tile");
-constexpr int kMaxClsOcc = 8; // queue heads per CU reserved for each class
+constexpr int kMaxClsOcc = kMaxWorkersPerCu; // queue heads per CU reserved for each class
 constexpr int kPoolCap = 64;  // fused pooling: lookups of a row pooled by the contraction itself
 constexpr int kSchedStatic = 1, kSchedSteal = 2, kSchedStealL2 = 3;
 // Default scheduling per rank class (8, 16, 32, 64), from the scheduling
@@ -87,30 +87,36 @@ __device__ void g3t_copy(const FwdArgs &a);
 __global__ __launch_bounds__(kThreads) void k_queue_init(FwdArgs a, ClassGrid g, int stride, int g3t)
 {
     if (g3t) g3t_copy(a);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        // the table's record for the class kernels
+        const int t = blockIdx.y;
+        const TableDesc &tb = a.tab[t];
+        FwdTab f;
+        f.g1 = a.cores.g[t][0];
+        f.g2 = a.cores.g[t][1];
+        f.g3t = a.ws.g3t + tb.g3t_off;
+        f.E = a.ws.E + a.ws.ebase[t];
+        f.Cg = a.ws.Cg ? a.ws.Cg + a.ws.cbase[t] : nullptr;
+        f.d1 = tb.d1;
+        f.d2 = tb.d2;
+        f.d3 = tb.d3;
+        f.i2_base = (int32_t)tb.i2_base;
+        f.Dp = tb.Dp;
+        f.pad = 0;
+        a.ws.ftab[t] = f;
+    }
     if (blockIdx.x != 0 || blockIdx.y != 0) return;
     const Ws &ws = a.ws;
     __shared__ int cstart[6];
-    const int64_t C = ws.ctrl[CTRL_CHUNKS];
     int split = ws.ctrl[CTRL_SPLIT];
-    if (split > kMaxCkptSlots) split = kMaxCkptSlots;
-    if (threadIdx.x <= 5) {
-        const int c = threadIdx.x; // first chunk whose class rank is >= c
-        int lo = 0, hi = (int)C;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            const int cls = ws.crec[mid].cls;
-            const int rank = cls < 0 ? 4 : cls;
-            if (rank < c) lo = mid + 1;
-            else hi = mid;
-        }
-        cstart[c] = c == 5 ? (int)C : lo;
-    }
+    if (split > ws.ckpt_slots) split = ws.ckpt_slots;
+    // first chunk of each rank class, from the work list (k_chunk_records)
+    if (threadIdx.x <= 5) cstart[threadIdx.x] = ws.ctrl[CTRL_CLS_START + threadIdx.x];
     __syncthreads();
     for (int c = 0; c < 4; ++c)
         for (int b = threadIdx.x; b < g.nb[c]; b += blockDim.x)
             ws.heads[(c * stride + b) * kHeadPad] = cstart[c] + range_begin(b, cstart[c + 1] - cstart[c], g.nb[c]);
     for (int i = threadIdx.x; i < split; i += blockDim.x) ws.flags[i] = 0;
-    if (threadIdx.x < 5) ws.ctrl[CTRL_CLS_START + threadIdx.x] = cstart[threadIdx.x];
     if (threadIdx.x < 4) ws.bstat[threadIdx.x * kStatBlocks].nb = 0; // forward class records
     if (threadIdx.x == 0) {
         ws.ctrl[CTRL_STEALS] = 0;
@@ -646,6 +652,691 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
     }
 }
 
+// ---------------------------------------------------------------------------
+// Per-wave contraction of the rank classes R <= 32 (R1 = R2 = R, d1, d2 <= 4,
+// d3 <= 16).  Every wave of the grid is an independent persistent worker with
+// its own static range of chunks (and, in the stealing modes, its own queue
+// head): no block barrier anywhere in the chunk loop.  Per chunk (one tile of
+// up to four prefix units sharing (table, i2), at most 32 of its unique rows):
+//  * C for the tile's units, [16 rows (unit, j1)] x [4R columns (j2, r2)], on
+//    v_mfma_f32_16x16x4_f32 with the G1[i1] slices stacked into the A operand
+//    and the whole G2[i2] slice as the B operand, held in the wave's registers
+//    while consecutive chunks keep (table, i2) (B-stationary: (R/4)^2 VGPRs);
+//  * C is written to the wave's own LDS region as [unit][m2 = j1*d2 + j2][r2]
+//    and stays there while the wave's next chunks continue the same tile;
+//  * rows: per output tile of P = 16/d3 rows of one unit,
+//      O[(slot, j3)][m2] = sum_r2 G3t[i3_slot][j3][r2] * C_u[m2][r2],
+//    A = the rows' transposed G3 slices (float4 loads), B = C_u read from LDS
+//    along r2; each lane then holds four consecutive columns of one E row
+//    (column m2*d3 + j3), written with one float4 store when d3 is 4, 8 or 16.
+// FlowTT page section 3.2 (C = A.B computed once per prefix group and kept
+// on chip, E = C.D for each row), section 3.3 (prefix groups as the unit of
+// work) and section 3.4 (persistent workers, stealing, L2 checkpoints of a
+// prefix tile split over several workers).
+template <int R>
+struct FwdW {
+    static constexpr int KQ = R / 4;       // K values each lane feeds per 16x16 output tile
+    static constexpr int NT = R / 4;       // 16-column tiles of the 4R columns of C
+    static constexpr int BREG = NT * KQ;   // G2 slice registers per lane
+    static constexpr int CSTR = R + 4;     // LDS row stride of C (floats)
+    static constexpr int CU = 16 * CSTR;   // floats per unit
+    static constexpr int OCC = R <= 16 ? 4 : 2; // blocks of four waves per CU
+    static constexpr int NQ = 4;           // row tiles whose operands are loaded together
+};
+template <int R> constexpr int fwd_workers_per_cu() { return FwdW<R>::OCC * (kThreads / 64); }
+static_assert(fwd_workers_per_cu<8>() <= kMaxClsOcc && fwd_workers_per_cu<16>() <= kMaxClsOcc &&
+              fwd_workers_per_cu<32>() <= kMaxClsOcc, "one queue head per worker");
+
+template <int R, bool KEEP>
+__global__ __launch_bounds__(kThreads, FwdW<R>::OCC) void k_contract_w(FwdArgs a, int heads_stride)
+{
+    using L = FwdW<R>;
+    constexpr int CLS = R == 8 ? 0 : R == 16 ? 1 : 2;
+    constexpr int KQ = L::KQ, NT = L::NT, CSTR = L::CSTR, CU = L::CU, NQ = L::NQ;
+    __shared__ __attribute__((aligned(16))) float Cs_all[kThreads / 64][4 * CU];
+    __shared__ long long s_t0;
+    __shared__ int s_work, s_rows, s_steals, s_hits, s_misses;
+    const int lane = threadIdx.x & 63, w = uni(threadIdx.x >> 6), li = lane & 15, kq = lane >> 4;
+    if (threadIdx.x == 0) {
+        s_t0 = wall_clock64();
+        s_work = s_rows = s_steals = s_hits = s_misses = 0;
+    }
+    float *Cw = Cs_all[w];
+    const Ws &ws = a.ws;
+    // worker numbering with worker % 8 = the XCD of its block (blocks go
+    // round-robin over the 8 XCDs and the grid is a multiple of 8 blocks)
+    const int nb = gridDim.x * (kThreads / 64), me = w * gridDim.x + blockIdx.x;
+    const int base = ws.ctrl[CTRL_CLS_START + CLS];
+    const int64_t C = ws.ctrl[CTRL_CLS_START + CLS + 1] - base;
+    int32_t *heads = ws.heads + CLS * heads_stride * kHeadPad;
+    const int nvict = a.sched == kSchedStatic ? 1 : nb >> 3;
+    int vi = 0, steals = 0, hits = 0, misses = 0, nwork = 0, nrows = 0;
+    float breg[L::BREG];
+#pragma unroll
+    for (int i = 0; i < L::BREG; ++i) breg[i] = 0.f;
+    int bkey = -1, ctile = -1;
+    // claims run one chunk ahead: chunk c+1 is claimed (and its record loaded)
+    // while chunk c runs
+    int c = claim_finish(heads, base, me, vi, nb, nvict, C, claim_start(heads, me, vi, nb, nvict), steals);
+    int rec = c >= 0 ? reinterpret_cast<const int *>(&ws.crec[c])[lane] : 0;
+    int raw = c >= 0 ? uni(claim_start(heads, me, vi, nb, nvict)) : 0x7fffffff;
+    while (c >= 0) {
+        const int cn = claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals);
+        const int recn = cn >= 0 ? reinterpret_cast<const int *>(&ws.crec[cn])[lane] : 0;
+        if (cn >= 0) raw = uni(claim_start(heads, me, vi, nb, nvict));
+        // record fields (ChunkRec, one dword per lane), wave-uniform
+        auto fld = [&](int i) { return __builtin_amdgcn_readlane(rec, i); };
+        const int tile = fld(0), t = fld(1), nu = fld(2), rbeg = fld(3), cslot = fld(5), i2 = fld(6);
+        const int nch = fld(30), ubeg = fld(31);
+        const int ps1 = fld(21), ps2 = fld(22), ps3 = fld(23), np = fld(20 + nu);
+        const auto &tb = kconst(a.tab)[t];
+        const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, D12 = d1 * d2, Dp = tb.Dp, P = 16 / d3;
+        if (tile != ctile) {
+            // ---- prefix tile C_u = G1[i1_u] . G2[i2] for the tile's units
+            bool have = false;
+            const bool split = cslot >= 0 && a.sched == kSchedStealL2;
+            if (split && rbeg > 0) {
+                int f = 0;
+                if (lane == 0) f = __hip_atomic_load(&ws.flags[cslot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+                if (uni(f)) {
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    const float4 *src = reinterpret_cast<const float4 *>(ws.ckpt + (size_t)cslot * kCTile);
+                    for (int e = lane; e < 4 * 16 * R / 4; e += 64) {
+                        const int j = e / (4 * R), f2 = e - j * (4 * R), m = f2 / (R / 4), c4 = f2 - m * (R / 4);
+                        *reinterpret_cast<float4 *>(Cw + j * CU + m * CSTR + 4 * c4) = src[e];
+                    }
+                    have = true;
+                }
+                if (have) ++hits;
+                else ++misses;
+            }
+            if (!have) {
+                const int key = (int)(tb.i2_base + (uint32_t)i2);
+                if (key != bkey) {
+                    // a new G2 slice: lane (kq, li) holds G2[i2][kq*KQ + s][col] for
+                    // its columns col = 16*n + li (zero past d2*R)
+                    const float *G2 = a.cores.g[t][1] + (int64_t)i2 * R * d2 * R;
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) {
+                        const int col = n * 16 + li, j2 = col / R, r2 = col - j2 * R;
+                        const bool ok = j2 < d2;
+                        const float *src = G2 + (ok ? j2 : 0) * R + r2;
+#pragma unroll
+                        for (int s2 = 0; s2 < KQ; ++s2) {
+                            const float v = src[(int64_t)(kq * KQ + s2) * d2 * R];
+                            breg[n * KQ + s2] = ok ? v : 0.f;
+                        }
+                    }
+                    bkey = key;
+                }
+                // A operand: lane (kq, li) holds G1[i1_u][j1][kq*KQ ..] of row li = (u, j1)
+                float av[KQ];
+                {
+                    const int g = li >> 2, j1 = li & 3;
+                    const int i1 = __shfl(rec, 8 + (g < nu ? g : 0), 64);
+                    const float *src = a.cores.g[t][0] + ((int64_t)i1 * d1 + (j1 < d1 ? j1 : 0)) * R + kq * KQ;
+                    if constexpr (KQ % 4 == 0) {
+#pragma unroll
+                        for (int s2 = 0; s2 < KQ; s2 += 4) {
+                            const float4 v = *reinterpret_cast<const float4 *>(src + s2);
+                            av[s2] = v.x;
+                            av[s2 + 1] = v.y;
+                            av[s2 + 2] = v.z;
+                            av[s2 + 3] = v.w;
+                        }
+                    } else {
+#pragma unroll
+                        for (int s2 = 0; s2 < KQ; ++s2) av[s2] = src[s2];
+                    }
+                }
+                floatx4 acc[NT];
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < KQ; ++s2)
+#pragma unroll
+                    for (int n = 0; n < NT; ++n)
+                        acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s2], breg[n * KQ + s2], acc[n], 0, 0, 0);
+                // lane (kq, li) holds rows 4*kq + v = (unit kq, j1 = v) of column 16n + li
+                const bool pub = split && rbeg == 0 && (nch > 2 || cn != c + 1);
+                float *ck = ws.ckpt + (size_t)(cslot >= 0 ? cslot : 0) * kCTile;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    const int col = n * 16 + li, j2 = col / R, r2 = col - j2 * R;
+                    if (j2 < d2 && kq < nu) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            if (v < d1) {
+                                const int m = v * d2 + j2;
+                                Cw[kq * CU + m * CSTR + r2] = acc[n][v];
+                                if (pub) ck[(kq * 16 + m) * R + r2] = acc[n][v];
+                            }
+                        }
+                    }
+                }
+                if (pub) {
+                    // publish when another worker may run a later chunk of this tile
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                    if (lane == 0) __hip_atomic_store(&ws.flags[cslot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            ctile = tile;
+            __builtin_amdgcn_wave_barrier();
+        }
+
+        // ---- rows: output tiles e = 0 .. np-1, NQ at a time
+        float *Et = ws.E + kconst(ws.ebase)[t];
+        const float *G3t = ws.g3t + tb.g3t_off;
+        const int slot = li / d3, j3l = li - slot * d3;
+        const int ro0 = fld(25), ro1 = fld(26), ro2 = fld(27), ro3 = fld(28);
+        const int cc0 = fld(16), cc1 = fld(17), cc2 = fld(18), cc3 = fld(19);
+        const int us0 = fld(12), us1 = fld(13), us2 = fld(14), us3 = fld(15);
+        auto sel = [](int j, int x0, int x1, int x2, int x3) { return j == 0 ? x0 : j == 1 ? x1 : j == 2 ? x2 : x3; };
+        // output tile e -> unit j, its first row (chunk numbering) and row count
+        auto piece = [&](int e, int &j, int &rb, int &cnt) {
+            j = (e >= ps1) + (e >= ps2) + (e >= ps3);
+            const int ro = sel(j, ro0, ro1, ro2, ro3);
+            rb = ro + (e - sel(j, 0, ps1, ps2, ps3)) * P;
+            const int rem = ro + sel(j, cc0, cc1, cc2, cc3) - rb;
+            cnt = rem < P ? rem : P;
+        };
+        for (int e0 = 0; e0 < np; e0 += NQ) {
+            float ga[NQ][KQ];
+            // operands of NQ output tiles: each lane's G3 row run (clamped to a
+            // valid row of the tile; results of padding rows are not stored)
+#pragma unroll
+            for (int k = 0; k < NQ; ++k) {
+                const int e = e0 + k < np ? e0 + k : np - 1;
+                int j, rb, cnt;
+                piece(e, j, rb, cnt);
+                const int q = rb + (slot < cnt ? slot : 0);
+                const int i3 = __shfl(rec, 32 + q, 64);
+                const float *src = G3t + ((int64_t)i3 * d3 + j3l) * R + kq * KQ;
+                if constexpr (KQ % 4 == 0) {
+#pragma unroll
+                    for (int s2 = 0; s2 < KQ; s2 += 4) {
+                        const float4 v = *reinterpret_cast<const float4 *>(src + s2);
+                        ga[k][s2] = v.x;
+                        ga[k][s2 + 1] = v.y;
+                        ga[k][s2 + 2] = v.z;
+                        ga[k][s2 + 3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int s2 = 0; s2 < KQ; ++s2) ga[k][s2] = src[s2];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < NQ; ++k) {
+                const int e = e0 + k;
+                if (e >= np) break;
+                int j, rb, cnt;
+                piece(e, j, rb, cnt);
+                const float *cb = Cw + j * CU + (li < D12 ? li : 0) * CSTR + kq * KQ;
+                floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (KQ % 4 == 0) {
+#pragma unroll
+                    for (int s2 = 0; s2 < KQ; s2 += 4) {
+                        const float4 v = *reinterpret_cast<const float4 *>(cb + s2);
+                        o = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[k][s2], v.x, o, 0, 0, 0);
+                        o = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[k][s2 + 1], v.y, o, 0, 0, 0);
+                        o = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[k][s2 + 2], v.z, o, 0, 0, 0);
+                        o = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[k][s2 + 3], v.w, o, 0, 0, 0);
+                    }
+                } else {
+#pragma unroll
+                    for (int s2 = 0; s2 < KQ; ++s2)
+                        o = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[k][s2], cb[s2], o, 0, 0, 0);
+                }
+                // lane (kq, li) holds O[4kq + v][li]: row slot (4kq+v)/d3, column li*d3 + (4kq+v)%d3
+                const int us = sel(j, us0, us1, us2, us3) + (rb - sel(j, ro0, ro1, ro2, ro3));
+                if (li < D12) {
+                    if (d3 == 4 || d3 == 8 || d3 == 16) {
+                        const int r4 = 4 * kq, sl = r4 / d3, jj = r4 - sl * d3;
+                        if (sl < cnt)
+                            *reinterpret_cast<floatx4 *>(Et + (int64_t)(us + sl) * Dp + li * d3 + jj) = o;
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int r = 4 * kq + v, sl = r / d3, jj = r - sl * d3;
+                            if (sl < cnt) Et[(int64_t)(us + sl) * Dp + li * d3 + jj] = o[v];
+                        }
+                    }
+                }
+            }
+        }
+        if constexpr (KEEP) {
+            // C of the tile's units, compact [unit position in the work order][16][R],
+            // written by the tile's first chunk
+            if (rbeg == 0) {
+                float4 *dst = reinterpret_cast<float4 *>(ws.Cg + kconst(ws.cbase)[t] + (int64_t)ubeg * 16 * R);
+                for (int e = lane; e < nu * 4 * R; e += 64) {
+                    const int j = e / (4 * R), f2 = e - j * (4 * R), m = f2 / (R / 4), c4 = f2 - m * (R / 4);
+                    dst[e] = *reinterpret_cast<const float4 *>(Cw + j * CU + m * CSTR + 4 * c4);
+                }
+            }
+        }
+        ++nwork;
+        nrows += fld(4) - rbeg;
+        rec = recn;
+        c = cn;
+    }
+    // scheduling statistics and the block's record
+    if (lane == 0) {
+        atomicAdd(&s_work, nwork);
+        atomicAdd(&s_rows, nrows);
+        atomicAdd(&s_steals, steals);
+        atomicAdd(&s_hits, hits);
+        atomicAdd(&s_misses, misses);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        block_stat_write(ws.bstat + CLS * kStatBlocks, s_t0, s_work, s_rows);
+        if (s_steals) atomicAdd(&ws.ctrl[CTRL_STEALS], s_steals);
+        if (s_hits) atomicAdd(&ws.ctrl[CTRL_CKPT_HIT], s_hits);
+        if (s_misses) atomicAdd(&ws.ctrl[CTRL_CKPT_MISS], s_misses);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tile-pipelined block contraction of the rank classes 32 and 64 (R1 = R2 =
+// R, d1, d2 <= 4, d3 <= 16): one persistent block of four waves walks its
+// chunks (static range, or claimed in the stealing modes), one block barrier
+// per chunk.  In the iteration of chunk c the waves
+//  (1) compute C of chunk c+1's prefix tile when it starts a new tile, wave w
+//      the columns of j2 = w (its quarter of the G2[i2] slice is held in
+//      registers while consecutive tiles keep (table, i2)), into the LDS slot
+//      that chunk c is not reading (two slots, double-buffered);
+//  (2) compute the rows of chunk c from the other slot, output tile e of the
+//      chunk on wave e mod 4, O[(slot, j3)][m2] = sum_r2 G3t[i3][j3][r2] *
+//      C_u[m2][r2] (A = transposed G3 slices, B = C read from LDS along r2;
+//      one float4 store per lane writes four columns of an E row), the next
+//      chunk's operands reloaded into the registers each tile has consumed
+//      before its result is stored;
+//  (3) prefetch the G1 slices of the tile computed in the next iteration.
+// So the matrix cores see C of one tile and the rows of another between two
+// barriers, and every operand arrives an iteration before it is used.
+// FlowTT page section 3.2 (C = A.B once per prefix group, kept on chip,
+// reused by each E = C.D; loads of the next TT slices overlapped with compute,
+// the pages' ping-pong buffering), section 3.4 (persistent blocks, stealing,
+// L2 checkpoints of split prefix tiles).
+template <int R>
+struct FwdT {
+    static constexpr int KQ = R / 4;           // K values each lane feeds per 16x16 output tile
+    static constexpr int NTW = R / 16;         // 16-column tiles of C per wave (one j2 each)
+    static constexpr int BREG = NTW * KQ;      // G2 registers per lane
+    static constexpr int CSTR = R + 4;         // LDS row stride of C (floats)
+    static constexpr int CU = 16 * CSTR + 16;  // floats per unit (+16 rotates banks between units)
+    static constexpr int CT = 4 * CU;          // floats per tile slot
+    static constexpr int OCC = R == 64 ? 2 : 3; // blocks per CU (register-limited, no spills)
+    static constexpr int PQ = R == 64 ? 3 : 2;  // output tiles per wave whose operands are prefetched
+};
+
+// Wave-uniform reads of values held one per lane (a record or a table entry).
+__device__ __forceinline__ int rl(int v, int k) { return __builtin_amdgcn_readlane(v, k); }
+typedef __attribute__((address_space(1))) float gfloat;
+typedef __attribute__((address_space(1))) floatx4 gfloatx4;
+// A global-memory pointer held as two dwords (lanes k, k+1): the address space
+// is stated so that accesses through it are global (vector memory counter
+// only), not flat ones, which the LDS counter also tracks.
+template <class T> __device__ __forceinline__ __attribute__((address_space(1))) T *rl_ptr(int v, int k)
+{
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane(v, k), hi = (uint32_t)__builtin_amdgcn_readlane(v, k + 1);
+    return reinterpret_cast<__attribute__((address_space(1))) T *>(lo | (hi << 32));
+}
+// ChunkRec fields as dword indices
+enum RecField { RF_TILE = 0, RF_T = 1, RF_NU = 2, RF_RBEG = 3, RF_REND = 4, RF_SLOT = 5, RF_I2 = 6, RF_I1 = 8,
+                RF_USTART = 12, RF_CCNT = 16, RF_PSTART = 20, RF_ROWOFF = 25, RF_NCH = 30, RF_UBEG = 31,
+                RF_I3 = 32 };
+static_assert(offsetof(ChunkRec, i1) == 4 * RF_I1 && offsetof(ChunkRec, ustart) == 4 * RF_USTART &&
+                  offsetof(ChunkRec, ccnt) == 4 * RF_CCNT && offsetof(ChunkRec, pstart) == 4 * RF_PSTART &&
+                  offsetof(ChunkRec, rowoff) == 4 * RF_ROWOFF && offsetof(ChunkRec, nch) == 4 * RF_NCH &&
+                  offsetof(ChunkRec, ubeg) == 4 * RF_UBEG && offsetof(ChunkRec, i3) == 4 * RF_I3,
+              "record field indices");
+static_assert(offsetof(FwdTab, g2) == 4 * FT_G2 && offsetof(FwdTab, g3t) == 4 * FT_G3T &&
+                  offsetof(FwdTab, E) == 4 * FT_E && offsetof(FwdTab, Cg) == 4 * FT_CG &&
+                  offsetof(FwdTab, d1) == 4 * FT_D1 && offsetof(FwdTab, i2_base) == 4 * FT_I2BASE &&
+                  offsetof(FwdTab, Dp) == 4 * FT_DP,
+              "table field indices");
+
+// Output tile e of a chunk (record rv, one dword per lane): unit j, first row
+// in chunk numbering rb, rows cnt (P rows per output tile).  Wave-uniform.
+__device__ __forceinline__ void rec_piece(int rv, int P, int e, int &j, int &rb, int &cnt)
+{
+    const int ps1 = rl(rv, RF_PSTART + 1), ps2 = rl(rv, RF_PSTART + 2), ps3 = rl(rv, RF_PSTART + 3);
+    j = (e >= ps1) + (e >= ps2) + (e >= ps3);
+    const int ps = j == 0 ? 0 : j == 1 ? ps1 : j == 2 ? ps2 : ps3;
+    const int ro = __builtin_amdgcn_readlane(rv, RF_ROWOFF + j);
+    rb = ro + (e - ps) * P;
+    const int rem = ro + __builtin_amdgcn_readlane(rv, RF_CCNT + j) - rb;
+    cnt = rem < P ? rem : P;
+}
+
+template <int R, bool KEEP, bool STEAL>
+__global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a, int heads_stride)
+{
+    using L = FwdT<R>;
+    constexpr int CLS = R == 32 ? 2 : 3;
+    constexpr int KQ = L::KQ, NTW = L::NTW, CSTR = L::CSTR, CU = L::CU, PQ = L::PQ;
+    __shared__ __attribute__((aligned(16))) float Cs[2][L::CT];
+    // records of ring entries k .. k+2 (iteration k), entry k+3 being written;
+    // entry k+4's record travels in wave 0's registers for a whole iteration
+    constexpr int NR = 5;
+    __shared__ ChunkRec rr[NR];
+    __shared__ int cid[NR], s_ck[NR];
+    __shared__ long long s_t0;
+    const int lane = threadIdx.x & 63, w = uni(threadIdx.x >> 6), li = lane & 15, kq = lane >> 4;
+    if (threadIdx.x == 0) s_t0 = wall_clock64();
+    const Ws &ws = a.ws;
+    const FwdTab *ftab = ws.ftab;
+    const int nb = gridDim.x, me = blockIdx.x;
+    const int base = ws.ctrl[CTRL_CLS_START + CLS];
+    const int64_t C = ws.ctrl[CTRL_CLS_START + CLS + 1] - base;
+    const int cend = base + range_begin(me + 1, C, nb); // end of the static range
+    int32_t *heads = ws.heads + CLS * heads_stride * kHeadPad;
+    const int nvict = STEAL ? nb >> 3 : 1;
+    int vi = 0, steals = 0, hits = 0, misses = 0, nwork = 0, nrows = 0, raw = 0x7fffffff;
+    int cstat = base + range_begin(me, C, nb); // next chunk of the static range
+    const bool l2 = a.sched == kSchedStealL2;
+
+    // next chunk id of this block (wave 0): its static range in order, then
+    // (stealing modes) chunks claimed from the other blocks of its XCD
+    auto next_id = [&]() -> int {
+        if constexpr (!STEAL) {
+            return cstat < cend ? cstat++ : -1;
+        } else {
+            const int got = claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals);
+            raw = got >= 0 ? uni(claim_start(heads, me, vi, nb, nvict)) : 0x7fffffff;
+            return got;
+        }
+    };
+    // checkpoint flag of ring entry i, read (thread 0) an iteration before its C is needed
+    auto read_ck = [&](int i, int prev_tile) {
+        int ok = 0;
+        const ChunkRec &r = rr[i];
+        if (l2 && cid[i] >= 0 && r.slot >= 0 && r.rbeg > 0 && r.tile != prev_tile)
+            ok = __hip_atomic_load(&ws.flags[r.slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+        s_ck[i] = ok;
+    };
+    int pre = 0, pre_id = -1; // wave 0: the record of the next ring entry to write, and its chunk
+    if (w == 0) {
+        if constexpr (STEAL) raw = uni(claim_start(heads, me, vi, nb, nvict));
+        int prev = 0;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int id = prev >= 0 ? next_id() : -1;
+            prev = id;
+            if (id >= 0) reinterpret_cast<int *>(&rr[i])[lane] = reinterpret_cast<const int *>(&ws.crec[id])[lane];
+            if (lane == 0) cid[i] = id;
+        }
+        pre_id = prev >= 0 ? next_id() : -1;
+        if (pre_id >= 0) pre = reinterpret_cast<const int *>(&ws.crec[pre_id])[lane];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        read_ck(0, -1);
+        read_ck(1, rr[0].tile);
+    }
+    __syncthreads();
+
+    float breg[L::BREG];
+#pragma unroll
+    for (int i = 0; i < L::BREG; ++i) breg[i] = 0.f;
+    int bkey = -1;
+    float anext[KQ], g3p[PQ][KQ];
+
+    // table records, one dword per lane; reloaded only when the table changes
+    auto tab_load = [&](int t) { return reinterpret_cast<const int *>(ftab + t)[lane & 15]; };
+    // G1 slices of record rv's units: lane (kq, li) holds row li = (unit, j1), K run kq*KQ ..
+    auto load_a = [&](int rv, int tv, float (&av)[KQ]) __attribute__((always_inline)) {
+        const int nu = rl(rv, RF_NU), d1 = rl(tv, FT_D1), g = li >> 2, j1 = li & 3;
+        const int i1 = __shfl(rv, RF_I1 + (g < nu ? g : 0), 64);
+        const gfloatx4 *src = reinterpret_cast<const gfloatx4 *>(rl_ptr<const float>(tv, FT_G1) +
+                                                                 ((int64_t)i1 * d1 + (j1 < d1 ? j1 : 0)) * R + kq * KQ);
+#pragma unroll
+        for (int s4 = 0; s4 < KQ / 4; ++s4) {
+            const floatx4 v = src[s4];
+            av[4 * s4] = v[0];
+            av[4 * s4 + 1] = v[1];
+            av[4 * s4 + 2] = v[2];
+            av[4 * s4 + 3] = v[3];
+        }
+    };
+    // A operand of output tile e of record rv: the lane's G3t run of its row
+    // (clamped to the tile's first row for padding lanes; their results are not stored)
+    auto load_g3 = [&](int rv, int tv, int e, float (&gv)[KQ]) __attribute__((always_inline)) {
+        const int d3 = rl(tv, FT_D3), P = 16 / d3;
+        int j, rb, cnt;
+        rec_piece(rv, P, e, j, rb, cnt);
+        const int slot = li / d3, j3 = li - slot * d3;
+        const int i3 = __shfl(rv, RF_I3 + rb + (slot < cnt ? slot : 0), 64);
+        const gfloatx4 *src = reinterpret_cast<const gfloatx4 *>(rl_ptr<const float>(tv, FT_G3T) +
+                                                                 ((int64_t)i3 * d3 + j3) * R + kq * KQ);
+#pragma unroll
+        for (int s4 = 0; s4 < KQ / 4; ++s4) {
+            const floatx4 v = src[s4];
+            gv[4 * s4] = v[0];
+            gv[4 * s4 + 1] = v[1];
+            gv[4 * s4 + 2] = v[2];
+            gv[4 * s4 + 3] = v[3];
+        }
+    };
+    // (1): C of record rv's tile into slot Ct, wave w the columns of j2 = w
+    auto compute_c = [&](int rv, int tv, const float (&av)[KQ], float *Ct) __attribute__((always_inline)) {
+        const int nu = rl(rv, RF_NU), i2 = rl(rv, RF_I2), d1 = rl(tv, FT_D1), d2 = rl(tv, FT_D2);
+        if (w >= d2) return; // no columns of this j2
+        const int key = rl(tv, FT_I2BASE) + i2;
+        if (key != bkey) {
+            // lane (kq, li) holds G2[i2][kq*KQ + s][w][16*j + li]
+            const gfloat *G2 = rl_ptr<const float>(tv, FT_G2) + ((int64_t)i2 * R * d2 + w) * R + li;
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                for (int s2 = 0; s2 < KQ; ++s2) breg[j * KQ + s2] = G2[(int64_t)(kq * KQ + s2) * d2 * R + 16 * j];
+            bkey = key;
+            // wait here (rare: a new (table, i2) run), not at every tile's first MFMA
+            __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0)
+        }
+        floatx4 acc[NTW];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < KQ; ++s2)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s2], breg[j * KQ + s2], acc[j], 0, 0, 0);
+        // lane (kq, li) holds C[(unit kq, j1 = v)][j2 = w][r2 = 16j + li]
+        if (kq < nu) {
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (v < d1) Ct[kq * CU + (v * d2 + w) * CSTR + 16 * j + li] = acc[j][v];
+        }
+    };
+    // (2): output tile e of record rv from slot Ct with operands gv; when
+    // reload, gv then takes the operands of output tile en of record rn
+    // before the E row is stored
+    auto rows_tile = [&](int rv, int tv, int e, float (&gv)[KQ], const float *Ct, bool reload, int rn, int tvn,
+                         int en) __attribute__((always_inline)) {
+        const int d1 = rl(tv, FT_D1), d2 = rl(tv, FT_D2), d3 = rl(tv, FT_D3), D12 = d1 * d2, Dp = rl(tv, FT_DP);
+        const int P = 16 / d3;
+        int j, rb, cnt;
+        rec_piece(rv, P, e, j, rb, cnt);
+        const float4 *cb = reinterpret_cast<const float4 *>(Ct + j * CU + (li < D12 ? li : 0) * CSTR + kq * KQ);
+        floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s4 = 0; s4 < KQ / 4; ++s4) {
+            const float4 v = cb[s4];
+            o = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[4 * s4], v.x, o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[4 * s4 + 1], v.y, o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[4 * s4 + 2], v.z, o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[4 * s4 + 3], v.w, o, 0, 0, 0);
+        }
+        // keep the reload after this tile's products and before its store:
+        // the products wait only for operands that arrived an iteration ago
+        __builtin_amdgcn_sched_barrier(0);
+        if (reload) load_g3(rn, tvn, en, gv);
+        __builtin_amdgcn_sched_barrier(0);
+        const int us = __builtin_amdgcn_readlane(rv, RF_USTART + j) + (rb - __builtin_amdgcn_readlane(rv, RF_ROWOFF + j));
+        gfloat *Et = rl_ptr<float>(tv, FT_E);
+        if (li < D12) {
+            if (d3 == 4 || d3 == 8 || d3 == 16) {
+                const int r4 = 4 * kq, sl = r4 / d3, jj = r4 - sl * d3;
+                if (sl < cnt) *reinterpret_cast<gfloatx4 *>(Et + (int64_t)(us + sl) * Dp + li * d3 + jj) = o;
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int rr4 = 4 * kq + v, sl = rr4 / d3, jj = rr4 - sl * d3;
+                    if (sl < cnt) Et[(int64_t)(us + sl) * Dp + li * d3 + jj] = o[v];
+                }
+            }
+        }
+    };
+    // C of a tile from a published checkpoint ([unit][16][R] compact) into a slot
+    auto ck_copy = [&](int cslot, float *Ct) __attribute__((always_inline)) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const float4 *src = reinterpret_cast<const float4 *>(ws.ckpt + (size_t)cslot * kCTile);
+        for (int e = threadIdx.x; e < 16 * R; e += kThreads) {
+            const int j = e / (4 * R), f = e - j * (4 * R), m = f / (R / 4), c4 = f - m * (R / 4);
+            *reinterpret_cast<float4 *>(Ct + j * CU + m * CSTR + 4 * c4) = src[e];
+        }
+    };
+
+    int cs = 0;
+    // records of the current chunk and the next, one dword per lane, with their
+    // tables' records (carried from one iteration to the next)
+    int recv = reinterpret_cast<const int *>(&rr[0])[lane], nrecv = reinterpret_cast<const int *>(&rr[1])[lane];
+    const int c0 = uni(cid[0]), c1 = uni(cid[1]);
+    int tv = 0, tvn = 0;
+    if (c0 >= 0) {
+        tv = tab_load(rl(recv, RF_T));
+        tvn = c1 >= 0 ? tab_load(rl(nrecv, RF_T)) : tv;
+        // prologue: C of the first chunk's tile, the next tile's G1 slices and
+        // the first chunk's row operands
+        if (uni(s_ck[0])) {
+            ck_copy(rl(recv, RF_SLOT), Cs[0]);
+            ++hits;
+        } else {
+            if (l2 && rl(recv, RF_SLOT) >= 0 && rl(recv, RF_RBEG) > 0) ++misses;
+            float a0[KQ];
+            load_a(recv, tv, a0);
+            compute_c(recv, tv, a0, Cs[0]);
+        }
+        if (c1 >= 0 && rl(nrecv, RF_TILE) != rl(recv, RF_TILE)) load_a(nrecv, tvn, anext);
+        const int np0 = __builtin_amdgcn_readlane(recv, RF_PSTART + rl(recv, RF_NU));
+#pragma unroll
+        for (int jq = 0; jq < PQ; ++jq) {
+            const int e = w + 4 * jq < np0 ? w + 4 * jq : np0 - 1;
+            load_g3(recv, tv, e, g3p[jq]);
+        }
+    }
+    __syncthreads();
+    int pub_slot = -1; // checkpoint whose flag this block sets after the next barrier
+    int i = 0; // ring slot of entry k
+    for (int k = 0;; ++k) {
+        const int i1 = i == NR - 1 ? 0 : i + 1, i2r = i1 == NR - 1 ? 0 : i1 + 1, i3r = i2r == NR - 1 ? 0 : i2r + 1;
+        const int c = uni(cid[i]);
+        if (c < 0) break;
+        if (threadIdx.x == 0 && pub_slot >= 0)
+            __hip_atomic_store(&ws.flags[pub_slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        pub_slot = -1;
+        const int cn = uni(cid[i1]), c2 = uni(cid[i2r]);
+        const int r2v = reinterpret_cast<const int *>(&rr[i2r])[lane];
+        const int tile = rl(recv, RF_TILE), ntile = rl(nrecv, RF_TILE);
+        const bool has_next = cn >= 0, next_new = has_next && ntile != tile;
+        const int ck_next = uni(s_ck[i1]);
+        // wave 0: ring entry k+3 (its record loaded an iteration ago) goes to the
+        // slot of entry k-2; the record of entry k+4 is loaded now
+        if (w == 0) {
+            if (pre_id >= 0) reinterpret_cast<int *>(&rr[i3r])[lane] = pre;
+            if (lane == 0) cid[i3r] = pre_id;
+            pre_id = pre_id >= 0 ? next_id() : -1;
+            if (pre_id >= 0) pre = reinterpret_cast<const int *>(&ws.crec[pre_id])[lane];
+        }
+        // table record of entry k+2 (the same table as entry k+1 nearly always)
+        int tv2 = tvn;
+        if (c2 >= 0 && rl(r2v, RF_T) != rl(nrecv, RF_T)) tv2 = tab_load(rl(r2v, RF_T));
+        // (1) C of the next chunk's tile
+        if (next_new) {
+            if (ck_next) {
+                ck_copy(rl(nrecv, RF_SLOT), Cs[cs ^ 1]);
+                ++hits;
+            } else {
+                if (l2 && rl(nrecv, RF_SLOT) >= 0 && rl(nrecv, RF_RBEG) > 0) ++misses;
+                compute_c(nrecv, tvn, anext, Cs[cs ^ 1]);
+            }
+        }
+        // (3) G1 slices of the tile computed in the next iteration
+        if (c2 >= 0 && rl(r2v, RF_TILE) != ntile) load_a(r2v, tv2, anext);
+        // (2) rows of chunk c: output tiles w, w+4, ... of the chunk
+        {
+            const int np = __builtin_amdgcn_readlane(recv, RF_PSTART + rl(recv, RF_NU));
+            const int npn = has_next ? __builtin_amdgcn_readlane(nrecv, RF_PSTART + rl(nrecv, RF_NU)) : 0;
+            const float *Ct = Cs[cs];
+#pragma unroll
+            for (int jq = 0; jq < PQ; ++jq) {
+                const int e = w + 4 * jq;
+                const int en = e < npn ? e : (npn > 0 ? npn - 1 : 0);
+                if (e < np) rows_tile(recv, tv, e, g3p[jq], Ct, has_next, nrecv, tvn, en);
+                else if (has_next) load_g3(nrecv, tvn, en, g3p[jq]);
+            }
+            // tiles past the prefetched ones (chunks of more than 4 * PQ output tiles)
+            for (int e = w + 4 * PQ; e < np; e += 4) {
+                float gv[KQ];
+                load_g3(recv, tv, e, gv);
+                rows_tile(recv, tv, e, gv, Ct, false, recv, tv, 0);
+            }
+        }
+        const int rbeg = rl(recv, RF_RBEG), nu = rl(recv, RF_NU);
+        // the tile's first chunk publishes its C when a later chunk of the tile
+        // may run on another block (the next chunk here is not its continuation)
+        const int cslot = rl(recv, RF_SLOT);
+        if (l2 && cslot >= 0 && rbeg == 0 && (rl(recv, RF_NCH) > 2 || cn != c + 1)) {
+            float4 *dst = reinterpret_cast<float4 *>(ws.ckpt + (size_t)cslot * kCTile);
+            for (int e = threadIdx.x; e < 16 * R; e += kThreads) {
+                const int j = e / (4 * R), f = e - j * (4 * R), m = f / (R / 4), c4 = f - m * (R / 4);
+                dst[e] = *reinterpret_cast<const float4 *>(Cs[cs] + j * CU + m * CSTR + 4 * c4);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            pub_slot = cslot;
+        }
+        if constexpr (KEEP) {
+            if (rbeg == 0) {
+                gfloatx4 *dst = reinterpret_cast<gfloatx4 *>(rl_ptr<float>(tv, FT_CG) + (int64_t)rl(recv, RF_UBEG) * 16 * R);
+                for (int e = threadIdx.x; e < nu * 4 * R; e += kThreads) {
+                    const int j = e / (4 * R), f = e - j * (4 * R), m = f / (R / 4), c4 = f - m * (R / 4);
+                    dst[e] = *reinterpret_cast<const floatx4 *>(Cs[cs] + j * CU + m * CSTR + 4 * c4);
+                }
+            }
+        }
+        if (threadIdx.x == 0) {
+            ++nwork;
+            nrows += rl(recv, RF_REND) - rbeg;
+            // checkpoint flag of entry k+2, whose tile the next iteration computes
+            read_ck(i2r, ntile);
+        }
+        __syncthreads(); // entry k done, entry k+3 written, C of the next tile complete
+        if (next_new) cs ^= 1;
+        i = i1;
+        recv = nrecv;
+        nrecv = r2v;
+        tv = tvn;
+        tvn = tv2;
+    }
+    if (threadIdx.x == 0 && pub_slot >= 0)
+        __hip_atomic_store(&ws.flags[pub_slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+        block_stat_write(ws.bstat + CLS * kStatBlocks, s_t0, nwork, nrows);
+        if (steals) atomicAdd(&ws.ctrl[CTRL_STEALS], steals);
+    }
+    // hits and misses are counted by every wave alike; wave 0 reports them
+    if (lane == 0 && w == 0) {
+        if (hits) atomicAdd(&ws.ctrl[CTRL_CKPT_HIT], hits);
+        if (misses) atomicAdd(&ws.ctrl[CTRL_CKPT_MISS], misses);
+    }
+}
+
 // Plain fp32 contraction for any shape within the create-time limits: one
 // block per unit, the prefix intermediate in LDS, then every unique row.
 __global__ __launch_bounds__(kThreads) void k_contract_generic(FwdArgs a, int force)
@@ -686,86 +1377,131 @@ __global__ __launch_bounds__(kThreads) void k_contract_generic(FwdArgs a, int fo
     }
 }
 
-// Bag-major sum pooling: one wave per bag; lanes split the columns in float4
-// and the lookups in 64/lanes-per-row interleaved streams, combined in a fixed
-// xor-tree order.  Empty bags write zeros.
-__global__ __launch_bounds__(kThreads) void k_pool(const TableDesc *tab, int T, int64_t B,
-                                                   const int64_t *offsets, int64_t nnz, Ws ws,
-                                                   float *out, int SD, int skip_mfma)
+// Bag-major sum pooling of the tables of one lane class (LPR lanes per row,
+// one float4 column -- or one float when VEC is false -- per lane; the class
+// of a table is its TableDesc::gcls).  A wave pools G = 64 / LPR consecutive
+// bags of one table at once, lane group g the bag bag0 + g: one load of the
+// G + 1 offsets, then per step of LPR lookups one load of their unique-row
+// ids and the LPR row loads of every group issued back to back, so a bag's
+// rows are in flight together instead of one short batch after another.
+// Each lane adds its bag's rows in lookup order (a fixed order, no atomics:
+// the output is bit-reproducible); empty bags write zeros.
+template <int LPR, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_pool(const TableDesc *tab, int64_t B, const int64_t *offsets,
+                                                   int64_t nnz, Ws ws, float *out, int SD, int gcls,
+                                                   int skip_mfma)
 {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t bag = (int64_t)blockIdx.x * (kThreads / 64) + w;
-    if (bag >= (int64_t)T * B) return;
-    const int t = (int)(bag / B);
-    const int64_t b = bag - (int64_t)t * B;
-    const TableDesc &tb = tab[t];
-    if (skip_mfma && tb.cls >= 0) return; // pooled inside the contraction
-    int64_t lo = offsets[bag], hi = offsets[bag + 1];
-    lo = lo < 0 ? 0 : (lo > nnz ? nnz : lo);
-    hi = hi < lo ? lo : (hi > nnz ? nnz : hi);
-    const int u0 = ws.tab_uniq_start[t], u1 = ws.tab_uniq_start[t + 1];
-    if (u1 <= u0) hi = lo;
-    const float *Et = ws.E + ws.ebase[t];
-    float *o = out + b * SD + tb.col_off;
-    const int D = tb.D;
-    if (D <= 256) {
-        // lanes per row: smallest power of two >= D/4 (float4 columns)
-        const int c4n = (D + 3) >> 2;
-        int lpr = 1;
-        while (lpr < c4n) lpr <<= 1;
-        const int rf = 64 / lpr;
-        const int c4 = lane & (lpr - 1), r = lane / lpr;
-        const int cc = c4 < c4n ? c4 : 0;
+    constexpr int G = 64 / LPR;
+    constexpr int UNR = LPR < 16 ? LPR : 16; // row loads in flight per lane
+    const int t = blockIdx.y;
+    const auto &tb = kconst(tab)[t];
+    if (tb.gcls != gcls || (skip_mfma && tb.cls >= 0)) return; // pooled inside the contraction
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane / LPR, gl = lane - grp * LPR;
+    const int64_t bag0 = ((int64_t)blockIdx.x * (kThreads / 64) + w) * G;
+    if (bag0 >= B) return;
+    // the lane group's bag and its lookup range (clamped into [0, nnz])
+    const bool live = bag0 + grp < B;
+    const int64_t bag = (int64_t)t * B + (live ? bag0 + grp : B - 1);
+    int64_t olo = offsets[bag], ohi = offsets[bag + 1];
+    olo = olo < 0 ? 0 : (olo > nnz ? nnz : olo);
+    ohi = ohi < 0 ? 0 : (ohi > nnz ? nnz : ohi);
+    const int lo = (int)olo;
+    int hi = (int)ohi;
+    const int u0 = kconst(ws.tab_uniq_start)[t], u1 = kconst(ws.tab_uniq_start)[t + 1];
+    if (!live || hi < lo || u1 <= u0) hi = lo;
+    const int len = hi - lo;
+    int maxlen = len;
+#pragma unroll
+    for (int m = LPR; m < 64; m <<= 1) {
+        const int y = __shfl_xor(maxlen, m, 64);
+        maxlen = y > maxlen ? y : maxlen;
+    }
+    maxlen = __builtin_amdgcn_readfirstlane(maxlen);
+    const float *Et = ws.E + kconst(ws.ebase)[t];
+    const int D = tb.D, Dp = tb.Dp, col_off = tb.col_off;
+    float *o_row = out + (int64_t)(bag0 + (live ? grp : 0)) * SD + col_off;
+    const int cn = VEC ? (D + 3) >> 2 : D;
+    for (int cb = 0; cb < cn; cb += LPR) {
+        const int c = cb + gl;
+        const bool okc = c < cn;
+        const int cc = okc ? c : 0;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        // 64 lookups at a time: one coalesced load of their unique rows, then
-        // the E rows in flight together (rf rows per instruction, 4 deep)
-        for (int64_t l0 = lo; l0 < hi; l0 += 64) {
-            const int n = hi - l0 < 64 ? (int)(hi - l0) : 64;
-            int uu = ws.inv[l0 + (lane < n ? lane : 0)];
+        for (int k0 = 0; k0 < maxlen; k0 += LPR) {
+            // unique-row ids of lookups k0 .. k0 + LPR - 1 of this lane's bag
+            int uu = k0 + gl < len ? ws.inv[lo + k0 + gl] : u0;
             uu = uu < u0 ? u0 : (uu >= u1 ? u1 - 1 : uu);
-            const int nk = (n + rf - 1) / rf; // row steps, uniform over the wave
-            for (int k0 = 0; k0 < nk; k0 += 4) {
-                float4 v[4];
+            const int nk = maxlen - k0 < LPR ? maxlen - k0 : LPR;
+            for (int kb = 0; kb < nk; kb += UNR) {
+                float4 v[UNR];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int i = r + (k0 + kk) * rf;
-                    const int u = __shfl(uu, i < n ? i : 0, 64);
-                    v[kk] = *reinterpret_cast<const float4 *>(Et + (int64_t)u * tb.Dp + 4 * cc);
-                    if (!(i < n && k0 + kk < nk && c4 < c4n)) v[kk] = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int k = 0; k < UNR; ++k) {
+                    const int u = __shfl(uu, grp * LPR + ((kb + k) & (LPR - 1)), 64);
+                    const float *src = Et + (int64_t)u * Dp;
+                    if (VEC) v[k] = *reinterpret_cast<const float4 *>(src + 4 * cc);
+                    else v[k] = make_float4(src[cc], 0.f, 0.f, 0.f);
                 }
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    acc.x += v[kk].x;
-                    acc.y += v[kk].y;
-                    acc.z += v[kk].z;
-                    acc.w += v[kk].w;
+                for (int k = 0; k < UNR; ++k) {
+                    if (k0 + kb + k < len) {
+                        acc.x += v[k].x;
+                        if (VEC) {
+                            acc.y += v[k].y;
+                            acc.z += v[k].z;
+                            acc.w += v[k].w;
+                        }
+                    }
                 }
             }
         }
-        for (int m = lpr; m < 64; m <<= 1) {
-            acc.x += __shfl_xor(acc.x, m, 64);
-            acc.y += __shfl_xor(acc.y, m, 64);
-            acc.z += __shfl_xor(acc.z, m, 64);
-            acc.w += __shfl_xor(acc.w, m, 64);
-        }
-        if (r == 0 && c4 < c4n) {
-            const int j = 4 * c4;
-            if (j + 0 < D) o[j + 0] = acc.x;
-            if (j + 1 < D) o[j + 1] = acc.y;
-            if (j + 2 < D) o[j + 2] = acc.z;
-            if (j + 3 < D) o[j + 3] = acc.w;
-        }
-    } else {
-        for (int j = lane; j < D; j += 64) {
-            float acc = 0.f;
-            for (int64_t l = lo; l < hi; ++l) {
-                int u = ws.inv[l];
-                u = u < u0 ? u0 : (u >= u1 ? u1 - 1 : u);
-                acc += Et[(int64_t)u * tb.Dp + j];
+        if (live && okc) {
+            if (VEC) {
+                const int j = 4 * c;
+                if (j + 3 < D) {
+                    *reinterpret_cast<float4 *>(o_row + j) = acc;
+                } else {
+                    if (j + 0 < D) o_row[j + 0] = acc.x;
+                    if (j + 1 < D) o_row[j + 1] = acc.y;
+                    if (j + 2 < D) o_row[j + 2] = acc.z;
+                }
+            } else {
+                o_row[c] = acc.x;
             }
-            o[j] = acc;
         }
     }
+}
+
+// One pooling launch per lane class present among the tables.
+static hipError_t launch_pool_classes(const Plan &p, const int64_t *offsets, float *out, int skip_mfma,
+                                      hipStream_t s)
+{
+    if (p.B <= 0) return hipSuccess;
+    for (int c = 0; c < 16; ++c) {
+        if (!(p.gcls_mask & (1 << c))) continue;
+        const int lpr = 1 << (c & 7), G = 64 / lpr;
+        const int64_t gx = (p.B + (int64_t)G * (kThreads / 64) - 1) / ((int64_t)G * (kThreads / 64));
+        const dim3 grid((unsigned)gx, (unsigned)p.T), block(kThreads);
+#define TT_POOL(L, V) hipLaunchKernelGGL((k_pool<L, V>), grid, block, 0, s, p.dtab, p.B, offsets, p.nnz, p.ws, out, \
+                                         p.sumD, c, skip_mfma)
+        switch (c) {
+        case 0: TT_POOL(1, false); break;
+        case 1: TT_POOL(2, false); break;
+        case 2: TT_POOL(4, false); break;
+        case 3: TT_POOL(8, false); break;
+        case 4: TT_POOL(16, false); break;
+        case 5: TT_POOL(32, false); break;
+        case 6: TT_POOL(64, false); break;
+        case 8: TT_POOL(1, true); break;
+        case 9: TT_POOL(2, true); break;
+        case 10: TT_POOL(4, true); break;
+        case 11: TT_POOL(8, true); break;
+        case 12: TT_POOL(16, true); break;
+        case 13: TT_POOL(32, true); break;
+        case 14: TT_POOL(64, true); break;
+        default: return hipErrorInvalidValue;
+        }
+#undef TT_POOL
+    }
+    return hipGetLastError();
 }
 
 // Fused pooling: the remaining lookups of hot rows (those past a row's first
@@ -802,13 +1538,7 @@ __global__ __launch_bounds__(kThreads) void k_pool_tail(FwdArgs a, int64_t nnz)
 
 hipError_t launch_pool(const Plan &p, const int64_t *offsets, float *out, hipStream_t s)
 {
-    const int64_t nbags = (int64_t)p.T * p.B;
-    if (nbags > 0) {
-        const int64_t g = (nbags + 3) / 4;
-        hipLaunchKernelGGL(k_pool, dim3((unsigned)g), dim3(kThreads), 0, s, p.dtab, p.T, p.B, offsets, p.nnz,
-                           p.ws, out, p.sumD, 0);
-    }
-    return hipGetLastError();
+    return launch_pool_classes(p, offsets, out, 0, s);
 }
 
 hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *offsets, float *out,
@@ -826,8 +1556,13 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
         if ((e = launch_lookup_meta(p, offsets, s)) != hipSuccess) return e;
     }
     if (p.nnz > 0) {
+        // workers of each class's persistent launch: waves of the per-wave
+        // kernel (ranks <= 32, deterministic pooling), blocks otherwise
+        // (ranks 8, 16 and 32: waves of the per-wave kernel; rank 64: blocks of
+        // the tile-pipelined kernel; fused pooling: blocks of k_contract)
         ClassGrid cg;
-        for (int c = 0; c < 4; ++c) cg.nb[c] = p.num_blocks * kClsOcc[c];
+        const int wpc[4] = {fwd_workers_per_cu<8>(), fwd_workers_per_cu<16>(), fwd_workers_per_cu<32>(), FwdT<64>::OCC};
+        for (int c = 0; c < 4; ++c) cg.nb[c] = p.num_blocks * (!fused ? wpc[c] : kClsOcc[c]);
         const int hs = p.num_blocks * kMaxClsOcc;
         if (p.force_generic) hipLaunchKernelGGL(k_queue_init, dim3(1), dim3(kThreads), 0, s, a, cg, hs, 0);
         else hipLaunchKernelGGL(k_queue_init, dim3(64, p.T), dim3(kThreads), 0, s, a, cg, hs, 1);
@@ -847,16 +1582,19 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
                     case 2: TT_FWD_CLASS(32, false, true); break;
                     default: TT_FWD_CLASS(64, false, true); break;
                     }
-                } else if (p.keep_c && c >= kKeepMinCls) {
-                    if (c == 2) TT_FWD_CLASS(32, true, false);
-                    else TT_FWD_CLASS(64, true, false);
+                } else if (c < 3) {
+#define TT_FWD_WAVE(RR, KK) hipLaunchKernelGGL((k_contract_w<RR, KK>), dim3(p.num_blocks * FwdW<RR>::OCC), block, 0, s, ac, hs)
+                    if (c == 0) TT_FWD_WAVE(8, false);
+                    else if (c == 1) TT_FWD_WAVE(16, false);
+                    else if (p.keep_c) TT_FWD_WAVE(32, true);
+                    else TT_FWD_WAVE(32, false);
+#undef TT_FWD_WAVE
                 } else {
-                    switch (c) {
-                    case 0: TT_FWD_CLASS(8, false, false); break;
-                    case 1: TT_FWD_CLASS(16, false, false); break;
-                    case 2: TT_FWD_CLASS(32, false, false); break;
-                    default: TT_FWD_CLASS(64, false, false); break;
-                    }
+                    const bool keep = p.keep_c != 0, steal = ac.sched != kSchedStatic;
+#define TT_FWD_TILE(RR, KK, SS) hipLaunchKernelGGL((k_contract_t<RR, KK, SS>), dim3(p.num_blocks * FwdT<RR>::OCC), block, 0, s, ac, hs)
+                    if (keep) { if (steal) TT_FWD_TILE(64, true, true); else TT_FWD_TILE(64, true, false); }
+                    else { if (steal) TT_FWD_TILE(64, false, true); else TT_FWD_TILE(64, false, false); }
+#undef TT_FWD_TILE
                 }
 #undef TT_FWD_CLASS
                 timer_end(p.timing, TM_FWD_CLS0 + c, s);
@@ -875,9 +1613,8 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
     timer_begin(p.timing, TM_POOL, s);
     if (nbags > 0 && (!fused || p.any_generic)) {
         // with fused pooling only the tables of the generic kernels are left
-        const int64_t g = (nbags + 3) / 4;
-        hipLaunchKernelGGL(k_pool, dim3((unsigned)g), dim3(kThreads), 0, s, p.dtab, p.T, p.B, offsets,
-                           p.nnz, p.ws, out, p.sumD, fused ? 1 : 0);
+        hipError_t e = launch_pool_classes(p, offsets, out, fused ? 1 : 0, s);
+        if (e != hipSuccess) return e;
     }
     timer_end(p.timing, TM_POOL, s);
     return hipGetLastError();

@@ -483,7 +483,7 @@ struct ChunkOp {
         const uint32_t lo = (uint32_t)(excl & 0xffffffffu), hi = (uint32_t)(excl >> 32);
         ws.tile_rows[tile] = r;
         ws.tile_cstart[tile] = (int32_t)lo;
-        ws.tile_slot[tile] = (nch > 1 && hi < (uint32_t)kMaxCkptSlots) ? (int32_t)hi : -1;
+        ws.tile_slot[tile] = (nch > 1 && hi < (uint32_t)ws.ckpt_slots) ? (int32_t)hi : -1;
         for (uint32_t c = 0; c < nch; ++c) {
             if ((int64_t)lo + c >= ws.chunk_cap) break; // reported by total()
             ws.chunk_tile[lo + c] = (int32_t)tile;
@@ -556,6 +556,19 @@ __global__ __launch_bounds__(kThreads) void k_chunk_records(const TableDesc *tab
         rec.rowoff[4] = coff;
         for (int r = coff; r < kMaxChunkRows; ++r) rec.i3[r] = 0;
         ws.crec[c] = rec;
+        // first chunk of each rank class (chunks are class-major; generic
+        // tables rank 4, after the MFMA classes), found where the rank steps
+        // up between neighbouring chunks; entry 5 is the chunk count
+        const int rank = tb.cls < 0 ? 4 : tb.cls;
+        int prev = __shfl_up(rank, 1, 64);
+        if ((threadIdx.x & 63) == 0 && c > 0) {
+            const int pt = segment_of(ws.tab_unit_start, T, ws.uorder[ws.tile_ubeg[ws.chunk_tile[c - 1]]]);
+            prev = tab[pt].cls < 0 ? 4 : tab[pt].cls;
+        }
+        if (c == 0) prev = -1;
+        for (int r = prev + 1; r <= rank; ++r) ws.ctrl[CTRL_CLS_START + r] = (int32_t)c;
+        if (c == C - 1)
+            for (int r = rank + 1; r <= 5; ++r) ws.ctrl[CTRL_CLS_START + r] = (int32_t)C;
     }
 }
 

@@ -73,6 +73,7 @@ struct TableDesc {
 };
 
 constexpr int kMaxChunkRows = 32; // rows per forward work chunk (upper limit)
+constexpr int kMaxWorkersPerCu = 32; // persistent workers (blocks or waves) per CU of one forward class
 constexpr int kSinkFloats = 8 * 4 * 256; // 8 float4 stores per thread of a 256-thread block
 // Prefix intermediates are kept from forward to backward for the rank classes
 // from this one up (ranks >= 32).  Measured: at rank 16 the forward's extra C
@@ -93,6 +94,20 @@ struct ChunkRec {
     int32_t i3[kMaxChunkRows]; // third digit of every row of the chunk
 };
 static_assert(sizeof(ChunkRec) == 256, "chunk record is one 256-byte line");
+
+// What the forward class kernels need of a table, 16 dwords, rebuilt by every
+// forward: a wave loads it with one dword per lane and reads fields with
+// readlane, so no scalar memory load sits in the chunk loops.
+struct FwdTab {
+    const float *g1, *g2; // cores 0 and 1
+    const float *g3t;     // transposed core 2, [n3][d3][R2]
+    float *E;             // unique-row buffer of the table, indexed by unique id (ebase applied)
+    float *Cg;            // kept prefix intermediates, indexed by work position (cbase applied)
+    int32_t d1, d2, d3, i2_base, Dp, pad;
+};
+static_assert(sizeof(FwdTab) == 64, "table record is 16 dwords");
+enum FwdTabField { FT_G1 = 0, FT_G2 = 2, FT_G3T = 4, FT_E = 6, FT_CG = 8, FT_D1 = 10, FT_D2 = 11, FT_D3 = 12,
+                   FT_I2BASE = 13, FT_DP = 14 };
 
 // Per-block record of the persistent matrix-core kernels (scheduling
 // evidence: how the work of one launch spread over blocks and compute units).
@@ -157,12 +172,14 @@ struct Ws {
     int64_t chunk_cap;       // capacity of the chunk arrays
     float *g3t;              // transposed G3 copies of the MFMA-class tables
     int32_t *heads;          // [num_blocks] queue heads
-    int32_t *flags;          // [kMaxCkptSlots] checkpoint ready flags
-    float *ckpt;             // [kMaxCkptSlots][4][16][max R2 + 4]
+    int32_t *flags;          // [ckpt_slots] checkpoint ready flags
+    float *ckpt;             // [ckpt_slots][4][16][max R2 + 4]
+    int32_t ckpt_slots;      // min(kMaxCkptSlots, chunk bound of the workspace)
     float *E;                // unique rows, per-table segments
     float *Cg;               // kept prefix intermediates: [work position][16][R2] per table (keep_prefix)
     int64_t *cbase;          // [T] offset of table t's units in Cg, minus tab_unit_start[t]*16*R2
     float *sink;             // [kSinkFloats] scratch target of stores that carry no result
+    struct FwdTab *ftab;     // [T] per-table pointers and shapes of the forward class kernels
     BlockStat *bstat;        // [kStatKernels][kStatBlocks] per-block scheduling records
     // backward
     int2 *lk;                // [nnz] (bag within its table, unique row) of each lookup

@@ -853,3 +853,38 @@ def test_kcore_most_cores_per_handle():
     got = [g.cpu().numpy() for g in run.backward(w.grad_out,
                                                   flags=tt.TT_EMB_REUSE_GROUPING | tt.TT_EMB_REUSE_PREFIX)]
     assert_grads_close(got, oracle.backward_k(w))
+
+
+# ------------------------------------------------ inference-only workspace
+
+def test_forward_only_workspace():
+    # a forward without kept prefix intermediates runs in the smaller forward
+    # workspace and matches the oracle; calls that need the backward's
+    # regions are refused on it
+    w = W.make_workload(5, bags=64)
+    emb = tt.TTEmbeddingBag(w.tables, DEV, forward_only=True)
+    full = tt.tt_emb_workspace_size(emb.handle, w.B, w.nnz)
+    fwd = tt.tt_emb_forward_workspace_size(emb.handle, w.B, w.nnz)
+    print(f"[ws] forward {fwd} of {full} bytes", flush=True)
+    assert 0 < fwd < full
+    cores = [torch.from_numpy(c).to(DEV) for c in w.cores]
+    idx = torch.from_numpy(w.indices).to(DEV)
+    off = torch.from_numpy(w.offsets).to(DEV)
+    out = emb.forward(cores, idx, off, w.B)
+    torch.cuda.synchronize()
+    assert emb.workspace(w.B, w.nnz).numel() == fwd
+    assert_out_close(w, out.cpu().numpy(), oracle.forward(w))
+    assert emb.poll_error() == 0
+    g = emb.grouping(w.B, w.nnz)
+    ref = oracle.grouping(w)
+    for k in ref:
+        assert np.array_equal(g[k].cpu().numpy(), ref[k]), k
+    with pytest.raises(tt.TTEmbError) as e:
+        emb.backward(torch.from_numpy(w.grad_out).to(DEV), cores, idx, off, w.B, flags=tt.TT_EMB_REUSE_GROUPING)
+    assert e.value.status == tt.TT_EMB_ERR_WORKSPACE
+    o = tt.tt_emb_options()
+    o.keep_prefix = 1
+    embk = tt.TTEmbeddingBag(w.tables, DEV, o, forward_only=True)
+    with pytest.raises(tt.TTEmbError) as e:
+        embk.forward(cores, idx, off, w.B, flags=tt.TT_EMB_KEEP_PREFIX)
+    assert e.value.status == tt.TT_EMB_ERR_WORKSPACE
