@@ -148,8 +148,10 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.g3t = (float *)take(4 * (size_t)h->g3t_elems);
     // 4 classes x up to kMaxWorkersPerCu workers per CU, one 128-byte line each
     w.heads = (int32_t *)take(4 * (size_t)h->num_blocks * 4 * kMaxWorkersPerCu * 32);
-    // checkpoint slots: one per split tile, at most one per chunk
-    const int64_t ckpt_slots = chunks < kMaxCkptSlots ? chunks : kMaxCkptSlots;
+    // L2 checkpoint slots (stealing with checkpoints only): one per split
+    // tile, and a split tile holds more than chunk_rows unique rows
+    int64_t ckpt_slots = h->sched_mode == 3 ? n / (h->chunk_rows + 1) + 1 : 0;
+    if (ckpt_slots > kMaxCkptSlots) ckpt_slots = kMaxCkptSlots;
     w.ckpt_slots = (int32_t)ckpt_slots;
     w.flags = (int32_t *)take(4 * (size_t)ckpt_slots);
     w.ckpt = (float *)take(4 * (size_t)ckpt_slots * (4 * (16 * 68 + 16)));
