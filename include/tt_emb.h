@@ -60,7 +60,8 @@ enum {
     TT_EMB_ERR_UNSUPPORTED = -4, /* shape outside what this build supports */
     TT_EMB_ERR_HIP = -5,         /* a HIP runtime call failed */
     TT_EMB_ERR_NOMEM = -6,       /* host or create-time device allocation failed */
-    TT_EMB_ERR_OFFSETS = -7      /* malformed offsets (device-detected) */
+    TT_EMB_ERR_OFFSETS = -7,     /* malformed offsets (device-detected) */
+    TT_EMB_ERR_TOO_LARGE = -8    /* input needs more than tt_emb_forward_noalloc's fixed scratch */
 };
 
 /* Scheduling of the persistent contraction kernel (FlowTT section 3.4 and the
@@ -210,6 +211,27 @@ int tt_emb_group(tt_emb_t h, const int64_t *indices, const int64_t *offsets, int
 int tt_emb_forward(tt_emb_t h, const float *const *cores, const int64_t *indices,
                    const int64_t *offsets, int64_t B, int64_t nnz, float *out, void *ws,
                    size_t ws_bytes, uint32_t flags, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * forward of tt_emb_forward (same kernels, same results bit for bit) with no
+ * workspace argument.  Its scratch is a fixed device array of
+ * TT_EMB_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends; the call itself allocates nothing (no hipMalloc, no
+ * allocating library routine).  The input must fit: when the forward
+ * workspace for (B, nnz) (tt_emb_forward_workspace_size) exceeds the array,
+ * returns TT_EMB_ERR_TOO_LARGE without launching anything.  flags:
+ * TT_EMB_REUSE_GROUPING (the array still holds the grouping of the same
+ * indices and offsets from the previous call on this GPU) and
+ * TT_EMB_ATOMIC_POOL; TT_EMB_KEEP_PREFIX is TT_EMB_ERR_ARG.  Every call on a
+ * GPU shares that GPU's array, which keeps the last call's contents: calls
+ * that overlap on one GPU (other streams, other threads, other handles) race
+ * and must be serialised by the caller; tt_emb_poll_error does not apply
+ * (device-detected errors of this call are not reported). */
+#define TT_EMB_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int tt_emb_forward_noalloc(tt_emb_t h, const float *const *cores, const int64_t *indices,
+                           const int64_t *offsets, int64_t B, int64_t nnz, float *out, uint32_t flags,
+                           void *stream);
 
 /* Backward of out = forward(cores) for the loss sum(grad_out * out) (FlowTT
  * section 3.2: the backward reverses the forward).  grad_out fp32 [B][sum D]

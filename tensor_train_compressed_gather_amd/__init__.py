@@ -26,6 +26,7 @@ TT_EMB_ERR_UNSUPPORTED = -4
 TT_EMB_ERR_HIP = -5
 TT_EMB_ERR_NOMEM = -6
 TT_EMB_ERR_OFFSETS = -7
+TT_EMB_ERR_TOO_LARGE = -8
 
 TT_EMB_SCHED_DEFAULT, TT_EMB_SCHED_STATIC, TT_EMB_SCHED_STEAL, TT_EMB_SCHED_STEAL_L2 = 0, 1, 2, 3
 TT_EMB_GROUP_DEFAULT, TT_EMB_GROUP_PREFIX, TT_EMB_GROUP_UNIQUE_ONLY = 0, 1, 2
@@ -36,7 +37,7 @@ TT_EMB_ATOMIC_POOL = 8
 
 EXPORTED = (
     "tt_emb_create", "tt_emb_create_k", "tt_emb_destroy", "tt_emb_workspace_size", "tt_emb_forward_workspace_size",
-    "tt_emb_group", "tt_emb_forward",
+    "tt_emb_group", "tt_emb_forward", "tt_emb_forward_noalloc",
     "tt_emb_backward", "tt_emb_sgd_update", "tt_emb_grouping_view", "tt_emb_poll_error",
     "tt_emb_status_string", "tt_emb_timing_enable", "tt_emb_timing_read", "tt_emb_timer_name",
     "tt_emb_block_stats", "tt_emb_victim_order", "tt_emb_peak_mfma",
@@ -90,6 +91,7 @@ def lib():
             L.tt_emb_forward_workspace_size.argtypes = [p, i64, i64, C.POINTER(C.c_size_t)]
             L.tt_emb_group.argtypes = [p, p, p, i64, i64, p, C.c_size_t, p]
             L.tt_emb_forward.argtypes = [p, p, p, p, i64, i64, p, p, C.c_size_t, u32, p]
+            L.tt_emb_forward_noalloc.argtypes = [p, p, p, p, i64, i64, p, u32, p]
             L.tt_emb_backward.argtypes = [p, p, p, p, p, i64, i64, p, p, C.c_size_t, u32, p]
             L.tt_emb_sgd_update.argtypes = [p, p, p, C.c_float, p]
             L.tt_emb_grouping_view.argtypes = [p, p, C.c_size_t, i64, i64, p, C.POINTER(tt_emb_grouping)]
@@ -242,6 +244,16 @@ def tt_emb_forward(h, cores, indices, offsets, B: int, out, ws, flags: int = 0, 
                               int(indices.numel()), _ptr(out), _ptr(ws), ws.numel(), int(flags),
                               _stream(stream))
     _check(rc, "tt_emb_forward")
+
+
+def tt_emb_forward_noalloc(h, cores, indices, offsets, B: int, out, flags: int = 0, stream=None):
+    """The forward with the library's fixed per-GPU scratch instead of a
+    workspace (allocates nothing; calls on one GPU must not overlap)."""
+    _need([(indices, "indices", "int64"), (offsets, "offsets", "int64"), (cores, "cores", "float32"),
+           (out, "out", "float32")])
+    rc = lib().tt_emb_forward_noalloc(h, _ptr_array(cores), _ptr(indices), _ptr(offsets), int(B),
+                                      int(indices.numel()), _ptr(out), int(flags), _stream(stream))
+    _check(rc, "tt_emb_forward_noalloc")
 
 
 def tt_emb_backward(h, grad_out, cores, indices, offsets, B: int, core_grads, ws, flags: int = 0,

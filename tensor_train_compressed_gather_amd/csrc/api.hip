@@ -1,6 +1,7 @@
 // api.hip -- host side of the C ABI declared in include/tt_emb.h: argument
 // checks, the workspace plan, and stream-ordered launch sequencing.
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -53,6 +54,30 @@ struct tt_emb {
 };
 
 namespace {
+
+// Scratch of tt_emb_forward_noalloc: one fixed array per GPU the library runs
+// on.  In host code `scratch` only names the symbol; its device address on
+// each GPU is looked up once (hipGetSymbolAddress with that GPU current) and
+// kept in noalloc_ptr, which is what the launches receive.
+static __device__ __align__(256) char scratch[TT_EMB_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex noalloc_mu;
+void *noalloc_ptr[kMaxDevices] = {};
+hipError_t noalloc_err[kMaxDevices] = {};
+bool noalloc_done[kMaxDevices] = {};
+
+// Called at create time with the handle's device current.
+void noalloc_setup(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return;
+    std::lock_guard<std::mutex> g(noalloc_mu);
+    if (noalloc_done[dev]) return;
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    noalloc_err[dev] = e;
+    noalloc_ptr[dev] = e == hipSuccess ? ptr : nullptr;
+    noalloc_done[dev] = true;
+}
 
 int bits_for(uint64_t max_value)
 {
@@ -523,6 +548,8 @@ int tt_emb_create(int32_t T, const int64_t *num_rows, const int32_t *n, const in
             // need more than 256 registers per lane (one wave per SIMD)
             h->num_blocks = (cus + 7) / 8 * 8;
         }
+        // the no-allocation forward's scratch on this device (looked up once per device)
+        noalloc_setup(h->device);
         if (hipMalloc((void **)&h->dtab, sizeof(TableDesc) * T) != hipSuccess) {
             delete h;
             return TT_EMB_ERR_NOMEM;
@@ -719,6 +746,27 @@ int tt_emb_forward(tt_emb_t h, const float *const *cores, const int64_t *indices
             if ((rc = hip_status(launch_grouping(p, indices, offsets, s)))) return rc;
         }
         return hip_status(launch_forward(p, cp, offsets, out, s));
+    } catch (...) {
+        return TT_EMB_ERR_NOMEM;
+    }
+}
+
+int tt_emb_forward_noalloc(tt_emb_t h, const float *const *cores, const int64_t *indices, const int64_t *offsets,
+                           int64_t B, int64_t nnz, float *out, uint32_t flags, void *stream)
+{
+    try {
+        if (!h || B < 0 || nnz < 0 || nnz >= (int64_t)0x7fffffff) return TT_EMB_ERR_ARG;
+        if (flags & TT_EMB_KEEP_PREFIX) return TT_EMB_ERR_ARG;
+        size_t need = 0;
+        plan_workspace(h, B, nnz, nullptr, nullptr, &need);
+        if (need > TT_EMB_NOALLOC_SCRATCH_BYTES) return TT_EMB_ERR_TOO_LARGE;
+        int rc = set_device(h);
+        if (rc) return rc;
+        if (h->device < 0 || h->device >= kMaxDevices || !noalloc_done[h->device]) return TT_EMB_ERR_HIP;
+        void *ws = noalloc_ptr[h->device];
+        if (!ws) return TT_EMB_ERR_HIP;
+        return tt_emb_forward(h, cores, indices, offsets, B, nnz, out, ws, TT_EMB_NOALLOC_SCRATCH_BYTES, flags,
+                              stream);
     } catch (...) {
         return TT_EMB_ERR_NOMEM;
     }
@@ -956,6 +1004,7 @@ const char *tt_emb_status_string(int status)
     case TT_EMB_ERR_HIP: return "HIP runtime error";
     case TT_EMB_ERR_NOMEM: return "out of memory";
     case TT_EMB_ERR_OFFSETS: return "malformed offsets";
+    case TT_EMB_ERR_TOO_LARGE: return "input too large for the fixed scratch of the no-allocation forward";
     default: return "unknown status";
     }
 }

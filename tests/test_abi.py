@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         s = tt.tt_emb_status_string(code)
         assert s and s != "unknown status"
     assert tt.tt_emb_status_string(-99) == "unknown status"
