@@ -23,6 +23,7 @@
  *  - indices and offsets are int64; offsets are table-major CSR with T*B+1
  *    entries (offsets[0] = 0, non-decreasing, offsets[T*B] = nnz); bag (t, b)
  *    is indices[offsets[t*B+b] .. offsets[t*B+b+1]); an empty bag pools to 0;
+ *    lookups need bags: nnz > 0 with B = 0 is TT_EMB_ERR_ARG;
  *  - out is fp32 [B][sum_t D_t], bag-major, tables concatenated in order;
  *  - valid rows are 0 <= i < N_t; anything else is an index error.
  *

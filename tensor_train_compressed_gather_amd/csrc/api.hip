@@ -200,7 +200,7 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.bstat = (BlockStat *)take(sizeof(BlockStat) * (size_t)kStatKernels * kStatBlocks);
     w.cbase = (int64_t *)take(8 * T);
     w.ftab = (FwdTab *)take(sizeof(FwdTab) * (size_t)T);
-    w.lk = (int2 *)take(8 * n);
+    w.lb = (int32_t *)take(4 * n);
     // K >= 4 cores: per prefix length m = 2..K-1, the group of each unique
     // row, the groups' first rows, and one intermediate per group (at most
     // min(prefixes of length m, rows, nnz) groups per table)
@@ -245,6 +245,8 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.Cg = (float *)take(4 * (cg_elems > 0 ? cg_elems : 4));
     w.gu_ml = (int32_t *)take(4 * tasks);
     w.gu_mr = (int32_t *)take(4 * tasks);
+    // gradient gather: sorted-order lookup metadata
+    w.sm = (int2 *)take(8 * n);
     w.P3 = (float *)take(4 * (p3_elems > part_elems ? p3_elems : part_elems));
     // G1 partials are indexed by work position (< units) with a uniform stride
     w.G1P = (float *)take(4 * (size_t)units_bound * h->max_d1R1);
@@ -361,6 +363,7 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
             Ws &v = p->ws;
             v.Cg = nullptr;
             v.gu_ml = v.gu_mr = nullptr;
+            v.sm = nullptr;
             v.P3 = v.G1P = v.G2P = nullptr;
             v.g3rng = v.run_pbase = v.run_sbase = v.piece_tb = v.piece_te = v.piece_slot = nullptr;
             v.rkey0 = v.rkey1 = nullptr;
@@ -386,6 +389,7 @@ int check_call(const tt_emb *h, int64_t B, int64_t nnz, const int64_t *indices, 
     if ((int64_t)h->T * B >= (int64_t)0x7fffffff) return TT_EMB_ERR_ARG;
     if (!offsets) return TT_EMB_ERR_ARG;
     if (nnz > 0 && !indices) return TT_EMB_ERR_ARG;
+    if (nnz > 0 && B == 0) return TT_EMB_ERR_ARG; // lookups with no bag to belong to
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return TT_EMB_ERR_WORKSPACE;
     size_t fwd = 0;
     const size_t all = plan_workspace(h, B, nnz, nullptr, nullptr, &fwd);

@@ -41,8 +41,7 @@ struct BwdArgs {
     int g2p_slots; // dG2 partial slots in the workspace (pieces of split runs)
 };
 
-// (bag within its table, unique row) of every lookup, in lookup order, so the
-// gather reads both with one load per sorted position.  A block takes
+// Bag within its table of every lookup, in lookup order.  A block takes
 // kThreads bags; their lookups are contiguous, so lanes walk them coalesced
 // and find their bag by binary search over the block's offsets in LDS.
 __global__ __launch_bounds__(kThreads) void k_lookup_meta(BwdArgs a)
@@ -65,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void k_lookup_meta(BwdArgs a)
                 else i1 = mid;
             }
             const int64_t b = b0 + i0;
-            a.ws.lk[l] = make_int2((int)(b - (b / a.B) * a.B), a.ws.inv[l]);
+            a.ws.lb[l] = (int)(b - (b / a.B) * a.B);
         }
         __syncthreads();
     }
@@ -74,39 +73,40 @@ __global__ __launch_bounds__(kThreads) void k_lookup_meta(BwdArgs a)
 // Gather task numbering.  The sorted positions of table t,
 // [tstart[t], tstart[t+1]), are cut into tasks of kGuTask positions; table t
 // owns tasks [base[t], base[t+1]) of the global order (partial slots, cut-run
-// records) and [cbase[t], cbase[t+1]) of the order of gather class gcls (all
-// tables when gcls < 0).  Both prefixes are built in LDS by wave 0.
-// Per-table values a gather task needs, copied to LDS once per block so that
-// no global load issued between a worker's stores has to wait for them.
+// records).  The gather works on ids over (table, column piece, task): table t
+// holds ids [qb[t], qb[t+1]), piece-major.  The prefixes are built in LDS by
+// wave 0.  Per-table values a gather task needs are copied to LDS once per
+// block so that no global load issued between a worker's stores has to wait
+// for them.
 struct GuTab {
     int64_t ebase;
-    int ts, te, u0, u1, D, Dp, col_off, pad;
+    int ts, te, u0, u1, D, Dp, col_off, ntask;
 };
 
-__device__ void gu_bases(const BwdArgs &a, int gcls, int *base, int *cbase, GuTab *gt)
+__device__ void gu_bases(const BwdArgs &a, int *base, int *qb, GuTab *gt)
 {
     if (threadIdx.x < 64) {
         const int t = threadIdx.x;
-        int n = 0, c = 0;
+        int n = 0, q = 0;
         if (t < a.T) {
             const TableDesc &tb = a.tab[t];
-            gt[t] = GuTab{a.ws.ebase[t], a.ws.tstart[t], a.ws.tstart[t + 1], a.ws.tab_uniq_start[t],
-                          a.ws.tab_uniq_start[t + 1], tb.D, tb.Dp, tb.col_off, 0};
             const int len = a.ws.tstart[t + 1] - a.ws.tstart[t];
             n = len > 0 ? (len + kGuTask - 1) / kGuTask : 0;
-            c = (gcls < 0 || a.tab[t].gcls == gcls) ? n : 0;
+            q = n * (tb.D > kGuCols ? (tb.D + kGuCols - 1) / kGuCols : 1);
+            gt[t] = GuTab{a.ws.ebase[t], a.ws.tstart[t], a.ws.tstart[t + 1], a.ws.tab_uniq_start[t],
+                          a.ws.tab_uniq_start[t + 1], tb.D, tb.Dp, tb.col_off, n};
         }
         for (int o = 1; o < 64; o <<= 1) {
-            const int yn = __shfl_up(n, o, 64), yc = __shfl_up(c, o, 64);
+            const int yn = __shfl_up(n, o, 64), yq = __shfl_up(q, o, 64);
             if (t >= o) {
                 n += yn;
-                c += yc;
+                q += yq;
             }
         }
-        if (t == 0) base[0] = cbase[0] = 0;
+        if (t == 0) base[0] = qb[0] = 0;
         if (t < a.T) {
             base[t + 1] = n;
-            cbase[t + 1] = c;
+            qb[t + 1] = q;
         }
     }
     __syncthreads();
@@ -124,126 +124,198 @@ __device__ inline int gu_table(const int *pre, int T, int id)
     return lo;
 }
 
-// Gradient gather g_u = sum of grad_out rows over the lookups of unique row u,
-// for the tables of one gather class.  A worker is a group of LPR lanes (one
-// grad_out row per instruction, a float4 or a float per lane); it walks the
+// Sorted-order metadata of the gather: Ws::sm[k] = (bag of the lookup at
+// sorted position k, its unique row).  Chunks of kSmChunk positions; the
+// blocks of virtual XCD x = blockIdx % 8 (launched in multiples of 8) take
+// the x-th eighth of the chunks, so the random reads of lb stay inside the
+// few tables that one L2 holds.  The unique row comes from the run starts:
+// the block loads the starts of the runs from the one holding its first
+// position (inv of that lookup) on, and each lane finds the last start at or
+// before its position.
+constexpr int kSmPer = 4, kSmChunk = kSmPer * kThreads;
+
+__global__ __launch_bounds__(kThreads) void k_sorted_meta(BwdArgs a)
+{
+    __shared__ int win[kSmChunk + 1];
+    const Ws &ws = a.ws;
+    const int64_t n = a.nnz, nch = (n + kSmChunk - 1) / kSmChunk;
+    const int x = blockIdx.x & 7, nbx = gridDim.x >> 3;
+    const int64_t c_hi = nch * (x + 1) / 8;
+    const int U = ws.ctrl[CTRL_U];
+    for (int64_t c = nch * x / 8 + (blockIdx.x >> 3); c < c_hi; c += nbx) {
+        const int64_t p0 = c * kSmChunk;
+        int l[kSmPer];
+#pragma unroll
+        for (int i = 0; i < kSmPer; ++i) {
+            const int64_t pos = p0 + threadIdx.x + i * kThreads;
+            l[i] = ws.perm[pos < n ? pos : n - 1];
+        }
+        int u0 = ws.inv[ws.perm[p0]];
+        u0 = u0 < 0 ? 0 : (u0 >= U ? U - 1 : u0);
+        __syncthreads(); // previous chunk's window read
+        for (int j = threadIdx.x; j <= kSmChunk; j += kThreads)
+            win[j] = u0 + j <= U ? ws.uniq_start[u0 + j] : 0x7fffffff;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSmPer; ++i) {
+            const int64_t pos = p0 + threadIdx.x + i * kThreads;
+            if (pos >= n) break;
+            // the chunk holds at most kSmChunk - 1 run starts after u0's, so
+            // the last start at or before pos is one of win[0 .. kSmChunk - 1]
+            int jl = 0, jh = kSmChunk;
+            while (jh - jl > 1) {
+                const int mid = (jl + jh) >> 1;
+                if (win[mid] <= pos) jl = mid;
+                else jh = mid;
+            }
+            ws.sm[pos] = make_int2(ws.lb[l[i]], u0 + jl);
+        }
+    }
+}
+
+// Gradient gather g_u = sum of grad_out rows over the lookups of unique row u.
+// A worker is LPR = kGuCols / 4 lanes, a float4 each: one piece of kGuCols
+// columns of a grad_out row (a whole row when D <= kGuCols).  It walks the
 // positions of its task in sorted order, kGuBatch rows in flight, summing
 // runs of equal u.  A run that lies inside the task goes straight to u's slot
 // of the unique-row buffer (E's space); a run cut by the task's left or right
-// edge leaves its sum in the task's left or right partial slot, recorded in
-// gu_ml / gu_mr, and k_gu_join adds the parts in task order.  The order of
-// every sum is fixed by the task cut alone.
-template <int LPR, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_gu_gather(BwdArgs a, int gcls)
+// edge leaves its sum in the task's left or right partial slot (this piece's
+// columns), recorded in gu_ml / gu_mr, and k_gu_join adds the parts in task
+// order.  The order of every sum is fixed by the task cut alone.  The blocks
+// of virtual XCD x = blockIdx % 8 (launched in multiples of 8) take the x-th
+// eighth of the ids in order, so one XCD's workers read the rows of about one
+// table at a time.  Measured on the 26-table training step: the random row
+// reads are bound by the line misses a compute unit keeps in flight, so whole
+// lines per request matter and L2 residency hardly does (64-column pieces
+// with these ids 0.70 ms; 32-column 0.72; 16-column pieces of a per-table
+// copy of grad_out, 2 MB per XCD, 1.1 ms; ids without XCD affinity, same
+// time as with).
+template <bool VEC>
+__device__ __forceinline__ float4 gu_row(const float *gr, int nv)
 {
-    constexpr int G = 64 / LPR;                                // workers per wave
-    constexpr int NS = LPR >= kGuBatch ? 1 : kGuBatch / LPR;   // metadata slots per lane
-    __shared__ int base[kMaxTables + 1], cbase[kMaxTables + 1];
+    if (VEC) return *reinterpret_cast<const float4 *>(gr);
+    // unaligned or partial: clamped scalar loads (columns past nv are dropped by the caller)
+    const int m = nv > 0 ? nv - 1 : 0;
+    return make_float4(gr[0 < m ? 0 : m], gr[1 < m ? 1 : m], gr[2 < m ? 2 : m], gr[3 < m ? 3 : m]);
+}
+
+template <bool VEC, int LPR, int NS>
+__device__ __forceinline__ void gu_walk(const BwdArgs &a, const Ws &ws, int k0, int k1, int u0, int u1, int uleft,
+                                        int uright, const float *go, int nv, float *Ej, int Dp, float *slotLj,
+                                        float *slotRj, int grp, int gl, int &mL, int &mR)
+{
+    auto clampu = [&](int u) { return u < u0 ? u0 : (u >= u1 ? u1 - 1 : u); };
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int ucur = clampu(ws.sm[k0].y);
+    bool first = true;
+    auto store = [&](float *dst) {
+        if (VEC || nv == 4) {
+            *reinterpret_cast<float4 *>(dst) = acc;
+        } else {
+            if (nv > 0) dst[0] = acc.x;
+            if (nv > 1) dst[1] = acc.y;
+            if (nv > 2) dst[2] = acc.z;
+        }
+    };
+    // metadata of a batch: position kb + e sits in lane e % LPR, slot e / LPR.
+    // Loads are unconditional (positions past the task read its last one, and
+    // their rows are never added), so all are in flight together; the next
+    // batch's metadata is loaded while this batch's rows are summed
+    int2 meta[NS];
+    auto load_meta = [&](int kb) {
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+            const int pos = kb + sl * LPR + gl;
+            meta[sl] = ws.sm[pos < k1 ? pos : k1 - 1];
+        }
+    };
+    load_meta(k0);
+    for (int kb = k0; kb < k1; kb += kGuBatch) {
+        int bg[NS], uu[NS];
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+            bg[sl] = meta[sl].x < 0 ? 0 : (meta[sl].x >= a.B ? (int)a.B - 1 : meta[sl].x);
+            uu[sl] = clampu(meta[sl].y);
+        }
+        float4 row[kGuBatch];
+#pragma unroll
+        for (int ii = 0; ii < kGuBatch; ++ii) {
+            const int b = __shfl(bg[ii / LPR], grp * LPR + ii % LPR, 64);
+            row[ii] = gu_row<VEC>(go + (int64_t)b * a.SD, nv);
+        }
+        load_meta(kb + kGuBatch < k1 ? kb + kGuBatch : kb);
+#pragma unroll
+        for (int ii = 0; ii < kGuBatch; ++ii) {
+            const int u = __shfl(uu[ii / LPR], grp * LPR + ii % LPR, 64);
+            if (kb + ii < k1) {
+                if (u != ucur) {
+                    // a run ends inside the task: its own row, or the left cut
+                    const bool cutl = first && ucur == uleft;
+                    if (cutl) mL = ucur;
+                    store(cutl ? slotLj : Ej + (int64_t)ucur * Dp);
+                    first = false;
+                    ucur = u;
+                    acc = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+                acc.x += row[ii].x;
+                acc.y += row[ii].y;
+                acc.z += row[ii].z;
+                acc.w += row[ii].w;
+            }
+        }
+    }
+    const bool cutl = first && ucur == uleft, cutr = ucur == uright;
+    if (cutl) mL = ucur;
+    if (cutr) mR = ucur;
+    store(cutl ? slotLj : (cutr ? slotRj : Ej + (int64_t)ucur * Dp));
+}
+
+__global__ __launch_bounds__(kThreads) void k_gu_gather(BwdArgs a)
+{
+    constexpr int LPR = kGuCols / 4, G = 64 / LPR, NS = kGuBatch / LPR; // NS metadata slots per lane
+    static_assert(LPR * NS == kGuBatch && G * LPR == 64, "batch and workers tile the wave");
+    __shared__ int base[kMaxTables + 1], qb[kMaxTables + 1];
     __shared__ GuTab gt[kMaxTables];
-    gu_bases(a, gcls, base, cbase, gt);
+    gu_bases(a, base, qb, gt);
     const Ws &ws = a.ws;
-    const int T = a.T, ntask = cbase[T];
+    const int T = a.T, nid = qb[T];
     const int lane = threadIdx.x & 63, grp = lane / LPR, gl = lane - grp * LPR;
-    const int gwave = (blockIdx.x * kThreads + threadIdx.x) >> 6;
-    const int nworkers = gridDim.x * (kThreads / 64) * G;
-    const int64_t SD = a.SD;
-    for (int id = gwave * G + grp; id < ntask; id += nworkers) {
-        const int t = gu_table(cbase, T, id);
-        const int task = base[t] + (id - cbase[t]);
+    const int x = blockIdx.x & 7, nbx = gridDim.x >> 3;
+    const int id_hi = (int)((int64_t)nid * (x + 1) / 8);
+    const int wk = ((blockIdx.x >> 3) * (kThreads / 64) + (threadIdx.x >> 6)) * G + grp;
+    const int nwk = nbx * (kThreads / 64) * G;
+    // rows move as float4 when every row of every table starts 16-byte aligned
+    const bool rows16 = (a.SD & 3) == 0 && (reinterpret_cast<uintptr_t>(a.grad_out) & 15) == 0;
+    for (int id = (int)((int64_t)nid * x / 8) + wk; id < id_hi; id += nwk) {
+        const int t = gu_table(qb, T, id);
         const GuTab tb = gt[t];
+        const int r = id - qb[t], pc = r / tb.ntask, k = r - pc * tb.ntask;
+        const int task = base[t] + k;
         const int ts = tb.ts, te = tb.te;
-        const int k0 = ts + (id - cbase[t]) * kGuTask;
+        const int k0 = ts + k * kGuTask;
         const int k1 = k0 + kGuTask < te ? k0 + kGuTask : te;
         const int u0 = tb.u0, u1 = tb.u1;
         int mL = -1, mR = -1;
         if (u1 > u0) {
             auto clampu = [&](int u) { return u < u0 ? u0 : (u >= u1 ? u1 - 1 : u); };
-            const int D = tb.D, Dp = tb.Dp;
-            float *Eu = ws.E + tb.ebase;
-            const float *go = a.grad_out + tb.col_off;
-            float *slotL = ws.P3 + (int64_t)(2 * task) * a.gstride, *slotR = slotL + a.gstride;
+            const int j = pc * kGuCols + 4 * gl; // first column of this lane
+            int nv = tb.D - j;                   // columns of this lane's float4 inside the table
+            nv = nv < 0 ? 0 : (nv > 4 ? 4 : nv);
+            const float *go = a.grad_out + tb.col_off + (nv > 0 ? j : 0);
+            float *Ej = ws.E + tb.ebase + j;
+            float *slotLj = ws.P3 + (int64_t)(2 * task) * a.gstride + j, *slotRj = slotLj + a.gstride;
             // unique rows of the positions just outside the task (-1: table edge)
-            const int uleft = k0 > ts ? clampu(ws.lk[ws.perm[k0 - 1]].y) : -1;
-            const int uright = k1 < te ? clampu(ws.lk[ws.perm[k1]].y) : -1;
-            const int cn = VEC ? (D + 3) >> 2 : D; // columns in float4 (or float) units
-            for (int cb = 0; cb < cn; cb += LPR) {
-                const int c = cb + gl;
-                const bool okc = c < cn;
-                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-                int ucur = -1;
-                bool first = true;
-                auto flush = [&](bool last) {
-                    const bool cutl = first && ucur == uleft;
-                    const bool cutr = last && ucur == uright;
-                    if (cutl) mL = ucur;
-                    if (cutr) mR = ucur;
-                    float *dst = cutl ? slotL : (cutr ? slotR : Eu + (int64_t)ucur * Dp);
-                    if (!okc) return;
-                    if (VEC) {
-                        const int j = 4 * c;
-                        if (j + 3 < D) {
-                            *reinterpret_cast<float4 *>(dst + j) = acc;
-                        } else {
-                            if (j + 0 < D) dst[j + 0] = acc.x;
-                            if (j + 1 < D) dst[j + 1] = acc.y;
-                            if (j + 2 < D) dst[j + 2] = acc.z;
-                        }
-                    } else {
-                        dst[c] = acc.x;
-                    }
-                };
-                for (int kb = k0; kb < k1; kb += kGuBatch) {
-                    // metadata of the batch: position kb + e sits in lane e % LPR, slot e / LPR
-                    int bg[NS], uu[NS];
-#pragma unroll
-                    for (int sl = 0; sl < NS; ++sl) {
-                        const int e = sl * LPR + gl, pos = kb + e;
-                        bg[sl] = 0;
-                        uu[sl] = -1;
-                        if (e < kGuBatch && pos < k1) {
-                            const int2 m = ws.lk[ws.perm[pos]];
-                            bg[sl] = m.x < 0 ? 0 : (m.x >= a.B ? (int)a.B - 1 : m.x);
-                            uu[sl] = clampu(m.y);
-                        }
-                    }
-                    float4 row[kGuBatch];
-#pragma unroll
-                    for (int ii = 0; ii < kGuBatch; ++ii) {
-                        const int src = grp * LPR + ii % LPR;
-                        const int b = __shfl(bg[ii / LPR < NS ? ii / LPR : 0], src, 64);
-                        row[ii] = make_float4(0.f, 0.f, 0.f, 0.f);
-                        if (okc && kb + ii < k1) {
-                            const float *gr = go + (int64_t)b * SD;
-                            if (VEC) row[ii] = reinterpret_cast<const float4 *>(gr)[c];
-                            else row[ii].x = gr[c];
-                        }
-                    }
-#pragma unroll
-                    for (int ii = 0; ii < kGuBatch; ++ii) {
-                        const int src = grp * LPR + ii % LPR;
-                        const int u = __shfl(uu[ii / LPR < NS ? ii / LPR : 0], src, 64);
-                        if (kb + ii < k1) {
-                            if (u != ucur) {
-                                if (ucur >= 0) {
-                                    flush(false);
-                                    first = false;
-                                }
-                                ucur = u;
-                                acc = make_float4(0.f, 0.f, 0.f, 0.f);
-                            }
-                            acc.x += row[ii].x;
-                            if (VEC) {
-                                acc.y += row[ii].y;
-                                acc.z += row[ii].z;
-                                acc.w += row[ii].w;
-                            }
-                        }
-                    }
-                }
-                if (ucur >= 0) flush(true);
-            }
+            const int uleft = k0 > ts ? clampu(ws.sm[k0 - 1].y) : -1;
+            const int uright = k1 < te ? clampu(ws.sm[k1].y) : -1;
+            const bool vec = rows16 && (tb.col_off & 3) == 0 && nv == 4;
+            if (__all(vec)) // wave-uniform: every lane of the wave reads whole float4
+                gu_walk<true, LPR, NS>(a, ws, k0, k1, u0, u1, uleft, uright, go, nv, Ej, tb.Dp, slotLj, slotRj,
+                                       grp, gl, mL, mR);
+            else
+                gu_walk<false, LPR, NS>(a, ws, k0, k1, u0, u1, uleft, uright, go, nv, Ej, tb.Dp, slotLj, slotRj,
+                                        grp, gl, mL, mR);
         }
-        if (gl == 0) {
+        if (gl == 0 && pc == 0) { // every piece of a task sees the same runs
             ws.gu_ml[task] = mL;
             ws.gu_mr[task] = mR;
         }
@@ -256,9 +328,9 @@ __global__ __launch_bounds__(kThreads) void k_gu_gather(BwdArgs a, int gcls)
 // that order, into u's slot.  One wave per task, lanes over columns.
 __global__ __launch_bounds__(kThreads) void k_gu_join(BwdArgs a)
 {
-    __shared__ int base[kMaxTables + 1], cbase[kMaxTables + 1];
+    __shared__ int base[kMaxTables + 1], qb[kMaxTables + 1];
     __shared__ GuTab gt[kMaxTables];
-    gu_bases(a, -1, base, cbase, gt);
+    gu_bases(a, base, qb, gt);
     const Ws &ws = a.ws;
     const int T = a.T, ntask = base[T];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -1257,30 +1329,17 @@ hipError_t launch_gu_gather(const Plan &p, const float *grad_out, const int64_t 
         int g = ceil_div(nbags, kThreads);
         if (g > 4096) g = 4096;
         hipLaunchKernelGGL(k_lookup_meta, dim3(g), dim3(kThreads), 0, s, a);
+        // virtual-XCD launches: multiples of 8 blocks
+        // one chunk per block where the grid allows (the chain of loads per
+        // chunk is then overlapped across resident blocks)
+        int64_t gm = ceil_div(p.nnz, (int64_t)kSmChunk);
+        gm = (gm + 7) & ~int64_t(7);
+        gm = gm > 65536 ? 65536 : gm;
+        hipLaunchKernelGGL(k_sorted_meta, dim3((int)gm), dim3(kThreads), 0, s, a);
         const int64_t tasks = p.nnz / kGuTask + T + 1;
-        for (int c = 0; c < 16; ++c) {
-            if (!(p.gcls_mask & (1 << c))) continue;
-            const int lpr = 1 << (c & 7), G = 64 / lpr;
-            int gb = ceil_div(tasks, (int64_t)G * (kThreads / 64));
-            gb = gb < 1 ? 1 : (gb > 8192 ? 8192 : gb);
-            switch (c) {
-            case 0: hipLaunchKernelGGL((k_gu_gather<1, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 1: hipLaunchKernelGGL((k_gu_gather<2, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 2: hipLaunchKernelGGL((k_gu_gather<4, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 3: hipLaunchKernelGGL((k_gu_gather<8, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 4: hipLaunchKernelGGL((k_gu_gather<16, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 5: hipLaunchKernelGGL((k_gu_gather<32, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 6: hipLaunchKernelGGL((k_gu_gather<64, false>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 8: hipLaunchKernelGGL((k_gu_gather<1, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 9: hipLaunchKernelGGL((k_gu_gather<2, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 10: hipLaunchKernelGGL((k_gu_gather<4, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 11: hipLaunchKernelGGL((k_gu_gather<8, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 12: hipLaunchKernelGGL((k_gu_gather<16, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 13: hipLaunchKernelGGL((k_gu_gather<32, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            case 14: hipLaunchKernelGGL((k_gu_gather<64, true>), dim3(gb), dim3(kThreads), 0, s, a, c); break;
-            default: return hipErrorInvalidValue;
-            }
-        }
+        int gg = (kGuBlocksPerCu * p.num_blocks) & ~7;
+        gg = gg < 8 ? 8 : gg;
+        hipLaunchKernelGGL(k_gu_gather, dim3(gg), dim3(kThreads), 0, s, a);
         int gj = ceil_div(tasks, kThreads / 64);
         gj = gj > 4096 ? 4096 : gj;
         hipLaunchKernelGGL(k_gu_join, dim3(gj), dim3(kThreads), 0, s, a);

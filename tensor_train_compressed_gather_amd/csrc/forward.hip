@@ -511,7 +511,7 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
                 if (staged && se < s1 && c < D) Et[(int64_t)u * Dp + c] = v;
                 for (int sb = s0; sb < se; sb += 64) {
                     const int n = se - sb < 64 ? se - sb : 64;
-                    const int bag = lane < n ? a.ws.lk[a.ws.perm[sb + lane]].x : 0;
+                    const int bag = lane < n ? a.ws.lb[a.ws.perm[sb + lane]] : 0;
                     for (int k = 0; k < n; ++k) {
                         const int b = __shfl(bag, k, 64);
                         // (a lookup outside every bag, from malformed offsets, is skipped)
@@ -1520,7 +1520,7 @@ __global__ __launch_bounds__(kThreads) void k_pool_tail(FwdArgs a, int64_t nnz)
             const int l = ws.perm[sp];
             u = ws.inv[l];
             tail = sp - ws.uniq_start[u] >= kPoolCap;
-            bag = ws.lk[l].x;
+            bag = ws.lb[l];
         }
         uint64_t m = __ballot(tail);
         while (m) {

@@ -24,6 +24,8 @@ constexpr int kMaxCkptSlots = 4096; // L2 checkpoint slots for split prefix tile
 constexpr int kUnitsPerTile = 4;    // prefix units sharing (table, i2) per tile
 constexpr int kGuTask = 256;        // sorted lookup positions per gradient-gather task
 constexpr int kGuBatch = 32;        // positions whose grad_out rows a gather worker has in flight
+constexpr int kGuCols = 64;         // columns of one gradient-gather piece (256 bytes: two lines)
+constexpr int kGuBlocksPerCu = 2;   // gradient-gather blocks per compute unit
 constexpr int kPieceTiles = 8;      // least tiles per piece of a split backward run
 constexpr int kSplitMaxCls = 2;     // runs of the rank classes 8, 16, 32 may be split
 constexpr int kMaxG2Slots = 32768;  // dG2 partial slots (pieces of split runs)
@@ -182,7 +184,8 @@ struct Ws {
     struct FwdTab *ftab;     // [T] per-table pointers and shapes of the forward class kernels
     BlockStat *bstat;        // [kStatKernels][kStatBlocks] per-block scheduling records
     // backward
-    int2 *lk;                // [nnz] (bag within its table, unique row) of each lookup
+    int32_t *lb;             // [nnz] bag within its table of each lookup, in lookup order
+    int2 *sm;                // [nnz] (bag within its table, unique row) of each sorted position
     int32_t *gu_ml;          // [gather tasks] unique row of the run cut at the task's left edge, or -1
     int32_t *gu_mr;          // [gather tasks] unique row of the run cut at its right edge, or -1
     // the partial sums of cut runs ([task][left, right][gstride]) live in P3's space
@@ -281,7 +284,7 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
 // Backward (backward.hip)
 hipError_t launch_backward(const Plan &p, const float *grad_out, const CorePtrs &cores,
                            const int64_t *offsets, const GradPtrs &grads, hipStream_t s);
-// Bag (within its table) and unique row of every lookup position, Ws::lk.
+// Bag (within its table) of every lookup, Ws::lb.
 hipError_t launch_lookup_meta(const Plan &p, const int64_t *offsets, hipStream_t s);
 // Bag-major pooling of the unique rows of every table (forward.hip).
 hipError_t launch_pool(const Plan &p, const int64_t *offsets, float *out, hipStream_t s);

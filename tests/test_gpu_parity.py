@@ -406,6 +406,11 @@ def test_host_detected_errors():
     with pytest.raises(tt.TTEmbError) as e:
         tt.tt_emb_forward(run.emb.handle, cores, run.idx, run.off, w.B, out, ws)
     assert e.value.status == tt.TT_EMB_ERR_ARG
+    # lookups but no bags (offsets [0], nnz > 0)
+    off0 = torch.zeros(1, dtype=torch.int64, device=DEV)
+    with pytest.raises(tt.TTEmbError) as e:
+        tt.tt_emb_forward(run.emb.handle, run.cores, run.idx, off0, 0, out[:0], ws)
+    assert e.value.status == tt.TT_EMB_ERR_ARG
 
 
 # ------------------------------------------------ fused atomic pooling
