@@ -123,7 +123,10 @@ size_t plan_workspace(const tt_emb *h, int64_t B, int64_t nnz, char *base, Plan 
     w.vals1 = (int32_t *)take(4 * n);
     w.uvals0 = (int32_t *)take(4 * n);
     w.uvals1 = (int32_t *)take(4 * n);
-    const int64_t nblk = (n + kSortTile - 1) / kSortTile;
+    // radix histograms: the largest sort is the lookups' or the backward's
+    // pieces (at most min(nnz, sum n2) + 1 + g2p_slots_for(nnz) keys)
+    const int64_t pieces_keys = (nnz < h->sum_n[1] ? nnz : h->sum_n[1]) + 1 + g2p_slots_for(nnz);
+    const int64_t nblk = sort_blocks(n > pieces_keys ? n : pieces_keys);
     w.hist = (uint32_t *)take(4 * 256 * nblk);
     w.part = (uint64_t *)take(8 * (kScanBlocks + 1));
     w.tstart = (int32_t *)take(4 * (T + 1));

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(const int64_t *indices, int
 
 // -------------------------------------------------------- radix sort
 //
-// Stable LSD radix sort of (u32 key, i32 value), 8-bit digits.  Per pass:
+// Stable LSD radix sort of (u32 key, i32 value), digits of at most 8 bits.  Per pass:
 // per-block digit counts (upsweep), one exclusive scan of the digit-major
 // count matrix, then a downsweep that ranks keys inside the block without
 // breaking ties (each wave owns a contiguous quarter of the tile and keeps
@@ -110,22 +110,35 @@ __global__ __launch_bounds__(kThreads) void k_decode(const int64_t *indices, int
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 
+// Tile of this block for n keys: the tiles that hold keys are laid out XCD by
+// XCD (the blocks of one XCD take consecutive tiles), so the partial lines a
+// tile scatters into each digit's run meet those of its neighbour tiles in
+// one L2 (measured: 0.70 -> 0.65 ms for the 17.9M-key sort).  Blocks past the
+// keys keep their own (empty) tile.
+__device__ __forceinline__ int sort_tile(int64_t n)
+{
+    const int nt = (int)(((n + kSortTile - 1) / kSortTile + 7) & ~int64_t(7));
+    return (int)blockIdx.x < nt ? xcd_slot(blockIdx.x, nt) : (int)blockIdx.x;
+}
+
 __global__ __launch_bounds__(kThreads) void k_sort_upsweep(const uint32_t *keys, int64_t n_max,
-                                                           const int32_t *n_dev, int shift,
+                                                           const int32_t *n_dev, int shift, int dbits,
                                                            uint32_t *hist, int nblk)
 {
     __shared__ uint32_t cnt[kRadix];
     for (int i = threadIdx.x; i < kRadix; i += kThreads) cnt[i] = 0;
     __syncthreads();
     const int64_t nd = n_dev ? (int64_t)*n_dev : n_max, n = nd < n_max ? nd : n_max; // never past the buffers
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    const int tile = sort_tile(n);
+    const int64_t base = (int64_t)tile * kSortTile;
+    const uint32_t dmask = (1u << dbits) - 1u;
 #pragma unroll 4
     for (int j = 0; j < kSortItems; ++j) {
         int64_t i = base + j * kThreads + threadIdx.x;
-        if (i < n) atomicAdd(&cnt[(keys[i] >> shift) & (kRadix - 1)], 1u);
+        if (i < n) atomicAdd(&cnt[(keys[i] >> shift) & dmask], 1u);
     }
     __syncthreads();
-    for (int d = threadIdx.x; d < kRadix; d += kThreads) hist[(int64_t)d * nblk + blockIdx.x] = cnt[d];
+    for (int d = threadIdx.x; d <= (int)dmask; d += kThreads) hist[(int64_t)d * nblk + tile] = cnt[d];
 }
 
 struct HistScanOp {
@@ -137,6 +150,7 @@ struct HistScanOp {
     __device__ void total(uint64_t, int64_t) const {}
 };
 
+template <int DB>
 __global__ __launch_bounds__(kThreads) void k_sort_downsweep(const uint32_t *kin, const int32_t *vin,
                                                              uint32_t *kout, int32_t *vout,
                                                              int64_t n_max, const int32_t *n_dev,
@@ -155,10 +169,12 @@ __global__ __launch_bounds__(kThreads) void k_sort_downsweep(const uint32_t *kin
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t nd = n_dev ? (int64_t)*n_dev : n_max, n = nd < n_max ? nd : n_max; // never past the buffers
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    const int tile = sort_tile(n); // as in the upsweep
+    const int64_t base = (int64_t)tile * kSortTile;
     if (base >= n) return;
     for (int i = tid; i < W * kRadix; i += kThreads) (&wcnt[0][0])[i] = 0;
-    for (int d = tid; d < kRadix; d += kThreads) gbase[d] = hist[(int64_t)d * nblk + blockIdx.x];
+    constexpr uint32_t dmask = (1u << DB) - 1u;
+    for (int d = tid; d <= (int)dmask; d += kThreads) gbase[d] = hist[(int64_t)d * nblk + tile];
     __syncthreads();
 
     uint32_t key[ROUNDS];
@@ -170,10 +186,10 @@ __global__ __launch_bounds__(kThreads) void k_sort_downsweep(const uint32_t *kin
         const int64_t i = base + w * SUB + r * 64 + lane;
         const bool valid = i < n;
         const uint32_t k = valid ? kin[i] : 0xffffffffu;
-        const uint32_t d = (k >> shift) & (kRadix - 1);
+        const uint32_t d = (k >> shift) & dmask;
         uint64_t m = __ballot(valid);
 #pragma unroll
-        for (int b = 0; b < kRadixBits; ++b) {
+        for (int b = 0; b < DB; ++b) {
             const bool bit = (d >> b) & 1u;
             const uint64_t bb = __ballot(bit);
             m &= bit ? bb : ~bb;
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_sort_downsweep(const uint32_t *kin
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
         if (rank[r] != 0xffffffffu) {
-            const uint32_t d = (key[r] >> shift) & (kRadix - 1);
+            const uint32_t d = (key[r] >> shift) & dmask;
             const uint32_t pos = dstart[d] + wcnt[w][d] + rank[r];
             skey[pos] = key[r];
             sval[pos] = val[r];
@@ -224,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void k_sort_downsweep(const uint32_t *kin
     const int cnt = (int)((n - base) < kSortTile ? (n - base) : kSortTile);
     for (int j = tid; j < cnt; j += kThreads) {
         const uint32_t k = skey[j];
-        const uint32_t d = (k >> shift) & (kRadix - 1);
+        const uint32_t d = (k >> shift) & dmask;
         const uint32_t o = gbase[d] + (uint32_t)j - dstart[d];
         kout[o] = k;
         vout[o] = sval[j];
@@ -238,19 +254,32 @@ hipError_t radix_sort_pairs(const Plan &p, uint32_t *k0, int32_t *v0, uint32_t *
     static_assert(kRadix == kThreads, "downsweep assumes one digit per thread");
     *result_in_1 = false;
     if (n_max <= 0 || bits <= 0) return hipSuccess;
-    const int nblk = ceil_div(n_max, kSortTile);
+    const int nblk = (int)sort_blocks(n_max);
+    // passes of at most 8 bits, the bits spread evenly over them (28-bit keys:
+    // 4 x 7 bits, so a 4096-key tile meets 128 digits, 32 keys each on average,
+    // and writes whole 128-byte runs)
     const int passes = (bits + kRadixBits - 1) / kRadixBits;
+    const int wd = (bits + passes - 1) / passes;
     uint32_t *kin = k0, *kout = k1;
     int32_t *vin = v0, *vout = v1;
     for (int pass = 0; pass < passes; ++pass) {
-        const int shift = pass * kRadixBits;
+        const int shift = pass * wd, dbits = bits - shift < wd ? bits - shift : wd;
         hipLaunchKernelGGL(k_sort_upsweep, dim3(nblk), dim3(kThreads), 0, s, kin, n_max, n_dev,
-                           shift, p.ws.hist, nblk);
-        HistScanOp op{p.ws.hist, (int64_t)kRadix * nblk};
+                           shift, dbits, p.ws.hist, nblk);
+        HistScanOp op{p.ws.hist, ((int64_t)1 << dbits) * nblk};
         hipError_t e = run_scan(op, p.ws.part, scan_blocks(op.n), s);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_sort_downsweep, dim3(nblk), dim3(kThreads), 0, s, kin, vin, kout, vout,
-                           n_max, n_dev, shift, p.ws.hist, nblk);
+        switch (dbits) {
+#define TT_SORT_DOWN(DB)                                                                                   \
+    case DB:                                                                                               \
+        hipLaunchKernelGGL(k_sort_downsweep<DB>, dim3(nblk), dim3(kThreads), 0, s, kin, vin, kout, vout, n_max, \
+                           n_dev, shift, p.ws.hist, nblk);                                                 \
+        break;
+            TT_SORT_DOWN(1) TT_SORT_DOWN(2) TT_SORT_DOWN(3) TT_SORT_DOWN(4)
+            TT_SORT_DOWN(5) TT_SORT_DOWN(6) TT_SORT_DOWN(7) TT_SORT_DOWN(8)
+#undef TT_SORT_DOWN
+        default: return hipErrorInvalidValue;
+        }
         uint32_t *tk = kin;
         kin = kout;
         kout = tk;
@@ -439,16 +468,9 @@ struct TileOp {
         const int64_t len = ws.run_start[r + 1] - ws.run_start[r];
         return (uint64_t)((len + kUnitsPerTile - 1) / kUnitsPerTile);
     }
-    __device__ void emit(int64_t r, uint64_t excl, uint64_t v) const
-    {
-        const int32_t b = ws.run_start[r], len = ws.run_start[r + 1] - b;
-        ws.run_tile_start[r] = (int32_t)excl;
-        for (uint64_t j = 0; j < v; ++j) {
-            ws.tile_ubeg[excl + j] = b + (int32_t)j * kUnitsPerTile;
-            const int32_t rem = len - (int32_t)j * kUnitsPerTile;
-            ws.tile_nu[excl + j] = rem < kUnitsPerTile ? rem : kUnitsPerTile;
-        }
-    }
+    // the tiles themselves are filled by k_tile_fill, one thread per tile (a
+    // run of a hot (table, i2) holds hundreds of units)
+    __device__ void emit(int64_t r, uint64_t excl, uint64_t) const { ws.run_tile_start[r] = (int32_t)excl; }
     __device__ void total(uint64_t tot, int64_t nruns) const
     {
         ws.ctrl[CTRL_TILES] = (int32_t)tot;
@@ -505,70 +527,126 @@ struct ChunkOp {
     }
 };
 
+// First unit and unit count of every tile: tile i lies in the run r with
+// run_tile_start[r] <= i < run_tile_start[r + 1] and takes that run's units
+// 4j .. 4j + 3, j = i - run_tile_start[r].
+__global__ __launch_bounds__(kThreads) void k_tile_fill(Ws ws)
+{
+    const int64_t nt = ws.ctrl[CTRL_TILES], nr = ws.ctrl[CTRL_RUNS];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nt; i += stride) {
+        int64_t lo = 0, hi = nr; // last r < nr with run_tile_start[r] <= i
+        while (hi - lo > 1) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (ws.run_tile_start[mid] <= i) lo = mid;
+            else hi = mid;
+        }
+        const int32_t j = (int32_t)(i - ws.run_tile_start[lo]);
+        const int32_t b = ws.run_start[lo], len = ws.run_start[lo + 1] - b;
+        const int32_t rem = len - j * kUnitsPerTile;
+        ws.tile_ubeg[i] = b + j * kUnitsPerTile;
+        ws.tile_nu[i] = rem < kUnitsPerTile ? rem : kUnitsPerTile;
+    }
+}
+
 // One record per chunk: the digits, row ranges and per-row i3 the persistent
-// contraction kernel needs, gathered here in parallel.
+// contraction kernel needs, gathered here in parallel.  A block takes
+// kThreads chunks: (A) a thread per chunk works out its header (dwords
+// 0-31) into LDS, (B) the block fills the i3 digits of all its chunks with
+// independent loads, (C) each wave copies 64 records out, one coalesced
+// 256-byte store per record.
+constexpr int kRecStride = 65; // dwords per record in LDS (odd: rows spread over the banks)
+
 __global__ __launch_bounds__(kThreads) void k_chunk_records(const TableDesc *tab, int T, int S, Ws ws)
 {
+    static_assert(sizeof(ChunkRec) == 64 * sizeof(int32_t), "64 dwords per record");
+    __shared__ int32_t rl[kThreads * kRecStride];
+    __shared__ int32_t n3l[kThreads];
     const int64_t C = ws.ctrl[CTRL_CHUNKS];
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < C; c += stride) {
-        ChunkRec rec;
-        const int tile = ws.chunk_tile[c];
-        const int rbeg = ws.chunk_rbeg[c], rend = ws.chunk_rend[c];
-        const int ubeg = ws.tile_ubeg[tile], nu = ws.tile_nu[tile];
-        const int u0 = ws.uorder[ubeg];
-        const int t = segment_of(ws.tab_unit_start, T, u0);
-        const TableDesc &tb = tab[t];
-        rec.tile = tile;
-        rec.t = t;
-        rec.nu = nu;
-        rec.rbeg = rbeg;
-        rec.rend = rend;
-        rec.slot = ws.tile_slot[tile];
-        rec.i2 = ws.unit_prefix[u0] % tb.n2;
-        rec.cls = tb.cls;
-        rec.nch = (ws.tile_rows[tile] + S - 1) / S;
-        rec.ubeg = ubeg;
-        const int P = (tb.d3 > 0 && tb.d3 <= 16) ? 16 / tb.d3 : 1;
-        int off = 0, coff = 0;
-        rec.pstart[0] = 0;
-        for (int j = 0; j < 4; ++j) {
-            int i1 = 0, us = 0, cc = 0;
-            if (j < nu) {
-                const int u = ws.uorder[ubeg + j];
-                const int s0 = ws.unit_start[u], cnt = ws.unit_start[u + 1] - s0;
-                const int lo = rbeg > off ? rbeg : off;
-                const int hi = rend < off + cnt ? rend : off + cnt;
-                cc = hi > lo ? hi - lo : 0;
-                us = s0 + (lo - off);
-                i1 = ws.unit_prefix[u] / tb.n2;
-                off += cnt;
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int64_t cb = (int64_t)blockIdx.x * kThreads; cb < C; cb += (int64_t)gridDim.x * kThreads) {
+        // (A) header of chunk cb + tid
+        const int64_t c = cb + tid;
+        int32_t *r = rl + tid * kRecStride;
+        int rank = 4;
+        if (c < C) {
+            const int tile = ws.chunk_tile[c];
+            const int rbeg = ws.chunk_rbeg[c], rend = ws.chunk_rend[c];
+            const int ubeg = ws.tile_ubeg[tile], nu = ws.tile_nu[tile];
+            const int u0 = ws.uorder[ubeg];
+            const int t = segment_of(ws.tab_unit_start, T, u0);
+            const TableDesc &tb = tab[t];
+            const int P = (tb.d3 > 0 && tb.d3 <= 16) ? 16 / tb.d3 : 1;
+            r[0] = tile;
+            r[1] = t;
+            r[2] = nu;
+            r[3] = rbeg;
+            r[4] = rend;
+            r[5] = ws.tile_slot[tile];
+            r[6] = ws.unit_prefix[u0] % tb.n2;
+            r[7] = tb.cls;
+            r[30] = (ws.tile_rows[tile] + S - 1) / S;
+            r[31] = ubeg;
+            n3l[tid] = tb.n3;
+            int off = 0, coff = 0, ps = 0;
+            r[20] = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int i1 = 0, us = 0, cc = 0;
+                if (j < nu) {
+                    const int u = ws.uorder[ubeg + j];
+                    const int s0 = ws.unit_start[u], cnt = ws.unit_start[u + 1] - s0;
+                    const int lo = rbeg > off ? rbeg : off;
+                    const int hi = rend < off + cnt ? rend : off + cnt;
+                    cc = hi > lo ? hi - lo : 0;
+                    us = s0 + (lo - off);
+                    i1 = ws.unit_prefix[u] / tb.n2;
+                    off += cnt;
+                }
+                r[8 + j] = i1;
+                r[12 + j] = us;
+                r[16 + j] = cc;
+                r[25 + j] = coff;
+                coff += cc;
+                ps += (cc + P - 1) / P;
+                r[21 + j] = ps;
             }
-            rec.i1[j] = i1;
-            rec.ustart[j] = us;
-            rec.ccnt[j] = cc;
-            rec.rowoff[j] = coff;
-            for (int r = 0; r < cc && coff + r < kMaxChunkRows; ++r)
-                rec.i3[coff + r] = ws.uniq_row[us + r] % tb.n3;
-            coff += cc;
-            rec.pstart[j + 1] = rec.pstart[j] + (cc + P - 1) / P;
+            r[29] = coff;
+            rank = tb.cls < 0 ? 4 : tb.cls;
         }
-        rec.rowoff[4] = coff;
-        for (int r = coff; r < kMaxChunkRows; ++r) rec.i3[r] = 0;
-        ws.crec[c] = rec;
         // first chunk of each rank class (chunks are class-major; generic
         // tables rank 4, after the MFMA classes), found where the rank steps
         // up between neighbouring chunks; entry 5 is the chunk count
-        const int rank = tb.cls < 0 ? 4 : tb.cls;
-        int prev = __shfl_up(rank, 1, 64);
-        if ((threadIdx.x & 63) == 0 && c > 0) {
-            const int pt = segment_of(ws.tab_unit_start, T, ws.uorder[ws.tile_ubeg[ws.chunk_tile[c - 1]]]);
-            prev = tab[pt].cls < 0 ? 4 : tab[pt].cls;
+        int prev = __shfl_up(rank, 1, 64); // every lane active
+        if (c < C) {
+            if (lane == 0 && c > 0) {
+                const int pt = segment_of(ws.tab_unit_start, T, ws.uorder[ws.tile_ubeg[ws.chunk_tile[c - 1]]]);
+                prev = tab[pt].cls < 0 ? 4 : tab[pt].cls;
+            }
+            if (c == 0) prev = -1;
+            for (int q = prev + 1; q <= rank; ++q) ws.ctrl[CTRL_CLS_START + q] = (int32_t)c;
+            if (c == C - 1)
+                for (int q = rank + 1; q <= 5; ++q) ws.ctrl[CTRL_CLS_START + q] = (int32_t)C;
         }
-        if (c == 0) prev = -1;
-        for (int r = prev + 1; r <= rank; ++r) ws.ctrl[CTRL_CLS_START + r] = (int32_t)c;
-        if (c == C - 1)
-            for (int r = rank + 1; r <= 5; ++r) ws.ctrl[CTRL_CLS_START + r] = (int32_t)C;
+        __syncthreads();
+        // (B) i3 of row e % 32 of chunk e / 32, e = i * kThreads + tid (zeros past the chunk's rows)
+#pragma unroll 8
+        for (int i = 0; i < kMaxChunkRows; ++i) {
+            const int e = i * kThreads + tid, k = e >> 5, row = e & 31;
+            const int32_t *rk = rl + k * kRecStride;
+            int v = 0;
+            if (cb + k < C && row < rk[29]) {
+                const int j = (row >= rk[26]) + (row >= rk[27]) + (row >= rk[28]);
+                v = ws.uniq_row[rk[12 + j] + (row - rk[25 + j])] % n3l[k];
+            }
+            rl[k * kRecStride + 32 + row] = v;
+        }
+        __syncthreads();
+        // (C) wave w writes records w*64 .. w*64+63 of the block, one per store
+        const int w = tid >> 6;
+        for (int k = w * 64; k < w * 64 + 64 && cb + k < C; ++k)
+            reinterpret_cast<int32_t *>(&ws.crec[cb + k])[lane] = rl[k * kRecStride + lane];
+        __syncthreads();
     }
 }
 
@@ -657,6 +735,7 @@ hipError_t launch_grouping(const Plan &p, const int64_t *indices, const int64_t 
         TileOp top{ws};
         e = run_scan(top, ws.part, scan_blocks(nnz), s);
         if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_tile_fill, dim3(g), dim3(kThreads), 0, s, ws);
         ChunkOp cop{ws, p.chunk_rows};
         e = run_scan(cop, ws.part, scan_blocks(nnz), s);
         if (e != hipSuccess) return e;

@@ -20,6 +20,9 @@ constexpr int kThreads = 256;       // threads per block for every kernel
 constexpr int kScanBlocks = 4096;   // blocks of the 3-phase scans (at most)
 constexpr int kSortTile = 4096;     // keys per radix-sort block (256 threads x 16)
 constexpr int kSortItems = kSortTile / kThreads;
+// Radix-sort blocks (tiles) for n keys, a multiple of 8 so that tiles can be
+// laid out XCD by XCD.
+inline int64_t sort_blocks(int64_t n) { return ((n > 0 ? (n + kSortTile - 1) / kSortTile : 1) + 7) & ~int64_t(7); }
 constexpr int kMaxCkptSlots = 4096; // L2 checkpoint slots for split prefix tiles
 constexpr int kUnitsPerTile = 4;    // prefix units sharing (table, i2) per tile
 constexpr int kGuTask = 256;        // sorted lookup positions per gradient-gather task

@@ -88,13 +88,27 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T *total, T *smem)
 // Every block owns one contiguous range, so emit() sees elements in order per block.
 constexpr int kScanItems = 4;
 
-__device__ __forceinline__ void scan_range(int64_t n, int64_t *lo, int64_t *hi)
+// Position of block b in a grid of nb blocks when the blocks of one XCD
+// (b % 8 under the round-robin dispatch) take consecutive positions: the
+// x-th eighth of the positions goes to XCD x, so the scattered accesses that
+// follow a position range stay in one L2.  Identity unless nb is a multiple of 8.
+__device__ __forceinline__ int xcd_slot(int b, int nb)
+{
+    return (nb & 7) ? b : (b & 7) * (nb >> 3) + (b >> 3);
+}
+
+// Measured: XCD-affine scan ranges made the grouping's scans slower (their
+// scattered writes gained nothing, and ranges of a device-side count smaller
+// than the grid crowd onto few XCDs), so block b takes range b.
+__device__ __forceinline__ int scan_range(int64_t n, int64_t *lo, int64_t *hi)
 {
     const int64_t tile = (int64_t)kThreads * kScanItems;
     int64_t per = (n + gridDim.x - 1) / gridDim.x;
     per = (per + tile - 1) / tile * tile;
-    *lo = (int64_t)blockIdx.x * per;
+    const int v = blockIdx.x;
+    *lo = (int64_t)v * per;
     *hi = *lo + per < n ? *lo + per : n;
+    return v;
 }
 
 template <class Op>
@@ -103,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void scan_phase1(Op op, uint64_t *part)
     __shared__ uint64_t sm[kThreads / 64];
     const int64_t n = op.count();
     int64_t lo, hi;
-    scan_range(n, &lo, &hi);
+    const int v = scan_range(n, &lo, &hi);
     uint64_t s = 0;
     for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) s += op.value(i);
     s = wave_sum(s);
@@ -112,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void scan_phase1(Op op, uint64_t *part)
     if (threadIdx.x == 0) {
         uint64_t t = 0;
         for (int i = 0; i < kThreads / 64; ++i) t += sm[i];
-        part[blockIdx.x] = t;
+        part[v] = t;
     }
 }
 
@@ -156,8 +170,8 @@ __global__ __launch_bounds__(kThreads) void scan_phase3(Op op, const uint64_t *p
     __shared__ uint64_t sm[kThreads / 64];
     const int64_t n = op.count();
     int64_t lo, hi;
-    scan_range(n, &lo, &hi);
-    uint64_t carry = part[blockIdx.x];
+    const int v = scan_range(n, &lo, &hi);
+    uint64_t carry = part[v];
     for (int64_t base = lo; base < hi; base += (int64_t)kThreads * kScanItems) {
         uint64_t v[kScanItems];
         uint64_t ts = 0;
