@@ -910,7 +910,8 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
 #pragma unroll
                 for (int i = 0; i < NACC2; ++i) dacc2[i] = floatx4{0.f, 0.f, 0.f, 0.f};
                 cur_tile = rec.tile;
-                __syncthreads(); // C tile written
+                // with REUSE the tile's C was committed before the loop-top barrier
+                if constexpr (!REUSE) __syncthreads(); // C tile written
             }
             // ---- (2) rows of this chunk, in staged batches of rb rows (the first is
             // staged).  Wave (mb, rg) covers r2 block mb for every RG-th row of each
@@ -966,7 +967,10 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                         }
                     }
                     // (2b) P3_u[r2][j3] = sum_m2 C_g[m2][r2] g_u[m2][j3], P rows per output
-                    // tile, the row groups dealt round-robin over the row-group waves
+                    // tile, the row groups dealt round-robin over the row-group waves.
+                    // The output tile is (row, j3) x r2, so a lane holds 4 consecutive
+                    // j3 of one row (d3 >= 4) and 16 lanes write 16 consecutive r2:
+                    // whole 256-byte runs of P3_u
                     if (qa + r0 * P < qb) {
                         float ca[4];
 #pragma unroll
@@ -975,7 +979,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                             const float cv = Cs[g * CUNIT + m2 * CSTR + (okr ? r2 : 0)];
                             ca[s] = (m2 < D12 && okr) ? cv : 0.f;
                         }
-                        const int slot_r = li / d3, j3 = li - slot_r * d3;
+                        const int slot_r = li / d3, j3 = li - slot_r * d3; // A row of this lane
                         for (int qs = qa + r0 * P; qs < qb; qs += rs * P) {
                             const int cnt = qb - qs < P ? qb - qs : P;
                             const bool okb = slot_r < cnt;
@@ -984,22 +988,32 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                             for (int s = 0; s < 4; ++s) {
                                 const int m2 = kq * 4 + s;
                                 const float gv = Gs[(qs + (okb ? slot_r : 0) - sb) * GST + (m2 < D12 ? m2 : 0) * d3 + j3];
-                                acc = mfma4(ca[s], (okb && m2 < D12) ? gv : 0.f, acc);
+                                acc = mfma4((okb && m2 < D12) ? gv : 0.f, ca[s], acc);
                             }
-                            if (okb) {
-                                const int u = rec.ustart[g] + (qs + slot_r - rec.rowoff[g]);
-                                float *dst = P3t + (int64_t)u * R * d3 + j3;
-#pragma unroll
-                                for (int v = 0; v < 4; ++v) {
-                                    const int rr = bm * 16 + 4 * kq + v;
-                                    if (rr < R) dst[rr * d3] = acc[v];
+                            // lane (li, kq) holds output rows 4kq + v = (row, j3) of column r2
+                            if (okr) {
+                                const int64_t ub = rec.ustart[g] + (qs - rec.rowoff[g]);
+                                if (d3 >= 4) {
+                                    const int sr = (4 * kq) / d3, j0 = 4 * kq - sr * d3;
+                                    if (sr < cnt)
+                                        *reinterpret_cast<floatx4 *>(P3t + (ub + sr) * R * d3 + r2 * d3 + j0) = acc;
+                                } else {
+#pragma unroll 1
+                                    for (int v = 0; v < 4; ++v) {
+                                        const int sr = (4 * kq + v) / d3, jj = 4 * kq + v - sr * d3;
+                                        if (sr < cnt) P3t[(ub + sr) * R * d3 + r2 * d3 + jj] = acc[v];
+                                    }
                                 }
                             }
                         }
                     }
                 }
             }
-            __syncthreads(); // rows done: C and the staged rows are free
+            // rows done: C and the staged rows are free.  At rank 64 a tile's end
+            // needs no barrier here: every wave reads C only in the blocks of its
+            // own items, which its dC replaces, and the staged rows are next
+            // written after the barrier that publishes dC
+            if (kBal || !tile_end) __syncthreads();
             if (tile_end) {
                 if constexpr (!kBal) {
 #pragma unroll
@@ -1044,6 +1058,8 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                     }
                 }
                 __syncthreads();
+                constexpr int NRED = (MT * 256 + BT - 1) / BT; // (3) outputs per thread
+                float rsum[NRED];
                 // ---- (3) G1 partial of each unit: sum over the columns (j2, r2) of
                 // dC[(g,j1)][col] G2[r1][col].  A wave takes MTW r1 blocks over
                 // one of KG column groups (independent accumulator chains of
@@ -1092,15 +1108,29 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
 #pragma unroll
                         for (int v = 0; v < 4; ++v) red[((kg * MT + mt0 + m) * 4 + v) * 64 + lane] = acc[m][v];
                     __syncthreads();
-                    for (int e = tid; e < MT * 256; e += BT) {
-                        float sum = 0.f;
+                    // the group sums, in group order
+                    if constexpr (kBal) {
+                        for (int e = tid; e < MT * 256; e += BT) {
+                            float sum = 0.f;
 #pragma unroll
-                        for (int k = 0; k < KG; ++k) sum += red[k * MT * 256 + e];
-                        // e = (mt*4 + v)*64 + lane: row (g = lane/16, j1 = v), r1 = mt*16 + lane%16
-                        const int mt = e >> 8, v = (e >> 6) & 3, ln = e & 63;
-                        const int r1 = mt * 16 + (ln & 15), gg = ln >> 4;
-                        if (r1 < R && gg < nu && v < d1)
-                            ws.G1P[(int64_t)(rec.ubeg + gg) * a.g1stride + v * R + r1] = sum;
+                            for (int k = 0; k < KG; ++k) sum += red[k * MT * 256 + e];
+                            // e = (mt*4 + v)*64 + lane: row (g = lane/16, j1 = v), r1 = mt*16 + lane%16
+                            const int mt = e >> 8, v = (e >> 6) & 3, ln = e & 63;
+                            const int r1 = mt * 16 + (ln & 15), gg = ln >> 4;
+                            if (r1 < R && gg < nu && v < d1)
+                                ws.G1P[(int64_t)(rec.ubeg + gg) * a.g1stride + v * R + r1] = sum;
+                        }
+                    } else {
+                        // rank 64: stored after (4), whose MFMAs cover the LDS
+                        // latency (at lower ranks the registers held across (4) spill)
+#pragma unroll
+                        for (int i = 0; i < NRED; ++i) {
+                            const int e = tid + i * BT;
+                            float sum = 0.f;
+#pragma unroll
+                            for (int k = 0; k < KG; ++k) sum += red[k * MT * 256 + (e < MT * 256 ? e : 0)];
+                            rsum[i] = sum;
+                        }
                     }
                 }
                 // ---- (4) dG2 += G1^T dC over (g, j1)
@@ -1130,6 +1160,16 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
 #pragma unroll
                                 for (int s = 0; s < 4; ++s) g2acc[mt][j] = mfma4(ga[mt][s], bv[s], g2acc[mt][j]);
                         }
+                    }
+                }
+                if constexpr (!kBal) {
+#pragma unroll
+                    for (int i = 0; i < NRED; ++i) {
+                        const int e = tid + i * BT;
+                        const int mt = e >> 8, v = (e >> 6) & 3, ln = e & 63;
+                        const int r1 = mt * 16 + (ln & 15), gg = ln >> 4;
+                        if (e < MT * 256 && r1 < R && gg < nu && v < d1)
+                            ws.G1P[(int64_t)(rec.ubeg + gg) * a.g1stride + v * R + r1] = rsum[i];
                     }
                 }
                 __syncthreads(); // (3) partials read, G1s and dC read before they are replaced
