@@ -127,6 +127,8 @@ TRAFFIC_KERNELS = {  # (the training step runs one instantiation per rank)
     "k_contract_w<32,": ("fwd_r32", ["forward.hip", "internal.h"]),
     "k_contract_w<16,": ("fwd_r16", ["forward.hip", "internal.h"]),
     "k_pool<": ("pool", ["forward.hip", "internal.h"]),
+    "k_gu_gather": ("bwd_gather", ["backward.hip", "internal.h"]),
+    "k_sorted_meta": ("bwd_sorted_meta", ["backward.hip", "internal.h"]),
 }
 
 
