@@ -540,12 +540,18 @@ __global__ __launch_bounds__(kThreads) void k_g3_bounds(BwdArgs a, const uint32_
 // order, of their partials; zero when none.  Each (phase, element) thread
 // keeps kG3Acc interleaved partial sums over its rows, added in order, and
 // the phases are added in order: a fixed order with several loads in flight.
+// The slot's row ids are staged in LDS (one coalesced load), so a row's
+// partial is one global load; a stage holds a whole number of groups of
+// kG3Acc * rp rows, so no group straddles two stages and the order of the
+// sums does not depend on the staging.
 constexpr int kG3Acc = 8;
+constexpr int kG3Stage = kG3Acc * kThreads; // at least one group for any phase count
 
 __global__ __launch_bounds__(kThreads) void k_reduce_g3(BwdArgs a, const int32_t *order, int total_slots)
 {
     const Ws &ws = a.ws;
     __shared__ float part[kThreads];
+    __shared__ int32_t ord[kG3Stage];
     for (int slot = blockIdx.x; slot < total_slots; slot += gridDim.x) {
         int t = 0;
         while (t + 1 < a.T && a.tab[t + 1].i3_base <= (uint32_t)slot) ++t;
@@ -558,37 +564,48 @@ __global__ __launch_bounds__(kThreads) void k_reduce_g3(BwdArgs a, const int32_t
         const float *src = ws.P3 + ws.p3base[t];
         const int rp = per >= kThreads ? 1 : kThreads / per;
         const int ph = threadIdx.x / per < rp ? threadIdx.x / per : rp; // rp = idle
+        const int64_t stg = (int64_t)(kG3Stage / (kG3Acc * rp)) * (kG3Acc * rp); // rows per stage
         for (int e0 = 0; e0 < per; e0 += kThreads) {
             const int e = e0 + (rp == 1 ? threadIdx.x : threadIdx.x - ph * per);
-            float c = 0.f;
-            if (ph < rp && e < per) {
-                float acc[kG3Acc];
+            const bool act = ph < rp && e < per;
+            float acc[kG3Acc];
 #pragma unroll
-                for (int k = 0; k < kG3Acc; ++k) acc[k] = 0.f;
-                int64_t q = first + ph;
-                for (; q + (kG3Acc - 1) * rp < last; q += kG3Acc * rp) {
+            for (int k = 0; k < kG3Acc; ++k) acc[k] = 0.f;
+            int64_t q = first + ph;
+            for (int64_t b0 = first; b0 < last; b0 += stg) {
+                const int64_t b1 = b0 + stg < last ? b0 + stg : last;
+                __syncthreads(); // previous stage read
+                for (int i = threadIdx.x; i < b1 - b0; i += kThreads) ord[i] = order[b0 + i];
+                __syncthreads();
+                if (act) {
+                    for (; q + (kG3Acc - 1) * rp < b1; q += kG3Acc * rp) {
 #pragma unroll
-                    for (int k = 0; k < kG3Acc; ++k) acc[k] += src[(int64_t)order[q + k * rp] * per + e];
+                        for (int k = 0; k < kG3Acc; ++k) acc[k] += src[(int64_t)ord[q - b0 + k * rp] * per + e];
+                    }
+                    if (b1 == last) {
+#pragma unroll
+                        for (int k = 0; k < kG3Acc; ++k)
+                            if (q + k * rp < last) acc[k] += src[(int64_t)ord[q - b0 + k * rp] * per + e];
+                    }
                 }
-#pragma unroll
-                for (int k = 0; k < kG3Acc; ++k)
-                    if (q + k * rp < last) acc[k] += src[(int64_t)order[q + k * rp] * per + e];
-#pragma unroll
-                for (int k = 0; k < kG3Acc; ++k) c += acc[k];
             }
+            float c = 0.f;
+#pragma unroll
+            for (int k = 0; k < kG3Acc; ++k) c += acc[k];
             if (rp == 1) {
                 if (e < per) dst[e] = c;
             } else {
+                __syncthreads();
                 part[threadIdx.x] = c;
                 __syncthreads();
                 if (threadIdx.x < per) {
-                    float s = 0.f;
-                    for (int k = 0; k < rp; ++k) s += part[k * per + threadIdx.x];
-                    dst[threadIdx.x] = s;
+                    float sum = 0.f;
+                    for (int k = 0; k < rp; ++k) sum += part[k * per + threadIdx.x];
+                    dst[threadIdx.x] = sum;
                 }
-                __syncthreads();
             }
         }
+        __syncthreads();
     }
 }
 
