@@ -945,13 +945,19 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                     // (unit g, r2 block bm) of accumulator i, and the rows it takes
                     const int item = kBal ? 0 : w + NW * i;
                     const int g = kBal ? i : item / MT, bm = kBal ? mb : item % MT;
-                    const int r0 = kBal ? rg : 0, rs = kBal ? RG : 1;
+                    const int rs = kBal ? RG : 1;
                     if (item >= 4 * MT || g >= nu) continue;
                     const int r2 = bm * 16 + li;
                     const bool okr = r2 < R;
                     const int qa = sb > rec.rowoff[g] ? sb : rec.rowoff[g];
                     const int qe = rec.rowoff[g] + rec.ccnt[g];
                     const int qb = sb + n < qe ? sb + n : qe;
+                    // row-group wave rg takes the chunk's rows q = rg (mod RG) and its
+                    // output tiles t = rg (mod RG), counted over the whole chunk, so
+                    // the waves share the rows evenly across units (counting within
+                    // each unit gave the first wave a unit's odd row every time)
+                    const int r0 = kBal ? ((rg - qa) % RG + RG) % RG : 0;
+                    const int r0p = kBal ? ((rg - rec.pstart[g]) % RG + RG) % RG : 0;
                     // (2a) dC_g[m2][r2] += sum_j3 g_u[m2][j3] G3[i3_u][r2][j3]; with
                     // d3 = 4 (one k step per row) two rows per step into two chains
                     auto row_ops = [&](int q, int j0, float &av, float &bv) {
@@ -988,7 +994,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                     // The output tile is (row, j3) x r2, so a lane holds 4 consecutive
                     // j3 of one row (d3 >= 4) and 16 lanes write 16 consecutive r2:
                     // whole 256-byte runs of P3_u
-                    if (qa + r0 * P < qb) {
+                    if (qa + r0p * P < qb) {
                         float ca[4];
 #pragma unroll
                         for (int s = 0; s < 4; ++s) {
@@ -997,7 +1003,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                             ca[s] = (m2 < D12 && okr) ? cv : 0.f;
                         }
                         const int slot_r = li / d3, j3 = li - slot_r * d3; // A row of this lane
-                        for (int qs = qa + r0 * P; qs < qb; qs += rs * P) {
+                        for (int qs = qa + r0p * P; qs < qb; qs += rs * P) {
                             const int cnt = qb - qs < P ? qb - qs : P;
                             const bool okb = slot_r < cnt;
                             floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
