@@ -653,7 +653,7 @@ struct BwdLds {
     static constexpr int NW = CLS == 3 ? 8 : 4;                  // waves per block
     // float4 registers per thread that carry the next chunk's first rows while
     // this chunk computes (the rows of a 64-column table at chunk_rows 32)
-    static constexpr int PF = CLS == 3 ? 2 : CLS == 2 ? 6 : CLS == 1 ? 3 : 2;
+    static constexpr int PF = CLS == 3 ? 2 : CLS == 2 ? 6 : CLS == 1 ? 4 : 2;
 };
 
 // REUSE: the prefix tiles C come from the forward (Ws::Cg) instead of step (1).
@@ -757,6 +757,9 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
         }
         const int c4g = Dp >> 2, c4t = (d3 * R) >> 2, c4r = c4g + c4t; // float4 per staged row
         const int pf_cap = PF * BT / c4r;                                // rows the prefetch carries
+        // e / c4r as a multiply-high (exact for e, c4r < 2^16: e < 32 rows x c4r here)
+        const uint32_t c4m = (uint32_t)((0x100000000ull + (uint64_t)c4r - 1) / (uint64_t)c4r);
+        auto row_of = [&](int e) __attribute__((always_inline)) { return (int)__umulhi((uint32_t)e, c4m); };
         auto first_rows = [&](const ChunkRec &r) __attribute__((always_inline)) {
             const int n = r.rowoff[4] < rb ? r.rowoff[4] : rb;
             return n < pf_cap ? n : pf_cap;
@@ -764,7 +767,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
         // Stage rows q0 .. q0+n-1 of chunk r into the batch that starts at row sb.
         auto stage_rows = [&](const ChunkRec &r, int sb, int q0, int n) __attribute__((always_inline)) {
             for (int e = tid; e < n * c4r; e += BT) {
-                const int qq = e / c4r, rem = e - qq * c4r, q = q0 + qq;
+                const int qq = row_of(e), rem = e - qq * c4r, q = q0 + qq;
                 const int j = (q >= r.rowoff[1]) + (q >= r.rowoff[2]) + (q >= r.rowoff[3]); // unit of row q
                 if (rem < c4g) {
                     const int u = r.ustart[j] + (q - r.rowoff[j]);
@@ -795,7 +798,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
             for (int i = 0; i < PF; ++i) {
                 int e = tid + i * BT;
                 e = e < n * c4r ? e : 0;
-                const int q = e / c4r, rem = e - q * c4r;
+                const int q = row_of(e), rem = e - q * c4r;
                 const int j = (q >= r.rowoff[1]) + (q >= r.rowoff[2]) + (q >= r.rowoff[3]); // unit of row q
                 const floatx4 *src = rem < c4g
                     ? reinterpret_cast<const floatx4 *>(Et + (int64_t)(r.ustart[j] + (q - r.rowoff[j])) * Dp) + rem
@@ -826,7 +829,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
             for (int i = 0; i < PF; ++i) {
                 const int e = tid + i * BT;
                 if (e < n * c4r) {
-                    const int q = e / c4r, rem = e - q * c4r;
+                    const int q = row_of(e), rem = e - q * c4r;
                     if (rem < c4g) {
                         *reinterpret_cast<floatx4 *>(Gs + q * GST + 4 * rem) = pfv[i];
                     } else {
