@@ -723,7 +723,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
         // wave-uniform: the table data below become scalar loads
         const int t = __builtin_amdgcn_readfirstlane(recs[0].t), i2 = __builtin_amdgcn_readfirstlane(recs[0].i2);
         const auto &tb = kconst(a.tab)[t];
-        const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, D12 = d1 * d2, Dp = tb.Dp, P = 16 / d3;
+        const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, D12 = d1 * d2, Dp = tb.Dp, P = small_div(16, d3);
         const float *G1 = a.cores.g[t][0];
         const float *G3t = ws.g3t + tb.g3t_off;
         // per-table bases read once per run: a global load issued after this
@@ -1005,7 +1005,7 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                             const float cv = Cs[g * CUNIT + m2 * CSTR + (okr ? r2 : 0)];
                             ca[s] = (m2 < D12 && okr) ? cv : 0.f;
                         }
-                        const int slot_r = li / d3, j3 = li - slot_r * d3; // A row of this lane
+                        const int slot_r = small_div(li, d3), j3 = li - slot_r * d3; // A row of this lane
                         for (int qs = qa + r0p * P; qs < qb; qs += rs * P) {
                             const int cnt = qb - qs < P ? qb - qs : P;
                             const bool okb = slot_r < cnt;
@@ -1020,13 +1020,13 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
                             if (okr) {
                                 const int64_t ub = rec.ustart[g] + (qs - rec.rowoff[g]);
                                 if (d3 >= 4) {
-                                    const int sr = (4 * kq) / d3, j0 = 4 * kq - sr * d3;
+                                    const int sr = small_div(4 * kq, d3), j0 = 4 * kq - sr * d3;
                                     if (sr < cnt)
                                         *reinterpret_cast<floatx4 *>(P3t + (ub + sr) * R * d3 + r2 * d3 + j0) = acc;
                                 } else {
 #pragma unroll 1
                                     for (int v = 0; v < 4; ++v) {
-                                        const int sr = (4 * kq + v) / d3, jj = 4 * kq + v - sr * d3;
+                                        const int sr = small_div(4 * kq + v, d3), jj = 4 * kq + v - sr * d3;
                                         if (sr < cnt) P3t[(ub + sr) * R * d3 + r2 * d3 + jj] = acc[v];
                                     }
                                 }

@@ -226,9 +226,9 @@ __device__ __forceinline__ void load_b_piece(const FwdArgs &a, const ChunkRec &r
     const auto &tb = kconst(a.tab)[t];
     const int d3 = tb.d3;
     const int lane = threadIdx.x & 63, li = lane & 15, kq = lane >> 4;
-    const int slot = li / d3, j3 = li - slot * d3;
+    const int slot = small_div(li, d3), j3 = li - slot * d3;
     int j, rb, cnt;
-    chunk_piece(r, 16 / d3, e, j, rb, cnt);
+    chunk_piece(r, small_div(16, d3), e, j, rb, cnt);
     const bool ok = slot < cnt;
     const float *src = a.ws.g3t + tb.g3t_off + ((int64_t)r.i3[rb + (ok ? slot : 0)] * d3 + j3) * R + kq * KQ;
     if constexpr (KQ % 4 == 0) {
@@ -327,14 +327,14 @@ __device__ __forceinline__ void chunk_mfma(const FwdArgs &a, const ChunkRec &rec
     float *Et = a.ws.E + kconst(a.ws.ebase)[t];
     const int w = uni(threadIdx.x >> 6), lane = threadIdx.x & 63, li = lane & 15, kq = lane >> 4;
     const float *G2 = a.cores.g[t][1];
-    const int P = 16 / d3;
+    const int P = small_div(16, d3);
     // record fields that steer control flow, made wave-uniform: a branch on a
     // value the compiler takes as per-lane runs both sides under exec masks,
     // and the waits of one side then apply to the other
     const int tile = uni(rec.tile), nu = uni(rec.nu), i2 = uni(rec.i2), cslot = uni(rec.slot);
     const int rbeg = uni(rec.rbeg), nch = uni(rec.nch);
     const int np = uni(rec.pstart[nu]);
-    const int slot = li / d3, j3 = li - slot * d3;
+    const int slot = small_div(li, d3), j3 = li - slot * d3;
 
     // -------- prefix tile C_u = G1[i1_u] . G2[i2] for the (<= 4) units
     if (uni(lds_tile) != tile) {
@@ -730,7 +730,7 @@ __global__ __launch_bounds__(kThreads, FwdW<R>::OCC) void k_contract_w(FwdArgs a
         const int nch = fld(30), ubeg = fld(31);
         const int ps1 = fld(21), ps2 = fld(22), ps3 = fld(23), np = fld(20 + nu);
         const auto &tb = kconst(a.tab)[t];
-        const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, D12 = d1 * d2, Dp = tb.Dp, P = 16 / d3;
+        const int d1 = tb.d1, d2 = tb.d2, d3 = tb.d3, D12 = d1 * d2, Dp = tb.Dp, P = small_div(16, d3);
         if (tile != ctile) {
             // ---- prefix tile C_u = G1[i1_u] . G2[i2] for the tile's units
             bool have = false;
@@ -827,7 +827,7 @@ __global__ __launch_bounds__(kThreads, FwdW<R>::OCC) void k_contract_w(FwdArgs a
         // ---- rows: output tiles e = 0 .. np-1, NQ at a time
         float *Et = ws.E + kconst(ws.ebase)[t];
         const float *G3t = ws.g3t + tb.g3t_off;
-        const int slot = li / d3, j3l = li - slot * d3;
+        const int slot = small_div(li, d3), j3l = li - slot * d3;
         const int ro0 = fld(25), ro1 = fld(26), ro2 = fld(27), ro3 = fld(28);
         const int cc0 = fld(16), cc1 = fld(17), cc2 = fld(18), cc3 = fld(19);
         const int us0 = fld(12), us1 = fld(13), us2 = fld(14), us3 = fld(15);
@@ -892,13 +892,13 @@ __global__ __launch_bounds__(kThreads, FwdW<R>::OCC) void k_contract_w(FwdArgs a
                 const int us = sel(j, us0, us1, us2, us3) + (rb - sel(j, ro0, ro1, ro2, ro3));
                 if (li < D12) {
                     if (d3 == 4 || d3 == 8 || d3 == 16) {
-                        const int r4 = 4 * kq, sl = r4 / d3, jj = r4 - sl * d3;
+                        const int r4 = 4 * kq, sl = small_div(r4, d3), jj = r4 - sl * d3;
                         if (sl < cnt)
                             *reinterpret_cast<floatx4 *>(Et + (int64_t)(us + sl) * Dp + li * d3 + jj) = o;
                     } else {
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
-                            const int r = 4 * kq + v, sl = r / d3, jj = r - sl * d3;
+                            const int r = 4 * kq + v, sl = small_div(r, d3), jj = r - sl * d3;
                             if (sl < cnt) Et[(int64_t)(us + sl) * Dp + li * d3 + jj] = o[v];
                         }
                     }
@@ -1105,10 +1105,10 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
     // A operand of output tile e of record rv: the lane's G3t run of its row
     // (clamped to the tile's first row for padding lanes; their results are not stored)
     auto load_g3 = [&](int rv, int tv, int e, float (&gv)[KQ]) __attribute__((always_inline)) {
-        const int d3 = rl(tv, FT_D3), P = 16 / d3;
+        const int d3 = rl(tv, FT_D3), P = small_div(16, d3);
         int j, rb, cnt;
         rec_piece(rv, P, e, j, rb, cnt);
-        const int slot = li / d3, j3 = li - slot * d3;
+        const int slot = small_div(li, d3), j3 = li - slot * d3;
         const int i3 = __shfl(rv, RF_I3 + rb + (slot < cnt ? slot : 0), 64);
         const gfloatx4 *src = reinterpret_cast<const gfloatx4 *>(rl_ptr<const float>(tv, FT_G3T) +
                                                                  ((int64_t)i3 * d3 + j3) * R + kq * KQ);
@@ -1160,7 +1160,7 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
     auto rows_tile = [&](int rv, int tv, int e, float (&gv)[KQ], const float *Ct, bool reload, int rn, int tvn,
                          int en) __attribute__((always_inline)) {
         const int d1 = rl(tv, FT_D1), d2 = rl(tv, FT_D2), d3 = rl(tv, FT_D3), D12 = d1 * d2, Dp = rl(tv, FT_DP);
-        const int P = 16 / d3;
+        const int P = small_div(16, d3);
         int j, rb, cnt;
         rec_piece(rv, P, e, j, rb, cnt);
         const float4 *cb = reinterpret_cast<const float4 *>(Ct + j * CU + (li < D12 ? li : 0) * CSTR + kq * KQ);
@@ -1182,12 +1182,12 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
         gfloat *Et = rl_ptr<float>(tv, FT_E);
         if (li < D12) {
             if (d3 == 4 || d3 == 8 || d3 == 16) {
-                const int r4 = 4 * kq, sl = r4 / d3, jj = r4 - sl * d3;
+                const int r4 = 4 * kq, sl = small_div(r4, d3), jj = r4 - sl * d3;
                 if (sl < cnt) *reinterpret_cast<gfloatx4 *>(Et + (int64_t)(us + sl) * Dp + li * d3 + jj) = o;
             } else {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int rr4 = 4 * kq + v, sl = rr4 / d3, jj = rr4 - sl * d3;
+                    const int rr4 = 4 * kq + v, sl = small_div(rr4, d3), jj = rr4 - sl * d3;
                     if (sl < cnt) Et[(int64_t)(us + sl) * Dp + li * d3 + jj] = o[v];
                 }
             }

@@ -39,6 +39,16 @@ __device__ __forceinline__ void block_stat_write(BlockStat *slot, int64_t t0, in
     slot[blockIdx.x] = r;
 }
 
+// x / d for 0 <= x < 1024 and 1 <= d <= 16 (row slots and columns of an output
+// tile against d3), through one reciprocal and one multiply instead of the
+// ~40-instruction integer division: floor((x + 0.5) / d) keeps a margin of
+// 0.5 / d >= 1/32 on both sides of the true quotient, far above the relative
+// error (< 2^-21) of the reciprocal and the product.
+__device__ __forceinline__ int small_div(int x, int d)
+{
+    return (int)(((float)x + 0.5f) * __builtin_amdgcn_rcpf((float)d));
+}
+
 // Inclusive scan inside one 64-lane wave.
 template <class T>
 __device__ __forceinline__ T wave_inclusive_scan(T x)
