@@ -155,6 +155,20 @@ __device__ __forceinline__ int claim_start(int32_t *heads, int me, int vi, int n
     return raw;
 }
 
+// claim_start() without its wait: lane 0's atomic stays in flight in the
+// returned register until claim_finish() reads it at the caller's next claim,
+// so a claim costs no round trip of its own.  The atomic is an increment that
+// wraps at 2^32 - 1 (heads stay far below): the compiler turns a single-lane
+// atomicAdd into a wave-aggregated one whose result it reads back at once,
+// which is the very wait this avoids.
+__device__ __forceinline__ int claim_issue(int32_t *heads, int me, int vi, int nb, int nvict)
+{
+    int raw = 0x7fffffff;
+    if (vi < nvict && (threadIdx.x & 63) == 0)
+        raw = (int)atomicInc(reinterpret_cast<unsigned *>(&heads[victim_of(me, vi, nb) * kHeadPad]), 0xffffffffu);
+    return raw;
+}
+
 // heads / chunk ids are offset by `base`, the class's first chunk; C = its count
 __device__ int claim_finish(int32_t *heads, int base, int me, int &vi, int nb, int nvict, int64_t C, int raw,
                             int &steals)
@@ -1025,17 +1039,21 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
     __shared__ ChunkRec rr[NR];
     __shared__ int cid[NR], s_ck[NR];
     __shared__ long long s_t0;
+    // the table records, read from LDS in the chunk loop (a table change then
+    // waits for an LDS read, not for the wave's memory operations in flight)
+    __shared__ int s_tab[kMaxTables * 16];
     const int lane = threadIdx.x & 63, w = uni(threadIdx.x >> 6), li = lane & 15, kq = lane >> 4;
     if (threadIdx.x == 0) s_t0 = wall_clock64();
     const Ws &ws = a.ws;
-    const FwdTab *ftab = ws.ftab;
+    for (int e = threadIdx.x; e < a.T * 16; e += kThreads) s_tab[e] = reinterpret_cast<const int *>(ws.ftab)[e];
     const int nb = gridDim.x, me = blockIdx.x;
     const int base = ws.ctrl[CTRL_CLS_START + CLS];
     const int64_t C = ws.ctrl[CTRL_CLS_START + CLS + 1] - base;
     const int cend = base + range_begin(me + 1, C, nb); // end of the static range
     int32_t *heads = ws.heads + CLS * heads_stride * kHeadPad;
     const int nvict = STEAL ? nb >> 3 : 1;
-    int vi = 0, steals = 0, hits = 0, misses = 0, nwork = 0, nrows = 0, raw = 0x7fffffff;
+    int vi = 0, steals = 0, hits = 0, misses = 0, nwork = 0, nrows = 0;
+    int raw = 0x7fffffff; // wave 0 (stealing): the claim in flight
     int cstat = base + range_begin(me, C, nb); // next chunk of the static range
     const bool l2 = a.sched == kSchedStealL2;
 
@@ -1046,7 +1064,7 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
             return cstat < cend ? cstat++ : -1;
         } else {
             const int got = claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals);
-            raw = got >= 0 ? uni(claim_start(heads, me, vi, nb, nvict)) : 0x7fffffff;
+            raw = claim_issue(heads, me, got >= 0 ? vi : nvict, nb, nvict);
             return got;
         }
     };
@@ -1060,7 +1078,7 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
     };
     int pre = 0, pre_id = -1; // wave 0: the record of the next ring entry to write, and its chunk
     if (w == 0) {
-        if constexpr (STEAL) raw = uni(claim_start(heads, me, vi, nb, nvict));
+        if constexpr (STEAL) raw = claim_issue(heads, me, vi, nb, nvict);
         int prev = 0;
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
@@ -1070,7 +1088,7 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
             if (lane == 0) cid[i] = id;
         }
         pre_id = prev >= 0 ? next_id() : -1;
-        if (pre_id >= 0) pre = reinterpret_cast<const int *>(&ws.crec[pre_id])[lane];
+        pre = reinterpret_cast<const int *>(&ws.crec[pre_id >= 0 ? pre_id : 0])[lane];
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1086,7 +1104,7 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
     float anext[KQ], g3p[PQ][KQ];
 
     // table records, one dword per lane; reloaded only when the table changes
-    auto tab_load = [&](int t) { return reinterpret_cast<const int *>(ftab + t)[lane & 15]; };
+    auto tab_load = [&](int t) { return s_tab[(t >= 0 && t < a.T ? t : 0) * 16 + (lane & 15)]; };
     // G1 slices of record rv's units: lane (kq, li) holds row li = (unit, j1), K run kq*KQ ..
     auto load_a = [&](int rv, int tv, float (&av)[KQ]) __attribute__((always_inline)) {
         const int nu = rl(rv, RF_NU), d1 = rl(tv, FT_D1), g = li >> 2, j1 = li & 3;
@@ -1154,30 +1172,35 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
                     if (v < d1) Ct[kq * CU + (v * d2 + w) * CSTR + 16 * j + li] = acc[j][v];
         }
     };
-    // (2): output tile e of record rv from slot Ct with operands gv; when
-    // reload, gv then takes the operands of output tile en of record rn
-    // before the E row is stored
-    auto rows_tile = [&](int rv, int tv, int e, float (&gv)[KQ], const float *Ct, bool reload, int rn, int tvn,
+    // (2): output tile e of record rv from slot Ct with operands gv, when
+    // act; then gv always takes the operands of output tile en of record rn
+    // (a valid tile, also where they go unused), before the E row is stored.
+    // The reload is unconditional: a load in a branch leaves its registers to
+    // be copied at the join, and the copy waits for the load to arrive.
+    auto rows_tile = [&](int rv, int tv, int e, bool act, float (&gv)[KQ], const float *Ct, int rn, int tvn,
                          int en) __attribute__((always_inline)) {
         const int d1 = rl(tv, FT_D1), d2 = rl(tv, FT_D2), d3 = rl(tv, FT_D3), D12 = d1 * d2, Dp = rl(tv, FT_DP);
         const int P = small_div(16, d3);
         int j, rb, cnt;
         rec_piece(rv, P, e, j, rb, cnt);
-        const float4 *cb = reinterpret_cast<const float4 *>(Ct + j * CU + (li < D12 ? li : 0) * CSTR + kq * KQ);
         floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (act) {
+            const float4 *cb = reinterpret_cast<const float4 *>(Ct + j * CU + (li < D12 ? li : 0) * CSTR + kq * KQ);
 #pragma unroll
-        for (int s4 = 0; s4 < KQ / 4; ++s4) {
-            const float4 v = cb[s4];
-            o = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[4 * s4], v.x, o, 0, 0, 0);
-            o = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[4 * s4 + 1], v.y, o, 0, 0, 0);
-            o = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[4 * s4 + 2], v.z, o, 0, 0, 0);
-            o = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[4 * s4 + 3], v.w, o, 0, 0, 0);
+            for (int s4 = 0; s4 < KQ / 4; ++s4) {
+                const float4 v = cb[s4];
+                o = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[4 * s4], v.x, o, 0, 0, 0);
+                o = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[4 * s4 + 1], v.y, o, 0, 0, 0);
+                o = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[4 * s4 + 2], v.z, o, 0, 0, 0);
+                o = __builtin_amdgcn_mfma_f32_16x16x4f32(gv[4 * s4 + 3], v.w, o, 0, 0, 0);
+            }
         }
         // keep the reload after this tile's products and before its store:
         // the products wait only for operands that arrived an iteration ago
         __builtin_amdgcn_sched_barrier(0);
-        if (reload) load_g3(rn, tvn, en, gv);
+        load_g3(rn, tvn, en, gv);
         __builtin_amdgcn_sched_barrier(0);
+        if (!act) return;
         const int us = __builtin_amdgcn_readlane(rv, RF_USTART + j) + (rb - __builtin_amdgcn_readlane(rv, RF_ROWOFF + j));
         gfloat *Et = rl_ptr<float>(tv, FT_E);
         if (li < D12) {
@@ -1246,14 +1269,6 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
         const int tile = rl(recv, RF_TILE), ntile = rl(nrecv, RF_TILE);
         const bool has_next = cn >= 0, next_new = has_next && ntile != tile;
         const int ck_next = uni(s_ck[i1]);
-        // wave 0: ring entry k+3 (its record loaded an iteration ago) goes to the
-        // slot of entry k-2; the record of entry k+4 is loaded now
-        if (w == 0) {
-            if (pre_id >= 0) reinterpret_cast<int *>(&rr[i3r])[lane] = pre;
-            if (lane == 0) cid[i3r] = pre_id;
-            pre_id = pre_id >= 0 ? next_id() : -1;
-            if (pre_id >= 0) pre = reinterpret_cast<const int *>(&ws.crec[pre_id])[lane];
-        }
         // table record of entry k+2 (the same table as entry k+1 nearly always)
         int tv2 = tvn;
         if (c2 >= 0 && rl(r2v, RF_T) != rl(nrecv, RF_T)) tv2 = tab_load(rl(r2v, RF_T));
@@ -1274,18 +1289,19 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
             const int np = __builtin_amdgcn_readlane(recv, RF_PSTART + rl(recv, RF_NU));
             const int npn = has_next ? __builtin_amdgcn_readlane(nrecv, RF_PSTART + rl(nrecv, RF_NU)) : 0;
             const float *Ct = Cs[cs];
+            // the operands reloaded for the next chunk's tiles (a chunk has at
+            // least one tile; past the last chunk the block's own last tile)
+            const int rn = has_next ? nrecv : recv, tn = has_next ? tvn : tv, nlast = has_next ? npn - 1 : np - 1;
 #pragma unroll
             for (int jq = 0; jq < PQ; ++jq) {
                 const int e = w + 4 * jq;
-                const int en = e < npn ? e : (npn > 0 ? npn - 1 : 0);
-                if (e < np) rows_tile(recv, tv, e, g3p[jq], Ct, has_next, nrecv, tvn, en);
-                else if (has_next) load_g3(nrecv, tvn, en, g3p[jq]);
+                rows_tile(recv, tv, e < np ? e : np - 1, e < np, g3p[jq], Ct, rn, tn, e < nlast ? e : nlast);
             }
             // tiles past the prefetched ones (chunks of more than 4 * PQ output tiles)
             for (int e = w + 4 * PQ; e < np; e += 4) {
                 float gv[KQ];
                 load_g3(recv, tv, e, gv);
-                rows_tile(recv, tv, e, gv, Ct, false, recv, tv, 0);
+                rows_tile(recv, tv, e, true, gv, Ct, recv, tv, e);
             }
         }
         const int rbeg = rl(recv, RF_RBEG), nu = rl(recv, RF_NU);
@@ -1309,6 +1325,19 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
                     dst[e] = *reinterpret_cast<const floatx4 *>(Cs[cs] + j * CU + m * CSTR + 4 * c4);
                 }
             }
+        }
+        // wave 0: ring entry k+3 (its record loaded an iteration ago) goes to the
+        // slot of entry k-2; the next chunk is claimed and the record of entry
+        // k+4 loaded.  Both loads are unconditional (past the last chunk, chunk
+        // 0's record under id -1, never used): a load in a branch is waited for
+        // at the join.  Placed after the rows' operand reloads, so that on
+        // every path the record and the claim issued an iteration ago are
+        // older than those reloads and no wait here covers them.
+        if (w == 0) {
+            reinterpret_cast<int *>(&rr[i3r])[lane] = pre;
+            if (lane == 0) cid[i3r] = pre_id;
+            pre_id = pre_id >= 0 ? next_id() : -1;
+            pre = reinterpret_cast<const int *>(&ws.crec[pre_id >= 0 ? pre_id : 0])[lane];
         }
         if (threadIdx.x == 0) {
             ++nwork;
