@@ -148,6 +148,22 @@ __device__ void g3t_copy(const FwdArgs &a)
 // drained, probes the next 64 victims in parallel and retries.  Every chunk is
 // handed out exactly once (heads only grow) and the loop ends once every
 // victim has been seen drained.
+//
+// The current victim (its order index vi, block v and range end, chunk ids
+// offset by the class's first chunk), recomputed only when vi changes: the
+// victim order and the range bounds take integer divisions by run-time
+// values, some hundred scalar instructions per claim otherwise.
+struct Victim {
+    int vi = -1, v = 0, end = 0;
+    __device__ __forceinline__ void at(int nvi, int me, int nb, int base, int64_t C)
+    {
+        if (nvi == vi) return;
+        vi = nvi;
+        v = victim_of(me, nvi, nb);
+        end = base + range_begin(v + 1, C, nb);
+    }
+};
+
 __device__ __forceinline__ int claim_start(int32_t *heads, int me, int vi, int nb, int nvict)
 {
     int raw = 0x7fffffff;
@@ -161,25 +177,27 @@ __device__ __forceinline__ int claim_start(int32_t *heads, int me, int vi, int n
 // wraps at 2^32 - 1 (heads stay far below): the compiler turns a single-lane
 // atomicAdd into a wave-aggregated one whose result it reads back at once,
 // which is the very wait this avoids.
-__device__ __forceinline__ int claim_issue(int32_t *heads, int me, int vi, int nb, int nvict)
+// The victim is cv (cv.vi == vi whenever vi < nvict).
+__device__ __forceinline__ int claim_issue(int32_t *heads, const Victim &cv, int vi, int nvict)
 {
     int raw = 0x7fffffff;
     if (vi < nvict && (threadIdx.x & 63) == 0)
-        raw = (int)atomicInc(reinterpret_cast<unsigned *>(&heads[victim_of(me, vi, nb) * kHeadPad]), 0xffffffffu);
+        raw = (int)atomicInc(reinterpret_cast<unsigned *>(&heads[cv.v * kHeadPad]), 0xffffffffu);
     return raw;
 }
 
 // heads / chunk ids are offset by `base`, the class's first chunk; C = its count
+// (cv caches the current victim; it is left at the victim of the chunk returned)
 __device__ int claim_finish(int32_t *heads, int base, int me, int &vi, int nb, int nvict, int64_t C, int raw,
-                            int &steals)
+                            int &steals, Victim &cv)
 {
     const int lane = threadIdx.x & 63;
     int res;
     for (;;) {
         const bool live = vi < nvict;
-        const int v = victim_of(me, live ? vi : 0, nb);
+        if (live) cv.at(vi, me, nb, base, C);
         int got = -1;
-        if ((lane == 0) & live & (raw < base + range_begin(v + 1, C, nb))) got = raw;
+        if ((lane == 0) & live & (raw < cv.end)) got = raw;
         got = uni(got); // lane 0's value (every lane of the wave is active here)
         if (got >= 0) {
             steals += vi != 0;
@@ -599,13 +617,14 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
 #pragma unroll
     for (int i = 0; i < FwdCfg<R>::BREG; ++i) breg[i] = 0.f;
     int bkey = -1, lds_tile = -1, vi = 0, steals = 0, hits = 0, misses = 0, nwork = 0, nrows = 0;
+    Victim cv;
     // wave 0 runs the claims two chunks ahead: chunk c+2 is claimed while
     // chunk c runs, and the record of chunk c+1 is loaded at the end of chunk c-1
     int pre = 0, raw = 0x7fffffff, c2w = -1;
     if (w == 0) {
-        const int c0 = claim_finish(heads, base, me, vi, nb, nvict, C, claim_start(heads, me, vi, nb, nvict), steals);
+        const int c0 = claim_finish(heads, base, me, vi, nb, nvict, C, claim_start(heads, me, vi, nb, nvict), steals, cv);
         const int c1 = c0 < 0 ? -1
-                              : claim_finish(heads, base, me, vi, nb, nvict, C, claim_start(heads, me, vi, nb, nvict), steals);
+                              : claim_finish(heads, base, me, vi, nb, nvict, C, claim_start(heads, me, vi, nb, nvict), steals, cv);
         if (c0 >= 0) reinterpret_cast<int *>(&rbuf[0])[lane] = reinterpret_cast<const int *>(&ws.crec[c0])[lane];
         if (c1 >= 0) {
             pre = reinterpret_cast<const int *>(&ws.crec[c1])[lane];
@@ -633,7 +652,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
             // claim of chunk c+2 (started at the end of chunk c-1)
             auto mid = [&]() {
                 if (w == 0) {
-                    c2w = cn < 0 ? -1 : claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals);
+                    c2w = cn < 0 ? -1 : claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals, cv);
                     if (lane == 0) s_next2 = c2w;
                 }
             };
@@ -664,6 +683,46 @@ __global__ __launch_bounds__(kThreads, FwdCfg<R>::OCC) void k_contract(FwdArgs a
         if (hits) atomicAdd(&ws.ctrl[CTRL_CKPT_HIT], hits);
         if (misses) atomicAdd(&ws.ctrl[CTRL_CKPT_MISS], misses);
     }
+}
+
+// Wave-uniform reads of values held one per lane (a record or a table entry).
+__device__ __forceinline__ int rl(int v, int k) { return __builtin_amdgcn_readlane(v, k); }
+typedef __attribute__((address_space(1))) float gfloat;
+typedef __attribute__((address_space(1))) floatx4 gfloatx4;
+// A global-memory pointer held as two dwords (lanes k, k+1): the address space
+// is stated so that accesses through it are global (vector memory counter
+// only), not flat ones, which the LDS counter also tracks.
+template <class T> __device__ __forceinline__ __attribute__((address_space(1))) T *rl_ptr(int v, int k)
+{
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane(v, k), hi = (uint32_t)__builtin_amdgcn_readlane(v, k + 1);
+    return reinterpret_cast<__attribute__((address_space(1))) T *>(lo | (hi << 32));
+}
+// ChunkRec fields as dword indices
+enum RecField { RF_TILE = 0, RF_T = 1, RF_NU = 2, RF_RBEG = 3, RF_REND = 4, RF_SLOT = 5, RF_I2 = 6, RF_I1 = 8,
+                RF_USTART = 12, RF_CCNT = 16, RF_PSTART = 20, RF_ROWOFF = 25, RF_NCH = 30, RF_UBEG = 31,
+                RF_I3 = 32 };
+static_assert(offsetof(ChunkRec, i1) == 4 * RF_I1 && offsetof(ChunkRec, ustart) == 4 * RF_USTART &&
+                  offsetof(ChunkRec, ccnt) == 4 * RF_CCNT && offsetof(ChunkRec, pstart) == 4 * RF_PSTART &&
+                  offsetof(ChunkRec, rowoff) == 4 * RF_ROWOFF && offsetof(ChunkRec, nch) == 4 * RF_NCH &&
+                  offsetof(ChunkRec, ubeg) == 4 * RF_UBEG && offsetof(ChunkRec, i3) == 4 * RF_I3,
+              "record field indices");
+static_assert(offsetof(FwdTab, g2) == 4 * FT_G2 && offsetof(FwdTab, g3t) == 4 * FT_G3T &&
+                  offsetof(FwdTab, E) == 4 * FT_E && offsetof(FwdTab, Cg) == 4 * FT_CG &&
+                  offsetof(FwdTab, d1) == 4 * FT_D1 && offsetof(FwdTab, i2_base) == 4 * FT_I2BASE &&
+                  offsetof(FwdTab, Dp) == 4 * FT_DP,
+              "table field indices");
+
+// Output tile e of a chunk (record rv, one dword per lane): unit j, first row
+// in chunk numbering rb, rows cnt (P rows per output tile).  Wave-uniform.
+__device__ __forceinline__ void rec_piece(int rv, int P, int e, int &j, int &rb, int &cnt)
+{
+    const int ps1 = rl(rv, RF_PSTART + 1), ps2 = rl(rv, RF_PSTART + 2), ps3 = rl(rv, RF_PSTART + 3);
+    j = (e >= ps1) + (e >= ps2) + (e >= ps3);
+    const int ps = j == 0 ? 0 : j == 1 ? ps1 : j == 2 ? ps2 : ps3;
+    const int ro = __builtin_amdgcn_readlane(rv, RF_ROWOFF + j);
+    rb = ro + (e - ps) * P;
+    const int rem = ro + __builtin_amdgcn_readlane(rv, RF_CCNT + j) - rb;
+    cnt = rem < P ? rem : P;
 }
 
 // ---------------------------------------------------------------------------
@@ -701,7 +760,7 @@ template <int R> constexpr int fwd_workers_per_cu() { return FwdW<R>::OCC * (kTh
 static_assert(fwd_workers_per_cu<8>() <= kMaxClsOcc && fwd_workers_per_cu<16>() <= kMaxClsOcc &&
               fwd_workers_per_cu<32>() <= kMaxClsOcc, "one queue head per worker");
 
-template <int R, bool KEEP>
+template <int R, bool KEEP, bool STEAL>
 __global__ __launch_bounds__(kThreads, FwdW<R>::OCC) void k_contract_w(FwdArgs a, int heads_stride)
 {
     using L = FwdW<R>;
@@ -723,21 +782,41 @@ __global__ __launch_bounds__(kThreads, FwdW<R>::OCC) void k_contract_w(FwdArgs a
     const int base = ws.ctrl[CTRL_CLS_START + CLS];
     const int64_t C = ws.ctrl[CTRL_CLS_START + CLS + 1] - base;
     int32_t *heads = ws.heads + CLS * heads_stride * kHeadPad;
-    const int nvict = a.sched == kSchedStatic ? 1 : nb >> 3;
+    const int nvict = STEAL ? nb >> 3 : 1;
     int vi = 0, steals = 0, hits = 0, misses = 0, nwork = 0, nrows = 0;
     float breg[L::BREG];
 #pragma unroll
     for (int i = 0; i < L::BREG; ++i) breg[i] = 0.f;
     int bkey = -1, ctile = -1;
-    // claims run one chunk ahead: chunk c+1 is claimed (and its record loaded)
-    // while chunk c runs
-    int c = claim_finish(heads, base, me, vi, nb, nvict, C, claim_start(heads, me, vi, nb, nvict), steals);
-    int rec = c >= 0 ? reinterpret_cast<const int *>(&ws.crec[c])[lane] : 0;
-    int raw = c >= 0 ? uni(claim_start(heads, me, vi, nb, nvict)) : 0x7fffffff;
+    Victim cv;
+    int cstat = base + range_begin(me, C, nb); // next chunk of the static range
+    const int cend = base + range_begin(me + 1, C, nb);
+    int raw = 0x7fffffff; // stealing: the claim in flight
+    // next chunk of this wave: its static range in order (no atomics), or in
+    // the stealing modes a claim from the workers of its XCD, the claim of the
+    // chunk after it left in flight
+    auto next_id = [&]() -> int {
+        if constexpr (!STEAL) {
+            return cstat < cend ? cstat++ : -1;
+        } else {
+            const int got = claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals, cv);
+            raw = claim_issue(heads, cv, got >= 0 ? vi : nvict, nvict);
+            return got;
+        }
+    };
+    if constexpr (STEAL) {
+        cv.at(0, me, nb, base, C);
+        raw = claim_issue(heads, cv, 0, nvict);
+    }
+    // the next chunk is known (and its record loaded) while chunk c runs; the
+    // record load is unconditional (past the last chunk chunk 0's, never
+    // used): a load in a branch leaves its register to be copied at the join,
+    // and the copy waits for the load
+    int c = next_id();
+    int rec = reinterpret_cast<const int *>(&ws.crec[c >= 0 ? c : 0])[lane];
     while (c >= 0) {
-        const int cn = claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals);
-        const int recn = cn >= 0 ? reinterpret_cast<const int *>(&ws.crec[cn])[lane] : 0;
-        if (cn >= 0) raw = uni(claim_start(heads, me, vi, nb, nvict));
+        const int cn = next_id();
+        const int recn = reinterpret_cast<const int *>(&ws.crec[cn >= 0 ? cn : 0])[lane];
         // record fields (ChunkRec, one dword per lane), wave-uniform
         auto fld = [&](int i) { return __builtin_amdgcn_readlane(rec, i); };
         const int tile = fld(0), t = fld(1), nu = fld(2), rbeg = fld(3), cslot = fld(5), i2 = fld(6);
@@ -986,46 +1065,6 @@ struct FwdT {
     static constexpr int PQ = R == 64 ? 3 : 2;  // output tiles per wave whose operands are prefetched
 };
 
-// Wave-uniform reads of values held one per lane (a record or a table entry).
-__device__ __forceinline__ int rl(int v, int k) { return __builtin_amdgcn_readlane(v, k); }
-typedef __attribute__((address_space(1))) float gfloat;
-typedef __attribute__((address_space(1))) floatx4 gfloatx4;
-// A global-memory pointer held as two dwords (lanes k, k+1): the address space
-// is stated so that accesses through it are global (vector memory counter
-// only), not flat ones, which the LDS counter also tracks.
-template <class T> __device__ __forceinline__ __attribute__((address_space(1))) T *rl_ptr(int v, int k)
-{
-    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane(v, k), hi = (uint32_t)__builtin_amdgcn_readlane(v, k + 1);
-    return reinterpret_cast<__attribute__((address_space(1))) T *>(lo | (hi << 32));
-}
-// ChunkRec fields as dword indices
-enum RecField { RF_TILE = 0, RF_T = 1, RF_NU = 2, RF_RBEG = 3, RF_REND = 4, RF_SLOT = 5, RF_I2 = 6, RF_I1 = 8,
-                RF_USTART = 12, RF_CCNT = 16, RF_PSTART = 20, RF_ROWOFF = 25, RF_NCH = 30, RF_UBEG = 31,
-                RF_I3 = 32 };
-static_assert(offsetof(ChunkRec, i1) == 4 * RF_I1 && offsetof(ChunkRec, ustart) == 4 * RF_USTART &&
-                  offsetof(ChunkRec, ccnt) == 4 * RF_CCNT && offsetof(ChunkRec, pstart) == 4 * RF_PSTART &&
-                  offsetof(ChunkRec, rowoff) == 4 * RF_ROWOFF && offsetof(ChunkRec, nch) == 4 * RF_NCH &&
-                  offsetof(ChunkRec, ubeg) == 4 * RF_UBEG && offsetof(ChunkRec, i3) == 4 * RF_I3,
-              "record field indices");
-static_assert(offsetof(FwdTab, g2) == 4 * FT_G2 && offsetof(FwdTab, g3t) == 4 * FT_G3T &&
-                  offsetof(FwdTab, E) == 4 * FT_E && offsetof(FwdTab, Cg) == 4 * FT_CG &&
-                  offsetof(FwdTab, d1) == 4 * FT_D1 && offsetof(FwdTab, i2_base) == 4 * FT_I2BASE &&
-                  offsetof(FwdTab, Dp) == 4 * FT_DP,
-              "table field indices");
-
-// Output tile e of a chunk (record rv, one dword per lane): unit j, first row
-// in chunk numbering rb, rows cnt (P rows per output tile).  Wave-uniform.
-__device__ __forceinline__ void rec_piece(int rv, int P, int e, int &j, int &rb, int &cnt)
-{
-    const int ps1 = rl(rv, RF_PSTART + 1), ps2 = rl(rv, RF_PSTART + 2), ps3 = rl(rv, RF_PSTART + 3);
-    j = (e >= ps1) + (e >= ps2) + (e >= ps3);
-    const int ps = j == 0 ? 0 : j == 1 ? ps1 : j == 2 ? ps2 : ps3;
-    const int ro = __builtin_amdgcn_readlane(rv, RF_ROWOFF + j);
-    rb = ro + (e - ps) * P;
-    const int rem = ro + __builtin_amdgcn_readlane(rv, RF_CCNT + j) - rb;
-    cnt = rem < P ? rem : P;
-}
-
 template <int R, bool KEEP, bool STEAL>
 __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a, int heads_stride)
 {
@@ -1054,6 +1093,7 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
     const int nvict = STEAL ? nb >> 3 : 1;
     int vi = 0, steals = 0, hits = 0, misses = 0, nwork = 0, nrows = 0;
     int raw = 0x7fffffff; // wave 0 (stealing): the claim in flight
+    Victim cv;
     int cstat = base + range_begin(me, C, nb); // next chunk of the static range
     const bool l2 = a.sched == kSchedStealL2;
 
@@ -1063,8 +1103,8 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
         if constexpr (!STEAL) {
             return cstat < cend ? cstat++ : -1;
         } else {
-            const int got = claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals);
-            raw = claim_issue(heads, me, got >= 0 ? vi : nvict, nb, nvict);
+            const int got = claim_finish(heads, base, me, vi, nb, nvict, C, raw, steals, cv);
+            raw = claim_issue(heads, cv, got >= 0 ? vi : nvict, nvict);
             return got;
         }
     };
@@ -1078,7 +1118,10 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
     };
     int pre = 0, pre_id = -1; // wave 0: the record of the next ring entry to write, and its chunk
     if (w == 0) {
-        if constexpr (STEAL) raw = claim_issue(heads, me, vi, nb, nvict);
+        if constexpr (STEAL) {
+            cv.at(vi, me, nb, base, C);
+            raw = claim_issue(heads, cv, vi, nvict);
+        }
         int prev = 0;
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
@@ -1121,15 +1164,18 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
         }
     };
     // A operand of output tile e of record rv: the lane's G3t run of its row
-    // (clamped to the tile's first row for padding lanes; their results are not stored)
-    auto load_g3 = [&](int rv, int tv, int e, float (&gv)[KQ]) __attribute__((always_inline)) {
+    // (clamped to the tile's first row for padding lanes; their results are not
+    // stored), as an offset in floats from the table's G3t
+    auto g3_off = [&](int rv, int tv, int e) __attribute__((always_inline)) -> int {
         const int d3 = rl(tv, FT_D3), P = small_div(16, d3);
         int j, rb, cnt;
         rec_piece(rv, P, e, j, rb, cnt);
         const int slot = small_div(li, d3), j3 = li - slot * d3;
         const int i3 = __shfl(rv, RF_I3 + rb + (slot < cnt ? slot : 0), 64);
-        const gfloatx4 *src = reinterpret_cast<const gfloatx4 *>(rl_ptr<const float>(tv, FT_G3T) +
-                                                                 ((int64_t)i3 * d3 + j3) * R + kq * KQ);
+        return (i3 * d3 + j3) * R + kq * KQ;
+    };
+    auto load_g3_at = [&](const gfloat *src0, float (&gv)[KQ]) __attribute__((always_inline)) {
+        const gfloatx4 *src = reinterpret_cast<const gfloatx4 *>(src0);
 #pragma unroll
         for (int s4 = 0; s4 < KQ / 4; ++s4) {
             const floatx4 v = src[s4];
@@ -1138,6 +1184,9 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
             gv[4 * s4 + 2] = v[2];
             gv[4 * s4 + 3] = v[3];
         }
+    };
+    auto load_g3 = [&](int rv, int tv, int e, float (&gv)[KQ]) __attribute__((always_inline)) {
+        load_g3_at(rl_ptr<const float>(tv, FT_G3T) + g3_off(rv, tv, e), gv);
     };
     // (1): C of record rv's tile into slot Ct, wave w the columns of j2 = w
     auto compute_c = [&](int rv, int tv, const float (&av)[KQ], float *Ct) __attribute__((always_inline)) {
@@ -1173,12 +1222,12 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
         }
     };
     // (2): output tile e of record rv from slot Ct with operands gv, when
-    // act; then gv always takes the operands of output tile en of record rn
-    // (a valid tile, also where they go unused), before the E row is stored.
-    // The reload is unconditional: a load in a branch leaves its registers to
-    // be copied at the join, and the copy waits for the load to arrive.
-    auto rows_tile = [&](int rv, int tv, int e, bool act, float (&gv)[KQ], const float *Ct, int rn, int tvn,
-                         int en) __attribute__((always_inline)) {
+    // act; then gv always takes the operands at nsrc (a valid tile, also
+    // where they go unused), before the E row is stored.  The reload is
+    // unconditional: a load in a branch leaves its registers to be copied at
+    // the join, and the copy waits for the load to arrive.
+    auto rows_tile = [&](int rv, int tv, int e, bool act, float (&gv)[KQ], const float *Ct,
+                         const gfloat *nsrc) __attribute__((always_inline)) {
         const int d1 = rl(tv, FT_D1), d2 = rl(tv, FT_D2), d3 = rl(tv, FT_D3), D12 = d1 * d2, Dp = rl(tv, FT_DP);
         const int P = small_div(16, d3);
         int j, rb, cnt;
@@ -1198,7 +1247,7 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
         // keep the reload after this tile's products and before its store:
         // the products wait only for operands that arrived an iteration ago
         __builtin_amdgcn_sched_barrier(0);
-        load_g3(rn, tvn, en, gv);
+        load_g3_at(nsrc, gv);
         __builtin_amdgcn_sched_barrier(0);
         if (!act) return;
         const int us = __builtin_amdgcn_readlane(rv, RF_USTART + j) + (rb - __builtin_amdgcn_readlane(rv, RF_ROWOFF + j));
@@ -1292,16 +1341,26 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
             // the operands reloaded for the next chunk's tiles (a chunk has at
             // least one tile; past the last chunk the block's own last tile)
             const int rn = has_next ? nrecv : recv, tn = has_next ? tvn : tv, nlast = has_next ? npn - 1 : np - 1;
+            // the reloads' sources first, as independent chains the compiler
+            // interleaves (behind each tile's products they ran one by one)
+            const gfloat *G3n = rl_ptr<const float>(tn, FT_G3T);
+            int noff[PQ];
 #pragma unroll
             for (int jq = 0; jq < PQ; ++jq) {
                 const int e = w + 4 * jq;
-                rows_tile(recv, tv, e < np ? e : np - 1, e < np, g3p[jq], Ct, rn, tn, e < nlast ? e : nlast);
+                noff[jq] = g3_off(rn, tn, e < nlast ? e : nlast);
+            }
+#pragma unroll
+            for (int jq = 0; jq < PQ; ++jq) {
+                const int e = w + 4 * jq;
+                rows_tile(recv, tv, e < np ? e : np - 1, e < np, g3p[jq], Ct, G3n + noff[jq]);
             }
             // tiles past the prefetched ones (chunks of more than 4 * PQ output tiles)
             for (int e = w + 4 * PQ; e < np; e += 4) {
                 float gv[KQ];
                 load_g3(recv, tv, e, gv);
-                rows_tile(recv, tv, e, true, gv, Ct, recv, tv, e);
+                const gfloat *src = rl_ptr<const float>(tv, FT_G3T) + g3_off(recv, tv, e);
+                rows_tile(recv, tv, e, true, gv, Ct, src);
             }
         }
         const int rbeg = rl(recv, RF_RBEG), nu = rl(recv, RF_NU);
@@ -1613,11 +1672,13 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
                     default: TT_FWD_CLASS(64, false, true); break;
                     }
                 } else if (c < 3) {
-#define TT_FWD_WAVE(RR, KK) hipLaunchKernelGGL((k_contract_w<RR, KK>), dim3(p.num_blocks * FwdW<RR>::OCC), block, 0, s, ac, hs)
-                    if (c == 0) TT_FWD_WAVE(8, false);
-                    else if (c == 1) TT_FWD_WAVE(16, false);
-                    else if (p.keep_c) TT_FWD_WAVE(32, true);
-                    else TT_FWD_WAVE(32, false);
+#define TT_FWD_WAVE(RR, KK, SS) hipLaunchKernelGGL((k_contract_w<RR, KK, SS>), dim3(p.num_blocks * FwdW<RR>::OCC), block, 0, s, ac, hs)
+#define TT_FWD_WAVES(RR, KK) if (ac.sched != kSchedStatic) TT_FWD_WAVE(RR, KK, true); else TT_FWD_WAVE(RR, KK, false)
+                    if (c == 0) TT_FWD_WAVES(8, false);
+                    else if (c == 1) TT_FWD_WAVES(16, false);
+                    else if (p.keep_c) TT_FWD_WAVES(32, true);
+                    else TT_FWD_WAVES(32, false);
+#undef TT_FWD_WAVES
 #undef TT_FWD_WAVE
                 } else {
                     // keeping C for the backward: the block-cooperative kernel, which
