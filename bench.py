@@ -123,7 +123,7 @@ TRAFFIC_KERNELS = {  # (the training step runs one instantiation per rank)
     "k_bwd_class<64,": ("bwd_r64", ["backward.hip", "internal.h"]),
     "k_bwd_class<32,": ("bwd_r32", ["backward.hip", "internal.h"]),
     "k_bwd_class<16,": ("bwd_r16", ["backward.hip", "internal.h"]),
-    "k_contract<64,": ("fwd_r64", ["forward.hip", "internal.h"]),
+    "k_contract_t<64,": ("fwd_r64", ["forward.hip", "internal.h"]),
     "k_contract_w<32,": ("fwd_r32", ["forward.hip", "internal.h"]),
     "k_contract_w<16,": ("fwd_r16", ["forward.hip", "internal.h"]),
     "k_pool<": ("pool", ["forward.hip", "internal.h"]),
@@ -170,7 +170,7 @@ def write_traffic(d):
     print(json.dumps(out, indent=1, sort_keys=True))
 
 
-COUNTER_KERNELS = (("k_contract_w<16", "fwd_r16"), ("k_contract_w<32", "fwd_r32"), ("k_contract<64", "fwd_r64"),
+COUNTER_KERNELS = (("k_contract_w<16", "fwd_r16"), ("k_contract_w<32", "fwd_r32"), ("k_contract_t<64", "fwd_r64"),
                    ("k_bwd_class<16", "bwd_r16"), ("k_bwd_class<32", "bwd_r32"), ("k_bwd_class<64", "bwd_r64"),
                    ("k_pool<", "pool"), ("k_gu_gather", "bwd_gather"))
 
@@ -186,9 +186,14 @@ def write_counters(d, trace_csv=None):
     import csv
 
     vals = {}
-    for sub in ("lds", "mfma", "busy"):  # busy/ (optional): SQ_BUSY_CU_CYCLES, GRBM_GUI_ACTIVE, OccupancyPercent
+    # busy/ (optional): SQ_BUSY_CU_CYCLES, GRBM_GUI_ACTIVE, OccupancyPercent;
+    # stallA/, stallB/ (optional): the sequencer's wave-cycle counters (where
+    # the waves' time goes: issuing each instruction type, waiting on
+    # s_waitcnt / barriers, waiting for an issue slot) and the matrix-core busy
+    # cycles
+    for sub in ("lds", "mfma", "busy", "stallA", "stallB"):
         path = os.path.join(d, sub, "run_counter_collection.csv")
-        if sub == "busy" and not os.path.exists(path):
+        if sub not in ("lds", "mfma") and not os.path.exists(path):
             continue
         with open(path) as f:
             for r in csv.DictReader(f):
@@ -222,6 +227,22 @@ def write_counters(d, trace_csv=None):
                      "mfma_util_pct": avg(sym, "MfmaUtil"), "mfma_f32_flops": fl,
                      "launch_ms": t * 1e3 if t else None,
                      "mfma_issued_tflops": fl / t / 1e12 if (fl and t) else None})
+        wc = avg(sym, "SQ_WAVE_CYCLES")
+        if wc:
+            # fractions of the waves' resident cycles
+            for key, ctr in (("wait_any", "SQ_WAIT_ANY"), ("wait_issue", "SQ_WAIT_INST_ANY"),
+                             ("active_any", "SQ_ACTIVE_INST_ANY"), ("active_valu", "SQ_ACTIVE_INST_VALU"),
+                             ("active_salu", "SQ_ACTIVE_INST_SCA"), ("active_lds", "SQ_ACTIVE_INST_LDS"),
+                             ("active_vmem", "SQ_ACTIVE_INST_VMEM"), ("active_misc", "SQ_ACTIVE_INST_MISC"),
+                             ("wait_lds_issue", "SQ_WAIT_INST_LDS")):
+                v = avg(sym, ctr)
+                rows[-1]["frac_" + key] = v / wc if v is not None else None
+            mb, gui2 = avg(sym, "SQ_VALU_MFMA_BUSY_CYCLES"), avg(sym, "GRBM_GUI_ACTIVE")
+            # matrix-core busy cycles over (GPU-active cycles per XCD x 1024 SIMDs)
+            rows[-1]["mfma_busy_pct_sq"] = 100.0 * mb / (gui2 / 8 * 1024) if (mb and gui2) else None
+            for key, ctr in (("insts_mfma", "SQ_INSTS_MFMA"), ("insts_vmem", "SQ_INSTS_VMEM"),
+                             ("insts_lds", "SQ_INSTS_LDS"), ("insts_salu", "SQ_INSTS_SALU")):
+                rows[-1][key] = avg(sym, ctr)
     print(json.dumps(rows, indent=1))
     return rows
 

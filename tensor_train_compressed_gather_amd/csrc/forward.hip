@@ -1650,7 +1650,7 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
         // the tile-pipelined kernel; fused pooling: blocks of k_contract)
         ClassGrid cg;
         const int wpc[4] = {fwd_workers_per_cu<8>(), fwd_workers_per_cu<16>(), fwd_workers_per_cu<32>(),
-                            p.keep_c ? kClsOcc[3] : FwdT<64>::OCC};
+                            FwdT<64>::OCC};
         for (int c = 0; c < 4; ++c) cg.nb[c] = p.num_blocks * (!fused ? wpc[c] : kClsOcc[c]);
         const int hs = p.num_blocks * kMaxClsOcc;
         if (p.force_generic) hipLaunchKernelGGL(k_queue_init, dim3(1), dim3(kThreads), 0, s, a, cg, hs, 0);
@@ -1681,14 +1681,16 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
 #undef TT_FWD_WAVES
 #undef TT_FWD_WAVE
                 } else {
-                    // keeping C for the backward: the block-cooperative kernel, which
-                    // writes C with a fixed count of stores per chunk (measured faster
-                    // with the extra stores: 1.15 against 1.24 ms on the 26-table step)
+                    // the tile-pipelined block kernel, also when it keeps C for the
+                    // backward (measured on the 26-table training step: 0.97 ms
+                    // against 1.10 for the block-cooperative kernel k_contract)
                     const bool steal = ac.sched != kSchedStatic;
-#define TT_FWD_TILE(RR, SS) hipLaunchKernelGGL((k_contract_t<RR, false, SS>), dim3(p.num_blocks * FwdT<RR>::OCC), block, 0, s, ac, hs)
-                    if (p.keep_c) TT_FWD_CLASS(64, true, false);
-                    else if (steal) TT_FWD_TILE(64, true);
-                    else TT_FWD_TILE(64, false);
+#define TT_FWD_TILE(RR, KK, SS) hipLaunchKernelGGL((k_contract_t<RR, KK, SS>), dim3(p.num_blocks * FwdT<RR>::OCC), block, 0, s, ac, hs)
+                    if (p.keep_c) {
+                        if (steal) TT_FWD_TILE(64, true, true);
+                        else TT_FWD_TILE(64, true, false);
+                    } else if (steal) TT_FWD_TILE(64, false, true);
+                    else TT_FWD_TILE(64, false, false);
 #undef TT_FWD_TILE
                 }
 #undef TT_FWD_CLASS
