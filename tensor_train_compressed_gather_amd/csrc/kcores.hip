@@ -63,12 +63,19 @@ struct KLevOp {
 };
 
 // Level m (2 <= m <= K-1): V_m[g] = V_{m-1}[parent] . G_{m-1}[i_{m-1}], one
-// wave per group; V_1 is the core slice G_0[i_0] itself.  The lanes take 64
-// output columns (j, r) at a time and up to 8 rows p: the core slice is read
-// coalesced straight from L2 (a core is small and shared by many groups), the
-// parent's entries are wave-uniform and come through scalar loads.  No LDS,
-// so many waves per SIMD hide the load latency.
+// wave per group; V_1 is the core slice G_0[i_0] itself.  When the output's
+// columns (j, r) come in whole 16s the product runs on the matrix cores as
+// O^T = G^T . V^T: v_mfma_f32_16x16x4_f32 with A = 16 columns of the core
+// slice (read coalesced straight from L2: a core is small and shared by many
+// groups), B = the parent's rows p (up to 16 per pass; fewer rows leave part
+// of the tile empty), K = the shared rank Rin four at a time, so each lane
+// ends with four consecutive output columns of one row p.  Other shapes take
+// the FMA form: the lanes over 64 output columns at a time and up to 8 rows p,
+// the parent's entries wave-uniform through scalar loads.  No LDS, so many
+// waves per SIMD hide the load latency.
 constexpr int kKRowBlk = 8;
+constexpr int kKTiles = 8; // 16-column output tiles a wave accumulates at once
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kKLastP = 32, kKLastD = 8; // register fast path of the last level's dV
 __global__ __launch_bounds__(kThreads) void k_klevel(KArgs a, int m)
 {
@@ -97,6 +104,46 @@ __global__ __launch_bounds__(kThreads) void k_klevel(KArgs a, int m)
         const float *gsl = a.cores.g[t * K + c] + ic * (int64_t)Rin * dk * Rout; // [Rin][dk * Rout]
         float *out = a.kp.V[m] + g * a.kp.smax[m];                            // [P][dk * Rout]
         const int cols = dk * Rout;
+        if (cols % 16 == 0) {
+            const int li = lane & 15, kq = lane >> 4;
+            for (int pb = 0; pb < P; pb += 16) {
+                const int p = pb + li;
+                const bool okp = p < P;
+                const float *vrow = par + (int64_t)(okp ? p : 0) * Rin; // B: V[p][q]
+                for (int cb = 0; cb < cols; cb += 16 * kKTiles) {
+                    const int nt = (cols - cb) / 16 < kKTiles ? (cols - cb) / 16 : kKTiles;
+                    floatx4 acc[kKTiles];
+#pragma unroll
+                    for (int t = 0; t < kKTiles; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    for (int q0 = 0; q0 < Rin; q0 += 4) {
+                        const int q = q0 + kq;
+                        const bool okq = q < Rin;
+                        const float vb = vrow[okq ? q : 0];
+                        const float bv = (okp && okq) ? vb : 0.f;
+                        const float *grow = gsl + (int64_t)(okq ? q : 0) * cols + cb + li; // A: G[q][col]
+#pragma unroll
+                        for (int t = 0; t < kKTiles; ++t) {
+                            if (t < nt) {
+                                const float ga = grow[16 * t];
+                                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(okq ? ga : 0.f, bv, acc[t], 0, 0, 0);
+                            }
+                        }
+                    }
+                    // lane (kq, li) holds row p, columns cb + 16t + 4kq .. +3
+                    if (okp) {
+                        float *orow = out + (int64_t)p * cols + cb + 4 * kq;
+#pragma unroll
+                        for (int t = 0; t < kKTiles; ++t) {
+                            if (t < nt) {
+#pragma unroll
+                                for (int v = 0; v < 4; ++v) orow[16 * t + v] = acc[t][v];
+                            }
+                        }
+                    }
+                }
+            }
+            continue;
+        }
         for (int c0 = 0; c0 < cols; c0 += 64) {
             const int jr = c0 + lane;
             const bool ok = jr < cols;
