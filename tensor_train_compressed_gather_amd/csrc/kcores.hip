@@ -74,7 +74,6 @@ struct KLevOp {
 // the parent's entries wave-uniform through scalar loads.  No LDS, so many
 // waves per SIMD hide the load latency.
 constexpr int kKRowBlk = 8;
-constexpr int kKTiles = 8; // 16-column output tiles a wave accumulates at once
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kKLastP = 32, kKLastD = 8; // register fast path of the last level's dV
 __global__ __launch_bounds__(kThreads) void k_klevel(KArgs a, int m)
@@ -105,39 +104,58 @@ __global__ __launch_bounds__(kThreads) void k_klevel(KArgs a, int m)
         float *out = a.kp.V[m] + g * a.kp.smax[m];                            // [P][dk * Rout]
         const int cols = dk * Rout;
         if (cols % 16 == 0) {
+            // Tile c of a 64-column block takes the columns cb + 4i + c (i = the
+            // tile row), so lane li loads one float4 G[q][cb + 4li .. +3] for four
+            // tiles, and after the products holds, over the tiles c and its
+            // outputs v, the 16 consecutive columns cb + 16kq + 4v + c of row p.
             const int li = lane & 15, kq = lane >> 4;
             for (int pb = 0; pb < P; pb += 16) {
                 const int p = pb + li;
                 const bool okp = p < P;
                 const float *vrow = par + (int64_t)(okp ? p : 0) * Rin; // B: V[p][q]
-                for (int cb = 0; cb < cols; cb += 16 * kKTiles) {
-                    const int nt = (cols - cb) / 16 < kKTiles ? (cols - cb) / 16 : kKTiles;
-                    floatx4 acc[kKTiles];
+                for (int cb = 0; cb < cols; cb += 64) {
+                    const bool full = cols - cb >= 64; // else a 16-, 32- or 48-column rest
+                    const int nt = full ? 4 : (cols - cb) / 16;
+                    floatx4 acc[4];
 #pragma unroll
-                    for (int t = 0; t < kKTiles; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    for (int c4 = 0; c4 < 4; ++c4) acc[c4] = floatx4{0.f, 0.f, 0.f, 0.f};
                     for (int q0 = 0; q0 < Rin; q0 += 4) {
                         const int q = q0 + kq;
                         const bool okq = q < Rin;
                         const float vb = vrow[okq ? q : 0];
                         const float bv = (okp && okq) ? vb : 0.f;
-                        const float *grow = gsl + (int64_t)(okq ? q : 0) * cols + cb + li; // A: G[q][col]
+                        const float *grow = gsl + (int64_t)(okq ? q : 0) * cols + cb;
+                        float ga[4];
+                        if (full) {
+                            const float4 g4 = *reinterpret_cast<const float4 *>(grow + 4 * li);
+                            ga[0] = g4.x;
+                            ga[1] = g4.y;
+                            ga[2] = g4.z;
+                            ga[3] = g4.w;
+                        } else {
+                            // the rest block: tile c takes the columns cb + 16c + i
 #pragma unroll
-                        for (int t = 0; t < kKTiles; ++t) {
-                            if (t < nt) {
-                                const float ga = grow[16 * t];
-                                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(okq ? ga : 0.f, bv, acc[t], 0, 0, 0);
-                            }
+                            for (int c4 = 0; c4 < 4; ++c4) ga[c4] = grow[16 * (c4 < nt ? c4 : 0) + li];
                         }
+#pragma unroll
+                        for (int c4 = 0; c4 < 4; ++c4)
+                            if (c4 < nt) acc[c4] = __builtin_amdgcn_mfma_f32_16x16x4f32(okq ? ga[c4] : 0.f, bv, acc[c4], 0, 0, 0);
                     }
-                    // lane (kq, li) holds row p, columns cb + 16t + 4kq .. +3
                     if (okp) {
-                        float *orow = out + (int64_t)p * cols + cb + 4 * kq;
+                        float *orow = out + (int64_t)p * cols + cb;
+                        if (full) {
+                            // columns 16kq + 4v + c
 #pragma unroll
-                        for (int t = 0; t < kKTiles; ++t) {
-                            if (t < nt) {
+                            for (int v = 0; v < 4; ++v)
 #pragma unroll
-                                for (int v = 0; v < 4; ++v) orow[16 * t + v] = acc[t][v];
-                            }
+                                for (int c4 = 0; c4 < 4; ++c4) orow[16 * kq + 4 * v + c4] = acc[c4][v];
+                        } else {
+                            // columns 16c + 4kq + v
+#pragma unroll
+                            for (int c4 = 0; c4 < 4; ++c4)
+                                if (c4 < nt)
+#pragma unroll
+                                    for (int v = 0; v < 4; ++v) orow[16 * c4 + 4 * kq + v] = acc[c4][v];
                         }
                     }
                 }
