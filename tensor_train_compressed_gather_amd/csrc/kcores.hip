@@ -248,6 +248,86 @@ __global__ __launch_bounds__(kThreads) void k_kb_last(KArgs a)
         const float *GK = a.cores.g[t * K + K - 1];                // [n][Rin][dk]
         const float *Et = ws.E + kconst(ws.ebase)[t];             // g_u rows, stride Dp
         float *dV = a.kp.dV[m] + g * a.kp.smax[m];
+        const uint32_t nk = (uint32_t)kt.n[K - 1];
+        if (dk % 4 == 0 && 16 % dk == 0 && P <= 32 && Rin <= 32) {
+            // Matrix cores.  dV = sum over the rows u and j of g_u[p][j] G_u[q][j]:
+            // output tiles (p block, q block), K = (u, j) four j at a time.
+            // PK_u[q][j] = sum_p V[p][q] g_u[p][j]: 16 / dk rows stacked as the
+            // tile rows (row slot, j), the columns q, K = p four at a time.
+            const int li = lane & 15, kq = lane >> 4;
+            const int npt = (P + 15) / 16, nqt = (Rin + 15) / 16;
+            floatx4 acc[2][2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) acc[i][k] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int u = u0; u < u1; ++u) {
+                const float *gu = Et + (int64_t)u * Dp;
+                const float *gs = GK + (int64_t)((uint32_t)uni(ws.uniq_row[u]) % nk) * Rin * dk;
+                for (int jb = 0; jb < dk; jb += 4) {
+                    const int j = jb + kq;
+                    float av[2], bv[2];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int p = i * 16 + li, q = i * 16 + li;
+                        const float x = gu[(p < P ? p : 0) * dk + j], y = gs[(q < Rin ? q : 0) * dk + j];
+                        av[i] = p < P ? x : 0.f;
+                        bv[i] = q < Rin ? y : 0.f;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int k = 0; k < 2; ++k)
+                            if (i < npt && k < nqt) acc[i][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[k], acc[i][k], 0, 0, 0);
+                }
+            }
+            // lane (kq, li) holds dV[p = 16i + 4kq + v][q = 16k + li]
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int q = 16 * k + li;
+                    if (i < npt && k < nqt && q < Rin) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int p = 16 * i + 4 * kq + v;
+                            if (p < P) dV[p * Rin + q] = acc[i][k][v];
+                        }
+                    }
+                }
+            const int RT = 16 / dk, slot = li / dk, jl = li - slot * dk;
+            for (int r0 = u0; r0 < u1; r0 += RT) {
+                const int us = r0 + slot < u1 ? r0 + slot : u1 - 1; // padding slots: the tile's last row
+                const float *gu = Et + (int64_t)us * Dp + jl;       // g_u[p][jl] at p * dk
+                floatx4 pa[2];
+                pa[0] = pa[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int p0 = 0; p0 < P; p0 += 4) {
+                    const int p = p0 + kq;
+                    const bool okp = p < P;
+                    const float x = gu[(okp ? p : 0) * dk];
+                    const float ax = okp ? x : 0.f;
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const int q = 16 * k + li;
+                        const float y = V[(okp ? p : 0) * Rin + (q < Rin ? q : 0)];
+                        if (k < nqt) pa[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(ax, (okp && q < Rin) ? y : 0.f, pa[k], 0, 0, 0);
+                    }
+                }
+                // lane (kq, li) holds PK of row slot (4kq+v)/dk, j = (4kq+v)%dk, q = 16k + li
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int q = 16 * k + li;
+                    if (k < nqt && q < Rin) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int r = 4 * kq + v, sl = r / dk, jj = r - sl * dk;
+                            if (r0 + sl < u1) a.kp.PK[(int64_t)(r0 + sl) * a.kp.pkmax + q * dk + jj] = pa[k][v];
+                        }
+                    }
+                }
+            }
+            continue;
+        }
         if (P <= kKLastP && Rin <= 64 && dk <= kKLastD) {
             // lane q keeps the P sums of column q; the rows' g_u entries are
             // wave-uniform (scalar loads), the lane's G slice column in
