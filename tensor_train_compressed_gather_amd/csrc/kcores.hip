@@ -415,6 +415,108 @@ __global__ __launch_bounds__(kThreads) void k_kb_q(KArgs a, int m)
         const float *gsl = a.cores.g[t * K + c] + (int64_t)ic * Rin * cols; // [Rin][cols]
         const float *dv = a.kp.dV[m] + g * a.kp.smax[m];                   // [P][cols]
         float *qo = a.kp.Q[m] + g * a.kp.qmax[m];
+        if (cols % 16 == 0 && a.kp.smax[m] % 4 == 0 && a.kp.qmax[m] % 4 == 0) {
+            // Matrix cores (float4 rows of dV_m and of the core slice: the
+            // workspace strides are multiples of 4 floats and cores 16-byte
+            // aligned).  Q^T[col][q] = sum_p dV[p][col] Vp[p][q]: tiles of 16
+            // columns (tile c of a 64-column block takes the columns cb + 4i + c,
+            // so one float4 feeds four tiles), the parent's columns q as B,
+            // K = p four at a time.
+            const int li = lane & 15, kq = lane >> 4;
+            for (int qb = 0; qb < Rin; qb += 16) {
+                const int q = qb + li;
+                const bool okq = q < Rin;
+                for (int cb = 0; cb < cols; cb += 64) {
+                    const bool full = cols - cb >= 64;
+                    const int nt = full ? 4 : (cols - cb) / 16;
+                    floatx4 acc[4];
+#pragma unroll
+                    for (int c4 = 0; c4 < 4; ++c4) acc[c4] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    for (int p0 = 0; p0 < P; p0 += 4) {
+                        const int pp = p0 + kq;
+                        const bool okp = pp < P;
+                        const float vb = Vp[(okp ? pp : 0) * Rin + (okq ? q : 0)];
+                        const float bv = (okp && okq) ? vb : 0.f;
+                        const float *drow = dv + (int64_t)(okp ? pp : 0) * cols + cb;
+                        float da[4];
+                        if (full) {
+                            const float4 d4 = *reinterpret_cast<const float4 *>(drow + 4 * li);
+                            da[0] = d4.x;
+                            da[1] = d4.y;
+                            da[2] = d4.z;
+                            da[3] = d4.w;
+                        } else {
+#pragma unroll
+                            for (int c4 = 0; c4 < 4; ++c4) da[c4] = drow[16 * (c4 < nt ? c4 : 0) + li];
+                        }
+#pragma unroll
+                        for (int c4 = 0; c4 < 4; ++c4)
+                            if (c4 < nt) acc[c4] = __builtin_amdgcn_mfma_f32_16x16x4f32(okp ? da[c4] : 0.f, bv, acc[c4], 0, 0, 0);
+                    }
+                    if (okq) {
+                        float *orow = qo + (int64_t)q * cols + cb;
+                        if (full) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                *reinterpret_cast<float4 *>(orow + 16 * kq + 4 * v) =
+                                    make_float4(acc[0][v], acc[1][v], acc[2][v], acc[3][v]);
+                        } else {
+#pragma unroll
+                            for (int c4 = 0; c4 < 4; ++c4)
+                                if (c4 < nt)
+                                    *reinterpret_cast<float4 *>(orow + 16 * c4 + 4 * kq) =
+                                        make_float4(acc[c4][0], acc[c4][1], acc[c4][2], acc[c4][3]);
+                        }
+                    }
+                }
+            }
+            // Cc[p][q] = sum_col dV[p][col] G[q][col]: K = the columns, in each
+            // block of 16 lane kq takes the columns 4kq .. 4kq+3 over four steps
+            // (one float4 of each operand; the sum covers every column once)
+            float *cc = a.kp.Cc[m] + g * a.kp.smax[m - 1];
+            for (int pb = 0; pb < P; pb += 16) {
+                const int pr = pb + li;
+                const bool okp = pr < P;
+                for (int qb = 0; qb < Rin; qb += 32) {
+                    floatx4 acc[2];
+                    acc[0] = acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    for (int c16 = 0; c16 < cols; c16 += 16) {
+                        const float4 a4 = *reinterpret_cast<const float4 *>(dv + (int64_t)(okp ? pr : 0) * cols + c16 + 4 * kq);
+                        float4 b4[2];
+#pragma unroll
+                        for (int k2 = 0; k2 < 2; ++k2) {
+                            const int q = qb + 16 * k2 + li;
+                            b4[k2] = *reinterpret_cast<const float4 *>(gsl + (int64_t)(q < Rin ? q : 0) * cols + c16 + 4 * kq);
+                        }
+                        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                        for (int k2 = 0; k2 < 2; ++k2) {
+                            const bool okq = qb + 16 * k2 + li < Rin;
+                            const float bv[4] = {b4[k2].x, b4[k2].y, b4[k2].z, b4[k2].w};
+                            if (qb + 16 * k2 < Rin) {
+#pragma unroll
+                                for (int s4 = 0; s4 < 4; ++s4)
+                                    acc[k2] = __builtin_amdgcn_mfma_f32_16x16x4f32(okp ? av[s4] : 0.f, okq ? bv[s4] : 0.f,
+                                                                                  acc[k2], 0, 0, 0);
+                            }
+                        }
+                    }
+                    // lane (kq, li) holds Cc[p = pb + 4kq + v][q = qb + 16k2 + li]
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2) {
+                        const int q = qb + 16 * k2 + li;
+                        if (q < Rin) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const int p = pb + 4 * kq + v;
+                                if (p < P) cc[p * Rin + q] = acc[k2][v];
+                            }
+                        }
+                    }
+                }
+            }
+            continue;
+        }
         if (P <= kKRowBlk) {
             // lanes over the columns (j, r): the P entries of dV_m in registers,
             // the parent's entries wave-uniform (scalar loads); same sums, same order
