@@ -143,7 +143,7 @@ __device__ void g3t_copy(const FwdArgs &a)
     }
 }
 
-// Claiming work (wave 0 of a block).  claim_start() issues the atomic on the
+// Claiming work (one wave of a block).  claim_start() issues the atomic on the
 // current victim's head; claim_finish() checks it and, when that victim is
 // drained, probes the next 64 victims in parallel and retries.  Every chunk is
 // handed out exactly once (heads only grow) and the loop ends once every
@@ -1073,7 +1073,7 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
     constexpr int KQ = L::KQ, NTW = L::NTW, CSTR = L::CSTR, CU = L::CU, PQ = L::PQ;
     __shared__ __attribute__((aligned(16))) float Cs[2][L::CT];
     // records of ring entries k .. k+2 (iteration k), entry k+3 being written;
-    // entry k+4's record travels in wave 0's registers for a whole iteration
+    // entry k+4's record travels in the ring owner's registers for a whole iteration
     constexpr int NR = 5;
     __shared__ ChunkRec rr[NR];
     __shared__ int cid[NR], s_ck[NR];
@@ -1092,12 +1092,12 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
     int32_t *heads = ws.heads + CLS * heads_stride * kHeadPad;
     const int nvict = STEAL ? nb >> 3 : 1;
     int vi = 0, steals = 0, hits = 0, misses = 0, nwork = 0, nrows = 0;
-    int raw = 0x7fffffff; // wave 0 (stealing): the claim in flight
+    int raw = 0x7fffffff; // ring owner (stealing): the claim in flight
     Victim cv;
     int cstat = base + range_begin(me, C, nb); // next chunk of the static range
     const bool l2 = a.sched == kSchedStealL2;
 
-    // next chunk id of this block (wave 0): its static range in order, then
+    // next chunk id of this block (ring owner): its static range in order, then
     // (stealing modes) chunks claimed from the other blocks of its XCD
     auto next_id = [&]() -> int {
         if constexpr (!STEAL) {
@@ -1116,8 +1116,11 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
             ok = __hip_atomic_load(&ws.flags[r.slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
         s_ck[i] = ok;
     };
-    int pre = 0, pre_id = -1; // wave 0: the record of the next ring entry to write, and its chunk
-    if (w == 0) {
+    // the ring's owner is the last wave: the output tiles w, w+4, ... leave it
+    // the fewest rows when a chunk's tile count is not a multiple of 4
+    constexpr int kRing = kThreads / 64 - 1;
+    int pre = 0, pre_id = -1; // ring owner: the record of the next ring entry to write, and its chunk
+    if (w == kRing) {
         if constexpr (STEAL) {
             cv.at(vi, me, nb, base, C);
             raw = claim_issue(heads, cv, vi, nvict);
@@ -1385,14 +1388,14 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
                 }
             }
         }
-        // wave 0: ring entry k+3 (its record loaded an iteration ago) goes to the
+        // ring owner: entry k+3 (its record loaded an iteration ago) goes to the
         // slot of entry k-2; the next chunk is claimed and the record of entry
         // k+4 loaded.  Both loads are unconditional (past the last chunk, chunk
         // 0's record under id -1, never used): a load in a branch is waited for
         // at the join.  Placed after the rows' operand reloads, so that on
         // every path the record and the claim issued an iteration ago are
         // older than those reloads and no wait here covers them.
-        if (w == 0) {
+        if (w == kRing) {
             reinterpret_cast<int *>(&rr[i3r])[lane] = pre;
             if (lane == 0) cid[i3r] = pre_id;
             pre_id = pre_id >= 0 ? next_id() : -1;
@@ -1414,10 +1417,8 @@ __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a
     }
     if (threadIdx.x == 0 && pub_slot >= 0)
         __hip_atomic_store(&ws.flags[pub_slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0) {
-        block_stat_write(ws.bstat + CLS * kStatBlocks, s_t0, nwork, nrows);
-        if (steals) atomicAdd(&ws.ctrl[CTRL_STEALS], steals);
-    }
+    if (threadIdx.x == 0) block_stat_write(ws.bstat + CLS * kStatBlocks, s_t0, nwork, nrows);
+    if (lane == 0 && w == kRing && steals) atomicAdd(&ws.ctrl[CTRL_STEALS], steals);
     // hits and misses are counted by every wave alike; wave 0 reports them
     if (lane == 0 && w == 0) {
         if (hits) atomicAdd(&ws.ctrl[CTRL_CKPT_HIT], hits);
