@@ -124,7 +124,7 @@ TRAFFIC_KERNELS = {  # (the training step runs one instantiation per rank)
     "k_bwd_class<32,": ("bwd_r32", ["backward.hip", "internal.h"]),
     "k_bwd_class<16,": ("bwd_r16", ["backward.hip", "internal.h"]),
     "k_contract_t<64,": ("fwd_r64", ["forward.hip", "internal.h"]),
-    "k_contract_w<32,": ("fwd_r32", ["forward.hip", "internal.h"]),
+    "k_contract_t<32,": ("fwd_r32", ["forward.hip", "internal.h"]),
     "k_contract_w<16,": ("fwd_r16", ["forward.hip", "internal.h"]),
     "k_pool<": ("pool", ["forward.hip", "internal.h"]),
     "k_gu_gather": ("bwd_gather", ["backward.hip", "internal.h"]),
@@ -170,7 +170,7 @@ def write_traffic(d):
     print(json.dumps(out, indent=1, sort_keys=True))
 
 
-COUNTER_KERNELS = (("k_contract_w<16", "fwd_r16"), ("k_contract_w<32", "fwd_r32"), ("k_contract_t<64", "fwd_r64"),
+COUNTER_KERNELS = (("k_contract_w<16", "fwd_r16"), ("k_contract_t<32", "fwd_r32"), ("k_contract_t<64", "fwd_r64"),
                    ("k_bwd_class<16", "bwd_r16"), ("k_bwd_class<32", "bwd_r32"), ("k_bwd_class<64", "bwd_r64"),
                    ("k_pool<", "pool"), ("k_gu_gather", "bwd_gather"))
 

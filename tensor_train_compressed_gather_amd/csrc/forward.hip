@@ -726,7 +726,7 @@ __device__ __forceinline__ void rec_piece(int rv, int P, int e, int &j, int &rb,
 }
 
 // ---------------------------------------------------------------------------
-// Per-wave contraction of the rank classes R <= 32 (R1 = R2 = R, d1, d2 <= 4,
+// Per-wave contraction of the rank classes R <= 16 (R1 = R2 = R, d1, d2 <= 4,
 // d3 <= 16).  Every wave of the grid is an independent persistent worker with
 // its own static range of chunks (and, in the stealing modes, its own queue
 // head): no block barrier anywhere in the chunk loop.  Per chunk (one tile of
@@ -753,18 +753,19 @@ struct FwdW {
     static constexpr int BREG = NT * KQ;   // G2 slice registers per lane
     static constexpr int CSTR = R + 4;     // LDS row stride of C (floats)
     static constexpr int CU = 16 * CSTR;   // floats per unit
-    static constexpr int OCC = R <= 16 ? 4 : 2; // blocks of four waves per CU
+    static constexpr int OCC = 4;          // blocks of four waves per CU
     static constexpr int NQ = 4;           // row tiles whose operands are loaded together
 };
 template <int R> constexpr int fwd_workers_per_cu() { return FwdW<R>::OCC * (kThreads / 64); }
-static_assert(fwd_workers_per_cu<8>() <= kMaxClsOcc && fwd_workers_per_cu<16>() <= kMaxClsOcc &&
-              fwd_workers_per_cu<32>() <= kMaxClsOcc, "one queue head per worker");
+static_assert(fwd_workers_per_cu<8>() <= kMaxClsOcc && fwd_workers_per_cu<16>() <= kMaxClsOcc,
+              "one queue head per worker");
 
-template <int R, bool KEEP, bool STEAL>
+template <int R, bool STEAL>
 __global__ __launch_bounds__(kThreads, FwdW<R>::OCC) void k_contract_w(FwdArgs a, int heads_stride)
 {
+    static_assert(R == 8 || R == 16, "ranks 32 and 64 run the tile-pipelined kernel");
     using L = FwdW<R>;
-    constexpr int CLS = R == 8 ? 0 : R == 16 ? 1 : 2;
+    constexpr int CLS = R == 8 ? 0 : 1;
     constexpr int KQ = L::KQ, NT = L::NT, CSTR = L::CSTR, CU = L::CU, NQ = L::NQ;
     __shared__ __attribute__((aligned(16))) float Cs_all[kThreads / 64][4 * CU];
     __shared__ long long s_t0;
@@ -998,17 +999,6 @@ __global__ __launch_bounds__(kThreads, FwdW<R>::OCC) void k_contract_w(FwdArgs a
                 }
             }
         }
-        if constexpr (KEEP) {
-            // C of the tile's units, compact [unit position in the work order][16][R],
-            // written by the tile's first chunk
-            if (rbeg == 0) {
-                float4 *dst = reinterpret_cast<float4 *>(ws.Cg + kconst(ws.cbase)[t] + (int64_t)ubeg * 16 * R);
-                for (int e = lane; e < nu * 4 * R; e += 64) {
-                    const int j = e / (4 * R), f2 = e - j * (4 * R), m = f2 / (R / 4), c4 = f2 - m * (R / 4);
-                    dst[e] = *reinterpret_cast<const float4 *>(Cw + j * CU + m * CSTR + 4 * c4);
-                }
-            }
-        }
         ++nwork;
         nrows += fld(4) - rbeg;
         rec = recn;
@@ -1061,9 +1051,10 @@ struct FwdT {
     static constexpr int CSTR = R + 4;         // LDS row stride of C (floats)
     static constexpr int CU = 16 * CSTR + 16;  // floats per unit (+16 rotates banks between units)
     static constexpr int CT = 4 * CU;          // floats per tile slot
-    static constexpr int OCC = R == 64 ? 2 : 3; // blocks per CU (register-limited, no spills)
+    static constexpr int OCC = R == 64 ? 2 : 4; // blocks per CU (register-limited, no spills; rank 32: 116 VGPRs)
     static constexpr int PQ = R == 64 ? 3 : 2;  // output tiles per wave whose operands are prefetched
 };
+static_assert(FwdT<32>::OCC <= kMaxClsOcc && FwdT<64>::OCC <= kMaxClsOcc, "one queue head per block");
 
 template <int R, bool KEEP, bool STEAL>
 __global__ __launch_bounds__(kThreads, FwdT<R>::OCC) void k_contract_t(FwdArgs a, int heads_stride)
@@ -1650,7 +1641,7 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
         // (ranks 8, 16 and 32: waves of the per-wave kernel; rank 64: blocks of
         // the tile-pipelined kernel; fused pooling: blocks of k_contract)
         ClassGrid cg;
-        const int wpc[4] = {fwd_workers_per_cu<8>(), fwd_workers_per_cu<16>(), fwd_workers_per_cu<32>(),
+        const int wpc[4] = {fwd_workers_per_cu<8>(), fwd_workers_per_cu<16>(), FwdT<32>::OCC,
                             FwdT<64>::OCC};
         for (int c = 0; c < 4; ++c) cg.nb[c] = p.num_blocks * (!fused ? wpc[c] : kClsOcc[c]);
         const int hs = p.num_blocks * kMaxClsOcc;
@@ -1672,26 +1663,26 @@ hipError_t launch_forward(const Plan &p, const CorePtrs &cores, const int64_t *o
                     case 2: TT_FWD_CLASS(32, false, true); break;
                     default: TT_FWD_CLASS(64, false, true); break;
                     }
-                } else if (c < 3) {
-#define TT_FWD_WAVE(RR, KK, SS) hipLaunchKernelGGL((k_contract_w<RR, KK, SS>), dim3(p.num_blocks * FwdW<RR>::OCC), block, 0, s, ac, hs)
-#define TT_FWD_WAVES(RR, KK) if (ac.sched != kSchedStatic) TT_FWD_WAVE(RR, KK, true); else TT_FWD_WAVE(RR, KK, false)
-                    if (c == 0) TT_FWD_WAVES(8, false);
-                    else if (c == 1) TT_FWD_WAVES(16, false);
-                    else if (p.keep_c) TT_FWD_WAVES(32, true);
-                    else TT_FWD_WAVES(32, false);
+                } else if (c < 2) {
+#define TT_FWD_WAVE(RR, SS) hipLaunchKernelGGL((k_contract_w<RR, SS>), dim3(p.num_blocks * FwdW<RR>::OCC), block, 0, s, ac, hs)
+#define TT_FWD_WAVES(RR) if (ac.sched != kSchedStatic) TT_FWD_WAVE(RR, true); else TT_FWD_WAVE(RR, false)
+                    if (c == 0) TT_FWD_WAVES(8);
+                    else TT_FWD_WAVES(16);
 #undef TT_FWD_WAVES
 #undef TT_FWD_WAVE
                 } else {
-                    // the tile-pipelined block kernel, also when it keeps C for the
-                    // backward (measured on the 26-table training step: 0.97 ms
-                    // against 1.10 for the block-cooperative kernel k_contract)
+                    // ranks 32 and 64: the tile-pipelined block kernel, also when it
+                    // keeps C for the backward (measured on the 26-table training
+                    // step: rank 64 0.97 ms against 1.10 for the block-cooperative
+                    // kernel k_contract; rank 32 0.14 against 0.17 ms, and 0.30
+                    // against 0.30 on the 26-table forward, for the per-wave kernel)
                     const bool steal = ac.sched != kSchedStatic;
 #define TT_FWD_TILE(RR, KK, SS) hipLaunchKernelGGL((k_contract_t<RR, KK, SS>), dim3(p.num_blocks * FwdT<RR>::OCC), block, 0, s, ac, hs)
-                    if (p.keep_c) {
-                        if (steal) TT_FWD_TILE(64, true, true);
-                        else TT_FWD_TILE(64, true, false);
-                    } else if (steal) TT_FWD_TILE(64, false, true);
-                    else TT_FWD_TILE(64, false, false);
+#define TT_FWD_TILES(RR) if (p.keep_c) { if (steal) TT_FWD_TILE(RR, true, true); else TT_FWD_TILE(RR, true, false); } \
+                         else if (steal) TT_FWD_TILE(RR, false, true); else TT_FWD_TILE(RR, false, false)
+                    if (c == 2) { TT_FWD_TILES(32); }
+                    else { TT_FWD_TILES(64); }
+#undef TT_FWD_TILES
 #undef TT_FWD_TILE
                 }
 #undef TT_FWD_CLASS
