@@ -151,10 +151,27 @@ __global__ __launch_bounds__(kThreads) void k_sorted_meta(BwdArgs a)
             l[i] = ws.perm[pos < n ? pos : n - 1];
         }
         int u0 = ws.inv[ws.perm[p0]];
+        // the bags of the chunk's lookups, all in flight before any store of
+        // this chunk (a load behind a store waits for it: one counter for both)
+        int bg[kSmPer];
+#pragma unroll
+        for (int i = 0; i < kSmPer; ++i) bg[i] = ws.lb[l[i]];
         u0 = u0 < 0 ? 0 : (u0 >= U ? U - 1 : u0);
         __syncthreads(); // previous chunk's window read
-        for (int j = threadIdx.x; j <= kSmChunk; j += kThreads)
-            win[j] = u0 + j <= U ? ws.uniq_start[u0 + j] : 0x7fffffff;
+        // window of run starts: unconditional loads at clamped positions
+        // (uniq_start holds U + 1 entries), then the entries past U masked
+        constexpr int kWinPer = (kSmChunk + 1 + kThreads - 1) / kThreads;
+        int wv[kWinPer];
+#pragma unroll
+        for (int k = 0; k < kWinPer; ++k) {
+            const int j = threadIdx.x + k * kThreads;
+            wv[k] = ws.uniq_start[u0 + j <= U ? u0 + j : U];
+        }
+#pragma unroll
+        for (int k = 0; k < kWinPer; ++k) {
+            const int j = threadIdx.x + k * kThreads;
+            if (j <= kSmChunk) win[j] = u0 + j <= U ? wv[k] : 0x7fffffff;
+        }
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < kSmPer; ++i) {
@@ -168,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void k_sorted_meta(BwdArgs a)
                 if (win[mid] <= pos) jl = mid;
                 else jh = mid;
             }
-            ws.sm[pos] = make_int2(ws.lb[l[i]], u0 + jl);
+            ws.sm[pos] = make_int2(bg[i], u0 + jl);
         }
     }
 }

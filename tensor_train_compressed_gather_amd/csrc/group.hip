@@ -132,10 +132,19 @@ __global__ __launch_bounds__(kThreads) void k_sort_upsweep(const uint32_t *keys,
     const int tile = sort_tile(n);
     const int64_t base = (int64_t)tile * kSortTile;
     const uint32_t dmask = (1u << dbits) - 1u;
-#pragma unroll 4
-    for (int j = 0; j < kSortItems; ++j) {
-        int64_t i = base + j * kThreads + threadIdx.x;
-        if (i < n) atomicAdd(&cnt[(keys[i] >> shift) & dmask], 1u);
+    if (base < n) {
+        // every key of the thread in flight at once: unconditional loads from
+        // clamped positions (a load under a condition is waited for before
+        // the next one is issued), the range test applied when counting
+        uint32_t kk[kSortItems];
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const int64_t i = base + j * kThreads + threadIdx.x;
+            kk[j] = keys[i < n ? i : n - 1];
+        }
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j)
+            if (base + j * kThreads + threadIdx.x < n) atomicAdd(&cnt[(kk[j] >> shift) & dmask], 1u);
     }
     __syncthreads();
     for (int d = threadIdx.x; d <= (int)dmask; d += kThreads) hist[(int64_t)d * nblk + tile] = cnt[d];
@@ -181,11 +190,20 @@ __global__ __launch_bounds__(kThreads) void k_sort_downsweep(const uint32_t *kin
     int32_t val[ROUNDS];
     uint32_t rank[ROUNDS];
     const uint64_t lt = (1ull << lane) - 1ull;
+    // the tile's keys and values all in flight at once: unconditional loads
+    // from clamped positions (a load under a condition is waited for before
+    // the next one is issued, one memory round trip per round)
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+        const int64_t i = base + w * SUB + r * 64 + lane, ic = i < n ? i : n - 1;
+        key[r] = kin[ic];
+        val[r] = vin[ic];
+    }
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
         const int64_t i = base + w * SUB + r * 64 + lane;
         const bool valid = i < n;
-        const uint32_t k = valid ? kin[i] : 0xffffffffu;
+        const uint32_t k = valid ? key[r] : 0xffffffffu;
         const uint32_t d = (k >> shift) & dmask;
         uint64_t m = __ballot(valid);
 #pragma unroll
@@ -200,7 +218,6 @@ __global__ __launch_bounds__(kThreads) void k_sort_downsweep(const uint32_t *kin
         if (valid && below == 0) wcnt[w][d] = prior + (uint32_t)__popcll(m);
         __builtin_amdgcn_wave_barrier();
         key[r] = k;
-        val[r] = valid ? vin[i] : -1;
         rank[r] = valid ? prior + below : 0xffffffffu;
     }
     __syncthreads();
@@ -299,15 +316,21 @@ struct UniqueOp {
     Ws ws;
     int64_t n;
     __device__ int64_t count() const { return n; }
-    __device__ uint64_t value(int64_t k) const { return (k == 0 || sk[k] != sk[k - 1]) ? 1 : 0; }
-    __device__ void emit(int64_t k, uint64_t excl, uint64_t v) const
+    __device__ uint64_t value(int64_t k) const
+    {
+        const uint32_t a = sk[k], b = sk[k > 0 ? k - 1 : 0]; // both loads unconditional
+        return (k == 0 || a != b) ? 1 : 0;
+    }
+    // the sorted key and original position of element k, loaded before any emit
+    __device__ int2 aux(int64_t k) const { return make_int2((int)sk[k], perm[k]); }
+    __device__ void emit(int64_t k, uint64_t excl, uint64_t v, int2 ax) const
     {
         const int32_t uid = (int32_t)(excl + v) - 1;
         if (v) {
-            ws.ukey[uid] = sk[k];
+            ws.ukey[uid] = (uint32_t)ax.x;
             ws.uniq_start[uid] = (int32_t)k;
         }
-        ws.inv[perm[k]] = uid;
+        ws.inv[ax.y] = uid;
     }
     __device__ void total(uint64_t tot, int64_t nn) const
     {
@@ -330,32 +353,38 @@ struct GroupOp {
         *row = (int32_t)(key - tab[*t].key_base);
         *q = *row / tab[*t].n3;
     }
+    // (table, row, prefix) of unique row u and the table of row u - 1 (-1 for
+    // the first), read unconditionally (row 0 stands in for row -1)
+    struct Aux {
+        int t, tprev;
+        int32_t row, q;
+    };
+    __device__ Aux aux(int64_t u) const
+    {
+        Aux g;
+        int32_t r0, q0;
+        info(u, &g.t, &g.row, &g.q);
+        info(u > 0 ? u - 1 : 0, &g.tprev, &r0, &q0);
+        g.tprev = u > 0 ? g.tprev : -1;
+        return g;
+    }
     __device__ uint64_t value(int64_t u) const
     {
-        if (u == 0) return 1;
         int t0, t1;
         int32_t r0, r1, q0, q1;
-        info(u - 1, &t0, &r0, &q0);
+        info(u > 0 ? u - 1 : 0, &t0, &r0, &q0);
         info(u, &t1, &r1, &q1);
-        return (t0 != t1 || q0 != q1) ? 1 : 0;
+        return (u == 0 || t0 != t1 || q0 != q1) ? 1 : 0;
     }
-    __device__ void emit(int64_t u, uint64_t excl, uint64_t v) const
+    __device__ void emit(int64_t u, uint64_t excl, uint64_t v, const Aux &g) const
     {
-        int t;
-        int32_t row, q;
-        info(u, &t, &row, &q);
         const int32_t gid = (int32_t)(excl + v) - 1;
-        ws.uniq_row[u] = row;
+        ws.uniq_row[u] = g.row;
         if (v) {
-            ws.grp_prefix[gid] = q;
+            ws.grp_prefix[gid] = g.q;
             ws.grp_start[gid] = (int32_t)u;
         }
-        int tprev = -1;
-        if (u > 0) {
-            int32_t r0, q0;
-            info(u - 1, &tprev, &r0, &q0);
-        }
-        for (int tt = tprev + 1; tt <= t; ++tt) {
+        for (int tt = g.tprev + 1; tt <= g.t; ++tt) {
             ws.tab_uniq_start[tt] = (int32_t)u;
             ws.tab_grp_start[tt] = gid;
         }
@@ -393,18 +422,32 @@ __global__ __launch_bounds__(kThreads) void k_units_unique(const TableDesc *tab,
 }
 
 // Per-table bases of the E rows and of the backward partial buffers.
-__global__ void k_finalize_bases(const TableDesc *tab, int T, int unique_only, Ws ws)
+__global__ __launch_bounds__(64) void k_finalize_bases(const TableDesc *tab, int T, int unique_only, Ws ws)
 {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    // one lane per table reads its figures (all loads in flight together, none
+    // behind a store); lane 0 then forms the running sums from LDS
+    __shared__ int64_t su[kMaxTables], sn[kMaxTables], sunits[kMaxTables];
+    __shared__ int sdp[kMaxTables], sp3[kMaxTables], scls[kMaxTables], sr2[kMaxTables];
+    const int t = threadIdx.x;
+    if (t < T) {
+        const TableDesc &d = tab[t];
+        su[t] = ws.tab_uniq_start[t];
+        sn[t] = ws.tab_uniq_start[t + 1] - ws.tab_uniq_start[t];
+        sunits[t] = ws.tab_unit_start[t + 1] - ws.tab_unit_start[t];
+        sdp[t] = d.Dp;
+        sp3[t] = d.R2 * d.d3;
+        scls[t] = d.cls;
+        sr2[t] = d.R2;
+    }
+    __syncthreads();
+    if (t != 0) return;
     if (!unique_only) ws.ctrl[CTRL_UNITS] = ws.ctrl[CTRL_G];
     int64_t e = 0, p3 = 0;
-    for (int t = 0; t < T; ++t) {
-        const TableDesc &d = tab[t];
-        const int64_t u0 = ws.tab_uniq_start[t], u1 = ws.tab_uniq_start[t + 1];
-        ws.ebase[t] = e - u0 * d.Dp;
-        e += (u1 - u0) * d.Dp;
-        ws.p3base[t] = p3 - u0 * (int64_t)d.R2 * d.d3;
-        p3 += (u1 - u0) * (int64_t)d.R2 * d.d3;
+    for (int k = 0; k < T; ++k) {
+        ws.ebase[k] = e - su[k] * sdp[k];
+        e += sn[k] * sdp[k];
+        ws.p3base[k] = p3 - su[k] * (int64_t)sp3[k];
+        p3 += sn[k] * (int64_t)sp3[k];
     }
     // kept prefix intermediates: 16 x R2 per unit of a table of the kept rank
     // classes, by position in the work order.  That order is class-major (tables grouped
@@ -412,14 +455,12 @@ __global__ void k_finalize_bases(const TableDesc *tab, int T, int unique_only, W
     // table's units are contiguous there but not at tab_unit_start.
     int64_t cg = 0, pos = 0;
     for (int c = 0; c <= 4; ++c)
-        for (int t = 0; t < T; ++t) {
-            const TableDesc &d = tab[t];
-            if ((d.cls < 0 ? 4 : d.cls) != c) continue;
-            const int64_t units = ws.tab_unit_start[t + 1] - ws.tab_unit_start[t];
-            const int64_t per = d.cls >= kKeepMinCls ? 16 * (int64_t)d.R2 : 0;
-            ws.cbase[t] = cg - pos * per;
-            cg += units * per;
-            pos += units;
+        for (int k = 0; k < T; ++k) {
+            if ((scls[k] < 0 ? 4 : scls[k]) != c) continue;
+            const int64_t per = scls[k] >= kKeepMinCls ? 16 * (int64_t)sr2[k] : 0;
+            ws.cbase[k] = cg - pos * per;
+            cg += sunits[k] * per;
+            pos += sunits[k];
         }
 }
 
@@ -448,7 +489,11 @@ struct RunOp {
     const uint32_t *k2;
     Ws ws;
     __device__ int64_t count() const { return ws.ctrl[CTRL_UNITS]; }
-    __device__ uint64_t value(int64_t k) const { return (k == 0 || k2[k] != k2[k - 1]) ? 1 : 0; }
+    __device__ uint64_t value(int64_t k) const
+    {
+        const uint32_t a = k2[k], b = k2[k > 0 ? k - 1 : 0]; // both loads unconditional
+        return (k == 0 || a != b) ? 1 : 0;
+    }
     __device__ void emit(int64_t k, uint64_t excl, uint64_t v) const
     {
         if (v) ws.run_start[excl] = (int32_t)k;
@@ -482,25 +527,29 @@ struct ChunkOp {
     Ws ws;
     int S;
     __device__ int64_t count() const { return ws.ctrl[CTRL_TILES]; }
+    // unique rows of a tile: its units' row counts, read unconditionally
+    // (units past the tile's count read its first unit and add nothing)
     __device__ int32_t rows(int64_t tile) const
     {
         const int32_t b = ws.tile_ubeg[tile], nu = ws.tile_nu[tile];
         int32_t r = 0;
-        for (int j = 0; j < nu; ++j) {
-            const int32_t u = ws.uorder[b + j];
-            r += ws.unit_start[u + 1] - ws.unit_start[u];
+#pragma unroll
+        for (int j = 0; j < kUnitsPerTile; ++j) {
+            const int32_t u = ws.uorder[b + (j < nu ? j : 0)];
+            const int32_t len = ws.unit_start[u + 1] - ws.unit_start[u];
+            r += j < nu ? len : 0;
         }
         return r;
     }
+    __device__ int32_t aux(int64_t tile) const { return rows(tile); }
     __device__ uint64_t value(int64_t tile) const
     {
         const int32_t r = rows(tile);
         const uint64_t nch = r <= S ? 1 : (uint64_t)((r + S - 1) / S);
         return nch | (nch > 1 ? (1ull << 32) : 0ull);
     }
-    __device__ void emit(int64_t tile, uint64_t excl, uint64_t v) const
+    __device__ void emit(int64_t tile, uint64_t excl, uint64_t v, int32_t r) const
     {
-        const int32_t r = rows(tile);
         const uint32_t nch = (uint32_t)(v & 0xffffffffu);
         const uint32_t lo = (uint32_t)(excl & 0xffffffffu), hi = (uint32_t)(excl >> 32);
         ws.tile_rows[tile] = r;

@@ -3,6 +3,9 @@
 
 #include "internal.h"
 
+#include <type_traits>
+#include <utility>
+
 namespace ttemb {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -121,6 +124,31 @@ __device__ __forceinline__ int scan_range(int64_t n, int64_t *lo, int64_t *hi)
     return v;
 }
 
+// Scan operators: count(), value(i) for i < count(), emit(i, exclusive, value)
+// and total(sum, count); an operator may also define aux(i), data of element i
+// that emit then takes as a fourth argument.  Every element's value and aux
+// are loaded before any emit runs: loads behind an emit's stores would wait
+// for those stores (one in-order counter for both), and a load under a
+// condition is waited for before the next one is issued, so the loads are
+// unconditional, from positions clamped into the block's range.
+template <class Op, class = void>
+struct ScanHasAux {
+    static constexpr bool value = false;
+};
+template <class Op>
+struct ScanHasAux<Op, decltype((void)std::declval<const Op &>().aux(int64_t(0)))> {
+    static constexpr bool value = true;
+};
+struct ScanNoAux {};
+template <class Op, bool A = ScanHasAux<Op>::value>
+struct ScanAux {
+    using type = ScanNoAux;
+};
+template <class Op>
+struct ScanAux<Op, true> {
+    using type = decltype(std::declval<const Op &>().aux(int64_t(0)));
+};
+
 template <class Op>
 __global__ __launch_bounds__(kThreads) void scan_phase1(Op op, uint64_t *part)
 {
@@ -129,7 +157,17 @@ __global__ __launch_bounds__(kThreads) void scan_phase1(Op op, uint64_t *part)
     int64_t lo, hi;
     const int v = scan_range(n, &lo, &hi);
     uint64_t s = 0;
-    for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) s += op.value(i);
+    for (int64_t base = lo; base < hi; base += (int64_t)kThreads * kScanItems) {
+        uint64_t x[kScanItems];
+#pragma unroll
+        for (int j = 0; j < kScanItems; ++j) {
+            const int64_t i = base + (int64_t)j * kThreads + threadIdx.x;
+            x[j] = op.value(i < hi ? i : hi - 1);
+        }
+#pragma unroll
+        for (int j = 0; j < kScanItems; ++j)
+            if (base + (int64_t)j * kThreads + threadIdx.x < hi) s += x[j];
+    }
     s = wave_sum(s);
     if (lane_id() == 0) sm[threadIdx.x >> 6] = s;
     __syncthreads();
@@ -181,14 +219,22 @@ __global__ __launch_bounds__(kThreads) void scan_phase3(Op op, const uint64_t *p
     const int64_t n = op.count();
     int64_t lo, hi;
     const int v = scan_range(n, &lo, &hi);
+    constexpr bool AUX = ScanHasAux<Op>::value;
     uint64_t carry = part[v];
     for (int64_t base = lo; base < hi; base += (int64_t)kThreads * kScanItems) {
         uint64_t v[kScanItems];
+        typename ScanAux<Op>::type ax[kScanItems];
         uint64_t ts = 0;
 #pragma unroll
         for (int j = 0; j < kScanItems; ++j) {
-            int64_t i = base + (int64_t)threadIdx.x * kScanItems + j;
-            v[j] = i < hi ? op.value(i) : 0;
+            const int64_t i = base + (int64_t)threadIdx.x * kScanItems + j, ic = i < hi ? i : hi - 1;
+            v[j] = op.value(ic);
+            if constexpr (AUX) ax[j] = op.aux(ic);
+        }
+#pragma unroll
+        for (int j = 0; j < kScanItems; ++j) {
+            const int64_t i = base + (int64_t)threadIdx.x * kScanItems + j;
+            v[j] = i < hi ? v[j] : 0;
             ts += v[j];
         }
         uint64_t tot;
@@ -196,7 +242,11 @@ __global__ __launch_bounds__(kThreads) void scan_phase3(Op op, const uint64_t *p
 #pragma unroll
         for (int j = 0; j < kScanItems; ++j) {
             int64_t i = base + (int64_t)threadIdx.x * kScanItems + j;
-            if (i < hi) op.emit(i, ex, v[j]);
+            if constexpr (AUX) {
+                if (i < hi) op.emit(i, ex, v[j], ax[j]);
+            } else {
+                if (i < hi) op.emit(i, ex, v[j]);
+            }
             ex += v[j];
         }
         carry += tot;
