@@ -611,8 +611,11 @@ __global__ __launch_bounds__(kThreads) void k_chunk_records(const TableDesc *tab
     static_assert(sizeof(ChunkRec) == 64 * sizeof(int32_t), "64 dwords per record");
     __shared__ int32_t rl[kThreads * kRecStride];
     __shared__ int32_t n3l[kThreads];
+    __shared__ int32_t tus[kMaxTables + 1]; // table unit starts: the table search reads LDS
     const int64_t C = ws.ctrl[CTRL_CHUNKS];
     const int tid = threadIdx.x, lane = tid & 63;
+    for (int t = tid; t <= T; t += kThreads) tus[t] = ws.tab_unit_start[t];
+    __syncthreads();
     for (int64_t cb = (int64_t)blockIdx.x * kThreads; cb < C; cb += (int64_t)gridDim.x * kThreads) {
         // (A) header of chunk cb + tid
         const int64_t c = cb + tid;
@@ -623,7 +626,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_records(const TableDesc *tab
             const int rbeg = ws.chunk_rbeg[c], rend = ws.chunk_rend[c];
             const int ubeg = ws.tile_ubeg[tile], nu = ws.tile_nu[tile];
             const int u0 = ws.uorder[ubeg];
-            const int t = segment_of(ws.tab_unit_start, T, u0);
+            const int t = segment_of(tus, T, u0);
             const TableDesc &tb = tab[t];
             const int P = (tb.d3 > 0 && tb.d3 <= 16) ? 16 / tb.d3 : 1;
             r[0] = tile;
@@ -641,15 +644,18 @@ __global__ __launch_bounds__(kThreads) void k_chunk_records(const TableDesc *tab
             r[20] = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                // units past the tile's count read its first unit (unconditional
+                // loads, all in flight together) and contribute nothing
+                const int u = ws.uorder[ubeg + (j < nu ? j : 0)];
+                const int s0 = ws.unit_start[u], cnt = j < nu ? ws.unit_start[u + 1] - s0 : 0;
+                const int pq = ws.unit_prefix[u];
                 int i1 = 0, us = 0, cc = 0;
                 if (j < nu) {
-                    const int u = ws.uorder[ubeg + j];
-                    const int s0 = ws.unit_start[u], cnt = ws.unit_start[u + 1] - s0;
                     const int lo = rbeg > off ? rbeg : off;
                     const int hi = rend < off + cnt ? rend : off + cnt;
                     cc = hi > lo ? hi - lo : 0;
                     us = s0 + (lo - off);
-                    i1 = ws.unit_prefix[u] / tb.n2;
+                    i1 = pq / tb.n2;
                     off += cnt;
                 }
                 r[8 + j] = i1;
@@ -669,7 +675,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_records(const TableDesc *tab
         int prev = __shfl_up(rank, 1, 64); // every lane active
         if (c < C) {
             if (lane == 0 && c > 0) {
-                const int pt = segment_of(ws.tab_unit_start, T, ws.uorder[ws.tile_ubeg[ws.chunk_tile[c - 1]]]);
+                const int pt = segment_of(tus, T, ws.uorder[ws.tile_ubeg[ws.chunk_tile[c - 1]]]);
                 prev = tab[pt].cls < 0 ? 4 : tab[pt].cls;
             }
             if (c == 0) prev = -1;
@@ -678,17 +684,32 @@ __global__ __launch_bounds__(kThreads) void k_chunk_records(const TableDesc *tab
                 for (int q = rank + 1; q <= 5; ++q) ws.ctrl[CTRL_CLS_START + q] = (int32_t)C;
         }
         __syncthreads();
-        // (B) i3 of row e % 32 of chunk e / 32, e = i * kThreads + tid (zeros past the chunk's rows)
-#pragma unroll 8
-        for (int i = 0; i < kMaxChunkRows; ++i) {
-            const int e = i * kThreads + tid, k = e >> 5, row = e & 31;
-            const int32_t *rk = rl + k * kRecStride;
-            int v = 0;
-            if (cb + k < C && row < rk[29]) {
+        // (B) i3 of row e % 32 of chunk e / 32, e = i * kThreads + tid (zeros past
+        // the chunk's rows).  Eight rows at a time, their loads all in flight:
+        // the header fields are read whatever the row (LDS, always in range),
+        // the load is unconditional (row 0 of the unique rows stands in past a
+        // chunk's rows, and its digit modulo 1 is the zero stored there), and
+        // the division's result is stored without a select (a select on it is
+        // turned into a branch around the division and the load)
+        static_assert(kMaxChunkRows % 8 == 0, "rows in groups of eight");
+#pragma unroll
+        for (int i0 = 0; i0 < kMaxChunkRows; i0 += 8) {
+            int x[8], n3v[8];
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) {
+                const int e = (i0 + ii) * kThreads + tid, k = e >> 5, row = e & 31;
+                const int32_t *rk = rl + k * kRecStride;
+                const bool ok = (cb + k < C) & (row < rk[29]);
                 const int j = (row >= rk[26]) + (row >= rk[27]) + (row >= rk[28]);
-                v = ws.uniq_row[rk[12 + j] + (row - rk[25 + j])] % n3l[k];
+                const int idx = rk[12 + j] + (row - rk[25 + j]);
+                x[ii] = ws.uniq_row[ok ? idx : 0];
+                n3v[ii] = ok ? n3l[k] : 1;
             }
-            rl[k * kRecStride + 32 + row] = v;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) {
+                const int e = (i0 + ii) * kThreads + tid, k = e >> 5, row = e & 31;
+                rl[k * kRecStride + 32 + row] = x[ii] % n3v[ii];
+            }
         }
         __syncthreads();
         // (C) wave w writes records w*64 .. w*64+63 of the block, one per store
