@@ -467,31 +467,56 @@ __global__ __launch_bounds__(kThreads) void k_bwd_runs(BwdArgs a)
 
 // dG1[t][i1] = sum of the unit partials of table t whose prefix has digit i1
 // (a contiguous range of the prefix-sorted units); zero when none.
+// Table of a reduction slot: the last table whose slot base (i1_base, or
+// i3_base when I3) is at most slot.  The bases ascend from 0 and T <= 64, so
+// each lane tests one table and the answer is the count of passing lanes: one
+// load round trip instead of a dependent walk over the tables.
+template <bool I3>
+__device__ __forceinline__ int slot_table(const TableDesc *tab, int T, int slot)
+{
+    const int lane = threadIdx.x & 63;
+    const TableDesc &d = tab[lane < T ? lane : 0];
+    const uint32_t base = I3 ? d.i3_base : d.i1_base;
+    return __popcll(__ballot(lane < T && base <= (uint32_t)slot)) - 1;
+}
+
+// First position in [lo, hi) of the ascending array v holding a value >= key
+// (hi if none), found by the whole wave: 64 probes per round, so a range of
+// 64^r positions takes r load round trips instead of log2 of its size.
+__device__ __forceinline__ int wave_lower_bound(const int32_t *v, int lo, int hi, int key)
+{
+    const int lane = threadIdx.x & 63;
+    if (hi <= lo) return lo; // empty range: no load at all
+    while (hi - lo > 64) {
+        const int step = (hi - lo + 63) / 64;
+        const int idx = lo + lane * step;
+        const bool ge = idx >= hi || v[idx < hi ? idx : lo] >= key;
+        const uint64_t m = __ballot(ge);
+        const int f = m ? __ffsll((unsigned long long)m) - 1 : 64; // lane 63 probes below hi, so f < 64 unless none
+        if (f == 0) return lo;
+        const int nhi = lo + f * step < hi ? lo + f * step : hi;
+        lo = lo + (f - 1) * step + 1;
+        hi = nhi;
+    }
+    const int idx = lo + lane;
+    const bool ge = idx >= hi || v[idx < hi ? idx : lo] >= key;
+    const uint64_t m = __ballot(ge);
+    return m ? lo + __ffsll((unsigned long long)m) - 1 : hi;
+}
+
 __global__ __launch_bounds__(kThreads) void k_reduce_g1(BwdArgs a, int total_slots)
 {
     const Ws &ws = a.ws;
     for (int slot = blockIdx.x; slot < total_slots; slot += gridDim.x) {
-        int t = 0;
-        while (t + 1 < a.T && a.tab[t + 1].i1_base <= (uint32_t)slot) ++t;
+        const int t = slot_table<false>(a.tab, a.T, slot);
         const TableDesc &tb = a.tab[t];
         const int i1 = slot - (int)tb.i1_base;
         if (i1 >= tb.n1) continue;
         const int lo0 = ws.tab_unit_start[t], hi0 = ws.tab_unit_start[t + 1];
         const int qlo = i1 * tb.n2, qhi = qlo + tb.n2;
-        int lo = lo0, hi = hi0;
-        while (lo < hi) { // first unit with prefix >= qlo
-            const int mid = (lo + hi) >> 1;
-            if (ws.unit_prefix[mid] < qlo) lo = mid + 1;
-            else hi = mid;
-        }
-        const int first = lo;
-        hi = hi0;
-        while (lo < hi) { // first unit with prefix >= qhi
-            const int mid = (lo + hi) >> 1;
-            if (ws.unit_prefix[mid] < qhi) lo = mid + 1;
-            else hi = mid;
-        }
-        const int last = lo;
+        // the table's units with prefix in [qlo, qhi) (prefixes ascend within a table)
+        const int first = wave_lower_bound(ws.unit_prefix, lo0, hi0, qlo);
+        const int last = wave_lower_bound(ws.unit_prefix, first, hi0, qhi);
         const int per = tb.d1 * tb.R1;
         float *dst = a.grads.g[t][0] + (int64_t)i1 * per;
         // partial rows of the slot's units (in unit order) staged kThreads at a
@@ -570,8 +595,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_g3(BwdArgs a, const int32_t
     __shared__ float part[kThreads];
     __shared__ int32_t ord[kG3Stage];
     for (int slot = blockIdx.x; slot < total_slots; slot += gridDim.x) {
-        int t = 0;
-        while (t + 1 < a.T && a.tab[t + 1].i3_base <= (uint32_t)slot) ++t;
+        const int t = slot_table<true>(a.tab, a.T, slot);
         const TableDesc &tb = a.tab[t];
         const int i3 = slot - (int)tb.i3_base;
         if (i3 >= tb.n3) continue;
