@@ -776,11 +776,37 @@ __global__ __launch_bounds__(BwdLds<R>::NW * 64, BwdLds<R>::OCC) void k_bwd_clas
         int rb = L::STAGE / (GST + G3ST);
         rb = rb < kMaxChunkRows ? rb : kMaxChunkRows;
         float *Gs = Sg, *G3s = Sg + rb * GST;
-        {   // stage G2[i2] as G2s[r][col] (row stride NCOL + 1), zero-padded to NCOL columns
+        {   // stage G2[i2] as G2s[r][col] (row stride NCOL + 1), zero-padded to NCOL
+            // columns: float4 loads (source rows of d2*R floats, 16-byte aligned),
+            // all of a thread's in flight at once -- unconditional, from a clamped
+            // address for the padding columns, which are written as zeros (a load
+            // under a condition is waited for before the next one is issued)
             const float *src = a.cores.g[t][1] + (int64_t)i2 * R * d2 * R;
-            for (int e = tid; e < R * NCOL; e += BT) {
-                const int r = e / NCOL, c = e - r * NCOL;
-                G2s[r * G2ST + c] = c < d2 * R ? src[r * d2 * R + c] : 0.f;
+            constexpr int N4 = R * NCOL / 4, PER = (N4 + BT - 1) / BT; // float4 per slice, per thread
+            constexpr int CH = PER < 4 ? PER : 4;                       // in flight together
+            static_assert(PER % CH == 0, "whole batches");
+            const int rowlen = d2 * R;
+#pragma unroll
+            for (int k0 = 0; k0 < PER; k0 += CH) {
+                float4 gv[CH];
+#pragma unroll
+                for (int k = 0; k < CH; ++k) {
+                    const int f = tid + (k0 + k) * BT, r = f / R, c4 = f - r * R; // NCOL / 4 == R float4 per row
+                    const bool ok = f < N4 && 4 * c4 < rowlen;
+                    gv[k] = *reinterpret_cast<const float4 *>(src + (ok ? r * rowlen + 4 * c4 : 0));
+                }
+#pragma unroll
+                for (int k = 0; k < CH; ++k) {
+                    const int f = tid + (k0 + k) * BT, r = f / R, c4 = f - r * R;
+                    if (f < N4) {
+                        const bool ok = 4 * c4 < rowlen;
+                        float *d = G2s + r * G2ST + 4 * c4;
+                        d[0] = ok ? gv[k].x : 0.f;
+                        d[1] = ok ? gv[k].y : 0.f;
+                        d[2] = ok ? gv[k].z : 0.f;
+                        d[3] = ok ? gv[k].w : 0.f;
+                    }
+                }
             }
         }
         // this wave's part of the units' dC; at rank 64 (few rows per wave
