@@ -753,7 +753,9 @@ struct FwdW {
     static constexpr int BREG = NT * KQ;   // G2 slice registers per lane
     static constexpr int CSTR = R + 4;     // LDS row stride of C (floats)
     static constexpr int CU = 16 * CSTR;   // floats per unit
-    static constexpr int OCC = 4;          // blocks of four waves per CU
+    // blocks of four waves per CU: rank 16 at five (96 VGPRs; on the 26-table
+    // training step 0.214 -> 0.200 ms against four, six spills)
+    static constexpr int OCC = R == 16 ? 5 : 4;
     static constexpr int NQ = 4;           // row tiles whose operands are loaded together
 };
 template <int R> constexpr int fwd_workers_per_cu() { return FwdW<R>::OCC * (kThreads / 64); }
